@@ -1,0 +1,93 @@
+"""Seeded synthetic inputs (fp16 K, V, Q) for the workloads in ``configs``.
+
+This module only draws random numbers; it holds none of the method's
+arithmetic.  Both the HIP path and the CPU oracle consume exactly these bits.
+
+Recipe (the pages give the distribution qualitatively: about 1% of key
+channels carry large outliers that stay fixed along the whole sequence, values
+show no such pattern -- "Makale Bülteni -- KIVI", section "İddia ve
+Gerçeklik: KIVI"):
+  * every (tensor, batch, kv-head) slice has its own numpy PCG64 stream,
+    seeded with SeedSequence([0x4B495649 + workload.index, tensor, b, h]);
+  * draw N(0, 1) in float32, row-major [T][dim];
+  * keys: the outlier channels (max(1, ceil(1% of n_kv_heads * key_dim))
+    channels of the flattened (kv head, channel) index, drawn once per
+    workload without replacement) are multiplied by ``outlier_scale`` in
+    float32;
+  * cast to fp16 with round-to-nearest-even; returned as uint16 bit patterns.
+A prefix of a longer draw equals the shorter draw, so caches of different
+lengths built from one workload agree on their common tokens.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+
+import numpy as np
+
+from .configs import Workload
+
+SEED_BASE = 0x4B495649
+T_KEY, T_VALUE, T_QUERY, T_OUTLIER = 0, 1, 2, 3
+
+
+def _rng(w: Workload, *words: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_BASE + w.index, *words])))
+
+
+def outlier_channels(w: Workload) -> np.ndarray:
+    """Sorted flat indices kvh * key_dim + channel of the outlier key channels."""
+    n = w.n_kv_heads * w.kd
+    return np.sort(_rng(w, T_OUTLIER).choice(n, size=w.n_outlier, replace=False))
+
+
+def _normal(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def key_slice(w: Workload, b: int, h: int, T: int | None = None, outliers: bool = True) -> np.ndarray:
+    T = w.T if T is None else T
+    x = _normal(_rng(w, T_KEY, b, h), (T, w.kd))
+    if outliers:
+        flat = outlier_channels(w)
+        ch = flat[flat // w.kd == h] % w.kd
+        if ch.size:
+            x[:, ch] *= np.float32(w.outlier_scale)
+    return x.astype(np.float16).view(np.uint16)
+
+
+def value_slice(w: Workload, b: int, h: int, T: int | None = None) -> np.ndarray:
+    T = w.T if T is None else T
+    return _normal(_rng(w, T_VALUE, b, h), (T, w.vd)).astype(np.float16).view(np.uint16)
+
+
+def query(w: Workload) -> np.ndarray:
+    """uint16 [B][Hq][qd]."""
+    x = _normal(_rng(w, T_QUERY), (w.batch, w.n_q_heads, w.qd))
+    return x.astype(np.float16).view(np.uint16)
+
+
+def _fill(fn, w: Workload, T: int, dim: int, out: np.ndarray | None, threads: int | None):
+    B, H = w.batch, w.n_kv_heads
+    if out is None:
+        out = np.empty((B, H, T, dim), np.uint16)
+    assert out.shape == (B, H, T, dim) and out.dtype == np.uint16
+
+    def job(bh):
+        b, h = divmod(bh, H)
+        out[b, h] = fn(w, b, h, T)
+
+    n = threads or min(16, os.cpu_count() or 1)
+    with cf.ThreadPoolExecutor(max_workers=n) as ex:
+        list(ex.map(job, range(B * H)))
+    return out
+
+
+def keys(w: Workload, T: int | None = None, out=None, threads=None) -> np.ndarray:
+    """uint16 [B][Hkv][T][kd]."""
+    return _fill(key_slice, w, w.T if T is None else T, w.kd, out, threads)
+
+
+def values(w: Workload, T: int | None = None, out=None, threads=None) -> np.ndarray:
+    """uint16 [B][Hkv][T][vd]."""
+    return _fill(value_slice, w, w.T if T is None else T, w.vd, out, threads)
