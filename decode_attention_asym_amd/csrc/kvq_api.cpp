@@ -1,0 +1,270 @@
+// kvq_api.cpp -- host side of libkvq: argument validation (always before any
+// HIP call), sizing, host counters, and the launch sequences behind the C ABI.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace kvq {
+
+Geom geom_of(const kvq_cache_cfg& c) {
+    Geom g;
+    g.B = c.batch;
+    g.Hkv = c.n_kv_heads;
+    g.kd = c.key.dim;
+    g.kG = c.key.group;
+    g.kbits = c.key.bits;
+    g.kW = c.key.group * c.key.bits / 32;
+    g.vd = c.value.dim;
+    g.vG = c.value.group;
+    g.vbits = c.value.bits;
+    g.vWT = c.value.dim * c.value.bits / 32;
+    g.vNG = c.value.dim / c.value.group;
+    g.cap = c.max_tokens;
+    g.nblk_cap = c.max_tokens / c.key.group;
+    return g;
+}
+
+}  // namespace kvq
+
+namespace {
+
+hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kvq_status check_cfg(const kvq_cache_cfg* c) {
+    if (!c) return KVQ_E_NULL;
+    if (c->kind != KVQ_KIND_KIVI && c->kind != KVQ_KIND_MLA) return KVQ_E_SHAPE;
+    if (c->reserved != 0) return KVQ_E_SHAPE;
+    if (c->batch < 1 || c->n_kv_heads < 1) return KVQ_E_SHAPE;
+    if (c->kind == KVQ_KIND_MLA && c->n_kv_heads != 1) return KVQ_E_SHAPE;
+    const kvq_stream_cfg &k = c->key, &v = c->value;
+    if ((k.bits != 2 && k.bits != 4) || (v.bits != 2 && v.bits != 4)) return KVQ_E_SHAPE;
+    if (k.axis != KVQ_AXIS_PER_CHANNEL || v.axis != KVQ_AXIS_PER_TOKEN) return KVQ_E_UNSUPPORTED;
+    if (k.dim < 32 || k.dim > 512 || k.dim % 32 != 0) return KVQ_E_SHAPE;
+    if (v.dim < 32 || v.dim > 512 || v.dim % 32 != 0) return KVQ_E_SHAPE;
+    if (k.group != 16 && k.group != 32 && k.group != 64 && k.group != 128) return KVQ_E_SHAPE;
+    if (k.group * k.bits / 32 > 8) return KVQ_E_UNSUPPORTED;
+    if (v.group != 32) return KVQ_E_UNSUPPORTED;
+    if (c->kind == KVQ_KIND_KIVI && k.dim != v.dim) return KVQ_E_SHAPE;
+    if (c->max_tokens < k.group || c->max_tokens % k.group != 0) return KVQ_E_SHAPE;
+    if (c->max_tokens > (int64_t(1) << 31)) return KVQ_E_SHAPE;
+    return KVQ_OK;
+}
+
+void sizes_of(const kvq_cache_cfg& c, kvq_buffer_sizes* s) {
+    const Geom g = geom_of(c);
+    const uint64_t bh = uint64_t(g.B) * g.Hkv;
+    s->k_codes = bh * g.nblk_cap * g.kd * g.kW * 4;
+    s->k_scale = bh * g.nblk_cap * g.kd * 2;
+    s->k_zero = s->k_scale;
+    s->k_resid = bh * g.kG * g.kd * 2;
+    s->v_codes = bh * g.cap * g.vWT * 4;
+    s->v_scale = bh * g.cap * g.vNG * 2;
+    s->v_zero = s->v_scale;
+}
+
+kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E_HIP; }
+
+int resolve_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64_t nblk, Variant v) {
+    const int64_t R = T - nblk * c.cfg.key.group;
+    const int64_t U = nblk + (R > 0 ? 1 : 0);
+    int64_t S = n_splits > 0 ? n_splits : auto_splits(c, Hq, T, v);
+    if (S > U) S = U;
+    if (S < 1) S = 1;
+    return int(S);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_str(kvq_status s) {
+    switch (s) {
+        case KVQ_OK: return "ok";
+        case KVQ_E_NULL: return "null pointer";
+        case KVQ_E_SHAPE: return "bad shape";
+        case KVQ_E_ALIGN: return "pointer not 16-byte aligned";
+        case KVQ_E_CAPACITY: return "capacity exceeded";
+        case KVQ_E_UNSUPPORTED: return "unsupported configuration";
+        case KVQ_E_WORKSPACE: return "workspace too small";
+        case KVQ_E_HIP: return "HIP launch failed";
+        case KVQ_E_STATE: return "cache holds no tokens";
+    }
+    return "unknown status";
+}
+
+kvq_status kv_cache_buffer_bytes(const kvq_cache_cfg* cfg, kvq_buffer_sizes* out) {
+    if (!out) return KVQ_E_NULL;
+    kvq_status st = check_cfg(cfg);
+    if (st != KVQ_OK) return st;
+    sizes_of(*cfg, out);
+    return KVQ_OK;
+}
+
+kvq_status kv_cache_init(const kvq_cache_cfg* cfg, const kvq_cache_buffers* bufs, kvq_cache** out) {
+    if (!out || !bufs) return KVQ_E_NULL;
+    kvq_status st = check_cfg(cfg);
+    if (st != KVQ_OK) return st;
+    const void* ptrs[7] = {bufs->k_codes, bufs->k_scale, bufs->k_zero, bufs->k_resid,
+                           bufs->v_codes, bufs->v_scale, bufs->v_zero};
+    for (const void* p : ptrs) {
+        if (!p) return KVQ_E_NULL;
+        if (!aligned16(p)) return KVQ_E_ALIGN;
+    }
+    kvq_cache* c = new (std::nothrow) kvq_cache;
+    if (!c) return KVQ_E_NULL;
+    c->cfg = *cfg;
+    c->buf = *bufs;
+    c->T = 0;
+    c->nblk = 0;
+    *out = c;
+    return KVQ_OK;
+}
+
+void kv_cache_destroy(kvq_cache* c) { delete c; }
+
+kvq_status kv_cache_reset(kvq_cache* c) {
+    if (!c) return KVQ_E_NULL;
+    c->T = 0;
+    c->nblk = 0;
+    return KVQ_OK;
+}
+
+kvq_status kv_cache_state(const kvq_cache* c, int64_t* n_tokens, int32_t* n_resid) {
+    if (!c) return KVQ_E_NULL;
+    if (n_tokens) *n_tokens = c->T;
+    if (n_resid) *n_resid = int32_t(c->T - c->nblk * c->cfg.key.group);
+    return KVQ_OK;
+}
+
+kvq_status kv_quantize_append(kvq_cache* c, const void* k, const void* v, int64_t n,
+                              uint32_t flags, void* stream) {
+    if (!c) return KVQ_E_NULL;
+    if (n < 0) return KVQ_E_SHAPE;
+    if (flags & ~KVQ_APPEND_NO_AUTOFLUSH) return KVQ_E_SHAPE;
+    if (n == 0) return KVQ_OK;
+    if (!k || !v) return KVQ_E_NULL;
+    if (!aligned16(k) || !aligned16(v)) return KVQ_E_ALIGN;
+    const Geom g = geom_of(c->cfg);
+    const int64_t G = g.kG;
+    if (c->T + n > g.cap) return KVQ_E_CAPACITY;
+    const int64_t R = c->T - c->nblk * G;
+    const bool manual = (flags & KVQ_APPEND_NO_AUTOFLUSH) != 0;
+    if (manual && R + n > G) return KVQ_E_CAPACITY;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_quant_values(*c, g, v, n, 0, n, c->T, st);
+    if (e != hipSuccess) return KVQ_E_HIP;
+    if (manual) {
+        e = launch_resid_copy(*c, g, k, n, 0, R, n, st);
+        if (e != hipSuccess) return KVQ_E_HIP;
+        c->T += n;
+        return KVQ_OK;
+    }
+    const int64_t pending = R + n;           // keys not yet in a quantized block
+    const int64_t full = pending / G;        // blocks that complete now
+    const int64_t tail = pending - full * G; // keys left in the residual
+    if (full > 0) {
+        // block tokens < c->T come from the residual (rows t - nblk*G)
+        e = launch_quant_keys(*c, g, k, n, c->T, c->nblk * G, c->nblk, full, st);
+        if (e != hipSuccess) return KVQ_E_HIP;
+        if (tail > 0) e = launch_resid_copy(*c, g, k, n, n - tail, 0, tail, st);
+    } else {
+        e = launch_resid_copy(*c, g, k, n, 0, R, n, st);
+    }
+    if (e != hipSuccess) return KVQ_E_HIP;
+    c->nblk += full;
+    c->T += n;
+    return KVQ_OK;
+}
+
+kvq_status kv_flush_residual(kvq_cache* c, void* stream, int32_t* flushed) {
+    if (!c) return KVQ_E_NULL;
+    if (flushed) *flushed = 0;
+    const Geom g = geom_of(c->cfg);
+    const int64_t R = c->T - c->nblk * g.kG;
+    if (R != g.kG) return KVQ_OK;
+    // every token of the block is a residual row; no input rows are read
+    hipError_t e = launch_quant_keys(*c, g, nullptr, 0, c->T, c->nblk * g.kG, c->nblk, 1,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return KVQ_E_HIP;
+    c->nblk += 1;
+    if (flushed) *flushed = 1;
+    return KVQ_OK;
+}
+
+kvq_status kv_decode_workspace_bytes(const kvq_cache* c, int32_t Hq, int32_t n_splits,
+                                     uint64_t* bytes) {
+    if (!c || !bytes) return KVQ_E_NULL;
+    if (Hq < 1 || Hq % c->cfg.n_kv_heads != 0) return KVQ_E_SHAPE;
+    if (n_splits < 0 || n_splits > KVQ_MAX_SPLITS) return KVQ_E_SHAPE;
+    const Geom g = geom_of(c->cfg);
+    const Variant v = pick_variant(*c, Hq);
+    int S = n_splits;
+    if (S == 0) {
+        // automatic split counts grow with the cache; cover the full capacity
+        S = auto_splits(*c, Hq, g.cap, v);
+        if (S < 1) S = 1;
+    }
+    *bytes = uint64_t(g.B) * Hq * S * (g.vd + 2) * 4;
+    return KVQ_OK;
+}
+
+kvq_status kv_decode_attention(const kvq_cache* c, const void* q, int32_t Hq, float sigma,
+                               int32_t n_splits, void* out, void* ws, uint64_t ws_bytes,
+                               void* stream) {
+    if (!c || !q || !out || !ws) return KVQ_E_NULL;
+    if (Hq < 1 || Hq % c->cfg.n_kv_heads != 0) return KVQ_E_SHAPE;
+    if (n_splits < 0 || n_splits > KVQ_MAX_SPLITS) return KVQ_E_SHAPE;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return KVQ_E_ALIGN;
+    if (c->T <= 0) return KVQ_E_STATE;
+    DecodeArgs a;
+    a.c = c;
+    a.g = geom_of(c->cfg);
+    const Variant v = pick_variant(*c, Hq);
+    a.q = q;
+    a.Hq = Hq;
+    a.sigma = sigma;
+    a.out = out;
+    a.T = c->T;
+    a.nblk = c->nblk;
+    a.R = int(c->T - c->nblk * a.g.kG);
+    a.U = int(a.nblk + (a.R > 0 ? 1 : 0));
+    a.S = resolve_splits(*c, Hq, n_splits, a.T, a.nblk, v);
+    const uint64_t need = uint64_t(a.g.B) * Hq * a.S * (a.g.vd + 2) * 4;
+    if (ws_bytes < need) return KVQ_E_WORKSPACE;
+    a.ws_acc = static_cast<float*>(ws);
+    a.ws_ml = a.ws_acc + uint64_t(a.g.B) * Hq * a.S * a.g.vd;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (g_ev_before) e = hipEventRecord(g_ev_before, st);
+    if (e != hipSuccess) return KVQ_E_HIP;
+    switch (v) {
+        default: e = launch_decode_generic(a, st); break;
+    }
+    if (e != hipSuccess) return KVQ_E_HIP;
+    if (g_ev_after) e = hipEventRecord(g_ev_after, st);
+    if (e != hipSuccess) return KVQ_E_HIP;
+    return hip_status(launch_merge(a, st));
+}
+
+kvq_status kv_set_timing_events(void* before, void* after) {
+    if ((before == nullptr) != (after == nullptr)) return KVQ_E_NULL;
+    g_ev_before = static_cast<hipEvent_t>(before);
+    g_ev_after = static_cast<hipEvent_t>(after);
+    return KVQ_OK;
+}
+
+const char* kv_decode_variant(const kvq_cache* c, int32_t Hq) {
+    if (!c || Hq < 1 || Hq % c->cfg.n_kv_heads != 0) return "invalid";
+    return variant_name(pick_variant(*c, Hq));
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// kvq_internal.h -- shared between the host library (kvq_api.cpp) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+struct kvq_cache {
+    kvq_cache_cfg cfg;
+    kvq_cache_buffers buf;
+    int64_t T;      // tokens held per sequence
+    int64_t nblk;   // quantized key blocks; residual keys = T - nblk * G (0..G)
+};
+
+namespace kvq {
+
+// Geometry derived from a validated configuration.
+struct Geom {
+    int B, Hkv;
+    int kd, kG, kbits, kW;        // key stream: dim, tokens per block, bits, words per (block, channel)
+    int vd, vG, vbits, vWT, vNG;  // value stream: dim, channels per group, bits, words per token, groups per token
+    int64_t cap, nblk_cap;        // token capacity, block capacity
+};
+
+Geom geom_of(const kvq_cache_cfg& c);
+
+// ---- quantize / append kernels (kvq_quant.hip) ----
+
+// Per-token value quantization of n_tok input rows v_in [B][Hkv][n_in][vd],
+// rows row0 .. row0 + n_tok - 1, stored at cache tokens t_dst0 ...
+hipError_t launch_quant_values(const kvq_cache& c, const Geom& g, const void* v_in,
+                               int64_t n_in, int64_t row0, int64_t n_tok, int64_t t_dst0,
+                               hipStream_t st);
+
+// Per-channel key quantization of blocks blk0 .. blk0 + nb - 1.  Key token t
+// of a block comes from the residual row (t - res_tok0) when t < in_tok0,
+// else from input row (t - in_tok0) of k_in [B][Hkv][n_in][kd].
+hipError_t launch_quant_keys(const kvq_cache& c, const Geom& g, const void* k_in, int64_t n_in,
+                             int64_t in_tok0, int64_t res_tok0, int64_t blk0, int64_t nb,
+                             hipStream_t st);
+
+// Copy m input key rows (from row src0) into residual rows dst0 ...
+hipError_t launch_resid_copy(const kvq_cache& c, const Geom& g, const void* k_in, int64_t n_in,
+                             int64_t src0, int64_t dst0, int64_t m, hipStream_t st);
+
+// ---- decode kernels (kvq_decode*.hip) ----
+
+enum Variant { V_GENERIC = 0, V_MHA = 1, V_GQA = 2, V_MLA = 3 };
+
+struct DecodeArgs {
+    const kvq_cache* c;
+    Geom g;
+    const void* q;
+    int Hq, S;          // query heads, splits
+    float sigma;
+    void* out;
+    float* ws_acc;      // [B][Hq][S][vd]
+    float* ws_ml;       // [B][Hq][S][2]
+    int64_t T, nblk;    // tokens, quantized blocks
+    int R;              // residual keys
+    int U;              // work units: nblk (+1 when R > 0)
+};
+
+Variant pick_variant(const kvq_cache& c, int Hq);
+const char* variant_name(Variant v);
+int auto_splits(const kvq_cache& c, int Hq, int64_t T, Variant v);
+
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace kvq

@@ -1,0 +1,197 @@
+/*
+ * kvq.h -- C ABI of libkvq: KIVI-style asymmetric low-bit KV cache and
+ * in-loop-dequant decode attention on AMD MI355X (gfx950).
+ *
+ * What the library computes (sources: page title + section):
+ *   "Makale Bülteni -- KIVI" (cmlonder.com paper-to-prod), lead paragraph and
+ *   section "İddia ve Gerçeklik: KIVI":
+ *     - keys are quantized per channel, values per token, to asymmetric 2-bit
+ *       codes (a zero point and a scale per group), with no calibration;
+ *     - per-channel key statistics need future tokens, so keys are grouped in
+ *       blocks of G = 32 or 64 tokens and the block that is not full yet stays
+ *       in a full-precision (fp16) residual buffer;
+ *     - decode attention reads the 2-bit cache, turning codes back into real
+ *       numbers inside the attention computation.
+ *   Section "Kod ve Entegrasyon Haritası": multi-query-head (GQA) models are
+ *   supported.
+ *   "QuantMLA: Düşük Bitli MLA KV Önbellekleme için Fonksiyon Uyumlu Çift
+ *   Yollu Kuantizasyon", sections "Giriş ve Problem Analizi" and "QuantMLA
+ *   Mimarisi ve Temel Bileşenleri": an MLA cache with a content latent at
+ *   INT2 and a decoupled RoPE key at INT4, unpacked and dequantized inside a
+ *   native attention kernel.
+ *
+ * Quantizer (one group of n values x_i, L = 2^bits - 1), computed in IEEE
+ * binary32 with no fast-math: mn = min x, mx = max x (after -0 -> +0),
+ * scale = (mx - mn) / L (true division), code_i = 0 if scale == 0 else
+ * clamp(round_half_even((x_i - mn) / scale), 0, L).  Stored side values are
+ * fp16(scale) (round to nearest even) and fp16(mn) (exact).  Dequantized
+ * value: code * scale_h + zero_h.
+ *
+ * Layouts (row-major, last index fastest; "word" = little-endian uint32;
+ * code i of a word sits in bits [bits*i, bits*i + bits)):
+ *   key stream   (per channel, groups of G tokens, blocks start at token 0)
+ *     k_codes  u32  [B][Hkv][max_tokens/G][kd][G*bits/32]
+ *              word j of channel c holds tokens (32/bits)*j .. of the block
+ *     k_scale, k_zero  fp16 [B][Hkv][max_tokens/G][kd]
+ *     k_resid  fp16 [B][Hkv][G][kd]   residual keys, token-major
+ *   value stream (per token, groups of Gv channels)
+ *     v_codes  u32  [B][Hkv][max_tokens][vd*bits/32]
+ *              word j of a token holds channels (32/bits)*j ..
+ *     v_scale, v_zero  fp16 [B][Hkv][max_tokens][vd/Gv]
+ *   KIVI: kd == vd == head dim; append inputs k, v are fp16 [B][Hkv][n][d];
+ *         q is fp16 [B][Hq][d]; out is fp16 [B][Hq][d].
+ *   MLA : Hkv == 1; key stream = RoPE key (kd), value stream = content
+ *         latent (vd); append inputs k = RoPE [B][n][kd], v = content
+ *         [B][n][vd]; q = fp16 [B][Hq][vd + kd] (content part, then RoPE
+ *         part); out = fp16 [B][Hq][vd].
+ *   Query head h reads KV head floor(h / (Hq / Hkv)).
+ *
+ * Ownership: the caller owns every device buffer (cache arrays, inputs,
+ * outputs, workspace); the library never allocates device memory.  A
+ * kvq_cache handle holds the device pointers plus host-side counters (tokens
+ * held, quantized key blocks) and is the only host allocation.
+ *
+ * Errors: every argument is validated on the host before any HIP call; on
+ * error nothing is launched and the handle is unchanged.  KVQ_E_HIP reports a
+ * launch failure (hipGetLastError).  Faults while a kernel runs surface at the
+ * caller's next synchronisation.  Calls are asynchronous on the given HIP
+ * stream (hipStream_t passed as void*; NULL = the default stream).  Calls on
+ * one handle must be ordered on one stream; a handle is not thread-safe.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_E_NULL = -1,        /* a required pointer is NULL                    */
+    KVQ_E_SHAPE = -2,       /* inconsistent or unsupported dimensions        */
+    KVQ_E_ALIGN = -3,       /* a device pointer is not 16-byte aligned       */
+    KVQ_E_CAPACITY = -4,    /* tokens would exceed max_tokens / the residual */
+    KVQ_E_UNSUPPORTED = -5, /* valid request this build does not implement   */
+    KVQ_E_WORKSPACE = -6,   /* workspace smaller than required               */
+    KVQ_E_HIP = -7,         /* a HIP launch failed                           */
+    KVQ_E_STATE = -8        /* the cache holds no tokens to attend over      */
+} kvq_status;
+
+enum { KVQ_KIND_KIVI = 0, KVQ_KIND_MLA = 1 };
+enum { KVQ_AXIS_PER_CHANNEL = 0,   /* groups of `group` tokens, one channel */
+       KVQ_AXIS_PER_TOKEN = 1 };   /* groups of `group` channels, one token */
+
+/* kv_quantize_append flag: do not quantize a key block when the residual
+ * fills; the caller flushes it with kv_flush_residual. */
+#define KVQ_APPEND_NO_AUTOFLUSH 1u
+
+typedef struct kvq_stream_cfg {
+    int32_t bits;    /* 2 or 4                                     */
+    int32_t axis;    /* key stream: PER_CHANNEL, value: PER_TOKEN  */
+    int32_t dim;     /* channels of the stream                     */
+    int32_t group;   /* key: G tokens; value: Gv channels          */
+} kvq_stream_cfg;
+
+typedef struct kvq_cache_cfg {
+    int32_t kind;          /* KVQ_KIND_KIVI or KVQ_KIND_MLA            */
+    int32_t batch;         /* B                                         */
+    int32_t n_kv_heads;    /* Hkv (MLA: 1)                              */
+    int32_t reserved;      /* must be 0                                 */
+    int64_t max_tokens;    /* capacity per sequence, a multiple of G    */
+    kvq_stream_cfg key;    /* MLA: the RoPE key                         */
+    kvq_stream_cfg value;  /* MLA: the content latent                   */
+} kvq_cache_cfg;
+
+typedef struct kvq_buffer_sizes {   /* bytes of each device array */
+    uint64_t k_codes, k_scale, k_zero, k_resid, v_codes, v_scale, v_zero;
+} kvq_buffer_sizes;
+
+typedef struct kvq_cache_buffers {  /* caller-owned device arrays, 16-B aligned */
+    void *k_codes, *k_scale, *k_zero, *k_resid, *v_codes, *v_scale, *v_zero;
+} kvq_cache_buffers;
+
+typedef struct kvq_cache kvq_cache;   /* opaque host handle */
+
+/* Sizes of the seven device arrays for `cfg` (the layouts above).
+ * Validates cfg: kind; batch, n_kv_heads >= 1 (MLA: n_kv_heads == 1);
+ * bits in {2,4}; key axis PER_CHANNEL with G a multiple of 32/bits and
+ * 16 <= G <= 128 and G*bits/32 in {1,2,4,8}; value axis PER_TOKEN with
+ * Gv == 32; dims multiples of 32 and <= 512; KIVI: kd == vd; max_tokens >= G
+ * and a multiple of G.  Returns KVQ_E_NULL / KVQ_E_SHAPE / KVQ_E_UNSUPPORTED. */
+kvq_status kv_cache_buffer_bytes(const kvq_cache_cfg* cfg, kvq_buffer_sizes* out);
+
+/* Create a handle over caller-owned device arrays (sizes from
+ * kv_cache_buffer_bytes, 16-byte aligned, contents need not be initialised).
+ * The cache starts empty.  Allocates the host handle only. */
+kvq_status kv_cache_init(const kvq_cache_cfg* cfg, const kvq_cache_buffers* bufs,
+                         kvq_cache** out);
+
+/* Free the host handle (device arrays stay the caller's).  NULL is a no-op. */
+void kv_cache_destroy(kvq_cache* cache);
+
+/* Forget every token (host counters only; device contents are left). */
+kvq_status kv_cache_reset(kvq_cache* cache);
+
+/* Tokens held, and how many of them are residual (fp16) keys. */
+kvq_status kv_cache_state(const kvq_cache* cache, int64_t* n_tokens, int32_t* n_resid);
+
+/* Append n_tokens tokens per sequence ("İddia ve Gerçeklik: KIVI": values
+ * quantized per token at once; keys join the residual and every block of G
+ * keys that fills is quantized per channel).  k_fp16 / v_fp16 are device
+ * arrays in the append layouts above; they are only read.  Without
+ * KVQ_APPEND_NO_AUTOFLUSH the residual never holds a full block afterwards;
+ * with it, R + n_tokens must be <= G (else KVQ_E_CAPACITY) and a residual
+ * that reaches G waits for kv_flush_residual.  n_tokens == 0 is a no-op.
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE (n_tokens < 0), KVQ_E_ALIGN,
+ * KVQ_E_CAPACITY (T + n_tokens > max_tokens), KVQ_E_HIP. */
+kvq_status kv_quantize_append(kvq_cache* cache, const void* k_fp16, const void* v_fp16,
+                              int64_t n_tokens, uint32_t flags, void* hip_stream);
+
+/* Quantize the residual as the next key block if it holds exactly G keys;
+ * otherwise do nothing (a partial block is never quantized, which is why the
+ * residual exists).  *n_blocks_flushed (may be NULL) receives 1 or 0. */
+kvq_status kv_flush_residual(kvq_cache* cache, void* hip_stream, int32_t* n_blocks_flushed);
+
+/* Split-K: the context is cut into n_splits contiguous token ranges handled
+ * by independent workgroups and merged by a second pass.  0 = automatic. */
+#define KVQ_MAX_SPLITS 256
+
+/* Workspace bytes kv_decode_attention needs for n_q_heads and n_splits
+ * (0 = automatic; the automatic figure covers every cache length up to
+ * max_tokens).  Errors: KVQ_E_NULL, KVQ_E_SHAPE. */
+kvq_status kv_decode_workspace_bytes(const kvq_cache* cache, int32_t n_q_heads,
+                                     int32_t n_splits, uint64_t* bytes);
+
+/* Decode attention of one query per (sequence, query head) over every token
+ * in the cache: logits sigma * q . khat_t over the quantized keys and the
+ * fp16 residual keys (MLA: sigma * (q_content . chat_t + q_rope . khat_t)),
+ * softmax, weighted sum of the dequantized values (MLA: of chat_t);
+ * fp32 accumulation, fp16 output.  The 2-bit codes are unpacked and
+ * dequantized inside the QK^T / softmax / PV loop ("İddia ve Gerçeklik:
+ * KIVI"; "QuantMLA Mimarisi ve Temel Bileşenleri").  q_fp16, out_fp16 and
+ * workspace are caller-owned device arrays, 16-byte aligned.
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE (n_q_heads not a positive multiple of
+ * Hkv, n_splits outside [0, KVQ_MAX_SPLITS]), KVQ_E_ALIGN, KVQ_E_STATE (no
+ * tokens), KVQ_E_WORKSPACE, KVQ_E_HIP. */
+kvq_status kv_decode_attention(const kvq_cache* cache, const void* q_fp16, int32_t n_q_heads,
+                               float softmax_scale, int32_t n_splits, void* out_fp16,
+                               void* workspace, uint64_t workspace_bytes, void* hip_stream);
+
+/* Profiling hook: when both are non-NULL, later kv_decode_attention calls
+ * record hipEvent_t ev_before / ev_after on their stream right before and
+ * after the split-K pass-1 kernel.  NULL, NULL switches it off.  Process-wide. */
+kvq_status kv_set_timing_events(void* ev_before, void* ev_after);
+
+/* Name of the decode kernel variant kv_decode_attention would launch. */
+const char* kv_decode_variant(const kvq_cache* cache, int32_t n_q_heads);
+
+/* Static description of a status code. */
+const char* kvq_status_str(kvq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -37,7 +37,7 @@ _lib = None
 
 class OrcCache(C.Structure):
     _fields_ = [("B", C.c_int64), ("H", C.c_int64), ("T", C.c_int64),
-                ("nblk_cap", C.c_int64), ("tok_cap", C.c_int64),
+                ("kq_blocks", C.c_int64), ("nblk_cap", C.c_int64), ("tok_cap", C.c_int64),
                 ("kd", C.c_int32), ("kG", C.c_int32), ("kbits", C.c_int32),
                 ("vd", C.c_int32), ("vG", C.c_int32), ("vbits", C.c_int32),
                 ("k_codes", C.c_void_p), ("k_scale", C.c_void_p),
@@ -168,13 +168,13 @@ def quantize_values(v_bits, Gv: int, bits: int, tok_cap: int | None = None):
 class Cache:
     """A quantized cache held in numpy arrays, in the oracle's layouts."""
 
-    def __init__(self, T, kG, kbits, vG, vbits, keys: dict, values: dict):
+    def __init__(self, T, kG, kbits, vG, vbits, keys: dict, values: dict, kq_blocks: int = -1):
         self.k = keys
         self.v = values
         B, H, nblk_cap, kd, _ = keys["k_codes"].shape
         _, _, tok_cap, _ = values["v_codes"].shape
         vd = values["v_scale"].shape[3] * vG
-        self.s = OrcCache(B, H, T, nblk_cap, tok_cap, kd, kG, kbits, vd, vG, vbits,
+        self.s = OrcCache(B, H, T, kq_blocks, nblk_cap, tok_cap, kd, kG, kbits, vd, vG, vbits,
                           _ptr(keys["k_codes"]).value, _ptr(keys["k_scale"]).value,
                           _ptr(keys["k_zero"]).value, _ptr(keys["k_resid"]).value,
                           _ptr(values["v_codes"]).value, _ptr(values["v_scale"]).value,
@@ -185,12 +185,25 @@ class Cache:
         return self.s.B, self.s.H, self.s.T, self.s.kd, self.s.vd
 
 
-def build_cache(k_bits, v_bits, kG, kbits, vG, vbits, nblk_cap=None, tok_cap=None) -> Cache:
+def build_cache(k_bits, v_bits, kG, kbits, vG, vbits, nblk_cap=None, tok_cap=None,
+                kq_blocks: int | None = None) -> Cache:
+    """Oracle cache of T tokens.  kq_blocks (default floor(T/kG)) quantized
+    key blocks; the remaining T - kq_blocks*kG (<= kG) keys stay fp16."""
     T = k_bits.shape[2]
     assert v_bits.shape[2] == T
-    keys = quantize_keys(k_bits, kG, kbits, nblk_cap)
+    if kq_blocks is None:
+        keys = quantize_keys(k_bits, kG, kbits, nblk_cap)
+        kq = -1
+    else:
+        Tq = kq_blocks * kG
+        assert 0 <= T - Tq <= kG
+        keys = quantize_keys(np.ascontiguousarray(k_bits[:, :, :Tq]), kG, kbits,
+                             nblk_cap if nblk_cap is not None else max(1, kq_blocks))
+        keys["k_resid"][:, :, :T - Tq] = k_bits[:, :, Tq:]
+        keys["R"] = T - Tq
+        kq = kq_blocks
     values = quantize_values(v_bits, vG, vbits, tok_cap)
-    return Cache(T, kG, kbits, vG, vbits, keys, values)
+    return Cache(T, kG, kbits, vG, vbits, keys, values, kq)
 
 
 def dequant_keys(cache: Cache, b: int, h: int) -> np.ndarray:

@@ -194,9 +194,13 @@ int orc_quantize_values(const uint16_t* v, int64_t B, int64_t H, int64_t T,
 
 /* code * scale + zero evaluated in binary64: exact, since the product of a
  * <=4-bit integer and an fp16 value has at most 15 significant bits. */
+static int64_t quantized_keys(const orc_cache* c) {
+    return (c->kq_blocks < 0 ? c->T / c->kG : c->kq_blocks) * c->kG;
+}
+
 static double key_at(const orc_cache* c, int64_t bh, int64_t t, int64_t ch) {
     const int64_t G = c->kG, per = 32 / c->kbits, W = G / per;
-    const int64_t Tq = (c->T / G) * G;
+    const int64_t Tq = quantized_keys(c);
     if (t >= Tq)
         return (double)orc_half_to_float(c->k_resid[(bh * G + (t - Tq)) * c->kd + ch]);
     const int64_t blk = t / G, i = t % G;
@@ -218,7 +222,9 @@ static double value_at(const orc_cache* c, int64_t bh, int64_t t, int64_t ch) {
 
 static int cache_ok(const orc_cache* c) {
     if (!c || c->B <= 0 || c->H <= 0 || c->T < 0) return 0;
-    if (c->T > c->tok_cap || c->T / c->kG > c->nblk_cap) return 0;
+    if (c->T > c->tok_cap || quantized_keys(c) / c->kG > c->nblk_cap) return 0;
+    if (c->kq_blocks >= 0 &&
+        (c->kq_blocks * c->kG > c->T || c->T - c->kq_blocks * c->kG > c->kG)) return 0;
     if (!c->k_codes || !c->k_scale || !c->k_zero || !c->k_resid) return 0;
     if (!c->v_codes || !c->v_scale || !c->v_zero) return 0;
     return 1;

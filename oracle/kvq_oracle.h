@@ -77,6 +77,9 @@ int orc_quantize_values(const uint16_t* v, int64_t B, int64_t H, int64_t T,
 /* A quantized cache as the oracle reads it (same layouts as above). */
 typedef struct orc_cache {
     int64_t B, H, T;          /* batch, kv heads, tokens held */
+    int64_t kq_blocks;        /* quantized key blocks; keys from kq_blocks*kG
+                                 on are fp16 residual keys (at most kG of
+                                 them); -1 means floor(T / kG)                */
     int64_t nblk_cap, tok_cap;/* capacities of the block and token axes   */
     int32_t kd, kG, kbits;    /* key stream: dim, token group, bits       */
     int32_t vd, vG, vbits;    /* value stream: dim, channel group, bits   */

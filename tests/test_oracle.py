@@ -388,3 +388,19 @@ def test_synth_prefix_property():
     assert synth.outlier_channels(configs.WORKLOADS[2]).size == 11
     assert synth.outlier_channels(configs.WORKLOADS[1]).size == 41
     assert synth.outlier_channels(configs.WORKLOADS[4]).size == 1
+
+
+def test_attention_unflushed_full_residual(orc):
+    """A residual that reached G keys without a flush keeps them in fp16."""
+    w = _tiny_kivi(96, Hq=4, Hkv=2)          # 3 blocks of 32; the last stays fp16
+    k, v = synth.keys(w), synth.values(w)
+    cache = orc.build_cache(k, v, w.kG, w.kbits, w.vG, w.vbits, kq_blocks=2)
+    q = synth.query(w)
+    got = orc.attention_kivi(cache, q, w.sigma)
+    flushed = orc.build_cache(k[:, :, :64], v[:, :, :64], w.kG, w.kbits, w.vG, w.vbits)
+    for hq in range(4):
+        kvh = hq // 2
+        kh = np.concatenate([np_dequant_keys(flushed, 0, kvh), f16(k[0, kvh, 64:])], 0)
+        vh = np_dequant_values(cache, 0, kvh)
+        s = float(np.float32(w.sigma)) * (kh @ f16(q[0, hq]))
+        assert np.abs(got[0, hq] - np_softmax_attend(s, vh)).max() <= 1e-12
