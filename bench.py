@@ -1,0 +1,224 @@
+"""Benchmark: 2-bit decode attention over a KIVI-style cache on one MI355X.
+
+One step = one decode token for every sequence of the workload: append the
+new token (per-token value quantize, key into the residual, per-channel key
+quantize of the block when it fills) followed by split-K decode attention over
+the whole cache and the merge pass.  Inputs are seeded synthetic fp16 tensors
+already resident in HBM.  Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+DEFAULT_WORKLOAD = "mistral_7b_gqa_t32805"
+
+
+class HipEvents:
+    """hipEvent_t pairs through libamdhip64 (the library records them on its
+    launch stream around the pass-1 kernel)."""
+
+    def __init__(self):
+        self.hip = C.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self):
+        e = C.c_void_p()
+        assert self.hip.hipEventCreate(C.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = C.c_float()
+        assert self.hip.hipEventElapsedTime(C.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-pairs", type=int, default=32)
+    ap.add_argument("--splits", type=int, default=0)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, k, v, q, cap, n_pairs):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    decode attention of n_pairs (batch, query head) pairs over the full cache
+    of their KV heads, threaded over the pairs."""
+    import oracle
+
+    group = w.n_q_heads // w.n_kv_heads
+    slices = []
+    p = 0
+    while len(slices) * group < n_pairs and p < w.batch * w.n_kv_heads:
+        slices.append(divmod(p * 7 % (w.batch * w.n_kv_heads), w.n_kv_heads))
+        p += 1
+    caches, qs = [], []
+    for b, h in slices:
+        caches.append(oracle.build_cache(k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], w.kG, w.kbits,
+                                         w.vG, w.vbits, nblk_cap=cap // w.kG, tok_cap=cap))
+        qs.append(np.ascontiguousarray(q[b:b + 1, h * group:(h + 1) * group]))
+    # one oracle call per slice would serialise on `group` threads; run the
+    # slices concurrently so that every host core has a pair
+    import concurrent.futures as cf
+    fn = oracle.attention_kivi if w.kind == "kivi" else oracle.attention_mla
+    cores = min(os.cpu_count() or 1, len(slices) * group)
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=len(slices)) as ex:
+        list(ex.map(lambda i: fn(caches[i], qs[i], w.sigma, nthreads=group), range(len(slices))))
+    dt = time.perf_counter() - t0
+    n_sl = len(slices)
+    sample_bytes = w.with_T(w.T).cache_bytes() // (w.batch * w.n_kv_heads) * n_sl \
+        + n_sl * group * (w.qd + w.vd) * 2
+    return {"value": sample_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_sl} (batch, kv-head) slices x {group} query heads = {n_sl * group} "
+                      f"decode pairs over T={w.T} (of {w.batch * w.n_q_heads}); {dt:.2f} s wall",
+            "tokens_per_s_attended": n_sl * w.T / dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from decode_attention_asym_amd import configs, kvq, synth
+
+    w = configs.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n_new = args.warmup + args.steps
+    Tall = w.T + n_new
+    cap = w.capacity(n_new + 1)
+    t0 = time.time()
+    k = synth.keys(w, Tall)
+    v = synth.values(w, Tall)
+    q = synth.query(w)
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def dev16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.float16).to(dev)
+
+    kd = dev16(k[:, :, :w.T])
+    vd = dev16(v[:, :, :w.T])
+    # one contiguous [B][Hkv][1][d] tensor per decode step
+    knew = dev16(np.ascontiguousarray(k[:, :, w.T:].transpose(2, 0, 1, 3))[:, :, :, None, :])
+    vnew = dev16(np.ascontiguousarray(v[:, :, w.T:].transpose(2, 0, 1, 3))[:, :, :, None, :])
+    qd = dev16(q)
+    dc = kvq.DeviceCache(kvq.cfg_for(w, cap), device=dev)
+    stream = torch.cuda.current_stream()
+
+    # ---- bulk prefill quantize (the context), timed over a few repetitions
+    reps = 3
+    qt = []
+    for _ in range(reps):
+        kvq.kv_cache_reset(dc.handle)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dc.append(kd, vd)
+        b.record(stream)
+        torch.cuda.synchronize()
+        qt.append(a.elapsed_time(b))
+    q_ms = float(np.median(qt))
+    q_bytes = 2 * w.batch * w.n_kv_heads * w.T * (w.kd + w.vd) + w.cache_bytes()
+    assert dc.state() == (w.T, w.R)
+
+    out = torch.empty((w.batch, w.n_q_heads, w.vd), dtype=torch.float16, device=dev)
+    ws = dc.workspace(w.n_q_heads, args.splits)
+    hip = HipEvents()
+    evs = [(hip.create(), hip.create()) for _ in range(args.steps)]
+
+    def step(i, timed):
+        if timed:
+            kvq.kv_set_timing_events(*evs[i - args.warmup])
+        dc.append(knew[i], vnew[i])
+        kvq.kv_decode_attention(dc.handle, qd.data_ptr(), w.n_q_heads, w.sigma, args.splits,
+                                out.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.warmup, n_new):
+        step(i, True)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    kvq.kv_set_timing_events(None, None)
+    total_ms = start.elapsed_time(stop)
+    pass1_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+
+    Ts = [w.T + i + 1 for i in range(args.warmup, n_new)]
+    alg_bytes = sum(w.decode_bytes(T) for T in Ts)
+    value = alg_bytes / (total_ms * 1e-3) / 1e9
+    p1_avg = float(np.mean(pass1_ms))
+    p1_bytes = float(np.mean([w.cache_bytes(T) + w.batch * w.n_q_heads * w.qd * 2 for T in Ts]))
+    achieved = p1_bytes / (p1_avg * 1e-3) / 1e9
+    ms_step = total_ms / args.steps
+
+    res = {
+        "metric": "2-bit decode attention KV bytes/s (tokens/s, % HBM peak; quantize GB/s)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.kd, "context": w.T, "G": w.kG,
+                   "bits": w.kbits, "value_group": w.vG, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None,
+                     "kernel": "decode pass-1 (" + dc.variant(w.n_q_heads) + ")",
+                     "avg_us": round(p1_avg * 1e3, 2), "alg_bytes_per_launch": int(p1_bytes)},
+        "extra": {
+            "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
+            "attended_kv_tokens_per_s": round(w.batch * float(np.mean(Ts)) / (ms_step * 1e-3), 1),
+            "hbm_frac_whole_step": round(value / HBM_PEAK_GBPS, 4),
+            "quantize_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 2),
+            "quantize_ms": round(q_ms, 4),
+            "quantize_bytes": int(q_bytes),
+            "cache_bytes": int(w.cache_bytes()),
+            "fp16_kv_equiv_bytes": int(w.fp16_kv_bytes()),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, k[:, :, :w.T], v[:, :, :w.T], q, cap, args.cpu_pairs)
+    print(json.dumps(res), flush=True)
+    dc.close()
+
+
+if __name__ == "__main__":
+    main()

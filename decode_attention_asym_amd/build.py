@@ -9,7 +9,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kvq_api.cpp", "kvq_plan.cpp", "kvq_quant.hip", "kvq_decode_generic.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_plan.cpp", "kvq_quant.hip", "kvq_decode_generic.hip",
+           "kvq_decode_gqa.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -71,15 +71,6 @@ void sizes_of(const kvq_cache_cfg& c, kvq_buffer_sizes* s) {
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E_HIP; }
 
-int resolve_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64_t nblk, Variant v) {
-    const int64_t R = T - nblk * c.cfg.key.group;
-    const int64_t U = nblk + (R > 0 ? 1 : 0);
-    int64_t S = n_splits > 0 ? n_splits : auto_splits(c, Hq, T, v);
-    if (S > U) S = U;
-    if (S < 1) S = 1;
-    return int(S);
-}
-
 }  // namespace
 
 extern "C" {
@@ -206,12 +197,7 @@ kvq_status kv_decode_workspace_bytes(const kvq_cache* c, int32_t Hq, int32_t n_s
     if (n_splits < 0 || n_splits > KVQ_MAX_SPLITS) return KVQ_E_SHAPE;
     const Geom g = geom_of(c->cfg);
     const Variant v = pick_variant(*c, Hq);
-    int S = n_splits;
-    if (S == 0) {
-        // automatic split counts grow with the cache; cover the full capacity
-        S = auto_splits(*c, Hq, g.cap, v);
-        if (S < 1) S = 1;
-    }
+    const int S = max_slots(*c, Hq, n_splits, v);   // covers every length up to capacity
     *bytes = uint64_t(g.B) * Hq * S * (g.vd + 2) * 4;
     return KVQ_OK;
 }
@@ -236,7 +222,10 @@ kvq_status kv_decode_attention(const kvq_cache* c, const void* q, int32_t Hq, fl
     a.nblk = c->nblk;
     a.R = int(c->T - c->nblk * a.g.kG);
     a.U = int(a.nblk + (a.R > 0 ? 1 : 0));
-    a.S = resolve_splits(*c, Hq, n_splits, a.T, a.nblk, v);
+    const SplitPlan sp = plan_splits(*c, Hq, n_splits, a.T, a.nblk, v);
+    a.S = sp.S;
+    a.S_main = sp.S_main;
+    a.ntiles = sp.ntiles;
     const uint64_t need = uint64_t(a.g.B) * Hq * a.S * (a.g.vd + 2) * 4;
     if (ws_bytes < need) return KVQ_E_WORKSPACE;
     a.ws_acc = static_cast<float*>(ws);
@@ -247,6 +236,7 @@ kvq_status kv_decode_attention(const kvq_cache* c, const void* q, int32_t Hq, fl
     if (g_ev_before) e = hipEventRecord(g_ev_before, st);
     if (e != hipSuccess) return KVQ_E_HIP;
     switch (v) {
+        case V_GQA: e = launch_decode_gqa(a, st); break;
         default: e = launch_decode_generic(a, st); break;
     }
     if (e != hipSuccess) return KVQ_E_HIP;

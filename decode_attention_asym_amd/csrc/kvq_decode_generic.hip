@@ -27,7 +27,7 @@ struct GenParams {
     int Hq, Hkv, S, U;
     int64_t T, nblk, cap, nblk_cap;
     int kd, kG, kbits, kW, vd, vbits, vWT, vNG;
-    float sigma;
+    float sigma2;   // softmax scale * log2(e): logits and maxima in log2 units
 };
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
@@ -89,15 +89,15 @@ __global__ __launch_bounds__(256) void k_decode_generic(GenParams p) {
             } else {
                 for (int c = 0; c < p.kd; ++c) dot = fmaf(qs[c], key_hat(p, bh, t, c), dot);
             }
-            sc = p.sigma * dot;
+            sc = p.sigma2 * dot;
         }
         float wm = wave_max(sc);
         if (lane == 0) red[0][wv] = wm;
         __syncthreads();
         const float cm = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
         const float mnew = fmaxf(m, cm);
-        const float pt = t < t1 ? expf(sc - mnew) : 0.0f;
-        const float alpha = expf(m - mnew);
+        const float pt = t < t1 ? exp2f(sc - mnew) : 0.0f;
+        const float alpha = exp2f(m - mnew);
         const float ws = wave_sum(pt);
         if (lane == 0) red[1][wv] = ws;
         ps[tid] = pt;
@@ -123,7 +123,8 @@ __global__ __launch_bounds__(256) void k_decode_generic(GenParams p) {
     }
 }
 
-// Pass 2: m = max_s m_s, L = sum_s l_s e^{m_s - m}, o = sum_s acc_s e^{m_s - m} / L.
+// Pass 2 (maxima in log2 units): m = max_s m_s, L = sum_s l_s 2^{m_s - m},
+// o = sum_s acc_s 2^{m_s - m} / L.
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ ws_acc,
                                                const float* __restrict__ ws_ml, int S, int vd,
                                                uint16_t* __restrict__ out) {
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ ws_acc,
     if (tid == 0) tot[0] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
     const float M = tot[0];
-    const float w = tid < S ? expf(mi - M) : 0.0f;
+    const float w = tid < S ? exp2f(mi - M) : 0.0f;
     if (tid < S) wsh[tid] = w;
     const float lsum = wave_sum(tid < S ? ml[tid * 2 + 1] * w : 0.0f);
     __syncthreads();
@@ -188,7 +189,7 @@ hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
     p.vbits = a.g.vbits;
     p.vWT = a.g.vWT;
     p.vNG = a.g.vNG;
-    p.sigma = a.sigma;
+    p.sigma2 = a.sigma * 1.4426950408889634f;
     const dim3 grid(a.S, a.Hq, a.g.B);
     if (c.cfg.kind == KVQ_KIND_MLA)
         hipLaunchKernelGGL(k_decode_generic<true>, grid, dim3(256), 0, st, p);

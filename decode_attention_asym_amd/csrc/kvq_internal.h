@@ -53,7 +53,9 @@ struct DecodeArgs {
     const kvq_cache* c;
     Geom g;
     const void* q;
-    int Hq, S;          // query heads, splits
+    int Hq, S;          // query heads, partial slots (main splits + tail slot)
+    int S_main;         // splits over whole tiles (variants with a tail slot)
+    int ntiles;         // whole 64-token tiles (MFMA variants)
     float sigma;
     void* out;
     float* ws_acc;      // [B][Hq][S][vd]
@@ -65,9 +67,19 @@ struct DecodeArgs {
 
 Variant pick_variant(const kvq_cache& c, int Hq);
 const char* variant_name(Variant v);
-int auto_splits(const kvq_cache& c, int Hq, int64_t T, Variant v);
 
+// Split plan for a cache of T tokens with nblk quantized key blocks.
+// n_splits == 0 picks automatically.  Returns the partial-slot count.
+struct SplitPlan {
+    int S_main, S, ntiles;
+};
+SplitPlan plan_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64_t nblk, Variant v);
+// Upper bound of SplitPlan::S over every T <= capacity.
+int max_slots(const kvq_cache& c, int Hq, int n_splits, Variant v);
+
+bool gqa_supported(const kvq_cache& c, int Hq);
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace kvq

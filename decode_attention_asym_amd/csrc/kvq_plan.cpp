@@ -1,11 +1,10 @@
-// kvq_plan.cpp -- which decode kernel runs, and with how many splits.
+// kvq_plan.cpp -- which decode kernel runs, and how the context is split.
 #include "kvq_internal.h"
 
 namespace kvq {
 
 Variant pick_variant(const kvq_cache& c, int Hq) {
-    (void)c;
-    (void)Hq;
+    if (gqa_supported(c, Hq)) return V_GQA;
     return V_GENERIC;
 }
 
@@ -19,16 +18,46 @@ const char* variant_name(Variant v) {
     return "unknown";
 }
 
-// Automatic split count.  It must not decrease as T grows (the workspace
-// query sizes for the full capacity); the caller clamps it to the number of
-// work units.
-int auto_splits(const kvq_cache& c, int Hq, int64_t T, Variant v) {
-    (void)T;
-    (void)v;
-    const int64_t wgs = int64_t(c.cfg.batch) * Hq;
-    int64_t S = (2048 + wgs - 1) / wgs;
-    if (S > KVQ_MAX_SPLITS) S = KVQ_MAX_SPLITS;
-    return int(S < 1 ? 1 : S);
+namespace {
+
+int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Automatic split count: enough workgroups to fill 256 CUs several times
+// over.  It does not depend on T, so the slot bound below covers every T.
+int64_t auto_main(const kvq_cache& c, int Hq, Variant v) {
+    const int64_t units = v == V_GQA ? int64_t(c.cfg.batch) * c.cfg.n_kv_heads
+                                     : int64_t(c.cfg.batch) * Hq;
+    const int64_t target = v == V_GQA ? 3072 : 2048;
+    return clamp64((target + units - 1) / units, 1, KVQ_MAX_SPLITS);
+}
+
+}  // namespace
+
+SplitPlan plan_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64_t nblk, Variant v) {
+    SplitPlan sp;
+    const int64_t G = c.cfg.key.group;
+    const int64_t want = n_splits > 0 ? n_splits : auto_main(c, Hq, v);
+    if (v == V_GQA) {
+        // whole 64-token tiles of quantized keys, then a tail slot for the rest
+        const int64_t ntiles = nblk * G / 64;
+        sp.ntiles = int(ntiles);
+        // the merge pass reads at most KVQ_MAX_SPLITS slots, tail slot included
+        sp.S_main = int(clamp64(clamp64(want, 0, KVQ_MAX_SPLITS - 1), 0, ntiles));
+        sp.S = sp.S_main + (T > ntiles * 64 ? 1 : 0);
+        return sp;
+    }
+    const int64_t R = T - nblk * G;
+    const int64_t U = nblk + (R > 0 ? 1 : 0);
+    sp.ntiles = 0;
+    sp.S_main = int(clamp64(want, 1, U));
+    sp.S = sp.S_main;
+    return sp;
+}
+
+int max_slots(const kvq_cache& c, int Hq, int n_splits, Variant v) {
+    const int64_t want = n_splits > 0 ? n_splits : auto_main(c, Hq, v);
+    if (v == V_GQA) return int(clamp64(want, 1, KVQ_MAX_SPLITS - 1) + 1);
+    return int(want);
 }
 
 }  // namespace kvq
