@@ -59,7 +59,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=32)
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
+
+
+def copy_probe():
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) of the decode kernel."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n, "launches": 5}), flush=True)
 
 
 def cpu_baseline(w, k, v, q, cap, n_pairs):
@@ -107,6 +123,9 @@ def main():
 
     from decode_attention_asym_amd import configs, kvq, synth
 
+    if args.copy_probe:
+        copy_probe()
+        return
     w = configs.BY_NAME[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

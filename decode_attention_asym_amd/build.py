@@ -19,6 +19,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-gpu-flush-denormals-to-zero",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # MFMA accumulators in VGPRs (no AGPR copies around VALU work on them)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -45,7 +45,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int HG = 4;       // query heads per KV head
 constexpr int D = 128;      // head dim
 constexpr int KSTR = 136;   // dwords per row of the key-code tile in LDS
-constexpr int VSTR = 72;    // dwords per row of the value-code tile in LDS
+constexpr int VSTR = 76;    // dwords per row of the value-code tile in LDS
+constexpr int QSTR = 68;    // dwords per q' row (128 fp16 + pad)
+constexpr int ASTR = 36;    // dwords per p' row (64 fp16 + pad)
 constexpr int PSTR = 68;    // floats per row of the weight tile in LDS
 constexpr float TAU = 8.0f; // lazy-rescale threshold (log2 units)
 
@@ -63,13 +65,13 @@ struct GqaParams {
 
 struct Tile {
     uint4 k0, k1, v0, v1;     // 2 KB of key codes and 2 KB of value codes, 32 B per lane
-    uint4 ksc[2], kze[2];     // key scale / zero of 8 channels, per block of the tile
-    uint4 vsc[2], vze[2];     // value scale / zero of 4 tokens x 4 groups
+    uint4 ks;                 // key scale (lanes 0..31) / zero (lanes 32..63) of the tile's blocks
+    uint4 vs;                 // value scale (lanes 0..31) / zero (lanes 32..63) of the tile's tokens
 };
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
-__device__ __forceinline__ float lo_h(uint32_t w) { return h2f(uint16_t(w & 0xffffu)); }
-__device__ __forceinline__ float hi_h(uint32_t w) { return h2f(uint16_t(w >> 16)); }
+__device__ __forceinline__ float lo_h(uint32_t w) { return float(__builtin_bit_cast(f16x2, w)[0]); }
+__device__ __forceinline__ float hi_h(uint32_t w) { return float(__builtin_bit_cast(f16x2, w)[1]); }
 
 __device__ __forceinline__ f16x8 as_f16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     u32x4 v = {a, b, c, d};
@@ -84,6 +86,16 @@ __device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
     hi = pk_rtz(x0, x1);
     lo = pk_rtz(x0 - lo_h(hi), x1 - hi_h(hi));
+}
+
+// hi/lo split of the products a0*b0, a1*b1 (a fp32, b an fp16 half): the
+// remainders are single fused operations a*b - hi
+__device__ __forceinline__ void split_prod2(float a0, float b0, float a1, float b1, uint32_t& hi,
+                                            uint32_t& lo) {
+    // fma(a, b, +0) is one v_fma_mix with the fp16 operand read in place
+    // (it cannot become a plain multiply: they differ for a*b == -0)
+    hi = pk_rtz(fmaf(a0, b0, 0.0f), fmaf(a1, b1, 0.0f));
+    lo = pk_rtz(fmaf(a0, b0, -lo_h(hi)), fmaf(a1, b1, -hi_h(hi)));
 }
 
 __device__ __forceinline__ float xor_max16(float x) {
@@ -103,28 +115,27 @@ __device__ __forceinline__ float pick4(const float* v, int i) {
     return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
 }
 
+// All global loads of one 64-token tile, 16-byte aligned, no lane reads
+// what another lane reads: codes 2 x 2 KB, key side 512 B (G = 64) or 1 KB
+// (G = 32), value side 1 KB.
 template <int G>
-__device__ __forceinline__ void load_tile(const GqaParams& p, int64_t bh, int64_t tt, int lane,
-                                          Tile& r) {
+__device__ __forceinline__ void load_tile(const GqaParams& p, int64_t bh, int64_t tt, int lane, Tile& r) {
     constexpr int NBT = 64 / G, W = G / 16;
-    const int chunk = lane & 15;
     const uint4* kb = reinterpret_cast<const uint4*>(p.kc + (bh * p.nblk_cap + tt * NBT) * D * W);
     r.k0 = kb[lane];
     r.k1 = kb[lane + 64];
     const uint4* vb = reinterpret_cast<const uint4*>(p.vc + (bh * p.cap + tt * 64) * 8);
     r.v0 = vb[lane];
     r.v1 = vb[lane + 64];
-#pragma unroll
-    for (int be = 0; be < NBT; ++be) {
-        const int64_t side = (bh * p.nblk_cap + tt * NBT + be) * D + 8 * chunk;
-        r.ksc[be] = *reinterpret_cast<const uint4*>(p.ks + side);
-        r.kze[be] = *reinterpret_cast<const uint4*>(p.kz + side);
+    const uint16_t* kside = (lane < 32 ? p.ks : p.kz) + (bh * p.nblk_cap + tt * NBT) * D;
+    if (G == 64) {
+        const uint2 v = reinterpret_cast<const uint2*>(kside)[lane & 31];
+        r.ks = make_uint4(v.x, v.y, 0u, 0u);
+    } else {
+        r.ks = reinterpret_cast<const uint4*>(kside)[lane & 31];
     }
-    const int64_t vside = (bh * p.cap + tt * 64 + 4 * chunk) * 4;
-    r.vsc[0] = reinterpret_cast<const uint4*>(p.vs + vside)[0];
-    r.vsc[1] = reinterpret_cast<const uint4*>(p.vs + vside)[1];
-    r.vze[0] = reinterpret_cast<const uint4*>(p.vz + vside)[0];
-    r.vze[1] = reinterpret_cast<const uint4*>(p.vz + vside)[1];
+    const uint16_t* vside = (lane < 32 ? p.vs : p.vz) + (bh * p.cap + tt * 64) * 4;
+    r.vs = reinterpret_cast<const uint4*>(vside)[lane & 31];
 }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
@@ -150,12 +161,17 @@ __device__ __forceinline__ float value_hat(const GqaParams& p, int64_t bh, int64
 
 // Trailing tokens [ntiles*64, T): partial key block and fp16 residual keys,
 // one token per lane for the logits, two channels per lane for the values.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 __device__ void tail_split(const GqaParams& p, int b, int kvh, int s, float* qf, float* pl) {
     const int lane = threadIdx.x;
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int hq0 = kvh * HG;
     for (int i = lane; i < HG * D; i += 64) qf[i] = h2f(p.q[(int64_t(b) * p.Hq + hq0) * D + i]);
-    __syncthreads();
+    wave_sync();
     const int64_t t0 = int64_t(p.ntiles) * 64;
     const int n_tail = int(p.T - t0);
     const int64_t t = t0 + lane;
@@ -181,7 +197,7 @@ __device__ void tail_split(const GqaParams& p, int b, int kvh, int s, float* qf,
         l[h] = sum;
         pl[h * PSTR + lane] = pv;
     }
-    __syncthreads();
+    wave_sync();
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         const int c = lane + 64 * half;
@@ -202,299 +218,465 @@ __device__ void tail_split(const GqaParams& p, int b, int kvh, int s, float* qf,
     }
 }
 
+// Row-of-16 reductions with DPP (quad xor 1, quad xor 2, half-row mirror,
+// row mirror): afterwards every lane of the 16-lane row holds the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp<0xb1>(x));
+    x = fmaxf(x, dpp<0x4e>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    return fmaxf(x, dpp<0x140>(x));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp<0xb1>(x);
+    x += dpp<0x4e>(x);
+    x += dpp<0x141>(x);
+    return x + dpp<0x140>(x);
+}
+__device__ __forceinline__ float sel4(int i, float a, float b, float c, float d) {
+    return (i & 2) ? ((i & 1) ? d : c) : ((i & 1) ? b : a);
+}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float readlane_f(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// ---------------------------------------------------------------------------
+// Two specialised waves per workgroup, software-pipelined by one tile:
+//   wave 0 (keys)   tile i: stage key codes, q' = q * s_k, S = q' . codes on
+//                   MFMA, online softmax -> weights p(i) and the rescale
+//                   factors alpha(i) into handoff buffer i & 1;
+//   wave 1 (values) tile i-1: stage value codes, rescale its accumulators by
+//                   alpha(i-1), p' = p * s_v, O += p' . codes on MFMA.
+// One workgroup barrier per iteration hands buffer i & 1 from wave 0 to
+// wave 1; each wave prefetches its own next tile into registers right
+// after staging the current one.
+
+struct LdsK {
+    uint32_t kl[4 * KSTR];                                  // key codes [word row][channel]
+    __attribute__((aligned(16))) uint32_t qa[2 * 8 * QSTR];  // q' rows (fp16) per key block
+    __attribute__((aligned(16))) uint32_t ksl[2 * 2 * 64];   // key [scale|zero][block][128 fp16]
+    float bias[8];                                          // sigma2 * sum_c q z_k per (block, head)
+};
+
+struct LdsV {
+    uint32_t vl[8 * VSTR];                                  // value codes [word][token]
+    __attribute__((aligned(16))) uint32_t pa[2 * 16 * ASTR];  // p' rows (fp16) per pass
+    __attribute__((aligned(16))) uint32_t vsl[2 * 128];      // value [scale|zero][token][4 fp16]
+};
+
+struct Handoff {
+    __attribute__((aligned(16))) float pl[HG * PSTR];  // softmax weights [head][token]
+    float alpha[HG];                                  // rescale of earlier accumulations
+};
+
+struct Lds {
+    LdsK k;
+    LdsV v;
+    Handoff hb[2];
+    float misc[64];
+};
+
+struct KTile {
+    uint4 k0, k1;   // 2 KB of key codes, 32 B per lane
+    uint4 ks;       // key scale (lanes 0..31) / zero (lanes 32..63)
+};
+struct VTile {
+    uint4 v0, v1;   // 2 KB of value codes
+    uint4 vs;       // value scale (lanes 0..31) / zero (lanes 32..63)
+};
+
 template <int G>
-__global__ __launch_bounds__(64) void k_decode_gqa(GqaParams p) {
-    constexpr int NBT = 64 / G;   // key blocks per 64-token tile
-    __shared__ uint32_t kl[4 * KSTR];
-    __shared__ uint32_t vl[8 * VSTR];
-    __shared__ __attribute__((aligned(16))) uint32_t ab[1024];  // q' rows, later p' rows (fp16)
-    __shared__ __attribute__((aligned(16))) float pl[HG * PSTR];
-    __shared__ float misc[64];
-
-    const int lane = threadIdx.x;
-    const int n = lane & 15, kg = lane >> 4;   // MFMA operand lane roles
-    const int hh = lane >> 4, chunk = lane & 15;  // q' / p' lane roles
-    const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-    const int64_t bh = int64_t(b) * p.Hkv + kvh;
-    const int hq0 = kvh * HG;
-    if (s >= p.S_main) {
-        tail_split(p, b, kvh, s, reinterpret_cast<float*>(ab), pl);
-        return;
+__device__ __forceinline__ void load_ktile(const GqaParams& p, int64_t bh, int64_t tt, int lane, KTile& r) {
+    constexpr int NBT = 64 / G, W = G / 16;
+    const uint4* kb = reinterpret_cast<const uint4*>(p.kc + (bh * p.nblk_cap + tt * NBT) * D * W);
+    r.k0 = kb[lane];
+    r.k1 = kb[lane + 64];
+    const uint16_t* kside = (lane < 32 ? p.ks : p.kz) + (bh * p.nblk_cap + tt * NBT) * D;
+    if (G == 64) {
+        const uint2 v = reinterpret_cast<const uint2*>(kside)[lane & 31];
+        r.ks = make_uint4(v.x, v.y, 0u, 0u);
+    } else {
+        r.ks = reinterpret_cast<const uint4*>(kside)[lane & 31];
     }
-    const int t_lo = int(int64_t(s) * p.ntiles / p.S_main);
-    const int t_hi = int(int64_t(s + 1) * p.ntiles / p.S_main);
+}
 
-    float qv[8];
-    {
-        const uint4 raw = *reinterpret_cast<const uint4*>(p.q + ((int64_t(b) * p.Hq + hq0 + hh) * D + 8 * chunk));
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+__device__ __forceinline__ void load_vtile(const GqaParams& p, int64_t bh, int64_t tt, int lane, VTile& r) {
+    const uint4* vb = reinterpret_cast<const uint4*>(p.vc + (bh * p.cap + tt * 64) * 8);
+    r.v0 = vb[lane];
+    r.v1 = vb[lane + 64];
+    const uint16_t* vside = (lane < 32 ? p.vs : p.vz) + (bh * p.cap + tt * 64) * 4;
+    r.vs = reinterpret_cast<const uint4*>(vside)[lane & 31];
+}
+
+struct KState {
+    float m0, m1, m2, m3;   // running maxima per head (log2 units, wave-uniform)
+};
+
+// Key side of one tile: produces p and alpha in `hb`.
+template <int G>
+__device__ __forceinline__ void key_tile(const GqaParams& p, KTile& cur, KState& st, LdsK& L,
+                                         Handoff& hb, const float* qv, uint32_t sel, int lane,
+                                         int64_t bh, int nxt, int end) {
+    constexpr int NBT = 64 / G;
+    const int n = lane & 15, kg = lane >> 4;
+    const int hh = lane >> 4, chunk = lane & 15;
+
+    // ---- stage key codes transposed to [word row][channel], and the side values
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const uint4 kw = half ? cur.k1 : cur.k0;
+        const int i = lane + 64 * half;
+        if (G == 64) {
+            L.kl[0 * KSTR + i] = kw.x;
+            L.kl[1 * KSTR + i] = kw.y;
+            L.kl[2 * KSTR + i] = kw.z;
+            L.kl[3 * KSTR + i] = kw.w;
+        } else {
+            const int be = i >> 6, c = 2 * (i & 63);
+            *reinterpret_cast<uint2*>(L.kl + (2 * be) * KSTR + c) = make_uint2(kw.x, kw.z);
+            *reinterpret_cast<uint2*>(L.kl + (2 * be + 1) * KSTR + c) = make_uint2(kw.y, kw.w);
+        }
+    }
+    if (G == 64)
+        *reinterpret_cast<uint2*>(L.ksl + (lane >> 5) * 128 + 2 * (lane & 31)) = make_uint2(cur.ks.x, cur.ks.y);
+    else
+        *reinterpret_cast<uint4*>(L.ksl + (lane >> 5) * 128 + 4 * (lane & 31)) = cur.ks;
+    if (nxt < end) load_ktile<G>(p, bh, nxt, lane, cur);
+    wave_sync();
+
+    // ---- q' = q * s_k as fp16 hi/lo rows, sigma2 * sum_c q z_k per (block, head)
+#pragma unroll
+    for (int be = 0; be < NBT; ++be) {
+        uint32_t hi[4], lo[4];
+        float bias = 0.0f;
+        const uint4 swv = *reinterpret_cast<const uint4*>(L.ksl + be * 64 + 4 * chunk);
+        const uint4 zwv = *reinterpret_cast<const uint4*>(L.ksl + 128 + be * 64 + 4 * chunk);
+        const uint32_t sw[4] = {swv.x, swv.y, swv.z, swv.w};
+        const uint32_t zw[4] = {zwv.x, zwv.y, zwv.z, zwv.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            qv[2 * i] = lo_h(w[i]);
-            qv[2 * i + 1] = hi_h(w[i]);
+            split_prod2(qv[2 * i], lo_h(sw[i]), qv[2 * i + 1], hi_h(sw[i]), hi[i], lo[i]);
+            bias = fmaf(qv[2 * i], lo_h(zw[i]), bias);
+            bias = fmaf(qv[2 * i + 1], hi_h(zw[i]), bias);
         }
+        uint32_t* row = L.qa + (be * 8 + 2 * hh) * QSTR + 4 * chunk;
+        *reinterpret_cast<uint4*>(row) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4*>(row + QSTR) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        bias = row_sum16(bias);
+        if (chunk == 0) L.bias[be * 4 + hh] = bias * p.sigma2;
     }
-    // v_perm selector: byte (n & 3) of the low-channel word -> byte 0, of the
-    // high-channel word -> byte 2, zero bytes 1 and 3
-    const uint32_t bsel = uint32_t(n & 3);
-    const uint32_t sel = bsel | (0x0cu << 8) | ((4u + bsel) << 16) | (0x0cu << 24);
+    wave_sync();
 
-    float m_run[HG] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    float lsum = 0.0f;
-    float vb[4] = {0.f, 0.f, 0.f, 0.f};
-    f32x4 O[2][4];
+    // ---- S = q' . codes: 4 MFMA tiles of 16 tokens x 4 K-steps of 32 channels.
+    // Rows 8..15 of the A operand repeat rows 0..7.
+    f32x4 S[4];
 #pragma unroll
-    for (int P = 0; P < 2; ++P)
+    for (int u = 0; u < 4; ++u) S[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) O[P][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    Tile cur, nxt;
-    load_tile<G>(p, bh, t_lo, lane, cur);
-    for (int tt = t_lo; tt < t_hi; ++tt) {
-        if (tt + 1 < t_hi) load_tile<G>(p, bh, tt + 1, lane, nxt);
-
-        // ---- 1. stage the code tiles in LDS, transposed to [word row][channel | token]
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const uint4 kw = half ? cur.k1 : cur.k0;
-            const int i = lane + 64 * half;
-            if (G == 64) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) kl[j * KSTR + i] = word_of(kw, j);
-            } else {
-                const int be = i >> 6, c = 2 * (i & 63);
-                kl[(2 * be) * KSTR + c] = kw.x;
-                kl[(2 * be + 1) * KSTR + c] = kw.y;
-                kl[(2 * be) * KSTR + c + 1] = kw.z;
-                kl[(2 * be + 1) * KSTR + c + 1] = kw.w;
-            }
-            const uint4 vw = half ? cur.v1 : cur.v0;
-            const int tok = i >> 1, w0 = 4 * (i & 1);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vl[(w0 + e) * VSTR + tok] = word_of(vw, e);
-        }
-
-        // ---- 2. q' = q * s_k (hi/lo rows) and the zero bias per (head, block)
+    for (int ksx = 0; ksx < 4; ++ksx) {
 #pragma unroll
         for (int be = 0; be < NBT; ++be) {
-            uint32_t hi[4], lo[4];
-            float bias = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t sw = word_of(cur.ksc[be], i), zw = word_of(cur.kze[be], i);
-                split2(qv[2 * i] * lo_h(sw), qv[2 * i + 1] * hi_h(sw), hi[i], lo[i]);
-                bias = fmaf(qv[2 * i], lo_h(zw), bias);
-                bias = fmaf(qv[2 * i + 1], hi_h(zw), bias);
-            }
-            uint4* row = reinterpret_cast<uint4*>(ab + (be * 8 + 2 * hh) * 64 + 4 * chunk);
-            row[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            row[16] = make_uint4(lo[0], lo[1], lo[2], lo[3]);   // next row (64 dwords on)
-            bias = xor_sum16(bias);
-            if (chunk == 0) misc[be * 4 + hh] = bias * p.sigma2;
-        }
-        __syncthreads();
-
-        // ---- 3. S = q' . codes on MFMA: 4 tiles of 16 tokens x 4 K-steps of 32 channels
-        f32x4 S[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) S[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ksx = 0; ksx < 4; ++ksx) {
-            f16x8 A[NBT];
-#pragma unroll
-            for (int be = 0; be < NBT; ++be) {
-                if (n < 8) {
-                    const uint4 a = *reinterpret_cast<const uint4*>(ab + (be * 8 + n) * 64 + 16 * ksx + 4 * kg);
-                    A[be] = as_f16x8(a.x, a.y, a.z, a.w);
-                } else {
-                    A[be] = as_f16x8(0u, 0u, 0u, 0u);
-                }
-            }
-#pragma unroll
-            for (int be = 0; be < NBT; ++be) {
-                const int r = G == 64 ? (n >> 2) : (2 * be + ((n & 7) >> 2));
-                const uint4* src = reinterpret_cast<const uint4*>(kl + r * KSTR + 32 * ksx + 8 * kg);
-                const uint4 w0 = src[0], w1 = src[1];
-                const uint32_t x0 = __builtin_amdgcn_perm(w0.y, w0.x, sel);
-                const uint32_t x1 = __builtin_amdgcn_perm(w0.w, w0.z, sel);
-                const uint32_t x2 = __builtin_amdgcn_perm(w1.y, w1.x, sel);
-                const uint32_t x3 = __builtin_amdgcn_perm(w1.w, w1.z, sel);
-                if (G == 64) {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const uint32_t mk = 0x00030003u << (2 * u);
-                        S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            A[0], as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), S[u], 0, 0, 0);
-                    }
-                } else {
-#pragma unroll
-                    for (int v = 0; v < 2; ++v) {
-                        const int up = 2 * v + (n >> 3);
-                        const uint32_t mk = 0x00030003u << (2 * up);
-                        S[2 * be + v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            A[be], as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), S[2 * be + v], 0, 0, 0);
-                    }
-                }
-            }
-        }
-
-        // ---- 4. softmax: lane (n, kg<2) holds heads 2kg (rows 0,1) and 2kg+1 (rows 2,3)
-        const int hA = 2 * (kg & 1), hB = hA + 1;
-        float sA[4], sB[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int up = G == 64 ? u : 2 * (u & 1) + (n >> 3);
-            const int be = G == 64 ? 0 : (u >> 1);
-            const float f = p.sigma2 * __builtin_ldexpf(1.0f, 24 - 2 * up);
-            sA[u] = fmaf(S[u][0] + S[u][1], f, misc[be * 4 + hA]);
-            sB[u] = fmaf(S[u][2] + S[u][3], f, misc[be * 4 + hB]);
-        }
-        const float mA = xor_max16(fmaxf(fmaxf(sA[0], sA[1]), fmaxf(sA[2], sA[3])));
-        const float mB = xor_max16(fmaxf(fmaxf(sB[0], sB[1]), fmaxf(sB[2], sB[3])));
-        float tmax[HG];
-        tmax[0] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mA), 0));
-        tmax[1] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mB), 0));
-        tmax[2] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mA), 16));
-        tmax[3] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mB), 16));
-        bool resc = false;
-#pragma unroll
-        for (int h = 0; h < HG; ++h) resc |= tmax[h] > m_run[h] + TAU;
-        if (resc) {
-            float alpha[HG];
-#pragma unroll
-            for (int h = 0; h < HG; ++h) {
-                const float mn = fmaxf(m_run[h], tmax[h]);
-                alpha[h] = exp2f(m_run[h] - mn);
-                m_run[h] = mn;
-            }
-            const float a0 = pick4(alpha, 2 * (kg & 1)), a1 = pick4(alpha, 2 * (kg & 1) + 1);
-#pragma unroll
-            for (int P = 0; P < 2; ++P)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    O[P][u][0] *= a0;
-                    O[P][u][1] *= a0;
-                    O[P][u][2] *= a1;
-                    O[P][u][3] *= a1;
-                }
-            const float ah = pick4(alpha, hh);
-            lsum *= ah;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) vb[g] *= ah;
-        }
-        const float mrA = pick4(m_run, hA), mrB = pick4(m_run, hB);
-        if (kg < 2) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                sA[u] = exp2f(sA[u] - mrA);
-                sB[u] = exp2f(sB[u] - mrB);
-            }
+            const uint4 a = *reinterpret_cast<const uint4*>(L.qa + (be * 8 + (n & 7)) * QSTR + 16 * ksx + 4 * kg);
+            const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
+            const int r = G == 64 ? (n >> 2) : (2 * be + ((n & 7) >> 2));
+            const uint4* src = reinterpret_cast<const uint4*>(L.kl + r * KSTR + 32 * ksx + 8 * kg);
+            const uint4 w0 = src[0], w1 = src[1];
+            const uint32_t x0 = __builtin_amdgcn_perm(w0.y, w0.x, sel);
+            const uint32_t x1 = __builtin_amdgcn_perm(w0.w, w0.z, sel);
+            const uint32_t x2 = __builtin_amdgcn_perm(w1.y, w1.x, sel);
+            const uint32_t x3 = __builtin_amdgcn_perm(w1.w, w1.z, sel);
             if (G == 64) {
-                *reinterpret_cast<float4*>(pl + hA * PSTR + 4 * n) = make_float4(sA[0], sA[1], sA[2], sA[3]);
-                *reinterpret_cast<float4*>(pl + hB * PSTR + 4 * n) = make_float4(sB[0], sB[1], sB[2], sB[3]);
-            } else {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int t = 32 * (u >> 1) + 16 * ((n & 7) >> 2) + 4 * (n & 3) + 2 * (u & 1) + (n >> 3);
-                    pl[hA * PSTR + t] = sA[u];
-                    pl[hB * PSTR + t] = sB[u];
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- 5. p' = p * s_v (hi/lo rows) per value group; sum_t p and sum_t p z_v
-        {
-            const float4 pv4 = *reinterpret_cast<const float4*>(pl + hh * PSTR + 4 * chunk);
-            const float pv[4] = {pv4.x, pv4.y, pv4.z, pv4.w};
-            lsum += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-            // scale / zero halves: token t (0..3), group g at half index 4t + g
-            float sv[4][4], zv[4][4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int g = 0; g < 4; g += 2) {
-                    const int hidx = 4 * t + g;
-                    const uint32_t sw = word_of(cur.vsc[hidx >> 3], (hidx & 7) >> 1);
-                    const uint32_t zw = word_of(cur.vze[hidx >> 3], (hidx & 7) >> 1);
-                    sv[t][g] = lo_h(sw);
-                    sv[t][g + 1] = hi_h(sw);
-                    zv[t][g] = lo_h(zw);
-                    zv[t][g + 1] = hi_h(zw);
-                }
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint32_t h01, l01, h23, l23;
-                split2(pv[0] * sv[0][g], pv[1] * sv[1][g], h01, l01);
-                split2(pv[2] * sv[2][g], pv[3] * sv[3][g], h23, l23);
-                // row ((pass*2 + gsel)*4 + head)*2 + hl, 64 tokens = 32 dwords per row
-                uint32_t* rowp = ab + ((((g >> 1) * 2 + (g & 1)) * 4 + hh) * 2) * 32 + 2 * chunk;
-                *reinterpret_cast<uint2*>(rowp) = make_uint2(h01, h23);
-                *reinterpret_cast<uint2*>(rowp + 32) = make_uint2(l01, l23);
-                vb[g] = fmaf(pv[0], zv[0][g], vb[g]);
-                vb[g] = fmaf(pv[1], zv[1][g], vb[g]);
-                vb[g] = fmaf(pv[2], zv[2][g], vb[g]);
-                vb[g] = fmaf(pv[3], zv[3][g], vb[g]);
-            }
-        }
-        __syncthreads();
-
-        // ---- 6. O += p' . codes on MFMA: 2 passes x 4 channel tiles x 2 K-steps of 32 tokens
-#pragma unroll
-        for (int P = 0; P < 2; ++P) {
-            const int wi = 4 * P + 2 * (n >> 3) + ((n & 7) >> 2);
-#pragma unroll
-            for (int ksx = 0; ksx < 2; ++ksx) {
-                const uint4 a = *reinterpret_cast<const uint4*>(ab + (P * 16 + n) * 32 + 16 * ksx + 4 * kg);
-                const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
-                const uint4* src = reinterpret_cast<const uint4*>(vl + wi * VSTR + 32 * ksx + 8 * kg);
-                const uint4 w0 = src[0], w1 = src[1];
-                const uint32_t x0 = __builtin_amdgcn_perm(w0.y, w0.x, sel);
-                const uint32_t x1 = __builtin_amdgcn_perm(w0.w, w0.z, sel);
-                const uint32_t x2 = __builtin_amdgcn_perm(w1.y, w1.x, sel);
-                const uint32_t x3 = __builtin_amdgcn_perm(w1.w, w1.z, sel);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const uint32_t mk = 0x00030003u << (2 * u);
-                    O[P][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        A, as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), O[P][u], 0, 0, 0);
+                    S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        A, as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), S[u], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    const uint32_t mk = 0x00030003u << (2 * (2 * v + (n >> 3)));
+                    S[2 * be + v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        A, as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), S[2 * be + v], 0, 0, 0);
                 }
             }
         }
-        __syncthreads();
-        cur = nxt;
     }
 
-    // ---- epilogue: reduce l and the value-zero sums over the 16 lanes of a head
-    lsum = xor_sum16(lsum);
+    // ---- softmax.  Lane (n, kg) holds rows 4kg..4kg+3; rows 8..15 repeat
+    // rows 0..7, so lanes kg and kg+2 see heads 2(kg&1), 2(kg&1)+1 (hi/lo row
+    // pairs) and split the tiles: kg < 2 take tiles 0, 1 and kg >= 2 tiles 2, 3.
+    const bool odd = (kg & 1) != 0;
+    const int u0 = 2 * (kg >> 1);
+    float sA[2], sB[2];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) vb[g] = xor_sum16(vb[g]);
-    if (chunk == 0) {
-        misc[16 + hh] = lsum;
+    for (int v = 0; v < 2; ++v) {
+        // element-wise selects keep the accumulators in registers
+        const bool up2 = (kg >> 1) != 0;
+        float Sv[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) misc[32 + hh * 4 + g] = vb[g];
+        for (int e = 0; e < 4; ++e) Sv[e] = up2 ? S[2 + v][e] : S[v][e];
+        const int up = G == 64 ? u0 + v : 2 * v + (n >> 3);
+        const int be = G == 64 ? 0 : (kg >> 1);
+        const float f = p.sigma2 * __builtin_ldexpf(1.0f, 24 - 2 * up);
+        sA[v] = fmaf(Sv[0] + Sv[1], f, L.bias[be * 4 + 2 * (kg & 1)]);
+        sB[v] = fmaf(Sv[2] + Sv[3], f, L.bias[be * 4 + 2 * (kg & 1) + 1]);
     }
-    __syncthreads();
-    if ((kg >> 1) == (n >> 3)) {
+    // the running maxima move only when some logit exceeds them by more than
+    // TAU; each lane tests its logits and one ballot decides
+    float a0 = 1.0f, a1 = 1.0f, a2 = 1.0f, a3 = 1.0f;
+    const float thA = (odd ? st.m2 : st.m0) + TAU, thB = (odd ? st.m3 : st.m1) + TAU;
+    const bool over = fmaxf(sA[0], sA[1]) > thA || fmaxf(sB[0], sB[1]) > thB;
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+        const float mA = row_max16(fmaxf(sA[0], sA[1]));
+        const float mB = row_max16(fmaxf(sB[0], sB[1]));
+        const float t0 = fmaxf(readlane_f(mA, 0), readlane_f(mA, 32));
+        const float t1 = fmaxf(readlane_f(mB, 0), readlane_f(mB, 32));
+        const float t2 = fmaxf(readlane_f(mA, 16), readlane_f(mA, 48));
+        const float t3 = fmaxf(readlane_f(mB, 16), readlane_f(mB, 48));
+        const float n0 = fmaxf(st.m0, t0), n1 = fmaxf(st.m1, t1);
+        const float n2 = fmaxf(st.m2, t2), n3 = fmaxf(st.m3, t3);
+        a0 = fast_exp2(st.m0 - n0);
+        a1 = fast_exp2(st.m1 - n1);
+        a2 = fast_exp2(st.m2 - n2);
+        a3 = fast_exp2(st.m3 - n3);
+        st.m0 = n0;
+        st.m1 = n1;
+        st.m2 = n2;
+        st.m3 = n3;
+    }
+    const float mrA = odd ? st.m2 : st.m0, mrB = odd ? st.m3 : st.m1;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+        sA[v] = fast_exp2(sA[v] - mrA);
+        sB[v] = fast_exp2(sB[v] - mrB);
+    }
+    const int hA = 2 * (kg & 1), hB = hA + 1;
+    if (G == 64) {
+        *reinterpret_cast<float2*>(hb.pl + hA * PSTR + 4 * n + u0) = make_float2(sA[0], sA[1]);
+        *reinterpret_cast<float2*>(hb.pl + hB * PSTR + 4 * n + u0) = make_float2(sB[0], sB[1]);
+    } else {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const int t = 32 * (kg >> 1) + 16 * ((n & 7) >> 2) + 4 * (n & 3) + 2 * v + (n >> 3);
+            hb.pl[hA * PSTR + t] = sA[v];
+            hb.pl[hB * PSTR + t] = sB[v];
+        }
+    }
+    if (lane < HG) hb.alpha[lane] = sel4(lane, a0, a1, a2, a3);
+}
+
+struct VState {
+    f32x4 O[2][4];   // PV accumulators [pass][channel tile]
+    float lsum;      // this lane's share of sum p for head (lane >> 4)
+    float vb[4];     // this lane's share of sum p z_v per group, head (lane >> 4)
+};
+
+// Value side of one tile, reading p and alpha from `hb`.
+__device__ __forceinline__ void value_tile(const GqaParams& p, VTile& cur, VState& st, LdsV& L,
+                                           const Handoff& hb, uint32_t sel, int lane, int64_t bh,
+                                           int nxt, int end) {
+    const int n = lane & 15, kg = lane >> 4;
+    const int hh = lane >> 4, chunk = lane & 15;
+    // ---- stage value codes transposed to [word][token], and the side values
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const uint4 vw = half ? cur.v1 : cur.v0;
+        const int i = lane + 64 * half;
+        const int tok = i >> 1, w0 = 4 * (i & 1);
+        L.vl[(w0 + 0) * VSTR + tok] = vw.x;
+        L.vl[(w0 + 1) * VSTR + tok] = vw.y;
+        L.vl[(w0 + 2) * VSTR + tok] = vw.z;
+        L.vl[(w0 + 3) * VSTR + tok] = vw.w;
+    }
+    *reinterpret_cast<uint4*>(L.vsl + (lane >> 5) * 128 + 4 * (lane & 31)) = cur.vs;
+    if (nxt < end) load_vtile(p, bh, nxt, lane, cur);
+
+    // ---- rescale what was accumulated with the previous maxima
+    const float a0 = hb.alpha[0], a1 = hb.alpha[1], a2 = hb.alpha[2], a3 = hb.alpha[3];
+    if (fminf(fminf(a0, a1), fminf(a2, a3)) < 1.0f) {
+        const bool odd = (kg & 1) != 0;
+        const float aA = odd ? a2 : a0, aB = odd ? a3 : a1;
 #pragma unroll
         for (int P = 0; P < 2; ++P)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int c = 64 * P + 32 * (n >> 3) + 4 * (n & 7) + u;
-                const int g = 2 * P + (n >> 3);
-                const float f = __builtin_ldexpf(1.0f, 24 - 2 * u);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int h = 2 * (kg & 1) + j;
-                    const float acc = fmaf(O[P][u][2 * j] + O[P][u][2 * j + 1], f, misc[32 + h * 4 + g]);
-                    p.ws_acc[((int64_t(b) * p.Hq + hq0 + h) * p.S + s) * D + c] = acc;
-                }
+                st.O[P][u][0] *= aA;
+                st.O[P][u][1] *= aA;
+                st.O[P][u][2] *= aB;
+                st.O[P][u][3] *= aB;
             }
+        const float ah = sel4(hh, a0, a1, a2, a3);
+        st.lsum *= ah;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) st.vb[g] *= ah;
     }
-    if (lane < HG) {
-        const int64_t slot = (int64_t(b) * p.Hq + hq0 + lane) * p.S + s;
-        p.ws_ml[slot * 2] = pick4(m_run, lane);
-        p.ws_ml[slot * 2 + 1] = misc[16 + lane];
+    wave_sync();
+
+    // ---- p' = p * s_v as fp16 hi/lo rows per value group; sum_t p, sum_t p z_v
+    {
+        const float4 pv4 = *reinterpret_cast<const float4*>(hb.pl + hh * PSTR + 4 * chunk);
+        const float pv[4] = {pv4.x, pv4.y, pv4.z, pv4.w};
+        st.lsum += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        // scale / zero halves of token t (0..3), group g (0..3) at half index 4t + g
+        const uint4* svp = reinterpret_cast<const uint4*>(L.vsl + 8 * chunk);
+        const uint4* zvp = reinterpret_cast<const uint4*>(L.vsl + 128 + 8 * chunk);
+        const uint4 s0 = svp[0], s1 = svp[1], z0 = zvp[0], z1 = zvp[1];
+        const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const uint32_t zw[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float sv[4], zv[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int hidx = 4 * t + g;
+                sv[t] = (hidx & 1) ? hi_h(sw[hidx >> 1]) : lo_h(sw[hidx >> 1]);
+                zv[t] = (hidx & 1) ? hi_h(zw[hidx >> 1]) : lo_h(zw[hidx >> 1]);
+            }
+            uint32_t h01, l01, h23, l23;
+            split_prod2(pv[0], sv[0], pv[1], sv[1], h01, l01);
+            split_prod2(pv[2], sv[2], pv[3], sv[3], h23, l23);
+            // row ((pass*2 + gsel)*4 + head)*2 + hl; 64 tokens = 32 dwords per row
+            uint32_t* rowp = L.pa + ((((g >> 1) * 2 + (g & 1)) * 4 + hh) * 2) * ASTR + 2 * chunk;
+            *reinterpret_cast<uint2*>(rowp) = make_uint2(h01, h23);
+            *reinterpret_cast<uint2*>(rowp + ASTR) = make_uint2(l01, l23);
+            float z = st.vb[g];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) z = fmaf(pv[t], zv[t], z);
+            st.vb[g] = z;
+        }
+    }
+    wave_sync();
+
+    // ---- O += p' . codes: 2 passes x 4 channel tiles x 2 K-steps of 32 tokens
+#pragma unroll
+    for (int P = 0; P < 2; ++P) {
+        const int wi = 4 * P + 2 * (n >> 3) + ((n & 7) >> 2);
+#pragma unroll
+        for (int ksx = 0; ksx < 2; ++ksx) {
+            const uint4 a = *reinterpret_cast<const uint4*>(L.pa + (P * 16 + n) * ASTR + 16 * ksx + 4 * kg);
+            const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
+            const uint4* src = reinterpret_cast<const uint4*>(L.vl + wi * VSTR + 32 * ksx + 8 * kg);
+            const uint4 w0 = src[0], w1 = src[1];
+            const uint32_t x0 = __builtin_amdgcn_perm(w0.y, w0.x, sel);
+            const uint32_t x1 = __builtin_amdgcn_perm(w0.w, w0.z, sel);
+            const uint32_t x2 = __builtin_amdgcn_perm(w1.y, w1.x, sel);
+            const uint32_t x3 = __builtin_amdgcn_perm(w1.w, w1.z, sel);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t mk = 0x00030003u << (2 * u);
+                st.O[P][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    A, as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), st.O[P][u], 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(128) void k_decode_gqa(GqaParams p) {
+    __shared__ Lds L;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n = lane & 15, kg = lane >> 4;
+    const int hh = lane >> 4, chunk = lane & 15;
+    const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int64_t bh = int64_t(b) * p.Hkv + kvh;
+    const int hq0 = kvh * HG;
+    if (s >= p.S_main) {
+        if (wave == 0) tail_split(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), L.hb[0].pl);
+        return;
+    }
+    const int t_lo = int(int64_t(s) * p.ntiles / p.S_main);
+    const int t_hi = int(int64_t(s + 1) * p.ntiles / p.S_main);
+    const int ntl = t_hi - t_lo;
+    // v_perm selector: byte (n & 3) of the low-channel (or low-token) word ->
+    // byte 0, of the high one -> byte 2, zero bytes 1 and 3
+    const uint32_t bsel = uint32_t(n & 3);
+    const uint32_t sel = bsel | (0x0cu << 8) | ((4u + bsel) << 16) | (0x0cu << 24);
+
+    if (wave == 0) {
+        float qv[8];
+        {
+            const uint4 raw = *reinterpret_cast<const uint4*>(p.q + ((int64_t(b) * p.Hq + hq0 + hh) * D + 8 * chunk));
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qv[2 * i] = lo_h(w[i]);
+                qv[2 * i + 1] = hi_h(w[i]);
+            }
+        }
+        KState st;
+        st.m0 = st.m1 = st.m2 = st.m3 = -INFINITY;
+        // two register tiles in flight: tile t is staged from set (t & 1),
+        // which then receives tile t + 2
+        KTile ta, tb;
+        load_ktile<G>(p, bh, t_lo, lane, ta);
+        if (ntl > 1) load_ktile<G>(p, bh, t_lo + 1, lane, tb);
+        for (int it = 0; it <= ntl; it += 2) {
+            if (it < ntl) key_tile<G>(p, ta, st, L.k, L.hb[0], qv, sel, lane, bh, t_lo + it + 2, t_hi);
+            if (it == ntl && lane < HG) L.misc[lane] = sel4(lane, st.m0, st.m1, st.m2, st.m3);
+            __syncthreads();
+            if (it + 1 > ntl) break;
+            if (it + 1 < ntl) key_tile<G>(p, tb, st, L.k, L.hb[1], qv, sel, lane, bh, t_lo + it + 3, t_hi);
+            if (it + 1 == ntl && lane < HG) L.misc[lane] = sel4(lane, st.m0, st.m1, st.m2, st.m3);
+            __syncthreads();
+        }
+    } else {
+        VState st;
+        st.lsum = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) st.vb[g] = 0.0f;
+#pragma unroll
+        for (int P = 0; P < 2; ++P)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) st.O[P][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // value work trails the key work by one tile (tile it - 1 at step it)
+        VTile ta, tb;
+        load_vtile(p, bh, t_lo, lane, ta);
+        if (ntl > 1) load_vtile(p, bh, t_lo + 1, lane, tb);
+        for (int it = 0; it <= ntl; it += 2) {
+            if (it >= 1) value_tile(p, tb, st, L.v, L.hb[1], sel, lane, bh, t_lo + it + 1, t_hi);
+            __syncthreads();
+            if (it + 1 > ntl) break;
+            value_tile(p, ta, st, L.v, L.hb[0], sel, lane, bh, t_lo + it + 2, t_hi);
+            __syncthreads();
+        }
+        // ---- epilogue: l and the value-zero sums over the 16 lanes of a head
+        const float lsum = row_sum16(st.lsum);
+        float vbs[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) vbs[g] = row_sum16(st.vb[g]);
+        if (chunk == 0) {
+            L.misc[16 + hh] = lsum;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) L.misc[32 + hh * 4 + g] = vbs[g];
+        }
+        wave_sync();
+        if ((kg >> 1) == (n >> 3)) {
+#pragma unroll
+            for (int P = 0; P < 2; ++P)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int c = 64 * P + 32 * (n >> 3) + 4 * (n & 7) + u;
+                    const int g = 2 * P + (n >> 3);
+                    const float f = __builtin_ldexpf(1.0f, 24 - 2 * u);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int h = 2 * (kg & 1) + j;
+                        const float acc = fmaf(st.O[P][u][2 * j] + st.O[P][u][2 * j + 1], f, L.misc[32 + h * 4 + g]);
+                        p.ws_acc[((int64_t(b) * p.Hq + hq0 + h) * p.S + s) * D + c] = acc;
+                    }
+                }
+        }
+        if (lane < HG) {
+            const int64_t slot = (int64_t(b) * p.Hq + hq0 + lane) * p.S + s;
+            p.ws_ml[slot * 2] = L.misc[lane];
+            p.ws_ml[slot * 2 + 1] = L.misc[16 + lane];
+        }
     }
 }
 
@@ -533,9 +715,9 @@ hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
     p.sigma2 = a.sigma * 1.4426950408889634f;
     const dim3 grid(a.S, a.g.Hkv, a.g.B);
     if (a.g.kG == 64)
-        hipLaunchKernelGGL(k_decode_gqa<64>, grid, dim3(64), 0, st, p);
+        hipLaunchKernelGGL(k_decode_gqa<64>, grid, dim3(128), 0, st, p);
     else
-        hipLaunchKernelGGL(k_decode_gqa<32>, grid, dim3(64), 0, st, p);
+        hipLaunchKernelGGL(k_decode_gqa<32>, grid, dim3(128), 0, st, p);
     return hipGetLastError();
 }
 

@@ -12,7 +12,8 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvq.so")
+# KVQ_LIB selects another build of the library (e.g. an instrumented one)
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(HERE, "libkvq.so")
 
 KVQ_KIND_KIVI, KVQ_KIND_MLA = 0, 1
 KVQ_AXIS_PER_CHANNEL, KVQ_AXIS_PER_TOKEN = 0, 1
