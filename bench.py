@@ -57,11 +57,28 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-pairs", type=int, default=32)
+    ap.add_argument("--cpu-pairs", type=int, default=256)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
+
+
+def profiled_traffic(variant: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 (FETCH_SIZE / WRITE_SIZE
+    scaled by a plain-copy calibration, profiles/traffic.json), or None when
+    no measurement exists or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{variant}/{workload}")
+    if not rec:
+        return None
+    src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    if hashlib.sha256(src).hexdigest()[:16] != rec["sha256_16"]:
+        return None
+    return int(rec["traffic_bytes"])
 
 
 def copy_probe():
@@ -219,7 +236,7 @@ def main():
                    "bits": w.kbits, "value_group": w.vG, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None,
+                     "traffic": profiled_traffic(dc.variant(w.n_q_heads), w.name),
                      "kernel": "decode pass-1 (" + dc.variant(w.n_q_heads) + ")",
                      "avg_us": round(p1_avg * 1e3, 2), "alg_bytes_per_launch": int(p1_bytes)},
         "extra": {
