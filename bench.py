@@ -1,12 +1,16 @@
 """Benchmark: 2-bit decode attention over a KIVI-style cache on one MI355X.
 
-One step = one decode token for every sequence of the workload: append the
-new token (per-token value quantize, key into the residual, per-channel key
-quantize of the block when it fills) followed by split-K decode attention over
-the whole cache and the merge pass.  Inputs are seeded synthetic fp16 tensors
-already resident in HBM.  Prints ONE JSON line.
+One step = one decode token for every sequence of the workload in one
+layer: append the new token (per-token value quantize, key into the residual,
+per-channel key quantize of the block when it fills) followed by split-K
+decode attention over the whole cache and the merge pass.  Steps rotate over
+several layers, each with its own cache, at least 1 GB in total, so that a
+cache smaller than the 256 MB Infinity Cache is still read from HBM.  Inputs
+are seeded synthetic fp16 tensors already resident in HBM.  Prints ONE JSON
+line.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers L]
+                  [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -59,6 +63,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=256)
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=0,
+                    help="caches to rotate over (default: enough for 1 GB, at most 32)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -93,6 +99,26 @@ def copy_probe():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_each_way": n, "launches": 5}), flush=True)
+
+
+def copy_ceiling_gbps():
+    """Read + write rate of a plain 1 GiB device copy on this GPU (median of 5)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    ts = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    del src, dst
+    return 2 * n / (float(np.median(ts)) * 1e-3) / 1e9
 
 
 def cpu_baseline(w, k, v, q, cap, n_pairs):
@@ -146,7 +172,9 @@ def main():
     w = configs.BY_NAME[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    n_new = args.warmup + args.steps
+    n_steps = args.warmup + args.steps
+    L = args.layers or min(32, max(1, -(-1_000_000_000 // w.cache_bytes())))
+    n_new = -(-n_steps // L)              # new tokens each layer receives
     Tall = w.T + n_new
     cap = w.capacity(n_new + 1)
     t0 = time.time()
@@ -164,7 +192,8 @@ def main():
     knew = dev16(np.ascontiguousarray(k[:, :, w.T:].transpose(2, 0, 1, 3))[:, :, :, None, :])
     vnew = dev16(np.ascontiguousarray(v[:, :, w.T:].transpose(2, 0, 1, 3))[:, :, :, None, :])
     qd = dev16(q)
-    dc = kvq.DeviceCache(kvq.cfg_for(w, cap), device=dev)
+    dcs = [kvq.DeviceCache(kvq.cfg_for(w, cap), device=dev) for _ in range(L)]
+    dc = dcs[0]
     stream = torch.cuda.current_stream()
 
     # ---- bulk prefill quantize (the context), timed over a few repetitions
@@ -180,7 +209,11 @@ def main():
         qt.append(a.elapsed_time(b))
     q_ms = float(np.median(qt))
     q_bytes = 2 * w.batch * w.n_kv_heads * w.T * (w.kd + w.vd) + w.cache_bytes()
-    assert dc.state() == (w.T, w.R)
+    for other in dcs[1:]:
+        other.append(kd, vd)
+    torch.cuda.synchronize()
+    assert all(c.state() == (w.T, w.R) for c in dcs)
+    del kd, vd
 
     out = torch.empty((w.batch, w.n_q_heads, w.vd), dtype=torch.float16, device=dev)
     ws = dc.workspace(w.n_q_heads, args.splits)
@@ -188,10 +221,12 @@ def main():
     evs = [(hip.create(), hip.create()) for _ in range(args.steps)]
 
     def step(i, timed):
+        # step i: layer i % L receives its token i // L
+        c = dcs[i % L]
         if timed:
             kvq.kv_set_timing_events(*evs[i - args.warmup])
-        dc.append(knew[i], vnew[i])
-        kvq.kv_decode_attention(dc.handle, qd.data_ptr(), w.n_q_heads, w.sigma, args.splits,
+        c.append(knew[i // L], vnew[i // L])
+        kvq.kv_decode_attention(c.handle, qd.data_ptr(), w.n_q_heads, w.sigma, args.splits,
                                 out.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream)
 
     for i in range(args.warmup):
@@ -199,7 +234,7 @@ def main():
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for i in range(args.warmup, n_new):
+    for i in range(args.warmup, n_steps):
         step(i, True)
     stop.record(stream)
     torch.cuda.synchronize()
@@ -210,13 +245,15 @@ def main():
         hip.destroy(a)
         hip.destroy(b)
 
-    Ts = [w.T + i + 1 for i in range(args.warmup, n_new)]
+    Ts = [w.T + i // L + 1 for i in range(args.warmup, n_steps)]
     alg_bytes = sum(w.decode_bytes(T) for T in Ts)
     value = alg_bytes / (total_ms * 1e-3) / 1e9
     p1_avg = float(np.mean(pass1_ms))
     p1_bytes = float(np.mean([w.cache_bytes(T) + w.batch * w.n_q_heads * w.qd * 2 for T in Ts]))
     achieved = p1_bytes / (p1_avg * 1e-3) / 1e9
     ms_step = total_ms / args.steps
+    p1_sorted = np.sort(pass1_ms)
+    copy_gbps = copy_ceiling_gbps()
 
     res = {
         "metric": "2-bit decode attention KV bytes/s (tokens/s, % HBM peak; quantize GB/s)",
@@ -233,7 +270,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.kd, "context": w.T, "G": w.kG,
-                   "bits": w.kbits, "value_group": w.vG, "parallelism": "none (1 GPU)"},
+                   "bits": w.kbits, "value_group": w.vG, "layers": L, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": profiled_traffic(dc.variant(w.n_q_heads), w.name),
@@ -243,6 +280,9 @@ def main():
             "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
             "attended_kv_tokens_per_s": round(w.batch * float(np.mean(Ts)) / (ms_step * 1e-3), 1),
             "hbm_frac_whole_step": round(value / HBM_PEAK_GBPS, 4),
+            "pass1_us_p10_p50_p90": [round(float(np.percentile(p1_sorted, x)) * 1e3, 2) for x in (10, 50, 90)],
+            "copy_ceiling_GBps": round(copy_gbps, 1),
+            "pass1_frac_of_copy_ceiling": round(achieved / copy_gbps, 4),
             "quantize_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 2),
             "quantize_ms": round(q_ms, 4),
             "quantize_bytes": int(q_bytes),
@@ -253,7 +293,8 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, k[:, :, :w.T], v[:, :, :w.T], q, cap, args.cpu_pairs)
     print(json.dumps(res), flush=True)
-    dc.close()
+    for c in dcs:
+        c.close()
 
 
 if __name__ == "__main__":

@@ -10,7 +10,7 @@ LIB = os.path.join(HERE, "libkvq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["kvq_api.cpp", "kvq_plan.cpp", "kvq_quant.hip", "kvq_decode_generic.hip",
-           "kvq_decode_gqa.hip"]
+           "kvq_decode_gqa.hip", "kvq_decode_mha.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

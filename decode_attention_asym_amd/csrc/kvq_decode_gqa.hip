@@ -25,225 +25,16 @@
 //    rows; sum_t p_t z_t per (head, group) is accumulated on the VALU.
 //  * online softmax in log2 units; the running maximum only moves when a
 //    tile exceeds it by more than 2^8 (weights stay <= 256, fp16-safe).
-// One 64-lane workgroup handles one contiguous run of 64-token tiles of one
-// (sequence, KV head); the work of the next tile's global loads overlaps the
-// current tile.  The keys of a trailing partial tile and the residual are
+// One two-wave workgroup handles one contiguous run of 64-token tiles of one
+// (sequence, KV head); the global loads of later tiles overlap the current
+// tile.  The keys of a trailing partial tile and the residual are
 // handled by one extra workgroup per (sequence, KV head) on the VALU.
-#include <hip/hip_fp16.h>
-#include <math.h>
-
-#include "kvq_internal.h"
+#include "kvq_mfma_tiles.h"
 
 namespace kvq {
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int HG = 4;       // query heads per KV head
-constexpr int D = 128;      // head dim
-constexpr int KSTR = 136;   // dwords per row of the key-code tile in LDS
-constexpr int VSTR = 76;    // dwords per row of the value-code tile in LDS
-constexpr int QSTR = 68;    // dwords per q' row (128 fp16 + pad)
-constexpr int ASTR = 36;    // dwords per p' row (64 fp16 + pad)
-constexpr int PSTR = 68;    // floats per row of the weight tile in LDS
-constexpr float TAU = 8.0f; // lazy-rescale threshold (log2 units)
-
-struct GqaParams {
-    const uint32_t* kc;
-    const uint16_t *ks, *kz, *kr;
-    const uint32_t* vc;
-    const uint16_t *vs, *vz;
-    const uint16_t* q;
-    float *ws_acc, *ws_ml;
-    int Hq, Hkv, S, S_main, ntiles, G;
-    int64_t T, nblk, cap, nblk_cap;
-    float sigma2;  // softmax scale * log2(e)
-};
-
-struct Tile {
-    uint4 k0, k1, v0, v1;     // 2 KB of key codes and 2 KB of value codes, 32 B per lane
-    uint4 ks;                 // key scale (lanes 0..31) / zero (lanes 32..63) of the tile's blocks
-    uint4 vs;                 // value scale (lanes 0..31) / zero (lanes 32..63) of the tile's tokens
-};
-
-__device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
-__device__ __forceinline__ float lo_h(uint32_t w) { return float(__builtin_bit_cast(f16x2, w)[0]); }
-__device__ __forceinline__ float hi_h(uint32_t w) { return float(__builtin_bit_cast(f16x2, w)[1]); }
-
-__device__ __forceinline__ f16x8 as_f16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    u32x4 v = {a, b, c, d};
-    return __builtin_bit_cast(f16x8, v);
-}
-
-__device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-}
-
-// fp16 hi/lo split of two fp32 values: (hi, lo) with hi + lo == x to ~2^-22
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-    hi = pk_rtz(x0, x1);
-    lo = pk_rtz(x0 - lo_h(hi), x1 - hi_h(hi));
-}
-
-// hi/lo split of the products a0*b0, a1*b1 (a fp32, b an fp16 half): the
-// remainders are single fused operations a*b - hi
-__device__ __forceinline__ void split_prod2(float a0, float b0, float a1, float b1, uint32_t& hi,
-                                            uint32_t& lo) {
-    // fma(a, b, +0) is one v_fma_mix with the fp16 operand read in place
-    // (it cannot become a plain multiply: they differ for a*b == -0)
-    hi = pk_rtz(fmaf(a0, b0, 0.0f), fmaf(a1, b1, 0.0f));
-    lo = pk_rtz(fmaf(a0, b0, -lo_h(hi)), fmaf(a1, b1, -hi_h(hi)));
-}
-
-__device__ __forceinline__ float xor_max16(float x) {
-    x = fmaxf(x, __shfl_xor(x, 1));
-    x = fmaxf(x, __shfl_xor(x, 2));
-    x = fmaxf(x, __shfl_xor(x, 4));
-    return fmaxf(x, __shfl_xor(x, 8));
-}
-__device__ __forceinline__ float xor_sum16(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    return x + __shfl_xor(x, 8);
-}
-
-__device__ __forceinline__ float pick4(const float* v, int i) {
-    return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
-}
-
-// All global loads of one 64-token tile, 16-byte aligned, no lane reads
-// what another lane reads: codes 2 x 2 KB, key side 512 B (G = 64) or 1 KB
-// (G = 32), value side 1 KB.
-template <int G>
-__device__ __forceinline__ void load_tile(const GqaParams& p, int64_t bh, int64_t tt, int lane, Tile& r) {
-    constexpr int NBT = 64 / G, W = G / 16;
-    const uint4* kb = reinterpret_cast<const uint4*>(p.kc + (bh * p.nblk_cap + tt * NBT) * D * W);
-    r.k0 = kb[lane];
-    r.k1 = kb[lane + 64];
-    const uint4* vb = reinterpret_cast<const uint4*>(p.vc + (bh * p.cap + tt * 64) * 8);
-    r.v0 = vb[lane];
-    r.v1 = vb[lane + 64];
-    const uint16_t* kside = (lane < 32 ? p.ks : p.kz) + (bh * p.nblk_cap + tt * NBT) * D;
-    if (G == 64) {
-        const uint2 v = reinterpret_cast<const uint2*>(kside)[lane & 31];
-        r.ks = make_uint4(v.x, v.y, 0u, 0u);
-    } else {
-        r.ks = reinterpret_cast<const uint4*>(kside)[lane & 31];
-    }
-    const uint16_t* vside = (lane < 32 ? p.vs : p.vz) + (bh * p.cap + tt * 64) * 4;
-    r.vs = reinterpret_cast<const uint4*>(vside)[lane & 31];
-}
-
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
-    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-__device__ __forceinline__ float key_hat(const GqaParams& p, int64_t bh, int64_t t, int c) {
-    const int64_t Tq = p.nblk * p.G;
-    if (t >= Tq) return h2f(p.kr[(bh * p.G + (t - Tq)) * D + c]);
-    const int64_t blk = t / p.G;
-    const int i = int(t - blk * p.G);
-    const int64_t side = (bh * p.nblk_cap + blk) * D + c;
-    const uint32_t w = p.kc[side * (p.G / 16) + i / 16];
-    return fmaf(float((w >> (2 * (i & 15))) & 3u), h2f(p.ks[side]), h2f(p.kz[side]));
-}
-
-__device__ __forceinline__ float value_hat(const GqaParams& p, int64_t bh, int64_t t, int c) {
-    const int64_t row = bh * p.cap + t;
-    const uint32_t w = p.vc[row * 8 + c / 16];
-    const int64_t side = row * 4 + c / 32;
-    return fmaf(float((w >> (2 * (c & 15))) & 3u), h2f(p.vs[side]), h2f(p.vz[side]));
-}
-
-// Trailing tokens [ntiles*64, T): partial key block and fp16 residual keys,
-// one token per lane for the logits, two channels per lane for the values.
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
-
-__device__ void tail_split(const GqaParams& p, int b, int kvh, int s, float* qf, float* pl) {
-    const int lane = threadIdx.x;
-    const int64_t bh = int64_t(b) * p.Hkv + kvh;
-    const int hq0 = kvh * HG;
-    for (int i = lane; i < HG * D; i += 64) qf[i] = h2f(p.q[(int64_t(b) * p.Hq + hq0) * D + i]);
-    wave_sync();
-    const int64_t t0 = int64_t(p.ntiles) * 64;
-    const int n_tail = int(p.T - t0);
-    const int64_t t = t0 + lane;
-    const bool valid = lane < n_tail;
-    float sc[HG] = {0.f, 0.f, 0.f, 0.f};
-    if (valid) {
-        for (int c = 0; c < D; ++c) {
-            const float kh = key_hat(p, bh, t, c);
-#pragma unroll
-            for (int h = 0; h < HG; ++h) sc[h] = fmaf(qf[h * D + c], kh, sc[h]);
-        }
-    }
-    float m[HG], l[HG];
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-        float x = valid ? sc[h] * p.sigma2 : -INFINITY;
-        float mx = x;
-        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        const float pv = valid ? exp2f(x - mx) : 0.0f;
-        float sum = pv;
-        for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-        m[h] = mx;
-        l[h] = sum;
-        pl[h * PSTR + lane] = pv;
-    }
-    wave_sync();
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int c = lane + 64 * half;
-        float acc[HG] = {0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < n_tail; ++j) {
-            const float vh = value_hat(p, bh, t0 + j, c);
-#pragma unroll
-            for (int h = 0; h < HG; ++h) acc[h] = fmaf(pl[h * PSTR + j], vh, acc[h]);
-        }
-#pragma unroll
-        for (int h = 0; h < HG; ++h)
-            p.ws_acc[((int64_t(b) * p.Hq + hq0 + h) * p.S + s) * D + c] = acc[h];
-    }
-    if (lane < HG) {
-        const int64_t slot = (int64_t(b) * p.Hq + hq0 + lane) * p.S + s;
-        p.ws_ml[slot * 2] = pick4(m, lane);
-        p.ws_ml[slot * 2 + 1] = pick4(l, lane);
-    }
-}
-
-// Row-of-16 reductions with DPP (quad xor 1, quad xor 2, half-row mirror,
-// row mirror): afterwards every lane of the 16-lane row holds the result.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                                 0xf, 0xf, false));
-}
-__device__ __forceinline__ float row_max16(float x) {
-    x = fmaxf(x, dpp<0xb1>(x));
-    x = fmaxf(x, dpp<0x4e>(x));
-    x = fmaxf(x, dpp<0x141>(x));
-    return fmaxf(x, dpp<0x140>(x));
-}
-__device__ __forceinline__ float row_sum16(float x) {
-    x += dpp<0xb1>(x);
-    x += dpp<0x4e>(x);
-    x += dpp<0x141>(x);
-    return x + dpp<0x140>(x);
-}
-__device__ __forceinline__ float sel4(int i, float a, float b, float c, float d) {
-    return (i & 2) ? ((i & 1) ? d : c) : ((i & 1) ? b : a);
-}
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float readlane_f(float x, int l) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
-}
+constexpr int HG = 4;  // query heads per KV head
 
 // ---------------------------------------------------------------------------
 // Two specialised waves per workgroup, software-pipelined by one tile:
@@ -281,71 +72,21 @@ struct Lds {
     float misc[64];
 };
 
-struct KTile {
-    uint4 k0, k1;   // 2 KB of key codes, 32 B per lane
-    uint4 ks;       // key scale (lanes 0..31) / zero (lanes 32..63)
-};
-struct VTile {
-    uint4 v0, v1;   // 2 KB of value codes
-    uint4 vs;       // value scale (lanes 0..31) / zero (lanes 32..63)
-};
-
-template <int G>
-__device__ __forceinline__ void load_ktile(const GqaParams& p, int64_t bh, int64_t tt, int lane, KTile& r) {
-    constexpr int NBT = 64 / G, W = G / 16;
-    const uint4* kb = reinterpret_cast<const uint4*>(p.kc + (bh * p.nblk_cap + tt * NBT) * D * W);
-    r.k0 = kb[lane];
-    r.k1 = kb[lane + 64];
-    const uint16_t* kside = (lane < 32 ? p.ks : p.kz) + (bh * p.nblk_cap + tt * NBT) * D;
-    if (G == 64) {
-        const uint2 v = reinterpret_cast<const uint2*>(kside)[lane & 31];
-        r.ks = make_uint4(v.x, v.y, 0u, 0u);
-    } else {
-        r.ks = reinterpret_cast<const uint4*>(kside)[lane & 31];
-    }
-}
-
-__device__ __forceinline__ void load_vtile(const GqaParams& p, int64_t bh, int64_t tt, int lane, VTile& r) {
-    const uint4* vb = reinterpret_cast<const uint4*>(p.vc + (bh * p.cap + tt * 64) * 8);
-    r.v0 = vb[lane];
-    r.v1 = vb[lane + 64];
-    const uint16_t* vside = (lane < 32 ? p.vs : p.vz) + (bh * p.cap + tt * 64) * 4;
-    r.vs = reinterpret_cast<const uint4*>(vside)[lane & 31];
-}
-
 struct KState {
     float m0, m1, m2, m3;   // running maxima per head (log2 units, wave-uniform)
 };
 
 // Key side of one tile: produces p and alpha in `hb`.
 template <int G>
-__device__ __forceinline__ void key_tile(const GqaParams& p, KTile& cur, KState& st, LdsK& L,
+__device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState& st, LdsK& L,
                                          Handoff& hb, const float* qv, uint32_t sel, int lane,
                                          int64_t bh, int nxt, int end) {
     constexpr int NBT = 64 / G;
     const int n = lane & 15, kg = lane >> 4;
     const int hh = lane >> 4, chunk = lane & 15;
 
-    // ---- stage key codes transposed to [word row][channel], and the side values
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const uint4 kw = half ? cur.k1 : cur.k0;
-        const int i = lane + 64 * half;
-        if (G == 64) {
-            L.kl[0 * KSTR + i] = kw.x;
-            L.kl[1 * KSTR + i] = kw.y;
-            L.kl[2 * KSTR + i] = kw.z;
-            L.kl[3 * KSTR + i] = kw.w;
-        } else {
-            const int be = i >> 6, c = 2 * (i & 63);
-            *reinterpret_cast<uint2*>(L.kl + (2 * be) * KSTR + c) = make_uint2(kw.x, kw.z);
-            *reinterpret_cast<uint2*>(L.kl + (2 * be + 1) * KSTR + c) = make_uint2(kw.y, kw.w);
-        }
-    }
-    if (G == 64)
-        *reinterpret_cast<uint2*>(L.ksl + (lane >> 5) * 128 + 2 * (lane & 31)) = make_uint2(cur.ks.x, cur.ks.y);
-    else
-        *reinterpret_cast<uint4*>(L.ksl + (lane >> 5) * 128 + 4 * (lane & 31)) = cur.ks;
+    // ---- stage key codes and side values, then prefetch tile i + 2
+    stage_keys<G>(cur, L.kl, L.ksl, lane);
     if (nxt < end) load_ktile<G>(p, bh, nxt, lane, cur);
     wave_sync();
 
@@ -478,23 +219,13 @@ struct VState {
 };
 
 // Value side of one tile, reading p and alpha from `hb`.
-__device__ __forceinline__ void value_tile(const GqaParams& p, VTile& cur, VState& st, LdsV& L,
+__device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VState& st, LdsV& L,
                                            const Handoff& hb, uint32_t sel, int lane, int64_t bh,
                                            int nxt, int end) {
     const int n = lane & 15, kg = lane >> 4;
     const int hh = lane >> 4, chunk = lane & 15;
-    // ---- stage value codes transposed to [word][token], and the side values
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const uint4 vw = half ? cur.v1 : cur.v0;
-        const int i = lane + 64 * half;
-        const int tok = i >> 1, w0 = 4 * (i & 1);
-        L.vl[(w0 + 0) * VSTR + tok] = vw.x;
-        L.vl[(w0 + 1) * VSTR + tok] = vw.y;
-        L.vl[(w0 + 2) * VSTR + tok] = vw.z;
-        L.vl[(w0 + 3) * VSTR + tok] = vw.w;
-    }
-    *reinterpret_cast<uint4*>(L.vsl + (lane >> 5) * 128 + 4 * (lane & 31)) = cur.vs;
+    // ---- stage value codes and side values, then prefetch tile i + 2
+    stage_values(cur, L.vl, L.vsl, lane);
     if (nxt < end) load_vtile(p, bh, nxt, lane, cur);
 
     // ---- rescale what was accumulated with the previous maxima
@@ -578,7 +309,7 @@ __device__ __forceinline__ void value_tile(const GqaParams& p, VTile& cur, VStat
 }
 
 template <int G>
-__global__ __launch_bounds__(128) void k_decode_gqa(GqaParams p) {
+__global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
     __shared__ Lds L;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 15, kg = lane >> 4;
@@ -587,16 +318,13 @@ __global__ __launch_bounds__(128) void k_decode_gqa(GqaParams p) {
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int hq0 = kvh * HG;
     if (s >= p.S_main) {
-        if (wave == 0) tail_split(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), L.hb[0].pl);
+        if (wave == 0) tail_split<HG>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), L.hb[0].pl);
         return;
     }
     const int t_lo = int(int64_t(s) * p.ntiles / p.S_main);
     const int t_hi = int(int64_t(s + 1) * p.ntiles / p.S_main);
     const int ntl = t_hi - t_lo;
-    // v_perm selector: byte (n & 3) of the low-channel (or low-token) word ->
-    // byte 0, of the high one -> byte 2, zero bytes 1 and 3
-    const uint32_t bsel = uint32_t(n & 3);
-    const uint32_t sel = bsel | (0x0cu << 8) | ((4u + bsel) << 16) | (0x0cu << 24);
+    const uint32_t sel = perm_selector(n);
 
     if (wave == 0) {
         float qv[8];
@@ -683,36 +411,11 @@ __global__ __launch_bounds__(128) void k_decode_gqa(GqaParams p) {
 }  // namespace
 
 bool gqa_supported(const kvq_cache& c, int Hq) {
-    const kvq_cache_cfg& g = c.cfg;
-    return g.kind == KVQ_KIND_KIVI && g.key.bits == 2 && g.value.bits == 2 && g.key.dim == D &&
-           g.value.dim == D && g.value.group == 32 && (g.key.group == 32 || g.key.group == 64) &&
-           Hq == HG * g.n_kv_heads;
+    return mfma_shape_ok(c) && Hq == HG * c.cfg.n_kv_heads;
 }
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
-    const kvq_cache& c = *a.c;
-    GqaParams p;
-    p.kc = static_cast<const uint32_t*>(c.buf.k_codes);
-    p.ks = static_cast<const uint16_t*>(c.buf.k_scale);
-    p.kz = static_cast<const uint16_t*>(c.buf.k_zero);
-    p.kr = static_cast<const uint16_t*>(c.buf.k_resid);
-    p.vc = static_cast<const uint32_t*>(c.buf.v_codes);
-    p.vs = static_cast<const uint16_t*>(c.buf.v_scale);
-    p.vz = static_cast<const uint16_t*>(c.buf.v_zero);
-    p.q = static_cast<const uint16_t*>(a.q);
-    p.ws_acc = a.ws_acc;
-    p.ws_ml = a.ws_ml;
-    p.Hq = a.Hq;
-    p.Hkv = a.g.Hkv;
-    p.S = a.S;
-    p.S_main = a.S_main;
-    p.ntiles = a.ntiles;
-    p.G = a.g.kG;
-    p.T = a.T;
-    p.nblk = a.nblk;
-    p.cap = a.g.cap;
-    p.nblk_cap = a.g.nblk_cap;
-    p.sigma2 = a.sigma * 1.4426950408889634f;
+    const MfmaParams p = mfma_params(a);
     const dim3 grid(a.S, a.g.Hkv, a.g.B);
     if (a.g.kG == 64)
         hipLaunchKernelGGL(k_decode_gqa<64>, grid, dim3(128), 0, st, p);

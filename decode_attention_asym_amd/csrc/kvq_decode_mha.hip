@@ -1,0 +1,322 @@
+// kvq_decode_mha.hip -- split-K decode attention on MFMA for multi-head
+// caches (one query head per KV head), head dim 128, 2-bit keys (G = 32 or
+// 64) and 2-bit values in 32-channel groups.
+//
+// Method ("Makale Bülteni -- KIVI", section "İddia ve Gerçeklik: KIVI"):
+// logits over the per-channel-quantized keys and the fp16 residual keys,
+// softmax, weighted sum of the per-token-quantized values, with the codes
+// unpacked and dequantized inside this loop.
+//
+// With a single query head both contractions are matrix-vector products, yet
+// the matrix cores still take them more cheaply than the VALU: the 2-bit
+// codes enter v_mfma_f32_16x16x32_f16 exactly as fp16 subnormals (one
+// v_perm_b32 plus one AND per register of two codes, as in the GQA kernel),
+// and the hi/lo halves of the folded scales ride along as extra rows of the
+// A operand at no cost.  The VALU is left with the unpacking, the online
+// softmax and the scale folding.
+//  * keys: q' = q * s_k per (block, channel) as rows hi, lo; the zero term
+//    sum_c q_c z_c is a per-block bias.  The other 14 rows repeat them.
+//  * values: p' = p * s_v per (token, group) as rows (group, hi/lo); of the
+//    16 rows, the 4 of the column's channel half are used.
+//  * online softmax in log2 units with a lazily moved maximum (TAU).
+// Work split and pipelining follow the GQA kernel: one two-wave workgroup
+// per run of 64-token tiles (wave 0 keys + softmax, wave 1 values one tile
+// behind, one workgroup barrier per tile), plus one VALU workgroup for the
+// trailing partial tile and the residual keys.
+#include "kvq_mfma_tiles.h"
+
+namespace kvq {
+namespace {
+
+struct LdsK {
+    uint32_t kl[4 * KSTR];                                  // key codes [word row][channel]
+    __attribute__((aligned(16))) uint32_t qa[2 * 2 * QSTR];  // q' rows [block][hi, lo]
+    __attribute__((aligned(16))) uint32_t ksl[2 * 2 * 64];   // key [scale|zero][block][128 fp16]
+};
+
+struct LdsV {
+    uint32_t vl[8 * VSTR];                               // value codes [word][token]
+    __attribute__((aligned(16))) uint32_t pa[8 * ASTR];   // p' rows [group][hi, lo]
+    __attribute__((aligned(16))) uint32_t vsl[2 * 128];   // value [scale|zero][token][4 fp16]
+};
+
+struct Handoff {
+    __attribute__((aligned(16))) float pl[64];  // softmax weights of the tile's tokens
+    float alpha;                                // rescale of earlier accumulations
+};
+
+struct Lds {
+    LdsK k;
+    LdsV v;
+    Handoff hb[2];
+    float misc[4];
+};
+
+// Key side of one tile: produces p and alpha in `hb`.  m_run is the running
+// maximum (log2 units, wave-uniform); q0, q1 are channels 2*lane, 2*lane+1.
+template <int G>
+__device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, float& m_run, LdsK& L,
+                                         Handoff& hb, float q0, float q1, uint32_t sel, int lane,
+                                         int64_t bh, int nxt, int end) {
+    constexpr int NBT = 64 / G;
+    const int n = lane & 15, kg = lane >> 4;
+
+    // ---- stage key codes and side values, then prefetch tile i + 2
+    stage_keys<G>(cur, L.kl, L.ksl, lane);
+    if (nxt < end) load_ktile<G>(p, bh, nxt, lane, cur);
+    wave_sync();
+
+    // ---- q' = q * s_k as fp16 rows hi, lo; sigma2 * sum_c q z_k per block
+    float bias[NBT];
+#pragma unroll
+    for (int be = 0; be < NBT; ++be) {
+        const uint32_t sw = L.ksl[be * 64 + lane], zw = L.ksl[128 + be * 64 + lane];
+        uint32_t hi, lo;
+        split_prod2(q0, lo_h(sw), q1, hi_h(sw), hi, lo);
+        L.qa[(2 * be) * QSTR + lane] = hi;
+        L.qa[(2 * be + 1) * QSTR + lane] = lo;
+        bias[be] = wave_sum(fmaf(q0, lo_h(zw), q1 * hi_h(zw))) * p.sigma2;
+    }
+    wave_sync();
+
+    // ---- S = q' . codes: 4 MFMA tiles of 16 tokens x 4 K-steps of 32 channels
+    f32x4 S[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) S[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ksx = 0; ksx < 4; ++ksx) {
+#pragma unroll
+        for (int be = 0; be < NBT; ++be) {
+            const uint4 a = *reinterpret_cast<const uint4*>(L.qa + (2 * be + (n & 1)) * QSTR + 16 * ksx + 4 * kg);
+            const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
+            const int r = G == 64 ? (n >> 2) : (2 * be + ((n & 7) >> 2));
+            const uint4* src = reinterpret_cast<const uint4*>(L.kl + r * KSTR + 32 * ksx + 8 * kg);
+            const uint4 w0 = src[0], w1 = src[1];
+            const uint32_t x0 = __builtin_amdgcn_perm(w0.y, w0.x, sel);
+            const uint32_t x1 = __builtin_amdgcn_perm(w0.w, w0.z, sel);
+            const uint32_t x2 = __builtin_amdgcn_perm(w1.y, w1.x, sel);
+            const uint32_t x3 = __builtin_amdgcn_perm(w1.w, w1.z, sel);
+            if (G == 64) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t mk = 0x00030003u << (2 * u);
+                    S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        A, as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), S[u], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    const uint32_t mk = 0x00030003u << (2 * (2 * v + (n >> 3)));
+                    S[2 * be + v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        A, as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), S[2 * be + v], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- softmax.  Result rows 4kg + j hold the hi (j even) and lo (j odd)
+    // partial logits, the same in every lane group kg; lane n has column n of
+    // each of the 4 MFMA tiles.  G = 64: tile u, column n is token 4n + u.
+    // G = 32: tile 2be + v, column n is token
+    // 32be + 16((n & 7) >> 2) + 4(n & 3) + 2v + (n >> 3).
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int up = G == 64 ? i : 2 * (i & 1) + (n >> 3);   // code position in the byte
+        const float f = p.sigma2 * __builtin_ldexpf(1.0f, 24 - 2 * up);
+        x[i] = fmaf(S[i][0] + S[i][1], f, bias[G == 64 ? 0 : (i >> 1)]);
+    }
+    const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    float alpha = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {
+        const float mnew = fmaxf(m_run, readlane_f(row_max16(mx), 0));
+        alpha = fast_exp2(m_run - mnew);
+        m_run = mnew;
+    }
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(x[i] - m_run);
+    if (kg == 0) {
+        if (G == 64) {
+            *reinterpret_cast<float4*>(hb.pl + 4 * n) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        } else {
+            const int t = 16 * ((n & 7) >> 2) + 4 * (n & 3) + (n >> 3);
+            hb.pl[t] = pv[0];
+            hb.pl[t + 2] = pv[1];
+            hb.pl[t + 32] = pv[2];
+            hb.pl[t + 34] = pv[3];
+        }
+    }
+    if (lane == 0) hb.alpha = alpha;
+}
+
+struct VState {
+    f32x4 O[2][4];   // PV accumulators [channel half][code position]
+    float lsum;      // this lane's share of sum p
+    float vb0, vb1;  // this lane's share of sum p z_v, groups 2gp and 2gp + 1
+};
+
+// Value side of one tile, reading p and alpha from `hb`.
+__device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VState& st, LdsV& L,
+                                           const Handoff& hb, uint32_t sel, int lane, int64_t bh,
+                                           int nxt, int end) {
+    const int n = lane & 15, kg = lane >> 4;
+    // ---- stage value codes and side values, then prefetch tile i + 2
+    stage_values(cur, L.vl, L.vsl, lane);
+    if (nxt < end) load_vtile(p, bh, nxt, lane, cur);
+
+    // ---- rescale what was accumulated with the previous maximum
+    const float alpha = hb.alpha;
+    if (alpha < 1.0f) {
+#pragma unroll
+        for (int P = 0; P < 2; ++P)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) st.O[P][u] *= alpha;
+        st.lsum *= alpha;
+        st.vb0 *= alpha;
+        st.vb1 *= alpha;
+    }
+    wave_sync();
+
+    // ---- p' = p * s_v as fp16 rows (group, hi/lo); sum_t p, sum_t p z_v.
+    // Lane (tp, gp): tokens 2tp, 2tp + 1 and groups 2gp, 2gp + 1.
+    {
+        const int tp = lane & 31, gp = lane >> 5;
+        const float2 pp = *reinterpret_cast<const float2*>(hb.pl + 2 * tp);
+        // dword 2t + gp of a side row holds groups 2gp (low half), 2gp + 1 of token t
+        const uint32_t s0 = L.vsl[4 * tp + gp], s1 = L.vsl[4 * tp + 2 + gp];
+        const uint32_t z0 = L.vsl[128 + 4 * tp + gp], z1 = L.vsl[128 + 4 * tp + 2 + gp];
+        uint32_t h, l;
+        split_prod2(pp.x, lo_h(s0), pp.y, lo_h(s1), h, l);
+        L.pa[(4 * gp) * ASTR + tp] = h;
+        L.pa[(4 * gp + 1) * ASTR + tp] = l;
+        split_prod2(pp.x, hi_h(s0), pp.y, hi_h(s1), h, l);
+        L.pa[(4 * gp + 2) * ASTR + tp] = h;
+        L.pa[(4 * gp + 3) * ASTR + tp] = l;
+        st.lsum += gp == 0 ? pp.x + pp.y : 0.0f;
+        st.vb0 = fmaf(pp.y, lo_h(z1), fmaf(pp.x, lo_h(z0), st.vb0));
+        st.vb1 = fmaf(pp.y, hi_h(z1), fmaf(pp.x, hi_h(z0), st.vb1));
+    }
+    wave_sync();
+
+    // ---- O += p' . codes: 2 channel halves x 4 code positions x 2 K-steps of
+    // 32 tokens.  A row n holds group 2P + ((n >> 1) & 1), hi (n even) / lo.
+#pragma unroll
+    for (int P = 0; P < 2; ++P) {
+        const int wi = 4 * P + 2 * (n >> 3) + ((n & 7) >> 2);
+        const int row = 4 * P + (n & 3);
+#pragma unroll
+        for (int ksx = 0; ksx < 2; ++ksx) {
+            const uint4 a = *reinterpret_cast<const uint4*>(L.pa + row * ASTR + 16 * ksx + 4 * kg);
+            const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
+            const uint4* src = reinterpret_cast<const uint4*>(L.vl + wi * VSTR + 32 * ksx + 8 * kg);
+            const uint4 w0 = src[0], w1 = src[1];
+            const uint32_t x0 = __builtin_amdgcn_perm(w0.y, w0.x, sel);
+            const uint32_t x1 = __builtin_amdgcn_perm(w0.w, w0.z, sel);
+            const uint32_t x2 = __builtin_amdgcn_perm(w1.y, w1.x, sel);
+            const uint32_t x3 = __builtin_amdgcn_perm(w1.w, w1.z, sel);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t mk = 0x00030003u << (2 * u);
+                st.O[P][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    A, as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), st.O[P][u], 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
+    __shared__ Lds L;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n = lane & 15, kg = lane >> 4;
+    const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int64_t bh = int64_t(b) * p.Hkv + kvh;
+    const int64_t slot = (int64_t(b) * p.Hq + kvh) * p.S + s;
+    if (s >= p.S_main) {
+        if (wave == 0) tail_split<1>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), L.hb[0].pl);
+        return;
+    }
+    const int t_lo = int(int64_t(s) * p.ntiles / p.S_main);
+    const int t_hi = int(int64_t(s + 1) * p.ntiles / p.S_main);
+    const int ntl = t_hi - t_lo;
+    const uint32_t sel = perm_selector(n);
+
+    if (wave == 0) {
+        const uint32_t qw = reinterpret_cast<const uint32_t*>(p.q + (int64_t(b) * p.Hq + kvh) * D)[lane];
+        const float q0 = lo_h(qw), q1 = hi_h(qw);
+        float m_run = -INFINITY;
+        // two register tiles in flight: tile t is staged from set (t & 1),
+        // which then receives tile t + 2
+        KTile ta, tb;
+        load_ktile<G>(p, bh, t_lo, lane, ta);
+        if (ntl > 1) load_ktile<G>(p, bh, t_lo + 1, lane, tb);
+        for (int it = 0; it <= ntl; it += 2) {
+            if (it < ntl) key_tile<G>(p, ta, m_run, L.k, L.hb[0], q0, q1, sel, lane, bh, t_lo + it + 2, t_hi);
+            if (it == ntl && lane == 0) L.misc[0] = m_run;
+            __syncthreads();
+            if (it + 1 > ntl) break;
+            if (it + 1 < ntl) key_tile<G>(p, tb, m_run, L.k, L.hb[1], q0, q1, sel, lane, bh, t_lo + it + 3, t_hi);
+            if (it + 1 == ntl && lane == 0) L.misc[0] = m_run;
+            __syncthreads();
+        }
+    } else {
+        VState st;
+        st.lsum = st.vb0 = st.vb1 = 0.0f;
+#pragma unroll
+        for (int P = 0; P < 2; ++P)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) st.O[P][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // value work trails the key work by one tile (tile it - 1 at step it)
+        VTile ta, tb;
+        load_vtile(p, bh, t_lo, lane, ta);
+        if (ntl > 1) load_vtile(p, bh, t_lo + 1, lane, tb);
+        for (int it = 0; it <= ntl; it += 2) {
+            if (it >= 1) value_tile(p, tb, st, L.v, L.hb[1], sel, lane, bh, t_lo + it + 1, t_hi);
+            __syncthreads();
+            if (it + 1 > ntl) break;
+            value_tile(p, ta, st, L.v, L.hb[0], sel, lane, bh, t_lo + it + 2, t_hi);
+            __syncthreads();
+        }
+        // ---- epilogue: l and the value-zero sums over the wave
+        const float lsum = wave_sum(st.lsum);
+        const float r0 = row_sum16(st.vb0), r1 = row_sum16(st.vb1);
+        // lanes 0..31 hold groups 0, 1; lanes 32..63 groups 2, 3
+        const float vz0 = readlane_f(r0, 0) + readlane_f(r0, 16), vz1 = readlane_f(r1, 0) + readlane_f(r1, 16);
+        const float vz2 = readlane_f(r0, 32) + readlane_f(r0, 48), vz3 = readlane_f(r1, 32) + readlane_f(r1, 48);
+        if (kg == 0) {
+            const bool up = (n >> 3) != 0;   // the column's group within the channel half
+            // (scalar selects: an indexed array here would be lowered to scratch)
+            const float zb0 = up ? vz1 : vz0, zb1 = up ? vz3 : vz2;
+#pragma unroll
+            for (int P = 0; P < 2; ++P)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int c = 64 * P + 32 * (n >> 3) + 4 * (n & 7) + u;
+                    const float hi = up ? st.O[P][u][2] : st.O[P][u][0];
+                    const float lo = up ? st.O[P][u][3] : st.O[P][u][1];
+                    p.ws_acc[slot * D + c] = fmaf(hi + lo, __builtin_ldexpf(1.0f, 24 - 2 * u), P ? zb1 : zb0);
+                }
+        }
+        if (lane == 0) {
+            p.ws_ml[slot * 2] = L.misc[0];
+            p.ws_ml[slot * 2 + 1] = lsum;
+        }
+    }
+}
+
+}  // namespace
+
+bool mha_supported(const kvq_cache& c, int Hq) { return mfma_shape_ok(c) && Hq == c.cfg.n_kv_heads; }
+
+hipError_t launch_decode_mha(const DecodeArgs& a, hipStream_t st) {
+    const MfmaParams p = mfma_params(a);
+    const dim3 grid(a.S, a.g.Hkv, a.g.B);
+    if (a.g.kG == 64)
+        hipLaunchKernelGGL(k_decode_mha<64>, grid, dim3(128), 0, st, p);
+    else
+        hipLaunchKernelGGL(k_decode_mha<32>, grid, dim3(128), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

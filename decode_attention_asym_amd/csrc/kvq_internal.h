@@ -78,8 +78,10 @@ SplitPlan plan_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64
 int max_slots(const kvq_cache& c, int Hq, int n_splits, Variant v);
 
 bool gqa_supported(const kvq_cache& c, int Hq);
+bool mha_supported(const kvq_cache& c, int Hq);
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_mha(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace kvq

@@ -5,13 +5,14 @@ namespace kvq {
 
 Variant pick_variant(const kvq_cache& c, int Hq) {
     if (gqa_supported(c, Hq)) return V_GQA;
+    if (mha_supported(c, Hq)) return V_MHA;
     return V_GENERIC;
 }
 
 const char* variant_name(Variant v) {
     switch (v) {
         case V_GENERIC: return "generic";
-        case V_MHA: return "mha_valu";
+        case V_MHA: return "mha_mfma";
         case V_GQA: return "gqa_mfma";
         case V_MLA: return "mla_mfma";
     }
@@ -25,9 +26,11 @@ int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > h
 // Automatic split count: enough workgroups to fill 256 CUs several times
 // over.  It does not depend on T, so the slot bound below covers every T.
 int64_t auto_main(const kvq_cache& c, int Hq, Variant v) {
-    const int64_t units = v == V_GQA ? int64_t(c.cfg.batch) * c.cfg.n_kv_heads
-                                     : int64_t(c.cfg.batch) * Hq;
-    const int64_t target = v == V_GQA ? 3072 : 2048;
+    const bool tiled = v == V_GQA || v == V_MHA;
+    const int64_t units = tiled ? int64_t(c.cfg.batch) * c.cfg.n_kv_heads : int64_t(c.cfg.batch) * Hq;
+    // measured on MI355X: about 12 tiles per two-wave workgroup suit the MHA
+    // kernel (64 tiles per sequence at 4K tokens), 6 waves per SIMD the GQA one
+    const int64_t target = v == V_MHA ? 1536 : tiled ? 3072 : 2048;
     return clamp64((target + units - 1) / units, 1, KVQ_MAX_SPLITS);
 }
 
@@ -37,7 +40,7 @@ SplitPlan plan_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64
     SplitPlan sp;
     const int64_t G = c.cfg.key.group;
     const int64_t want = n_splits > 0 ? n_splits : auto_main(c, Hq, v);
-    if (v == V_GQA) {
+    if (v == V_GQA || v == V_MHA) {
         // whole 64-token tiles of quantized keys, then a tail slot for the rest
         const int64_t ntiles = nblk * G / 64;
         sp.ntiles = int(ntiles);
@@ -56,7 +59,7 @@ SplitPlan plan_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64
 
 int max_slots(const kvq_cache& c, int Hq, int n_splits, Variant v) {
     const int64_t want = n_splits > 0 ? n_splits : auto_main(c, Hq, v);
-    if (v == V_GQA) return int(clamp64(want, 1, KVQ_MAX_SPLITS - 1) + 1);
+    if (v == V_GQA || v == V_MHA) return int(clamp64(want, 1, KVQ_MAX_SPLITS - 1) + 1);
     return int(want);
 }
 

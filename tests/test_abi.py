@@ -142,7 +142,7 @@ def test_decode_validation_before_hip():
         with pytest.raises(kvq.KvqError) as e:                # empty cache
             kvq.kv_decode_attention(h, 0x1000, 8, 1.0, 0, 0x2000, 0x3000, ws)
         assert e.value.status == -8
-        assert kvq.kv_decode_variant(h, 8) in ("generic", "mha_valu", "gqa_mfma", "mla_mfma")
+        assert kvq.kv_decode_variant(h, 8) in ("generic", "mha_mfma", "gqa_mfma", "mla_mfma")
     finally:
         kvq.kv_cache_destroy(h)
 
@@ -157,3 +157,21 @@ def test_timing_hook_arguments():
     with pytest.raises(kvq.KvqError):
         kvq.kv_set_timing_events(0x10, None)
     kvq.kv_set_timing_events(None, None)
+
+
+@pytest.mark.parametrize("name,variant", [
+    ("tiny_mha_d64_t250", "generic"),
+    ("llama2_7b_layer_mha_t4096", "mha_mfma"),
+    ("mistral_7b_gqa_t32805", "gqa_mfma"),
+    ("longctx_gqa_t131072", "gqa_mfma"),
+    ("mla_absorbed_b64_t16384", "generic"),
+])
+def test_variant_per_workload(name, variant):
+    """Which decode kernel each workload reaches (host-side choice)."""
+    from decode_attention_asym_amd import configs
+    w = configs.BY_NAME[name]
+    h = kvq.kv_cache_init(kvq.cfg_for(w, w.capacity()), kvq.CacheBuffers(*FAKE))
+    try:
+        assert kvq.kv_decode_variant(h, w.n_q_heads) == variant
+    finally:
+        kvq.kv_cache_destroy(h)

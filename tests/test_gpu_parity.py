@@ -91,11 +91,25 @@ def _check_decode(orc, w, dc, k, v, n_splits=0, kq_blocks=None):
     return got
 
 
-@pytest.mark.parametrize("T", [1, 15, 31, 32, 33, 101, 3 * 64 + 5, 700])
-@pytest.mark.parametrize("shape", ["mha", "gqa4", "gqa8_g64", "mla"])
-def test_edge_lengths(orc, T, shape):
+def _shape(shape, T):
+    """Small caches that reach each decode kernel: generic (D = 64, 8-way
+    GQA, MLA), the MHA and GQA MFMA kernels (D = 128) with both G."""
     if shape == "mha":
-        w = _tiny(T, Hq=2, Hkv=2)
+        return _tiny(T, Hq=2, Hkv=2)
+    if shape == "mha128_g32":
+        return _tiny(T, Hq=2, Hkv=2, D=128, G=32)
+    if shape == "mha128_g64":
+        return _tiny(T, Hq=2, Hkv=2, D=128, G=64)
+    if shape == "gqa4_g64":
+        return _tiny(T, Hq=8, Hkv=2, D=128, G=64)
+    raise KeyError(shape)
+
+
+@pytest.mark.parametrize("T", [1, 15, 31, 32, 33, 101, 3 * 64 + 5, 700])
+@pytest.mark.parametrize("shape", ["mha", "mha128_g32", "mha128_g64", "gqa4", "gqa8_g64", "mla"])
+def test_edge_lengths(orc, T, shape):
+    if shape in ("mha", "mha128_g32", "mha128_g64"):
+        w = _shape(shape, T)
     elif shape == "gqa4":
         w = _tiny(T, Hq=8, Hkv=2, D=128)
     elif shape == "gqa8_g64":
@@ -114,8 +128,9 @@ def test_edge_lengths(orc, T, shape):
 
 
 @pytest.mark.parametrize("n_splits", [1, 2, 3, 7, 64, 256])
-def test_split_counts(orc, n_splits):
-    w = _tiny(1000, Hq=8, Hkv=2, D=128, G=32)
+@pytest.mark.parametrize("shape", ["gqa4", "mha128_g32"])
+def test_split_counts(orc, n_splits, shape):
+    w = _tiny(1000, Hq=8, Hkv=2, D=128, G=32) if shape == "gqa4" else _shape(shape, 1000)
     cap = w.capacity()
     k, v = synth.keys(w), synth.values(w)
     dc = new_cache(w, cap)
@@ -178,6 +193,25 @@ def test_unflushed_full_residual(orc):
         dc.append(dev_f16(k[:, :, :1]), dev_f16(v[:, :, :1]), kvq.KVQ_APPEND_NO_AUTOFLUSH)
     assert dc.flush() == 1 and dc.state() == (96, 0)
     _check_decode(orc, w, dc, k, v)
+
+
+@pytest.mark.parametrize("shape", ["gqa4_g32", "mha128_g32", "gqa4_g64", "mha128_g64"])
+def test_unflushed_full_residual_mfma(orc, shape):
+    """MFMA kernels: the VALU tail then holds the longest it can, a whole
+    quantized block plus a full residual (G = 32), or a full residual of 64
+    keys (G = 64)."""
+    G = 32 if shape.endswith("g32") else 64
+    nq = 3 * 32 if G == 32 else 2 * 64          # quantized tokens, odd block count for G = 32
+    T = nq + G
+    w = _tiny(T, Hq=8, Hkv=2, D=128, G=G) if shape.startswith("gqa4") else _shape(shape, T)
+    cap = w.capacity(G)
+    k, v = synth.keys(w), synth.values(w)
+    dc = new_cache(w, cap)
+    dc.append(dev_f16(k[:, :, :nq]), dev_f16(v[:, :, :nq]))
+    dc.append(dev_f16(k[:, :, nq:]), dev_f16(v[:, :, nq:]), kvq.KVQ_APPEND_NO_AUTOFLUSH)
+    assert dc.state() == (T, G)
+    log(f"[{shape}] variant {dc.variant(w.n_q_heads)}")
+    _check_decode(orc, w, dc, k, v, kq_blocks=nq // G)
 
 
 @pytest.mark.parametrize("kbits,vbits,G", [(4, 4, 32), (4, 2, 64), (2, 4, 16), (2, 2, 128), (4, 4, 16)])
