@@ -1,34 +1,58 @@
 """Build libkvq.so (all HIP kernels + the C-ABI host code) for gfx950, in-tree."""
 from __future__ import annotations
 
+import concurrent.futures as cf
 import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kvq_api.cpp", "kvq_plan.cpp", "kvq_quant.hip", "kvq_decode_generic.hip",
-           "kvq_decode_gqa.hip", "kvq_decode_mha.hip"]
-
-FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+COMMON = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-function",
     # packed fp32 VALU forms stay off (only scalar / non-packed fp32 code)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-gpu-flush-denormals-to-zero",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
-    # MFMA accumulators in VGPRs (no AGPR copies around VALU work on them)
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
+# MFMA accumulators in VGPRs (no AGPR copies around VALU work on them): for
+# kernels whose accumulators fit next to everything else in 256 VGPRs
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+
+# source -> extra flags (the MLA kernel keeps its 256 accumulators in AGPRs)
+SOURCES = {
+    "kvq_api.cpp": VGPR_FORM,
+    "kvq_plan.cpp": VGPR_FORM,
+    "kvq_quant.hip": VGPR_FORM,
+    "kvq_decode_generic.hip": VGPR_FORM,
+    "kvq_decode_gqa.hip": VGPR_FORM,
+    "kvq_decode_mha.hip": VGPR_FORM,
+    "kvq_decode_mla.hip": [],
+}
+FLAGS = COMMON + VGPR_FORM   # kept for tools that print the main flag set
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [HIPCC, *COMMON, *SOURCES[src], *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True, cwd=CSRC)
+    return obj
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into libkvq.so (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every source and link libkvq.so (always recompiles)."""
+    os.makedirs(OBJ, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True, cwd=CSRC)

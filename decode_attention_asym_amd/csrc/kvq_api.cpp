@@ -238,6 +238,7 @@ kvq_status kv_decode_attention(const kvq_cache* c, const void* q, int32_t Hq, fl
     switch (v) {
         case V_GQA: e = launch_decode_gqa(a, st); break;
         case V_MHA: e = launch_decode_mha(a, st); break;
+        case V_MLA: e = launch_decode_mla(a, st); break;
         default: e = launch_decode_generic(a, st); break;
     }
     if (e != hipSuccess) return KVQ_E_HIP;

@@ -55,7 +55,7 @@ struct DecodeArgs {
     const void* q;
     int Hq, S;          // query heads, partial slots (main splits + tail slot)
     int S_main;         // splits over whole tiles (variants with a tail slot)
-    int ntiles;         // whole 64-token tiles (MFMA variants)
+    int ntiles;         // whole 64-token tiles (KIVI MFMA variants); 16-token tiles (MLA)
     float sigma;
     void* out;
     float* ws_acc;      // [B][Hq][S][vd]
@@ -79,9 +79,11 @@ int max_slots(const kvq_cache& c, int Hq, int n_splits, Variant v);
 
 bool gqa_supported(const kvq_cache& c, int Hq);
 bool mha_supported(const kvq_cache& c, int Hq);
+bool mla_supported(const kvq_cache& c, int Hq);
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_mha(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace kvq

@@ -6,6 +6,7 @@ namespace kvq {
 Variant pick_variant(const kvq_cache& c, int Hq) {
     if (gqa_supported(c, Hq)) return V_GQA;
     if (mha_supported(c, Hq)) return V_MHA;
+    if (mla_supported(c, Hq)) return V_MLA;
     return V_GENERIC;
 }
 
@@ -26,6 +27,8 @@ int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > h
 // Automatic split count: enough workgroups to fill 256 CUs several times
 // over.  It does not depend on T, so the slot bound below covers every T.
 int64_t auto_main(const kvq_cache& c, int Hq, Variant v) {
+    // MLA: one four-wave workgroup per CU, Hq / 64 of them per sequence and split
+    if (v == V_MLA) return clamp64((256 * 64 / Hq + c.cfg.batch - 1) / c.cfg.batch, 1, KVQ_MAX_SPLITS);
     const bool tiled = v == V_GQA || v == V_MHA;
     const int64_t units = tiled ? int64_t(c.cfg.batch) * c.cfg.n_kv_heads : int64_t(c.cfg.batch) * Hq;
     // measured on MI355X: about 12 tiles per two-wave workgroup suit the MHA
@@ -47,6 +50,14 @@ SplitPlan plan_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64
         // the merge pass reads at most KVQ_MAX_SPLITS slots, tail slot included
         sp.S_main = int(clamp64(clamp64(want, 0, KVQ_MAX_SPLITS - 1), 0, ntiles));
         sp.S = sp.S_main + (T > ntiles * 64 ? 1 : 0);
+        return sp;
+    }
+    if (v == V_MLA) {
+        // 16-token tiles over every token; the RoPE residual is read in place
+        const int64_t ntiles = (T + 15) / 16;
+        sp.ntiles = int(ntiles);
+        sp.S_main = int(clamp64(want, 1, ntiles));
+        sp.S = sp.S_main;
         return sp;
     }
     const int64_t R = T - nblk * G;

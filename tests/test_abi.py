@@ -164,7 +164,7 @@ def test_timing_hook_arguments():
     ("llama2_7b_layer_mha_t4096", "mha_mfma"),
     ("mistral_7b_gqa_t32805", "gqa_mfma"),
     ("longctx_gqa_t131072", "gqa_mfma"),
-    ("mla_absorbed_b64_t16384", "generic"),
+    ("mla_absorbed_b64_t16384", "mla_mfma"),
 ])
 def test_variant_per_workload(name, variant):
     """Which decode kernel each workload reaches (host-side choice)."""

@@ -102,13 +102,18 @@ def _shape(shape, T):
         return _tiny(T, Hq=2, Hkv=2, D=128, G=64)
     if shape == "gqa4_g64":
         return _tiny(T, Hq=8, Hkv=2, D=128, G=64)
+    if shape == "mla64":
+        return _mla_tiny(T, Hq=64)
+    if shape == "mla128":
+        return _mla_tiny(T, Hq=128, B=1)
     raise KeyError(shape)
 
 
 @pytest.mark.parametrize("T", [1, 15, 31, 32, 33, 101, 3 * 64 + 5, 700])
-@pytest.mark.parametrize("shape", ["mha", "mha128_g32", "mha128_g64", "gqa4", "gqa8_g64", "mla"])
+@pytest.mark.parametrize("shape", ["mha", "mha128_g32", "mha128_g64", "gqa4", "gqa8_g64", "mla", "mla64",
+                                   "mla128"])
 def test_edge_lengths(orc, T, shape):
-    if shape in ("mha", "mha128_g32", "mha128_g64"):
+    if shape in ("mha", "mha128_g32", "mha128_g64", "mla64", "mla128"):
         w = _shape(shape, T)
     elif shape == "gqa4":
         w = _tiny(T, Hq=8, Hkv=2, D=128)
@@ -128,7 +133,7 @@ def test_edge_lengths(orc, T, shape):
 
 
 @pytest.mark.parametrize("n_splits", [1, 2, 3, 7, 64, 256])
-@pytest.mark.parametrize("shape", ["gqa4", "mha128_g32"])
+@pytest.mark.parametrize("shape", ["gqa4", "mha128_g32", "mla64"])
 def test_split_counts(orc, n_splits, shape):
     w = _tiny(1000, Hq=8, Hkv=2, D=128, G=32) if shape == "gqa4" else _shape(shape, 1000)
     cap = w.capacity()
@@ -195,15 +200,16 @@ def test_unflushed_full_residual(orc):
     _check_decode(orc, w, dc, k, v)
 
 
-@pytest.mark.parametrize("shape", ["gqa4_g32", "mha128_g32", "gqa4_g64", "mha128_g64"])
+@pytest.mark.parametrize("shape", ["gqa4_g32", "mha128_g32", "gqa4_g64", "mha128_g64", "mla64"])
 def test_unflushed_full_residual_mfma(orc, shape):
-    """MFMA kernels: the VALU tail then holds the longest it can, a whole
+    """MFMA kernels: the KIVI tail then holds the longest it can, a whole
     quantized block plus a full residual (G = 32), or a full residual of 64
-    keys (G = 64)."""
+    keys (G = 64); the MLA kernel reads a full 64-key RoPE residual."""
     G = 32 if shape.endswith("g32") else 64
     nq = 3 * 32 if G == 32 else 2 * 64          # quantized tokens, odd block count for G = 32
     T = nq + G
     w = _tiny(T, Hq=8, Hkv=2, D=128, G=G) if shape.startswith("gqa4") else _shape(shape, T)
+    assert w.kG == G
     cap = w.capacity(G)
     k, v = synth.keys(w), synth.values(w)
     dc = new_cache(w, cap)
