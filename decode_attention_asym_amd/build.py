@@ -23,7 +23,7 @@ COMMON = [
 # kernels whose accumulators fit next to everything else in 256 VGPRs
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
-# source -> extra flags (the MLA kernel keeps its 256 accumulators in AGPRs)
+# source -> extra flags
 SOURCES = {
     "kvq_api.cpp": VGPR_FORM,
     "kvq_plan.cpp": VGPR_FORM,
@@ -31,7 +31,7 @@ SOURCES = {
     "kvq_decode_generic.hip": VGPR_FORM,
     "kvq_decode_gqa.hip": VGPR_FORM,
     "kvq_decode_mha.hip": VGPR_FORM,
-    "kvq_decode_mla.hip": [],
+    "kvq_decode_mla.hip": VGPR_FORM,
 }
 FLAGS = COMMON + VGPR_FORM   # kept for tools that print the main flag set
 

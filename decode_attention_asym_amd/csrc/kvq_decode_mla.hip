@@ -13,22 +13,28 @@
 // content quantizer and per-channel key quantizer are KIVI's ("Makale
 // Bülteni -- KIVI", section "İddia ve Gerçeklik: KIVI").
 //
-// Every content element is reused by the 64 query heads of a workgroup, so
-// it is dequantized once per workgroup and both contractions run on the
-// matrix cores (128 heads take two workgroups):
-//  * wave w owns latent channels [128w, 128w + 128).  Per 16-token tile it
-//    dequantizes them (codes as exact fp16 integers via an exponent trick:
-//    (bits & mask) | exponent(2^(10-2u)) is 2^(10-2u) + code), computing
-//    c_hat = code * s + z with one fused fp16 FMA (the correctly rounded hi)
-//    and the remainder c_hat - hi in fp32 (lo);
-//  * QK^T: wave w takes 16 of the group's query heads over all 512 channels, reading the token-major hi copy of the whole tile from LDS
-//    (v_mfma_f32_16x16x32_f16; Q stays in registers).  The RoPE term uses
-//    exact 4-bit code operands (fp16 subnormals) against q' = q_r * s_k in
-//    hi/lo rows plus the bias sum_c q_r z_k, or the fp16 residual keys;
-//  * online softmax per head in log2 units (lazily moved maxima); the
-//    weights go to LDS in fp16 and the row sums add up the same fp16 values;
-//  * PV: O[heads][own channels] += P . (hi + lo) on v_mfma_f32_32x32x16_f16,
-//    the accumulators in AGPRs.
+// One workgroup of 8 waves (two per SIMD) takes 64 query heads of one
+// sequence over a run of 16-token tiles; 128 heads take two workgroups.
+// Wave w owns latent channels [64w, 64w + 64) and does all the work on
+// them, so every content element is dequantized once per workgroup:
+//  * dequant: codes become exact fp16 integers by an exponent trick
+//    ((bits & mask) | exponent of 2^(10-2u) is 2^(10-2u) + code);
+//    c_hat = code * s + z is one fused fp16 FMA (the correctly rounded hi)
+//    plus the fp32 remainder c_hat - hi (lo);
+//  * QK^T: partial logits of all 64 heads over the wave's own channels
+//    (v_mfma_f32_16x16x32_f16, Q in registers, the hi tile transposed to
+//    token-major through a wave-private LDS block); the RoPE term of one
+//    (16-head, 32-channel) block per wave uses exact 4-bit code operands
+//    (fp16 subnormals) against q' = q_r * s_k in hi/lo rows plus the bias
+//    sum_c q_r z_k, or the fp16 residual keys;
+//  * softmax: wave w sums the 8 partials of heads [8w, 8w + 8), runs the
+//    online softmax in log2 units (lazily moved maxima) and writes fp16
+//    weights; the row sums add up the same fp16 values;
+//  * PV: O[64 heads][own channels] += P . (hi + lo) on
+//    v_mfma_f32_32x32x16_f16.
+// Three tiles are in flight: a step does PV of tile i-2, the softmax of tile
+// i-1 and dequant + QK^T of tile i, with one workgroup barrier, so the matrix
+// work of one wave overlaps the vector work of the other.
 // Tokens at or past T in the last tile get zero weight; their codes are read
 // (they lie inside the caller's capacity) but never contribute.
 #include <hip/hip_fp16.h>
@@ -49,7 +55,10 @@ constexpr int VD = 512;      // content latent dim
 constexpr int KD = 64;       // RoPE dim
 constexpr int QD = VD + KD;  // query row
 constexpr int GR = 64;       // RoPE key block (tokens)
-constexpr int CHS = 260;     // dwords per token row of the hi tile (512 fp16 + pad)
+constexpr int HQ = 64;       // query heads per workgroup
+constexpr int NW = 8;        // waves per workgroup
+constexpr int CWS = 36;      // dwords per token row of a wave's hi block (64 fp16 + pad)
+constexpr int SXS = 68;      // floats per token row of a partial-logit block (64 heads + pad)
 constexpr int RCS = 68;      // dwords per word row of the RoPE code block (64 + pad)
 constexpr int QRS = 36;      // dwords per head row of q' (64 fp16 + pad)
 constexpr int PS = 12;       // dwords per head row of P (16 fp16 + pad)
@@ -65,22 +74,24 @@ struct MlaParams {
     int Hq, S, ntiles;           // ntiles = ceil(T / 16)
     int64_t T, nblk, cap, nblk_cap;
     float sigma2;                // softmax scale * log2(e)
+    float neg1;                  // -1, kept opaque so c*s + z - hi stays one mixed FMA
 };
 
-template <int HQ>
 struct Lds {
-    uint32_t chi[16 * CHS];                        // content hi, token-major [token][512 fp16]
-    uint32_t cst[4][8 * 16];                       // per wave: content codes [word][token]
-    uint32_t sst[4][2 * 4 * 8];                    // per wave: content [scale|zero][group][16 fp16]
-    uint32_t rc[8 * RCS];                          // RoPE codes of the block [word][channel]
-    uint32_t rs[2 * 32];                           // RoPE [scale|zero][64 fp16]
-    __attribute__((aligned(16))) uint32_t qr[HQ * 32];     // q_r fp16 [head][64]
-    __attribute__((aligned(16))) uint32_t qrh[HQ * QRS];   // q' = q_r * s_k, hi [head][64 fp16]
-    __attribute__((aligned(16))) uint32_t qrl[HQ * QRS];   // lo
-    float rbp[256 / HQ][HQ];                       // partial sums q_r . z_k [channel chunk][head]
-    __attribute__((aligned(16))) uint32_t pm[HQ * PS];     // weights fp16 [head][16 tokens]
-    float alpha[HQ];                               // rescale factors of this tile
-    int wflag[4];                                  // wave w moved some maxima this tile
+    __attribute__((aligned(16))) float sx[2][NW][16 * SXS];  // partial logits [buf][wave][token][head]
+    __attribute__((aligned(16))) float srx[2][NW][16 * 20];  // RoPE partials [buf][wave][token][16 heads]
+    __attribute__((aligned(16))) uint32_t chw[NW][16 * CWS]; // per wave: hi, token-major [token][64 fp16]
+    __attribute__((aligned(16))) uint32_t cst[NW][4 * 16];   // per wave: content codes [word][token]
+    __attribute__((aligned(16))) uint32_t sst[NW][2 * 2 * 8];  // per wave: [scale|zero][group][16 fp16]
+    __attribute__((aligned(16))) uint32_t pm[2][HQ * PS];    // weights fp16 [buf][head][16 tokens]
+    __attribute__((aligned(16))) uint32_t rc[8 * RCS];       // RoPE codes of the block [word][channel]
+    uint32_t rs[2 * 32];                                     // RoPE [scale|zero][64 fp16]
+    __attribute__((aligned(16))) uint32_t qr[HQ * 32];       // q_r fp16 [head][64]
+    __attribute__((aligned(16))) uint32_t qrh[HQ * QRS];     // q' = q_r * s_k, hi [head][64 fp16]
+    __attribute__((aligned(16))) uint32_t qrl[HQ * QRS];     // lo
+    float rbias[HQ];                                         // RoPE zero bias of the block per head
+    float alpha[2][HQ];                                      // rescale factors [buf][head]
+    __attribute__((aligned(16))) int wflag[2][NW];           // softmax wave w moved some maxima
 };
 
 __device__ __forceinline__ float lo_h(uint32_t w) { return float(__builtin_bit_cast(f16x2, w)[0]); }
@@ -125,150 +136,156 @@ __device__ __forceinline__ uint32_t byte_pair_sel(int k) {
     return uint32_t(k) | (0x0cu << 8) | ((4u + uint32_t(k)) << 16) | (0x0cu << 24);
 }
 
-// fp16 pair c_hat = code * s + z, rounded once (fused), and its fp32 remainder.
-// `h` holds (2^(10-2u) + code) in each half, `bias2` the pair (-2^(10-2u)).
+// fp16 pair c_hat = code * s + z, rounded once (fused), and its remainder.
+// `h` holds (2^(10-2u) + code) in each half, `bias2` the pair -2^(10-2u).
 __device__ __forceinline__ void dequant_pair(uint32_t h, uint32_t bias2, uint32_t s, uint32_t z,
-                                             uint32_t& hi, uint32_t& lo) {
+                                             float neg1, uint32_t& hi, uint32_t& lo) {
     const f16x2 c = __builtin_bit_cast(f16x2, h) + __builtin_bit_cast(f16x2, bias2);  // exact codes
     const f16x2 sv = __builtin_bit_cast(f16x2, s), zv = __builtin_bit_cast(f16x2, z);
     const f16x2 hv = __builtin_elementwise_fma(c, sv, zv);
     hi = __builtin_bit_cast(uint32_t, hv);
+    // c*s + z in fp32 (one rounding), minus hi (exact): both fp16-operand FMAs
     const float d0 = fmaf(float(c[0]), float(sv[0]), float(zv[0]));
     const float d1 = fmaf(float(c[1]), float(sv[1]), float(zv[1]));
-    lo = pk_rtz(d0 - float(hv[0]), d1 - float(hv[1]));
+    const f16x2 lv = {_Float16(fmaf(float(hv[0]), neg1, d0)), _Float16(fmaf(float(hv[1]), neg1, d1))};
+    lo = __builtin_bit_cast(uint32_t, lv);
 }
 
-template <int HQ>
-__global__ __launch_bounds__(256) void k_decode_mla(MlaParams p) {
-    constexpr int QM = HQ / 64;      // 16-head MFMA rows per wave in QK^T
-    constexpr int PM = HQ / 32;      // 32-head MFMA rows in PV
-    constexpr int HW = HQ / 4;       // query heads per wave in QK^T
-    constexpr int NC = 256 / HQ;     // RoPE channel chunks when forming q' (one head per thread)
-    constexpr int CW = KD / NC;      // channels per chunk
-    __shared__ Lds<HQ> L;
+struct Frags {
+    uint32_t h[2][4], l[2][4];   // [channel 2*c32 + v][token pair]
+};
+
+__global__ __launch_bounds__(512) void k_decode_mla(MlaParams p) {
+    __shared__ Lds L;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, kg = lane >> 4;        // 16x16x32 operand layout
     const int c32 = lane & 31, h32 = lane >> 5;     // 32x32x16 operand layout
-    const int s = blockIdx.x, b = blockIdx.y;   // blockIdx.z: group of HQ query heads
+    const int tq = lane & 15, hp = lane >> 4;       // softmax: token, head pair
+    const int s = blockIdx.x, b = blockIdx.y;       // blockIdx.z: group of 64 query heads
     const int t_lo = int(int64_t(s) * p.ntiles / p.S);
     const int t_hi = int(int64_t(s + 1) * p.ntiles / p.S);
-    const int hw0 = wave * HW;
     const int64_t qrow0 = int64_t(b) * p.Hq + int64_t(blockIdx.z) * HQ;
+    const int ch0 = 64 * wave;                      // first own latent channel
 
-    // ---- q_r to LDS; this wave's content query rows as MFMA A operands
-    for (int i = tid; i < HQ * 32; i += 256)
+    // ---- q_r to LDS; content query rows of the own channels as A operands
+    for (int i = tid; i < HQ * 32; i += 512)
         L.qr[i] = reinterpret_cast<const uint32_t*>(p.q + (qrow0 + i / 32) * QD + VD)[i % 32];
-    f16x8 QA[QM][16];
+    f16x8 QA[4][2];
 #pragma unroll
-    for (int m = 0; m < QM; ++m)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks)
+        for (int ks = 0; ks < 2; ++ks)
             QA[m][ks] = as_f16x8(*reinterpret_cast<const uint4*>(
-                p.q + (qrow0 + hw0 + 16 * m + n) * QD + 32 * ks + 8 * kg));
+                p.q + (qrow0 + 16 * m + n) * QD + ch0 + 32 * ks + 8 * kg));
 
-    f32x16 O[PM][4];
+    f32x16 O[2][2];   // [32-head row block][channel 2*c32 + v]
 #pragma unroll
-    for (int pm = 0; pm < PM; ++pm)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int v = 0; v < 2; ++v)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) O[pm][u][e] = 0.0f;
-    // softmax state of rows (heads) hw0 + 16m + 4kg + j, this lane's column share
-    float mrun[QM][4], lrun[QM][4];
-#pragma unroll
-    for (int m = 0; m < QM; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            mrun[m][j] = -INFINITY;
-            lrun[m][j] = 0.0f;
-        }
+            for (int e = 0; e < 16; ++e) O[m][v][e] = 0.0f;
+    // softmax state of heads 8w + 2hp + e, this lane's token share
+    float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.0f, 0.0f};
 
-    // content tile loads (one ahead): codes of token t0 + (lane >> 2), words
-    // 8w + 2(lane & 3), +1; side: scale (lanes < 32) / zero of token
-    // t0 + ((lane >> 1) & 15), groups 4w + 2(lane & 1), +1
-    const uint32_t* vcb = p.vc + int64_t(b) * p.cap * 32 + 8 * wave + 2 * (lane & 3);
-    const uint16_t* vsb = (lane < 32 ? p.vs : p.vz) + int64_t(b) * p.cap * 16 + 4 * wave + 2 * (lane & 1);
-    auto load_content = [&](int tile, uint2& cw, uint32_t& sw) {
+    // per-lane dequant constants: channels ch0 + 2*c32 + v sit at code
+    // position u = 2(c32 & 1) + v of byte (c32 & 7) >> 1 of word c32 >> 3
+    uint32_t dmk[2], de2[2], dnb[2];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+        const int u = 2 * (c32 & 1) + v;
+        const uint32_t ex = uint32_t(25 - 2 * u) << 10;   // exponent field of 2^(10-2u)
+        dmk[v] = 0x00030003u << (2 * u);
+        de2[v] = ex | (ex << 16);
+        dnb[v] = de2[v] | 0x80008000u;
+    }
+    const uint32_t csel = byte_pair_sel((c32 & 7) >> 1);
+    const uint32_t rsel = byte_pair_sel((n & 7) >> 1);    // RoPE: byte of the lane's token
+    // (its code is the low nibble for even n, the high one for odd n)
+    const int mr = wave >> 1, kr = wave & 1;              // this wave's RoPE block
+
+    // content loads (two tiles ahead): code word (lane & 3) of the own 4 words
+    // of token t0 + (lane >> 2); side (lanes < 32): scale (lanes < 16) / zero
+    // pair of the own 2 groups of token t0 + (lane & 15)
+    const uint32_t* vcb = p.vc + int64_t(b) * p.cap * 32 + 4 * wave + (lane & 3);
+    const uint16_t* vsb = ((lane & 16) ? p.vz : p.vs) + int64_t(b) * p.cap * 16 + 2 * wave;
+    auto load_content = [&](int tile, uint32_t& cw, uint32_t& sw) {
         const int64_t t0 = int64_t(tile) * 16;
-        cw = *reinterpret_cast<const uint2*>(vcb + (t0 + (lane >> 2)) * 32);
-        sw = *reinterpret_cast<const uint32_t*>(vsb + (t0 + ((lane >> 1) & 15)) * 16);
+        cw = vcb[(t0 + (lane >> 2)) * 32];
+        sw = lane < 32 ? *reinterpret_cast<const uint32_t*>(vsb + (t0 + (lane & 15)) * 16) : 0u;
     };
-    // RoPE block loads: codes u32 pair 2*tid of the block; side (tid < 64)
-    auto load_rope = [&](int64_t blk, uint2& rw, uint32_t& rsw) {
-        rw = reinterpret_cast<const uint2*>(p.kc + (int64_t(b) * p.nblk_cap + blk) * GR * 8)[tid];
+    // RoPE block loads: code word tid of the block; side (tid < 64)
+    auto load_rope = [&](int64_t blk, uint32_t& rw, uint32_t& rsw) {
+        rw = p.kc[(int64_t(b) * p.nblk_cap + blk) * GR * 8 + tid];
         rsw = tid < 64 ? reinterpret_cast<const uint32_t*>((tid < 32 ? p.ks : p.kz) +
                                                            (int64_t(b) * p.nblk_cap + blk) * KD)[tid & 31]
                        : 0u;
     };
-    uint2 cw_n;
-    uint32_t sw_n;
-    load_content(t_lo, cw_n, sw_n);
-    uint2 rw_n = make_uint2(0u, 0u);
-    uint32_t rsw_n = 0u;
+    // tile i's content words in slot (i - t_lo) & 1
+    uint32_t cwq[2] = {0u, 0u}, swq[2] = {0u, 0u}, rw_n = 0u, rsw_n = 0u;
+    load_content(t_lo, cwq[0], swq[0]);
+    if (t_lo + 1 < t_hi) load_content(t_lo + 1, cwq[1], swq[1]);
     if (int64_t(t_lo) * 16 / GR < p.nblk) load_rope(int64_t(t_lo) * 16 / GR, rw_n, rsw_n);
     __syncthreads();
 
-    const uint32_t csel = byte_pair_sel(c32 & 3);         // content: byte of the lane's channels
-    const uint32_t rsel = byte_pair_sel((n & 7) >> 1);    // RoPE: byte of the lane's token
+    Frags F[2];        // tile i's operands in F[(i - t_lo) & 1]
     int64_t cur_blk = -1;
 
-    for (int i = t_lo; i < t_hi; ++i) {
+    // ---- stage 1 of tile i: dequant, QK^T partials -> sx[i & 1]
+    auto front = [&](int i, Frags& fr, uint32_t& cwr, uint32_t& swr) {
         const int64_t t0 = int64_t(i) * 16;
         const int64_t blk = t0 / GR;
         const bool qrope = blk < p.nblk;
-
-        // ---- A0: entering a quantized RoPE block: codes, side, q' and bias
         if (qrope && blk != cur_blk) {
-            L.rc[(2 * (tid & 3)) * RCS + (tid >> 2)] = rw_n.x;
-            L.rc[(2 * (tid & 3) + 1) * RCS + (tid >> 2)] = rw_n.y;
+            // entering a quantized RoPE block: codes, side, q' = q_r * s_k, bias
+            L.rc[(tid & 7) * RCS + (tid >> 3)] = rw_n;
             if (tid < 64) L.rs[tid] = rsw_n;
             cur_blk = blk;
             if (blk + 1 < p.nblk && (blk + 1) * GR < int64_t(t_hi) * 16) load_rope(blk + 1, rw_n, rsw_n);
             __syncthreads();
-            const int h = tid % HQ, c0 = (tid / HQ) * CW;
-            float bp = 0.0f;
+            // lane (cp = lane & 31) takes channel pair cp of heads 2*(tid >> 6)
+            // + (lane >> 5) + 16k; the bias sum runs over the 32 lanes of a head
+            const int cp = lane & 31;
+            const uint32_t sv = L.rs[cp], zv = L.rs[32 + cp];
 #pragma unroll
-            for (int k = 0; k < CW / 2; ++k) {
-                const int cp = c0 / 2 + k;                      // channel pair
-                const uint32_t qv = L.qr[h * 32 + cp], sv = L.rs[cp], zv = L.rs[32 + cp];
+            for (int k = 0; k < 4; ++k) {
+                const int h = 2 * wave + (lane >> 5) + 16 * k;
+                const uint32_t qv = L.qr[h * 32 + cp];
                 uint32_t hi, lo;
                 split_prod2(lo_h(qv), lo_h(sv), hi_h(qv), hi_h(sv), hi, lo);
                 L.qrh[h * QRS + cp] = hi;
                 L.qrl[h * QRS + cp] = lo;
-                bp = fmaf(lo_h(qv), lo_h(zv), bp);
-                bp = fmaf(hi_h(qv), hi_h(zv), bp);
+                float bp = fmaf(hi_h(qv), hi_h(zv), lo_h(qv) * lo_h(zv));
+                bp = row_sum16(bp);
+                bp += __shfl_xor(bp, 16);
+                if (cp == 0) L.rbias[h] = bp;
             }
-            L.rbp[tid / HQ][h] = bp;
         }
-
-        // ---- A1: stage this wave's content codes and side values
+        // stage the own codes and side values, prefetch tile i + 2
         {
-            const uint2 cw = cw_n;
-            const uint32_t sw = sw_n;
-            if (i + 1 < t_hi) load_content(i + 1, cw_n, sw_n);
-            uint32_t* cs = L.cst[wave];
-            cs[(2 * (lane & 3)) * 16 + (lane >> 2)] = cw.x;
-            cs[(2 * (lane & 3) + 1) * 16 + (lane >> 2)] = cw.y;
-            uint16_t* ss = reinterpret_cast<uint16_t*>(L.sst[wave]);
-            const int sz = lane >> 5, tl = (lane >> 1) & 15, g0 = 2 * (lane & 1);
-            ss[(sz * 4 + g0) * 16 + tl] = uint16_t(sw & 0xffffu);
-            ss[(sz * 4 + g0 + 1) * 16 + tl] = uint16_t(sw >> 16);
+            const uint32_t cw = cwr, sw = swr;
+            if (i + 2 < t_hi) load_content(i + 2, cwr, swr);
+            L.cst[wave][(lane & 3) * 16 + (lane >> 2)] = cw;
+            // lane (sz, tl) holds groups (0, 1) of token tl; even tl writes
+            // group 0 of tokens (tl, tl + 1), odd tl group 1
+            const uint32_t other = uint32_t(__builtin_amdgcn_update_dpp(0, int(sw), 0xb1, 0xf, 0xf, false));
+            const int sz = (lane >> 4) & 1, tl = lane & 15;
+            const bool odd = (tl & 1) != 0;
+            const uint32_t wv = odd ? __builtin_amdgcn_perm(sw, other, 0x07060302u)
+                                    : __builtin_amdgcn_perm(other, sw, 0x05040100u);
+            if (lane < 32) L.sst[wave][(sz * 2 + (odd ? 1 : 0)) * 8 + (tl >> 1)] = wv;
         }
         wave_sync();
-
-        // ---- A2: dequantize channels 128w + 4*c32 + u (u = 0..3) of tokens
-        // 8*h32 .. 8*h32 + 7: PV operands hi/lo (token pairs per register) and
-        // the token-major hi copy
-        uint32_t PH[4][4], PL[4][4];   // [u][token pair]
+        // dequant channels ch0 + 2*c32 + v of tokens 8*h32 .. 8*h32 + 7
         {
-            const uint32_t* cs = L.cst[wave] + (c32 >> 2) * 16 + 8 * h32;
+            const uint32_t* cs = L.cst[wave] + (c32 >> 3) * 16 + 8 * h32;
             const uint4 wa = *reinterpret_cast<const uint4*>(cs);
             const uint4 wb = *reinterpret_cast<const uint4*>(cs + 4);
             const uint32_t x[4] = {__builtin_amdgcn_perm(wa.y, wa.x, csel), __builtin_amdgcn_perm(wa.w, wa.z, csel),
                                    __builtin_amdgcn_perm(wb.y, wb.x, csel), __builtin_amdgcn_perm(wb.w, wb.z, csel)};
-            const uint32_t* sp = L.sst[wave] + (c32 >> 3) * 8 + 4 * h32;
+            const uint32_t* sp = L.sst[wave] + (c32 >> 4) * 8 + 4 * h32;
             const uint4 sv = *reinterpret_cast<const uint4*>(sp);
-            const uint4 zv = *reinterpret_cast<const uint4*>(sp + 32);
+            const uint4 zv = *reinterpret_cast<const uint4*>(sp + 16);
             uint32_t sa[4] = {sv.x, sv.y, sv.z, sv.w}, za[4] = {zv.x, zv.y, zv.z, zv.w};
             if (t0 + 16 > p.T) {
                 // tokens at or past T: scale and zero 0, so every value is 0
@@ -281,177 +298,198 @@ __global__ __launch_bounds__(256) void k_decode_mla(MlaParams p) {
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t ex = uint32_t(25 - 2 * u) << 10;   // exponent of 2^(10-2u)
-                const uint32_t mk = 0x00030003u << (2 * u);
-                const uint32_t e2 = ex | (ex << 16);
-                const uint32_t nb = e2 | 0x80008000u;             // (-2^(10-2u)) pair
+            for (int v = 0; v < 2; ++v)
 #pragma unroll
                 for (int q2 = 0; q2 < 4; ++q2)
-                    dequant_pair((x[q2] & mk) | e2, nb, sa[q2], za[q2], PH[u][q2], PL[u][q2]);
-            }
-            // token-major: token 8*h32 + 2*q2 (+1), channels 4*c32 .. 4*c32 + 3
+                    dequant_pair((x[q2] & dmk[v]) | de2[v], dnb[v], sa[q2], za[q2], p.neg1, fr.h[v][q2],
+                                 fr.l[v][q2]);
+            // token-major hi: token 8*h32 + 2*q2 (+1), channels 2*c32, 2*c32 + 1
+            uint32_t* cw = L.chw[wave];
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2) {
-                const uint32_t a0 = __builtin_amdgcn_perm(PH[1][q2], PH[0][q2], 0x05040100u);
-                const uint32_t a1 = __builtin_amdgcn_perm(PH[3][q2], PH[2][q2], 0x05040100u);
-                const uint32_t b0 = __builtin_amdgcn_perm(PH[1][q2], PH[0][q2], 0x07060302u);
-                const uint32_t b1 = __builtin_amdgcn_perm(PH[3][q2], PH[2][q2], 0x07060302u);
-                uint32_t* row = L.chi + (8 * h32 + 2 * q2) * CHS + 64 * wave + 2 * c32;
-                *reinterpret_cast<uint2*>(row) = make_uint2(a0, a1);
-                *reinterpret_cast<uint2*>(row + CHS) = make_uint2(b0, b1);
+                cw[(8 * h32 + 2 * q2) * CWS + c32] = __builtin_amdgcn_perm(fr.h[1][q2], fr.h[0][q2], 0x05040100u);
+                cw[(8 * h32 + 2 * q2 + 1) * CWS + c32] = __builtin_amdgcn_perm(fr.h[1][q2], fr.h[0][q2], 0x07060302u);
             }
         }
-        __syncthreads();   // hi tile, q' and bias complete
+        wave_sync();
+        // partial logits of all 64 heads over the own channels
+        f32x4 Sc[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) Sc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const f16x8 Bv = as_f16x8(*reinterpret_cast<const uint4*>(L.chw[wave] + n * CWS + 16 * ks + 4 * kg));
+#pragma unroll
+            for (int m = 0; m < 4; ++m) Sc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(QA[m][ks], Bv, Sc[m], 0, 0, 0);
+        }
+        // RoPE partial of heads 16mr .. 16mr + 15 over channels 32kr .. 32kr + 31
+        // to srx: A = q' hi, lo against the codes as exact fp16 integers (low
+        // nibble: (bits | exponent of 2^10) is 2^10 + code, high nibble: 2^6 +
+        // code), or q_r against the fp16 residual keys
+        const int hr = 16 * mr + n;
+        f32x4 Sr = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (qrope) {
+            const int wr = 2 * int((t0 % GR) / 16) + (n >> 3);   // code word of token n
+            const bool hin = (n & 1) != 0;
+            const uint32_t nm = hin ? 0x00f000f0u : 0x000f000fu;
+            const uint32_t ne = hin ? 0x54005400u : 0x64006400u;   // 2^6 | 2^10 exponent pairs
+            const f16x2 nb = __builtin_bit_cast(f16x2, hin ? 0xd400d400u : 0xe400e400u);
+            const uint32_t* src = L.rc + wr * RCS + 32 * kr + 8 * kg;
+            const uint4 w0 = *reinterpret_cast<const uint4*>(src);
+            const uint4 w1 = *reinterpret_cast<const uint4*>(src + 4);
+            auto code2 = [&](uint32_t hw, uint32_t lw) {
+                const uint32_t x = (__builtin_amdgcn_perm(hw, lw, rsel) & nm) | ne;
+                return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, x) + nb);
+            };
+            const f16x8 Bv = as_f16x8(code2(w0.y, w0.x), code2(w0.w, w0.z), code2(w1.y, w1.x), code2(w1.w, w1.z));
+            const f16x8 Ah = as_f16x8(*reinterpret_cast<const uint4*>(L.qrh + hr * QRS + 16 * kr + 4 * kg));
+            const f16x8 Al = as_f16x8(*reinterpret_cast<const uint4*>(L.qrl + hr * QRS + 16 * kr + 4 * kg));
+            Sr = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bv, Sr, 0, 0, 0);
+            Sr = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bv, Sr, 0, 0, 0);
+        } else {
+            // residual keys, fp16: row t0 + n - nblk*64 of the residual
+            const int64_t r = t0 + n - p.nblk * GR;
+            uint4 kv = make_uint4(0u, 0u, 0u, 0u);
+            if (r < GR && t0 + n < p.T)
+                kv = *reinterpret_cast<const uint4*>(p.kr + (int64_t(b) * GR + r) * KD + 32 * kr + 8 * kg);
+            const f16x8 Aq = as_f16x8(*reinterpret_cast<const uint4*>(L.qr + hr * 32 + 16 * kr + 4 * kg));
+            Sr = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aq, as_f16x8(kv), Sr, 0, 0, 0);
+        }
+        *reinterpret_cast<f32x4*>(L.srx[i & 1][wave] + n * 20 + 4 * kg) = Sr;
+        // partial logits to sx[i & 1][wave][token n][heads 16m + 4kg .. +3]
+        float* dst = L.sx[i & 1][wave] + n * SXS + 4 * kg;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) *reinterpret_cast<f32x4*>(dst + 16 * m) = Sc[m];
+    };
 
-        // ---- B: logits of heads hw0 .. hw0 + HW - 1, online softmax, weights to LDS
-        {
-            f32x4 Sc[QM], Sr[QM];
+    // ---- stage 2 of tile i: sum the partials of heads 8w + 2hp + e, softmax,
+    // weights -> pm[i & 1], rescale factors -> alpha[i & 1], wflag[i & 1]
+    auto softmax = [&](int i) {
+        const int64_t t0 = int64_t(i) * 16;
+        const bool qrope = t0 / GR < p.nblk;
+        const int bf = i & 1;
+        const int h0 = 8 * wave + 2 * hp;
+        float x[2] = {0.0f, 0.0f};
 #pragma unroll
-            for (int m = 0; m < QM; ++m) {
-                Sc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-                Sr[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int ks = 0; ks < 16; ++ks) {
-                const f16x8 Bv = as_f16x8(*reinterpret_cast<const uint4*>(L.chi + n * CHS + 16 * ks + 4 * kg));
-#pragma unroll
-                for (int m = 0; m < QM; ++m)
-                    Sc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(QA[m][ks], Bv, Sc[m], 0, 0, 0);
-            }
-            float rf = 1.0f;   // scale of the RoPE partial logits of this lane's column
-            if (qrope) {
-                const int wr = 2 * int((t0 % GR) / 16) + (n >> 3);   // code word of token n
-                const uint32_t nm = (n & 1) ? 0x00f000f0u : 0x000f000fu;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const uint32_t* src = L.rc + wr * RCS + 32 * ks + 8 * kg;
-                    const uint4 w0 = *reinterpret_cast<const uint4*>(src);
-                    const uint4 w1 = *reinterpret_cast<const uint4*>(src + 4);
-                    const f16x8 Bv = as_f16x8(__builtin_amdgcn_perm(w0.y, w0.x, rsel) & nm,
-                                              __builtin_amdgcn_perm(w0.w, w0.z, rsel) & nm,
-                                              __builtin_amdgcn_perm(w1.y, w1.x, rsel) & nm,
-                                              __builtin_amdgcn_perm(w1.w, w1.z, rsel) & nm);
-#pragma unroll
-                    for (int m = 0; m < QM; ++m) {
-                        const int hr = hw0 + 16 * m + n;
-                        const f16x8 Ah = as_f16x8(*reinterpret_cast<const uint4*>(L.qrh + hr * QRS + 16 * ks + 4 * kg));
-                        const f16x8 Al = as_f16x8(*reinterpret_cast<const uint4*>(L.qrl + hr * QRS + 16 * ks + 4 * kg));
-                        Sr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bv, Sr[m], 0, 0, 0);
-                        Sr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bv, Sr[m], 0, 0, 0);
-                    }
-                }
-                rf = __builtin_ldexpf(1.0f, (n & 1) ? 20 : 24);
-            } else {
-                // residual keys, fp16: row t0 + n - nblk*64 of the residual
-                const int64_t r = t0 + n - p.nblk * GR;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    uint4 kv = make_uint4(0u, 0u, 0u, 0u);
-                    if (r < GR && t0 + n < p.T)
-                        kv = *reinterpret_cast<const uint4*>(p.kr + (int64_t(b) * GR + r) * KD + 32 * ks + 8 * kg);
-                    const f16x8 Bv = as_f16x8(kv);
-#pragma unroll
-                    for (int m = 0; m < QM; ++m) {
-                        const int hr = hw0 + 16 * m + n;
-                        const f16x8 Aq = as_f16x8(*reinterpret_cast<const uint4*>(L.qr + hr * 32 + 16 * ks + 4 * kg));
-                        Sr[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aq, Bv, Sr[m], 0, 0, 0);
-                    }
-                }
-            }
-            const bool valid = t0 + n < p.T;
-            float x[QM][4];
-            bool over = false;
-#pragma unroll
-            for (int m = 0; m < QM; ++m)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int h = hw0 + 16 * m + 4 * kg + j;
-                    float bias = 0.0f;
-                    if (qrope) {
-#pragma unroll
-                        for (int cc = 0; cc < NC; ++cc) bias += L.rbp[cc][h];
-                    }
-                    const float lg = (Sc[m][j] + fmaf(Sr[m][j], rf, bias)) * p.sigma2;
-                    x[m][j] = valid ? lg : -INFINITY;
-                    over = over || x[m][j] > mrun[m][j] + TAU;
-                }
-            const bool moved = __builtin_amdgcn_ballot_w64(over) != 0;
-            if (moved) {
-#pragma unroll
-                for (int m = 0; m < QM; ++m)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float mn = fmaxf(mrun[m][j], row_max16(x[m][j]));
-                        const float a = __builtin_amdgcn_exp2f(mrun[m][j] - mn);
-                        mrun[m][j] = mn;
-                        lrun[m][j] *= a;
-                        if (n == 0) L.alpha[hw0 + 16 * m + 4 * kg + j] = a;
-                    }
-            }
-            if (lane == 0) L.wflag[wave] = moved ? 1 : 0;
-            uint16_t* pw = reinterpret_cast<uint16_t*>(L.pm);
-#pragma unroll
-            for (int m = 0; m < QM; ++m)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float pv = valid ? __builtin_amdgcn_exp2f(x[m][j] - mrun[m][j]) : 0.0f;
-                    const _Float16 ph = _Float16(pv);
-                    lrun[m][j] += float(ph);
-                    pw[(hw0 + 16 * m + 4 * kg + j) * (2 * PS) + n] = __builtin_bit_cast(uint16_t, ph);
-                }
+        for (int w = 0; w < NW; ++w) {
+            const float2 v = *reinterpret_cast<const float2*>(L.sx[bf][w] + tq * SXS + h0);
+            x[0] += v.x;
+            x[1] += v.y;
         }
-        __syncthreads();   // weights and rescale factors complete
+        // RoPE partials of heads h0, h0 + 1: waves 2(h0 >> 4) and 2(h0 >> 4) + 1
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const float2 v = *reinterpret_cast<const float2*>(L.srx[bf][2 * (h0 >> 4) + r] + tq * 20 + (h0 & 15));
+            x[0] += v.x;
+            x[1] += v.y;
+        }
+        const bool valid = t0 + tq < p.T;
+        bool over = false;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float bias = qrope ? L.rbias[h0 + e] : 0.0f;
+            x[e] = valid ? (x[e] + bias) * p.sigma2 : -INFINITY;
+            over = over || x[e] > mrun[e] + TAU;
+        }
+        const bool moved = __builtin_amdgcn_ballot_w64(over) != 0;
+        if (moved) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float mn = fmaxf(mrun[e], row_max16(x[e]));
+                const float a = __builtin_amdgcn_exp2f(mrun[e] - mn);
+                mrun[e] = mn;
+                lrun[e] *= a;
+                if (tq == 0) L.alpha[bf][h0 + e] = a;
+            }
+        }
+        if (lane == 0) L.wflag[bf][wave] = moved ? 1 : 0;
+        _Float16 ph[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float pv = valid ? __builtin_amdgcn_exp2f(x[e] - mrun[e]) : 0.0f;
+            ph[e] = _Float16(pv);
+            lrun[e] += float(ph[e]);
+        }
+        // even tq writes tokens (tq, tq + 1) of head h0, odd tq those of h0 + 1
+        const uint32_t mine = __builtin_bit_cast(uint32_t, f16x2{ph[0], ph[1]});
+        const uint32_t other = uint32_t(__builtin_amdgcn_update_dpp(0, int(mine), 0xb1, 0xf, 0xf, false));
+        const bool odd = (tq & 1) != 0;
+        const uint32_t wv = odd ? __builtin_amdgcn_perm(mine, other, 0x07060302u)
+                                : __builtin_amdgcn_perm(other, mine, 0x05040100u);
+        L.pm[bf][(h0 + (odd ? 1 : 0)) * PS + (tq >> 1)] = wv;
+    };
 
-        // ---- C: rescale, then O += P . (hi + lo) for this wave's channels
-        {
-            const int f0 = L.wflag[0], f1 = L.wflag[1], f2 = L.wflag[2], f3 = L.wflag[3];
-            if ((f0 | f1 | f2 | f3) != 0) {
+    // ---- stage 3 of tile i: rescale, O += P . (hi + lo)
+    auto pv_stage = [&](int i, const Frags& fr) {
+        const int bf = i & 1;
+        const int4 fa = *reinterpret_cast<const int4*>(L.wflag[bf]);
+        const int4 fb = *reinterpret_cast<const int4*>(L.wflag[bf] + 4);
+        if ((fa.x | fa.y | fa.z | fa.w | fb.x | fb.y | fb.z | fb.w) != 0) {
 #pragma unroll
-                for (int pm = 0; pm < PM; ++pm)
+            for (int m = 0; m < 2; ++m)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int h = 32 * pm + 8 * (e >> 2) + 4 * h32 + (e & 3);
-                        const int hw = h / HW;
-                        const int fl = hw == 0 ? f0 : hw == 1 ? f1 : hw == 2 ? f2 : f3;
-                        const float a = fl ? L.alpha[h] : 1.0f;
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) O[pm][u][e] *= a;
-                    }
-            }
-#pragma unroll
-            for (int pm = 0; pm < PM; ++pm) {
-                const f16x8 A = as_f16x8(*reinterpret_cast<const uint4*>(L.pm + (32 * pm + c32) * PS + 4 * h32));
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    O[pm][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        A, as_f16x8(PH[u][0], PH[u][1], PH[u][2], PH[u][3]), O[pm][u], 0, 0, 0);
-                    O[pm][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        A, as_f16x8(PL[u][0], PL[u][1], PL[u][2], PL[u][3]), O[pm][u], 0, 0, 0);
+                for (int e = 0; e < 16; ++e) {
+                    // row e of block m is head 32m + 8(e >> 2) + 4h32 + (e & 3),
+                    // whose softmax ran on wave 4m + (e >> 2)
+                    const int h = 32 * m + 8 * (e >> 2) + 4 * h32 + (e & 3);
+                    const int hw = 4 * m + (e >> 2);
+                    const int fl = hw == 0 ? fa.x : hw == 1 ? fa.y : hw == 2 ? fa.z : hw == 3 ? fa.w
+                                 : hw == 4 ? fb.x : hw == 5 ? fb.y : hw == 6 ? fb.z : fb.w;
+                    const float a = fl ? L.alpha[bf][h] : 1.0f;
+                    O[m][0][e] *= a;
+                    O[m][1][e] *= a;
                 }
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const f16x8 A = as_f16x8(*reinterpret_cast<const uint4*>(L.pm[bf] + (32 * m + c32) * PS + 4 * h32));
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                O[m][v] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    A, as_f16x8(fr.h[v][0], fr.h[v][1], fr.h[v][2], fr.h[v][3]), O[m][v], 0, 0, 0);
+                O[m][v] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    A, as_f16x8(fr.l[v][0], fr.l[v][1], fr.l[v][2], fr.l[v][3]), O[m][v], 0, 0, 0);
             }
         }
+    };
+
+    // step k: PV of tile t_lo + k - 2, softmax of t_lo + k - 1, front of
+    // t_lo + k; the operands of tile i live in F[(i - t_lo) & 1]
+    const int nt = t_hi - t_lo;
+    // Waves w and w + 4 share a SIMD; the second one runs its softmax before
+    // its PV so that the two overlap matrix and vector work.
+    const bool sm_first = wave >= 4;
+    for (int k = 0; k < nt + 2; k += 2) {
+        if (sm_first && k >= 1 && k - 1 < nt) softmax(t_lo + k - 1);
+        if (k >= 2) pv_stage(t_lo + k - 2, F[0]);
+        if (!sm_first && k >= 1 && k - 1 < nt) softmax(t_lo + k - 1);
+        if (k < nt) front(t_lo + k, F[0], cwq[0], swq[0]);
+        __syncthreads();
+        if (k + 1 >= nt + 2) break;
+        if (sm_first && k < nt) softmax(t_lo + k);
+        if (k >= 1) pv_stage(t_lo + k - 1, F[1]);
+        if (!sm_first && k < nt) softmax(t_lo + k);
+        if (k + 1 < nt) front(t_lo + k + 1, F[1], cwq[1], swq[1]);
+        __syncthreads();
     }
 
-    // ---- epilogue: running maxima and row sums per head, partial outputs
+    // ---- epilogue: running maxima and row sums, partial outputs
 #pragma unroll
-    for (int m = 0; m < QM; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float l = row_sum16(lrun[m][j]);
-            if (n == 0) {
-                const int64_t slot = (qrow0 + hw0 + 16 * m + 4 * kg + j) * p.S + s;
-                p.ws_ml[slot * 2] = mrun[m][j];
-                p.ws_ml[slot * 2 + 1] = l;
-            }
+    for (int e = 0; e < 2; ++e) {
+        const float l = row_sum16(lrun[e]);
+        if (tq == 0) {
+            const int64_t slot = (qrow0 + 8 * wave + 2 * hp + e) * p.S + s;
+            p.ws_ml[slot * 2] = mrun[e];
+            p.ws_ml[slot * 2 + 1] = l;
         }
+    }
 #pragma unroll
-    for (int pm = 0; pm < PM; ++pm)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int h = 32 * pm + 8 * (e >> 2) + 4 * h32 + (e & 3);
-            float4 v = make_float4(O[pm][0][e], O[pm][1][e], O[pm][2][e], O[pm][3][e]);
-            *reinterpret_cast<float4*>(p.ws_acc + ((qrow0 + h) * p.S + s) * VD + 128 * wave + 4 * c32) = v;
+            const int h = 32 * m + 8 * (e >> 2) + 4 * h32 + (e & 3);
+            *reinterpret_cast<float2*>(p.ws_acc + ((qrow0 + h) * p.S + s) * VD + ch0 + 2 * c32) =
+                make_float2(O[m][0][e], O[m][1][e]);
         }
 }
 
@@ -485,9 +523,9 @@ hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st) {
     p.cap = a.g.cap;
     p.nblk_cap = a.g.nblk_cap;
     p.sigma2 = a.sigma * 1.4426950408889634f;
-    // 64 query heads per workgroup (the register budget of one wave per SIMD)
-    const dim3 grid(a.S, a.g.B, a.Hq / 64);
-    hipLaunchKernelGGL(k_decode_mla<64>, grid, dim3(256), 0, st, p);
+    p.neg1 = -1.0f;
+    const dim3 grid(a.S, a.g.B, a.Hq / HQ);
+    hipLaunchKernelGGL(k_decode_mla, grid, dim3(64 * NW), 0, st, p);
     return hipGetLastError();
 }
 
