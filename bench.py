@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
 DEFAULT_WORKLOAD = "mistral_7b_gqa_t32805"
 
 
@@ -81,8 +82,11 @@ def profiled_traffic(variant: str, workload: str):
     rec = json.load(open(path)).get(f"{variant}/{workload}")
     if not rec:
         return None
-    src = open(os.path.join(ROOT, rec["source"]), "rb").read()
-    if hashlib.sha256(src).hexdigest()[:16] != rec["sha256_16"]:
+    srcs = rec["source"] if isinstance(rec["source"], list) else [rec["source"]]
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest()[:16] != rec["sha256_16"]:
         return None
     return int(rec["traffic_bytes"])
 
@@ -251,10 +255,28 @@ def main():
     p1_avg = float(np.mean(pass1_ms))
     p1_bytes = float(np.mean([w.cache_bytes(T) + w.batch * w.n_q_heads * w.qd * 2 for T in Ts]))
     achieved = p1_bytes / (p1_avg * 1e-3) / 1e9
+    p1_flops = float(np.mean([w.decode_flops(T) for T in Ts]))
+    tflops = p1_flops / (p1_avg * 1e-3) / 1e12
     ms_step = total_ms / args.steps
     p1_sorted = np.sort(pass1_ms)
     copy_gbps = copy_ceiling_gbps()
 
+    variant = dc.variant(w.n_q_heads)
+    if variant == "mla_mfma":
+        # the absorbed MLA kernel is bound by the matrix cores: 2 flops per
+        # multiply-add of q.c_hat, q_r.k_hat_r and p.c_hat
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                    "traffic": profiled_traffic(variant, w.name),
+                    "kernel": "decode pass-1 (" + variant + ")", "avg_us": round(p1_avg * 1e3, 2),
+                    "alg_flops_per_launch": int(p1_flops), "alg_bytes_per_launch": int(p1_bytes),
+                    "hbm_GBps": round(achieved, 2)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": profiled_traffic(variant, w.name),
+                    "kernel": "decode pass-1 (" + variant + ")", "avg_us": round(p1_avg * 1e3, 2),
+                    "alg_bytes_per_launch": int(p1_bytes)}
     res = {
         "metric": "2-bit decode attention KV bytes/s (tokens/s, % HBM peak; quantize GB/s)",
         "value": round(value, 2),
@@ -271,11 +293,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.kd, "context": w.T, "G": w.kG,
                    "bits": w.kbits, "value_group": w.vG, "layers": L, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": profiled_traffic(dc.variant(w.n_q_heads), w.name),
-                     "kernel": "decode pass-1 (" + dc.variant(w.n_q_heads) + ")",
-                     "avg_us": round(p1_avg * 1e3, 2), "alg_bytes_per_launch": int(p1_bytes)},
+        "roofline": roofline,
         "extra": {
             "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
             "attended_kv_tokens_per_s": round(w.batch * float(np.mean(Ts)) / (ms_step * 1e-3), 1),
