@@ -7,13 +7,16 @@
 // "QuantMLA Mimarisi ve Temel Bileşenleri": the same per-token rule serves the
 // INT2 content latent and the per-channel rule the INT4 RoPE key.
 //
-// Exactness: codes must equal round_half_even(fl32(fl32(x - mn) / scale32))
+// Exactness: codes must equal round_half_even(fl32(fl32(x - mn) / scale))
 // with an IEEE binary32 division.  A correctly rounded division costs ~10
 // VALU instructions, so each code is first taken from q = fl32(x - mn) *
 // rcp(scale) (v_rcp_f32, <= 1 ulp).  |q - fl32(true quotient)| <= 6.6e-7 for
 // quotients <= 2^bits - 1, so whenever q lies more than 2^-19 from a
-// half-integer both round to the same integer; a group with any code closer
-// than that to a tie is recomputed with the IEEE division.
+// half-integer both round to the same integer; a code closer than that to a
+// tie takes the IEEE division (a branch per code: on fp16 data about 1 code
+// in 10^4 does, so a wave almost never executes the division).
+// No clamp is needed: 0 <= fl32(x - mn) <= fl32(max - mn), so both quotients
+// round into [0, 2^bits - 1].
 #include <hip/hip_fp16.h>
 
 #include "kvq_internal.h"
@@ -25,16 +28,20 @@ namespace {
 
 constexpr float kTieBand = 0.5f - 0x1p-19f;
 
-__device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
-    return __half2float(__ushort_as_half(static_cast<unsigned short>(h16)));
-}
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
 
-__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
-    return __half_as_ushort(__float2half_rn(f));
+// fl32(x - mn) for the fp16 half HALF of w, in one instruction: v_fma_mix
+// converts the fp16 operand exactly and rounds x * 1 + (-mn) once
+template <int HALF>
+__device__ __forceinline__ float sub_half(uint32_t w, float neg_mn) {
+    float d;
+    if (HALF == 0)
+        asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(neg_mn));
+    else
+        asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(neg_mn));
+    return d;
 }
-
-// binary32 value of an fp16 input, with -0 canonicalised to +0
-__device__ __forceinline__ float canon(uint32_t h16) { return half_bits_to_float(h16) + 0.0f; }
 
 struct GroupQ {
     float mn, scale, rcp;
@@ -48,24 +55,30 @@ __device__ __forceinline__ GroupQ make_group(float mn, float mx, float L) {
     return q;
 }
 
-__device__ __forceinline__ uint32_t code_fast(float x, const GroupQ& q, float L, bool& tie) {
-    const float qa = (x - q.mn) * q.rcp;
-    const float k = __builtin_rintf(qa);
-    tie |= __builtin_fabsf(qa - k) > kTieBand;
-    return static_cast<uint32_t>(__builtin_fminf(k, L));
+// code of d = fl32(x - mn): round-half-even of d * rcp, or of the IEEE
+// quotient d / scale when the product lies within the tie band (scale == 0
+// gives rcp == 0, product 0, never in the band)
+__device__ __forceinline__ uint32_t code_of(float d, const GroupQ& q) {
+    const float qa = d * q.rcp;
+    float k = __builtin_rintf(qa);
+    if (__builtin_fabsf(qa - k) > kTieBand) k = __builtin_rintf(d / q.scale);
+    return static_cast<uint32_t>(k);
 }
 
-__device__ __forceinline__ uint32_t code_exact(float x, const GroupQ& q, float L) {
-    if (q.scale == 0.0f) return 0u;
-    const float d = x - q.mn;
-    const float qt = d / q.scale;
-    const float k = __builtin_rintf(qt);
-    return static_cast<uint32_t>(__builtin_fminf(__builtin_fmaxf(k, 0.0f), L));
+__device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
+    return __half2float(__ushort_as_half(static_cast<unsigned short>(h16)));
+}
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+    return __half_as_ushort(__float2half_rn(f));
 }
 
 // ------------------------------------------------------------------ values
-// One thread = 8 consecutive channels of one token (one 16-byte load); four
-// neighbouring lanes form a 32-channel group and reduce min/max by shuffles.
+// One thread = 8 consecutive channels (one 16-byte load) of VT consecutive
+// tokens, all loads issued first; four neighbouring lanes form a 32-channel
+// group and reduce min/max by shuffles.
+constexpr int VT = 4;
+
 template <int BITS>
 __global__ __launch_bounds__(256) void k_quant_values(
     const uint16_t* __restrict__ vin, int64_t n_in, int64_t row0, int64_t n_tok,
@@ -73,66 +86,69 @@ __global__ __launch_bounds__(256) void k_quant_values(
     uint16_t* __restrict__ scale, uint16_t* __restrict__ zero) {
     constexpr float L = float((1 << BITS) - 1);
     const int tpt = vd / 8;
-    const int64_t total = int64_t(BH) * n_tok * tpt;
+    const int64_t nq = (n_tok + VT - 1) / VT;
+    const int64_t total = int64_t(BH) * nq * tpt;
     const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (idx >= total) return;
+    if (idx >= total) return;   // a whole 4-lane group leaves together (tpt % 4 == 0)
     const int sub = int(idx % tpt);
-    const int64_t tok = (idx / tpt) % n_tok;
-    const int64_t bh = idx / tpt / n_tok;
+    const int64_t tq = (idx / tpt) % nq;
+    const int64_t bh = idx / tpt / nq;
 
-    const uint4 raw = *reinterpret_cast<const uint4*>(vin + ((bh * n_in) + row0 + tok) * vd + sub * 8);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    float x[8];
+    uint4 raw[VT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[2 * i] = canon(w[i] & 0xffffu);
-        x[2 * i + 1] = canon(w[i] >> 16);
+    for (int j = 0; j < VT; ++j) {
+        const int64_t tok = tq * VT + j;
+        raw[j] = tok < n_tok ? *reinterpret_cast<const uint4*>(vin + ((bh * n_in) + row0 + tok) * vd + sub * 8)
+                             : make_uint4(0u, 0u, 0u, 0u);
     }
-    float mn = x[0], mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) {
-        mn = __builtin_fminf(mn, x[i]);
-        mx = __builtin_fmaxf(mx, x[i]);
-    }
-    mn = __builtin_fminf(mn, __shfl_xor(mn, 1));
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1));
-    mn = __builtin_fminf(mn, __shfl_xor(mn, 2));
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 2));
-    const GroupQ q = make_group(mn, mx, L);
-
-    uint32_t c[8];
-    bool tie = false;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = code_fast(x[i], q, L, tie);
-    if (tie) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = code_exact(x[i], q, L);
-    }
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= c[i] << (BITS * i);
-
-    const int64_t t = t_dst0 + tok;
     const int vWT = vd * BITS / 32;
-    uint32_t* wrow = codes + (bh * cap + t) * vWT;
-    if (BITS == 2) {
-        const uint32_t other = __shfl_xor(packed, 1);
-        if ((sub & 1) == 0) wrow[sub >> 1] = packed | (other << 16);
-    } else {
-        wrow[sub] = packed;
-    }
-    if ((sub & 3) == 0) {
-        const int64_t side = (bh * cap + t) * (vd / 32) + (sub >> 2);
-        scale[side] = float_to_half_bits(q.scale);
-        zero[side] = float_to_half_bits(q.mn);
+#pragma unroll
+    for (int j = 0; j < VT; ++j) {
+        const int64_t tok = tq * VT + j;
+        const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+        // min / max of the 8 values (packed fp16, exact; -0 is canonicalised after)
+        f16x2 mn2 = __builtin_elementwise_min(__builtin_elementwise_min(as_h2(w[0]), as_h2(w[1])),
+                                              __builtin_elementwise_min(as_h2(w[2]), as_h2(w[3])));
+        f16x2 mx2 = __builtin_elementwise_max(__builtin_elementwise_max(as_h2(w[0]), as_h2(w[1])),
+                                              __builtin_elementwise_max(as_h2(w[2]), as_h2(w[3])));
+        float mn = __builtin_fminf(float(mn2[0]), float(mn2[1]));
+        float mx = __builtin_fmaxf(float(mx2[0]), float(mx2[1]));
+        mn = __builtin_fminf(mn, __shfl_xor(mn, 1));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1));
+        mn = __builtin_fminf(mn, __shfl_xor(mn, 2));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 2));
+        const GroupQ q = make_group(mn + 0.0f, mx + 0.0f, L);
+
+        uint32_t packed = 0;
+        const float nmn = -q.mn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            packed |= code_of(sub_half<0>(w[i], nmn), q) << (BITS * (2 * i));
+            packed |= code_of(sub_half<1>(w[i], nmn), q) << (BITS * (2 * i + 1));
+        }
+        const int64_t t = t_dst0 + tok;
+        uint32_t* wrow = codes + (bh * cap + t) * vWT;
+        const bool valid = tok < n_tok;
+        if (BITS == 2) {
+            const uint32_t other = __shfl_xor(packed, 1);
+            if (valid && (sub & 1) == 0) wrow[sub >> 1] = packed | (other << 16);
+        } else if (valid) {
+            wrow[sub] = packed;
+        }
+        if (valid && (sub & 3) == 0) {
+            const int64_t side = (bh * cap + t) * (vd / 32) + (sub >> 2);
+            scale[side] = float_to_half_bits(q.scale);
+            zero[side] = float_to_half_bits(q.mn);
+        }
     }
 }
 
 // -------------------------------------------------------------------- keys
-// One thread = 2 adjacent channels of one G-token block: it reads the G
-// token rows (4 bytes each; a wave covers 128 channels = 256 contiguous bytes
-// per row), reduces min/max per channel, and writes each channel's G codes
-// as G*BITS/32 consecutive words.
+// One thread = 2 adjacent channels over up to 32 rows of one G-token block
+// (4-byte loads; lanes side by side read contiguous bytes of a row); for
+// G > 32 the SPL = G/32 threads of a channel pair sit in one wave and merge
+// their min/max by shuffles.  Each thread writes its rows' codes as
+// consecutive words of the channel's G*BITS/32.
 template <int W>
 struct WordVec;
 template <> struct WordVec<1> { static __device__ void st(uint32_t* p, const uint32_t* w) { p[0] = w[0]; } };
@@ -159,60 +175,77 @@ __global__ __launch_bounds__(256) void k_quant_keys(
     uint16_t* __restrict__ zero) {
     constexpr float L = float((1 << BITS) - 1);
     constexpr int PER = 32 / BITS;
-    constexpr int W = G / PER;
+    constexpr int W = G / PER;                 // words per (block, channel)
+    constexpr int TG = G < 32 ? G : 32;        // rows per thread
+    constexpr int SPL = G / TG;                // threads per channel pair
+    constexpr int CPW = 64 / SPL;              // channel pairs per wave (SPL > 1)
+    constexpr int WT = TG / PER;               // words per thread and channel
     const int tpb = kd / 2;
-    const int64_t total = int64_t(BH) * nb * tpb;
+    const int64_t total = int64_t(BH) * nb * tpb * SPL;
     const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (idx >= total) return;
-    const int cp = int(idx % tpb);
-    const int64_t blk = blk0 + (idx / tpb) % nb;
-    const int64_t bh = idx / tpb / nb;
+    if (idx >= total) return;   // whole waves: total is a multiple of 64 when SPL > 1
+    int cp, sp;
+    int64_t blk, bh;
+    if (SPL == 1) {
+        sp = 0;
+        cp = int(idx % tpb);
+        blk = blk0 + (idx / tpb) % nb;
+        bh = idx / tpb / nb;
+    } else {
+        // a wave holds the SPL row ranges of CPW consecutive channel pairs
+        const int lane = int(idx & 63);
+        const int64_t wv = idx >> 6;
+        const int chunks = tpb / CPW;
+        sp = lane / CPW;
+        cp = int(wv % chunks) * CPW + lane % CPW;
+        blk = blk0 + (wv / chunks) % nb;
+        bh = wv / chunks / nb;
+    }
 
-    uint32_t raw[G];
+    uint32_t raw[TG];
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-        const int64_t tok = blk * G + i;
+    for (int i = 0; i < TG; ++i) {
+        const int64_t tok = blk * G + sp * TG + i;
         const uint16_t* row = tok < in_tok0 ? resid + (bh * G + (tok - res_tok0)) * kd
                                             : kin + (bh * n_in + (tok - in_tok0)) * kd;
         raw[i] = *reinterpret_cast<const uint32_t*>(row + 2 * cp);
     }
+    // per-channel min / max over the rows, both channels at once (packed
+    // fp16, exact; -0 is canonicalised after), then across the row ranges
+    f16x2 mn2 = as_h2(raw[0]), mx2 = mn2;
+#pragma unroll
+    for (int i = 1; i < TG; ++i) {
+        mn2 = __builtin_elementwise_min(mn2, as_h2(raw[i]));
+        mx2 = __builtin_elementwise_max(mx2, as_h2(raw[i]));
+    }
+#pragma unroll
+    for (int o = CPW; o < 64 && SPL > 1; o <<= 1) {
+        mn2 = __builtin_elementwise_min(mn2, as_h2(__shfl_xor(__builtin_bit_cast(uint32_t, mn2), o)));
+        mx2 = __builtin_elementwise_max(mx2, as_h2(__shfl_xor(__builtin_bit_cast(uint32_t, mx2), o)));
+    }
     GroupQ q[2];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        float mn = canon((raw[0] >> (16 * e)) & 0xffffu), mx = mn;
-#pragma unroll
-        for (int i = 1; i < G; ++i) {
-            const float x = canon((raw[i] >> (16 * e)) & 0xffffu);
-            mn = __builtin_fminf(mn, x);
-            mx = __builtin_fmaxf(mx, x);
-        }
-        q[e] = make_group(mn, mx, L);
-    }
+    for (int e = 0; e < 2; ++e) q[e] = make_group(float(mn2[e]) + 0.0f, float(mx2[e]) + 0.0f, L);
     const int64_t side = (bh * nblk_cap + blk) * kd + 2 * cp;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        uint32_t words[W];
+        uint32_t words[WT];
 #pragma unroll
-        for (int j = 0; j < W; ++j) words[j] = 0;
-        bool tie = false;
+        for (int j = 0; j < WT; ++j) words[j] = 0;
+        const float nmn = -q[e].mn;
 #pragma unroll
-        for (int i = 0; i < G; ++i)
-            words[i / PER] |= code_fast(canon((raw[i] >> (16 * e)) & 0xffffu), q[e], L, tie)
-                              << (BITS * (i % PER));
-        if (tie) {
-#pragma unroll
-            for (int j = 0; j < W; ++j) words[j] = 0;
-#pragma unroll
-            for (int i = 0; i < G; ++i)
-                words[i / PER] |= code_exact(canon((raw[i] >> (16 * e)) & 0xffffu), q[e], L)
-                                  << (BITS * (i % PER));
+        for (int i = 0; i < TG; ++i) {
+            const float d = e == 0 ? sub_half<0>(raw[i], nmn) : sub_half<1>(raw[i], nmn);
+            words[i / PER] |= code_of(d, q[e]) << (BITS * (i % PER));
         }
-        WordVec<W>::st(codes + (side + e) * W, words);
+        WordVec<WT>::st(codes + (side + e) * W + sp * WT, words);
     }
-    *reinterpret_cast<uint32_t*>(scale + side) =
-        uint32_t(float_to_half_bits(q[0].scale)) | (uint32_t(float_to_half_bits(q[1].scale)) << 16);
-    *reinterpret_cast<uint32_t*>(zero + side) =
-        uint32_t(float_to_half_bits(q[0].mn)) | (uint32_t(float_to_half_bits(q[1].mn)) << 16);
+    if (sp == 0) {
+        *reinterpret_cast<uint32_t*>(scale + side) =
+            uint32_t(float_to_half_bits(q[0].scale)) | (uint32_t(float_to_half_bits(q[1].scale)) << 16);
+        *reinterpret_cast<uint32_t*>(zero + side) =
+            uint32_t(float_to_half_bits(q[0].mn)) | (uint32_t(float_to_half_bits(q[1].mn)) << 16);
+    }
 }
 
 // ---------------------------------------------------------- residual copy
@@ -237,7 +270,7 @@ hipError_t launch_keys_t(const kvq_cache& c, const Geom& g, const void* k_in, in
                          int64_t in_tok0, int64_t res_tok0, int64_t blk0, int64_t nb,
                          hipStream_t st) {
     const int BH = g.B * g.Hkv;
-    const int64_t threads = int64_t(BH) * nb * (g.kd / 2);
+    const int64_t threads = int64_t(BH) * nb * (g.kd / 2) * (G > 32 ? G / 32 : 1);
     hipLaunchKernelGGL((k_quant_keys<G, BITS>), dim3(grid_of(threads)), dim3(256), 0, st,
                        static_cast<const uint16_t*>(k_in), n_in, in_tok0,
                        static_cast<const uint16_t*>(c.buf.k_resid), res_tok0, blk0, int(nb), g.kd,
@@ -252,7 +285,7 @@ hipError_t launch_quant_values(const kvq_cache& c, const Geom& g, const void* v_
                                int64_t row0, int64_t n_tok, int64_t t_dst0, hipStream_t st) {
     if (n_tok <= 0) return hipSuccess;
     const int BH = g.B * g.Hkv;
-    const int64_t threads = int64_t(BH) * n_tok * (g.vd / 8);
+    const int64_t threads = int64_t(BH) * ((n_tok + VT - 1) / VT) * (g.vd / 8);
     const auto* vin = static_cast<const uint16_t*>(v_in);
     auto* codes = static_cast<uint32_t*>(c.buf.v_codes);
     auto* sc = static_cast<uint16_t*>(c.buf.v_scale);
