@@ -87,7 +87,10 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState
 
     // ---- stage key codes and side values, then prefetch tile i + 2
     stage_keys<G>(cur, L.kl, L.ksl, lane);
-    if (nxt < end) load_ktile<G>(p, bh, nxt, lane, cur);
+    // unconditional (clamped to the last tile of the run) so that every path
+    // has the same loads in flight and the wait before staging covers only
+    // the older tile
+    load_ktile<G>(p, bh, nxt < end ? nxt : end - 1, lane, cur);
     wave_sync();
 
     // ---- q' = q * s_k as fp16 hi/lo rows, sigma2 * sum_c q z_k per (block, head)
@@ -226,7 +229,7 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
     const int hh = lane >> 4, chunk = lane & 15;
     // ---- stage value codes and side values, then prefetch tile i + 2
     stage_values(cur, L.vl, L.vsl, lane);
-    if (nxt < end) load_vtile(p, bh, nxt, lane, cur);
+    load_vtile(p, bh, nxt < end ? nxt : end - 1, lane, cur);
 
     // ---- rescale what was accumulated with the previous maxima
     const float a0 = hb.alpha[0], a1 = hb.alpha[1], a2 = hb.alpha[2], a3 = hb.alpha[3];
@@ -339,20 +342,31 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
         }
         KState st;
         st.m0 = st.m1 = st.m2 = st.m3 = -INFINITY;
-        // two register tiles in flight: tile t is staged from set (t & 1),
-        // which then receives tile t + 2
         KTile ta, tb;
         load_ktile<G>(p, bh, t_lo, lane, ta);
-        if (ntl > 1) load_ktile<G>(p, bh, t_lo + 1, lane, tb);
-        for (int it = 0; it <= ntl; it += 2) {
-            if (it < ntl) key_tile<G>(p, ta, st, L.k, L.hb[0], qv, sel, lane, bh, t_lo + it + 2, t_hi);
-            if (it == ntl && lane < HG) L.misc[lane] = sel4(lane, st.m0, st.m1, st.m2, st.m3);
+        load_ktile<G>(p, bh, ntl > 1 ? t_lo + 1 : t_lo, lane, tb);
+        // keep these loads ahead of (not interleaved with) the prefetch of tile 2
+        __builtin_amdgcn_sched_barrier(0);
+        // two register tiles in flight: tile j is staged from set j & 1,
+        // which then receives tile j + 2, and hands over through hb[j & 1].
+        // The loop body always processes two tiles, so every path has the
+        // same loads in flight and the wait before staging covers only the
+        // older tile.
+        key_tile<G>(p, ta, st, L.k, L.hb[0], qv, sel, lane, bh, t_lo + 2, t_hi);
+        __syncthreads();
+        int j = 1;
+        for (; j + 1 < ntl; j += 2) {
+            key_tile<G>(p, tb, st, L.k, L.hb[1], qv, sel, lane, bh, t_lo + j + 2, t_hi);
             __syncthreads();
-            if (it + 1 > ntl) break;
-            if (it + 1 < ntl) key_tile<G>(p, tb, st, L.k, L.hb[1], qv, sel, lane, bh, t_lo + it + 3, t_hi);
-            if (it + 1 == ntl && lane < HG) L.misc[lane] = sel4(lane, st.m0, st.m1, st.m2, st.m3);
+            key_tile<G>(p, ta, st, L.k, L.hb[0], qv, sel, lane, bh, t_lo + j + 3, t_hi);
             __syncthreads();
         }
+        if (j < ntl) {
+            key_tile<G>(p, tb, st, L.k, L.hb[1], qv, sel, lane, bh, t_lo + j + 2, t_hi);
+            __syncthreads();
+        }
+        if (lane < HG) L.misc[lane] = sel4(lane, st.m0, st.m1, st.m2, st.m3);
+        __syncthreads();
     } else {
         VState st;
         st.lsum = 0.0f;
@@ -362,15 +376,23 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
         for (int P = 0; P < 2; ++P)
 #pragma unroll
             for (int u = 0; u < 4; ++u) st.O[P][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // value work trails the key work by one tile (tile it - 1 at step it)
+        // value work trails the key work by one tile: tile j after barrier j
         VTile ta, tb;
         load_vtile(p, bh, t_lo, lane, ta);
-        if (ntl > 1) load_vtile(p, bh, t_lo + 1, lane, tb);
-        for (int it = 0; it <= ntl; it += 2) {
-            if (it >= 1) value_tile(p, tb, st, L.v, L.hb[1], sel, lane, bh, t_lo + it + 1, t_hi);
+        load_vtile(p, bh, ntl > 1 ? t_lo + 1 : t_lo, lane, tb);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        value_tile(p, ta, st, L.v, L.hb[0], sel, lane, bh, t_lo + 2, t_hi);
+        __syncthreads();
+        int j = 1;
+        for (; j + 1 < ntl; j += 2) {
+            value_tile(p, tb, st, L.v, L.hb[1], sel, lane, bh, t_lo + j + 2, t_hi);
             __syncthreads();
-            if (it + 1 > ntl) break;
-            value_tile(p, ta, st, L.v, L.hb[0], sel, lane, bh, t_lo + it + 2, t_hi);
+            value_tile(p, ta, st, L.v, L.hb[0], sel, lane, bh, t_lo + j + 3, t_hi);
+            __syncthreads();
+        }
+        if (j < ntl) {
+            value_tile(p, tb, st, L.v, L.hb[1], sel, lane, bh, t_lo + j + 2, t_hi);
             __syncthreads();
         }
         // ---- epilogue: l and the value-zero sums over the 16 lanes of a head

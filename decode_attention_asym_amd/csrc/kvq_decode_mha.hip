@@ -63,7 +63,10 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, float&
 
     // ---- stage key codes and side values, then prefetch tile i + 2
     stage_keys<G>(cur, L.kl, L.ksl, lane);
-    if (nxt < end) load_ktile<G>(p, bh, nxt, lane, cur);
+    // unconditional (clamped to the last tile of the run) so that every path
+    // has the same loads in flight and the wait before staging covers only
+    // the older tile
+    load_ktile<G>(p, bh, nxt < end ? nxt : end - 1, lane, cur);
     wave_sync();
 
     // ---- q' = q * s_k as fp16 rows hi, lo; sigma2 * sum_c q z_k per block
@@ -163,7 +166,7 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
     const int n = lane & 15, kg = lane >> 4;
     // ---- stage value codes and side values, then prefetch tile i + 2
     stage_values(cur, L.vl, L.vsl, lane);
-    if (nxt < end) load_vtile(p, bh, nxt, lane, cur);
+    load_vtile(p, bh, nxt < end ? nxt : end - 1, lane, cur);
 
     // ---- rescale what was accumulated with the previous maximum
     const float alpha = hb.alpha;
@@ -246,20 +249,31 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
         const uint32_t qw = reinterpret_cast<const uint32_t*>(p.q + (int64_t(b) * p.Hq + kvh) * D)[lane];
         const float q0 = lo_h(qw), q1 = hi_h(qw);
         float m_run = -INFINITY;
-        // two register tiles in flight: tile t is staged from set (t & 1),
-        // which then receives tile t + 2
         KTile ta, tb;
         load_ktile<G>(p, bh, t_lo, lane, ta);
-        if (ntl > 1) load_ktile<G>(p, bh, t_lo + 1, lane, tb);
-        for (int it = 0; it <= ntl; it += 2) {
-            if (it < ntl) key_tile<G>(p, ta, m_run, L.k, L.hb[0], q0, q1, sel, lane, bh, t_lo + it + 2, t_hi);
-            if (it == ntl && lane == 0) L.misc[0] = m_run;
+        load_ktile<G>(p, bh, ntl > 1 ? t_lo + 1 : t_lo, lane, tb);
+        // keep these loads ahead of (not interleaved with) the prefetch of tile 2
+        __builtin_amdgcn_sched_barrier(0);
+        // two register tiles in flight: tile j is staged from set j & 1,
+        // which then receives tile j + 2, and hands over through hb[j & 1].
+        // The loop body always processes two tiles, so every path has the
+        // same loads in flight and the wait before staging covers only the
+        // older tile.
+        key_tile<G>(p, ta, m_run, L.k, L.hb[0], q0, q1, sel, lane, bh, t_lo + 2, t_hi);
+        __syncthreads();
+        int j = 1;
+        for (; j + 1 < ntl; j += 2) {
+            key_tile<G>(p, tb, m_run, L.k, L.hb[1], q0, q1, sel, lane, bh, t_lo + j + 2, t_hi);
             __syncthreads();
-            if (it + 1 > ntl) break;
-            if (it + 1 < ntl) key_tile<G>(p, tb, m_run, L.k, L.hb[1], q0, q1, sel, lane, bh, t_lo + it + 3, t_hi);
-            if (it + 1 == ntl && lane == 0) L.misc[0] = m_run;
+            key_tile<G>(p, ta, m_run, L.k, L.hb[0], q0, q1, sel, lane, bh, t_lo + j + 3, t_hi);
             __syncthreads();
         }
+        if (j < ntl) {
+            key_tile<G>(p, tb, m_run, L.k, L.hb[1], q0, q1, sel, lane, bh, t_lo + j + 2, t_hi);
+            __syncthreads();
+        }
+        if (lane == 0) L.misc[0] = m_run;
+        __syncthreads();
     } else {
         VState st;
         st.lsum = st.vb0 = st.vb1 = 0.0f;
@@ -267,15 +281,23 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
         for (int P = 0; P < 2; ++P)
 #pragma unroll
             for (int u = 0; u < 4; ++u) st.O[P][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // value work trails the key work by one tile (tile it - 1 at step it)
+        // value work trails the key work by one tile: tile j after barrier j
         VTile ta, tb;
         load_vtile(p, bh, t_lo, lane, ta);
-        if (ntl > 1) load_vtile(p, bh, t_lo + 1, lane, tb);
-        for (int it = 0; it <= ntl; it += 2) {
-            if (it >= 1) value_tile(p, tb, st, L.v, L.hb[1], sel, lane, bh, t_lo + it + 1, t_hi);
+        load_vtile(p, bh, ntl > 1 ? t_lo + 1 : t_lo, lane, tb);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        value_tile(p, ta, st, L.v, L.hb[0], sel, lane, bh, t_lo + 2, t_hi);
+        __syncthreads();
+        int j = 1;
+        for (; j + 1 < ntl; j += 2) {
+            value_tile(p, tb, st, L.v, L.hb[1], sel, lane, bh, t_lo + j + 2, t_hi);
             __syncthreads();
-            if (it + 1 > ntl) break;
-            value_tile(p, ta, st, L.v, L.hb[0], sel, lane, bh, t_lo + it + 2, t_hi);
+            value_tile(p, ta, st, L.v, L.hb[0], sel, lane, bh, t_lo + j + 3, t_hi);
+            __syncthreads();
+        }
+        if (j < ntl) {
+            value_tile(p, tb, st, L.v, L.hb[1], sel, lane, bh, t_lo + j + 2, t_hi);
             __syncthreads();
         }
         // ---- epilogue: l and the value-zero sums over the wave
