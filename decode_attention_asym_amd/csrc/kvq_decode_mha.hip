@@ -29,13 +29,13 @@ namespace kvq {
 namespace {
 
 struct LdsK {
-    uint32_t kl[4 * KSTR];                                  // key codes [word row][channel]
+    __attribute__((aligned(16))) uint32_t kl[KTILE_DW];      // key codes, cache layout
     __attribute__((aligned(16))) uint32_t qa[2 * 2 * QSTR];  // q' rows [block][hi, lo]
     __attribute__((aligned(16))) uint32_t ksl[2 * 2 * 64];   // key [scale|zero][block][128 fp16]
 };
 
 struct LdsV {
-    uint32_t vl[8 * VSTR];                               // value codes [word][token]
+    __attribute__((aligned(16))) uint32_t vl[VTILE_DW];  // value codes, cache layout
     __attribute__((aligned(16))) uint32_t pa[8 * ASTR];   // p' rows [group][hi, lo]
     __attribute__((aligned(16))) uint32_t vsl[2 * 128];   // value [scale|zero][token][4 fp16]
 };
@@ -56,7 +56,7 @@ struct Lds {
 // maximum (log2 units, wave-uniform); q0, q1 are channels 2*lane, 2*lane+1.
 template <int G>
 __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, float& m_run, LdsK& L,
-                                         Handoff& hb, float q0, float q1, uint32_t sel, int lane,
+                                         Handoff& hb, float q0, float q1, int lane,
                                          int64_t bh, int nxt, int end) {
     constexpr int NBT = 64 / G;
     const int n = lane & 15, kg = lane >> 4;
@@ -92,13 +92,8 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, float&
         for (int be = 0; be < NBT; ++be) {
             const uint4 a = *reinterpret_cast<const uint4*>(L.qa + (2 * be + (n & 1)) * QSTR + 16 * ksx + 4 * kg);
             const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
-            const int r = G == 64 ? (n >> 2) : (2 * be + ((n & 7) >> 2));
-            const uint4* src = reinterpret_cast<const uint4*>(L.kl + r * KSTR + 32 * ksx + 8 * kg);
-            const uint4 w0 = src[0], w1 = src[1];
-            const uint32_t x0 = __builtin_amdgcn_perm(w0.y, w0.x, sel);
-            const uint32_t x1 = __builtin_amdgcn_perm(w0.w, w0.z, sel);
-            const uint32_t x2 = __builtin_amdgcn_perm(w1.y, w1.x, sel);
-            const uint32_t x3 = __builtin_amdgcn_perm(w1.w, w1.z, sel);
+            uint32_t x0, x1, x2, x3;
+            spread_bytes(ld_tr8(L.kl + key_row_dw<G>(ksx, be, kg, n)), x0, x1, x2, x3);
             if (G == 64) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -161,7 +156,7 @@ struct VState {
 
 // Value side of one tile, reading p and alpha from `hb`.
 __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VState& st, LdsV& L,
-                                           const Handoff& hb, uint32_t sel, int lane, int64_t bh,
+                                           const Handoff& hb, int lane, int64_t bh,
                                            int nxt, int end) {
     const int n = lane & 15, kg = lane >> 4;
     // ---- stage value codes and side values, then prefetch tile i + 2
@@ -206,18 +201,13 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
     // 32 tokens.  A row n holds group 2P + ((n >> 1) & 1), hi (n even) / lo.
 #pragma unroll
     for (int P = 0; P < 2; ++P) {
-        const int wi = 4 * P + 2 * (n >> 3) + ((n & 7) >> 2);
         const int row = 4 * P + (n & 3);
 #pragma unroll
         for (int ksx = 0; ksx < 2; ++ksx) {
             const uint4 a = *reinterpret_cast<const uint4*>(L.pa + row * ASTR + 16 * ksx + 4 * kg);
             const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
-            const uint4* src = reinterpret_cast<const uint4*>(L.vl + wi * VSTR + 32 * ksx + 8 * kg);
-            const uint4 w0 = src[0], w1 = src[1];
-            const uint32_t x0 = __builtin_amdgcn_perm(w0.y, w0.x, sel);
-            const uint32_t x1 = __builtin_amdgcn_perm(w0.w, w0.z, sel);
-            const uint32_t x2 = __builtin_amdgcn_perm(w1.y, w1.x, sel);
-            const uint32_t x3 = __builtin_amdgcn_perm(w1.w, w1.z, sel);
+            uint32_t x0, x1, x2, x3;
+            spread_bytes(ld_tr8(L.vl + value_row_dw(ksx, P, kg, n)), x0, x1, x2, x3);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const uint32_t mk = 0x00030003u << (2 * u);
@@ -243,7 +233,6 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
     const int t_lo = int(int64_t(s) * p.ntiles / p.S_main);
     const int t_hi = int(int64_t(s + 1) * p.ntiles / p.S_main);
     const int ntl = t_hi - t_lo;
-    const uint32_t sel = perm_selector(n);
 
     if (wave == 0) {
         const uint32_t qw = reinterpret_cast<const uint32_t*>(p.q + (int64_t(b) * p.Hq + kvh) * D)[lane];
@@ -259,17 +248,17 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
         // The loop body always processes two tiles, so every path has the
         // same loads in flight and the wait before staging covers only the
         // older tile.
-        key_tile<G>(p, ta, m_run, L.k, L.hb[0], q0, q1, sel, lane, bh, t_lo + 2, t_hi);
+        key_tile<G>(p, ta, m_run, L.k, L.hb[0], q0, q1, lane, bh, t_lo + 2, t_hi);
         __syncthreads();
         int j = 1;
         for (; j + 1 < ntl; j += 2) {
-            key_tile<G>(p, tb, m_run, L.k, L.hb[1], q0, q1, sel, lane, bh, t_lo + j + 2, t_hi);
+            key_tile<G>(p, tb, m_run, L.k, L.hb[1], q0, q1, lane, bh, t_lo + j + 2, t_hi);
             __syncthreads();
-            key_tile<G>(p, ta, m_run, L.k, L.hb[0], q0, q1, sel, lane, bh, t_lo + j + 3, t_hi);
+            key_tile<G>(p, ta, m_run, L.k, L.hb[0], q0, q1, lane, bh, t_lo + j + 3, t_hi);
             __syncthreads();
         }
         if (j < ntl) {
-            key_tile<G>(p, tb, m_run, L.k, L.hb[1], q0, q1, sel, lane, bh, t_lo + j + 2, t_hi);
+            key_tile<G>(p, tb, m_run, L.k, L.hb[1], q0, q1, lane, bh, t_lo + j + 2, t_hi);
             __syncthreads();
         }
         if (lane == 0) L.misc[0] = m_run;
@@ -287,17 +276,17 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
         load_vtile(p, bh, ntl > 1 ? t_lo + 1 : t_lo, lane, tb);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        value_tile(p, ta, st, L.v, L.hb[0], sel, lane, bh, t_lo + 2, t_hi);
+        value_tile(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + 2, t_hi);
         __syncthreads();
         int j = 1;
         for (; j + 1 < ntl; j += 2) {
-            value_tile(p, tb, st, L.v, L.hb[1], sel, lane, bh, t_lo + j + 2, t_hi);
+            value_tile(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, t_hi);
             __syncthreads();
-            value_tile(p, ta, st, L.v, L.hb[0], sel, lane, bh, t_lo + j + 3, t_hi);
+            value_tile(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + j + 3, t_hi);
             __syncthreads();
         }
         if (j < ntl) {
-            value_tile(p, tb, st, L.v, L.hb[1], sel, lane, bh, t_lo + j + 2, t_hi);
+            value_tile(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, t_hi);
             __syncthreads();
         }
         // ---- epilogue: l and the value-zero sums over the wave

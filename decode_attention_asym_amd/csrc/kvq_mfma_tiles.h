@@ -38,8 +38,8 @@ __device__ __forceinline__ uint2 ld_stream(const uint2* p) {
 }
 
 constexpr int D = 128;      // head dim
-constexpr int KSTR = 136;   // dwords per row of the key-code tile in LDS
-constexpr int VSTR = 76;    // dwords per row of the value-code tile in LDS
+constexpr int KTILE_DW = 512;   // key-code tile in LDS (dwords): the cache layout, copied
+constexpr int VTILE_DW = 528;   // value-code tile in LDS (dwords): the cache layout + pad
 constexpr int QSTR = 68;    // dwords per q' row (128 fp16 + pad)
 constexpr int ASTR = 36;    // dwords per p' row (64 fp16 + pad)
 constexpr int PSTR = 68;    // floats per row of the weight tile in LDS
@@ -190,53 +190,72 @@ __device__ __forceinline__ void load_vtile(const MfmaParams& p, int64_t bh, int6
     r.vs = ld_stream(reinterpret_cast<const uint4*>(vside) + (lane & 31));
 }
 
-// Key codes transposed to kl [word row][channel] (a word row holds 16 tokens
-// of every channel; G = 32 tiles hold two blocks, rows 2be and 2be + 1), and
-// the side values to ksl [scale | zero][block][128 fp16].
+// Key codes staged in their cache layout: G = 64, channel c of the tile at
+// dwords 4c..4c+3 (word j = tokens 16j..16j+15); G = 32, block be, channel c
+// at dwords 256be + 2c, +1.  Side values to ksl [scale | zero][block][128 fp16].
 template <int G>
 __device__ __forceinline__ void stage_keys(const KTile& cur, uint32_t* kl, uint32_t* ksl, int lane) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const uint4 kw = half ? cur.k1 : cur.k0;
-        const int i = lane + 64 * half;
-        if (G == 64) {
-            kl[0 * KSTR + i] = kw.x;
-            kl[1 * KSTR + i] = kw.y;
-            kl[2 * KSTR + i] = kw.z;
-            kl[3 * KSTR + i] = kw.w;
-        } else {
-            const int be = i >> 6, c = 2 * (i & 63);
-            *reinterpret_cast<uint2*>(kl + (2 * be) * KSTR + c) = make_uint2(kw.x, kw.z);
-            *reinterpret_cast<uint2*>(kl + (2 * be + 1) * KSTR + c) = make_uint2(kw.y, kw.w);
-        }
-    }
+    *reinterpret_cast<uint4*>(kl + 4 * lane) = cur.k0;
+    *reinterpret_cast<uint4*>(kl + 4 * (lane + 64)) = cur.k1;
     if (G == 64)
         *reinterpret_cast<uint2*>(ksl + (lane >> 5) * 128 + 2 * (lane & 31)) = make_uint2(cur.ks.x, cur.ks.y);
     else
         *reinterpret_cast<uint4*>(ksl + (lane >> 5) * 128 + 4 * (lane & 31)) = cur.ks;
 }
 
-// Value codes transposed to vl [word][token], and the side values to
+// dword of word w of token t in the staged value tile: the cache layout
+// (8 words per token) with 16 bytes of pad before every odd group of 8
+// tokens (group g starts 4 * ((g + 1) >> 1) dwords late), so that the two
+// 16-lane groups of a transposed read (groups 2k, 2k + 1) hit different banks
+__device__ __forceinline__ int vtile_dw(int t, int w) { return 8 * t + w + 4 * (((t >> 3) + 1) >> 1); }
+
+// Value codes staged in the cache layout (padded as above), side values to
 // vsl [scale | zero][token][4 fp16].
 __device__ __forceinline__ void stage_values(const VTile& cur, uint32_t* vl, uint32_t* vsl, int lane) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-        const uint4 vw = half ? cur.v1 : cur.v0;
         const int i = lane + 64 * half;
-        const int tok = i >> 1, w0 = 4 * (i & 1);
-        vl[(w0 + 0) * VSTR + tok] = vw.x;
-        vl[(w0 + 1) * VSTR + tok] = vw.y;
-        vl[(w0 + 2) * VSTR + tok] = vw.z;
-        vl[(w0 + 3) * VSTR + tok] = vw.w;
+        *reinterpret_cast<uint4*>(vl + vtile_dw(i >> 1, 4 * (i & 1))) = half ? cur.v1 : cur.v0;
     }
     *reinterpret_cast<uint4*>(vsl + (lane >> 5) * 128 + 4 * (lane & 31)) = cur.vs;
 }
 
-// v_perm selector: byte (n & 3) of the low-channel (or low-token) word ->
-// byte 0, of the high one -> byte 2, zero bytes 1 and 3
-__device__ __forceinline__ uint32_t perm_selector(int n) {
-    const uint32_t bsel = uint32_t(n & 3);
-    return bsel | (0x0cu << 8) | ((4u + bsel) << 16) | (0x0cu << 24);
+// ds_read_b64_tr_b8: within each group of 16 lanes, lane i names an 8-byte
+// row; lane j receives byte (j & 7) of the rows named by lanes
+// 2e + (j >> 3), e = 0..7 (in that order).  The operand builders below use
+// it so that each lane reads only the code bytes its MFMA column needs.
+typedef int lds_v2i __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ld_tr8(const uint32_t* p) {
+    const lds_v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) lds_v2i*)(p));
+    return make_uint2(uint32_t(r.x), uint32_t(r.y));
+}
+
+// Key-code row named by lane n of group kg for K-step ksx (32 channels):
+// lanes 2e, 2e + 1 name channel 32ksx + 8kg + e, words 0-1 and 2-3 (G = 64),
+// or both its two words in block be (G = 32).  Lane n then holds byte n & 3
+// of word row n >> 2 (G = 64) or (n >> 2) & 1 (G = 32) for the 8 channels.
+template <int G>
+__device__ __forceinline__ int key_row_dw(int ksx, int be, int kg, int n) {
+    const int c = 32 * ksx + 8 * kg + (n >> 1);
+    return G == 64 ? 4 * c + 2 * (n & 1) : 256 * be + 2 * c;
+}
+
+// Value-code row named by lane n of group kg for K-step ksx (32 tokens) and
+// channel half P: lanes 2e, 2e + 1 name token 32ksx + 8kg + e, words
+// 4P + 0-1 and 4P + 2-3.  Lane n then holds byte n & 3 of word 4P + (n >> 2)
+// for the 8 tokens.
+__device__ __forceinline__ int value_row_dw(int ksx, int P, int kg, int n) {
+    return vtile_dw(32 * ksx + 8 * kg + (n >> 1), 4 * P + 2 * (n & 1));
+}
+
+// the 8 code bytes of a transposed read spread over the fp16 halves of four
+// registers (byte e -> low byte of half e), in order
+__device__ __forceinline__ void spread_bytes(uint2 r, uint32_t& x0, uint32_t& x1, uint32_t& x2, uint32_t& x3) {
+    x0 = __builtin_amdgcn_perm(0u, r.x, 0x0c010c00u);
+    x1 = __builtin_amdgcn_perm(0u, r.x, 0x0c030c02u);
+    x2 = __builtin_amdgcn_perm(0u, r.y, 0x0c010c00u);
+    x3 = __builtin_amdgcn_perm(0u, r.y, 0x0c030c02u);
 }
 
 // ---- trailing tokens [ntiles*64, T) on the VALU: partial key block and the
