@@ -50,19 +50,24 @@ constexpr int HG = 4;  // query heads per KV head
 struct LdsK {
     __attribute__((aligned(16))) uint32_t kl[KTILE_DW];      // key codes, cache layout
     __attribute__((aligned(16))) uint32_t qa[2 * 8 * QSTR];  // q' rows (fp16) per key block
-    __attribute__((aligned(16))) uint32_t ksl[2 * 2 * 64];   // key [scale|zero][block][128 fp16]
+    __attribute__((aligned(16))) uint32_t ksl[2 * 2 * 64];   // key [scale|zero][block][128 fp16], quad order
     float bias[8];                                          // sigma2 * sum_c q z_k per (block, head)
 };
 
 struct LdsV {
     __attribute__((aligned(16))) uint32_t vl[VTILE_DW];      // value codes, cache layout
     __attribute__((aligned(16))) uint32_t pa[2 * 16 * ASTR];  // p' rows (fp16) per pass
-    __attribute__((aligned(16))) uint32_t vsl[2 * 128];      // value [scale|zero][token][4 fp16]
+    __attribute__((aligned(16))) uint32_t vsl[2 * 128];      // value [scale|zero][group][token pair]
 };
 
+// softmax weights p as fp16 hi + lo pairs: [head][token pair], dword 2k + j
+// holding tokens 4k + j, 4k + j + 2; 48-dword rows keep the key wave's
+// writes free of bank conflicts
+constexpr int PHS = 48;
 struct Handoff {
-    __attribute__((aligned(16))) float pl[HG * PSTR];  // softmax weights [head][token]
-    float alpha[HG];                                  // rescale of earlier accumulations
+    __attribute__((aligned(16))) uint32_t ph[HG * PHS];
+    __attribute__((aligned(16))) uint32_t pq[HG * PHS];
+    float alpha[HG];   // rescale of earlier accumulations
 };
 
 struct Lds {
@@ -76,10 +81,11 @@ struct KState {
     float m0, m1, m2, m3;   // running maxima per head (log2 units, wave-uniform)
 };
 
-// Key side of one tile: produces p and alpha in `hb`.
+// Key side of one tile: produces p and alpha in `hb`.  qw holds this lane's
+// query channels 8 chunk .. 8 chunk + 7 as fp16 pairs in quad order.
 template <int G>
 __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState& st, LdsK& L,
-                                         Handoff& hb, const float* qv, int lane,
+                                         Handoff& hb, const uint32_t* qw, int lane,
                                          int64_t bh, int nxt, int end) {
     constexpr int NBT = 64 / G;
     const int n = lane & 15, kg = lane >> 4;
@@ -104,9 +110,8 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState
         const uint32_t zw[4] = {zwv.x, zwv.y, zwv.z, zwv.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            split_prod2(qv[2 * i], lo_h(sw[i]), qv[2 * i + 1], hi_h(sw[i]), hi[i], lo[i]);
-            bias = fmaf(qv[2 * i], lo_h(zw[i]), bias);
-            bias = fmaf(qv[2 * i + 1], hi_h(zw[i]), bias);
+            split_prod_h(qw[i], sw[i], hi[i], lo[i]);
+            bias = dot2h(qw[i], zw[i], bias);
         }
         uint32_t* row = L.qa + (be * 8 + 2 * hh) * QSTR + 4 * chunk;
         *reinterpret_cast<uint4*>(row) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
@@ -129,21 +134,16 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState
             const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
             // byte n & 3 of word row n >> 2 (G = 64; (n >> 2) & 1 of block be
             // for G = 32) of channels 32ksx + 8kg + 0..7
-            uint32_t x0, x1, x2, x3;
-            spread_bytes(ld_tr8(L.kl + key_row_dw<G>(ksx, be, kg, n)), x0, x1, x2, x3);
+            const CodeRegs c = code_operands(ld_tr8(L.kl + key_row_dw<G>(ksx, be, kg, n)));
             if (G == 64) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const uint32_t mk = 0x00030003u << (2 * u);
-                    S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        A, as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), S[u], 0, 0, 0);
-                }
+                for (int u = 0; u < 4; ++u)
+                    S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x00030003u << (2 * u)), S[u], 0, 0, 0);
             } else {
 #pragma unroll
                 for (int v = 0; v < 2; ++v) {
                     const uint32_t mk = 0x00030003u << (2 * (2 * v + (n >> 3)));
-                    S[2 * be + v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        A, as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), S[2 * be + v], 0, 0, 0);
+                    S[2 * be + v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, mk), S[2 * be + v], 0, 0, 0);
                 }
             }
         }
@@ -151,18 +151,24 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState
 
     // ---- softmax.  Lane (n, kg) holds rows 4kg..4kg+3; rows 8..15 repeat
     // rows 0..7, so lanes kg and kg+2 see heads 2(kg&1), 2(kg&1)+1 (hi/lo row
-    // pairs) and split the tiles: kg < 2 take tiles 0, 1 and kg >= 2 tiles 2, 3.
+    // pairs) and split the columns' tokens so that each lane ends up with a
+    // token pair 4k + j, 4k + j + 2:
+    //   G = 64: tile u, column n is token 4n + u; lanes kg < 2 take tiles 0, 2
+    //           and kg >= 2 tiles 1, 3 (k = n, j = kg >> 1);
+    //   G = 32: tile 2be + v, column n is token
+    //           32be + 16((n & 7) >> 2) + 4(n & 3) + 2v + (n >> 3); lanes
+    //           kg < 2 take block 0 and kg >= 2 block 1 (j = n >> 3).
     const bool odd = (kg & 1) != 0;
-    const int u0 = 2 * (kg >> 1);
+    const bool up2 = (kg >> 1) != 0;
     float sA[2], sB[2];
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
         // element-wise selects keep the accumulators in registers
-        const bool up2 = (kg >> 1) != 0;
         float Sv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Sv[e] = up2 ? S[2 + v][e] : S[v][e];
-        const int up = G == 64 ? u0 + v : 2 * v + (n >> 3);
+        for (int e = 0; e < 4; ++e)
+            Sv[e] = G == 64 ? (up2 ? S[2 * v + 1][e] : S[2 * v][e]) : (up2 ? S[2 + v][e] : S[v][e]);
+        const int up = G == 64 ? 2 * v + (kg >> 1) : 2 * v + (n >> 3);
         const int be = G == 64 ? 0 : (kg >> 1);
         const float f = p.sigma2 * __builtin_ldexpf(1.0f, 24 - 2 * up);
         sA[v] = fmaf(Sv[0] + Sv[1], f, L.bias[be * 4 + 2 * (kg & 1)]);
@@ -197,18 +203,17 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState
         sA[v] = fast_exp2(sA[v] - mrA);
         sB[v] = fast_exp2(sB[v] - mrB);
     }
+    // ---- weights as fp16 hi + lo pairs (tokens 4k + j, 4k + j + 2)
     const int hA = 2 * (kg & 1), hB = hA + 1;
-    if (G == 64) {
-        *reinterpret_cast<float2*>(hb.pl + hA * PSTR + 4 * n + u0) = make_float2(sA[0], sA[1]);
-        *reinterpret_cast<float2*>(hb.pl + hB * PSTR + 4 * n + u0) = make_float2(sB[0], sB[1]);
-    } else {
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-            const int t = 32 * (kg >> 1) + 16 * ((n & 7) >> 2) + 4 * (n & 3) + 2 * v + (n >> 3);
-            hb.pl[hA * PSTR + t] = sA[v];
-            hb.pl[hB * PSTR + t] = sB[v];
-        }
-    }
+    const int dw = G == 64 ? 2 * n + (kg >> 1)
+                           : 2 * (8 * (kg >> 1) + 4 * ((n & 7) >> 2) + (n & 3)) + (n >> 3);
+    uint32_t h, l;
+    split_f32(sA[0], sA[1], p.neg1, h, l);
+    hb.ph[hA * PHS + dw] = h;
+    hb.pq[hA * PHS + dw] = l;
+    split_f32(sB[0], sB[1], p.neg1, h, l);
+    hb.ph[hB * PHS + dw] = h;
+    hb.pq[hB * PHS + dw] = l;
     if (lane < HG) hb.alpha[lane] = sel4(lane, a0, a1, a2, a3);
 }
 
@@ -249,37 +254,28 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
     }
     wave_sync();
 
-    // ---- p' = p * s_v as fp16 hi/lo rows per value group; sum_t p, sum_t p z_v
+    // ---- p' = p * s_v as fp16 hi/lo rows per value group; sum_t p, sum_t p z_v.
+    // Lane (hh, chunk): tokens 4 chunk .. 4 chunk + 3 of head hh, as the pairs
+    // (t0, t2), (t1, t3) that the rows hold in quad order.
     {
-        const float4 pv4 = *reinterpret_cast<const float4*>(hb.pl + hh * PSTR + 4 * chunk);
-        const float pv[4] = {pv4.x, pv4.y, pv4.z, pv4.w};
-        st.lsum += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-        // scale / zero halves of token t (0..3), group g (0..3) at half index 4t + g
-        const uint4* svp = reinterpret_cast<const uint4*>(L.vsl + 8 * chunk);
-        const uint4* zvp = reinterpret_cast<const uint4*>(L.vsl + 128 + 8 * chunk);
-        const uint4 s0 = svp[0], s1 = svp[1], z0 = zvp[0], z1 = zvp[1];
-        const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        const uint32_t zw[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+        const uint2 ph = *reinterpret_cast<const uint2*>(hb.ph + hh * PHS + 2 * chunk);
+        const uint2 pq = *reinterpret_cast<const uint2*>(hb.pq + hh * PHS + 2 * chunk);
+        // p of tokens t0, t2 (pair x) and t1, t3 (pair y) in fp32
+        const float p0 = join_lo(ph.x, pq.x, p.neg1), p2 = join_hi(ph.x, pq.x, p.neg1);
+        const float p1 = join_lo(ph.y, pq.y, p.neg1), p3 = join_hi(ph.y, pq.y, p.neg1);
+        st.lsum += (p0 + p1) + (p2 + p3);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            float sv[4], zv[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int hidx = 4 * t + g;
-                sv[t] = (hidx & 1) ? hi_h(sw[hidx >> 1]) : lo_h(sw[hidx >> 1]);
-                zv[t] = (hidx & 1) ? hi_h(zw[hidx >> 1]) : lo_h(zw[hidx >> 1]);
-            }
-            uint32_t h01, l01, h23, l23;
-            split_prod2(pv[0], sv[0], pv[1], sv[1], h01, l01);
-            split_prod2(pv[2], sv[2], pv[3], sv[3], h23, l23);
+            const uint2 sv = *reinterpret_cast<const uint2*>(L.vsl + g * 32 + 2 * chunk);
+            const uint2 zv = *reinterpret_cast<const uint2*>(L.vsl + 128 + g * 32 + 2 * chunk);
+            uint32_t h0, l0, h1, l1;
+            split_prod_hl(ph.x, pq.x, sv.x, h0, l0);
+            split_prod_hl(ph.y, pq.y, sv.y, h1, l1);
             // row ((pass*2 + gsel)*4 + head)*2 + hl; 64 tokens = 32 dwords per row
             uint32_t* rowp = L.pa + ((((g >> 1) * 2 + (g & 1)) * 4 + hh) * 2) * ASTR + 2 * chunk;
-            *reinterpret_cast<uint2*>(rowp) = make_uint2(h01, h23);
-            *reinterpret_cast<uint2*>(rowp + ASTR) = make_uint2(l01, l23);
-            float z = st.vb[g];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) z = fmaf(pv[t], zv[t], z);
-            st.vb[g] = z;
+            *reinterpret_cast<uint2*>(rowp) = make_uint2(h0, h1);
+            *reinterpret_cast<uint2*>(rowp + ASTR) = make_uint2(l0, l1);
+            st.vb[g] = fmaf(p3, hi_h(zv.y), fmaf(p1, lo_h(zv.y), fmaf(p2, hi_h(zv.x), fmaf(p0, lo_h(zv.x), st.vb[g]))));
         }
     }
     wave_sync();
@@ -292,14 +288,11 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
             const uint4 a = *reinterpret_cast<const uint4*>(L.pa + (P * 16 + n) * ASTR + 16 * ksx + 4 * kg);
             const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
             // byte n & 3 of word 4P + (n >> 2) of tokens 32ksx + 8kg + 0..7
-            uint32_t x0, x1, x2, x3;
-            spread_bytes(ld_tr8(L.vl + value_row_dw(ksx, P, kg, n)), x0, x1, x2, x3);
+            const CodeRegs c = code_operands(ld_tr8(L.vl + value_row_dw(ksx, P, kg, n)));
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t mk = 0x00030003u << (2 * u);
-                st.O[P][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    A, as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), st.O[P][u], 0, 0, 0);
-            }
+            for (int u = 0; u < 4; ++u)
+                st.O[P][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x00030003u << (2 * u)),
+                                                                    st.O[P][u], 0, 0, 0);
         }
     }
 }
@@ -314,7 +307,7 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int hq0 = kvh * HG;
     if (s >= p.S_main) {
-        if (wave == 0) tail_split<HG>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), L.hb[0].pl);
+        if (wave == 0) tail_split<HG>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
         return;
     }
     const int t_lo = int(int64_t(s) * p.ntiles / p.S_main);
@@ -322,16 +315,10 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
     const int ntl = t_hi - t_lo;
 
     if (wave == 0) {
-        float qv[8];
-        {
-            const uint4 raw = *reinterpret_cast<const uint4*>(p.q + ((int64_t(b) * p.Hq + hq0 + hh) * D + 8 * chunk));
-            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                qv[2 * i] = lo_h(w[i]);
-                qv[2 * i + 1] = hi_h(w[i]);
-            }
-        }
+        // query channels 8 chunk .. 8 chunk + 7 of head hh, in quad order
+        const uint4 raw = *reinterpret_cast<const uint4*>(p.q + ((int64_t(b) * p.Hq + hq0 + hh) * D + 8 * chunk));
+        const uint32_t qv[4] = {pair_lo(raw.x, raw.y), pair_hi(raw.x, raw.y), pair_lo(raw.z, raw.w),
+                                pair_hi(raw.z, raw.w)};
         KState st;
         st.m0 = st.m1 = st.m2 = st.m3 = -INFINITY;
         KTile ta, tb;

@@ -31,18 +31,21 @@ namespace {
 struct LdsK {
     __attribute__((aligned(16))) uint32_t kl[KTILE_DW];      // key codes, cache layout
     __attribute__((aligned(16))) uint32_t qa[2 * 2 * QSTR];  // q' rows [block][hi, lo]
-    __attribute__((aligned(16))) uint32_t ksl[2 * 2 * 64];   // key [scale|zero][block][128 fp16]
+    __attribute__((aligned(16))) uint32_t ksl[2 * 2 * 64];   // key [scale|zero][block][128 fp16], quad order
 };
 
 struct LdsV {
     __attribute__((aligned(16))) uint32_t vl[VTILE_DW];  // value codes, cache layout
     __attribute__((aligned(16))) uint32_t pa[8 * ASTR];   // p' rows [group][hi, lo]
-    __attribute__((aligned(16))) uint32_t vsl[2 * 128];   // value [scale|zero][token][4 fp16]
+    __attribute__((aligned(16))) uint32_t vsl[2 * 128];   // value [scale|zero][group][token pair]
 };
 
+// softmax weights p as fp16 hi + lo pairs: dword 2k + j holds tokens
+// 4k + j, 4k + j + 2 (the quad order of the K dimension)
 struct Handoff {
-    __attribute__((aligned(16))) float pl[64];  // softmax weights of the tile's tokens
-    float alpha;                                // rescale of earlier accumulations
+    __attribute__((aligned(16))) uint32_t ph[32];
+    __attribute__((aligned(16))) uint32_t pq[32];
+    float alpha;   // rescale of earlier accumulations
 };
 
 struct Lds {
@@ -53,10 +56,11 @@ struct Lds {
 };
 
 // Key side of one tile: produces p and alpha in `hb`.  m_run is the running
-// maximum (log2 units, wave-uniform); q0, q1 are channels 2*lane, 2*lane+1.
+// maximum (log2 units, wave-uniform); qw holds query channels
+// 4(lane >> 1) + (lane & 1) and that + 2 (fp16, quad order).
 template <int G>
 __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, float& m_run, LdsK& L,
-                                         Handoff& hb, float q0, float q1, int lane,
+                                         Handoff& hb, uint32_t qw, int lane,
                                          int64_t bh, int nxt, int end) {
     constexpr int NBT = 64 / G;
     const int n = lane & 15, kg = lane >> 4;
@@ -75,10 +79,10 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, float&
     for (int be = 0; be < NBT; ++be) {
         const uint32_t sw = L.ksl[be * 64 + lane], zw = L.ksl[128 + be * 64 + lane];
         uint32_t hi, lo;
-        split_prod2(q0, lo_h(sw), q1, hi_h(sw), hi, lo);
+        split_prod_h(qw, sw, hi, lo);
         L.qa[(2 * be) * QSTR + lane] = hi;
         L.qa[(2 * be + 1) * QSTR + lane] = lo;
-        bias[be] = wave_sum(fmaf(q0, lo_h(zw), q1 * hi_h(zw))) * p.sigma2;
+        bias[be] = wave_sum(dot2h(qw, zw, 0.0f)) * p.sigma2;
     }
     wave_sync();
 
@@ -92,21 +96,16 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, float&
         for (int be = 0; be < NBT; ++be) {
             const uint4 a = *reinterpret_cast<const uint4*>(L.qa + (2 * be + (n & 1)) * QSTR + 16 * ksx + 4 * kg);
             const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
-            uint32_t x0, x1, x2, x3;
-            spread_bytes(ld_tr8(L.kl + key_row_dw<G>(ksx, be, kg, n)), x0, x1, x2, x3);
+            const CodeRegs c = code_operands(ld_tr8(L.kl + key_row_dw<G>(ksx, be, kg, n)));
             if (G == 64) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const uint32_t mk = 0x00030003u << (2 * u);
-                    S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        A, as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), S[u], 0, 0, 0);
-                }
+                for (int u = 0; u < 4; ++u)
+                    S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x00030003u << (2 * u)), S[u], 0, 0, 0);
             } else {
 #pragma unroll
                 for (int v = 0; v < 2; ++v) {
                     const uint32_t mk = 0x00030003u << (2 * (2 * v + (n >> 3)));
-                    S[2 * be + v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        A, as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), S[2 * be + v], 0, 0, 0);
+                    S[2 * be + v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, mk), S[2 * be + v], 0, 0, 0);
                 }
             }
         }
@@ -134,15 +133,24 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, float&
     float pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(x[i] - m_run);
+    // weights as fp16 hi + lo pairs (tokens 4k + j, 4k + j + 2)
     if (kg == 0) {
+        uint32_t h0, l0, h1, l1;
         if (G == 64) {
-            *reinterpret_cast<float4*>(hb.pl + 4 * n) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+            // tokens 4n + u: pairs (u = 0, 2) and (1, 3) of quad n
+            split_f32(pv[0], pv[2], p.neg1, h0, l0);
+            split_f32(pv[1], pv[3], p.neg1, h1, l1);
+            *reinterpret_cast<uint2*>(hb.ph + 2 * n) = make_uint2(h0, h1);
+            *reinterpret_cast<uint2*>(hb.pq + 2 * n) = make_uint2(l0, l1);
         } else {
-            const int t = 16 * ((n & 7) >> 2) + 4 * (n & 3) + (n >> 3);
-            hb.pl[t] = pv[0];
-            hb.pl[t + 2] = pv[1];
-            hb.pl[t + 32] = pv[2];
-            hb.pl[t + 34] = pv[3];
+            // tiles 2be + v: pair (v = 0, 1) of quad k = 8be + 4((n & 7) >> 2) + (n & 3), j = n >> 3
+            split_f32(pv[0], pv[1], p.neg1, h0, l0);
+            split_f32(pv[2], pv[3], p.neg1, h1, l1);
+            const int dw = 2 * (4 * ((n & 7) >> 2) + (n & 3)) + (n >> 3);
+            hb.ph[dw] = h0;
+            hb.pq[dw] = l0;
+            hb.ph[dw + 16] = h1;
+            hb.pq[dw + 16] = l1;
         }
     }
     if (lane == 0) hb.alpha = alpha;
@@ -177,23 +185,24 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
     wave_sync();
 
     // ---- p' = p * s_v as fp16 rows (group, hi/lo); sum_t p, sum_t p z_v.
-    // Lane (tp, gp): tokens 2tp, 2tp + 1 and groups 2gp, 2gp + 1.
+    // Lane (tp, gp): token pair tp (tokens 4(tp >> 1) + (tp & 1) and that + 2,
+    // quad order) and groups 2gp, 2gp + 1.
     {
         const int tp = lane & 31, gp = lane >> 5;
-        const float2 pp = *reinterpret_cast<const float2*>(hb.pl + 2 * tp);
-        // dword 2t + gp of a side row holds groups 2gp (low half), 2gp + 1 of token t
-        const uint32_t s0 = L.vsl[4 * tp + gp], s1 = L.vsl[4 * tp + 2 + gp];
-        const uint32_t z0 = L.vsl[128 + 4 * tp + gp], z1 = L.vsl[128 + 4 * tp + 2 + gp];
+        const uint32_t ph = hb.ph[tp], pq = hb.pq[tp];
+        const uint32_t s0 = L.vsl[(2 * gp) * 32 + tp], s1 = L.vsl[(2 * gp + 1) * 32 + tp];
+        const uint32_t z0 = L.vsl[128 + (2 * gp) * 32 + tp], z1 = L.vsl[128 + (2 * gp + 1) * 32 + tp];
         uint32_t h, l;
-        split_prod2(pp.x, lo_h(s0), pp.y, lo_h(s1), h, l);
+        split_prod_hl(ph, pq, s0, h, l);
         L.pa[(4 * gp) * ASTR + tp] = h;
         L.pa[(4 * gp + 1) * ASTR + tp] = l;
-        split_prod2(pp.x, hi_h(s0), pp.y, hi_h(s1), h, l);
+        split_prod_hl(ph, pq, s1, h, l);
         L.pa[(4 * gp + 2) * ASTR + tp] = h;
         L.pa[(4 * gp + 3) * ASTR + tp] = l;
-        st.lsum += gp == 0 ? pp.x + pp.y : 0.0f;
-        st.vb0 = fmaf(pp.y, lo_h(z1), fmaf(pp.x, lo_h(z0), st.vb0));
-        st.vb1 = fmaf(pp.y, hi_h(z1), fmaf(pp.x, hi_h(z0), st.vb1));
+        const float pa = join_lo(ph, pq, p.neg1), pb = join_hi(ph, pq, p.neg1);
+        st.lsum += gp == 0 ? pa + pb : 0.0f;
+        st.vb0 = fmaf(pb, hi_h(z0), fmaf(pa, lo_h(z0), st.vb0));
+        st.vb1 = fmaf(pb, hi_h(z1), fmaf(pa, lo_h(z1), st.vb1));
     }
     wave_sync();
 
@@ -206,14 +215,11 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
         for (int ksx = 0; ksx < 2; ++ksx) {
             const uint4 a = *reinterpret_cast<const uint4*>(L.pa + row * ASTR + 16 * ksx + 4 * kg);
             const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
-            uint32_t x0, x1, x2, x3;
-            spread_bytes(ld_tr8(L.vl + value_row_dw(ksx, P, kg, n)), x0, x1, x2, x3);
+            const CodeRegs c = code_operands(ld_tr8(L.vl + value_row_dw(ksx, P, kg, n)));
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t mk = 0x00030003u << (2 * u);
-                st.O[P][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    A, as_f16x8(x0 & mk, x1 & mk, x2 & mk, x3 & mk), st.O[P][u], 0, 0, 0);
-            }
+            for (int u = 0; u < 4; ++u)
+                st.O[P][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x00030003u << (2 * u)),
+                                                                    st.O[P][u], 0, 0, 0);
         }
     }
 }
@@ -227,7 +233,7 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int64_t slot = (int64_t(b) * p.Hq + kvh) * p.S + s;
     if (s >= p.S_main) {
-        if (wave == 0) tail_split<1>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), L.hb[0].pl);
+        if (wave == 0) tail_split<1>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
         return;
     }
     const int t_lo = int(int64_t(s) * p.ntiles / p.S_main);
@@ -235,8 +241,9 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
     const int ntl = t_hi - t_lo;
 
     if (wave == 0) {
-        const uint32_t qw = reinterpret_cast<const uint32_t*>(p.q + (int64_t(b) * p.Hq + kvh) * D)[lane];
-        const float q0 = lo_h(qw), q1 = hi_h(qw);
+        // query channel pair of this lane in quad order
+        const uint2 qq = reinterpret_cast<const uint2*>(p.q + (int64_t(b) * p.Hq + kvh) * D)[lane >> 1];
+        const uint32_t qw = (lane & 1) ? pair_hi(qq.x, qq.y) : pair_lo(qq.x, qq.y);
         float m_run = -INFINITY;
         KTile ta, tb;
         load_ktile<G>(p, bh, t_lo, lane, ta);
@@ -248,17 +255,17 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
         // The loop body always processes two tiles, so every path has the
         // same loads in flight and the wait before staging covers only the
         // older tile.
-        key_tile<G>(p, ta, m_run, L.k, L.hb[0], q0, q1, lane, bh, t_lo + 2, t_hi);
+        key_tile<G>(p, ta, m_run, L.k, L.hb[0], qw, lane, bh, t_lo + 2, t_hi);
         __syncthreads();
         int j = 1;
         for (; j + 1 < ntl; j += 2) {
-            key_tile<G>(p, tb, m_run, L.k, L.hb[1], q0, q1, lane, bh, t_lo + j + 2, t_hi);
+            key_tile<G>(p, tb, m_run, L.k, L.hb[1], qw, lane, bh, t_lo + j + 2, t_hi);
             __syncthreads();
-            key_tile<G>(p, ta, m_run, L.k, L.hb[0], q0, q1, lane, bh, t_lo + j + 3, t_hi);
+            key_tile<G>(p, ta, m_run, L.k, L.hb[0], qw, lane, bh, t_lo + j + 3, t_hi);
             __syncthreads();
         }
         if (j < ntl) {
-            key_tile<G>(p, tb, m_run, L.k, L.hb[1], q0, q1, lane, bh, t_lo + j + 2, t_hi);
+            key_tile<G>(p, tb, m_run, L.k, L.hb[1], qw, lane, bh, t_lo + j + 2, t_hi);
             __syncthreads();
         }
         if (lane == 0) L.misc[0] = m_run;

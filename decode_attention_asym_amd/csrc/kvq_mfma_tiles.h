@@ -55,6 +55,7 @@ struct MfmaParams {
     int Hq, Hkv, S, S_main, ntiles, G;
     int64_t T, nblk, cap, nblk_cap;
     float sigma2;  // softmax scale * log2(e)
+    float neg1;    // -1, kept opaque so p - fp16(p) stays one mixed FMA
 };
 
 inline MfmaParams mfma_params(const DecodeArgs& a) {
@@ -81,6 +82,7 @@ inline MfmaParams mfma_params(const DecodeArgs& a) {
     p.cap = a.g.cap;
     p.nblk_cap = a.g.nblk_cap;
     p.sigma2 = a.sigma * 1.4426950408889634f;
+    p.neg1 = -1.0f;
     return p;
 }
 
@@ -114,6 +116,60 @@ __device__ __forceinline__ void split_prod2(float a0, float b0, float a1, float 
     hi = pk_rtz(fmaf(a0, b0, 0.0f), fmaf(a1, b1, 0.0f));
     lo = pk_rtz(fmaf(a0, b0, -lo_h(hi)), fmaf(a1, b1, -hi_h(hi)));
 }
+
+// ---- packed fp16 products (v_pk_mul_f16, v_pk_fma_f16, v_dot2_f32_f16)
+__device__ __forceinline__ f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+
+// a * b (fp16 pairs) as hi + lo: hi = fp16(a b), lo = a b - hi, which is
+// exact in fp16 (the rounding error of a product of two 11-bit significands
+// fits in 11 bits, barring underflow), so the pair carries a b to ~22 bits
+__device__ __forceinline__ void split_prod_h(uint32_t a, uint32_t b, uint32_t& hi, uint32_t& lo) {
+    const f16x2 h = as_h2(a) * as_h2(b);
+    hi = as_u32(h);
+    lo = as_u32(__builtin_elementwise_fma(as_h2(a), as_h2(b), -h));
+}
+
+// (ah + al) * b as hi + lo: hi = fp16(ah b), lo = fp16(al b + (ah b - hi))
+// with ah b - hi exact as above and one rounding in the outer fma
+__device__ __forceinline__ void split_prod_hl(uint32_t ah, uint32_t al, uint32_t b, uint32_t& hi,
+                                              uint32_t& lo) {
+    const f16x2 h = as_h2(ah) * as_h2(b);
+    hi = as_u32(h);
+    lo = as_u32(__builtin_elementwise_fma(as_h2(al), as_h2(b),
+                                          __builtin_elementwise_fma(as_h2(ah), as_h2(b), -h)));
+}
+
+// c + a.x b.x + a.y b.y in fp32 with fp16 operands read in place (two
+// v_fma_mix).  v_dot2_f32_f16 would be one instruction, but on MI355X it is
+// not correctly rounded (measured: ~11% of random inputs off, relative error
+// up to 1.5e-3), too coarse for the zero-point sums.
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
+    return fmaf(hi_h(a), hi_h(b), fmaf(lo_h(a), lo_h(b), c));
+}
+
+// fp32 values hi + lo of two fp16 hi/lo pairs (exact: the halves of lo lie
+// below the last bit of hi); neg1 = -1 keeps each a single v_fma_mix
+__device__ __forceinline__ float join_lo(uint32_t hi, uint32_t lo, float neg1) {
+    return -fmaf(lo_h(hi), neg1, -lo_h(lo));
+}
+__device__ __forceinline__ float join_hi(uint32_t hi, uint32_t lo, float neg1) {
+    return -fmaf(hi_h(hi), neg1, -hi_h(lo));
+}
+
+// two fp32 values as fp16 hi + lo (hi = fp16(x), lo = fp16(x - hi); x - hi
+// is exact in fp32)
+__device__ __forceinline__ void split_f32(float a, float b, float neg1, uint32_t& hi, uint32_t& lo) {
+    const f16x2 h = {_Float16(a), _Float16(b)};
+    hi = as_u32(h);
+    const f16x2 l = {_Float16(fmaf(float(h[0]), neg1, a)), _Float16(fmaf(float(h[1]), neg1, b))};
+    lo = as_u32(l);
+}
+
+// halves (x.lo, y.lo) and (x.hi, y.hi): the K dimension of every contraction
+// here runs in the quad order 0, 2, 1, 3 (see code_operands)
+__device__ __forceinline__ uint32_t pair_lo(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
 
 // Row-of-16 reductions with DPP (quad xor 1, quad xor 2, half-row mirror,
 // row mirror): afterwards every lane of the 16-lane row holds the result.
@@ -164,7 +220,7 @@ struct KTile {
 };
 struct VTile {
     uint4 v0, v1;   // value codes
-    uint4 vs;       // value scale (lanes 0..31) / zero (lanes 32..63)
+    uint4 vs;       // value scale (lanes 0..31) / zero (lanes 32..63) of two tokens
 };
 
 template <int G>
@@ -186,21 +242,31 @@ __device__ __forceinline__ void load_vtile(const MfmaParams& p, int64_t bh, int6
     const uint4* vb = reinterpret_cast<const uint4*>(p.vc + (bh * p.cap + tt * 64) * 8);
     r.v0 = ld_stream(vb + lane);
     r.v1 = ld_stream(vb + lane + 64);
+    // lane l (mod 32) takes tokens t = 4(l >> 1) + (l & 1) and t + 2: a pair
+    // in the quad order of the K dimension
     const uint16_t* vside = (lane < 32 ? p.vs : p.vz) + (bh * p.cap + tt * 64) * 4;
-    r.vs = ld_stream(reinterpret_cast<const uint4*>(vside) + (lane & 31));
+    const int t = 4 * ((lane & 31) >> 1) + (lane & 1);
+    const uint2 a = ld_stream(reinterpret_cast<const uint2*>(vside + 4 * t));
+    const uint2 b = ld_stream(reinterpret_cast<const uint2*>(vside + 4 * (t + 2)));
+    r.vs = make_uint4(a.x, a.y, b.x, b.y);
 }
 
 // Key codes staged in their cache layout: G = 64, channel c of the tile at
 // dwords 4c..4c+3 (word j = tokens 16j..16j+15); G = 32, block be, channel c
-// at dwords 256be + 2c, +1.  Side values to ksl [scale | zero][block][128 fp16].
+// at dwords 256be + 2c, +1.  Side values to ksl [scale | zero][block][128 fp16]
+// in quad order.
 template <int G>
 __device__ __forceinline__ void stage_keys(const KTile& cur, uint32_t* kl, uint32_t* ksl, int lane) {
     *reinterpret_cast<uint4*>(kl + 4 * lane) = cur.k0;
     *reinterpret_cast<uint4*>(kl + 4 * (lane + 64)) = cur.k1;
+    // side values with the channels of each quad in the order 0, 2, 1, 3
     if (G == 64)
-        *reinterpret_cast<uint2*>(ksl + (lane >> 5) * 128 + 2 * (lane & 31)) = make_uint2(cur.ks.x, cur.ks.y);
+        *reinterpret_cast<uint2*>(ksl + (lane >> 5) * 128 + 2 * (lane & 31)) =
+            make_uint2(pair_lo(cur.ks.x, cur.ks.y), pair_hi(cur.ks.x, cur.ks.y));
     else
-        *reinterpret_cast<uint4*>(ksl + (lane >> 5) * 128 + 4 * (lane & 31)) = cur.ks;
+        *reinterpret_cast<uint4*>(ksl + (lane >> 5) * 128 + 4 * (lane & 31)) =
+            make_uint4(pair_lo(cur.ks.x, cur.ks.y), pair_hi(cur.ks.x, cur.ks.y),
+                       pair_lo(cur.ks.z, cur.ks.w), pair_hi(cur.ks.z, cur.ks.w));
 }
 
 // dword of word w of token t in the staged value tile: the cache layout
@@ -210,14 +276,19 @@ __device__ __forceinline__ void stage_keys(const KTile& cur, uint32_t* kl, uint3
 __device__ __forceinline__ int vtile_dw(int t, int w) { return 8 * t + w + 4 * (((t >> 3) + 1) >> 1); }
 
 // Value codes staged in the cache layout (padded as above), side values to
-// vsl [scale | zero][token][4 fp16].
+// vsl [scale | zero][group][32 token pairs]: dword 2k + j of a group row
+// holds tokens 4k + j, 4k + j + 2 (the quad order of the K dimension).
 __device__ __forceinline__ void stage_values(const VTile& cur, uint32_t* vl, uint32_t* vsl, int lane) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         const int i = lane + 64 * half;
         *reinterpret_cast<uint4*>(vl + vtile_dw(i >> 1, 4 * (i & 1))) = half ? cur.v1 : cur.v0;
     }
-    *reinterpret_cast<uint4*>(vsl + (lane >> 5) * 128 + 4 * (lane & 31)) = cur.vs;
+    uint32_t* row = vsl + (lane >> 5) * 128 + (lane & 31);
+    row[0] = pair_lo(cur.vs.x, cur.vs.z);
+    row[32] = pair_hi(cur.vs.x, cur.vs.z);
+    row[64] = pair_lo(cur.vs.y, cur.vs.w);
+    row[96] = pair_hi(cur.vs.y, cur.vs.w);
 }
 
 // ds_read_b64_tr_b8: within each group of 16 lanes, lane i names an 8-byte
@@ -249,13 +320,19 @@ __device__ __forceinline__ int value_row_dw(int ksx, int P, int kg, int n) {
     return vtile_dw(32 * ksx + 8 * kg + (n >> 1), 4 * P + 2 * (n & 1));
 }
 
-// the 8 code bytes of a transposed read spread over the fp16 halves of four
-// registers (byte e -> low byte of half e), in order
-__device__ __forceinline__ void spread_bytes(uint2 r, uint32_t& x0, uint32_t& x1, uint32_t& x2, uint32_t& x3) {
-    x0 = __builtin_amdgcn_perm(0u, r.x, 0x0c010c00u);
-    x1 = __builtin_amdgcn_perm(0u, r.x, 0x0c030c02u);
-    x2 = __builtin_amdgcn_perm(0u, r.y, 0x0c010c00u);
-    x3 = __builtin_amdgcn_perm(0u, r.y, 0x0c030c02u);
+// The 8 code bytes e = 0..7 of a transposed read as MFMA operand registers
+// r.x, r.x >> 8, r.y, r.y >> 8: ANDed with a mask that keeps one 2-bit code
+// position in bytes 0 and 2, their fp16 halves hold bytes (0, 2), (1, 3),
+// (4, 6), (5, 7), i.e. the K index runs over e in the quad order 0, 2, 1, 3.
+// The A operands (q', p') are laid out in the same order.
+struct CodeRegs {
+    uint32_t x0, x1, x2, x3;
+};
+__device__ __forceinline__ CodeRegs code_operands(uint2 r) {
+    return CodeRegs{r.x, r.x >> 8, r.y, r.y >> 8};
+}
+__device__ __forceinline__ f16x8 code_slice(const CodeRegs& c, uint32_t mk) {
+    return as_f16x8(c.x0 & mk, c.x1 & mk, c.x2 & mk, c.x3 & mk);
 }
 
 // ---- trailing tokens [ntiles*64, T) on the VALU: partial key block and the

@@ -5,7 +5,7 @@ result, on all five workloads and on edge cases."""
 import numpy as np
 import pytest
 
-from gpu_util import (TOL, assert_slices_equal, configs, dev_f16, host_u16, kvq, log, new_cache,
+from gpu_util import (MEAN_EXCESS_TOL, TOL, assert_slices_equal, mean_excess, configs, dev_f16, host_u16, kvq, log, new_cache,
                       oracle_attention, oracle_cache_full, oracle_slice, sample_pairs, slice_of,
                       synth, torch)
 
@@ -45,7 +45,7 @@ def test_workload_parity(orc, name):
         slices = slices[::8] + [slices[-1]] if len(slices) > 32 else slices
     else:
         slices = sorted({(b, hq // group) for b, hq in sample_pairs(w, 4, seed=w.index)})
-    worst, omax = 0.0, 0.0
+    worst, omax, gots, refs = 0.0, 0.0, [], []
     for b, h in slices:
         ref = oracle_slice(orc, w, k[b, h], v[b, h], cap // w.kG, cap)
         assert_slices_equal(slice_of(dc, b, h, w.T, w.n_blocks), ref, f"{name} b{b} h{h}")
@@ -64,11 +64,14 @@ def test_workload_parity(orc, name):
             sub = configs.Workload(w.name, w.index, "mla", 1, len(heads), 1, w.T, w.kd, w.kG,
                                    w.kbits, w.vd, w.vG, w.vbits, w.outlier_scale)
         ref_o = oracle_attention(orc, sub, cache, qs)[0]
-        err = np.abs(got[b, list(heads)] - ref_o).max()
-        worst = max(worst, err)
+        gots.append(got[b, list(heads)].ravel())
+        refs.append(ref_o.ravel())
+        worst = max(worst, np.abs(gots[-1] - refs[-1]).max())
         omax = max(omax, np.abs(ref_o).max())
-    log(f"[{name}] slices {len(slices)} max|err| {worst:.3e} max|o| {omax:.3f}")
+    excess = mean_excess(np.concatenate(gots), np.concatenate(refs))
+    log(f"[{name}] slices {len(slices)} max|err| {worst:.3e} mean excess {excess:.2e} max|o| {omax:.3f}")
     assert worst <= TOL
+    assert excess <= MEAN_EXCESS_TOL
 
 
 def _tiny(T, Hq=4, Hkv=2, D=64, G=32, kbits=2, vbits=2, B=2, idx=200):
@@ -88,6 +91,8 @@ def _check_decode(orc, w, dc, k, v, n_splits=0, kq_blocks=None):
     ref = oracle_attention(orc, w, cache, q)
     err = np.abs(got - ref).max()
     assert err <= TOL, (w, n_splits, err)
+    excess = mean_excess(got, ref)
+    assert excess <= MEAN_EXCESS_TOL, (w, n_splits, excess)
     return got
 
 
