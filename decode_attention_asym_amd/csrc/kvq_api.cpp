@@ -210,7 +210,7 @@ kvq_status kv_decode_attention(const kvq_cache* c, const void* q, int32_t Hq, fl
     if (n_splits < 0 || n_splits > KVQ_MAX_SPLITS) return KVQ_E_SHAPE;
     if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return KVQ_E_ALIGN;
     if (c->T <= 0) return KVQ_E_STATE;
-    DecodeArgs a;
+    DecodeArgs a{};
     a.c = c;
     a.g = geom_of(c->cfg);
     const Variant v = pick_variant(*c, Hq);
@@ -231,18 +231,17 @@ kvq_status kv_decode_attention(const kvq_cache* c, const void* q, int32_t Hq, fl
     a.ws_acc = static_cast<float*>(ws);
     a.ws_ml = a.ws_acc + uint64_t(a.g.B) * Hq * a.S * a.g.vd;
 
+    a.ev_start = g_ev_before;
+    a.ev_stop = g_ev_after;
+
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    if (g_ev_before) e = hipEventRecord(g_ev_before, st);
-    if (e != hipSuccess) return KVQ_E_HIP;
     switch (v) {
         case V_GQA: e = launch_decode_gqa(a, st); break;
         case V_MHA: e = launch_decode_mha(a, st); break;
         case V_MLA: e = launch_decode_mla(a, st); break;
         default: e = launch_decode_generic(a, st); break;
     }
-    if (e != hipSuccess) return KVQ_E_HIP;
-    if (g_ev_after) e = hipEventRecord(g_ev_after, st);
     if (e != hipSuccess) return KVQ_E_HIP;
     return hip_status(launch_merge(a, st));
 }

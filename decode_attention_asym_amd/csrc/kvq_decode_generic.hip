@@ -192,9 +192,9 @@ hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
     p.sigma2 = a.sigma * 1.4426950408889634f;
     const dim3 grid(a.S, a.Hq, a.g.B);
     if (c.cfg.kind == KVQ_KIND_MLA)
-        hipLaunchKernelGGL(k_decode_generic<true>, grid, dim3(256), 0, st, p);
+        hipExtLaunchKernelGGL(k_decode_generic<true>, grid, dim3(256), 0, st, a.ev_start, a.ev_stop, 0, p);
     else
-        hipLaunchKernelGGL(k_decode_generic<false>, grid, dim3(256), 0, st, p);
+        hipExtLaunchKernelGGL(k_decode_generic<false>, grid, dim3(256), 0, st, a.ev_start, a.ev_stop, 0, p);
     return hipGetLastError();
 }
 

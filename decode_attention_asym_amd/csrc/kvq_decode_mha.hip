@@ -331,9 +331,9 @@ hipError_t launch_decode_mha(const DecodeArgs& a, hipStream_t st) {
     const MfmaParams p = mfma_params(a);
     const dim3 grid(a.S, a.g.Hkv, a.g.B);
     if (a.g.kG == 64)
-        hipLaunchKernelGGL(k_decode_mha<64>, grid, dim3(128), 0, st, p);
+        hipExtLaunchKernelGGL(k_decode_mha<64>, grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
     else
-        hipLaunchKernelGGL(k_decode_mha<32>, grid, dim3(128), 0, st, p);
+        hipExtLaunchKernelGGL(k_decode_mha<32>, grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
     return hipGetLastError();
 }
 

@@ -525,7 +525,7 @@ hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st) {
     p.sigma2 = a.sigma * 1.4426950408889634f;
     p.neg1 = -1.0f;
     const dim3 grid(a.S, a.g.B, a.Hq / HQ);
-    hipLaunchKernelGGL(k_decode_mla, grid, dim3(64 * NW), 0, st, p);
+    hipExtLaunchKernelGGL(k_decode_mla, grid, dim3(64 * NW), 0, st, a.ev_start, a.ev_stop, 0, p);
     return hipGetLastError();
 }
 

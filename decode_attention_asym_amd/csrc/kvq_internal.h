@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "../../include/kvq.h"
@@ -63,6 +64,9 @@ struct DecodeArgs {
     int64_t T, nblk;    // tokens, quantized blocks
     int R;              // residual keys
     int U;              // work units: nblk (+1 when R > 0)
+    // optional profiling events; the pass-1 launch records its own start and
+    // stop timestamps into them (hipExtLaunchKernel), with no extra packets
+    hipEvent_t ev_start, ev_stop;
 };
 
 Variant pick_variant(const kvq_cache& c, int Hq);

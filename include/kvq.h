@@ -180,9 +180,11 @@ kvq_status kv_decode_attention(const kvq_cache* cache, const void* q_fp16, int32
                                float softmax_scale, int32_t n_splits, void* out_fp16,
                                void* workspace, uint64_t workspace_bytes, void* hip_stream);
 
-/* Profiling hook: when both are non-NULL, later kv_decode_attention calls
- * record hipEvent_t ev_before / ev_after on their stream right before and
- * after the split-K pass-1 kernel.  NULL, NULL switches it off.  Process-wide. */
+/* Profiling hook: when both are non-NULL (hipEvent_t, created by the caller),
+ * later kv_decode_attention calls launch their split-K pass-1 kernel with
+ * hipExtLaunchKernel so that the launch itself records its start and stop
+ * timestamps into ev_before / ev_after (no separate event packets in the
+ * stream).  NULL, NULL switches it off.  Process-wide. */
 kvq_status kv_set_timing_events(void* ev_before, void* ev_after);
 
 /* Name of the decode kernel variant kv_decode_attention would launch. */
