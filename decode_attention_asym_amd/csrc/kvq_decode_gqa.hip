@@ -86,17 +86,17 @@ struct KState {
 template <int G>
 __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState& st, LdsK& L,
                                          Handoff& hb, const uint32_t* qw, int lane,
-                                         int64_t bh, int nxt, int end) {
+                                         int64_t bh, int nxt, const TileRun& run) {
     constexpr int NBT = 64 / G;
     const int n = lane & 15, kg = lane >> 4;
     const int hh = lane >> 4, chunk = lane & 15;
 
     // ---- stage key codes and side values, then prefetch tile i + 2
     stage_keys<G>(cur, L.kl, L.ksl, lane);
-    // unconditional (clamped to the last tile of the run) so that every path
-    // has the same loads in flight and the wait before staging covers only
-    // the older tile
-    load_ktile<G>(p, bh, nxt < end ? nxt : end - 1, lane, cur);
+    // unconditional (past the run it reads nothing) so that every path has
+    // the same loads in flight and the wait before staging covers only the
+    // older tile
+    load_ktile<G>(p, run, bh, nxt, lane, cur);
     wave_sync();
 
     // ---- q' = q * s_k as fp16 hi/lo rows, sigma2 * sum_c q z_k per (block, head)
@@ -226,12 +226,12 @@ struct VState {
 // Value side of one tile, reading p and alpha from `hb`.
 __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VState& st, LdsV& L,
                                            const Handoff& hb, int lane, int64_t bh,
-                                           int nxt, int end) {
+                                           int nxt, const TileRun& run) {
     const int n = lane & 15, kg = lane >> 4;
     const int hh = lane >> 4, chunk = lane & 15;
     // ---- stage value codes and side values, then prefetch tile i + 2
     stage_values(cur, L.vl, L.vsl, lane);
-    load_vtile(p, bh, nxt < end ? nxt : end - 1, lane, cur);
+    load_vtile(p, run, bh, nxt, lane, cur);
 
     // ---- rescale what was accumulated with the previous maxima
     const float a0 = hb.alpha[0], a1 = hb.alpha[1], a2 = hb.alpha[2], a3 = hb.alpha[3];
@@ -322,8 +322,9 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
         KState st;
         st.m0 = st.m1 = st.m2 = st.m3 = -INFINITY;
         KTile ta, tb;
-        load_ktile<G>(p, bh, t_lo, lane, ta);
-        load_ktile<G>(p, bh, ntl > 1 ? t_lo + 1 : t_lo, lane, tb);
+        const TileRun run = tile_run<G>(p, bh, t_lo, t_hi);
+        load_ktile<G>(p, run, bh, t_lo, lane, ta);
+        load_ktile<G>(p, run, bh, t_lo + 1, lane, tb);
         // keep these loads ahead of (not interleaved with) the prefetch of tile 2
         __builtin_amdgcn_sched_barrier(0);
         // two register tiles in flight: tile j is staged from set j & 1,
@@ -331,17 +332,17 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
         // The loop body always processes two tiles, so every path has the
         // same loads in flight and the wait before staging covers only the
         // older tile.
-        key_tile<G>(p, ta, st, L.k, L.hb[0], qv, lane, bh, t_lo + 2, t_hi);
+        key_tile<G>(p, ta, st, L.k, L.hb[0], qv, lane, bh, t_lo + 2, run);
         __syncthreads();
         int j = 1;
         for (; j + 1 < ntl; j += 2) {
-            key_tile<G>(p, tb, st, L.k, L.hb[1], qv, lane, bh, t_lo + j + 2, t_hi);
+            key_tile<G>(p, tb, st, L.k, L.hb[1], qv, lane, bh, t_lo + j + 2, run);
             __syncthreads();
-            key_tile<G>(p, ta, st, L.k, L.hb[0], qv, lane, bh, t_lo + j + 3, t_hi);
+            key_tile<G>(p, ta, st, L.k, L.hb[0], qv, lane, bh, t_lo + j + 3, run);
             __syncthreads();
         }
         if (j < ntl) {
-            key_tile<G>(p, tb, st, L.k, L.hb[1], qv, lane, bh, t_lo + j + 2, t_hi);
+            key_tile<G>(p, tb, st, L.k, L.hb[1], qv, lane, bh, t_lo + j + 2, run);
             __syncthreads();
         }
         if (lane < HG) L.misc[lane] = sel4(lane, st.m0, st.m1, st.m2, st.m3);
@@ -357,21 +358,22 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
             for (int u = 0; u < 4; ++u) st.O[P][u] = f32x4{0.f, 0.f, 0.f, 0.f};
         // value work trails the key work by one tile: tile j after barrier j
         VTile ta, tb;
-        load_vtile(p, bh, t_lo, lane, ta);
-        load_vtile(p, bh, ntl > 1 ? t_lo + 1 : t_lo, lane, tb);
+        const TileRun run = tile_run<G>(p, bh, t_lo, t_hi);
+        load_vtile(p, run, bh, t_lo, lane, ta);
+        load_vtile(p, run, bh, t_lo + 1, lane, tb);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        value_tile(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + 2, t_hi);
+        value_tile(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + 2, run);
         __syncthreads();
         int j = 1;
         for (; j + 1 < ntl; j += 2) {
-            value_tile(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, t_hi);
+            value_tile(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
             __syncthreads();
-            value_tile(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + j + 3, t_hi);
+            value_tile(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + j + 3, run);
             __syncthreads();
         }
         if (j < ntl) {
-            value_tile(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, t_hi);
+            value_tile(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
             __syncthreads();
         }
         // ---- epilogue: l and the value-zero sums over the 16 lanes of a head

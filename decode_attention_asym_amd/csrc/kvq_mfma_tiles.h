@@ -213,7 +213,12 @@ __device__ __forceinline__ void wave_sync() {
 // ---- one 64-token tile in registers, 16-byte loads, no lane reads what
 // another lane reads: key codes 2 KB, key side 512 B (G = 64) or 1 KB
 // (G = 32); value codes 2 KB, value side 1 KB.
-
+//
+// The code tiles of a workgroup's run [t_lo, t_hi) are read through buffer
+// resources that span exactly that run: the prefetches that run past its
+// end (every path issues the same loads, see the kernels) then return zeros
+// without touching memory.  The small side-value loads are clamped to the
+// last tile instead.
 struct KTile {
     uint4 k0, k1;   // key codes, 32 B per lane
     uint4 ks;       // key scale (lanes 0..31) / zero (lanes 32..63)
@@ -223,13 +228,41 @@ struct VTile {
     uint4 vs;       // value scale (lanes 0..31) / zero (lanes 32..63) of two tokens
 };
 
+struct TileRun {
+    __amdgpu_buffer_rsrc_t kc, vc;
+    int t0, t_last;
+};
+
 template <int G>
-__device__ __forceinline__ void load_ktile(const MfmaParams& p, int64_t bh, int64_t tt, int lane, KTile& r) {
+__device__ __forceinline__ TileRun tile_run(const MfmaParams& p, int64_t bh, int t_lo, int t_hi) {
     constexpr int NBT = 64 / G, W = G / 16;
-    const uint4* kb = reinterpret_cast<const uint4*>(p.kc + (bh * p.nblk_cap + tt * NBT) * D * W);
-    r.k0 = ld_stream(kb + lane);
-    r.k1 = ld_stream(kb + lane + 64);
-    const uint16_t* kside = (lane < 32 ? p.ks : p.kz) + (bh * p.nblk_cap + tt * NBT) * D;
+    constexpr int FLAGS = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
+    TileRun r;
+    const int bytes = (t_hi - t_lo) * 2048;
+    r.kc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(p.kc + (bh * p.nblk_cap + int64_t(t_lo) * NBT) * D * W),
+                                             0, bytes, FLAGS);
+    r.vc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(p.vc + (bh * p.cap + int64_t(t_lo) * 64) * 8), 0,
+                                             bytes, FLAGS);
+    r.t0 = t_lo;
+    r.t_last = t_hi - 1;
+    return r;
+}
+
+// 16-byte streaming load at byte offset off of a run (non-temporal)
+__device__ __forceinline__ uint4 ld_run(__amdgpu_buffer_rsrc_t rs, int off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int G>
+__device__ __forceinline__ void load_ktile(const MfmaParams& p, const TileRun& run, int64_t bh, int tt, int lane,
+                                           KTile& r) {
+    constexpr int NBT = 64 / G;
+    const int off = (tt - run.t0) * 2048 + 16 * lane;
+    r.k0 = ld_run(run.kc, off);
+    r.k1 = ld_run(run.kc, off + 1024);
+    const int ts = tt < run.t_last ? tt : run.t_last;
+    const uint16_t* kside = (lane < 32 ? p.ks : p.kz) + (bh * p.nblk_cap + int64_t(ts) * NBT) * D;
     if (G == 64) {
         const uint2 v = ld_stream(reinterpret_cast<const uint2*>(kside) + (lane & 31));
         r.ks = make_uint4(v.x, v.y, 0u, 0u);
@@ -238,13 +271,15 @@ __device__ __forceinline__ void load_ktile(const MfmaParams& p, int64_t bh, int6
     }
 }
 
-__device__ __forceinline__ void load_vtile(const MfmaParams& p, int64_t bh, int64_t tt, int lane, VTile& r) {
-    const uint4* vb = reinterpret_cast<const uint4*>(p.vc + (bh * p.cap + tt * 64) * 8);
-    r.v0 = ld_stream(vb + lane);
-    r.v1 = ld_stream(vb + lane + 64);
+__device__ __forceinline__ void load_vtile(const MfmaParams& p, const TileRun& run, int64_t bh, int tt, int lane,
+                                           VTile& r) {
+    const int off = (tt - run.t0) * 2048 + 16 * lane;
+    r.v0 = ld_run(run.vc, off);
+    r.v1 = ld_run(run.vc, off + 1024);
+    const int64_t ts = tt < run.t_last ? tt : run.t_last;
     // lane l (mod 32) takes tokens t = 4(l >> 1) + (l & 1) and t + 2: a pair
     // in the quad order of the K dimension
-    const uint16_t* vside = (lane < 32 ? p.vs : p.vz) + (bh * p.cap + tt * 64) * 4;
+    const uint16_t* vside = (lane < 32 ? p.vs : p.vz) + (bh * p.cap + ts * 64) * 4;
     const int t = 4 * ((lane & 31) >> 1) + (lane & 1);
     const uint2 a = ld_stream(reinterpret_cast<const uint2*>(vside + 4 * t));
     const uint2 b = ld_stream(reinterpret_cast<const uint2*>(vside + 4 * (t + 2)));
