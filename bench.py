@@ -32,8 +32,8 @@ DEFAULT_WORKLOAD = "mistral_7b_gqa_t32805"
 
 
 class HipEvents:
-    """hipEvent_t pairs through libamdhip64 (the library records them on its
-    launch stream around the pass-1 kernel)."""
+    """hipEvent_t pairs through libamdhip64 (the pass-1 launch records its own
+    start and stop timestamps into them)."""
 
     def __init__(self):
         self.hip = C.CDLL("libamdhip64.so")
@@ -224,14 +224,26 @@ def main():
     hip = HipEvents()
     evs = [(hip.create(), hip.create()) for _ in range(args.steps)]
 
+    # the step loop calls the C ABI with everything it needs precomputed, so
+    # that host-side Python does not pace the small workloads
+    lib = kvq.lib()
+    c_append, c_decode, c_timing = lib.kv_quantize_append, lib.kv_decode_attention, lib.kv_set_timing_events
+    handles = [c.handle for c in dcs]
+    kptr = [knew[j].data_ptr() for j in range(knew.shape[0])]
+    vptr = [vnew[j].data_ptr() for j in range(vnew.shape[0])]
+    n_new = knew.shape[-2]
+    sptr, qptr, optr, wptr, wbytes = stream.cuda_stream, qd.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel()
+
     def step(i, timed):
         # step i: layer i % L receives its token i // L
-        c = dcs[i % L]
+        h = handles[i % L]
         if timed:
-            kvq.kv_set_timing_events(*evs[i - args.warmup])
-        c.append(knew[i // L], vnew[i // L])
-        kvq.kv_decode_attention(c.handle, qd.data_ptr(), w.n_q_heads, w.sigma, args.splits,
-                                out.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream)
+            st = c_timing(*evs[i - args.warmup])
+            assert st == 0, st
+        st = c_append(h, kptr[i // L], vptr[i // L], n_new, 0, sptr)
+        assert st == 0, kvq.kvq_status_str(st)
+        st = c_decode(h, qptr, w.n_q_heads, w.sigma, args.splits, optr, wptr, wbytes, sptr)
+        assert st == 0, kvq.kvq_status_str(st)
 
     for i in range(args.warmup):
         step(i, False)

@@ -150,25 +150,22 @@ kvq_status kv_quantize_append(kvq_cache* c, const void* k, const void* v, int64_
     if (manual && R + n > G) return KVQ_E_CAPACITY;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_quant_values(*c, g, v, n, 0, n, c->T, st);
-    if (e != hipSuccess) return KVQ_E_HIP;
-    if (manual) {
-        e = launch_resid_copy(*c, g, k, n, 0, R, n, st);
-        if (e != hipSuccess) return KVQ_E_HIP;
+    const int64_t pending = R + n;           // keys not yet in a quantized block
+    if (manual || pending < G) {
+        // no block completes (with NO_AUTOFLUSH a full residual waits for
+        // kv_flush_residual): values and residual keys in one launch
+        if (launch_append_rows(*c, g, k, v, n, R, st) != hipSuccess) return KVQ_E_HIP;
         c->T += n;
         return KVQ_OK;
     }
-    const int64_t pending = R + n;           // keys not yet in a quantized block
-    const int64_t full = pending / G;        // blocks that complete now
+    hipError_t e = launch_quant_values(*c, g, v, n, 0, n, c->T, st);
+    if (e != hipSuccess) return KVQ_E_HIP;
+    const int64_t full = pending / G;        // blocks that complete now (>= 1)
     const int64_t tail = pending - full * G; // keys left in the residual
-    if (full > 0) {
-        // block tokens < c->T come from the residual (rows t - nblk*G)
-        e = launch_quant_keys(*c, g, k, n, c->T, c->nblk * G, c->nblk, full, st);
-        if (e != hipSuccess) return KVQ_E_HIP;
-        if (tail > 0) e = launch_resid_copy(*c, g, k, n, n - tail, 0, tail, st);
-    } else {
-        e = launch_resid_copy(*c, g, k, n, 0, R, n, st);
-    }
+    // block tokens < c->T come from the residual (rows t - nblk*G)
+    e = launch_quant_keys(*c, g, k, n, c->T, c->nblk * G, c->nblk, full, st);
+    if (e != hipSuccess) return KVQ_E_HIP;
+    if (tail > 0) e = launch_resid_copy(*c, g, k, n, n - tail, 0, tail, st);
     if (e != hipSuccess) return KVQ_E_HIP;
     c->nblk += full;
     c->T += n;

@@ -46,6 +46,12 @@ hipError_t launch_quant_keys(const kvq_cache& c, const Geom& g, const void* k_in
 hipError_t launch_resid_copy(const kvq_cache& c, const Geom& g, const void* k_in, int64_t n_in,
                              int64_t src0, int64_t dst0, int64_t m, hipStream_t st);
 
+// An append of n rows that completes no key block (R + n < G, R residual
+// keys before it), in one launch: the n value rows are quantized at cache
+// tokens c.T ... and the n key rows go to residual rows R ...
+hipError_t launch_append_rows(const kvq_cache& c, const Geom& g, const void* k_in, const void* v_in,
+                              int64_t n, int64_t R, hipStream_t st);
+
 // ---- decode kernels (kvq_decode*.hip) ----
 
 enum Variant { V_GENERIC = 0, V_MHA = 1, V_GQA = 2, V_MLA = 3 };

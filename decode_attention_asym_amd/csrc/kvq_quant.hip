@@ -79,17 +79,32 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
 // group and reduce min/max by shuffles.
 constexpr int VT = 4;
 
+struct ValueArgs {
+    const uint16_t* vin;
+    int64_t n_in, row0, n_tok, t_dst0, cap;
+    int vd, BH;
+    uint32_t* codes;
+    uint16_t *scale, *zero;
+};
+
+// threads that quantize n_tok value rows: BH * ceil(n_tok / VT) * (vd / 8),
+// a multiple of 4 (vd / 8 is)
+__host__ __device__ inline int64_t value_threads(int BH, int64_t n_tok, int vd) { return int64_t(BH) * ((n_tok + VT - 1) / VT) * (vd / 8); }
+
+// Thread idx < value_threads(...) quantizes 8 channels of up to VT rows;
+// the 4 threads of a 32-channel group are adjacent lanes and exchange their
+// min / max by shuffles, so callers keep whole 4-lane groups together.
 template <int BITS>
-__global__ __launch_bounds__(256) void k_quant_values(
-    const uint16_t* __restrict__ vin, int64_t n_in, int64_t row0, int64_t n_tok,
-    int64_t t_dst0, int vd, int64_t cap, int BH, uint32_t* __restrict__ codes,
-    uint16_t* __restrict__ scale, uint16_t* __restrict__ zero) {
+__device__ __forceinline__ void quant_values_thread(const ValueArgs& a, int64_t idx) {
+    const uint16_t* __restrict__ vin = a.vin;
+    const int64_t n_in = a.n_in, row0 = a.row0, n_tok = a.n_tok, t_dst0 = a.t_dst0, cap = a.cap;
+    const int vd = a.vd;
+    uint32_t* __restrict__ codes = a.codes;
+    uint16_t* __restrict__ scale = a.scale;
+    uint16_t* __restrict__ zero = a.zero;
     constexpr float L = float((1 << BITS) - 1);
     const int tpt = vd / 8;
     const int64_t nq = (n_tok + VT - 1) / VT;
-    const int64_t total = int64_t(BH) * nq * tpt;
-    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (idx >= total) return;   // a whole 4-lane group leaves together (tpt % 4 == 0)
     const int sub = int(idx % tpt);
     const int64_t tq = (idx / tpt) % nq;
     const int64_t bh = idx / tpt / nq;
@@ -141,6 +156,13 @@ __global__ __launch_bounds__(256) void k_quant_values(
             zero[side] = float_to_half_bits(q.mn);
         }
     }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_quant_values(ValueArgs a) {
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= value_threads(a.BH, a.n_tok, a.vd)) return;   // whole 4-lane groups leave together
+    quant_values_thread<BITS>(a, idx);
 }
 
 // -------------------------------------------------------------------- keys
@@ -249,18 +271,42 @@ __global__ __launch_bounds__(256) void k_quant_keys(
 }
 
 // ---------------------------------------------------------- residual copy
-__global__ __launch_bounds__(256) void k_resid_copy(const uint16_t* __restrict__ kin, int64_t n_in,
-                                                    int64_t src0, int64_t dst0, int64_t m, int kd,
-                                                    int G, int BH, uint16_t* __restrict__ resid) {
-    const int vpr = kd / 8;
-    const int64_t total = int64_t(BH) * m * vpr;
-    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (idx >= total) return;
+struct ResidArgs {
+    const uint16_t* kin;
+    int64_t n_in, src0, dst0, m;
+    int kd, G, BH;
+    uint16_t* resid;
+};
+
+__host__ __device__ inline int64_t resid_threads(const ResidArgs& a) { return int64_t(a.BH) * a.m * (a.kd / 8); }
+
+// thread idx < resid_threads(...) copies 8 channels of one key row into the residual
+__device__ __forceinline__ void resid_copy_thread(const ResidArgs& a, int64_t idx) {
+    const int vpr = a.kd / 8;
     const int v = int(idx % vpr);
-    const int64_t r = (idx / vpr) % m;
-    const int64_t bh = idx / vpr / m;
-    *reinterpret_cast<uint4*>(resid + (bh * G + dst0 + r) * kd + v * 8) =
-        *reinterpret_cast<const uint4*>(kin + (bh * n_in + src0 + r) * kd + v * 8);
+    const int64_t r = (idx / vpr) % a.m;
+    const int64_t bh = idx / vpr / a.m;
+    *reinterpret_cast<uint4*>(a.resid + (bh * a.G + a.dst0 + r) * a.kd + v * 8) =
+        *reinterpret_cast<const uint4*>(a.kin + (bh * a.n_in + a.src0 + r) * a.kd + v * 8);
+}
+
+__global__ __launch_bounds__(256) void k_resid_copy(ResidArgs a) {
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= resid_threads(a)) return;
+    resid_copy_thread(a, idx);
+}
+
+// An append that completes no key block: the value rows are quantized and
+// the key rows land in the residual, in one launch (value threads first;
+// their count is a multiple of 4, so no 4-lane group is split).
+template <int BITS>
+__global__ __launch_bounds__(256) void k_append_rows(ValueArgs va, ResidArgs ka) {
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t nv = value_threads(va.BH, va.n_tok, va.vd);
+    if (idx < nv)
+        quant_values_thread<BITS>(va, idx);
+    else if (idx - nv < resid_threads(ka))
+        resid_copy_thread(ka, idx - nv);
 }
 
 inline unsigned grid_of(int64_t threads) { return unsigned((threads + 255) / 256); }
@@ -281,21 +327,61 @@ hipError_t launch_keys_t(const kvq_cache& c, const Geom& g, const void* k_in, in
 
 }  // namespace
 
+namespace {
+ValueArgs value_args(const kvq_cache& c, const Geom& g, const void* v_in, int64_t n_in, int64_t row0,
+                     int64_t n_tok, int64_t t_dst0) {
+    ValueArgs a;
+    a.vin = static_cast<const uint16_t*>(v_in);
+    a.n_in = n_in;
+    a.row0 = row0;
+    a.n_tok = n_tok;
+    a.t_dst0 = t_dst0;
+    a.cap = g.cap;
+    a.vd = g.vd;
+    a.BH = g.B * g.Hkv;
+    a.codes = static_cast<uint32_t*>(c.buf.v_codes);
+    a.scale = static_cast<uint16_t*>(c.buf.v_scale);
+    a.zero = static_cast<uint16_t*>(c.buf.v_zero);
+    return a;
+}
+ResidArgs resid_args(const kvq_cache& c, const Geom& g, const void* k_in, int64_t n_in, int64_t src0,
+                     int64_t dst0, int64_t m) {
+    ResidArgs a;
+    a.kin = static_cast<const uint16_t*>(k_in);
+    a.n_in = n_in;
+    a.src0 = src0;
+    a.dst0 = dst0;
+    a.m = m;
+    a.kd = g.kd;
+    a.G = g.kG;
+    a.BH = g.B * g.Hkv;
+    a.resid = static_cast<uint16_t*>(c.buf.k_resid);
+    return a;
+}
+}  // namespace
+
 hipError_t launch_quant_values(const kvq_cache& c, const Geom& g, const void* v_in, int64_t n_in,
                                int64_t row0, int64_t n_tok, int64_t t_dst0, hipStream_t st) {
     if (n_tok <= 0) return hipSuccess;
-    const int BH = g.B * g.Hkv;
-    const int64_t threads = int64_t(BH) * ((n_tok + VT - 1) / VT) * (g.vd / 8);
-    const auto* vin = static_cast<const uint16_t*>(v_in);
-    auto* codes = static_cast<uint32_t*>(c.buf.v_codes);
-    auto* sc = static_cast<uint16_t*>(c.buf.v_scale);
-    auto* ze = static_cast<uint16_t*>(c.buf.v_zero);
+    const ValueArgs a = value_args(c, g, v_in, n_in, row0, n_tok, t_dst0);
+    const unsigned grid = grid_of(value_threads(a.BH, n_tok, a.vd));
     if (g.vbits == 2)
-        hipLaunchKernelGGL(k_quant_values<2>, dim3(grid_of(threads)), dim3(256), 0, st, vin, n_in,
-                           row0, n_tok, t_dst0, g.vd, g.cap, BH, codes, sc, ze);
+        hipLaunchKernelGGL(k_quant_values<2>, dim3(grid), dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL(k_quant_values<4>, dim3(grid_of(threads)), dim3(256), 0, st, vin, n_in,
-                           row0, n_tok, t_dst0, g.vd, g.cap, BH, codes, sc, ze);
+        hipLaunchKernelGGL(k_quant_values<4>, dim3(grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_rows(const kvq_cache& c, const Geom& g, const void* k_in, const void* v_in,
+                              int64_t n, int64_t R, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const ValueArgs va = value_args(c, g, v_in, n, 0, n, c.T);
+    const ResidArgs ka = resid_args(c, g, k_in, n, 0, R, n);
+    const unsigned grid = grid_of(value_threads(va.BH, n, va.vd) + resid_threads(ka));
+    if (g.vbits == 2)
+        hipLaunchKernelGGL(k_append_rows<2>, dim3(grid), dim3(256), 0, st, va, ka);
+    else
+        hipLaunchKernelGGL(k_append_rows<4>, dim3(grid), dim3(256), 0, st, va, ka);
     return hipGetLastError();
 }
 
@@ -320,11 +406,8 @@ hipError_t launch_quant_keys(const kvq_cache& c, const Geom& g, const void* k_in
 hipError_t launch_resid_copy(const kvq_cache& c, const Geom& g, const void* k_in, int64_t n_in,
                              int64_t src0, int64_t dst0, int64_t m, hipStream_t st) {
     if (m <= 0) return hipSuccess;
-    const int BH = g.B * g.Hkv;
-    const int64_t threads = int64_t(BH) * m * (g.kd / 8);
-    hipLaunchKernelGGL(k_resid_copy, dim3(grid_of(threads)), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(k_in), n_in, src0, dst0, m, g.kd, g.kG, BH,
-                       static_cast<uint16_t*>(c.buf.k_resid));
+    const ResidArgs a = resid_args(c, g, k_in, n_in, src0, dst0, m);
+    hipLaunchKernelGGL(k_resid_copy, dim3(grid_of(resid_threads(a))), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
