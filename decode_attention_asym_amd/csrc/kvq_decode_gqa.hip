@@ -57,7 +57,8 @@ struct LdsK {
 struct LdsV {
     __attribute__((aligned(16))) uint32_t vl[VTILE_DW];      // value codes, cache layout
     __attribute__((aligned(16))) uint32_t pa[2 * 16 * ASTR];  // p' rows (fp16) per pass
-    __attribute__((aligned(16))) uint32_t vsl[2 * 128];      // value [scale|zero][group][token pair]
+    // value [scale|zero][group][token pair], then a row of fp16 ones and a row of zeros
+    __attribute__((aligned(16))) uint32_t vsl[2 * 128 + 2 * 32];
 };
 
 // softmax weights p as fp16 hi + lo pairs: [head][token pair], dword 2k + j
@@ -219,8 +220,10 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState
 
 struct VState {
     f32x4 O[2][4];   // PV accumulators [pass][channel tile]
-    float lsum;      // this lane's share of sum p for head (lane >> 4)
-    float vb[4];     // this lane's share of sum p z_v per group, head (lane >> 4)
+    // sum_t p z_v per (head, group) and l = sum_t p on MFMA: rows 2h (hi),
+    // 2h + 1 (lo) of head h (rows 8..15 repeat them), column g < 4 the
+    // zero-point sum of group g, column 4 the weight sum
+    f32x4 Z;
 };
 
 // Value side of one tile, reading p and alpha from `hb`.
@@ -247,27 +250,22 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
                 st.O[P][u][2] *= aB;
                 st.O[P][u][3] *= aB;
             }
-        const float ah = sel4(hh, a0, a1, a2, a3);
-        st.lsum *= ah;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) st.vb[g] *= ah;
+        st.Z[0] *= aA;
+        st.Z[1] *= aA;
+        st.Z[2] *= aB;
+        st.Z[3] *= aB;
     }
     wave_sync();
 
-    // ---- p' = p * s_v as fp16 hi/lo rows per value group; sum_t p, sum_t p z_v.
-    // Lane (hh, chunk): tokens 4 chunk .. 4 chunk + 3 of head hh, as the pairs
-    // (t0, t2), (t1, t3) that the rows hold in quad order.
+    // ---- p' = p * s_v as fp16 hi/lo rows per value group.  Lane (hh, chunk):
+    // tokens 4 chunk .. 4 chunk + 3 of head hh, as the pairs (t0, t2),
+    // (t1, t3) that the rows hold in quad order.
     {
         const uint2 ph = *reinterpret_cast<const uint2*>(hb.ph + hh * PHS + 2 * chunk);
         const uint2 pq = *reinterpret_cast<const uint2*>(hb.pq + hh * PHS + 2 * chunk);
-        // p of tokens t0, t2 (pair x) and t1, t3 (pair y) in fp32
-        const float p0 = join_lo(ph.x, pq.x, p.neg1), p2 = join_hi(ph.x, pq.x, p.neg1);
-        const float p1 = join_lo(ph.y, pq.y, p.neg1), p3 = join_hi(ph.y, pq.y, p.neg1);
-        st.lsum += (p0 + p1) + (p2 + p3);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const uint2 sv = *reinterpret_cast<const uint2*>(L.vsl + g * 32 + 2 * chunk);
-            const uint2 zv = *reinterpret_cast<const uint2*>(L.vsl + 128 + g * 32 + 2 * chunk);
             uint32_t h0, l0, h1, l1;
             split_prod_hl(ph.x, pq.x, sv.x, h0, l0);
             split_prod_hl(ph.y, pq.y, sv.y, h1, l1);
@@ -275,7 +273,21 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
             uint32_t* rowp = L.pa + ((((g >> 1) * 2 + (g & 1)) * 4 + hh) * 2) * ASTR + 2 * chunk;
             *reinterpret_cast<uint2*>(rowp) = make_uint2(h0, h1);
             *reinterpret_cast<uint2*>(rowp + ASTR) = make_uint2(l0, l1);
-            st.vb[g] = fmaf(p3, hi_h(zv.y), fmaf(p1, lo_h(zv.y), fmaf(p2, hi_h(zv.x), fmaf(p0, lo_h(zv.x), st.vb[g]))));
+        }
+    }
+    // ---- sum_t p z_v and sum_t p: A = the weights' hi/lo rows (row n & 7 =
+    // head (n & 7) >> 1, hi or lo), B column n = the zero-points of group n
+    // (n < 4), ones (n = 4) or zeros, over the tile's 64 tokens in quad order
+    {
+        const int r = n & 7;
+        const uint32_t* arow = ((r & 1) ? hb.pq : hb.ph) + (r >> 1) * PHS + 4 * kg;
+        const uint32_t* brow = L.vsl + 128 + (n < 5 ? n : 5) * 32 + 4 * kg;
+#pragma unroll
+        for (int ksx = 0; ksx < 2; ++ksx) {
+            const uint4 a = *reinterpret_cast<const uint4*>(arow + 16 * ksx);
+            const uint4 z = *reinterpret_cast<const uint4*>(brow + 16 * ksx);
+            st.Z = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a.x, a.y, a.z, a.w), as_f16x8(z.x, z.y, z.z, z.w),
+                                                          st.Z, 0, 0, 0);
         }
     }
     wave_sync();
@@ -349,9 +361,9 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
         __syncthreads();
     } else {
         VState st;
-        st.lsum = 0.0f;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) st.vb[g] = 0.0f;
+        st.Z = f32x4{0.f, 0.f, 0.f, 0.f};
+        // the ones and zeros rows after the side values (B operand of the sums)
+        L.v.vsl[256 + lane] = lane < 32 ? 0x3c003c00u : 0u;
 #pragma unroll
         for (int P = 0; P < 2; ++P)
 #pragma unroll
@@ -376,15 +388,14 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
             value_tile(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
             __syncthreads();
         }
-        // ---- epilogue: l and the value-zero sums over the 16 lanes of a head
-        const float lsum = row_sum16(st.lsum);
-        float vbs[4];
+        // ---- epilogue: l and the value-zero sums, hi + lo rows of each head
+        if (kg < 2 && n < 5) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) vbs[g] = row_sum16(st.vb[g]);
-        if (chunk == 0) {
-            L.misc[16 + hh] = lsum;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) L.misc[32 + hh * 4 + g] = vbs[g];
+            for (int j = 0; j < 2; ++j) {
+                const int h = 2 * kg + j;
+                const float v = st.Z[2 * j] + st.Z[2 * j + 1];
+                L.misc[n < 4 ? 32 + h * 4 + n : 16 + h] = v;
+            }
         }
         wave_sync();
         if ((kg >> 1) == (n >> 3)) {
