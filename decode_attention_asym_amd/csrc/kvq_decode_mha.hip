@@ -37,7 +37,8 @@ struct LdsK {
 struct LdsV {
     __attribute__((aligned(16))) uint32_t vl[VTILE_DW];  // value codes, cache layout
     __attribute__((aligned(16))) uint32_t pa[8 * ASTR];   // p' rows [group][hi, lo]
-    __attribute__((aligned(16))) uint32_t vsl[2 * 128];   // value [scale|zero][group][token pair]
+    // value [scale|zero][group][token pair], then a row of fp16 ones and a row of zeros
+    __attribute__((aligned(16))) uint32_t vsl[2 * 128 + 2 * 32];
 };
 
 // softmax weights p as fp16 hi + lo pairs: dword 2k + j holds tokens
@@ -158,8 +159,9 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, float&
 
 struct VState {
     f32x4 O[2][4];   // PV accumulators [channel half][code position]
-    float lsum;      // this lane's share of sum p
-    float vb0, vb1;  // this lane's share of sum p z_v, groups 2gp and 2gp + 1
+    // sum_t p z_v per group and l = sum_t p on MFMA: even rows hi, odd rows
+    // lo; column g < 4 the zero-point sum of group g, column 4 the weight sum
+    f32x4 Z;
 };
 
 // Value side of one tile, reading p and alpha from `hb`.
@@ -178,9 +180,7 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
         for (int P = 0; P < 2; ++P)
 #pragma unroll
             for (int u = 0; u < 4; ++u) st.O[P][u] *= alpha;
-        st.lsum *= alpha;
-        st.vb0 *= alpha;
-        st.vb1 *= alpha;
+        st.Z *= alpha;
     }
     wave_sync();
 
@@ -191,7 +191,6 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
         const int tp = lane & 31, gp = lane >> 5;
         const uint32_t ph = hb.ph[tp], pq = hb.pq[tp];
         const uint32_t s0 = L.vsl[(2 * gp) * 32 + tp], s1 = L.vsl[(2 * gp + 1) * 32 + tp];
-        const uint32_t z0 = L.vsl[128 + (2 * gp) * 32 + tp], z1 = L.vsl[128 + (2 * gp + 1) * 32 + tp];
         uint32_t h, l;
         split_prod_hl(ph, pq, s0, h, l);
         L.pa[(4 * gp) * ASTR + tp] = h;
@@ -199,10 +198,20 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
         split_prod_hl(ph, pq, s1, h, l);
         L.pa[(4 * gp + 2) * ASTR + tp] = h;
         L.pa[(4 * gp + 3) * ASTR + tp] = l;
-        const float pa = join_lo(ph, pq, p.neg1), pb = join_hi(ph, pq, p.neg1);
-        st.lsum += gp == 0 ? pa + pb : 0.0f;
-        st.vb0 = fmaf(pb, hi_h(z0), fmaf(pa, lo_h(z0), st.vb0));
-        st.vb1 = fmaf(pb, hi_h(z1), fmaf(pa, lo_h(z1), st.vb1));
+    }
+    // ---- sum_t p z_v and sum_t p: A = the weights' hi (even rows) and lo
+    // (odd rows), B column n = the zero-points of group n (n < 4), ones
+    // (n = 4) or zeros, over the tile's 64 tokens in quad order
+    {
+        const uint32_t* arow = ((n & 1) ? hb.pq : hb.ph) + 4 * kg;
+        const uint32_t* brow = L.vsl + 128 + (n < 5 ? n : 5) * 32 + 4 * kg;
+#pragma unroll
+        for (int ksx = 0; ksx < 2; ++ksx) {
+            const uint4 a = *reinterpret_cast<const uint4*>(arow + 16 * ksx);
+            const uint4 z = *reinterpret_cast<const uint4*>(brow + 16 * ksx);
+            st.Z = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a.x, a.y, a.z, a.w), as_f16x8(z.x, z.y, z.z, z.w),
+                                                          st.Z, 0, 0, 0);
+        }
     }
     wave_sync();
 
@@ -273,7 +282,9 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
         __syncthreads();
     } else {
         VState st;
-        st.lsum = st.vb0 = st.vb1 = 0.0f;
+        st.Z = f32x4{0.f, 0.f, 0.f, 0.f};
+        // the ones and zeros rows after the side values (B operand of the sums)
+        L.v.vsl[256 + lane] = lane < 32 ? 0x3c003c00u : 0u;
 #pragma unroll
         for (int P = 0; P < 2; ++P)
 #pragma unroll
@@ -298,12 +309,12 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
             value_tile(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
             __syncthreads();
         }
-        // ---- epilogue: l and the value-zero sums over the wave
-        const float lsum = wave_sum(st.lsum);
-        const float r0 = row_sum16(st.vb0), r1 = row_sum16(st.vb1);
-        // lanes 0..31 hold groups 0, 1; lanes 32..63 groups 2, 3
-        const float vz0 = readlane_f(r0, 0) + readlane_f(r0, 16), vz1 = readlane_f(r1, 0) + readlane_f(r1, 16);
-        const float vz2 = readlane_f(r0, 32) + readlane_f(r0, 48), vz3 = readlane_f(r1, 32) + readlane_f(r1, 48);
+        // ---- epilogue: l and the value-zero sums (hi + lo rows; lanes 0..3
+        // hold groups 0..3, lane 4 the weight sum)
+        const float zsum = st.Z[0] + st.Z[1];
+        const float vz0 = readlane_f(zsum, 0), vz1 = readlane_f(zsum, 1);
+        const float vz2 = readlane_f(zsum, 2), vz3 = readlane_f(zsum, 3);
+        const float lsum = readlane_f(zsum, 4);
         if (kg == 0) {
             const bool up = (n >> 3) != 0;   // the column's group within the channel half
             // (scalar selects: an indexed array here would be lowered to scratch)
