@@ -31,6 +31,18 @@ constexpr float kTieBand = 0.5f - 0x1p-19f;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
 
+// The fp16 inputs are read exactly once: non-temporal loads keep them from
+// displacing other lines (measured: +4..5% on the bulk quantize; the same
+// hint on the code stores made it slower).
+typedef unsigned int qu4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_once4(const uint16_t* p) {
+    const qu4 v = __builtin_nontemporal_load(reinterpret_cast<const qu4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_once1(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
 // fl32(x - mn) for the fp16 half HALF of w, in one instruction: v_fma_mix
 // converts the fp16 operand exactly and rounds x * 1 + (-mn) once
 template <int HALF>
@@ -113,7 +125,7 @@ __device__ __forceinline__ void quant_values_thread(const ValueArgs& a, int64_t 
 #pragma unroll
     for (int j = 0; j < VT; ++j) {
         const int64_t tok = tq * VT + j;
-        raw[j] = tok < n_tok ? *reinterpret_cast<const uint4*>(vin + ((bh * n_in) + row0 + tok) * vd + sub * 8)
+        raw[j] = tok < n_tok ? ld_once4(vin + ((bh * n_in) + row0 + tok) * vd + sub * 8)
                              : make_uint4(0u, 0u, 0u, 0u);
     }
     const int vWT = vd * BITS / 32;
@@ -230,7 +242,7 @@ __global__ __launch_bounds__(256) void k_quant_keys(
         const int64_t tok = blk * G + sp * TG + i;
         const uint16_t* row = tok < in_tok0 ? resid + (bh * G + (tok - res_tok0)) * kd
                                             : kin + (bh * n_in + (tok - in_tok0)) * kd;
-        raw[i] = *reinterpret_cast<const uint32_t*>(row + 2 * cp);
+        raw[i] = ld_once1(row + 2 * cp);
     }
     // per-channel min / max over the rows, both channels at once (packed
     // fp16, exact; -0 is canonicalised after), then across the row ranges
