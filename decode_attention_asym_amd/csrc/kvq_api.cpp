@@ -71,6 +71,30 @@ void sizes_of(const kvq_cache_cfg& c, kvq_buffer_sizes* s) {
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E_HIP; }
 
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+void paged_sizes_of(const kvq_cache_cfg& c, int32_t n_pages, kvq_buffer_sizes* s) {
+    const Geom g = geom_of(c);
+    const uint64_t ph = uint64_t(n_pages) * g.Hkv;   // (page, KV head) block rows
+    s->k_codes = ph * g.kd * g.kW * 4;
+    s->k_scale = ph * g.kd * 2;
+    s->k_zero = s->k_scale;
+    s->k_resid = uint64_t(g.B) * g.Hkv * g.kG * g.kd * 2;
+    s->v_codes = ph * g.kG * g.vWT * 4;
+    s->v_scale = ph * g.kG * g.vNG * 2;
+    s->v_zero = s->v_scale;
+}
+
+PagedSeq paged_seq(const kvq_paged& c, const int32_t* table, const int32_t* lens, const int32_t* n_new) {
+    PagedSeq ps;
+    ps.table = table;
+    ps.lens = lens;
+    ps.n_new = n_new;
+    ps.maxb = int(c.cfg.max_tokens / c.cfg.key.group);
+    ps.n_pages = c.n_pages;
+    return ps;
+}
+
 }  // namespace
 
 extern "C" {
@@ -241,6 +265,107 @@ kvq_status kv_decode_attention(const kvq_cache* c, const void* q, int32_t Hq, fl
     }
     if (e != hipSuccess) return KVQ_E_HIP;
     return hip_status(launch_merge(a, st));
+}
+
+// ------------------------------------------------------------------ paged
+
+kvq_status kv_paged_buffer_bytes(const kvq_cache_cfg* cfg, int32_t n_pages, kvq_buffer_sizes* out) {
+    if (!out) return KVQ_E_NULL;
+    kvq_status st = check_cfg(cfg);
+    if (st != KVQ_OK) return st;
+    if (n_pages < 1) return KVQ_E_SHAPE;
+    paged_sizes_of(*cfg, n_pages, out);
+    return KVQ_OK;
+}
+
+kvq_status kv_paged_init(const kvq_cache_cfg* cfg, int32_t n_pages, const kvq_cache_buffers* bufs,
+                         kvq_paged** out) {
+    if (!out || !bufs) return KVQ_E_NULL;
+    kvq_status st = check_cfg(cfg);
+    if (st != KVQ_OK) return st;
+    if (n_pages < 1) return KVQ_E_SHAPE;
+    const void* ptrs[7] = {bufs->k_codes, bufs->k_scale, bufs->k_zero, bufs->k_resid,
+                           bufs->v_codes, bufs->v_scale, bufs->v_zero};
+    for (const void* p : ptrs) {
+        if (!p) return KVQ_E_NULL;
+        if (!aligned16(p)) return KVQ_E_ALIGN;
+    }
+    kvq_paged* c = new (std::nothrow) kvq_paged;
+    if (!c) return KVQ_E_NULL;
+    c->cfg = *cfg;
+    c->buf = *bufs;
+    c->n_pages = n_pages;
+    *out = c;
+    return KVQ_OK;
+}
+
+void kv_paged_destroy(kvq_paged* c) { delete c; }
+
+kvq_status kv_paged_append(kvq_paged* c, const void* k, const void* v, int32_t n_max, const int32_t* n_new,
+                           const int32_t* seq_lens, const int32_t* block_table, void* stream) {
+    if (!c) return KVQ_E_NULL;
+    if (n_max < 0) return KVQ_E_SHAPE;
+    if (n_max == 0) return KVQ_OK;
+    if (!k || !v || !seq_lens || !block_table) return KVQ_E_NULL;
+    if (!aligned16(k) || !aligned16(v)) return KVQ_E_ALIGN;
+    if (!aligned4(seq_lens) || !aligned4(block_table) || !aligned4(n_new)) return KVQ_E_ALIGN;
+    if (n_max > c->cfg.max_tokens) return KVQ_E_CAPACITY;
+    const Geom g = geom_of(c->cfg);
+    const PagedSeq ps = paged_seq(*c, block_table, seq_lens, n_new);
+    return hip_status(launch_paged_append(*c, g, k, v, n_max, ps, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kv_paged_workspace_bytes(const kvq_paged* c, int32_t Hq, int32_t max_len, int32_t n_splits,
+                                    uint64_t* bytes) {
+    if (!c || !bytes) return KVQ_E_NULL;
+    if (Hq < 1 || Hq % c->cfg.n_kv_heads != 0) return KVQ_E_SHAPE;
+    if (n_splits < 0 || n_splits > KVQ_MAX_SPLITS) return KVQ_E_SHAPE;
+    if (max_len < 0 || max_len > c->cfg.max_tokens) return KVQ_E_SHAPE;
+    const Variant v = pick_paged_variant(*c, Hq, n_splits, max_len);
+    const PagedPlan pp = plan_paged(*c, Hq, n_splits, max_len, v);
+    *bytes = uint64_t(c->cfg.batch) * Hq * pp.S * (c->cfg.value.dim + 2) * 4;
+    return KVQ_OK;
+}
+
+kvq_status kv_paged_decode(const kvq_paged* c, const void* q, int32_t Hq, float sigma, const int32_t* seq_lens,
+                           const int32_t* block_table, int32_t max_len, int32_t n_splits, void* out, void* ws,
+                           uint64_t ws_bytes, void* stream) {
+    if (!c || !q || !out || !ws || !seq_lens || !block_table) return KVQ_E_NULL;
+    if (Hq < 1 || Hq % c->cfg.n_kv_heads != 0) return KVQ_E_SHAPE;
+    if (n_splits < 0 || n_splits > KVQ_MAX_SPLITS) return KVQ_E_SHAPE;
+    if (max_len < 0 || max_len > c->cfg.max_tokens) return KVQ_E_SHAPE;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return KVQ_E_ALIGN;
+    if (!aligned4(seq_lens) || !aligned4(block_table)) return KVQ_E_ALIGN;
+    DecodeArgs a{};
+    a.pc = c;
+    a.g = geom_of(c->cfg);
+    const Variant v = pick_paged_variant(*c, Hq, n_splits, max_len);
+    const PagedPlan pp = plan_paged(*c, Hq, n_splits, max_len, v);
+    a.q = q;
+    a.Hq = Hq;
+    a.sigma = sigma;
+    a.out = out;
+    a.S = pp.S;
+    a.S_main = pp.S_main;
+    a.chunk = pp.chunk;
+    a.max_len = max_len;
+    a.ps = paged_seq(*c, block_table, seq_lens, nullptr);
+    const uint64_t need = uint64_t(a.g.B) * Hq * a.S * (a.g.vd + 2) * 4;
+    if (ws_bytes < need) return KVQ_E_WORKSPACE;
+    a.ws_acc = static_cast<float*>(ws);
+    a.ws_ml = a.ws_acc + uint64_t(a.g.B) * Hq * a.S * a.g.vd;
+    a.ev_start = g_ev_before;
+    a.ev_stop = g_ev_after;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e = v == V_GQA ? launch_decode_gqa_paged(a, st) : launch_decode_generic_paged(a, st);
+    if (e != hipSuccess) return KVQ_E_HIP;
+    return hip_status(launch_merge(a, st));
+}
+
+const char* kv_paged_variant(const kvq_paged* c, int32_t Hq, int32_t max_len) {
+    if (!c || Hq < 1 || Hq % c->cfg.n_kv_heads != 0 || max_len < 0 || max_len > c->cfg.max_tokens)
+        return "invalid";
+    return paged_variant_name(pick_paged_variant(*c, Hq, 0, max_len));
 }
 
 kvq_status kv_set_timing_events(void* before, void* after) {

@@ -28,25 +28,46 @@ struct GenParams {
     int64_t T, nblk, cap, nblk_cap;
     int kd, kG, kbits, kW, vd, vbits, vWT, vNG;
     float sigma2;   // softmax scale * log2(e): logits and maxima in log2 units
+    // paged caches: block table [B][maxb], lengths [B] (clamped to
+    // [0, max_len]), pool size, key blocks per split
+    const int32_t *table, *lens;
+    int maxb, npages, chunk, max_len;
 };
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 
-__device__ __forceinline__ float key_hat(const GenParams& p, int64_t bh, int64_t t, int c) {
-    const int64_t Tq = p.nblk * p.kG;
-    if (t >= Tq) return h2f(p.kr[(bh * p.kG + (t - Tq)) * p.kd + c]);
+// block row of key block j of (b, kvh): key codes at row * kd * kW words,
+// key side values at row * kd, value rows row * kG + i.  Contiguous:
+// (b * Hkv + kvh) * nblk_cap + j; paged: page * Hkv + kvh (the table entry
+// clamped into the pool, so a bad entry never reads outside the arrays).
+template <bool PAGED>
+__device__ __forceinline__ int64_t block_row(const GenParams& p, int b, int kvh, int64_t j) {
+    if (PAGED) {
+        int pg = p.table[int64_t(b) * p.maxb + j];
+        pg = pg < 0 ? 0 : (pg >= p.npages ? p.npages - 1 : pg);
+        return int64_t(pg) * p.Hkv + kvh;
+    }
+    return (int64_t(b) * p.Hkv + kvh) * p.nblk_cap + j;
+}
+
+template <bool PAGED>
+__device__ __forceinline__ float key_hat(const GenParams& p, int b, int kvh, int64_t nblk, int64_t t, int c) {
+    const int64_t Tq = nblk * p.kG;
+    if (t >= Tq) return h2f(p.kr[((int64_t(b) * p.Hkv + kvh) * p.kG + (t - Tq)) * p.kd + c]);
     const int per = 32 / p.kbits;
     const int64_t blk = t / p.kG;
     const int i = int(t - blk * p.kG);
-    const int64_t side = (bh * p.nblk_cap + blk) * p.kd + c;
+    const int64_t side = block_row<PAGED>(p, b, kvh, blk) * p.kd + c;
     const uint32_t w = p.kc[side * p.kW + i / per];
     const uint32_t code = (w >> (p.kbits * (i % per))) & ((1u << p.kbits) - 1u);
     return fmaf(float(code), h2f(p.ks[side]), h2f(p.kz[side]));
 }
 
-__device__ __forceinline__ float value_hat(const GenParams& p, int64_t bh, int64_t t, int c) {
+template <bool PAGED>
+__device__ __forceinline__ float value_hat(const GenParams& p, int b, int kvh, int64_t t, int c) {
     const int per = 32 / p.vbits;
-    const int64_t row = bh * p.cap + t;
+    const int64_t blk = t / p.kG;
+    const int64_t row = block_row<PAGED>(p, b, kvh, blk) * p.kG + (t - blk * p.kG);
     const uint32_t w = p.vc[row * p.vWT + c / per];
     const uint32_t code = (w >> (p.vbits * (c % per))) & ((1u << p.vbits) - 1u);
     const int64_t side = row * p.vNG + c / 32;
@@ -62,7 +83,7 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-template <bool MLA>
+template <bool MLA, bool PAGED>
 __global__ __launch_bounds__(256) void k_decode_generic(GenParams p) {
     __shared__ float qs[1024];
     __shared__ float ps[256];
@@ -70,12 +91,25 @@ __global__ __launch_bounds__(256) void k_decode_generic(GenParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int s = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
     const int kvh = hq / (p.Hq / p.Hkv);
-    const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int qd = MLA ? p.vd + p.kd : p.kd;
     for (int i = tid; i < qd; i += 256) qs[i] = h2f(p.q[(int64_t(b) * p.Hq + hq) * qd + i]);
-    const int64_t u0 = int64_t(s) * p.U / p.S, u1 = int64_t(s + 1) * p.U / p.S;
+    // work units: key blocks, the residual counting as one more.  Contiguous:
+    // the splits share the units evenly; paged: each sequence has its own
+    // length and split s takes units [s * chunk, (s + 1) * chunk)
+    int64_t T = p.T, nblk = p.nblk, u0, u1;
+    if (PAGED) {
+        const int l = p.lens[b];
+        T = l < 0 ? 0 : (l > p.max_len ? p.max_len : l);
+        nblk = T / p.kG;
+        const int64_t U = nblk + (T > nblk * p.kG ? 1 : 0);
+        u0 = int64_t(s) * p.chunk;
+        u1 = u0 + p.chunk < U ? u0 + p.chunk : U;
+    } else {
+        u0 = int64_t(s) * p.U / p.S;
+        u1 = int64_t(s + 1) * p.U / p.S;
+    }
     const int64_t t0 = u0 * p.kG;
-    const int64_t t1 = u1 * p.kG < p.T ? u1 * p.kG : p.T;
+    const int64_t t1 = u1 * p.kG < T ? u1 * p.kG : T;
     float m = -INFINITY, l = 0.0f, acc0 = 0.0f, acc1 = 0.0f;
     __syncthreads();
     for (int64_t base = t0; base < t1; base += 256) {
@@ -84,10 +118,10 @@ __global__ __launch_bounds__(256) void k_decode_generic(GenParams p) {
         if (t < t1) {
             float dot = 0.0f;
             if (MLA) {
-                for (int c = 0; c < p.vd; ++c) dot = fmaf(qs[c], value_hat(p, bh, t, c), dot);
-                for (int c = 0; c < p.kd; ++c) dot = fmaf(qs[p.vd + c], key_hat(p, bh, t, c), dot);
+                for (int c = 0; c < p.vd; ++c) dot = fmaf(qs[c], value_hat<PAGED>(p, b, kvh, t, c), dot);
+                for (int c = 0; c < p.kd; ++c) dot = fmaf(qs[p.vd + c], key_hat<PAGED>(p, b, kvh, nblk, t, c), dot);
             } else {
-                for (int c = 0; c < p.kd; ++c) dot = fmaf(qs[c], key_hat(p, bh, t, c), dot);
+                for (int c = 0; c < p.kd; ++c) dot = fmaf(qs[c], key_hat<PAGED>(p, b, kvh, nblk, t, c), dot);
             }
             sc = p.sigma2 * dot;
         }
@@ -108,8 +142,8 @@ __global__ __launch_bounds__(256) void k_decode_generic(GenParams p) {
         const int n = int(t1 - base < 256 ? t1 - base : 256);
         for (int j = 0; j < n; ++j) {
             const float pj = ps[j];
-            if (tid < p.vd) acc0 = fmaf(pj, value_hat(p, bh, base + j, tid), acc0);
-            if (tid + 256 < p.vd) acc1 = fmaf(pj, value_hat(p, bh, base + j, tid + 256), acc1);
+            if (tid < p.vd) acc0 = fmaf(pj, value_hat<PAGED>(p, b, kvh, base + j, tid), acc0);
+            if (tid + 256 < p.vd) acc1 = fmaf(pj, value_hat<PAGED>(p, b, kvh, base + j, tid + 256), acc1);
         }
         m = mnew;
         __syncthreads();
@@ -124,7 +158,9 @@ __global__ __launch_bounds__(256) void k_decode_generic(GenParams p) {
 }
 
 // Pass 2 (maxima in log2 units): m = max_s m_s, L = sum_s l_s 2^{m_s - m},
-// o = sum_s acc_s 2^{m_s - m} / L.
+// o = sum_s acc_s 2^{m_s - m} / L.  Empty slots (m_s = -inf, l_s = 0, from
+// splits past a short paged sequence) weigh 0; a sequence with no tokens
+// gets o = 0.
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ ws_acc,
                                                const float* __restrict__ ws_ml, int S, int vd,
                                                uint16_t* __restrict__ out) {
@@ -141,7 +177,7 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ ws_acc,
     if (tid == 0) tot[0] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
     const float M = tot[0];
-    const float w = tid < S ? exp2f(mi - M) : 0.0f;
+    const float w = tid < S && mi > -INFINITY ? exp2f(mi - M) : 0.0f;
     if (tid < S) wsh[tid] = w;
     const float lsum = wave_sum(tid < S ? ml[tid * 2 + 1] * w : 0.0f);
     __syncthreads();
@@ -149,7 +185,7 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ ws_acc,
     __syncthreads();
     if (tid == 0) tot[1] = (red[0] + red[1]) + (red[2] + red[3]);
     __syncthreads();
-    const float inv = 1.0f / tot[1];
+    const float inv = tot[1] > 0.0f ? 1.0f / tot[1] : 0.0f;
     const float* acc = ws_acc + pair * S * vd;
     for (int c = tid; c < vd; c += 256) {
         float o = 0.0f;
@@ -160,16 +196,17 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ ws_acc,
 
 }  // namespace
 
-hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
-    const kvq_cache& c = *a.c;
+namespace {
+GenParams gen_params(const DecodeArgs& a) {
+    const kvq_cache_buffers& buf = a.pc ? a.pc->buf : a.c->buf;
     GenParams p;
-    p.kc = static_cast<const uint32_t*>(c.buf.k_codes);
-    p.ks = static_cast<const uint16_t*>(c.buf.k_scale);
-    p.kz = static_cast<const uint16_t*>(c.buf.k_zero);
-    p.kr = static_cast<const uint16_t*>(c.buf.k_resid);
-    p.vc = static_cast<const uint32_t*>(c.buf.v_codes);
-    p.vs = static_cast<const uint16_t*>(c.buf.v_scale);
-    p.vz = static_cast<const uint16_t*>(c.buf.v_zero);
+    p.kc = static_cast<const uint32_t*>(buf.k_codes);
+    p.ks = static_cast<const uint16_t*>(buf.k_scale);
+    p.kz = static_cast<const uint16_t*>(buf.k_zero);
+    p.kr = static_cast<const uint16_t*>(buf.k_resid);
+    p.vc = static_cast<const uint32_t*>(buf.v_codes);
+    p.vs = static_cast<const uint16_t*>(buf.v_scale);
+    p.vz = static_cast<const uint16_t*>(buf.v_zero);
     p.q = static_cast<const uint16_t*>(a.q);
     p.ws_acc = a.ws_acc;
     p.ws_ml = a.ws_ml;
@@ -190,11 +227,33 @@ hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
     p.vWT = a.g.vWT;
     p.vNG = a.g.vNG;
     p.sigma2 = a.sigma * 1.4426950408889634f;
+    p.table = a.ps.table;
+    p.lens = a.ps.lens;
+    p.maxb = a.ps.maxb;
+    p.npages = a.ps.n_pages;
+    p.chunk = a.chunk;
+    p.max_len = a.max_len;
+    return p;
+}
+}  // namespace
+
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
+    const GenParams p = gen_params(a);
     const dim3 grid(a.S, a.Hq, a.g.B);
-    if (c.cfg.kind == KVQ_KIND_MLA)
-        hipExtLaunchKernelGGL(k_decode_generic<true>, grid, dim3(256), 0, st, a.ev_start, a.ev_stop, 0, p);
+    if (a.c->cfg.kind == KVQ_KIND_MLA)
+        hipExtLaunchKernelGGL((k_decode_generic<true, false>), grid, dim3(256), 0, st, a.ev_start, a.ev_stop, 0, p);
     else
-        hipExtLaunchKernelGGL(k_decode_generic<false>, grid, dim3(256), 0, st, a.ev_start, a.ev_stop, 0, p);
+        hipExtLaunchKernelGGL((k_decode_generic<false, false>), grid, dim3(256), 0, st, a.ev_start, a.ev_stop, 0, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_generic_paged(const DecodeArgs& a, hipStream_t st) {
+    const GenParams p = gen_params(a);
+    const dim3 grid(a.S, a.Hq, a.g.B);
+    if (a.pc->cfg.kind == KVQ_KIND_MLA)
+        hipExtLaunchKernelGGL((k_decode_generic<true, true>), grid, dim3(256), 0, st, a.ev_start, a.ev_stop, 0, p);
+    else
+        hipExtLaunchKernelGGL((k_decode_generic<false, true>), grid, dim3(256), 0, st, a.ev_start, a.ev_stop, 0, p);
     return hipGetLastError();
 }
 

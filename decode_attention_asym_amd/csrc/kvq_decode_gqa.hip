@@ -84,10 +84,10 @@ struct KState {
 
 // Key side of one tile: produces p and alpha in `hb`.  qw holds this lane's
 // query channels 8 chunk .. 8 chunk + 7 as fp16 pairs in quad order.
-template <int G>
+template <int G, class Run>
 __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState& st, LdsK& L,
                                          Handoff& hb, const uint32_t* qw, int lane,
-                                         int64_t bh, int nxt, const TileRun& run) {
+                                         int64_t bh, int nxt, const Run& run) {
     constexpr int NBT = 64 / G;
     const int n = lane & 15, kg = lane >> 4;
     const int hh = lane >> 4, chunk = lane & 15;
@@ -227,14 +227,15 @@ struct VState {
 };
 
 // Value side of one tile, reading p and alpha from `hb`.
+template <int G, class Run>
 __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VState& st, LdsV& L,
                                            const Handoff& hb, int lane, int64_t bh,
-                                           int nxt, const TileRun& run) {
+                                           int nxt, const Run& run) {
     const int n = lane & 15, kg = lane >> 4;
     const int hh = lane >> 4, chunk = lane & 15;
     // ---- stage value codes and side values, then prefetch tile i + 2
     stage_values(cur, L.vl, L.vsl, lane);
-    load_vtile(p, run, bh, nxt, lane, cur);
+    load_vtile<G>(p, run, bh, nxt, lane, cur);
 
     // ---- rescale what was accumulated with the previous maxima
     const float a0 = hb.alpha[0], a1 = hb.alpha[1], a2 = hb.alpha[2], a3 = hb.alpha[3];
@@ -309,7 +310,18 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
     }
 }
 
-template <int G>
+// the code-tile run of a main split: contiguous (one buffer resource per
+// run) or paged (per-tile resources over the pages of the block table)
+template <int G, bool PAGED>
+__device__ __forceinline__ auto make_run(const MfmaParams& p, int b, int kvh, int64_t bh, int t_lo, int t_hi,
+                                         int lane) {
+    if constexpr (PAGED)
+        return paged_run<G>(p, b, kvh, t_lo, t_hi, lane);
+    else
+        return tile_run<G>(p, bh, t_lo, t_hi);
+}
+
+template <int G, bool PAGED>
 __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
     __shared__ Lds L;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -318,12 +330,33 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
     const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int hq0 = kvh * HG;
-    if (s >= p.S_main) {
-        if (wave == 0) tail_split<HG>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
-        return;
+    // a paged sequence has its own length; its main splits take p.chunk
+    // tiles each from the start, so those past its tiles are empty
+    int t_lo, t_hi;
+    if constexpr (PAGED) {
+        const int len = seq_len(p, b);
+        const int64_t nblk = len / G;
+        const int ntiles = int(nblk * G / 64);
+        if (s >= p.S_main) {
+            if (wave == 0)
+                tail_split<HG>(p, PagedBlocks{}, b, kvh, s, reinterpret_cast<float*>(L.k.qa),
+                               reinterpret_cast<float*>(L.v.pa), len, nblk, ntiles);
+            return;
+        }
+        t_lo = s * p.chunk;
+        t_hi = t_lo + p.chunk < ntiles ? t_lo + p.chunk : ntiles;
+        if (t_lo >= t_hi) {
+            empty_partial<HG>(p, b, kvh, s);
+            return;
+        }
+    } else {
+        if (s >= p.S_main) {
+            if (wave == 0) tail_split<HG>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
+            return;
+        }
+        t_lo = int(int64_t(s) * p.ntiles / p.S_main);
+        t_hi = int(int64_t(s + 1) * p.ntiles / p.S_main);
     }
-    const int t_lo = int(int64_t(s) * p.ntiles / p.S_main);
-    const int t_hi = int(int64_t(s + 1) * p.ntiles / p.S_main);
     const int ntl = t_hi - t_lo;
 
     if (wave == 0) {
@@ -334,7 +367,7 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
         KState st;
         st.m0 = st.m1 = st.m2 = st.m3 = -INFINITY;
         KTile ta, tb;
-        const TileRun run = tile_run<G>(p, bh, t_lo, t_hi);
+        const auto run = make_run<G, PAGED>(p, b, kvh, bh, t_lo, t_hi, lane);
         load_ktile<G>(p, run, bh, t_lo, lane, ta);
         load_ktile<G>(p, run, bh, t_lo + 1, lane, tb);
         // keep these loads ahead of (not interleaved with) the prefetch of tile 2
@@ -370,22 +403,22 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
             for (int u = 0; u < 4; ++u) st.O[P][u] = f32x4{0.f, 0.f, 0.f, 0.f};
         // value work trails the key work by one tile: tile j after barrier j
         VTile ta, tb;
-        const TileRun run = tile_run<G>(p, bh, t_lo, t_hi);
-        load_vtile(p, run, bh, t_lo, lane, ta);
-        load_vtile(p, run, bh, t_lo + 1, lane, tb);
+        const auto run = make_run<G, PAGED>(p, b, kvh, bh, t_lo, t_hi, lane);
+        load_vtile<G>(p, run, bh, t_lo, lane, ta);
+        load_vtile<G>(p, run, bh, t_lo + 1, lane, tb);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        value_tile(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + 2, run);
+        value_tile<G>(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + 2, run);
         __syncthreads();
         int j = 1;
         for (; j + 1 < ntl; j += 2) {
-            value_tile(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
+            value_tile<G>(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
             __syncthreads();
-            value_tile(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + j + 3, run);
+            value_tile<G>(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + j + 3, run);
             __syncthreads();
         }
         if (j < ntl) {
-            value_tile(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
+            value_tile<G>(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
             __syncthreads();
         }
         // ---- epilogue: l and the value-zero sums, hi + lo rows of each head
@@ -428,13 +461,25 @@ bool gqa_supported(const kvq_cache& c, int Hq) {
     return mfma_shape_ok(c) && Hq == HG * c.cfg.n_kv_heads;
 }
 
+bool gqa_cfg_supported(const kvq_cache_cfg& c, int Hq) { return mfma_cfg_ok(c) && Hq == HG * c.n_kv_heads; }
+
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
     const MfmaParams p = mfma_params(a);
     const dim3 grid(a.S, a.g.Hkv, a.g.B);
     if (a.g.kG == 64)
-        hipExtLaunchKernelGGL(k_decode_gqa<64>, grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+        hipExtLaunchKernelGGL((k_decode_gqa<64, false>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
     else
-        hipExtLaunchKernelGGL(k_decode_gqa<32>, grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+        hipExtLaunchKernelGGL((k_decode_gqa<32, false>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_gqa_paged(const DecodeArgs& a, hipStream_t st) {
+    const MfmaParams p = mfma_params(a);
+    const dim3 grid(a.S, a.g.Hkv, a.g.B);
+    if (a.g.kG == 64)
+        hipExtLaunchKernelGGL((k_decode_gqa<64, true>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+    else
+        hipExtLaunchKernelGGL((k_decode_gqa<32, true>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
     return hipGetLastError();
 }
 

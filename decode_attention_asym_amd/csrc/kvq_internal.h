@@ -15,6 +15,14 @@ struct kvq_cache {
     int64_t nblk;   // quantized key blocks; residual keys = T - nblk * G (0..G)
 };
 
+// Paged cache: pools of pages (one G-token key block plus the values of the
+// same tokens, all KV heads) and one residual block per sequence slot.
+struct kvq_paged {
+    kvq_cache_cfg cfg;   // batch = sequence slots, max_tokens = per-sequence capacity
+    kvq_cache_buffers buf;
+    int32_t n_pages;
+};
+
 namespace kvq {
 
 // Geometry derived from a validated configuration.
@@ -52,6 +60,23 @@ hipError_t launch_resid_copy(const kvq_cache& c, const Geom& g, const void* k_in
 hipError_t launch_append_rows(const kvq_cache& c, const Geom& g, const void* k_in, const void* v_in,
                               int64_t n, int64_t R, hipStream_t st);
 
+// ---- paged append (kvq_quant.hip) ----
+
+// Sequence-side inputs of a paged call (device arrays owned by the caller).
+struct PagedSeq {
+    const int32_t* table;   // [B][maxb] page of block j of sequence b
+    const int32_t* lens;    // [B] tokens of sequence b (before an append)
+    const int32_t* n_new;   // [B] rows appended to sequence b, or null = n_max each
+    int maxb;               // table row length = max_tokens / G
+    int n_pages;
+};
+
+// Append up to n_max rows per sequence (inputs [B][Hkv][n_max][d]): values
+// quantized into the pages of their blocks, keys into the residual, every
+// block that fills quantized into its page.
+hipError_t launch_paged_append(const kvq_paged& c, const Geom& g, const void* k_in, const void* v_in,
+                               int n_max, const PagedSeq& ps, hipStream_t st);
+
 // ---- decode kernels (kvq_decode*.hip) ----
 
 enum Variant { V_GENERIC = 0, V_MHA = 1, V_GQA = 2, V_MLA = 3 };
@@ -73,6 +98,12 @@ struct DecodeArgs {
     // optional profiling events; the pass-1 launch records its own start and
     // stop timestamps into them (hipExtLaunchKernel), with no extra packets
     hipEvent_t ev_start, ev_stop;
+    // paged caches: the sequence inputs, the tile count of a main split
+    // (chunk), and the length bound the splits were planned for
+    const kvq_paged* pc;
+    PagedSeq ps;
+    int chunk;
+    int max_len;
 };
 
 Variant pick_variant(const kvq_cache& c, int Hq);
@@ -88,6 +119,7 @@ SplitPlan plan_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64
 int max_slots(const kvq_cache& c, int Hq, int n_splits, Variant v);
 
 bool gqa_supported(const kvq_cache& c, int Hq);
+bool gqa_cfg_supported(const kvq_cache_cfg& c, int Hq);
 bool mha_supported(const kvq_cache& c, int Hq);
 bool mla_supported(const kvq_cache& c, int Hq);
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
@@ -95,5 +127,15 @@ hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_mha(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t st);
+
+// Paged decode: variant choice, split plan over the length bound, launches.
+Variant pick_paged_variant(const kvq_paged& c, int Hq, int n_splits, int max_len);
+const char* paged_variant_name(Variant v);
+struct PagedPlan {
+    int S_main, S, chunk;   // main splits, slots (+1 tail), tiles (GQA) / blocks (generic) per main split
+};
+PagedPlan plan_paged(const kvq_paged& c, int Hq, int n_splits, int max_len, Variant v);
+hipError_t launch_decode_gqa_paged(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_generic_paged(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace kvq

@@ -56,18 +56,22 @@ struct MfmaParams {
     int64_t T, nblk, cap, nblk_cap;
     float sigma2;  // softmax scale * log2(e)
     float neg1;    // -1, kept opaque so p - fp16(p) stays one mixed FMA
+    // paged caches: block table [B][maxb], lengths [B] (clamped to
+    // [0, max_len]), pool size, tiles per main split
+    const int32_t *table, *lens;
+    int maxb, npages, chunk, max_len;
 };
 
 inline MfmaParams mfma_params(const DecodeArgs& a) {
-    const kvq_cache& c = *a.c;
+    const kvq_cache_buffers& buf = a.pc ? a.pc->buf : a.c->buf;
     MfmaParams p;
-    p.kc = static_cast<const uint32_t*>(c.buf.k_codes);
-    p.ks = static_cast<const uint16_t*>(c.buf.k_scale);
-    p.kz = static_cast<const uint16_t*>(c.buf.k_zero);
-    p.kr = static_cast<const uint16_t*>(c.buf.k_resid);
-    p.vc = static_cast<const uint32_t*>(c.buf.v_codes);
-    p.vs = static_cast<const uint16_t*>(c.buf.v_scale);
-    p.vz = static_cast<const uint16_t*>(c.buf.v_zero);
+    p.kc = static_cast<const uint32_t*>(buf.k_codes);
+    p.ks = static_cast<const uint16_t*>(buf.k_scale);
+    p.kz = static_cast<const uint16_t*>(buf.k_zero);
+    p.kr = static_cast<const uint16_t*>(buf.k_resid);
+    p.vc = static_cast<const uint32_t*>(buf.v_codes);
+    p.vs = static_cast<const uint16_t*>(buf.v_scale);
+    p.vz = static_cast<const uint16_t*>(buf.v_zero);
     p.q = static_cast<const uint16_t*>(a.q);
     p.ws_acc = a.ws_acc;
     p.ws_ml = a.ws_ml;
@@ -83,15 +87,46 @@ inline MfmaParams mfma_params(const DecodeArgs& a) {
     p.nblk_cap = a.g.nblk_cap;
     p.sigma2 = a.sigma * 1.4426950408889634f;
     p.neg1 = -1.0f;
+    p.table = a.ps.table;
+    p.lens = a.ps.lens;
+    p.maxb = a.ps.maxb;
+    p.npages = a.ps.n_pages;
+    p.chunk = a.chunk;
+    p.max_len = a.max_len;
     return p;
 }
 
 // The shapes these kernels take: KIVI, D = 128, 2-bit keys and values,
 // 32-channel value groups, G in {32, 64}.
-inline bool mfma_shape_ok(const kvq_cache& c) {
-    const kvq_cache_cfg& g = c.cfg;
+inline bool mfma_cfg_ok(const kvq_cache_cfg& g) {
     return g.kind == KVQ_KIND_KIVI && g.key.bits == 2 && g.value.bits == 2 && g.key.dim == D &&
            g.value.dim == D && g.value.group == 32 && (g.key.group == 32 || g.key.group == 64);
+}
+inline bool mfma_shape_ok(const kvq_cache& c) { return mfma_cfg_ok(c.cfg); }
+
+// ---- where key block j of (sequence b, KV head kvh) lives: its block row r
+// (key codes at r * D * G/16 words, key side values at r * D, value rows
+// r * G + i).  Contiguous: (b * Hkv + kvh) * nblk_cap + j; paged:
+// page * Hkv + kvh with the page from the block table (clamped into the pool,
+// so a bad entry reads the wrong page but never outside the arrays).
+__device__ __forceinline__ int page_of(const MfmaParams& p, int b, int64_t j) {
+    const int pg = p.table[int64_t(b) * p.maxb + j];
+    return pg < 0 ? 0 : (pg >= p.npages ? p.npages - 1 : pg);
+}
+struct ContigBlocks {
+    __device__ int64_t operator()(const MfmaParams& p, int b, int kvh, int64_t j) const {
+        return (int64_t(b) * p.Hkv + kvh) * p.nblk_cap + j;
+    }
+};
+struct PagedBlocks {
+    __device__ int64_t operator()(const MfmaParams& p, int b, int kvh, int64_t j) const {
+        return int64_t(page_of(p, b, j)) * p.Hkv + kvh;
+    }
+};
+// tokens of sequence b in a paged call
+__device__ __forceinline__ int seq_len(const MfmaParams& p, int b) {
+    const int l = p.lens[b];
+    return l < 0 ? 0 : (l > p.max_len ? p.max_len : l);
 }
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
@@ -286,6 +321,92 @@ __device__ __forceinline__ void load_vtile(const MfmaParams& p, const TileRun& r
     r.vs = make_uint4(a.x, a.y, b.x, b.y);
 }
 
+// Paged runs: the tiles of a run lie in the pages the block table names.
+// Lane l holds the page of block NBT * t_lo + l (a run spans at most 64
+// blocks); each tile's code loads go through buffer resources over its own
+// page(s), empty past the run, so the same branch-free prefetch works.
+struct PagedRun {
+    int pg;   // this lane's page
+    int t0, t_last, kvh;
+};
+
+template <int G>
+__device__ __forceinline__ PagedRun paged_run(const MfmaParams& p, int b, int kvh, int t_lo, int t_hi, int lane) {
+    constexpr int NBT = 64 / G;
+    PagedRun r;
+    r.pg = lane < (t_hi - t_lo) * NBT ? page_of(p, b, int64_t(t_lo) * NBT + lane) : 0;
+    r.t0 = t_lo;
+    r.t_last = t_hi - 1;
+    r.kvh = kvh;
+    return r;
+}
+
+// block row of block e (0 .. NBT-1) of tile tt (clamped into the run); the
+// lane index is wave-uniform
+template <int G>
+__device__ __forceinline__ int64_t paged_row(const MfmaParams& p, const PagedRun& run, int tt, int e) {
+    constexpr int NBT = 64 / G;
+    const int ic = (tt <= run.t_last ? tt : run.t_last) - run.t0;
+    return int64_t(__builtin_amdgcn_readlane(run.pg, ic * NBT + e)) * p.Hkv + run.kvh;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint32_t* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(base), 0, bytes, 0x00020000);
+}
+
+template <int G>
+__device__ __forceinline__ void load_ktile(const MfmaParams& p, const PagedRun& run, int64_t, int tt, int lane,
+                                           KTile& r) {
+    constexpr int W = G / 16;
+    const bool in = tt <= run.t_last;
+    const int64_t ra = paged_row<G>(p, run, tt, 0);
+    const uint16_t* side = lane < 32 ? p.ks : p.kz;
+    if (G == 64) {
+        const __amdgpu_buffer_rsrc_t rs = page_rsrc(p.kc + ra * D * W, in ? 2048 : 0);
+        r.k0 = ld_run(rs, 16 * lane);
+        r.k1 = ld_run(rs, 16 * lane + 1024);
+        const uint2 v = ld_stream(reinterpret_cast<const uint2*>(side + ra * D) + (lane & 31));
+        r.ks = make_uint4(v.x, v.y, 0u, 0u);
+    } else {
+        const int64_t rb = paged_row<G>(p, run, tt, 1);
+        r.k0 = ld_run(page_rsrc(p.kc + ra * D * W, in ? 1024 : 0), 16 * lane);
+        r.k1 = ld_run(page_rsrc(p.kc + rb * D * W, in ? 1024 : 0), 16 * lane);
+        r.ks = ld_stream(reinterpret_cast<const uint4*>(side + ((lane & 16) ? rb : ra) * D) + (lane & 15));
+    }
+}
+
+template <int G>
+__device__ __forceinline__ void load_vtile(const MfmaParams& p, const PagedRun& run, int64_t, int tt, int lane,
+                                           VTile& r) {
+    const bool in = tt <= run.t_last;
+    const int64_t ra = paged_row<G>(p, run, tt, 0);
+    // lane l (mod 32) takes tokens t = 4(l >> 1) + (l & 1) and t + 2 (same block)
+    const int t = 4 * ((lane & 31) >> 1) + (lane & 1);
+    int64_t vrow;
+    if (G == 64) {
+        const __amdgpu_buffer_rsrc_t rs = page_rsrc(p.vc + ra * 64 * 8, in ? 2048 : 0);
+        r.v0 = ld_run(rs, 16 * lane);
+        r.v1 = ld_run(rs, 16 * lane + 1024);
+        vrow = ra * 64 + t;
+    } else {
+        const int64_t rb = paged_row<G>(p, run, tt, 1);
+        r.v0 = ld_run(page_rsrc(p.vc + ra * 32 * 8, in ? 1024 : 0), 16 * lane);
+        r.v1 = ld_run(page_rsrc(p.vc + rb * 32 * 8, in ? 1024 : 0), 16 * lane);
+        vrow = t < 32 ? ra * 32 + t : rb * 32 + (t - 32);
+    }
+    const uint16_t* vside = (lane < 32 ? p.vs : p.vz) + vrow * 4;
+    const uint2 a = ld_stream(reinterpret_cast<const uint2*>(vside));
+    const uint2 b = ld_stream(reinterpret_cast<const uint2*>(vside + 8));
+    r.vs = make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// contiguous runs, same call shape as the paged overload
+template <int G>
+__device__ __forceinline__ void load_vtile(const MfmaParams& p, const TileRun& run, int64_t bh, int tt, int lane,
+                                           VTile& r) {
+    load_vtile(p, run, bh, tt, lane, r);
+}
+
 // Key codes staged in their cache layout: G = 64, channel c of the tile at
 // dwords 4c..4c+3 (word j = tokens 16j..16j+15); G = 32, block be, channel c
 // at dwords 256be + 2c, +1.  Side values to ksl [scale | zero][block][128 fp16]
@@ -374,32 +495,39 @@ __device__ __forceinline__ f16x8 code_slice(const CodeRegs& c, uint32_t mk) {
 // fp16 residual keys, one token per lane for the logits, two channels per
 // lane for the values.  Runs on one wave; qf holds HG*D floats, pl HG*PSTR.
 
-__device__ __forceinline__ float key_hat(const MfmaParams& p, int64_t bh, int64_t t, int c) {
-    const int64_t Tq = p.nblk * p.G;
-    if (t >= Tq) return h2f(p.kr[(bh * p.G + (t - Tq)) * D + c]);
+template <class Blocks>
+__device__ __forceinline__ float key_hat(const MfmaParams& p, const Blocks& blocks, int b, int kvh, int64_t nblk,
+                                         int64_t t, int c) {
+    const int64_t Tq = nblk * p.G;
+    if (t >= Tq) return h2f(p.kr[((int64_t(b) * p.Hkv + kvh) * p.G + (t - Tq)) * D + c]);
     const int64_t blk = t / p.G;
     const int i = int(t - blk * p.G);
-    const int64_t side = (bh * p.nblk_cap + blk) * D + c;
+    const int64_t side = blocks(p, b, kvh, blk) * D + c;
     const uint32_t w = p.kc[side * (p.G / 16) + i / 16];
     return fmaf(float((w >> (2 * (i & 15))) & 3u), h2f(p.ks[side]), h2f(p.kz[side]));
 }
 
-__device__ __forceinline__ float value_hat(const MfmaParams& p, int64_t bh, int64_t t, int c) {
-    const int64_t row = bh * p.cap + t;
+template <class Blocks>
+__device__ __forceinline__ float value_hat(const MfmaParams& p, const Blocks& blocks, int b, int kvh, int64_t t,
+                                           int c) {
+    const int64_t blk = t / p.G;
+    const int64_t row = blocks(p, b, kvh, blk) * p.G + (t - blk * p.G);
     const uint32_t w = p.vc[row * 8 + c / 16];
     const int64_t side = row * 4 + c / 32;
     return fmaf(float((w >> (2 * (c & 15))) & 3u), h2f(p.vs[side]), h2f(p.vz[side]));
 }
 
-template <int HG>
-__device__ void tail_split(const MfmaParams& p, int b, int kvh, int s, float* qf, float* pl) {
+// tokens [ntiles * 64, T) of sequence b, nblk of its key blocks quantized
+// (an empty range writes an empty partial: m = -inf, l = 0, acc = 0)
+template <int HG, class Blocks>
+__device__ void tail_split(const MfmaParams& p, const Blocks& blocks, int b, int kvh, int s, float* qf, float* pl,
+                           int64_t T, int64_t nblk, int ntiles) {
     const int lane = threadIdx.x & 63;
-    const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int hq0 = kvh * HG;
     for (int i = lane; i < HG * D; i += 64) qf[i] = h2f(p.q[(int64_t(b) * p.Hq + hq0) * D + i]);
     wave_sync();
-    const int64_t t0 = int64_t(p.ntiles) * 64;
-    const int n_tail = int(p.T - t0);
+    const int64_t t0 = int64_t(ntiles) * 64;
+    const int n_tail = int(T - t0);
     const int64_t t = t0 + lane;
     const bool valid = lane < n_tail;
     float sc[HG];
@@ -407,7 +535,7 @@ __device__ void tail_split(const MfmaParams& p, int b, int kvh, int s, float* qf
     for (int h = 0; h < HG; ++h) sc[h] = 0.0f;
     if (valid) {
         for (int c = 0; c < D; ++c) {
-            const float kh = key_hat(p, bh, t, c);
+            const float kh = key_hat(p, blocks, b, kvh, nblk, t, c);
 #pragma unroll
             for (int h = 0; h < HG; ++h) sc[h] = fmaf(qf[h * D + c], kh, sc[h]);
         }
@@ -433,7 +561,7 @@ __device__ void tail_split(const MfmaParams& p, int b, int kvh, int s, float* qf
 #pragma unroll
         for (int h = 0; h < HG; ++h) acc[h] = 0.0f;
         for (int j = 0; j < n_tail; ++j) {
-            const float vh = value_hat(p, bh, t0 + j, c);
+            const float vh = value_hat(p, blocks, b, kvh, t0 + j, c);
 #pragma unroll
             for (int h = 0; h < HG; ++h) acc[h] = fmaf(pl[h * PSTR + j], vh, acc[h]);
         }
@@ -448,6 +576,25 @@ __device__ void tail_split(const MfmaParams& p, int b, int kvh, int s, float* qf
             p.ws_ml[slot * 2] = m[h];
             p.ws_ml[slot * 2 + 1] = l[h];
         }
+    }
+}
+
+// the contiguous cache's tail: its counters are in the parameters
+template <int HG>
+__device__ void tail_split(const MfmaParams& p, int b, int kvh, int s, float* qf, float* pl) {
+    tail_split<HG>(p, ContigBlocks{}, b, kvh, s, qf, pl, p.T, p.nblk, p.ntiles);
+}
+
+// a main split with no tiles (a sequence shorter than the split's range)
+template <int HG>
+__device__ void empty_partial(const MfmaParams& p, int b, int kvh, int s) {
+    const int hq0 = kvh * HG;
+    for (int i = threadIdx.x; i < HG * D; i += blockDim.x)
+        p.ws_acc[((int64_t(b) * p.Hq + hq0 + i / D) * p.S + s) * D + i % D] = 0.0f;
+    if (threadIdx.x < HG) {
+        const int64_t slot = (int64_t(b) * p.Hq + hq0 + threadIdx.x) * p.S + s;
+        p.ws_ml[slot * 2] = -INFINITY;
+        p.ws_ml[slot * 2 + 1] = 0.0f;
     }
 }
 

@@ -68,6 +68,45 @@ SplitPlan plan_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64
     return sp;
 }
 
+// ---- paged caches.  Lengths differ per sequence and live on the device, so
+// the splits are planned for the caller's bound max_len: every main split
+// covers a fixed count (chunk) of tiles / key blocks from the sequence start
+// and those past a shorter sequence's end write empty partials.
+PagedPlan plan_paged(const kvq_paged& c, int Hq, int n_splits, int max_len, Variant v) {
+    const int64_t G = c.cfg.key.group;
+    PagedPlan pp;
+    if (v == V_GQA) {
+        const int64_t ntiles = int64_t(max_len) / G * G / 64;
+        const int64_t units = int64_t(c.cfg.batch) * c.cfg.n_kv_heads;
+        const int64_t want = n_splits > 0 ? n_splits : clamp64((3072 + units - 1) / units, 1, KVQ_MAX_SPLITS - 1);
+        int64_t chunk = ntiles > 0 ? (ntiles + want - 1) / want : 1;
+        // the page numbers of a run sit one per lane: at most 64 key blocks
+        chunk = clamp64(chunk, 1, G);
+        pp.chunk = int(chunk);
+        pp.S_main = int((ntiles + chunk - 1) / chunk);
+        pp.S = pp.S_main + 1;   // + the tail slot (partial tile and residual keys)
+        return pp;
+    }
+    const int64_t U = (int64_t(max_len) + G - 1) / G;   // key blocks, the residual one included
+    const int64_t units = int64_t(c.cfg.batch) * Hq;
+    const int64_t want = n_splits > 0 ? n_splits : clamp64((2048 + units - 1) / units, 1, KVQ_MAX_SPLITS);
+    const int64_t s0 = clamp64(want, 1, U > 0 ? U : 1);
+    const int64_t chunk = U > 0 ? (U + s0 - 1) / s0 : 1;
+    pp.chunk = int(chunk);
+    pp.S_main = int(U > 0 ? (U + chunk - 1) / chunk : 1);
+    pp.S = pp.S_main;
+    return pp;
+}
+
+Variant pick_paged_variant(const kvq_paged& c, int Hq, int n_splits, int max_len) {
+    // the MFMA kernel while its main splits fit the merge's slot limit
+    if (gqa_cfg_supported(c.cfg, Hq) && plan_paged(c, Hq, n_splits, max_len, V_GQA).S <= KVQ_MAX_SPLITS)
+        return V_GQA;
+    return V_GENERIC;
+}
+
+const char* paged_variant_name(Variant v) { return v == V_GQA ? "gqa_mfma_paged" : "generic_paged"; }
+
 int max_slots(const kvq_cache& c, int Hq, int n_splits, Variant v) {
     const int64_t want = n_splits > 0 ? n_splits : auto_main(c, Hq, v);
     if (v == V_GQA || v == V_MHA) return int(clamp64(want, 1, KVQ_MAX_SPLITS - 1) + 1);

@@ -92,11 +92,46 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
 constexpr int VT = 4;
 
 struct ValueArgs {
-    const uint16_t* vin;
-    int64_t n_in, row0, n_tok, t_dst0, cap;
+    const uint16_t* vin;   // [BH][n_in][vd]
+    int64_t n_in, row0, n_tok;
     int vd, BH;
     uint32_t* codes;
     uint16_t *scale, *zero;
+};
+
+// Destination rows of the value stream.  Contiguous cache: token t of
+// (b, kvh) is row bh * cap + t.
+struct ContigRows {
+    int64_t cap, t_dst0, n_tok;
+    __device__ int64_t count(int64_t) const { return n_tok; }
+    __device__ int64_t row(int64_t bh, int64_t tok) const { return bh * cap + t_dst0 + tok; }
+};
+
+// Paged cache: rows appended to sequence b (0 when its length, row count or
+// capacity is out of range, so nothing is written for it)
+__device__ __forceinline__ int seq_rows(const PagedSeq& ps, int b, int n_max, int G) {
+    const int pos = ps.lens[b];
+    const int n = ps.n_new ? ps.n_new[b] : n_max;
+    if (pos < 0 || n < 0 || n > n_max || int64_t(pos) + n > int64_t(ps.maxb) * G) return 0;
+    return n;
+}
+// block row page * Hkv + kvh of block j of sequence b, or -1 when the table
+// names a page outside the pool
+__device__ __forceinline__ int64_t paged_block_row(const PagedSeq& ps, int b, int kvh, int Hkv, int64_t j) {
+    const int pg = ps.table[int64_t(b) * ps.maxb + j];
+    return (pg < 0 || pg >= ps.n_pages) ? -1 : int64_t(pg) * Hkv + kvh;
+}
+// value row of token t: block row * G + t mod G
+struct PagedRows {
+    PagedSeq ps;
+    int Hkv, G, n_max;
+    __device__ int64_t count(int64_t bh) const { return seq_rows(ps, int(bh / Hkv), n_max, G); }
+    __device__ int64_t row(int64_t bh, int64_t tok) const {
+        const int b = int(bh / Hkv), kvh = int(bh % Hkv);
+        const int64_t t = ps.lens[b] + tok;
+        const int64_t r = paged_block_row(ps, b, kvh, Hkv, t / G);
+        return r < 0 ? -1 : r * G + t % G;
+    }
 };
 
 // threads that quantize n_tok value rows: BH * ceil(n_tok / VT) * (vd / 8),
@@ -106,27 +141,30 @@ __host__ __device__ inline int64_t value_threads(int BH, int64_t n_tok, int vd) 
 // Thread idx < value_threads(...) quantizes 8 channels of up to VT rows;
 // the 4 threads of a 32-channel group are adjacent lanes and exchange their
 // min / max by shuffles, so callers keep whole 4-lane groups together.
-template <int BITS>
-__device__ __forceinline__ void quant_values_thread(const ValueArgs& a, int64_t idx) {
+// Rows tok < rows.count(bh) are quantized into rows.row(bh, tok) (skipped
+// when that is negative).
+template <int BITS, class Rows>
+__device__ __forceinline__ void quant_values_thread(const ValueArgs& a, const Rows& rows, int64_t idx) {
     const uint16_t* __restrict__ vin = a.vin;
-    const int64_t n_in = a.n_in, row0 = a.row0, n_tok = a.n_tok, t_dst0 = a.t_dst0, cap = a.cap;
+    const int64_t n_in = a.n_in, row0 = a.row0;
     const int vd = a.vd;
     uint32_t* __restrict__ codes = a.codes;
     uint16_t* __restrict__ scale = a.scale;
     uint16_t* __restrict__ zero = a.zero;
     constexpr float L = float((1 << BITS) - 1);
     const int tpt = vd / 8;
-    const int64_t nq = (n_tok + VT - 1) / VT;
+    const int64_t nq = (a.n_tok + VT - 1) / VT;
     const int sub = int(idx % tpt);
     const int64_t tq = (idx / tpt) % nq;
     const int64_t bh = idx / tpt / nq;
+    const int64_t cnt = rows.count(bh);
 
     uint4 raw[VT];
 #pragma unroll
     for (int j = 0; j < VT; ++j) {
         const int64_t tok = tq * VT + j;
-        raw[j] = tok < n_tok ? ld_once4(vin + ((bh * n_in) + row0 + tok) * vd + sub * 8)
-                             : make_uint4(0u, 0u, 0u, 0u);
+        raw[j] = tok < cnt ? ld_once4(vin + ((bh * n_in) + row0 + tok) * vd + sub * 8)
+                           : make_uint4(0u, 0u, 0u, 0u);
     }
     const int vWT = vd * BITS / 32;
 #pragma unroll
@@ -153,17 +191,17 @@ __device__ __forceinline__ void quant_values_thread(const ValueArgs& a, int64_t 
             packed |= code_of(sub_half<0>(w[i], nmn), q) << (BITS * (2 * i));
             packed |= code_of(sub_half<1>(w[i], nmn), q) << (BITS * (2 * i + 1));
         }
-        const int64_t t = t_dst0 + tok;
-        uint32_t* wrow = codes + (bh * cap + t) * vWT;
-        const bool valid = tok < n_tok;
+        // the same for the 4 lanes of a group (same bh, same token)
+        const int64_t row = tok < cnt ? rows.row(bh, tok) : -1;
+        const bool valid = row >= 0;
         if (BITS == 2) {
             const uint32_t other = __shfl_xor(packed, 1);
-            if (valid && (sub & 1) == 0) wrow[sub >> 1] = packed | (other << 16);
+            if (valid && (sub & 1) == 0) codes[row * vWT + (sub >> 1)] = packed | (other << 16);
         } else if (valid) {
-            wrow[sub] = packed;
+            codes[row * vWT + sub] = packed;
         }
         if (valid && (sub & 3) == 0) {
-            const int64_t side = (bh * cap + t) * (vd / 32) + (sub >> 2);
+            const int64_t side = row * (vd / 32) + (sub >> 2);
             scale[side] = float_to_half_bits(q.scale);
             zero[side] = float_to_half_bits(q.mn);
         }
@@ -171,10 +209,10 @@ __device__ __forceinline__ void quant_values_thread(const ValueArgs& a, int64_t 
 }
 
 template <int BITS>
-__global__ __launch_bounds__(256) void k_quant_values(ValueArgs a) {
+__global__ __launch_bounds__(256) void k_quant_values(ValueArgs a, ContigRows rows) {
     const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
     if (idx >= value_threads(a.BH, a.n_tok, a.vd)) return;   // whole 4-lane groups leave together
-    quant_values_thread<BITS>(a, idx);
+    quant_values_thread<BITS>(a, rows, idx);
 }
 
 // -------------------------------------------------------------------- keys
@@ -202,77 +240,98 @@ template <> struct WordVec<8> {
 };
 
 template <int G, int BITS>
-__global__ __launch_bounds__(256) void k_quant_keys(
-    const uint16_t* __restrict__ kin, int64_t n_in, int64_t in_tok0,
-    const uint16_t* __restrict__ resid, int64_t res_tok0, int64_t blk0, int nb, int kd,
-    int64_t nblk_cap, int BH, uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
-    uint16_t* __restrict__ zero) {
-    constexpr float L = float((1 << BITS) - 1);
-    constexpr int PER = 32 / BITS;
-    constexpr int W = G / PER;                 // words per (block, channel)
-    constexpr int TG = G < 32 ? G : 32;        // rows per thread
-    constexpr int SPL = G / TG;                // threads per channel pair
-    constexpr int CPW = 64 / SPL;              // channel pairs per wave (SPL > 1)
-    constexpr int WT = TG / PER;               // words per thread and channel
+struct KeyShape {
+    static constexpr int PER = 32 / BITS;
+    static constexpr int W = G / PER;            // words per (block, channel)
+    static constexpr int TG = G < 32 ? G : 32;   // rows per thread
+    static constexpr int SPL = G / TG;           // threads per channel pair
+    static constexpr int CPW = 64 / SPL;         // channel pairs per wave (SPL > 1)
+    static constexpr int WT = TG / PER;          // words per thread and channel
+};
+
+// Threads per (sequence, KV head, block).  With SPL > 1 a wave holds the SPL
+// row ranges of CPW channel pairs, so the count is rounded up to whole waves;
+// lanes past the last pair (kd / 2 < CPW) take part in the shuffles only.
+template <int G, int BITS>
+__host__ __device__ inline int64_t key_threads_per_block(int kd) {
+    using S = KeyShape<G, BITS>;
     const int tpb = kd / 2;
-    const int64_t total = int64_t(BH) * nb * tpb * SPL;
-    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (idx >= total) return;   // whole waves: total is a multiple of 64 when SPL > 1
-    int cp, sp;
-    int64_t blk, bh;
-    if (SPL == 1) {
+    return S::SPL == 1 ? tpb : int64_t((tpb + S::CPW - 1) / S::CPW) * 64;
+}
+
+// thread idx -> (block unit, channel pair, row range)
+template <int G, int BITS>
+__device__ __forceinline__ void key_thread_coords(int64_t idx, int kd, int64_t& unit, int& cp, int& sp) {
+    using S = KeyShape<G, BITS>;
+    const int tpb = kd / 2;
+    if (S::SPL == 1) {
         sp = 0;
         cp = int(idx % tpb);
-        blk = blk0 + (idx / tpb) % nb;
-        bh = idx / tpb / nb;
+        unit = idx / tpb;
     } else {
-        // a wave holds the SPL row ranges of CPW consecutive channel pairs
         const int lane = int(idx & 63);
         const int64_t wv = idx >> 6;
-        const int chunks = tpb / CPW;
-        sp = lane / CPW;
-        cp = int(wv % chunks) * CPW + lane % CPW;
-        blk = blk0 + (wv / chunks) % nb;
-        bh = wv / chunks / nb;
+        const int chunks = (tpb + S::CPW - 1) / S::CPW;
+        sp = lane / S::CPW;
+        cp = int(wv % chunks) * S::CPW + lane % S::CPW;
+        unit = wv / chunks;
     }
+}
 
-    uint32_t raw[TG];
+// One key block as a thread sees it: token tok < in_tok0 is residual row
+// tok - res_tok0, later ones input row tok - in_tok0; codes go to block row
+// dst (codes at dst * kd * W, side values at dst * kd).
+struct KeyJob {
+    const uint16_t* kin;     // input rows of this (sequence, KV head)
+    const uint16_t* resid;   // residual rows of this (sequence, KV head)
+    int64_t blk_tok0, in_tok0, res_tok0;
+    int64_t dst;
+};
+
+template <int G, int BITS>
+__device__ __forceinline__ void quant_key_pair(const KeyJob& j, int kd, int cp, int sp,
+                                               uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
+                                               uint16_t* __restrict__ zero) {
+    using S = KeyShape<G, BITS>;
+    constexpr float L = float((1 << BITS) - 1);
+    const bool active = cp < kd / 2;
+    uint32_t raw[S::TG];
 #pragma unroll
-    for (int i = 0; i < TG; ++i) {
-        const int64_t tok = blk * G + sp * TG + i;
-        const uint16_t* row = tok < in_tok0 ? resid + (bh * G + (tok - res_tok0)) * kd
-                                            : kin + (bh * n_in + (tok - in_tok0)) * kd;
-        raw[i] = ld_once1(row + 2 * cp);
+    for (int i = 0; i < S::TG; ++i) {
+        const int64_t tok = j.blk_tok0 + sp * S::TG + i;
+        const uint16_t* row = tok < j.in_tok0 ? j.resid + (tok - j.res_tok0) * kd : j.kin + (tok - j.in_tok0) * kd;
+        raw[i] = active ? ld_once1(row + 2 * cp) : 0u;
     }
     // per-channel min / max over the rows, both channels at once (packed
     // fp16, exact; -0 is canonicalised after), then across the row ranges
     f16x2 mn2 = as_h2(raw[0]), mx2 = mn2;
 #pragma unroll
-    for (int i = 1; i < TG; ++i) {
+    for (int i = 1; i < S::TG; ++i) {
         mn2 = __builtin_elementwise_min(mn2, as_h2(raw[i]));
         mx2 = __builtin_elementwise_max(mx2, as_h2(raw[i]));
     }
 #pragma unroll
-    for (int o = CPW; o < 64 && SPL > 1; o <<= 1) {
+    for (int o = S::CPW; o < 64 && S::SPL > 1; o <<= 1) {
         mn2 = __builtin_elementwise_min(mn2, as_h2(__shfl_xor(__builtin_bit_cast(uint32_t, mn2), o)));
         mx2 = __builtin_elementwise_max(mx2, as_h2(__shfl_xor(__builtin_bit_cast(uint32_t, mx2), o)));
     }
+    if (!active) return;
     GroupQ q[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) q[e] = make_group(float(mn2[e]) + 0.0f, float(mx2[e]) + 0.0f, L);
-    const int64_t side = (bh * nblk_cap + blk) * kd + 2 * cp;
+    const int64_t side = j.dst * kd + 2 * cp;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        uint32_t words[WT];
+        uint32_t words[S::WT];
 #pragma unroll
-        for (int j = 0; j < WT; ++j) words[j] = 0;
+        for (int w = 0; w < S::WT; ++w) words[w] = 0;
         const float nmn = -q[e].mn;
 #pragma unroll
-        for (int i = 0; i < TG; ++i) {
+        for (int i = 0; i < S::TG; ++i) {
             const float d = e == 0 ? sub_half<0>(raw[i], nmn) : sub_half<1>(raw[i], nmn);
-            words[i / PER] |= code_of(d, q[e]) << (BITS * (i % PER));
+            words[i / S::PER] |= code_of(d, q[e]) << (BITS * (i % S::PER));
         }
-        WordVec<WT>::st(codes + (side + e) * W + sp * WT, words);
+        WordVec<S::WT>::st(codes + (side + e) * S::W + sp * S::WT, words);
     }
     if (sp == 0) {
         *reinterpret_cast<uint32_t*>(scale + side) =
@@ -280,6 +339,30 @@ __global__ __launch_bounds__(256) void k_quant_keys(
         *reinterpret_cast<uint32_t*>(zero + side) =
             uint32_t(float_to_half_bits(q[0].mn)) | (uint32_t(float_to_half_bits(q[1].mn)) << 16);
     }
+}
+
+// Contiguous cache: blocks blk0 .. blk0 + nb - 1 of every (sequence, KV head)
+struct KeyArgs {
+    const uint16_t* kin;     // [BH][n_in][kd]
+    const uint16_t* resid;   // [BH][G][kd]
+    int64_t n_in, in_tok0, res_tok0, blk0, nblk_cap;
+    int nb, kd, BH;
+    uint32_t* codes;
+    uint16_t *scale, *zero;
+};
+
+template <int G, int BITS>
+__global__ __launch_bounds__(256) void k_quant_keys(KeyArgs a) {
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    // whole waves leave together: the per-block count is a multiple of 64 when SPL > 1
+    if (idx >= int64_t(a.BH) * a.nb * key_threads_per_block<G, BITS>(a.kd)) return;
+    int64_t unit;
+    int cp, sp;
+    key_thread_coords<G, BITS>(idx, a.kd, unit, cp, sp);
+    const int64_t blk = a.blk0 + unit % a.nb, bh = unit / a.nb;
+    const KeyJob j{a.kin + bh * a.n_in * a.kd, a.resid + bh * G * a.kd, blk * G, a.in_tok0, a.res_tok0,
+                   bh * a.nblk_cap + blk};
+    quant_key_pair<G, BITS>(j, a.kd, cp, sp, a.codes, a.scale, a.zero);
 }
 
 // ---------------------------------------------------------- residual copy
@@ -312,13 +395,111 @@ __global__ __launch_bounds__(256) void k_resid_copy(ResidArgs a) {
 // the key rows land in the residual, in one launch (value threads first;
 // their count is a multiple of 4, so no 4-lane group is split).
 template <int BITS>
-__global__ __launch_bounds__(256) void k_append_rows(ValueArgs va, ResidArgs ka) {
+__global__ __launch_bounds__(256) void k_append_rows(ValueArgs va, ContigRows rows, ResidArgs ka) {
     const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
     const int64_t nv = value_threads(va.BH, va.n_tok, va.vd);
     if (idx < nv)
-        quant_values_thread<BITS>(va, idx);
+        quant_values_thread<BITS>(va, rows, idx);
     else if (idx - nv < resid_threads(ka))
         resid_copy_thread(ka, idx - nv);
+}
+
+// ------------------------------------------------------------ paged append
+// Pages hold one G-token key block and the values of the same tokens; the
+// residual keeps one block per sequence slot.  Sequence b appends rows at
+// tokens lens[b] ..; inputs are [BH][n_max][d].
+
+struct PagedKeyArgs {
+    const uint16_t* kin;     // [BH][n_max][kd]
+    uint16_t* resid;         // [BH][G][kd]
+    PagedSeq ps;
+    int n_max, kd, Hkv, BH, J;   // J: block slots per sequence that may complete
+    uint32_t* codes;
+    uint16_t *scale, *zero;
+};
+
+// Every block that the append completes, quantized into its page: slot j of
+// sequence b is block lens[b] / G + j.  Units (sequence, KV head, slot) map
+// to whole waves when SPL > 1, and every exit below is per unit.
+template <int G, int BITS>
+__global__ __launch_bounds__(256) void k_paged_keys(PagedKeyArgs a) {
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= int64_t(a.BH) * a.J * key_threads_per_block<G, BITS>(a.kd)) return;
+    int64_t unit;
+    int cp, sp;
+    key_thread_coords<G, BITS>(idx, a.kd, unit, cp, sp);
+    const int js = int(unit % a.J);
+    const int64_t bh = unit / a.J;
+    const int b = int(bh / a.Hkv), kvh = int(bh % a.Hkv);
+    const int n = seq_rows(a.ps, b, a.n_max, G);
+    if (n == 0) return;
+    const int64_t pos = a.ps.lens[b];
+    const int64_t fb = pos / G, blk = fb + js;
+    if ((blk + 1) * G > pos + n) return;   // not completed by this append
+    const int64_t dst = paged_block_row(a.ps, b, kvh, a.Hkv, blk);
+    if (dst < 0) return;
+    const KeyJob j{a.kin + bh * a.n_max * a.kd, a.resid + bh * G * a.kd, blk * G, pos, fb * G, dst};
+    quant_key_pair<G, BITS>(j, a.kd, cp, sp, a.codes, a.scale, a.zero);
+}
+
+// Value rows into their pages, and the key rows of the block left unfilled
+// into the residual (rows t mod G).  Runs after k_paged_keys, which reads
+// the residual rows it replaces.
+template <int BITS>
+__global__ __launch_bounds__(256) void k_paged_rows(ValueArgs va, PagedRows rows, const uint16_t* __restrict__ kin,
+                                                    uint16_t* __restrict__ resid, int kd) {
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t nv = value_threads(va.BH, va.n_tok, va.vd);
+    if (idx < nv) {
+        quant_values_thread<BITS>(va, rows, idx);
+        return;
+    }
+    const int vpr = kd / 8;
+    const int64_t i = idx - nv;
+    if (i >= int64_t(va.BH) * va.n_tok * vpr) return;
+    const int v = int(i % vpr);
+    const int64_t tok = (i / vpr) % va.n_tok, bh = i / vpr / va.n_tok;
+    const int G = rows.G;
+    const int64_t n = rows.count(bh);
+    if (tok >= n) return;
+    const int64_t pos = rows.ps.lens[bh / rows.Hkv], t = pos + tok;
+    if (t < (pos + n) / G * G) return;   // in a block this append completed
+    *reinterpret_cast<uint4*>(resid + (bh * G + t % G) * kd + v * 8) =
+        *reinterpret_cast<const uint4*>(kin + (bh * va.n_tok + tok) * kd + v * 8);
+}
+
+// One row per sequence (the decode step) in one launch: a workgroup per
+// (sequence, KV head) quantizes the value row into its page and either puts
+// the key into the residual or, when it is the block's last key, quantizes
+// the block (G - 1 residual rows and the new key) into its page.
+template <int G, int KBITS, int VBITS>
+__global__ __launch_bounds__(256) void k_paged_token(ValueArgs va, PagedRows rows, PagedKeyArgs ka) {
+    const int64_t bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int b = int(bh / ka.Hkv), kvh = int(bh % ka.Hkv);
+    if (seq_rows(ka.ps, b, 1, G) == 0) return;   // the whole workgroup
+    const int tpt = va.vd / 8;
+    if (tid < tpt) quant_values_thread<VBITS>(va, rows, bh * tpt + tid);   // whole 4-lane groups
+    const int64_t pos = ka.ps.lens[b];
+    const int kd = ka.kd;
+    if (pos % G == G - 1) {
+        const int64_t fb = pos / G;
+        const int64_t dst = paged_block_row(ka.ps, b, kvh, ka.Hkv, fb);
+        if (dst < 0) return;
+        const KeyJob j{ka.kin + bh * kd, ka.resid + bh * G * kd, fb * G, pos, fb * G, dst};
+        const int64_t nk = key_threads_per_block<G, KBITS>(kd);   // a multiple of 64 when SPL > 1
+        for (int64_t base = 0; base < nk; base += 256) {
+            const int64_t idx = base + tid;
+            if (idx >= nk) break;
+            int64_t unit;
+            int cp, sp;
+            key_thread_coords<G, KBITS>(idx, kd, unit, cp, sp);
+            quant_key_pair<G, KBITS>(j, kd, cp, sp, ka.codes, ka.scale, ka.zero);
+        }
+    } else if (tid < kd / 8) {
+        *reinterpret_cast<uint4*>(ka.resid + (bh * G + pos % G) * kd + tid * 8) =
+            *reinterpret_cast<const uint4*>(ka.kin + bh * kd + tid * 8);
+    }
 }
 
 inline unsigned grid_of(int64_t threads) { return unsigned((threads + 255) / 256); }
@@ -327,33 +508,40 @@ template <int G, int BITS>
 hipError_t launch_keys_t(const kvq_cache& c, const Geom& g, const void* k_in, int64_t n_in,
                          int64_t in_tok0, int64_t res_tok0, int64_t blk0, int64_t nb,
                          hipStream_t st) {
-    const int BH = g.B * g.Hkv;
-    const int64_t threads = int64_t(BH) * nb * (g.kd / 2) * (G > 32 ? G / 32 : 1);
-    hipLaunchKernelGGL((k_quant_keys<G, BITS>), dim3(grid_of(threads)), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(k_in), n_in, in_tok0,
-                       static_cast<const uint16_t*>(c.buf.k_resid), res_tok0, blk0, int(nb), g.kd,
-                       g.nblk_cap, BH, static_cast<uint32_t*>(c.buf.k_codes),
-                       static_cast<uint16_t*>(c.buf.k_scale), static_cast<uint16_t*>(c.buf.k_zero));
+    KeyArgs a;
+    a.kin = static_cast<const uint16_t*>(k_in);
+    a.resid = static_cast<const uint16_t*>(c.buf.k_resid);
+    a.n_in = n_in;
+    a.in_tok0 = in_tok0;
+    a.res_tok0 = res_tok0;
+    a.blk0 = blk0;
+    a.nblk_cap = g.nblk_cap;
+    a.nb = int(nb);
+    a.kd = g.kd;
+    a.BH = g.B * g.Hkv;
+    a.codes = static_cast<uint32_t*>(c.buf.k_codes);
+    a.scale = static_cast<uint16_t*>(c.buf.k_scale);
+    a.zero = static_cast<uint16_t*>(c.buf.k_zero);
+    const int64_t threads = int64_t(a.BH) * nb * key_threads_per_block<G, BITS>(g.kd);
+    hipLaunchKernelGGL((k_quant_keys<G, BITS>), dim3(grid_of(threads)), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 namespace {
-ValueArgs value_args(const kvq_cache& c, const Geom& g, const void* v_in, int64_t n_in, int64_t row0,
-                     int64_t n_tok, int64_t t_dst0) {
+ValueArgs value_args(const kvq_cache_buffers& buf, const Geom& g, const void* v_in, int64_t n_in, int64_t row0,
+                     int64_t n_tok) {
     ValueArgs a;
     a.vin = static_cast<const uint16_t*>(v_in);
     a.n_in = n_in;
     a.row0 = row0;
     a.n_tok = n_tok;
-    a.t_dst0 = t_dst0;
-    a.cap = g.cap;
     a.vd = g.vd;
     a.BH = g.B * g.Hkv;
-    a.codes = static_cast<uint32_t*>(c.buf.v_codes);
-    a.scale = static_cast<uint16_t*>(c.buf.v_scale);
-    a.zero = static_cast<uint16_t*>(c.buf.v_zero);
+    a.codes = static_cast<uint32_t*>(buf.v_codes);
+    a.scale = static_cast<uint16_t*>(buf.v_scale);
+    a.zero = static_cast<uint16_t*>(buf.v_zero);
     return a;
 }
 ResidArgs resid_args(const kvq_cache& c, const Geom& g, const void* k_in, int64_t n_in, int64_t src0,
@@ -375,25 +563,27 @@ ResidArgs resid_args(const kvq_cache& c, const Geom& g, const void* k_in, int64_
 hipError_t launch_quant_values(const kvq_cache& c, const Geom& g, const void* v_in, int64_t n_in,
                                int64_t row0, int64_t n_tok, int64_t t_dst0, hipStream_t st) {
     if (n_tok <= 0) return hipSuccess;
-    const ValueArgs a = value_args(c, g, v_in, n_in, row0, n_tok, t_dst0);
+    const ValueArgs a = value_args(c.buf, g, v_in, n_in, row0, n_tok);
+    const ContigRows rows{g.cap, t_dst0, n_tok};
     const unsigned grid = grid_of(value_threads(a.BH, n_tok, a.vd));
     if (g.vbits == 2)
-        hipLaunchKernelGGL(k_quant_values<2>, dim3(grid), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_quant_values<2>, dim3(grid), dim3(256), 0, st, a, rows);
     else
-        hipLaunchKernelGGL(k_quant_values<4>, dim3(grid), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_quant_values<4>, dim3(grid), dim3(256), 0, st, a, rows);
     return hipGetLastError();
 }
 
 hipError_t launch_append_rows(const kvq_cache& c, const Geom& g, const void* k_in, const void* v_in,
                               int64_t n, int64_t R, hipStream_t st) {
     if (n <= 0) return hipSuccess;
-    const ValueArgs va = value_args(c, g, v_in, n, 0, n, c.T);
+    const ValueArgs va = value_args(c.buf, g, v_in, n, 0, n);
+    const ContigRows rows{g.cap, c.T, n};
     const ResidArgs ka = resid_args(c, g, k_in, n, 0, R, n);
     const unsigned grid = grid_of(value_threads(va.BH, n, va.vd) + resid_threads(ka));
     if (g.vbits == 2)
-        hipLaunchKernelGGL(k_append_rows<2>, dim3(grid), dim3(256), 0, st, va, ka);
+        hipLaunchKernelGGL(k_append_rows<2>, dim3(grid), dim3(256), 0, st, va, rows, ka);
     else
-        hipLaunchKernelGGL(k_append_rows<4>, dim3(grid), dim3(256), 0, st, va, ka);
+        hipLaunchKernelGGL(k_append_rows<4>, dim3(grid), dim3(256), 0, st, va, rows, ka);
     return hipGetLastError();
 }
 
@@ -421,6 +611,62 @@ hipError_t launch_resid_copy(const kvq_cache& c, const Geom& g, const void* k_in
     const ResidArgs a = resid_args(c, g, k_in, n_in, src0, dst0, m);
     hipLaunchKernelGGL(k_resid_copy, dim3(grid_of(resid_threads(a))), dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+namespace {
+template <int G, int KB>
+hipError_t launch_paged_t(const kvq_paged& c, const Geom& g, const void* k_in, const void* v_in, int n_max,
+                          const PagedSeq& ps, hipStream_t st) {
+    const ValueArgs va = value_args(c.buf, g, v_in, n_max, 0, n_max);
+    const PagedRows rows{ps, g.Hkv, G, n_max};
+    PagedKeyArgs ka;
+    ka.kin = static_cast<const uint16_t*>(k_in);
+    ka.resid = static_cast<uint16_t*>(c.buf.k_resid);
+    ka.ps = ps;
+    ka.n_max = n_max;
+    ka.kd = g.kd;
+    ka.Hkv = g.Hkv;
+    ka.BH = g.B * g.Hkv;
+    // blocks one append can complete: (R + n) / G with R <= G - 1
+    ka.J = (n_max + G - 1) / G;
+    ka.codes = static_cast<uint32_t*>(c.buf.k_codes);
+    ka.scale = static_cast<uint16_t*>(c.buf.k_scale);
+    ka.zero = static_cast<uint16_t*>(c.buf.k_zero);
+    if (n_max == 1) {
+        if (g.vbits == 2)
+            hipLaunchKernelGGL((k_paged_token<G, KB, 2>), dim3(ka.BH), dim3(256), 0, st, va, rows, ka);
+        else
+            hipLaunchKernelGGL((k_paged_token<G, KB, 4>), dim3(ka.BH), dim3(256), 0, st, va, rows, ka);
+        return hipGetLastError();
+    }
+    const int64_t kthreads = int64_t(ka.BH) * ka.J * key_threads_per_block<G, KB>(g.kd);
+    hipLaunchKernelGGL((k_paged_keys<G, KB>), dim3(grid_of(kthreads)), dim3(256), 0, st, ka);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rthreads = value_threads(va.BH, n_max, g.vd) + int64_t(va.BH) * n_max * (g.kd / 8);
+    uint16_t* resid = static_cast<uint16_t*>(c.buf.k_resid);
+    if (g.vbits == 2)
+        hipLaunchKernelGGL(k_paged_rows<2>, dim3(grid_of(rthreads)), dim3(256), 0, st, va, rows, ka.kin, resid, g.kd);
+    else
+        hipLaunchKernelGGL(k_paged_rows<4>, dim3(grid_of(rthreads)), dim3(256), 0, st, va, rows, ka.kin, resid, g.kd);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_paged_append(const kvq_paged& c, const Geom& g, const void* k_in, const void* v_in, int n_max,
+                               const PagedSeq& ps, hipStream_t st) {
+    if (n_max <= 0) return hipSuccess;
+#define KVQ_PAGED(GG, BB) \
+    if (g.kG == GG && g.kbits == BB) return launch_paged_t<GG, BB>(c, g, k_in, v_in, n_max, ps, st);
+    KVQ_PAGED(16, 2)
+    KVQ_PAGED(32, 2)
+    KVQ_PAGED(64, 2)
+    KVQ_PAGED(128, 2)
+    KVQ_PAGED(16, 4)
+    KVQ_PAGED(32, 4)
+    KVQ_PAGED(64, 4)
+#undef KVQ_PAGED
+    return hipErrorInvalidValue;
 }
 
 }  // namespace kvq

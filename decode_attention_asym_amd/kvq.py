@@ -25,7 +25,9 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_E_NULL", -2: "KVQ_E_SHAPE", -3: "KVQ_E_ALIGN",
 EXPORTS = ["kv_cache_buffer_bytes", "kv_cache_init", "kv_cache_destroy", "kv_cache_reset",
            "kv_cache_state", "kv_quantize_append", "kv_flush_residual",
            "kv_decode_workspace_bytes", "kv_decode_attention", "kv_set_timing_events",
-           "kv_decode_variant", "kvq_status_str"]
+           "kv_decode_variant", "kvq_status_str",
+           "kv_paged_buffer_bytes", "kv_paged_init", "kv_paged_destroy", "kv_paged_append",
+           "kv_paged_workspace_bytes", "kv_paged_decode", "kv_paged_variant"]
 
 
 class KvqError(RuntimeError):
@@ -79,6 +81,13 @@ def lib():
             "kv_set_timing_events": (C.c_int, [p, p]),
             "kv_decode_variant": (C.c_char_p, [p, i32]),
             "kvq_status_str": (C.c_char_p, [C.c_int]),
+            "kv_paged_buffer_bytes": (C.c_int, [C.POINTER(CacheCfg), i32, C.POINTER(BufferSizes)]),
+            "kv_paged_init": (C.c_int, [C.POINTER(CacheCfg), i32, C.POINTER(CacheBuffers), C.POINTER(p)]),
+            "kv_paged_destroy": (None, [p]),
+            "kv_paged_append": (C.c_int, [p, p, p, i32, p, p, p, p]),
+            "kv_paged_workspace_bytes": (C.c_int, [p, i32, i32, i32, C.POINTER(u64)]),
+            "kv_paged_decode": (C.c_int, [p, p, i32, C.c_float, p, p, i32, i32, p, p, u64, p]),
+            "kv_paged_variant": (C.c_char_p, [p, i32, i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -154,6 +163,44 @@ def kv_set_timing_events(ev_before, ev_after) -> None:
 
 def kv_decode_variant(handle, n_q_heads: int) -> str:
     return lib().kv_decode_variant(handle, n_q_heads).decode()
+
+
+def kv_paged_buffer_bytes(cfg: CacheCfg, n_pages: int) -> BufferSizes:
+    out = BufferSizes()
+    _check(lib().kv_paged_buffer_bytes(C.byref(cfg), n_pages, C.byref(out)), "kv_paged_buffer_bytes")
+    return out
+
+
+def kv_paged_init(cfg: CacheCfg, n_pages: int, bufs: CacheBuffers) -> int:
+    h = C.c_void_p()
+    _check(lib().kv_paged_init(C.byref(cfg), n_pages, C.byref(bufs), C.byref(h)), "kv_paged_init")
+    return h.value
+
+
+def kv_paged_destroy(handle) -> None:
+    lib().kv_paged_destroy(handle)
+
+
+def kv_paged_append(handle, k_ptr, v_ptr, n_max: int, n_new_ptr, seq_lens_ptr, table_ptr, stream=None) -> None:
+    _check(lib().kv_paged_append(handle, k_ptr, v_ptr, n_max, n_new_ptr, seq_lens_ptr, table_ptr, stream),
+           "kv_paged_append")
+
+
+def kv_paged_workspace_bytes(handle, n_q_heads: int, max_len: int, n_splits: int = 0) -> int:
+    b = C.c_uint64()
+    _check(lib().kv_paged_workspace_bytes(handle, n_q_heads, max_len, n_splits, C.byref(b)),
+           "kv_paged_workspace_bytes")
+    return b.value
+
+
+def kv_paged_decode(handle, q_ptr, n_q_heads: int, softmax_scale: float, seq_lens_ptr, table_ptr,
+                    max_len: int, n_splits: int, out_ptr, ws_ptr, ws_bytes: int, stream=None) -> None:
+    _check(lib().kv_paged_decode(handle, q_ptr, n_q_heads, C.c_float(softmax_scale), seq_lens_ptr, table_ptr,
+                                 max_len, n_splits, out_ptr, ws_ptr, ws_bytes, stream), "kv_paged_decode")
+
+
+def kv_paged_variant(handle, n_q_heads: int, max_len: int) -> str:
+    return lib().kv_paged_variant(handle, n_q_heads, max_len).decode()
 
 
 # ------------------------------------------------------------- config helpers
@@ -254,4 +301,91 @@ class DeviceCache:
             "v_codes": v("v_codes", torch.int32, (B, H, cap, vd * vb // 32)),
             "v_scale": v("v_scale", torch.int16, (B, H, cap, vd // vG)),
             "v_zero": v("v_zero", torch.int16, (B, H, cap, vd // vG)),
+        }
+
+
+class PagedCache:
+    """Caller-owned page pools and residual (allocated with torch) plus a
+    kvq_paged handle.  Block tables and lengths are the caller's int32 device
+    tensors, passed to each call."""
+
+    def __init__(self, cfg: CacheCfg, n_pages: int, device="cuda"):
+        import torch
+
+        self.torch = torch
+        self.cfg = cfg
+        self.n_pages = n_pages
+        self.device = torch.device(device)
+        sizes = kv_paged_buffer_bytes(cfg, n_pages)
+        self.arrays = {}
+        for n in BUFFER_NAMES:
+            nbytes = max(16, int(getattr(sizes, n)))
+            self.arrays[n] = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.bufs = CacheBuffers(*[self.arrays[n].data_ptr() for n in BUFFER_NAMES])
+        self.handle = kv_paged_init(cfg, n_pages, self.bufs)
+        self.sizes = sizes
+
+    def close(self):
+        if self.handle:
+            kv_paged_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def stream(self):
+        return self.torch.cuda.current_stream(self.device).cuda_stream
+
+    def append(self, k, v, seq_lens, block_table, n_new=None):
+        """k, v: [B][Hkv][n_max][d] fp16; seq_lens, block_table, n_new: int32 device tensors."""
+        n_max = k.shape[-2]
+        kv_paged_append(self.handle, k.data_ptr(), v.data_ptr(), n_max,
+                        None if n_new is None else n_new.data_ptr(), seq_lens.data_ptr(),
+                        block_table.data_ptr(), self.stream())
+
+    def workspace(self, n_q_heads: int, max_len: int, n_splits: int = 0):
+        nbytes = kv_paged_workspace_bytes(self.handle, n_q_heads, max_len, n_splits)
+        return self.torch.empty(max(16, nbytes), dtype=self.torch.uint8, device=self.device)
+
+    def decode(self, q, softmax_scale: float, seq_lens, block_table, max_len: int, n_splits: int = 0,
+               out=None, ws=None):
+        torch = self.torch
+        B, Hq = q.shape[0], q.shape[1]
+        if out is None:
+            out = torch.empty((B, Hq, self.cfg.value.dim), dtype=torch.float16, device=self.device)
+        if ws is None:
+            ws = self.workspace(Hq, max_len, n_splits)
+        kv_paged_decode(self.handle, q.data_ptr(), Hq, softmax_scale, seq_lens.data_ptr(),
+                        block_table.data_ptr(), max_len, n_splits, out.data_ptr(), ws.data_ptr(),
+                        ws.numel(), self.stream())
+        return out
+
+    def variant(self, n_q_heads: int, max_len: int) -> str:
+        return kv_paged_variant(self.handle, n_q_heads, max_len)
+
+    def views(self):
+        """Typed views of the page pools and the residual in the documented layouts."""
+        torch = self.torch
+        c = self.cfg
+        B, H, P = c.batch, c.n_kv_heads, self.n_pages
+        kd, G, kb, vd, vG, vb = c.key.dim, c.key.group, c.key.bits, c.value.dim, c.value.group, c.value.bits
+        a = self.arrays
+
+        def v(name, dtype, shape):
+            n = 1
+            for s in shape:
+                n *= s
+            return a[name].view(dtype)[:n].view(*shape)
+
+        return {
+            "k_codes": v("k_codes", torch.int32, (P, H, kd, G * kb // 32)),
+            "k_scale": v("k_scale", torch.int16, (P, H, kd)),
+            "k_zero": v("k_zero", torch.int16, (P, H, kd)),
+            "k_resid": v("k_resid", torch.int16, (B, H, G, kd)),
+            "v_codes": v("v_codes", torch.int32, (P, H, G, vd * vb // 32)),
+            "v_scale": v("v_scale", torch.int16, (P, H, G, vd // vG)),
+            "v_zero": v("v_zero", torch.int16, (P, H, G, vd // vG)),
         }

@@ -28,7 +28,7 @@ import numpy as np
 from .configs import Workload
 
 SEED_BASE = 0x4B495649
-T_KEY, T_VALUE, T_QUERY, T_OUTLIER = 0, 1, 2, 3
+T_KEY, T_VALUE, T_QUERY, T_OUTLIER, T_LENS, T_PAGES = 0, 1, 2, 3, 4, 5
 
 
 def _rng(w: Workload, *words: int) -> np.random.Generator:
@@ -91,3 +91,32 @@ def keys(w: Workload, T: int | None = None, out=None, threads=None) -> np.ndarra
 def values(w: Workload, T: int | None = None, out=None, threads=None) -> np.ndarray:
     """uint16 [B][Hkv][T][vd]."""
     return _fill(value_slice, w, w.T if T is None else T, w.vd, out, threads)
+
+
+# ---------------------------------------------------------------- paged caches
+# Serving-style inputs: sequences of different lengths whose key blocks sit
+# in pages scattered over one pool.  Lengths: uniform integers in
+# [lo_frac * T, T], the last sequence exactly T (so the longest equals the
+# fixed-length workload); pages: a seeded random permutation of the pool,
+# handed out block by block, with `spare` pages never used.
+
+def ragged_lengths(w: Workload, lo_frac: float = 0.5) -> np.ndarray:
+    """int32 [B] sequence lengths."""
+    lo = int(lo_frac * w.T)
+    lens = _rng(w, T_LENS).integers(lo, w.T + 1, size=w.batch).astype(np.int32)
+    lens[-1] = w.T
+    return lens
+
+
+def page_table(w: Workload, blocks: np.ndarray, maxb: int, spare: int = 3, seed_word: int = 0):
+    """(table int32 [B][maxb], n_pages): sequence b gets blocks[b] pages from a
+    shuffled pool of sum(blocks) + spare pages; unused entries are -1."""
+    n_pages = int(np.sum(blocks)) + spare
+    perm = _rng(w, T_PAGES, seed_word).permutation(n_pages).astype(np.int32)
+    table = np.full((w.batch, maxb), -1, np.int32)
+    k = 0
+    for b in range(w.batch):
+        nb = int(blocks[b])
+        table[b, :nb] = perm[k:k + nb]
+        k += nb
+    return table, n_pages

@@ -180,8 +180,83 @@ kvq_status kv_decode_attention(const kvq_cache* cache, const void* q_fp16, int32
                                float softmax_scale, int32_t n_splits, void* out_fp16,
                                void* workspace, uint64_t workspace_bytes, void* hip_stream);
 
+/* ------------------------------------------------------------ paged cache
+ * "Makale Bülteni -- KIVI", section "Kod ve Entegrasyon Haritası": the grouped
+ * residual and the asymmetric layout do not fit a serving engine's paged
+ * block manager as they are; serving a 2-bit asymmetric cache needs paged
+ * 2-bit kernels.  Here a page holds one key block (G tokens, per-channel
+ * codes, all KV heads) and the per-token value codes of the same G tokens;
+ * each sequence slot keeps its own fp16 residual block.
+ *
+ * Layouts for P pages (same element types and word packing as above):
+ *   k_codes  u32  [P][Hkv][kd][G*bits/32]    k_scale, k_zero fp16 [P][Hkv][kd]
+ *   v_codes  u32  [P][Hkv][G][vd*bits/32]    v_scale, v_zero fp16 [P][Hkv][G][vd/Gv]
+ *   k_resid  fp16 [B][Hkv][G][kd]            one residual block per sequence slot
+ * Caller-owned int32 device arrays passed to each call (4-byte aligned):
+ *   block_table [B][max_tokens/G]: page of key block j of sequence b.  The
+ *     page of a block must be in the table before the block's first token is
+ *     appended (its values go to that page at once).
+ *   seq_lens [B]: tokens of sequence b.  Sequences are independent (ragged
+ *     lengths); the library never changes these arrays.
+ * Device-side entries are not seen by the host: an append skips every
+ * sequence whose length, row count or capacity is out of range and every
+ * row whose page number is outside [0, P); decode clamps lengths to
+ * [0, max_len] and page numbers into [0, P), so bad entries give wrong
+ * output but no access outside the arrays.
+ * B (batch) in the configuration is the number of sequence slots and
+ * max_tokens the capacity of one sequence. */
+typedef struct kvq_paged kvq_paged;   /* opaque host handle */
+
+/* Sizes of the seven device arrays of a paged cache with n_pages pages.
+ * Validation of cfg as kv_cache_buffer_bytes; n_pages >= 1 (else
+ * KVQ_E_SHAPE). */
+kvq_status kv_paged_buffer_bytes(const kvq_cache_cfg* cfg, int32_t n_pages, kvq_buffer_sizes* out);
+
+/* Handle over caller-owned paged arrays (sizes from kv_paged_buffer_bytes,
+ * 16-byte aligned).  Holds no lengths: those are the caller's device array.
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE, KVQ_E_ALIGN, KVQ_E_UNSUPPORTED. */
+kvq_status kv_paged_init(const kvq_cache_cfg* cfg, int32_t n_pages, const kvq_cache_buffers* bufs,
+                         kvq_paged** out);
+
+/* Free the host handle.  NULL is a no-op. */
+void kv_paged_destroy(kvq_paged* cache);
+
+/* Append rows to every sequence: sequence b takes n_new[b] rows (all n_max
+ * when n_new is NULL; 0 <= n_new[b] <= n_max) at tokens seq_lens[b] ..
+ * ("İddia ve Gerçeklik: KIVI": values quantized per token at once, into the
+ * page of their block; keys join the residual, and every block of G keys
+ * that fills is quantized per channel into its page).  k_fp16 / v_fp16 are
+ * [B][Hkv][n_max][d] (MLA: [B][n_max][d]).  seq_lens holds the lengths
+ * before the append; the caller advances them afterwards.  n_max == 1 (the
+ * decode step) is one launch; larger appends two.
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE (n_max < 0), KVQ_E_ALIGN, KVQ_E_CAPACITY
+ * (n_max > max_tokens), KVQ_E_HIP. */
+kvq_status kv_paged_append(kvq_paged* cache, const void* k_fp16, const void* v_fp16, int32_t n_max,
+                           const int32_t* n_new, const int32_t* seq_lens, const int32_t* block_table,
+                           void* hip_stream);
+
+/* Workspace bytes kv_paged_decode needs for n_q_heads, the length bound
+ * max_len (0 <= max_len <= max_tokens) and n_splits (0 = automatic).
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE. */
+kvq_status kv_paged_workspace_bytes(const kvq_paged* cache, int32_t n_q_heads, int32_t max_len,
+                                    int32_t n_splits, uint64_t* bytes);
+
+/* Decode attention of one query per (sequence, query head) over the
+ * seq_lens[b] tokens of each sequence, as kv_decode_attention computes it
+ * for one sequence; max_len (host) bounds every length and sizes the split
+ * plan.  A sequence of length 0 gets a zero output.
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE (n_q_heads, n_splits, max_len out of
+ * range), KVQ_E_ALIGN, KVQ_E_WORKSPACE, KVQ_E_HIP. */
+kvq_status kv_paged_decode(const kvq_paged* cache, const void* q_fp16, int32_t n_q_heads, float softmax_scale,
+                           const int32_t* seq_lens, const int32_t* block_table, int32_t max_len,
+                           int32_t n_splits, void* out_fp16, void* workspace, uint64_t workspace_bytes,
+                           void* hip_stream);
+
+/* Name of the kernel kv_paged_decode would launch (automatic splits). */
+const char* kv_paged_variant(const kvq_paged* cache, int32_t n_q_heads, int32_t max_len);
+
 /* Profiling hook: when both are non-NULL (hipEvent_t, created by the caller),
- * later kv_decode_attention calls launch their split-K pass-1 kernel with
+ * later kv_decode_attention / kv_paged_decode calls launch their split-K pass-1 kernel with
  * hipExtLaunchKernel so that the launch itself records its start and stop
  * timestamps into ev_before / ev_after (no separate event packets in the
  * stream).  NULL, NULL switches it off.  Process-wide. */

@@ -175,3 +175,117 @@ def test_variant_per_workload(name, variant):
         assert kvq.kv_decode_variant(h, w.n_q_heads) == variant
     finally:
         kvq.kv_cache_destroy(h)
+
+
+# ------------------------------------------------------------------ paged
+
+def test_paged_buffer_sizes_follow_layout():
+    for kw in (dict(), dict(kG=64), dict(kbits=4, vbits=4, kd=64, vd=64)):
+        cfg = kivi_cfg(**kw)
+        P = 37
+        s = kvq.kv_paged_buffer_bytes(cfg, P)
+        H, kd, G, vd = cfg.n_kv_heads, cfg.key.dim, cfg.key.group, cfg.value.dim
+        assert s.k_codes == P * H * kd * (G * cfg.key.bits // 32) * 4
+        assert s.k_scale == s.k_zero == P * H * kd * 2
+        assert s.k_resid == cfg.batch * H * G * kd * 2
+        assert s.v_codes == P * H * G * vd * cfg.value.bits // 8
+        assert s.v_scale == s.v_zero == P * H * G * (vd // 32) * 2
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kv_paged_buffer_bytes(kivi_cfg(), 0)
+    assert e.value.status == -2
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kv_paged_buffer_bytes(kivi_cfg(kG=48), 4)
+    assert e.value.status == -2
+
+
+def _paged(cfg=None, n_pages=8):
+    cfg = cfg or kivi_cfg()
+    return kvq.kv_paged_init(cfg, n_pages, kvq.CacheBuffers(*FAKE))
+
+
+def test_paged_init_checks():
+    L = kvq.lib()
+    h = C.c_void_p()
+    cfg = kivi_cfg()
+    assert L.kv_paged_init(C.byref(cfg), 8, None, C.byref(h)) == -1
+    bad = list(FAKE)
+    bad[5] += 2
+    assert L.kv_paged_init(C.byref(cfg), 8, C.byref(kvq.CacheBuffers(*bad)), C.byref(h)) == -3
+    bad[5] = 0
+    assert L.kv_paged_init(C.byref(cfg), 8, C.byref(kvq.CacheBuffers(*bad)), C.byref(h)) == -1
+    assert L.kv_paged_init(C.byref(cfg), 0, C.byref(kvq.CacheBuffers(*FAKE)), C.byref(h)) == -2
+    kvq.kv_paged_destroy(_paged())
+    kvq.kv_paged_destroy(None)
+
+
+def test_paged_append_validation_before_hip():
+    L = kvq.lib()
+    h = _paged()
+    k, v, lens, table, nn = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    try:
+        assert L.kv_paged_append(h, k, v, 0, None, lens, table, None) == 0        # nothing to do
+        assert L.kv_paged_append(h, k, v, -1, None, lens, table, None) == -2
+        assert L.kv_paged_append(None, k, v, 1, None, lens, table, None) == -1
+        assert L.kv_paged_append(h, k, v, 1, None, None, table, None) == -1
+        assert L.kv_paged_append(h, k, v, 1, None, lens, None, None) == -1
+        assert L.kv_paged_append(h, None, v, 1, None, lens, table, None) == -1
+        assert L.kv_paged_append(h, k + 8, v, 1, None, lens, table, None) == -3
+        assert L.kv_paged_append(h, k, v, 1, None, lens + 2, table, None) == -3
+        assert L.kv_paged_append(h, k, v, 1, nn + 1, lens, table, None) == -3
+        assert L.kv_paged_append(h, k, v, 257, None, lens, table, None) == -4      # > max_tokens
+    finally:
+        kvq.kv_paged_destroy(h)
+
+
+def test_paged_decode_validation_before_hip():
+    L = kvq.lib()
+    h = _paged()
+    q, out, ws, lens, table = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    try:
+        need = kvq.kv_paged_workspace_bytes(h, 8, 256)
+        assert need > 0 and need % 4 == 0
+        ok = (h, q, 8, C.c_float(0.1), lens, table, 256, 0, out, ws, need, None)
+
+        def call(**kw):
+            a = list(ok)
+            names = ["h", "q", "hq", "sigma", "lens", "table", "max_len", "ns", "out", "ws", "wsb", "st"]
+            for key, val in kw.items():
+                a[names.index(key)] = val
+            return L.kv_paged_decode(*a)
+
+        assert call(h=None) == -1
+        assert call(lens=None) == -1
+        assert call(table=None) == -1
+        assert call(hq=6) == -2                 # not a multiple of Hkv = 4
+        assert call(ns=257) == -2
+        assert call(max_len=257) == -2          # above max_tokens
+        assert call(max_len=-1) == -2
+        assert call(q=q + 4) == -3
+        assert call(lens=lens + 1) == -3
+        assert call(wsb=need - 4) == -6
+        for bad in ((8, -1, 0), (8, 300, 0), (6, 64, 0), (8, 64, 300)):
+            with pytest.raises(kvq.KvqError):
+                kvq.kv_paged_workspace_bytes(h, bad[0], bad[1], bad[2])
+        # a longer bound never needs less workspace
+        sizes = [kvq.kv_paged_workspace_bytes(h, 8, m) for m in (0, 1, 64, 65, 200, 256)]
+        assert sizes == sorted(sizes)
+    finally:
+        kvq.kv_paged_destroy(h)
+
+
+def test_paged_variant_choice():
+    gqa = _paged(kivi_cfg(batch=4, n_kv_heads=2, max_tokens=1 << 20, kG=64), 64)
+    d64 = _paged(kivi_cfg(kd=64, vd=64), 8)
+    mla = _paged(kvq.cache_cfg(kvq.KVQ_KIND_MLA, 2, 1, 1024, 64, 64, 4, 512, 32, 2), 8)
+    try:
+        assert kvq.kv_paged_variant(gqa, 8, 4096) == "gqa_mfma_paged"
+        assert kvq.kv_paged_variant(gqa, 8, 0) == "gqa_mfma_paged"
+        # more than 255 runs of 64 tiles do not fit the merge's slots
+        assert kvq.kv_paged_variant(gqa, 8, 1 << 20) == "generic_paged"
+        assert kvq.kv_paged_variant(gqa, 16, 4096) == "generic_paged"   # 8 q heads per KV head
+        assert kvq.kv_paged_variant(d64, 8, 256) == "generic_paged"
+        assert kvq.kv_paged_variant(mla, 16, 1024) == "generic_paged"
+        assert kvq.kv_paged_variant(gqa, 8, -1) == "invalid"
+    finally:
+        for h in (gqa, d64, mla):
+            kvq.kv_paged_destroy(h)

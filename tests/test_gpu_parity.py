@@ -225,6 +225,25 @@ def test_unflushed_full_residual_mfma(orc, shape):
     _check_decode(orc, w, dc, k, v, kq_blocks=nq // G)
 
 
+@pytest.mark.parametrize("G,kbits", [(64, 2), (128, 2), (64, 4)])
+def test_head_dim_32(orc, G, kbits):
+    """kd = 32: fewer channel pairs than a wave's share when a block spans
+    several row ranges (G > 32), bulk and single-token appends."""
+    w = _tiny(3 * G + 7, Hq=2, Hkv=2, D=32, G=G, kbits=kbits)
+    cap = w.capacity(8)
+    k, v = synth.keys(w), synth.values(w)
+    dc = new_cache(w, cap)
+    n0 = w.T - 5
+    dc.append(dev_f16(np.ascontiguousarray(k[:, :, :n0])), dev_f16(np.ascontiguousarray(v[:, :, :n0])))
+    for t in range(n0, w.T):
+        dc.append(dev_f16(np.ascontiguousarray(k[:, :, t:t + 1])), dev_f16(np.ascontiguousarray(v[:, :, t:t + 1])))
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            assert_slices_equal(slice_of(dc, b, h, w.T, w.n_blocks),
+                                oracle_slice(orc, w, k[b, h], v[b, h], cap // w.kG, cap))
+    _check_decode(orc, w, dc, k, v)
+
+
 @pytest.mark.parametrize("kbits,vbits,G", [(4, 4, 32), (4, 2, 64), (2, 4, 16), (2, 2, 128), (4, 4, 16)])
 def test_bit_widths_and_groups(orc, kbits, vbits, G):
     w = _tiny(3 * G + 7, Hq=4, Hkv=2, D=64, G=G, kbits=kbits, vbits=vbits)
