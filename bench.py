@@ -68,6 +68,8 @@ def parse():
                     help="caches to rotate over (default: enough for 1 GB, at most 32)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--paged", action="store_true",
+                    help="paged cache: ragged lengths in [T/2, T], blocks in shuffled pages")
     return ap.parse_args()
 
 
@@ -125,10 +127,11 @@ def copy_ceiling_gbps():
     return 2 * n / (float(np.median(ts)) * 1e-3) / 1e9
 
 
-def cpu_baseline(w, k, v, q, cap, n_pairs):
+def cpu_baseline(w, k, v, q, cap, n_pairs, lens=None):
     """The oracle, as it stands, on a bounded sample of the same workload:
     decode attention of n_pairs (batch, query head) pairs over the full cache
-    of their KV heads, threaded over the pairs."""
+    of their KV heads (sequence b's first lens[b] tokens when lengths are
+    ragged), threaded over the pairs."""
     import oracle
 
     group = w.n_q_heads // w.n_kv_heads
@@ -139,7 +142,9 @@ def cpu_baseline(w, k, v, q, cap, n_pairs):
         p += 1
     caches, qs = [], []
     for b, h in slices:
-        caches.append(oracle.build_cache(k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], w.kG, w.kbits,
+        T = w.T if lens is None else int(lens[b])
+        caches.append(oracle.build_cache(np.ascontiguousarray(k[b:b + 1, h:h + 1, :T]),
+                                         np.ascontiguousarray(v[b:b + 1, h:h + 1, :T]), w.kG, w.kbits,
                                          w.vG, w.vbits, nblk_cap=cap // w.kG, tok_cap=cap))
         qs.append(np.ascontiguousarray(q[b:b + 1, h * group:(h + 1) * group]))
     # one oracle call per slice would serialise on `group` threads; run the
@@ -152,12 +157,14 @@ def cpu_baseline(w, k, v, q, cap, n_pairs):
         list(ex.map(lambda i: fn(caches[i], qs[i], w.sigma, nthreads=group), range(len(slices))))
     dt = time.perf_counter() - t0
     n_sl = len(slices)
-    sample_bytes = w.with_T(w.T).cache_bytes() // (w.batch * w.n_kv_heads) * n_sl \
+    Ts = [w.T if lens is None else int(lens[b]) for b, _ in slices]
+    sample_bytes = sum(w.cache_bytes(T) // (w.batch * w.n_kv_heads) for T in Ts) \
         + n_sl * group * (w.qd + w.vd) * 2
+    span = f"T={w.T}" if lens is None else f"their lengths ({min(Ts)}..{max(Ts)})"
     return {"value": sample_bytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{n_sl} (batch, kv-head) slices x {group} query heads = {n_sl * group} "
-                      f"decode pairs over T={w.T} (of {w.batch * w.n_q_heads}); {dt:.2f} s wall",
-            "tokens_per_s_attended": n_sl * w.T / dt}
+                      f"decode pairs over {span} (of {w.batch * w.n_q_heads}); {dt:.2f} s wall",
+            "tokens_per_s_attended": sum(Ts) / dt}
 
 
 def main():
@@ -176,6 +183,9 @@ def main():
     w = configs.BY_NAME[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.paged:
+        main_paged(args, w, dev)
+        return
     n_steps = args.warmup + args.steps
     L = args.layers or min(32, max(1, -(-1_000_000_000 // w.cache_bytes())))
     n_new = -(-n_steps // L)              # new tokens each layer receives
@@ -324,6 +334,158 @@ def main():
         res["cpu_baseline"] = cpu_baseline(w, k[:, :, :w.T], v[:, :, :w.T], q, cap, args.cpu_pairs)
     print(json.dumps(res), flush=True)
     for c in dcs:
+        c.close()
+
+
+def main_paged(args, w, dev):
+    """The same step on a paged cache: sequence b holds lens[b] tokens
+    (uniform in [T/2, T], the longest exactly T), its key blocks in pages of
+    a shuffled pool; each step appends one token to every sequence
+    (kv_paged_append) and attends over each sequence's own length
+    (kv_paged_decode)."""
+    import torch
+
+    from decode_attention_asym_amd import kvq, synth
+
+    n_steps = args.warmup + args.steps
+    lens0 = synth.ragged_lengths(w)
+    mean_bytes = float(np.mean([w.cache_bytes(int(T)) for T in lens0]))
+    L = args.layers or min(32, max(1, -(-1_000_000_000 // int(mean_bytes))))
+    n_new = -(-n_steps // L)
+    cap = w.capacity(n_new + 1)
+    maxb = cap // w.kG
+    max_len = w.T + n_new
+    t0 = time.time()
+    k = synth.keys(w, w.T + n_new)
+    v = synth.values(w, w.T + n_new)
+    q = synth.query(w)
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def dev16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.float16).to(dev)
+
+    def dev32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    blocks = -(-(lens0 + n_new) // w.kG)
+    caches, tables = [], []
+    for layer in range(L):
+        table, n_pages = synth.page_table(w, blocks, maxb, spare=7, seed_word=layer)
+        caches.append(kvq.PagedCache(kvq.cfg_for(w, cap), n_pages, device=dev))
+        tables.append(dev32(table))
+    stream = torch.cuda.current_stream()
+    # prefill: every sequence's lens[b] tokens in one append
+    kd, vd = dev16(k[:, :, :w.T]), dev16(v[:, :, :w.T])
+    zeros, l0 = dev32(np.zeros(w.batch)), dev32(lens0)
+    qt = []
+    for layer in range(L):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        caches[layer].append(kd, vd, zeros, tables[layer], l0)
+        b.record(stream)
+        torch.cuda.synchronize()
+        qt.append(a.elapsed_time(b))
+    q_ms = float(np.median(qt))
+    q_bytes = int(sum(2 * w.n_kv_heads * int(T) * (w.kd + w.vd) + w.cache_bytes(int(T)) // w.batch
+                      for T in lens0))
+    del kd, vd
+    # the new token of step j for sequence b is its row lens0[b] + j
+    rows = lens0[:, None] + np.arange(n_new)[None, :]                      # [B][n_new]
+    kn = np.take_along_axis(k, rows[:, None, :, None], axis=2)              # [B][Hkv][n_new][kd]
+    vn = np.take_along_axis(v, rows[:, None, :, None], axis=2)
+    knew = dev16(np.ascontiguousarray(kn.transpose(2, 0, 1, 3))[:, :, :, None, :])
+    vnew = dev16(np.ascontiguousarray(vn.transpose(2, 0, 1, 3))[:, :, :, None, :])
+    lens_dev = [dev32(lens0 + j) for j in range(n_new + 1)]
+    qd = dev16(q)
+    out = torch.empty((w.batch, w.n_q_heads, w.vd), dtype=torch.float16, device=dev)
+    ws = caches[0].workspace(w.n_q_heads, max_len, args.splits)
+    hip = HipEvents()
+    evs = [(hip.create(), hip.create()) for _ in range(args.steps)]
+
+    lib = kvq.lib()
+    c_append, c_decode, c_timing = lib.kv_paged_append, lib.kv_paged_decode, lib.kv_set_timing_events
+    handles = [c.handle for c in caches]
+    tptr = [t.data_ptr() for t in tables]
+    lptr = [t.data_ptr() for t in lens_dev]
+    kptr = [knew[j].data_ptr() for j in range(n_new)]
+    vptr = [vnew[j].data_ptr() for j in range(n_new)]
+    sptr, qptr, optr, wptr, wbytes = stream.cuda_stream, qd.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel()
+
+    def step(i, timed):
+        layer, j = i % L, i // L
+        if timed:
+            st = c_timing(*evs[i - args.warmup])
+            assert st == 0, st
+        st = c_append(handles[layer], kptr[j], vptr[j], 1, None, lptr[j], tptr[layer], sptr)
+        assert st == 0, kvq.kvq_status_str(st)
+        st = c_decode(handles[layer], qptr, w.n_q_heads, w.sigma, lptr[j + 1], tptr[layer], max_len, args.splits,
+                      optr, wptr, wbytes, sptr)
+        assert st == 0, kvq.kvq_status_str(st)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.warmup, n_steps):
+        step(i, True)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    kvq.kv_set_timing_events(None, None)
+    total_ms = start.elapsed_time(stop)
+    pass1_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+
+    def step_bytes(j, qo):
+        # every sequence after its append: lens0[b] + j + 1 tokens
+        return sum(w.cache_bytes(int(T) + j + 1) // w.batch for T in lens0) + qo
+
+    js = [i // L for i in range(args.warmup, n_steps)]
+    alg_bytes = sum(step_bytes(j, w.qo_bytes()) for j in js)
+    value = alg_bytes / (total_ms * 1e-3) / 1e9
+    p1_avg = float(np.mean(pass1_ms))
+    p1_bytes = float(np.mean([step_bytes(j, w.batch * w.n_q_heads * w.qd * 2) for j in js]))
+    achieved = p1_bytes / (p1_avg * 1e-3) / 1e9
+    ms_step = total_ms / args.steps
+    p1_sorted = np.sort(pass1_ms)
+    variant = caches[0].variant(w.n_q_heads, max_len)
+    res = {
+        "metric": "2-bit decode attention KV bytes/s (tokens/s, % HBM peak; quantize GB/s)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name + "_paged_ragged", "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.kd, "context": f"{int(lens0.min())}..{w.T}",
+                   "mean_context": round(float(lens0.mean()), 1), "G": w.kG, "bits": w.kbits,
+                   "value_group": w.vG, "layers": L, "page_tokens": w.kG, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": profiled_traffic(variant, w.name + "_paged_ragged"),
+                     "kernel": "decode pass-1 (" + variant + ")", "avg_us": round(p1_avg * 1e3, 2),
+                     "alg_bytes_per_launch": int(p1_bytes)},
+        "extra": {
+            "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
+            "attended_kv_tokens_per_s": round(float(np.mean([np.sum(lens0 + j + 1) for j in js])) / (ms_step * 1e-3), 1),
+            "hbm_frac_whole_step": round(value / HBM_PEAK_GBPS, 4),
+            "pass1_us_p10_p50_p90": [round(float(np.percentile(p1_sorted, x)) * 1e3, 2) for x in (10, 50, 90)],
+            "prefill_quantize_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 2),
+            "prefill_quantize_ms": round(q_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, k, v, q, cap, args.cpu_pairs, lens=lens0)
+    print(json.dumps(res), flush=True)
+    for c in caches:
         c.close()
 
 

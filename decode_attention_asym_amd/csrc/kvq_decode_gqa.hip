@@ -311,12 +311,12 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
 }
 
 // the code-tile run of a main split: contiguous (one buffer resource per
-// run) or paged (per-tile resources over the pages of the block table)
+// run) or paged (per-tile resources over the pages of the block table,
+// loaded at the kernel's start)
 template <int G, bool PAGED>
-__device__ __forceinline__ auto make_run(const MfmaParams& p, int b, int kvh, int64_t bh, int t_lo, int t_hi,
-                                         int lane) {
+__device__ __forceinline__ auto pick_run(const MfmaParams& p, const PagedRun& prun, int64_t bh, int t_lo, int t_hi) {
     if constexpr (PAGED)
-        return paged_run<G>(p, b, kvh, t_lo, t_hi, lane);
+        return prun;
     else
         return tile_run<G>(p, bh, t_lo, t_hi);
 }
@@ -327,30 +327,37 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 15, kg = lane >> 4;
     const int hh = lane >> 4, chunk = lane & 15;
-    const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    bool tail;
+    const int s = slot_of_block(p, tail);
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int hq0 = kvh * HG;
-    // a paged sequence has its own length; its main splits take p.chunk
-    // tiles each from the start, so those past its tiles are empty
+    // a paged sequence has its own length; main split s takes tiles
+    // [s * chunk, (s + 1) * chunk) of it, so the splits past a shorter
+    // sequence's tiles are empty, and the page numbers of a split are known
+    // before its length is
     int t_lo, t_hi;
+    [[maybe_unused]] PagedRun prun;
     if constexpr (PAGED) {
-        const int len = seq_len(p, b);
-        const int64_t nblk = len / G;
-        const int ntiles = int(nblk * G / 64);
-        if (s >= p.S_main) {
+        if (tail) {
+            const int len = seq_len(p, b);
+            const int64_t nblk = len / G;
             if (wave == 0)
                 tail_split<HG>(p, PagedBlocks{}, b, kvh, s, reinterpret_cast<float*>(L.k.qa),
-                               reinterpret_cast<float*>(L.v.pa), len, nblk, ntiles);
+                               reinterpret_cast<float*>(L.v.pa), len, nblk, int(nblk * G / 64));
             return;
         }
         t_lo = s * p.chunk;
+        prun = paged_run<G>(p, b, kvh, t_lo, lane);
+        const int ntiles = seq_len(p, b) / G * G / 64;
         t_hi = t_lo + p.chunk < ntiles ? t_lo + p.chunk : ntiles;
         if (t_lo >= t_hi) {
             empty_partial<HG>(p, b, kvh, s);
             return;
         }
+        prun.t_last = t_hi - 1;
     } else {
-        if (s >= p.S_main) {
+        if (tail) {
             if (wave == 0) tail_split<HG>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
             return;
         }
@@ -367,7 +374,7 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
         KState st;
         st.m0 = st.m1 = st.m2 = st.m3 = -INFINITY;
         KTile ta, tb;
-        const auto run = make_run<G, PAGED>(p, b, kvh, bh, t_lo, t_hi, lane);
+        const auto run = pick_run<G, PAGED>(p, prun, bh, t_lo, t_hi);
         load_ktile<G>(p, run, bh, t_lo, lane, ta);
         load_ktile<G>(p, run, bh, t_lo + 1, lane, tb);
         // keep these loads ahead of (not interleaved with) the prefetch of tile 2
@@ -403,7 +410,7 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
             for (int u = 0; u < 4; ++u) st.O[P][u] = f32x4{0.f, 0.f, 0.f, 0.f};
         // value work trails the key work by one tile: tile j after barrier j
         VTile ta, tb;
-        const auto run = make_run<G, PAGED>(p, b, kvh, bh, t_lo, t_hi, lane);
+        const auto run = pick_run<G, PAGED>(p, prun, bh, t_lo, t_hi);
         load_vtile<G>(p, run, bh, t_lo, lane, ta);
         load_vtile<G>(p, run, bh, t_lo + 1, lane, tb);
         __builtin_amdgcn_sched_barrier(0);

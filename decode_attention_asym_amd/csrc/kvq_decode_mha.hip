@@ -238,10 +238,12 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
     __shared__ Lds L;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 15, kg = lane >> 4;
-    const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    bool tail;
+    const int s = slot_of_block(p, tail);
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int64_t slot = (int64_t(b) * p.Hq + kvh) * p.S + s;
-    if (s >= p.S_main) {
+    if (tail) {
         if (wave == 0) tail_split<1>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
         return;
     }

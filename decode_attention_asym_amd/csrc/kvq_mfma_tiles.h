@@ -330,13 +330,19 @@ struct PagedRun {
     int t0, t_last, kvh;
 };
 
+// The page numbers of the p.chunk tiles from t_lo (those inside the table
+// row): they do not depend on the sequence length, so this load is issued
+// alongside the length's instead of after it (two dependent round trips
+// before the first tile arrives, not three).  t_last is set once the length
+// is known.
 template <int G>
-__device__ __forceinline__ PagedRun paged_run(const MfmaParams& p, int b, int kvh, int t_lo, int t_hi, int lane) {
+__device__ __forceinline__ PagedRun paged_run(const MfmaParams& p, int b, int kvh, int t_lo, int lane) {
     constexpr int NBT = 64 / G;
     PagedRun r;
-    r.pg = lane < (t_hi - t_lo) * NBT ? page_of(p, b, int64_t(t_lo) * NBT + lane) : 0;
+    const int64_t j = int64_t(t_lo) * NBT + lane;
+    r.pg = lane < p.chunk * NBT && j < p.maxb ? page_of(p, b, j) : 0;
     r.t0 = t_lo;
-    r.t_last = t_hi - 1;
+    r.t_last = t_lo - 1;
     r.kvh = kvh;
     return r;
 }
@@ -495,49 +501,64 @@ __device__ __forceinline__ f16x8 code_slice(const CodeRegs& c, uint32_t mk) {
 // fp16 residual keys, one token per lane for the logits, two channels per
 // lane for the values.  Runs on one wave; qf holds HG*D floats, pl HG*PSTR.
 
-template <class Blocks>
-__device__ __forceinline__ float key_hat(const MfmaParams& p, const Blocks& blocks, int b, int kvh, int64_t nblk,
-                                         int64_t t, int c) {
-    const int64_t Tq = nblk * p.G;
-    if (t >= Tq) return h2f(p.kr[((int64_t(b) * p.Hkv + kvh) * p.G + (t - Tq)) * D + c]);
-    const int64_t blk = t / p.G;
-    const int i = int(t - blk * p.G);
-    const int64_t side = blocks(p, b, kvh, blk) * D + c;
-    const uint32_t w = p.kc[side * (p.G / 16) + i / 16];
-    return fmaf(float((w >> (2 * (i & 15))) & 3u), h2f(p.ks[side]), h2f(p.kz[side]));
-}
-
-template <class Blocks>
-__device__ __forceinline__ float value_hat(const MfmaParams& p, const Blocks& blocks, int b, int kvh, int64_t t,
-                                           int c) {
-    const int64_t blk = t / p.G;
-    const int64_t row = blocks(p, b, kvh, blk) * p.G + (t - blk * p.G);
-    const uint32_t w = p.vc[row * 8 + c / 16];
-    const int64_t side = row * 4 + c / 32;
-    return fmaf(float((w >> (2 * (c & 15))) & 3u), h2f(p.vs[side]), h2f(p.vz[side]));
-}
-
 // tokens [ntiles * 64, T) of sequence b, nblk of its key blocks quantized
-// (an empty range writes an empty partial: m = -inf, l = 0, acc = 0)
+// (an empty range writes an empty partial: m = -inf, l = 0, acc = 0).  The
+// tail spans at most two key blocks, whose rows are looked up once; keys
+// and values are read 8 channels / 8 tokens at a time, all loads of a group
+// before its arithmetic (one wave: the latency of dependent round trips is
+// what bounds it), with the accumulation order of a plain loop.
 template <int HG, class Blocks>
 __device__ void tail_split(const MfmaParams& p, const Blocks& blocks, int b, int kvh, int s, float* qf, float* pl,
                            int64_t T, int64_t nblk, int ntiles) {
     const int lane = threadIdx.x & 63;
     const int hq0 = kvh * HG;
     for (int i = lane; i < HG * D; i += 64) qf[i] = h2f(p.q[(int64_t(b) * p.Hq + hq0) * D + i]);
-    wave_sync();
     const int64_t t0 = int64_t(ntiles) * 64;
     const int n_tail = int(T - t0);
+    const int64_t Tq = nblk * p.G;
+    const int64_t jb = t0 / p.G;   // first key block of the tail
+    const int64_t row0 = n_tail > 0 ? blocks(p, b, kvh, jb) : 0;
+    const int64_t row1 = n_tail > 0 && (T - 1) / p.G > jb ? blocks(p, b, kvh, jb + 1) : row0;
+    wave_sync();
     const int64_t t = t0 + lane;
     const bool valid = lane < n_tail;
     float sc[HG];
 #pragma unroll
     for (int h = 0; h < HG; ++h) sc[h] = 0.0f;
     if (valid) {
-        for (int c = 0; c < D; ++c) {
-            const float kh = key_hat(p, blocks, b, kvh, nblk, t, c);
+        // a residual key row, or token i of quantized block jb (G = 32 only)
+        const bool resid = t >= Tq;
+        const uint16_t* krow = p.kr + ((int64_t(b) * p.Hkv + kvh) * p.G + (resid ? t - Tq : 0)) * D;
+        const int i = int(t - jb * p.G);
+        for (int c0 = 0; c0 < D; c0 += 8) {
+            float kh[8];
+            if (resid) {
+                const uint4 r = *reinterpret_cast<const uint4*>(krow + c0);
+                const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-            for (int h = 0; h < HG; ++h) sc[h] = fmaf(qf[h * D + c], kh, sc[h]);
+                for (int e = 0; e < 4; ++e) {
+                    kh[2 * e] = lo_h(w[e]);
+                    kh[2 * e + 1] = hi_h(w[e]);
+                }
+            } else {
+                const int64_t side = row0 * D + c0;
+                const uint4 sv = *reinterpret_cast<const uint4*>(p.ks + side);
+                const uint4 zv = *reinterpret_cast<const uint4*>(p.kz + side);
+                uint32_t wd[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wd[e] = p.kc[(side + e) * (p.G / 16) + i / 16];
+                const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w}, zw[4] = {zv.x, zv.y, zv.z, zv.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float sc_e = (e & 1) ? hi_h(sw[e >> 1]) : lo_h(sw[e >> 1]);
+                    const float z_e = (e & 1) ? hi_h(zw[e >> 1]) : lo_h(zw[e >> 1]);
+                    kh[e] = fmaf(float((wd[e] >> (2 * (i & 15))) & 3u), sc_e, z_e);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int h = 0; h < HG; ++h) sc[h] = fmaf(qf[h * D + c0 + e], kh[e], sc[h]);
         }
     }
     float m[HG], l[HG];
@@ -560,10 +581,25 @@ __device__ void tail_split(const MfmaParams& p, const Blocks& blocks, int b, int
         float acc[HG];
 #pragma unroll
         for (int h = 0; h < HG; ++h) acc[h] = 0.0f;
-        for (int j = 0; j < n_tail; ++j) {
-            const float vh = value_hat(p, blocks, b, kvh, t0 + j, c);
+        for (int j0 = 0; j0 < n_tail; j0 += 8) {
+            float vh[8];
 #pragma unroll
-            for (int h = 0; h < HG; ++h) acc[h] = fmaf(pl[h * PSTR + j], vh, acc[h]);
+            for (int e = 0; e < 8; ++e) {
+                // past the tail: reload its last token (in bounds, unused)
+                const int64_t tt = t0 + (j0 + e < n_tail ? j0 + e : n_tail - 1);
+                const int64_t blk = tt / p.G;
+                const int64_t row = (blk == jb ? row0 : row1) * p.G + (tt - blk * p.G);
+                const uint32_t w = p.vc[row * 8 + c / 16];
+                const int64_t side = row * 4 + c / 32;
+                vh[e] = fmaf(float((w >> (2 * (c & 15))) & 3u), h2f(p.vs[side]), h2f(p.vz[side]));
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (j0 + e < n_tail) {
+#pragma unroll
+                    for (int h = 0; h < HG; ++h) acc[h] = fmaf(pl[h * PSTR + j0 + e], vh[e], acc[h]);
+                }
+            }
         }
 #pragma unroll
         for (int h = 0; h < HG; ++h)
@@ -583,6 +619,16 @@ __device__ void tail_split(const MfmaParams& p, const Blocks& blocks, int b, int
 template <int HG>
 __device__ void tail_split(const MfmaParams& p, int b, int kvh, int s, float* qf, float* pl) {
     tail_split<HG>(p, ContigBlocks{}, b, kvh, s, qf, pl, p.T, p.nblk, p.ntiles);
+}
+
+// The tail workgroup (partial tile and residual keys, a chain of dependent
+// loads on one wave) is block x = 0 of its (sequence, KV head), so that it
+// starts with the first wave of workgroups instead of the last; it still
+// writes partial slot S_main.  Returns the partial slot of this workgroup.
+__device__ __forceinline__ int slot_of_block(const MfmaParams& p, bool& tail) {
+    const bool has_tail = p.S > p.S_main;
+    tail = has_tail && blockIdx.x == 0;
+    return tail ? p.S_main : int(blockIdx.x) - (has_tail ? 1 : 0);
 }
 
 // a main split with no tiles (a sequence shorter than the split's range)

@@ -69,9 +69,10 @@ SplitPlan plan_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64
 }
 
 // ---- paged caches.  Lengths differ per sequence and live on the device, so
-// the splits are planned for the caller's bound max_len: every main split
-// covers a fixed count (chunk) of tiles / key blocks from the sequence start
-// and those past a shorter sequence's end write empty partials.
+// the splits are planned for the caller's bound max_len: split s covers
+// tiles (GQA) / key blocks (generic) [s * chunk, (s + 1) * chunk) of its
+// sequence, and the splits past a shorter sequence's end write empty
+// partials.
 PagedPlan plan_paged(const kvq_paged& c, int Hq, int n_splits, int max_len, Variant v) {
     const int64_t G = c.cfg.key.group;
     PagedPlan pp;
