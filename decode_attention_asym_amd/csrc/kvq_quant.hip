@@ -444,7 +444,9 @@ __global__ __launch_bounds__(256) void k_paged_keys(PagedKeyArgs a) {
 
 // Value rows into their pages, and the key rows of the block left unfilled
 // into the residual (rows t mod G).  Runs after k_paged_keys, which reads
-// the residual rows it replaces.
+// the residual rows it replaces.  Only the last G input rows of a sequence
+// can stay in the residual, so the copy threads cover (sequence, KV head,
+// one of those G rows, 8 channels).
 template <int BITS>
 __global__ __launch_bounds__(256) void k_paged_rows(ValueArgs va, PagedRows rows, const uint16_t* __restrict__ kin,
                                                     uint16_t* __restrict__ resid, int kd) {
@@ -455,13 +457,15 @@ __global__ __launch_bounds__(256) void k_paged_rows(ValueArgs va, PagedRows rows
         return;
     }
     const int vpr = kd / 8;
-    const int64_t i = idx - nv;
-    if (i >= int64_t(va.BH) * va.n_tok * vpr) return;
-    const int v = int(i % vpr);
-    const int64_t tok = (i / vpr) % va.n_tok, bh = i / vpr / va.n_tok;
     const int G = rows.G;
+    const int64_t i = idx - nv;
+    if (i >= int64_t(va.BH) * G * vpr) return;
+    const int v = int(i % vpr);
+    const int r = int((i / vpr) % G);
+    const int64_t bh = i / vpr / G;
     const int64_t n = rows.count(bh);
-    if (tok >= n) return;
+    const int64_t tok = n - G + r;   // the last G rows of this sequence's input
+    if (tok < 0) return;
     const int64_t pos = rows.ps.lens[bh / rows.Hkv], t = pos + tok;
     if (t < (pos + n) / G * G) return;   // in a block this append completed
     *reinterpret_cast<uint4*>(resid + (bh * G + t % G) * kd + v * 8) =
@@ -643,7 +647,7 @@ hipError_t launch_paged_t(const kvq_paged& c, const Geom& g, const void* k_in, c
     hipLaunchKernelGGL((k_paged_keys<G, KB>), dim3(grid_of(kthreads)), dim3(256), 0, st, ka);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t rthreads = value_threads(va.BH, n_max, g.vd) + int64_t(va.BH) * n_max * (g.kd / 8);
+    const int64_t rthreads = value_threads(va.BH, n_max, g.vd) + int64_t(va.BH) * G * (g.kd / 8);
     uint16_t* resid = static_cast<uint16_t*>(c.buf.k_resid);
     if (g.vbits == 2)
         hipLaunchKernelGGL(k_paged_rows<2>, dim3(grid_of(rthreads)), dim3(256), 0, st, va, rows, ka.kin, resid, g.kd);
