@@ -1,16 +1,17 @@
 """Benchmark: 2-bit decode attention over a KIVI-style cache on one MI355X.
 
 One step = one decode token for every sequence of the workload in one
-layer: append the new token (per-token value quantize, key into the residual,
-per-channel key quantize of the block when it fills) followed by split-K
-decode attention over the whole cache and the merge pass.  Steps rotate over
+layer (kv_decode_step): append the new token (per-token value quantize, key
+into the residual, per-channel key quantize of the block when it fills) and
+split-K decode attention over the whole cache with the merge pass; while the
+new key completes no block, the append runs inside the attention launch.  Steps rotate over
 several layers, each with its own cache, at least 1 GB in total, so that a
 cache smaller than the 256 MB Infinity Cache is still read from HBM.  Inputs
 are seeded synthetic fp16 tensors already resident in HBM.  Prints ONE JSON
 line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers L]
-                  [--no-cpu-baseline]
+                  [--no-cpu-baseline] [--paged] [--separate-calls]
 """
 from __future__ import annotations
 
@@ -70,6 +71,10 @@ def parse():
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--paged", action="store_true",
                     help="paged cache: ragged lengths in [T/2, T], blocks in shuffled pages")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="sequences per step (default: the workload's); names the workload ..._b<N>")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="step as kv_quantize_append + kv_decode_attention instead of kv_decode_step")
     return ap.parse_args()
 
 
@@ -181,6 +186,9 @@ def main():
         copy_probe()
         return
     w = configs.BY_NAME[args.workload]
+    if args.batch:
+        import dataclasses
+        w = dataclasses.replace(w, batch=args.batch, name=f"{w.name}_b{args.batch}")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.paged:
@@ -238,6 +246,7 @@ def main():
     # that host-side Python does not pace the small workloads
     lib = kvq.lib()
     c_append, c_decode, c_timing = lib.kv_quantize_append, lib.kv_decode_attention, lib.kv_set_timing_events
+    c_step = None if args.separate_calls else lib.kv_decode_step
     handles = [c.handle for c in dcs]
     kptr = [knew[j].data_ptr() for j in range(knew.shape[0])]
     vptr = [vnew[j].data_ptr() for j in range(vnew.shape[0])]
@@ -250,9 +259,13 @@ def main():
         if timed:
             st = c_timing(*evs[i - args.warmup])
             assert st == 0, st
-        st = c_append(h, kptr[i // L], vptr[i // L], n_new, 0, sptr)
-        assert st == 0, kvq.kvq_status_str(st)
-        st = c_decode(h, qptr, w.n_q_heads, w.sigma, args.splits, optr, wptr, wbytes, sptr)
+        if args.separate_calls:
+            st = c_append(h, kptr[i // L], vptr[i // L], n_new, 0, sptr)
+            assert st == 0, kvq.kvq_status_str(st)
+            st = c_decode(h, qptr, w.n_q_heads, w.sigma, args.splits, optr, wptr, wbytes, sptr)
+        else:
+            st = c_step(h, kptr[i // L], vptr[i // L], qptr, w.n_q_heads, w.sigma, args.splits, optr, wptr,
+                        wbytes, sptr)
         assert st == 0, kvq.kvq_status_str(st)
 
     for i in range(args.warmup):

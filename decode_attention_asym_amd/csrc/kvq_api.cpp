@@ -368,6 +368,58 @@ const char* kv_paged_variant(const kvq_paged* c, int32_t Hq, int32_t max_len) {
     return paged_variant_name(pick_paged_variant(*c, Hq, 0, max_len));
 }
 
+kvq_status kv_decode_step(kvq_cache* c, const void* k, const void* v, const void* q, int32_t Hq, float sigma,
+                          int32_t n_splits, void* out, void* ws, uint64_t ws_bytes, void* stream) {
+    // everything both halves would check, before any HIP call
+    if (!c || !k || !v || !q || !out || !ws) return KVQ_E_NULL;
+    if (Hq < 1 || Hq % c->cfg.n_kv_heads != 0) return KVQ_E_SHAPE;
+    if (n_splits < 0 || n_splits > KVQ_MAX_SPLITS) return KVQ_E_SHAPE;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(out) || !aligned16(ws)) return KVQ_E_ALIGN;
+    const Geom g = geom_of(c->cfg);
+    if (c->T + 1 > g.cap) return KVQ_E_CAPACITY;
+    const Variant v_ = pick_variant(*c, Hq);
+    const int64_t R = c->T - c->nblk * g.kG;
+    const int64_t T1 = c->T + 1;
+    // the block count after the append (auto-flush when the key fills it)
+    const int64_t nblk1 = c->nblk + (R + 1 >= g.kG ? 1 : 0);
+    const SplitPlan sp = plan_splits(*c, Hq, n_splits, T1, nblk1, v_);
+    const uint64_t need = uint64_t(g.B) * Hq * sp.S * (g.vd + 2) * 4;
+    if (ws_bytes < need) return KVQ_E_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((v_ == V_GQA || v_ == V_MHA) && R + 1 < g.kG) {
+        // no block completes: the tail workgroup of pass-1 appends the token
+        // and attends over it, so the step is pass-1 + merge
+        DecodeArgs a{};
+        a.c = c;
+        a.g = g;
+        a.q = q;
+        a.Hq = Hq;
+        a.sigma = sigma;
+        a.out = out;
+        a.T = T1;
+        a.nblk = c->nblk;
+        a.R = int(R + 1);
+        a.U = int(a.nblk + 1);
+        a.S = sp.S;
+        a.S_main = sp.S_main;
+        a.ntiles = sp.ntiles;
+        a.ws_acc = static_cast<float*>(ws);
+        a.ws_ml = a.ws_acc + uint64_t(g.B) * Hq * a.S * g.vd;
+        a.ev_start = g_ev_before;
+        a.ev_stop = g_ev_after;
+        a.k_new = k;
+        a.v_new = v;
+        a.fuse = 1;
+        const hipError_t e = v_ == V_GQA ? launch_decode_gqa(a, st) : launch_decode_mha(a, st);
+        if (e != hipSuccess) return KVQ_E_HIP;
+        c->T = T1;
+        return hip_status(launch_merge(a, st));
+    }
+    kvq_status r = kv_quantize_append(c, k, v, 1, 0, stream);
+    if (r != KVQ_OK) return r;
+    return kv_decode_attention(c, q, Hq, sigma, n_splits, out, ws, ws_bytes, stream);
+}
+
 kvq_status kv_set_timing_events(void* before, void* after) {
     if ((before == nullptr) != (after == nullptr)) return KVQ_E_NULL;
     g_ev_before = static_cast<hipEvent_t>(before);

@@ -187,10 +187,39 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ ws_acc,
     __syncthreads();
     const float inv = tot[1] > 0.0f ? 1.0f / tot[1] : 0.0f;
     const float* acc = ws_acc + pair * S * vd;
-    for (int c = tid; c < vd; c += 256) {
+    // P threads per channel (P = 256 / vd for vd <= 128) sum interleaved
+    // slots s = part, part + P, ..., 8 loads in flight per round; the parts
+    // add up in LDS (part order)
+    const int P = vd >= 256 ? 1 : 256 / vd;
+    const int cw = 256 / P;   // channels per pass
+    __shared__ float part_sum[256];
+    for (int c0 = 0; c0 < vd; c0 += cw) {
+        const int c = c0 + tid % cw, part = tid / cw;
         float o = 0.0f;
-        for (int s = 0; s < S; ++s) o = fmaf(acc[int64_t(s) * vd + c], wsh[s], o);
-        out[pair * vd + c] = __half_as_ushort(__float2half_rn(o * inv));
+        if (c < vd) {
+            for (int s0 = part; s0 < S; s0 += 8 * P) {
+                float a[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int sl = s0 + e * P;
+                    a[e] = sl < S ? acc[int64_t(sl) * vd + c] : 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int sl = s0 + e * P;
+                    if (sl < S) o = fmaf(a[e], wsh[sl], o);
+                }
+            }
+        }
+        if (P > 1) {
+            __syncthreads();
+            part_sum[tid] = o;
+            __syncthreads();
+            if (part == 0 && c < vd) {
+                for (int q = 1; q < P; ++q) o += part_sum[q * cw + tid];
+            }
+        }
+        if (part == 0 && c < vd) out[pair * vd + c] = __half_as_ushort(__float2half_rn(o * inv));
     }
 }
 

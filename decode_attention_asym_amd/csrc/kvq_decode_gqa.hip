@@ -342,9 +342,8 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
         if (tail) {
             const int len = seq_len(p, b);
             const int64_t nblk = len / G;
-            if (wave == 0)
-                tail_split<HG>(p, PagedBlocks{}, b, kvh, s, reinterpret_cast<float*>(L.k.qa),
-                               reinterpret_cast<float*>(L.v.pa), len, nblk, int(nblk * G / 64));
+            tail_split<HG>(p, PagedBlocks{}, b, kvh, s, reinterpret_cast<float*>(L.k.qa),
+                           reinterpret_cast<float*>(L.v.pa), len, nblk, int(nblk * G / 64));
             return;
         }
         t_lo = s * p.chunk;
@@ -358,7 +357,7 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
         prun.t_last = t_hi - 1;
     } else {
         if (tail) {
-            if (wave == 0) tail_split<HG>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
+            tail_split<HG>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
             return;
         }
         t_lo = int(int64_t(s) * p.ntiles / p.S_main);

@@ -244,7 +244,7 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int64_t slot = (int64_t(b) * p.Hq + kvh) * p.S + s;
     if (tail) {
-        if (wave == 0) tail_split<1>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
+        tail_split<1>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
         return;
     }
     const int t_lo = int(int64_t(s) * p.ntiles / p.S_main);

@@ -104,6 +104,11 @@ struct DecodeArgs {
     PagedSeq ps;
     int chunk;
     int max_len;
+    // decode step with its append fused in (GQA / MHA kernels): T counts
+    // the new token, whose key and value rows ([B][Hkv][1][D]) the tail
+    // workgroup stores before attending
+    const void *k_new, *v_new;
+    int fuse;
 };
 
 Variant pick_variant(const kvq_cache& c, int Hq);

@@ -14,6 +14,7 @@
 #include <math.h>
 
 #include "kvq_internal.h"
+#include "kvq_quant_dev.h"
 
 namespace kvq {
 namespace {
@@ -60,6 +61,11 @@ struct MfmaParams {
     // [0, max_len]), pool size, tiles per main split
     const int32_t *table, *lens;
     int maxb, npages, chunk, max_len;
+    // fused append of token T - 1 (see fused_append)
+    const uint16_t *k_new, *v_new;
+    uint32_t* vc_w;
+    uint16_t *vs_w, *vz_w, *kr_w;
+    int fuse;
 };
 
 inline MfmaParams mfma_params(const DecodeArgs& a) {
@@ -93,6 +99,13 @@ inline MfmaParams mfma_params(const DecodeArgs& a) {
     p.npages = a.ps.n_pages;
     p.chunk = a.chunk;
     p.max_len = a.max_len;
+    p.k_new = static_cast<const uint16_t*>(a.k_new);
+    p.v_new = static_cast<const uint16_t*>(a.v_new);
+    p.vc_w = static_cast<uint32_t*>(buf.v_codes);
+    p.vs_w = static_cast<uint16_t*>(buf.v_scale);
+    p.vz_w = static_cast<uint16_t*>(buf.v_zero);
+    p.kr_w = static_cast<uint16_t*>(buf.k_resid);
+    p.fuse = a.fuse;
     return p;
 }
 
@@ -502,122 +515,190 @@ __device__ __forceinline__ f16x8 code_slice(const CodeRegs& c, uint32_t mk) {
 // lane for the values.  Runs on one wave; qf holds HG*D floats, pl HG*PSTR.
 
 // tokens [ntiles * 64, T) of sequence b, nblk of its key blocks quantized
-// (an empty range writes an empty partial: m = -inf, l = 0, acc = 0).  The
-// tail spans at most two key blocks, whose rows are looked up once; keys
-// and values are read 8 channels / 8 tokens at a time, all loads of a group
-// before its arithmetic (one wave: the latency of dependent round trips is
-// what bounds it), with the accumulation order of a plain loop.
+// (an empty range writes an empty partial: m = -inf, l = 0, acc = 0).  Run
+// by both waves of the workgroup; it is a chain of dependent round trips
+// that a launch can end on, so every phase issues all of its loads before
+// using any:
+//  - wave 0, lane j = token j: the query (one 16-byte load per lane) and
+//    the token's whole fp16 residual key row (16 loads), or for a quantized
+//    token (G = 32 only) its codes and side values 16 channels at a time;
+//    logits in channel order, softmax, weights to LDS;
+//  - both waves, lane = channel (wave w: channels 64w ..): values 16
+//    tokens at a time, accumulated in token order.
+// The tail spans at most two key blocks, whose rows are looked up once.
 template <int HG, class Blocks>
 __device__ void tail_split(const MfmaParams& p, const Blocks& blocks, int b, int kvh, int s, float* qf, float* pl,
                            int64_t T, int64_t nblk, int ntiles) {
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int hq0 = kvh * HG;
-    for (int i = lane; i < HG * D; i += 64) qf[i] = h2f(p.q[(int64_t(b) * p.Hq + hq0) * D + i]);
     const int64_t t0 = int64_t(ntiles) * 64;
     const int n_tail = int(T - t0);
     const int64_t Tq = nblk * p.G;
     const int64_t jb = t0 / p.G;   // first key block of the tail
     const int64_t row0 = n_tail > 0 ? blocks(p, b, kvh, jb) : 0;
     const int64_t row1 = n_tail > 0 && (T - 1) / p.G > jb ? blocks(p, b, kvh, jb + 1) : row0;
-    wave_sync();
-    const int64_t t = t0 + lane;
-    const bool valid = lane < n_tail;
-    float sc[HG];
-#pragma unroll
-    for (int h = 0; h < HG; ++h) sc[h] = 0.0f;
-    if (valid) {
-        // a residual key row, or token i of quantized block jb (G = 32 only)
+    float m[HG], l[HG];
+    if (wave == 0) {
+        // the query: HG * D fp16, 8 per lane
+        uint4 qv = make_uint4(0u, 0u, 0u, 0u);
+        if (lane < HG * D / 8) qv = *reinterpret_cast<const uint4*>(p.q + (int64_t(b) * p.Hq + hq0) * D + 8 * lane);
+        const int64_t t = t0 + lane;
+        const bool valid = lane < n_tail;
         const bool resid = t >= Tq;
-        const uint16_t* krow = p.kr + ((int64_t(b) * p.Hkv + kvh) * p.G + (resid ? t - Tq : 0)) * D;
-        const int i = int(t - jb * p.G);
-        for (int c0 = 0; c0 < D; c0 += 8) {
-            float kh[8];
-            if (resid) {
-                const uint4 r = *reinterpret_cast<const uint4*>(krow + c0);
-                const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+        // a residual key row: all 16 loads at once
+        uint4 kr[16];
+        const uint16_t* krow = p.kr + ((int64_t(b) * p.Hkv + kvh) * p.G + (valid && resid ? t - Tq : 0)) * D;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kh[2 * e] = lo_h(w[e]);
-                    kh[2 * e + 1] = hi_h(w[e]);
-                }
-            } else {
-                const int64_t side = row0 * D + c0;
-                const uint4 sv = *reinterpret_cast<const uint4*>(p.ks + side);
-                const uint4 zv = *reinterpret_cast<const uint4*>(p.kz + side);
-                uint32_t wd[8];
+        for (int i = 0; i < 16; ++i)
+            kr[i] = valid && resid ? *reinterpret_cast<const uint4*>(krow + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+        if (lane < HG * D / 8) {
+            const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) wd[e] = p.kc[(side + e) * (p.G / 16) + i / 16];
-                const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w}, zw[4] = {zv.x, zv.y, zv.z, zv.w};
+            for (int e = 0; e < 4; ++e) {
+                qf[8 * lane + 2 * e] = lo_h(w[e]);
+                qf[8 * lane + 2 * e + 1] = hi_h(w[e]);
+            }
+        }
+        wave_sync();
+        float sc[HG];
+#pragma unroll
+        for (int h = 0; h < HG; ++h) sc[h] = 0.0f;
+        if (valid && resid) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float sc_e = (e & 1) ? hi_h(sw[e >> 1]) : lo_h(sw[e >> 1]);
-                    const float z_e = (e & 1) ? hi_h(zw[e >> 1]) : lo_h(zw[e >> 1]);
-                    kh[e] = fmaf(float((wd[e] >> (2 * (i & 15))) & 3u), sc_e, z_e);
+                    const float kh = (e & 1) ? hi_h(w[e >> 1]) : lo_h(w[e >> 1]);
+#pragma unroll
+                    for (int h = 0; h < HG; ++h) sc[h] = fmaf(qf[h * D + 8 * i + e], kh, sc[h]);
                 }
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-#pragma unroll
-                for (int h = 0; h < HG; ++h) sc[h] = fmaf(qf[h * D + c0 + e], kh[e], sc[h]);
         }
-    }
-    float m[HG], l[HG];
+        // (a separate pass, so that the residual row's registers are free)
+        if (valid && !resid) {
+            // token i of quantized block jb
+            const int i = int(t - jb * p.G);
+            for (int c0 = 0; c0 < D; c0 += 16) {
+                const int64_t side = row0 * D + c0;
+                uint32_t wd[16];
 #pragma unroll
-    for (int h = 0; h < HG; ++h) {
-        float x = valid ? sc[h] * p.sigma2 : -INFINITY;
-        float mx = x;
-        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        const float pv = valid ? exp2f(x - mx) : 0.0f;
-        float sum = pv;
-        for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-        m[h] = mx;
-        l[h] = sum;
-        pl[h * PSTR + lane] = pv;
-    }
-    wave_sync();
+                for (int e = 0; e < 16; ++e) wd[e] = p.kc[(side + e) * (p.G / 16) + i / 16];
+                uint32_t sw[8], zw[8];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int c = lane + 64 * half;
-        float acc[HG];
+                for (int e = 0; e < 2; ++e) {
+                    const uint4 sv = *reinterpret_cast<const uint4*>(p.ks + side + 8 * e);
+                    const uint4 zv = *reinterpret_cast<const uint4*>(p.kz + side + 8 * e);
+                    sw[4 * e] = sv.x; sw[4 * e + 1] = sv.y; sw[4 * e + 2] = sv.z; sw[4 * e + 3] = sv.w;
+                    zw[4 * e] = zv.x; zw[4 * e + 1] = zv.y; zw[4 * e + 2] = zv.z; zw[4 * e + 3] = zv.w;
+                }
 #pragma unroll
-        for (int h = 0; h < HG; ++h) acc[h] = 0.0f;
-        for (int j0 = 0; j0 < n_tail; j0 += 8) {
-            float vh[8];
+                for (int e = 0; e < 16; ++e) {
+                    const float se = (e & 1) ? hi_h(sw[e >> 1]) : lo_h(sw[e >> 1]);
+                    const float ze = (e & 1) ? hi_h(zw[e >> 1]) : lo_h(zw[e >> 1]);
+                    const float kh = fmaf(float((wd[e] >> (2 * (i & 15))) & 3u), se, ze);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                // past the tail: reload its last token (in bounds, unused)
-                const int64_t tt = t0 + (j0 + e < n_tail ? j0 + e : n_tail - 1);
-                const int64_t blk = tt / p.G;
-                const int64_t row = (blk == jb ? row0 : row1) * p.G + (tt - blk * p.G);
-                const uint32_t w = p.vc[row * 8 + c / 16];
-                const int64_t side = row * 4 + c / 32;
-                vh[e] = fmaf(float((w >> (2 * (c & 15))) & 3u), h2f(p.vs[side]), h2f(p.vz[side]));
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (j0 + e < n_tail) {
-#pragma unroll
-                    for (int h = 0; h < HG; ++h) acc[h] = fmaf(pl[h * PSTR + j0 + e], vh[e], acc[h]);
+                    for (int h = 0; h < HG; ++h) sc[h] = fmaf(qf[h * D + c0 + e], kh, sc[h]);
                 }
             }
         }
 #pragma unroll
-        for (int h = 0; h < HG; ++h)
-            p.ws_acc[((int64_t(b) * p.Hq + hq0 + h) * p.S + s) * D + c] = acc[h];
-    }
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-        if (lane == h) {
-            const int64_t slot = (int64_t(b) * p.Hq + hq0 + h) * p.S + s;
-            p.ws_ml[slot * 2] = m[h];
-            p.ws_ml[slot * 2 + 1] = l[h];
+        for (int h = 0; h < HG; ++h) {
+            float x = valid ? sc[h] * p.sigma2 : -INFINITY;
+            float mx = x;
+            for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            const float pv = valid ? exp2f(x - mx) : 0.0f;
+            float sum = pv;
+            for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+            m[h] = mx;
+            l[h] = sum;
+            pl[h * PSTR + lane] = pv;
         }
     }
+    __syncthreads();
+    // PV: this lane's channel, 16 tokens per round of loads
+    const int c = 64 * wave + lane;
+    float acc[HG];
+#pragma unroll
+    for (int h = 0; h < HG; ++h) acc[h] = 0.0f;
+    for (int j0 = 0; j0 < n_tail; j0 += 16) {
+        uint32_t w[16];
+        uint16_t sv[16], zv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            // past the tail: reload its last token (in bounds, unused).  The
+            // tail starts on a block boundary (t0 = jb * G), so token j of it
+            // is in block jb + (j >= G)
+            const int j = j0 + e < n_tail ? j0 + e : n_tail - 1;
+            const int64_t row = j < p.G ? row0 * p.G + j : row1 * p.G + (j - p.G);
+            w[e] = p.vc[row * 8 + c / 16];
+            sv[e] = p.vs[row * 4 + c / 32];
+            zv[e] = p.vz[row * 4 + c / 32];
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            if (j0 + e < n_tail) {
+                const float vh = fmaf(float((w[e] >> (2 * (c & 15))) & 3u), h2f(sv[e]), h2f(zv[e]));
+#pragma unroll
+                for (int h = 0; h < HG; ++h) acc[h] = fmaf(pl[h * PSTR + j0 + e], vh, acc[h]);
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < HG; ++h) p.ws_acc[((int64_t(b) * p.Hq + hq0 + h) * p.S + s) * D + c] = acc[h];
+    if (wave == 0) {
+#pragma unroll
+        for (int h = 0; h < HG; ++h) {
+            if (lane == h) {
+                const int64_t slot = (int64_t(b) * p.Hq + hq0 + h) * p.S + s;
+                p.ws_ml[slot * 2] = m[h];
+                p.ws_ml[slot * 2 + 1] = l[h];
+            }
+        }
+    }
+}
+
+// The decode step's append, done by the tail workgroup (both waves call
+// it; wave 0's lanes do the work) before it attends: the new token T - 1 completes no key block, so its key is
+// residual row T - 1 - nblk * G and its value row is quantized by the same
+// device code as the append kernels (bit-identical).  No other workgroup
+// reads these rows: the main splits end at the last whole tile, and the
+// tail covers everything after it.
+__device__ void fused_append(const MfmaParams& p, int b, int kvh, int lane) {
+    const int64_t bh = int64_t(b) * p.Hkv + kvh;
+    const int64_t t = p.T - 1;
+    constexpr int TPR = D / 8;   // threads per row: 8 channels each
+    if (threadIdx.x >= 64) {
+        // wave 1 only waits for wave 0's stores
+    } else if (lane < TPR) {
+        // one value row: whole 4-lane groups (lanes 0 .. 15)
+        qdev::ValueArgs va;
+        va.vin = p.v_new;
+        va.n_in = 1;
+        va.row0 = 0;
+        va.n_tok = 1;
+        va.vd = D;
+        va.BH = 0;   // unused by the row routine
+        va.codes = p.vc_w;
+        va.scale = p.vs_w;
+        va.zero = p.vz_w;
+        const qdev::ContigRows rows{p.cap, t, 1};
+        qdev::quant_values_thread<2>(va, rows, bh * TPR + lane);
+    } else if (lane < 2 * TPR) {
+        const int v = lane - TPR;
+        const int64_t r = t - p.nblk * p.G;
+        *reinterpret_cast<uint4*>(p.kr_w + (bh * p.G + r) * D + v * 8) =
+            *reinterpret_cast<const uint4*>(p.k_new + bh * D + v * 8);
+    }
+    // the stores complete before either wave reads these rows back
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __syncthreads();
 }
 
 // the contiguous cache's tail: its counters are in the parameters
 template <int HG>
 __device__ void tail_split(const MfmaParams& p, int b, int kvh, int s, float* qf, float* pl) {
+    if (p.fuse) fused_append(p, b, kvh, threadIdx.x & 63);
     tail_split<HG>(p, ContigBlocks{}, b, kvh, s, qf, pl, p.T, p.nblk, p.ntiles);
 }
 

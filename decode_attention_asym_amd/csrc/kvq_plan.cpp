@@ -25,8 +25,12 @@ namespace {
 int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // Automatic split count: enough workgroups to fill 256 CUs several times
-// over.  It does not depend on T, so the slot bound below covers every T.
-int64_t auto_main(const kvq_cache& c, int Hq, Variant v) {
+// over, but (matrix-core kernels) no shorter runs than 16 tiles (GQA) / 8
+// tiles (MHA): at small batch more splits cost more in per-split start-up
+// and in the merge than they gain (measured on MI355X, 32K-token GQA at one
+// sequence: 255 splits 36 us per step, 32 splits 27 us).  Non-decreasing in
+// ntiles, so the slot bound at full capacity covers every length.
+int64_t auto_main(const kvq_cache& c, int Hq, Variant v, int64_t ntiles) {
     // MLA: one four-wave workgroup per CU, Hq / 64 of them per sequence and split
     if (v == V_MLA) return clamp64((256 * 64 / Hq + c.cfg.batch - 1) / c.cfg.batch, 1, KVQ_MAX_SPLITS);
     const bool tiled = v == V_GQA || v == V_MHA;
@@ -34,7 +38,12 @@ int64_t auto_main(const kvq_cache& c, int Hq, Variant v) {
     // measured on MI355X: about 12 tiles per two-wave workgroup suit the MHA
     // kernel (64 tiles per sequence at 4K tokens), 6 waves per SIMD the GQA one
     const int64_t target = v == V_MHA ? 1536 : tiled ? 3072 : 2048;
-    return clamp64((target + units - 1) / units, 1, KVQ_MAX_SPLITS);
+    int64_t want = (target + units - 1) / units;
+    if (tiled) {
+        const int64_t min_run = v == V_MHA ? 8 : 16;
+        want = want < (ntiles + min_run - 1) / min_run ? want : (ntiles + min_run - 1) / min_run;
+    }
+    return clamp64(want, 1, KVQ_MAX_SPLITS);
 }
 
 }  // namespace
@@ -42,7 +51,7 @@ int64_t auto_main(const kvq_cache& c, int Hq, Variant v) {
 SplitPlan plan_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64_t nblk, Variant v) {
     SplitPlan sp;
     const int64_t G = c.cfg.key.group;
-    const int64_t want = n_splits > 0 ? n_splits : auto_main(c, Hq, v);
+    const int64_t want = n_splits > 0 ? n_splits : auto_main(c, Hq, v, nblk * G / 64);
     if (v == V_GQA || v == V_MHA) {
         // whole 64-token tiles of quantized keys, then a tail slot for the rest
         const int64_t ntiles = nblk * G / 64;
@@ -79,7 +88,9 @@ PagedPlan plan_paged(const kvq_paged& c, int Hq, int n_splits, int max_len, Vari
     if (v == V_GQA) {
         const int64_t ntiles = int64_t(max_len) / G * G / 64;
         const int64_t units = int64_t(c.cfg.batch) * c.cfg.n_kv_heads;
-        const int64_t want = n_splits > 0 ? n_splits : clamp64((3072 + units - 1) / units, 1, KVQ_MAX_SPLITS - 1);
+        // as for a contiguous cache: fill the GPU, runs of at least 16 tiles
+        const int64_t fill = (3072 + units - 1) / units, runs = (ntiles + 15) / 16;
+        const int64_t want = n_splits > 0 ? n_splits : clamp64(fill < runs ? fill : runs, 1, KVQ_MAX_SPLITS - 1);
         int64_t chunk = ntiles > 0 ? (ntiles + want - 1) / want : 1;
         // the page numbers of a run sit one per lane: at most 64 key blocks
         chunk = clamp64(chunk, 1, G);
@@ -109,7 +120,7 @@ Variant pick_paged_variant(const kvq_paged& c, int Hq, int n_splits, int max_len
 const char* paged_variant_name(Variant v) { return v == V_GQA ? "gqa_mfma_paged" : "generic_paged"; }
 
 int max_slots(const kvq_cache& c, int Hq, int n_splits, Variant v) {
-    const int64_t want = n_splits > 0 ? n_splits : auto_main(c, Hq, v);
+    const int64_t want = n_splits > 0 ? n_splits : auto_main(c, Hq, v, c.cfg.max_tokens / 64);
     if (v == V_GQA || v == V_MHA) return int(clamp64(want, 1, KVQ_MAX_SPLITS - 1) + 1);
     return int(want);
 }

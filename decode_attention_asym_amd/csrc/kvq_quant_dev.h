@@ -1,0 +1,219 @@
+// kvq_quant_dev.h -- the per-token value quantizer as device code, shared
+// by the quantize kernels (kvq_quant.hip) and the decode kernels that append
+// a token inside their tail workgroup (kvq_mfma_tiles.h), so that both write
+// the same bits.  Also the destination-row policies of the contiguous and
+// paged layouts.
+//
+// "Makale Bülteni -- KIVI", section "İddia ve Gerçeklik: KIVI": values are
+// quantized per token, as asymmetric low-bit codes (zero = group minimum,
+// scale = range / (2^bits - 1)).
+//
+// Exactness: codes must equal round_half_even(fl32(fl32(x - mn) / scale))
+// with an IEEE binary32 division.  A correctly rounded division costs ~10
+// VALU instructions, so each code is first taken from q = fl32(x - mn) *
+// rcp(scale) (v_rcp_f32, <= 1 ulp).  |q - fl32(true quotient)| <= 6.6e-7 for
+// quotients <= 2^bits - 1, so whenever q lies more than 2^-19 from a
+// half-integer both round to the same integer; a code closer than that to a
+// tie takes the IEEE division (a branch per code: on fp16 data about 1 code
+// in 10^4 does, so a wave almost never executes the division).
+// No clamp is needed: 0 <= fl32(x - mn) <= fl32(max - mn), so both quotients
+// round into [0, 2^bits - 1].  Floating-point contraction is off in every
+// function here (the including file's setting does not matter).
+#pragma once
+
+#include <hip/hip_fp16.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+namespace qdev {
+
+constexpr float kTieBand = 0.5f - 0x1p-19f;
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
+
+// The fp16 inputs are read exactly once: non-temporal loads keep them from
+// displacing other lines (measured: +4..5% on the bulk quantize; the same
+// hint on the code stores made it slower).
+typedef unsigned int qu4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_once4(const uint16_t* p) {
+    const qu4 v = __builtin_nontemporal_load(reinterpret_cast<const qu4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_once1(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+// fl32(x - mn) for the fp16 half HALF of w, in one instruction: v_fma_mix
+// converts the fp16 operand exactly and rounds x * 1 + (-mn) once
+template <int HALF>
+__device__ __forceinline__ float sub_half(uint32_t w, float neg_mn) {
+    float d;
+    if (HALF == 0)
+        asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(neg_mn));
+    else
+        asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(neg_mn));
+    return d;
+}
+
+struct GroupQ {
+    float mn, scale, rcp;
+};
+
+__device__ __forceinline__ GroupQ make_group(float mn, float mx, float L) {
+#pragma clang fp contract(off)
+    GroupQ q;
+    q.mn = mn;
+    q.scale = (mx - mn) / L;   // IEEE division (HIP default: correctly rounded)
+    q.rcp = q.scale == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(q.scale);
+    return q;
+}
+
+// code of d = fl32(x - mn): round-half-even of d * rcp, or of the IEEE
+// quotient d / scale when the product lies within the tie band (scale == 0
+// gives rcp == 0, product 0, never in the band)
+__device__ __forceinline__ uint32_t code_of(float d, const GroupQ& q) {
+#pragma clang fp contract(off)
+    const float qa = d * q.rcp;
+    float k = __builtin_rintf(qa);
+    if (__builtin_fabsf(qa - k) > kTieBand) k = __builtin_rintf(d / q.scale);
+    return static_cast<uint32_t>(k);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
+    return __half2float(__ushort_as_half(static_cast<unsigned short>(h16)));
+}
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+    return __half_as_ushort(__float2half_rn(f));
+}
+
+// ------------------------------------------------------------------ values
+// One thread = 8 consecutive channels (one 16-byte load) of VT consecutive
+// tokens, all loads issued first; four neighbouring lanes form a 32-channel
+// group and reduce min/max by shuffles.
+constexpr int VT = 4;
+
+struct ValueArgs {
+    const uint16_t* vin;   // [BH][n_in][vd]
+    int64_t n_in, row0, n_tok;
+    int vd, BH;
+    uint32_t* codes;
+    uint16_t *scale, *zero;
+};
+
+// Destination rows of the value stream.  Contiguous cache: token t of
+// (b, kvh) is row bh * cap + t.
+struct ContigRows {
+    int64_t cap, t_dst0, n_tok;
+    __device__ int64_t count(int64_t) const { return n_tok; }
+    __device__ int64_t row(int64_t bh, int64_t tok) const { return bh * cap + t_dst0 + tok; }
+};
+
+// Paged cache: rows appended to sequence b (0 when its length, row count or
+// capacity is out of range, so nothing is written for it)
+__device__ __forceinline__ int seq_rows(const PagedSeq& ps, int b, int n_max, int G) {
+    const int pos = ps.lens[b];
+    const int n = ps.n_new ? ps.n_new[b] : n_max;
+    if (pos < 0 || n < 0 || n > n_max || int64_t(pos) + n > int64_t(ps.maxb) * G) return 0;
+    return n;
+}
+// block row page * Hkv + kvh of block j of sequence b, or -1 when the table
+// names a page outside the pool
+__device__ __forceinline__ int64_t paged_block_row(const PagedSeq& ps, int b, int kvh, int Hkv, int64_t j) {
+    const int pg = ps.table[int64_t(b) * ps.maxb + j];
+    return (pg < 0 || pg >= ps.n_pages) ? -1 : int64_t(pg) * Hkv + kvh;
+}
+// value row of token t: block row * G + t mod G
+struct PagedRows {
+    PagedSeq ps;
+    int Hkv, G, n_max;
+    __device__ int64_t count(int64_t bh) const { return seq_rows(ps, int(bh / Hkv), n_max, G); }
+    __device__ int64_t row(int64_t bh, int64_t tok) const {
+        const int b = int(bh / Hkv), kvh = int(bh % Hkv);
+        const int64_t t = ps.lens[b] + tok;
+        const int64_t r = paged_block_row(ps, b, kvh, Hkv, t / G);
+        return r < 0 ? -1 : r * G + t % G;
+    }
+};
+
+// threads that quantize n_tok value rows: BH * ceil(n_tok / VT) * (vd / 8),
+// a multiple of 4 (vd / 8 is)
+__host__ __device__ inline int64_t value_threads(int BH, int64_t n_tok, int vd) { return int64_t(BH) * ((n_tok + VT - 1) / VT) * (vd / 8); }
+
+// Thread idx < value_threads(...) quantizes 8 channels of up to VT rows;
+// the 4 threads of a 32-channel group are adjacent lanes and exchange their
+// min / max by shuffles, so callers keep whole 4-lane groups together.
+// Rows tok < rows.count(bh) are quantized into rows.row(bh, tok) (skipped
+// when that is negative).
+template <int BITS, class Rows>
+__device__ __forceinline__ void quant_values_thread(const ValueArgs& a, const Rows& rows, int64_t idx) {
+#pragma clang fp contract(off)
+    const uint16_t* __restrict__ vin = a.vin;
+    const int64_t n_in = a.n_in, row0 = a.row0;
+    const int vd = a.vd;
+    uint32_t* __restrict__ codes = a.codes;
+    uint16_t* __restrict__ scale = a.scale;
+    uint16_t* __restrict__ zero = a.zero;
+    constexpr float L = float((1 << BITS) - 1);
+    const int tpt = vd / 8;
+    const int64_t nq = (a.n_tok + VT - 1) / VT;
+    const int sub = int(idx % tpt);
+    const int64_t tq = (idx / tpt) % nq;
+    const int64_t bh = idx / tpt / nq;
+    const int64_t cnt = rows.count(bh);
+
+    uint4 raw[VT];
+#pragma unroll
+    for (int j = 0; j < VT; ++j) {
+        const int64_t tok = tq * VT + j;
+        raw[j] = tok < cnt ? ld_once4(vin + ((bh * n_in) + row0 + tok) * vd + sub * 8)
+                           : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int vWT = vd * BITS / 32;
+#pragma unroll
+    for (int j = 0; j < VT; ++j) {
+        const int64_t tok = tq * VT + j;
+        const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+        // min / max of the 8 values (packed fp16, exact; -0 is canonicalised after)
+        f16x2 mn2 = __builtin_elementwise_min(__builtin_elementwise_min(as_h2(w[0]), as_h2(w[1])),
+                                              __builtin_elementwise_min(as_h2(w[2]), as_h2(w[3])));
+        f16x2 mx2 = __builtin_elementwise_max(__builtin_elementwise_max(as_h2(w[0]), as_h2(w[1])),
+                                              __builtin_elementwise_max(as_h2(w[2]), as_h2(w[3])));
+        float mn = __builtin_fminf(float(mn2[0]), float(mn2[1]));
+        float mx = __builtin_fmaxf(float(mx2[0]), float(mx2[1]));
+        mn = __builtin_fminf(mn, __shfl_xor(mn, 1));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1));
+        mn = __builtin_fminf(mn, __shfl_xor(mn, 2));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 2));
+        const GroupQ q = make_group(mn + 0.0f, mx + 0.0f, L);
+
+        uint32_t packed = 0;
+        const float nmn = -q.mn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            packed |= code_of(sub_half<0>(w[i], nmn), q) << (BITS * (2 * i));
+            packed |= code_of(sub_half<1>(w[i], nmn), q) << (BITS * (2 * i + 1));
+        }
+        // the same for the 4 lanes of a group (same bh, same token)
+        const int64_t row = tok < cnt ? rows.row(bh, tok) : -1;
+        const bool valid = row >= 0;
+        if (BITS == 2) {
+            const uint32_t other = __shfl_xor(packed, 1);
+            if (valid && (sub & 1) == 0) codes[row * vWT + (sub >> 1)] = packed | (other << 16);
+        } else if (valid) {
+            codes[row * vWT + sub] = packed;
+        }
+        if (valid && (sub & 3) == 0) {
+            const int64_t side = row * (vd / 32) + (sub >> 2);
+            scale[side] = float_to_half_bits(q.scale);
+            zero[side] = float_to_half_bits(q.mn);
+        }
+    }
+}
+
+}  // namespace qdev
+}  // namespace
+}  // namespace kvq

@@ -27,7 +27,7 @@ EXPORTS = ["kv_cache_buffer_bytes", "kv_cache_init", "kv_cache_destroy", "kv_cac
            "kv_decode_workspace_bytes", "kv_decode_attention", "kv_set_timing_events",
            "kv_decode_variant", "kvq_status_str",
            "kv_paged_buffer_bytes", "kv_paged_init", "kv_paged_destroy", "kv_paged_append",
-           "kv_paged_workspace_bytes", "kv_paged_decode", "kv_paged_variant"]
+           "kv_paged_workspace_bytes", "kv_paged_decode", "kv_paged_variant", "kv_decode_step"]
 
 
 class KvqError(RuntimeError):
@@ -88,9 +88,17 @@ def lib():
             "kv_paged_workspace_bytes": (C.c_int, [p, i32, i32, i32, C.POINTER(u64)]),
             "kv_paged_decode": (C.c_int, [p, p, i32, C.c_float, p, p, i32, i32, p, p, u64, p]),
             "kv_paged_variant": (C.c_char_p, [p, i32, i32]),
+            "kv_decode_step": (C.c_int, [p, p, p, p, i32, C.c_float, i32, p, p, u64, p]),
         }
         for name, (res, args) in sig.items():
-            f = getattr(L, name)
+            try:
+                f = getattr(L, name)
+            except AttributeError:
+                # only an override build (KVQ_LIB, e.g. an older revision)
+                # may lack an entry point; calling it then fails
+                if not os.environ.get("KVQ_LIB"):
+                    raise
+                continue
             f.restype, f.argtypes = res, args
         _lib = L
     return _lib
@@ -155,6 +163,12 @@ def kv_decode_attention(handle, q_ptr, n_q_heads: int, softmax_scale: float, n_s
                         out_ptr, ws_ptr, ws_bytes: int, stream=None) -> None:
     _check(lib().kv_decode_attention(handle, q_ptr, n_q_heads, C.c_float(softmax_scale), n_splits,
                                      out_ptr, ws_ptr, ws_bytes, stream), "kv_decode_attention")
+
+
+def kv_decode_step(handle, k_ptr, v_ptr, q_ptr, n_q_heads: int, softmax_scale: float, n_splits: int,
+                   out_ptr, ws_ptr, ws_bytes: int, stream=None) -> None:
+    _check(lib().kv_decode_step(handle, k_ptr, v_ptr, q_ptr, n_q_heads, C.c_float(softmax_scale), n_splits,
+                                out_ptr, ws_ptr, ws_bytes, stream), "kv_decode_step")
 
 
 def kv_set_timing_events(ev_before, ev_after) -> None:
@@ -277,6 +291,18 @@ class DeviceCache:
 
     def variant(self, n_q_heads: int) -> str:
         return kv_decode_variant(self.handle, n_q_heads)
+
+    def step(self, k, v, q, softmax_scale: float, n_splits: int = 0, out=None, ws=None):
+        """Append one token per sequence (k, v: [B][Hkv][1][d]) and attend (kv_decode_step)."""
+        torch = self.torch
+        B, Hq = q.shape[0], q.shape[1]
+        if out is None:
+            out = torch.empty((B, Hq, self.cfg.value.dim), dtype=torch.float16, device=self.device)
+        if ws is None:
+            ws = self.workspace(Hq, n_splits)
+        kv_decode_step(self.handle, k.data_ptr(), v.data_ptr(), q.data_ptr(), Hq, softmax_scale, n_splits,
+                       out.data_ptr(), ws.data_ptr(), ws.numel(), self.stream())
+        return out
 
     # typed views of the device arrays in the documented layouts
     def views(self):

@@ -255,8 +255,26 @@ kvq_status kv_paged_decode(const kvq_paged* cache, const void* q_fp16, int32_t n
 /* Name of the kernel kv_paged_decode would launch (automatic splits). */
 const char* kv_paged_variant(const kvq_paged* cache, int32_t n_q_heads, int32_t max_len);
 
+/* One decode step: kv_quantize_append of one token per sequence (k_fp16 /
+ * v_fp16 [B][Hkv][1][d], auto-flush) followed by kv_decode_attention, with
+ * the same results bit for bit.  When the new key completes no block (G - 1
+ * steps in G) and the cache runs the GQA or MHA matrix-core kernel, the
+ * append happens inside the attention launch: the workgroup that handles
+ * the tokens after the last whole tile stores the new key and value rows
+ * (the same value quantizer as the append kernels) and then attends over
+ * them, so the step is two launches (attention, merge) instead of three.
+ * Otherwise it is the two calls.  ("İddia ve Gerçeklik: KIVI" puts the
+ * residual append and the in-loop dequantized attention on the decode
+ * path; the source names per-step latency at small batch as KIVI's cost.)
+ * Every argument of both halves, the workspace size for the grown cache
+ * included, is checked before any HIP call.
+ * Errors: those of kv_quantize_append and kv_decode_attention. */
+kvq_status kv_decode_step(kvq_cache* cache, const void* k_fp16, const void* v_fp16, const void* q_fp16,
+                          int32_t n_q_heads, float softmax_scale, int32_t n_splits, void* out_fp16,
+                          void* workspace, uint64_t workspace_bytes, void* hip_stream);
+
 /* Profiling hook: when both are non-NULL (hipEvent_t, created by the caller),
- * later kv_decode_attention / kv_paged_decode calls launch their split-K pass-1 kernel with
+ * later kv_decode_attention / kv_decode_step / kv_paged_decode calls launch their split-K pass-1 kernel with
  * hipExtLaunchKernel so that the launch itself records its start and stop
  * timestamps into ev_before / ev_after (no separate event packets in the
  * stream).  NULL, NULL switches it off.  Process-wide. */

@@ -289,3 +289,29 @@ def test_paged_variant_choice():
     finally:
         for h in (gqa, d64, mla):
             kvq.kv_paged_destroy(h)
+
+
+def test_decode_step_validation_before_hip():
+    L = kvq.lib()
+    cfg = kivi_cfg()   # B2, 4 KV heads, 256 tokens, D128, G32
+    h = kvq.kv_cache_init(cfg, kvq.CacheBuffers(*FAKE))
+    k, v, q, out, ws = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    try:
+        need = kvq.kv_decode_workspace_bytes(h, 8)
+        ok = [h, k, v, q, 8, C.c_float(0.1), 0, out, ws, need, None]
+
+        def call(i, val):
+            a = list(ok)
+            a[i] = val
+            return L.kv_decode_step(*a)
+
+        for i in (0, 1, 2, 3, 7, 8):
+            assert call(i, None) == -1, i
+        assert call(4, 6) == -2          # not a multiple of Hkv
+        assert call(6, 300) == -2        # n_splits
+        for i in (1, 2, 3, 7, 8):
+            assert call(i, ok[i] + 4) == -3, i
+        assert call(9, 16) == -6         # workspace
+        assert kvq.kv_cache_state(h) == (0, 0)   # nothing happened
+    finally:
+        kvq.kv_cache_destroy(h)

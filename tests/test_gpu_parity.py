@@ -107,6 +107,8 @@ def _shape(shape, T):
         return _tiny(T, Hq=2, Hkv=2, D=128, G=64)
     if shape == "gqa4_g64":
         return _tiny(T, Hq=8, Hkv=2, D=128, G=64)
+    if shape == "gqa4":
+        return _tiny(T, Hq=8, Hkv=2, D=128)
     if shape == "mla64":
         return _mla_tiny(T, Hq=64)
     if shape == "mla128":
@@ -317,3 +319,42 @@ def test_random_bit_pattern_fuzz(orc):
     dc.append(dev_f16(k), dev_f16(v))
     assert_slices_equal(slice_of(dc, 0, 0, T, T // 32),
                         oracle_slice(orc, w, k[0, 0], v[0, 0], cap // 32, cap), "fuzz")
+
+
+@pytest.mark.parametrize("shape", ["gqa4_g64", "gqa4", "mha128_g32", "mha128_g64", "mha", "mla64"])
+def test_decode_step_matches_separate_calls(orc, shape):
+    """kv_decode_step (append fused into the attention launch for the GQA and
+    MHA kernels while no block completes) against kv_quantize_append +
+    kv_decode_attention: caches and outputs bit-identical over steps that
+    cross key-block boundaries, starting from an empty cache."""
+    G = 64 if shape in ("gqa4_g64", "mha128_g64", "mla64") else 32
+    n0 = 2 * G - 3
+    steps = G + 6
+    w = _shape(shape, n0 + steps)
+    cap = w.capacity(8)
+    k, v, q = synth.keys(w), synth.values(w), synth.query(w)
+    a, b = new_cache(w, cap), new_cache(w, cap)
+    qd = dev_f16(q)
+    t = torch()
+    for dc in (a, b):
+        dc.append(dev_f16(np.ascontiguousarray(k[:, :, :n0])), dev_f16(np.ascontiguousarray(v[:, :, :n0])))
+    ws = a.workspace(w.n_q_heads)
+    fused = 0
+    for j in range(steps):
+        tok = n0 + j
+        kn = dev_f16(np.ascontiguousarray(k[:, :, tok:tok + 1]))
+        vn = dev_f16(np.ascontiguousarray(v[:, :, tok:tok + 1]))
+        fused += (tok % G) != G - 1
+        oa = a.step(kn, vn, qd, w.sigma, ws=ws)
+        b.append(kn, vn)
+        ob = b.decode(qd, w.sigma)
+        t.cuda.synchronize()
+        assert a.state() == b.state() == (tok + 1, (tok + 1) % G)
+        ga, gb = host_u16(oa), host_u16(ob)
+        assert np.array_equal(ga, gb), (shape, tok, int(np.sum(ga != gb)))
+    for bb in range(w.batch):
+        for h in range(w.n_kv_heads):
+            sa = slice_of(a, bb, h, w.T, w.n_blocks)
+            assert_slices_equal(sa, slice_of(b, bb, h, w.T, w.n_blocks), f"{shape} b{bb} h{h}")
+    _check_decode(orc, w, a, k, v)
+    log(f"[step {shape}] variant {a.variant(w.n_q_heads)}, {steps} steps, {fused} with the append fused")
