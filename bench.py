@@ -73,6 +73,8 @@ def parse():
                     help="paged cache: ragged lengths in [T/2, T], blocks in shuffled pages")
     ap.add_argument("--batch", type=int, default=0,
                     help="sequences per step (default: the workload's); names the workload ..._b<N>")
+    ap.add_argument("--bits", type=int, default=0, choices=[0, 2, 4],
+                    help="key and value code width (default: the workload's); names the workload ..._<N>bit")
     ap.add_argument("--separate-calls", action="store_true",
                     help="step as kv_quantize_append + kv_decode_attention instead of kv_decode_step")
     return ap.parse_args()
@@ -189,6 +191,9 @@ def main():
     if args.batch:
         import dataclasses
         w = dataclasses.replace(w, batch=args.batch, name=f"{w.name}_b{args.batch}")
+    if args.bits and w.kind == "kivi" and args.bits != w.kbits:
+        import dataclasses
+        w = dataclasses.replace(w, kbits=args.bits, vbits=args.bits, name=f"{w.name}_{args.bits}bit")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.paged:

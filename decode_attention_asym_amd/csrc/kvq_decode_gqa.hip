@@ -461,10 +461,336 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 4-bit keys and values: the same two-wave pipeline over the 4 KB tiles of
+// kvq_mfma_tiles.h.  A code byte holds two tokens (keys) or two channels
+// (values), taken by the masks 0x000F000F << 4 nib.
+
+struct LdsK4 {
+    __attribute__((aligned(16))) uint32_t kl[KTILE4_DW];
+    __attribute__((aligned(16))) uint32_t qa[2 * 8 * QSTR];
+    __attribute__((aligned(16))) uint32_t ksl[2 * 2 * 64];
+    float bias[8];
+};
+struct LdsV4 {
+    __attribute__((aligned(16))) uint32_t vl[VTILE4_DW];
+    __attribute__((aligned(16))) uint32_t pa[2 * 16 * ASTR];   // p' rows: pass P (= value group), head, hi/lo
+    __attribute__((aligned(16))) uint32_t vsl[2 * 128 + 2 * 32];
+};
+struct Lds4 {
+    LdsK4 k;
+    LdsV4 v;
+    Handoff hb[2];
+    float misc[64];
+};
+
+template <int G>
+__device__ __forceinline__ void key_tile4(const MfmaParams& p, KTile4& cur, KState& st, LdsK4& L, Handoff& hb,
+                                          const uint32_t* qw, int lane, int64_t bh, int nxt, const TileRun& run) {
+    constexpr int NBT = 64 / G;
+    const int n = lane & 15, kg = lane >> 4;
+    const int hh = lane >> 4, chunk = lane & 15;
+
+    stage_keys4<G>(cur, L.kl, L.ksl, lane);
+    load_ktile4<G>(p, run, bh, nxt, lane, cur);
+    wave_sync();
+
+    // ---- q' = q * s_k as fp16 hi/lo rows, sigma2 * sum_c q z_k per (block, head): as for 2 bits
+#pragma unroll
+    for (int be = 0; be < NBT; ++be) {
+        uint32_t hi[4], lo[4];
+        float bias = 0.0f;
+        const uint4 swv = *reinterpret_cast<const uint4*>(L.ksl + be * 64 + 4 * chunk);
+        const uint4 zwv = *reinterpret_cast<const uint4*>(L.ksl + 128 + be * 64 + 4 * chunk);
+        const uint32_t sw[4] = {swv.x, swv.y, swv.z, swv.w};
+        const uint32_t zw[4] = {zwv.x, zwv.y, zwv.z, zwv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            split_prod_h(qw[i], sw[i], hi[i], lo[i]);
+            bias = dot2h(qw[i], zw[i], bias);
+        }
+        uint32_t* row = L.qa + (be * 8 + 2 * hh) * QSTR + 4 * chunk;
+        *reinterpret_cast<uint4*>(row) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4*>(row + QSTR) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        bias = row_sum16(bias);
+        if (chunk == 0) L.bias[be * 4 + hh] = bias * p.sigma2;
+    }
+    wave_sync();
+
+    // ---- S = q' . codes: per K-step of 32 channels, two transposed reads
+    // (tile tokens 0..31 and 32..63; for G = 32 the two blocks) of two
+    // nibbles each.  S[2r + nib], column n = token 32r + 2n + nib.
+    f32x4 S[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) S[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ksx = 0; ksx < 4; ++ksx) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int be = G == 64 ? 0 : r;
+            const uint4 a = *reinterpret_cast<const uint4*>(L.qa + (be * 8 + (n & 7)) * QSTR + 16 * ksx + 4 * kg);
+            const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
+            const CodeRegs c = code_operands(ld_tr8(L.kl + key_row_dw4<G>(ksx, r, kg, n)));
+#pragma unroll
+            for (int nib = 0; nib < 2; ++nib)
+                S[2 * r + nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x000F000Fu << (4 * nib)),
+                                                                       S[2 * r + nib], 0, 0, 0);
+        }
+    }
+
+    // ---- softmax: lanes kg and kg + 2 see heads 2(kg&1), 2(kg&1)+1 (rows 8..15
+    // repeat rows 0..7); lanes kg < 2 take the first half of the tile
+    // (r = 0), kg >= 2 the second, so a lane holds tokens 32r + 2n, + 1
+    const bool odd = (kg & 1) != 0;
+    const bool up2 = (kg >> 1) != 0;
+    const int beh = G == 64 ? 0 : (kg >> 1);
+    float sA[2], sB[2];
+#pragma unroll
+    for (int nib = 0; nib < 2; ++nib) {
+        float Sv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sv[e] = up2 ? S[2 + nib][e] : S[nib][e];
+        const float f = p.sigma2 * __builtin_ldexpf(1.0f, 24 - 4 * nib);
+        sA[nib] = fmaf(Sv[0] + Sv[1], f, L.bias[beh * 4 + 2 * (kg & 1)]);
+        sB[nib] = fmaf(Sv[2] + Sv[3], f, L.bias[beh * 4 + 2 * (kg & 1) + 1]);
+    }
+    float a0 = 1.0f, a1 = 1.0f, a2 = 1.0f, a3 = 1.0f;
+    const float thA = (odd ? st.m2 : st.m0) + TAU, thB = (odd ? st.m3 : st.m1) + TAU;
+    const bool over = fmaxf(sA[0], sA[1]) > thA || fmaxf(sB[0], sB[1]) > thB;
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+        const float mA = row_max16(fmaxf(sA[0], sA[1]));
+        const float mB = row_max16(fmaxf(sB[0], sB[1]));
+        const float t0 = fmaxf(readlane_f(mA, 0), readlane_f(mA, 32));
+        const float t1 = fmaxf(readlane_f(mB, 0), readlane_f(mB, 32));
+        const float t2 = fmaxf(readlane_f(mA, 16), readlane_f(mA, 48));
+        const float t3 = fmaxf(readlane_f(mB, 16), readlane_f(mB, 48));
+        const float n0 = fmaxf(st.m0, t0), n1 = fmaxf(st.m1, t1);
+        const float n2 = fmaxf(st.m2, t2), n3 = fmaxf(st.m3, t3);
+        a0 = fast_exp2(st.m0 - n0);
+        a1 = fast_exp2(st.m1 - n1);
+        a2 = fast_exp2(st.m2 - n2);
+        a3 = fast_exp2(st.m3 - n3);
+        st.m0 = n0;
+        st.m1 = n1;
+        st.m2 = n2;
+        st.m3 = n3;
+    }
+    const float mrA = odd ? st.m2 : st.m0, mrB = odd ? st.m3 : st.m1;
+#pragma unroll
+    for (int nib = 0; nib < 2; ++nib) {
+        sA[nib] = fast_exp2(sA[nib] - mrA);
+        sB[nib] = fast_exp2(sB[nib] - mrB);
+    }
+    // ---- weights as fp16 hi + lo pairs (tokens 4k + j, 4k + j + 2): lane n
+    // holds 4k + 2(n & 1) + nib with k = 8r + (n >> 1), so an even lane pairs
+    // its low-nibble token with its odd neighbour's and the odd lane its
+    // high-nibble token with the even neighbour's (dword 16r + n)
+    const int hA = 2 * (kg & 1), hB = hA + 1;
+    const int dw = 16 * (kg >> 1) + n;
+    const bool nodd = (n & 1) != 0;
+    const float oA = dpp<0xb1>(nodd ? sA[0] : sA[1]);
+    const float oB = dpp<0xb1>(nodd ? sB[0] : sB[1]);
+    uint32_t h, l;
+    split_f32(nodd ? oA : sA[0], nodd ? sA[1] : oA, p.neg1, h, l);
+    hb.ph[hA * PHS + dw] = h;
+    hb.pq[hA * PHS + dw] = l;
+    split_f32(nodd ? oB : sB[0], nodd ? sB[1] : oB, p.neg1, h, l);
+    hb.ph[hB * PHS + dw] = h;
+    hb.pq[hB * PHS + dw] = l;
+    if (lane < HG) hb.alpha[lane] = sel4(lane, a0, a1, a2, a3);
+}
+
+struct VState4 {
+    f32x4 O[4][2];   // PV accumulators [pass = value group][nibble]
+    f32x4 Z;         // as VState::Z
+};
+
+template <int G>
+__device__ __forceinline__ void value_tile4(const MfmaParams& p, VTile4& cur, VState4& st, LdsV4& L, const Handoff& hb,
+                                            int lane, int64_t bh, int nxt, const TileRun& run) {
+    const int n = lane & 15, kg = lane >> 4;
+    const int hh = lane >> 4, chunk = lane & 15;
+    stage_values4(cur, L.vl, L.vsl, lane);
+    load_vtile4(p, run, bh, nxt, lane, cur);
+
+    const float a0 = hb.alpha[0], a1 = hb.alpha[1], a2 = hb.alpha[2], a3 = hb.alpha[3];
+    if (fminf(fminf(a0, a1), fminf(a2, a3)) < 1.0f) {
+        const bool odd = (kg & 1) != 0;
+        const float aA = odd ? a2 : a0, aB = odd ? a3 : a1;
+#pragma unroll
+        for (int P = 0; P < 4; ++P)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                st.O[P][u][0] *= aA;
+                st.O[P][u][1] *= aA;
+                st.O[P][u][2] *= aB;
+                st.O[P][u][3] *= aB;
+            }
+        st.Z[0] *= aA;
+        st.Z[1] *= aA;
+        st.Z[2] *= aB;
+        st.Z[3] *= aB;
+    }
+    wave_sync();
+
+    // ---- p' = p * s_v as fp16 hi/lo rows per value group g: rows (g * 4 +
+    // head) * 2 + hl, the same rows as for 2 bits (there pass g >> 1, half g & 1)
+    {
+        const uint2 ph = *reinterpret_cast<const uint2*>(hb.ph + hh * PHS + 2 * chunk);
+        const uint2 pq = *reinterpret_cast<const uint2*>(hb.pq + hh * PHS + 2 * chunk);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint2 sv = *reinterpret_cast<const uint2*>(L.vsl + g * 32 + 2 * chunk);
+            uint32_t h0, l0, h1, l1;
+            split_prod_hl(ph.x, pq.x, sv.x, h0, l0);
+            split_prod_hl(ph.y, pq.y, sv.y, h1, l1);
+            uint32_t* rowp = L.pa + ((g * 4 + hh) * 2) * ASTR + 2 * chunk;
+            *reinterpret_cast<uint2*>(rowp) = make_uint2(h0, h1);
+            *reinterpret_cast<uint2*>(rowp + ASTR) = make_uint2(l0, l1);
+        }
+    }
+    // ---- sum_t p z_v and sum_t p on the matrix cores, as for 2 bits
+    {
+        const int r = n & 7;
+        const uint32_t* arow = ((r & 1) ? hb.pq : hb.ph) + (r >> 1) * PHS + 4 * kg;
+        const uint32_t* brow = L.vsl + 128 + (n < 5 ? n : 5) * 32 + 4 * kg;
+#pragma unroll
+        for (int ksx = 0; ksx < 2; ++ksx) {
+            const uint4 a = *reinterpret_cast<const uint4*>(arow + 16 * ksx);
+            const uint4 z = *reinterpret_cast<const uint4*>(brow + 16 * ksx);
+            st.Z = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a.x, a.y, a.z, a.w), as_f16x8(z.x, z.y, z.z, z.w),
+                                                          st.Z, 0, 0, 0);
+        }
+    }
+    wave_sync();
+
+    // ---- O += p' . codes: 4 passes (one value group each) x 2 K-steps of
+    // 32 tokens x 2 nibbles; A rows 8..15 repeat rows 0..7
+#pragma unroll
+    for (int P = 0; P < 4; ++P) {
+#pragma unroll
+        for (int ksx = 0; ksx < 2; ++ksx) {
+            const uint4 a = *reinterpret_cast<const uint4*>(L.pa + (P * 8 + (n & 7)) * ASTR + 16 * ksx + 4 * kg);
+            const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
+            const CodeRegs c = code_operands(ld_tr8(L.vl + value_row_dw4(ksx, P, kg, n)));
+#pragma unroll
+            for (int nib = 0; nib < 2; ++nib)
+                st.O[P][nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x000F000Fu << (4 * nib)),
+                                                                      st.O[P][nib], 0, 0, 0);
+        }
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(128) void k_decode_gqa4(MfmaParams p) {
+    __shared__ Lds4 L;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n = lane & 15, kg = lane >> 4;
+    const int hh = lane >> 4, chunk = lane & 15;
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    bool tail;
+    const int s = slot_of_block(p, tail);
+    const int64_t bh = int64_t(b) * p.Hkv + kvh;
+    const int hq0 = kvh * HG;
+    if (tail) {
+        tail_split<HG, 4>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
+        return;
+    }
+    const int t_lo = int(int64_t(s) * p.ntiles / p.S_main);
+    const int t_hi = int(int64_t(s + 1) * p.ntiles / p.S_main);
+    const int ntl = t_hi - t_lo;
+
+    if (wave == 0) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(p.q + ((int64_t(b) * p.Hq + hq0 + hh) * D + 8 * chunk));
+        const uint32_t qv[4] = {pair_lo(raw.x, raw.y), pair_hi(raw.x, raw.y), pair_lo(raw.z, raw.w),
+                                pair_hi(raw.z, raw.w)};
+        KState st;
+        st.m0 = st.m1 = st.m2 = st.m3 = -INFINITY;
+        KTile4 ta, tb;
+        const TileRun run = tile_run4<G>(p, bh, t_lo, t_hi);
+        load_ktile4<G>(p, run, bh, t_lo, lane, ta);
+        load_ktile4<G>(p, run, bh, t_lo + 1, lane, tb);
+        __builtin_amdgcn_sched_barrier(0);
+        key_tile4<G>(p, ta, st, L.k, L.hb[0], qv, lane, bh, t_lo + 2, run);
+        __syncthreads();
+        int j = 1;
+        for (; j + 1 < ntl; j += 2) {
+            key_tile4<G>(p, tb, st, L.k, L.hb[1], qv, lane, bh, t_lo + j + 2, run);
+            __syncthreads();
+            key_tile4<G>(p, ta, st, L.k, L.hb[0], qv, lane, bh, t_lo + j + 3, run);
+            __syncthreads();
+        }
+        if (j < ntl) {
+            key_tile4<G>(p, tb, st, L.k, L.hb[1], qv, lane, bh, t_lo + j + 2, run);
+            __syncthreads();
+        }
+        if (lane < HG) L.misc[lane] = sel4(lane, st.m0, st.m1, st.m2, st.m3);
+        __syncthreads();
+    } else {
+        VState4 st;
+        st.Z = f32x4{0.f, 0.f, 0.f, 0.f};
+        L.v.vsl[256 + lane] = lane < 32 ? 0x3c003c00u : 0u;
+#pragma unroll
+        for (int P = 0; P < 4; ++P)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) st.O[P][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        VTile4 ta, tb;
+        const TileRun run = tile_run4<G>(p, bh, t_lo, t_hi);
+        load_vtile4(p, run, bh, t_lo, lane, ta);
+        load_vtile4(p, run, bh, t_lo + 1, lane, tb);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        value_tile4<G>(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + 2, run);
+        __syncthreads();
+        int j = 1;
+        for (; j + 1 < ntl; j += 2) {
+            value_tile4<G>(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
+            __syncthreads();
+            value_tile4<G>(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + j + 3, run);
+            __syncthreads();
+        }
+        if (j < ntl) {
+            value_tile4<G>(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
+            __syncthreads();
+        }
+        // ---- epilogue: l and the value-zero sums, as for 2 bits
+        if (kg < 2 && n < 5) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int h = 2 * kg + j;
+                const float v = st.Z[2 * j] + st.Z[2 * j + 1];
+                L.misc[n < 4 ? 32 + h * 4 + n : 16 + h] = v;
+            }
+        }
+        wave_sync();
+        // rows 0..7 (head 2kg + j, hi/lo); rows 8..15 repeat them
+        if (kg < 2) {
+#pragma unroll
+            for (int P = 0; P < 4; ++P)
+#pragma unroll
+                for (int nib = 0; nib < 2; ++nib) {
+                    const int c = 32 * P + 8 * (n >> 2) + 2 * (n & 3) + nib;
+                    const float f = __builtin_ldexpf(1.0f, 24 - 4 * nib);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int h = 2 * kg + j;
+                        const float acc = fmaf(st.O[P][nib][2 * j] + st.O[P][nib][2 * j + 1], f, L.misc[32 + h * 4 + P]);
+                        p.ws_acc[((int64_t(b) * p.Hq + hq0 + h) * p.S + s) * D + c] = acc;
+                    }
+                }
+        }
+        if (lane < HG) {
+            const int64_t slot = (int64_t(b) * p.Hq + hq0 + lane) * p.S + s;
+            p.ws_ml[slot * 2] = L.misc[lane];
+            p.ws_ml[slot * 2 + 1] = L.misc[16 + lane];
+        }
+    }
+}
+
 }  // namespace
 
 bool gqa_supported(const kvq_cache& c, int Hq) {
-    return mfma_shape_ok(c) && Hq == HG * c.cfg.n_kv_heads;
+    return (mfma_cfg_ok(c.cfg) || mfma_cfg_ok4(c.cfg)) && Hq == HG * c.cfg.n_kv_heads;
 }
 
 bool gqa_cfg_supported(const kvq_cache_cfg& c, int Hq) { return mfma_cfg_ok(c) && Hq == HG * c.n_kv_heads; }
@@ -472,6 +798,13 @@ bool gqa_cfg_supported(const kvq_cache_cfg& c, int Hq) { return mfma_cfg_ok(c) &
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
     const MfmaParams p = mfma_params(a);
     const dim3 grid(a.S, a.g.Hkv, a.g.B);
+    if (a.g.kbits == 4) {
+        if (a.g.kG == 64)
+            hipExtLaunchKernelGGL(k_decode_gqa4<64>, grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+        else
+            hipExtLaunchKernelGGL(k_decode_gqa4<32>, grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+        return hipGetLastError();
+    }
     if (a.g.kG == 64)
         hipExtLaunchKernelGGL((k_decode_gqa<64, false>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
     else

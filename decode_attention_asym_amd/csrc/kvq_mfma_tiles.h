@@ -116,6 +116,11 @@ inline bool mfma_cfg_ok(const kvq_cache_cfg& g) {
            g.value.dim == D && g.value.group == 32 && (g.key.group == 32 || g.key.group == 64);
 }
 inline bool mfma_shape_ok(const kvq_cache& c) { return mfma_cfg_ok(c.cfg); }
+// the same shapes with 4-bit keys and values (GQA kernel, contiguous cache)
+inline bool mfma_cfg_ok4(const kvq_cache_cfg& g) {
+    return g.kind == KVQ_KIND_KIVI && g.key.bits == 4 && g.value.bits == 4 && g.key.dim == D &&
+           g.value.dim == D && g.value.group == 32 && (g.key.group == 32 || g.key.group == 64);
+}
 
 // ---- where key block j of (sequence b, KV head kvh) lives: its block row r
 // (key codes at r * D * G/16 words, key side values at r * D, value rows
@@ -334,6 +339,129 @@ __device__ __forceinline__ void load_vtile(const MfmaParams& p, const TileRun& r
     r.vs = make_uint4(a.x, a.y, b.x, b.y);
 }
 
+// ---- 4-bit tiles: 4 KB of key codes and 4 KB of value codes per 64-token
+// tile (16 words per token, G/8 words per key block and channel); side
+// values as for 2 bits.  A code nibble ANDed into an fp16 lane at bits
+// [4 nib, 4 nib + 3] is the exact subnormal code * 16^nib * 2^-24, so each
+// code byte feeds two MFMAs instead of four: twice the bytes and transposed
+// reads per tile, the same MFMA and AND counts.
+struct KTile4 {
+    uint4 k[4];   // key codes, 64 B per lane
+    uint4 ks;     // key scale (lanes 0..31) / zero (lanes 32..63)
+};
+struct VTile4 {
+    uint4 v[4];   // value codes
+    uint4 vs;     // value scale / zero of two tokens
+};
+
+constexpr int KTILE4_DW = 1088;   // key-code tile in LDS (dwords), padded (kdw4_64)
+constexpr int VTILE4_DW = 1088;   // value-code tile in LDS (dwords), padded (vdw4)
+
+template <int G>
+__device__ __forceinline__ TileRun tile_run4(const MfmaParams& p, int64_t bh, int t_lo, int t_hi) {
+    constexpr int NBT = 64 / G, W = G / 8;
+    constexpr int FLAGS = 0x00020000;
+    TileRun r;
+    const int bytes = (t_hi - t_lo) * 4096;
+    r.kc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(p.kc + (bh * p.nblk_cap + int64_t(t_lo) * NBT) * D * W),
+                                             0, bytes, FLAGS);
+    r.vc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(p.vc + (bh * p.cap + int64_t(t_lo) * 64) * 16), 0,
+                                             bytes, FLAGS);
+    r.t0 = t_lo;
+    r.t_last = t_hi - 1;
+    return r;
+}
+
+template <int G>
+__device__ __forceinline__ void load_ktile4(const MfmaParams& p, const TileRun& run, int64_t bh, int tt, int lane,
+                                            KTile4& r) {
+    constexpr int NBT = 64 / G;
+    const int off = (tt - run.t0) * 4096 + 16 * lane;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r.k[q] = ld_run(run.kc, off + 1024 * q);
+    const int ts = tt < run.t_last ? tt : run.t_last;
+    const uint16_t* kside = (lane < 32 ? p.ks : p.kz) + (bh * p.nblk_cap + int64_t(ts) * NBT) * D;
+    if (G == 64) {
+        const uint2 v = ld_stream(reinterpret_cast<const uint2*>(kside) + (lane & 31));
+        r.ks = make_uint4(v.x, v.y, 0u, 0u);
+    } else {
+        r.ks = ld_stream(reinterpret_cast<const uint4*>(kside) + (lane & 31));
+    }
+}
+
+__device__ __forceinline__ void load_vtile4(const MfmaParams& p, const TileRun& run, int64_t bh, int tt, int lane,
+                                            VTile4& r) {
+    const int off = (tt - run.t0) * 4096 + 16 * lane;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r.v[q] = ld_run(run.vc, off + 1024 * q);
+    const int64_t ts = tt < run.t_last ? tt : run.t_last;
+    const uint16_t* vside = (lane < 32 ? p.vs : p.vz) + (bh * p.cap + ts * 64) * 4;
+    const int t = 4 * ((lane & 31) >> 1) + (lane & 1);
+    const uint2 a = ld_stream(reinterpret_cast<const uint2*>(vside + 4 * t));
+    const uint2 b = ld_stream(reinterpret_cast<const uint2*>(vside + 4 * (t + 2)));
+    r.vs = make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// dword of word w (0..7) of channel c in the staged G = 64 key tile: the
+// cache layout with 4 dwords of pad after every 8 channels, so that the two
+// 16-lane groups of a transposed read hit different banks
+__device__ __forceinline__ int kdw4_64(int c, int w) { return 8 * c + w + 4 * (c >> 3); }
+// dword of word w (0..15) of token t in the staged value tile: 4 dwords of
+// pad after every 4 tokens (16 consecutive tokens on distinct banks)
+__device__ __forceinline__ int vdw4(int t, int w) { return 16 * t + w + 4 * (t >> 2); }
+
+// Key codes staged: G = 64 in kdw4_64 order; G = 32 in the cache layout
+// (block be, channel c at dwords 512be + 4c .. 4c + 3).  Side values as for
+// 2 bits.
+template <int G>
+__device__ __forceinline__ void stage_keys4(const KTile4& cur, uint32_t* kl, uint32_t* ksl, int lane) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = 64 * q + lane;   // 16-byte piece of the tile
+        *reinterpret_cast<uint4*>(kl + (G == 64 ? kdw4_64(i >> 1, 4 * (i & 1)) : 4 * i)) = cur.k[q];
+    }
+    if (G == 64)
+        *reinterpret_cast<uint2*>(ksl + (lane >> 5) * 128 + 2 * (lane & 31)) =
+            make_uint2(pair_lo(cur.ks.x, cur.ks.y), pair_hi(cur.ks.x, cur.ks.y));
+    else
+        *reinterpret_cast<uint4*>(ksl + (lane >> 5) * 128 + 4 * (lane & 31)) =
+            make_uint4(pair_lo(cur.ks.x, cur.ks.y), pair_hi(cur.ks.x, cur.ks.y),
+                       pair_lo(cur.ks.z, cur.ks.w), pair_hi(cur.ks.z, cur.ks.w));
+}
+
+// Value codes staged in vdw4 order, side values as for 2 bits.
+__device__ __forceinline__ void stage_values4(const VTile4& cur, uint32_t* vl, uint32_t* vsl, int lane) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = 64 * q + lane;
+        *reinterpret_cast<uint4*>(vl + vdw4(i >> 2, 4 * (i & 3))) = cur.v[q];
+    }
+    uint32_t* row = vsl + (lane >> 5) * 128 + (lane & 31);
+    row[0] = pair_lo(cur.vs.x, cur.vs.z);
+    row[32] = pair_hi(cur.vs.x, cur.vs.z);
+    row[64] = pair_lo(cur.vs.y, cur.vs.w);
+    row[96] = pair_hi(cur.vs.y, cur.vs.w);
+}
+
+// Key row named by lane n of group kg for K-step ksx and half r (tokens
+// 32r .. 32r + 31 of the tile; the block r for G = 32): lanes 2e, 2e + 1
+// name channel 32ksx + 8kg + e, bytes 0-7 and 8-15 of that half.  Lane n
+// then holds tokens 32r + 2n (low nibble) and 32r + 2n + 1 (high nibble) of
+// the 8 channels.
+template <int G>
+__device__ __forceinline__ int key_row_dw4(int ksx, int r, int kg, int n) {
+    const int c = 32 * ksx + 8 * kg + (n >> 1);
+    return G == 64 ? kdw4_64(c, 4 * r + 2 * (n & 1)) : 512 * r + 4 * c + 2 * (n & 1);
+}
+
+// Value row named by lane n of group kg for K-step ksx (32 tokens) and pass
+// P (words 4P .. 4P + 3 = channels 32P .. 32P + 31, one value group): lane
+// n then holds channels 32P + 8(n >> 2) + 2(n & 3) (low nibble) and + 1
+// (high nibble) of the 8 tokens.
+__device__ __forceinline__ int value_row_dw4(int ksx, int P, int kg, int n) {
+    return vdw4(32 * ksx + 8 * kg + (n >> 1), 4 * P + 2 * (n & 1));
+}
+
 // Paged runs: the tiles of a run lie in the pages the block table names.
 // Lane l holds the page of block NBT * t_lo + l (a run spans at most 64
 // blocks); each tile's code loads go through buffer resources over its own
@@ -526,9 +654,11 @@ __device__ __forceinline__ f16x8 code_slice(const CodeRegs& c, uint32_t mk) {
 //  - both waves, lane = channel (wave w: channels 64w ..): values 16
 //    tokens at a time, accumulated in token order.
 // The tail spans at most two key blocks, whose rows are looked up once.
-template <int HG, class Blocks>
+template <int HG, class Blocks, int BITS = 2>
 __device__ void tail_split(const MfmaParams& p, const Blocks& blocks, int b, int kvh, int s, float* qf, float* pl,
                            int64_t T, int64_t nblk, int ntiles) {
+    constexpr int PER = 32 / BITS;              // codes per word
+    constexpr uint32_t LMASK = (1u << BITS) - 1u;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int hq0 = kvh * HG;
     const int64_t t0 = int64_t(ntiles) * 64;
@@ -583,7 +713,7 @@ __device__ void tail_split(const MfmaParams& p, const Blocks& blocks, int b, int
                 const int64_t side = row0 * D + c0;
                 uint32_t wd[16];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) wd[e] = p.kc[(side + e) * (p.G / 16) + i / 16];
+                for (int e = 0; e < 16; ++e) wd[e] = p.kc[(side + e) * (p.G / PER) + i / PER];
                 uint32_t sw[8], zw[8];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
@@ -596,7 +726,7 @@ __device__ void tail_split(const MfmaParams& p, const Blocks& blocks, int b, int
                 for (int e = 0; e < 16; ++e) {
                     const float se = (e & 1) ? hi_h(sw[e >> 1]) : lo_h(sw[e >> 1]);
                     const float ze = (e & 1) ? hi_h(zw[e >> 1]) : lo_h(zw[e >> 1]);
-                    const float kh = fmaf(float((wd[e] >> (2 * (i & 15))) & 3u), se, ze);
+                    const float kh = fmaf(float((wd[e] >> (BITS * (i % PER))) & LMASK), se, ze);
 #pragma unroll
                     for (int h = 0; h < HG; ++h) sc[h] = fmaf(qf[h * D + c0 + e], kh, sc[h]);
                 }
@@ -631,14 +761,14 @@ __device__ void tail_split(const MfmaParams& p, const Blocks& blocks, int b, int
             // is in block jb + (j >= G)
             const int j = j0 + e < n_tail ? j0 + e : n_tail - 1;
             const int64_t row = j < p.G ? row0 * p.G + j : row1 * p.G + (j - p.G);
-            w[e] = p.vc[row * 8 + c / 16];
+            w[e] = p.vc[row * (D / PER) + c / PER];
             sv[e] = p.vs[row * 4 + c / 32];
             zv[e] = p.vz[row * 4 + c / 32];
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             if (j0 + e < n_tail) {
-                const float vh = fmaf(float((w[e] >> (2 * (c & 15))) & 3u), h2f(sv[e]), h2f(zv[e]));
+                const float vh = fmaf(float((w[e] >> (BITS * (c % PER))) & LMASK), h2f(sv[e]), h2f(zv[e]));
 #pragma unroll
                 for (int h = 0; h < HG; ++h) acc[h] = fmaf(pl[h * PSTR + j0 + e], vh, acc[h]);
             }
@@ -664,6 +794,7 @@ __device__ void tail_split(const MfmaParams& p, const Blocks& blocks, int b, int
 // device code as the append kernels (bit-identical).  No other workgroup
 // reads these rows: the main splits end at the last whole tile, and the
 // tail covers everything after it.
+template <int BITS>
 __device__ void fused_append(const MfmaParams& p, int b, int kvh, int lane) {
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int64_t t = p.T - 1;
@@ -683,7 +814,7 @@ __device__ void fused_append(const MfmaParams& p, int b, int kvh, int lane) {
         va.scale = p.vs_w;
         va.zero = p.vz_w;
         const qdev::ContigRows rows{p.cap, t, 1};
-        qdev::quant_values_thread<2>(va, rows, bh * TPR + lane);
+        qdev::quant_values_thread<BITS>(va, rows, bh * TPR + lane);
     } else if (lane < 2 * TPR) {
         const int v = lane - TPR;
         const int64_t r = t - p.nblk * p.G;
@@ -696,10 +827,10 @@ __device__ void fused_append(const MfmaParams& p, int b, int kvh, int lane) {
 }
 
 // the contiguous cache's tail: its counters are in the parameters
-template <int HG>
+template <int HG, int BITS = 2>
 __device__ void tail_split(const MfmaParams& p, int b, int kvh, int s, float* qf, float* pl) {
-    if (p.fuse) fused_append(p, b, kvh, threadIdx.x & 63);
-    tail_split<HG>(p, ContigBlocks{}, b, kvh, s, qf, pl, p.T, p.nblk, p.ntiles);
+    if (p.fuse) fused_append<BITS>(p, b, kvh, threadIdx.x & 63);
+    tail_split<HG, ContigBlocks, BITS>(p, ContigBlocks{}, b, kvh, s, qf, pl, p.T, p.nblk, p.ntiles);
 }
 
 // The tail workgroup (partial tile and residual keys, a chain of dependent

@@ -109,6 +109,10 @@ def _shape(shape, T):
         return _tiny(T, Hq=8, Hkv=2, D=128, G=64)
     if shape == "gqa4":
         return _tiny(T, Hq=8, Hkv=2, D=128)
+    if shape == "gqa4_4bit_g64":
+        return _tiny(T, Hq=8, Hkv=2, D=128, G=64, kbits=4, vbits=4)
+    if shape == "gqa4_4bit_g32":
+        return _tiny(T, Hq=8, Hkv=2, D=128, G=32, kbits=4, vbits=4)
     if shape == "mla64":
         return _mla_tiny(T, Hq=64)
     if shape == "mla128":
@@ -118,9 +122,9 @@ def _shape(shape, T):
 
 @pytest.mark.parametrize("T", [1, 15, 31, 32, 33, 101, 3 * 64 + 5, 700])
 @pytest.mark.parametrize("shape", ["mha", "mha128_g32", "mha128_g64", "gqa4", "gqa8_g64", "mla", "mla64",
-                                   "mla128"])
+                                   "mla128", "gqa4_4bit_g64", "gqa4_4bit_g32"])
 def test_edge_lengths(orc, T, shape):
-    if shape in ("mha", "mha128_g32", "mha128_g64", "mla64", "mla128"):
+    if shape in ("mha", "mha128_g32", "mha128_g64", "mla64", "mla128", "gqa4_4bit_g64", "gqa4_4bit_g32"):
         w = _shape(shape, T)
     elif shape == "gqa4":
         w = _tiny(T, Hq=8, Hkv=2, D=128)
@@ -140,7 +144,7 @@ def test_edge_lengths(orc, T, shape):
 
 
 @pytest.mark.parametrize("n_splits", [1, 2, 3, 7, 64, 256])
-@pytest.mark.parametrize("shape", ["gqa4", "mha128_g32", "mla64"])
+@pytest.mark.parametrize("shape", ["gqa4", "mha128_g32", "mla64", "gqa4_4bit_g64", "gqa4_4bit_g32"])
 def test_split_counts(orc, n_splits, shape):
     w = _tiny(1000, Hq=8, Hkv=2, D=128, G=32) if shape == "gqa4" else _shape(shape, 1000)
     cap = w.capacity()
@@ -321,13 +325,14 @@ def test_random_bit_pattern_fuzz(orc):
                         oracle_slice(orc, w, k[0, 0], v[0, 0], cap // 32, cap), "fuzz")
 
 
-@pytest.mark.parametrize("shape", ["gqa4_g64", "gqa4", "mha128_g32", "mha128_g64", "mha", "mla64"])
+@pytest.mark.parametrize("shape", ["gqa4_g64", "gqa4", "mha128_g32", "mha128_g64", "mha", "mla64", "gqa4_4bit_g64",
+                                   "gqa4_4bit_g32"])
 def test_decode_step_matches_separate_calls(orc, shape):
     """kv_decode_step (append fused into the attention launch for the GQA and
     MHA kernels while no block completes) against kv_quantize_append +
     kv_decode_attention: caches and outputs bit-identical over steps that
     cross key-block boundaries, starting from an empty cache."""
-    G = 64 if shape in ("gqa4_g64", "mha128_g64", "mla64") else 32
+    G = 64 if shape in ("gqa4_g64", "mha128_g64", "mla64", "gqa4_4bit_g64") else 32
     n0 = 2 * G - 3
     steps = G + 6
     w = _shape(shape, n0 + steps)
@@ -358,3 +363,36 @@ def test_decode_step_matches_separate_calls(orc, shape):
             assert_slices_equal(sa, slice_of(b, bb, h, w.T, w.n_blocks), f"{shape} b{bb} h{h}")
     _check_decode(orc, w, a, k, v)
     log(f"[step {shape}] variant {a.variant(w.n_q_heads)}, {steps} steps, {fused} with the append fused")
+
+
+@pytest.mark.parametrize("G", [64, 32])
+def test_gqa_4bit_full_size(orc, G):
+    """The 32K-token, 32q/8kv, D = 128 GQA workload with 4-bit keys and
+    values (4 KB tiles on the matrix cores): cache bit-exact and attention
+    within 2e-3 on sampled (sequence, KV head) slices."""
+    import dataclasses
+    base = configs.BY_NAME["mistral_7b_gqa_t32805"]
+    w = dataclasses.replace(base, name=f"gqa_4bit_g{G}", kG=G, kbits=4, vbits=4, batch=4)
+    cap = w.capacity(64)
+    k, v, q = synth.keys(w), synth.values(w), synth.query(w)
+    dc = new_cache(w, cap)
+    dc.append(dev_f16(k), dev_f16(v))
+    assert dc.variant(w.n_q_heads) == "gqa_mfma"
+    got = _decode(dc, w, q)
+    group = w.n_q_heads // w.n_kv_heads
+    worst, gots, refs = 0.0, [], []
+    for b, h in [(0, 0), (1, 5), (3, 7)]:
+        ref = oracle_slice(orc, w, k[b, h], v[b, h], cap // w.kG, cap)
+        assert_slices_equal(slice_of(dc, b, h, w.T, w.n_blocks), ref, f"4-bit G{G} b{b} h{h}")
+        heads = list(range(h * group, (h + 1) * group))
+        cache = oracle_cache_full(orc, w, k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], cap)
+        sub = configs.Workload(w.name, w.index, "kivi", 1, group, 1, w.T, w.kd, w.kG, w.kbits, w.vd, w.vG, w.vbits,
+                               w.outlier_scale)
+        ref_o = oracle_attention(orc, sub, cache, np.ascontiguousarray(q[b:b + 1, heads]))[0]
+        gots.append(got[b, heads].ravel())
+        refs.append(ref_o.ravel())
+        worst = max(worst, float(np.abs(gots[-1] - refs[-1]).max()))
+    excess = mean_excess(np.concatenate(gots), np.concatenate(refs))
+    log(f"[4-bit G{G}] max|err| {worst:.3e} mean excess {excess:.2e}")
+    assert worst <= TOL
+    assert excess <= MEAN_EXCESS_TOL
