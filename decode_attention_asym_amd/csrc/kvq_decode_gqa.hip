@@ -1,6 +1,7 @@
 // kvq_decode_gqa.hip -- split-K decode attention on MFMA for GQA caches:
 // 4 query heads per KV head, head dim 128, 2-bit keys (G = 32 or 64) and
-// 2-bit values (32-channel groups).
+// 2-bit values (32-channel groups); k_decode_gqa4 takes 4-bit keys and
+// values.
 //
 // Method ("Makale Bülteni -- KIVI", section "İddia ve Gerçeklik: KIVI"):
 // logits over the per-channel-quantized keys and the fp16 residual keys,

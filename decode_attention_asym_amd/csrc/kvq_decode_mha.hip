@@ -1,6 +1,6 @@
 // kvq_decode_mha.hip -- split-K decode attention on MFMA for multi-head
-// caches (one query head per KV head), head dim 128, 2-bit keys (G = 32 or
-// 64) and 2-bit values in 32-channel groups.
+// caches (one query head per KV head), head dim 128, 2-bit or 4-bit keys
+// (G = 32 or 64) and values in 32-channel groups.
 //
 // Method ("Makale Bülteni -- KIVI", section "İddia ve Gerçeklik: KIVI"):
 // logits over the per-channel-quantized keys and the fp16 residual keys,
@@ -338,13 +338,269 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 4-bit keys and values (the 4 KB tiles of kvq_mfma_tiles.h): per K-step two
+// transposed key reads of two nibbles each, four value passes of one group
+// each; the A rows are the 2-bit kernel's hi/lo rows.
+
+struct LdsK4 {
+    __attribute__((aligned(16))) uint32_t kl[KTILE4_DW];
+    __attribute__((aligned(16))) uint32_t qa[2 * 2 * QSTR];
+    __attribute__((aligned(16))) uint32_t ksl[2 * 2 * 64];
+};
+struct LdsV4 {
+    __attribute__((aligned(16))) uint32_t vl[VTILE4_DW];
+    __attribute__((aligned(16))) uint32_t pa[8 * ASTR];   // p' rows [group][hi, lo]
+    __attribute__((aligned(16))) uint32_t vsl[2 * 128 + 2 * 32];
+};
+struct Lds4 {
+    LdsK4 k;
+    LdsV4 v;
+    Handoff hb[2];
+    float misc[4];
+};
+
+template <int G>
+__device__ __forceinline__ void key_tile4(const MfmaParams& p, KTile4& cur, float& m_run, LdsK4& L, Handoff& hb,
+                                          uint32_t qw, int lane, int64_t bh, int nxt, const TileRun& run) {
+    constexpr int NBT = 64 / G;
+    const int n = lane & 15, kg = lane >> 4;
+    stage_keys4<G>(cur, L.kl, L.ksl, lane);
+    load_ktile4<G>(p, run, bh, nxt, lane, cur);
+    wave_sync();
+
+    float bias[NBT];
+#pragma unroll
+    for (int be = 0; be < NBT; ++be) {
+        const uint32_t sw = L.ksl[be * 64 + lane], zw = L.ksl[128 + be * 64 + lane];
+        uint32_t hi, lo;
+        split_prod_h(qw, sw, hi, lo);
+        L.qa[(2 * be) * QSTR + lane] = hi;
+        L.qa[(2 * be + 1) * QSTR + lane] = lo;
+        bias[be] = wave_sum(dot2h(qw, zw, 0.0f)) * p.sigma2;
+    }
+    wave_sync();
+
+    // ---- S[2r + nib], column n = token 32r + 2n + nib
+    f32x4 S[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) S[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ksx = 0; ksx < 4; ++ksx) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int be = G == 64 ? 0 : r;
+            const uint4 a = *reinterpret_cast<const uint4*>(L.qa + (2 * be + (n & 1)) * QSTR + 16 * ksx + 4 * kg);
+            const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
+            const CodeRegs c = code_operands(ld_tr8(L.kl + key_row_dw4<G>(ksx, r, kg, n)));
+#pragma unroll
+            for (int nib = 0; nib < 2; ++nib)
+                S[2 * r + nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x000F000Fu << (4 * nib)),
+                                                                       S[2 * r + nib], 0, 0, 0);
+        }
+    }
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float f = p.sigma2 * __builtin_ldexpf(1.0f, 24 - 4 * (i & 1));
+        x[i] = fmaf(S[i][0] + S[i][1], f, bias[G == 64 ? 0 : (i >> 1)]);
+    }
+    const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    float alpha = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {
+        const float mnew = fmaxf(m_run, readlane_f(row_max16(mx), 0));
+        alpha = fast_exp2(m_run - mnew);
+        m_run = mnew;
+    }
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(x[i] - m_run);
+    // ---- weights as fp16 hi + lo pairs (tokens 4k + j, 4k + j + 2): for each
+    // half r, the even lane pairs its low-nibble token with the odd
+    // neighbour's, the odd lane its high-nibble token (dword 16r + n)
+    const bool nodd = (n & 1) != 0;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const float o = dpp<0xb1>(nodd ? pv[2 * r] : pv[2 * r + 1]);
+        uint32_t h, l;
+        split_f32(nodd ? o : pv[2 * r], nodd ? pv[2 * r + 1] : o, p.neg1, h, l);
+        if (kg == 0) {
+            hb.ph[16 * r + n] = h;
+            hb.pq[16 * r + n] = l;
+        }
+    }
+    if (lane == 0) hb.alpha = alpha;
+}
+
+struct VState4 {
+    f32x4 O[4][2];   // PV accumulators [pass = value group][nibble]
+    f32x4 Z;
+};
+
+template <int G>
+__device__ __forceinline__ void value_tile4(const MfmaParams& p, VTile4& cur, VState4& st, LdsV4& L, const Handoff& hb,
+                                            int lane, int64_t bh, int nxt, const TileRun& run) {
+    const int n = lane & 15, kg = lane >> 4;
+    stage_values4(cur, L.vl, L.vsl, lane);
+    load_vtile4(p, run, bh, nxt, lane, cur);
+    const float alpha = hb.alpha;
+    if (alpha < 1.0f) {
+#pragma unroll
+        for (int P = 0; P < 4; ++P)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) st.O[P][u] *= alpha;
+        st.Z *= alpha;
+    }
+    wave_sync();
+    // ---- p' = p * s_v as fp16 rows (group, hi/lo), as for 2 bits
+    {
+        const int tp = lane & 31, gp = lane >> 5;
+        const uint32_t ph = hb.ph[tp], pq = hb.pq[tp];
+        const uint32_t s0 = L.vsl[(2 * gp) * 32 + tp], s1 = L.vsl[(2 * gp + 1) * 32 + tp];
+        uint32_t h, l;
+        split_prod_hl(ph, pq, s0, h, l);
+        L.pa[(4 * gp) * ASTR + tp] = h;
+        L.pa[(4 * gp + 1) * ASTR + tp] = l;
+        split_prod_hl(ph, pq, s1, h, l);
+        L.pa[(4 * gp + 2) * ASTR + tp] = h;
+        L.pa[(4 * gp + 3) * ASTR + tp] = l;
+    }
+    {
+        const uint32_t* arow = ((n & 1) ? hb.pq : hb.ph) + 4 * kg;
+        const uint32_t* brow = L.vsl + 128 + (n < 5 ? n : 5) * 32 + 4 * kg;
+#pragma unroll
+        for (int ksx = 0; ksx < 2; ++ksx) {
+            const uint4 a = *reinterpret_cast<const uint4*>(arow + 16 * ksx);
+            const uint4 z = *reinterpret_cast<const uint4*>(brow + 16 * ksx);
+            st.Z = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a.x, a.y, a.z, a.w), as_f16x8(z.x, z.y, z.z, z.w),
+                                                          st.Z, 0, 0, 0);
+        }
+    }
+    wave_sync();
+    // ---- O += p' . codes: pass P = value group P, A rows (P, hi/lo) repeated
+#pragma unroll
+    for (int P = 0; P < 4; ++P) {
+        const int row = 2 * P + (n & 1);
+#pragma unroll
+        for (int ksx = 0; ksx < 2; ++ksx) {
+            const uint4 a = *reinterpret_cast<const uint4*>(L.pa + row * ASTR + 16 * ksx + 4 * kg);
+            const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
+            const CodeRegs c = code_operands(ld_tr8(L.vl + value_row_dw4(ksx, P, kg, n)));
+#pragma unroll
+            for (int nib = 0; nib < 2; ++nib)
+                st.O[P][nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x000F000Fu << (4 * nib)),
+                                                                      st.O[P][nib], 0, 0, 0);
+        }
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(128) void k_decode_mha4(MfmaParams p) {
+    __shared__ Lds4 L;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n = lane & 15, kg = lane >> 4;
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    bool tail;
+    const int s = slot_of_block(p, tail);
+    const int64_t bh = int64_t(b) * p.Hkv + kvh;
+    const int64_t slot = (int64_t(b) * p.Hq + kvh) * p.S + s;
+    if (tail) {
+        tail_split<1, 4>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
+        return;
+    }
+    const int t_lo = int(int64_t(s) * p.ntiles / p.S_main);
+    const int t_hi = int(int64_t(s + 1) * p.ntiles / p.S_main);
+    const int ntl = t_hi - t_lo;
+
+    if (wave == 0) {
+        const uint2 qq = reinterpret_cast<const uint2*>(p.q + (int64_t(b) * p.Hq + kvh) * D)[lane >> 1];
+        const uint32_t qw = (lane & 1) ? pair_hi(qq.x, qq.y) : pair_lo(qq.x, qq.y);
+        float m_run = -INFINITY;
+        KTile4 ta, tb;
+        const TileRun run = tile_run4<G>(p, bh, t_lo, t_hi);
+        load_ktile4<G>(p, run, bh, t_lo, lane, ta);
+        load_ktile4<G>(p, run, bh, t_lo + 1, lane, tb);
+        __builtin_amdgcn_sched_barrier(0);
+        key_tile4<G>(p, ta, m_run, L.k, L.hb[0], qw, lane, bh, t_lo + 2, run);
+        __syncthreads();
+        int j = 1;
+        for (; j + 1 < ntl; j += 2) {
+            key_tile4<G>(p, tb, m_run, L.k, L.hb[1], qw, lane, bh, t_lo + j + 2, run);
+            __syncthreads();
+            key_tile4<G>(p, ta, m_run, L.k, L.hb[0], qw, lane, bh, t_lo + j + 3, run);
+            __syncthreads();
+        }
+        if (j < ntl) {
+            key_tile4<G>(p, tb, m_run, L.k, L.hb[1], qw, lane, bh, t_lo + j + 2, run);
+            __syncthreads();
+        }
+        if (lane == 0) L.misc[0] = m_run;
+        __syncthreads();
+    } else {
+        VState4 st;
+        st.Z = f32x4{0.f, 0.f, 0.f, 0.f};
+        L.v.vsl[256 + lane] = lane < 32 ? 0x3c003c00u : 0u;
+#pragma unroll
+        for (int P = 0; P < 4; ++P)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) st.O[P][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        VTile4 ta, tb;
+        const TileRun run = tile_run4<G>(p, bh, t_lo, t_hi);
+        load_vtile4(p, run, bh, t_lo, lane, ta);
+        load_vtile4(p, run, bh, t_lo + 1, lane, tb);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        value_tile4<G>(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + 2, run);
+        __syncthreads();
+        int j = 1;
+        for (; j + 1 < ntl; j += 2) {
+            value_tile4<G>(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
+            __syncthreads();
+            value_tile4<G>(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + j + 3, run);
+            __syncthreads();
+        }
+        if (j < ntl) {
+            value_tile4<G>(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
+            __syncthreads();
+        }
+        const float zsum = st.Z[0] + st.Z[1];
+        const float vz0 = readlane_f(zsum, 0), vz1 = readlane_f(zsum, 1);
+        const float vz2 = readlane_f(zsum, 2), vz3 = readlane_f(zsum, 3);
+        const float lsum = readlane_f(zsum, 4);
+        if (kg == 0) {
+#pragma unroll
+            for (int P = 0; P < 4; ++P)
+#pragma unroll
+                for (int nib = 0; nib < 2; ++nib) {
+                    const int c = 32 * P + 8 * (n >> 2) + 2 * (n & 3) + nib;
+                    const float zb = sel4(P, vz0, vz1, vz2, vz3);
+                    p.ws_acc[slot * D + c] = fmaf(st.O[P][nib][0] + st.O[P][nib][1],
+                                                  __builtin_ldexpf(1.0f, 24 - 4 * nib), zb);
+                }
+        }
+        if (lane == 0) {
+            p.ws_ml[slot * 2] = L.misc[0];
+            p.ws_ml[slot * 2 + 1] = lsum;
+        }
+    }
+}
+
 }  // namespace
 
-bool mha_supported(const kvq_cache& c, int Hq) { return mfma_shape_ok(c) && Hq == c.cfg.n_kv_heads; }
+bool mha_supported(const kvq_cache& c, int Hq) {
+    return (mfma_shape_ok(c) || mfma_cfg_ok4(c.cfg)) && Hq == c.cfg.n_kv_heads;
+}
 
 hipError_t launch_decode_mha(const DecodeArgs& a, hipStream_t st) {
     const MfmaParams p = mfma_params(a);
     const dim3 grid(a.S, a.g.Hkv, a.g.B);
+    if (a.g.kbits == 4) {
+        if (a.g.kG == 64)
+            hipExtLaunchKernelGGL(k_decode_mha4<64>, grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+        else
+            hipExtLaunchKernelGGL(k_decode_mha4<32>, grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+        return hipGetLastError();
+    }
     if (a.g.kG == 64)
         hipExtLaunchKernelGGL(k_decode_mha<64>, grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
     else

@@ -109,6 +109,10 @@ def _shape(shape, T):
         return _tiny(T, Hq=8, Hkv=2, D=128, G=64)
     if shape == "gqa4":
         return _tiny(T, Hq=8, Hkv=2, D=128)
+    if shape == "mha128_4bit_g64":
+        return _tiny(T, Hq=2, Hkv=2, D=128, G=64, kbits=4, vbits=4)
+    if shape == "mha128_4bit_g32":
+        return _tiny(T, Hq=2, Hkv=2, D=128, G=32, kbits=4, vbits=4)
     if shape == "gqa4_4bit_g64":
         return _tiny(T, Hq=8, Hkv=2, D=128, G=64, kbits=4, vbits=4)
     if shape == "gqa4_4bit_g32":
@@ -122,9 +126,11 @@ def _shape(shape, T):
 
 @pytest.mark.parametrize("T", [1, 15, 31, 32, 33, 101, 3 * 64 + 5, 700])
 @pytest.mark.parametrize("shape", ["mha", "mha128_g32", "mha128_g64", "gqa4", "gqa8_g64", "mla", "mla64",
-                                   "mla128", "gqa4_4bit_g64", "gqa4_4bit_g32"])
+                                   "mla128", "gqa4_4bit_g64", "gqa4_4bit_g32", "mha128_4bit_g64",
+                                   "mha128_4bit_g32"])
 def test_edge_lengths(orc, T, shape):
-    if shape in ("mha", "mha128_g32", "mha128_g64", "mla64", "mla128", "gqa4_4bit_g64", "gqa4_4bit_g32"):
+    if shape in ("mha", "mha128_g32", "mha128_g64", "mla64", "mla128", "gqa4_4bit_g64", "gqa4_4bit_g32",
+                 "mha128_4bit_g64", "mha128_4bit_g32"):
         w = _shape(shape, T)
     elif shape == "gqa4":
         w = _tiny(T, Hq=8, Hkv=2, D=128)
@@ -144,7 +150,7 @@ def test_edge_lengths(orc, T, shape):
 
 
 @pytest.mark.parametrize("n_splits", [1, 2, 3, 7, 64, 256])
-@pytest.mark.parametrize("shape", ["gqa4", "mha128_g32", "mla64", "gqa4_4bit_g64", "gqa4_4bit_g32"])
+@pytest.mark.parametrize("shape", ["gqa4", "mha128_g32", "mla64", "gqa4_4bit_g64", "gqa4_4bit_g32", "mha128_4bit_g32"])
 def test_split_counts(orc, n_splits, shape):
     w = _tiny(1000, Hq=8, Hkv=2, D=128, G=32) if shape == "gqa4" else _shape(shape, 1000)
     cap = w.capacity()
@@ -326,13 +332,13 @@ def test_random_bit_pattern_fuzz(orc):
 
 
 @pytest.mark.parametrize("shape", ["gqa4_g64", "gqa4", "mha128_g32", "mha128_g64", "mha", "mla64", "gqa4_4bit_g64",
-                                   "gqa4_4bit_g32"])
+                                   "gqa4_4bit_g32", "mha128_4bit_g64", "mha128_4bit_g32"])
 def test_decode_step_matches_separate_calls(orc, shape):
     """kv_decode_step (append fused into the attention launch for the GQA and
     MHA kernels while no block completes) against kv_quantize_append +
     kv_decode_attention: caches and outputs bit-identical over steps that
     cross key-block boundaries, starting from an empty cache."""
-    G = 64 if shape in ("gqa4_g64", "mha128_g64", "mla64", "gqa4_4bit_g64") else 32
+    G = 64 if shape in ("gqa4_g64", "mha128_g64", "mla64", "gqa4_4bit_g64", "mha128_4bit_g64") else 32
     n0 = 2 * G - 3
     steps = G + 6
     w = _shape(shape, n0 + steps)
