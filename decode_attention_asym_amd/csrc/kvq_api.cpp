@@ -357,7 +357,9 @@ kvq_status kv_paged_decode(const kvq_paged* c, const void* q, int32_t Hq, float 
     a.ev_start = g_ev_before;
     a.ev_stop = g_ev_after;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const hipError_t e = v == V_GQA ? launch_decode_gqa_paged(a, st) : launch_decode_generic_paged(a, st);
+    const hipError_t e = v == V_GQA   ? launch_decode_gqa_paged(a, st)
+                         : v == V_MHA ? launch_decode_mha_paged(a, st)
+                                      : launch_decode_generic_paged(a, st);
     if (e != hipSuccess) return KVQ_E_HIP;
     return hip_status(launch_merge(a, st));
 }

@@ -311,16 +311,6 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
     }
 }
 
-// the code-tile run of a main split: contiguous (one buffer resource per
-// run) or paged (per-tile resources over the pages of the block table,
-// loaded at the kernel's start)
-template <int G, bool PAGED>
-__device__ __forceinline__ auto pick_run(const MfmaParams& p, const PagedRun& prun, int64_t bh, int t_lo, int t_hi) {
-    if constexpr (PAGED)
-        return prun;
-    else
-        return tile_run<G>(p, bh, t_lo, t_hi);
-}
 
 template <int G, bool PAGED>
 __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {

@@ -59,10 +59,10 @@ struct Lds {
 // Key side of one tile: produces p and alpha in `hb`.  m_run is the running
 // maximum (log2 units, wave-uniform); qw holds query channels
 // 4(lane >> 1) + (lane & 1) and that + 2 (fp16, quad order).
-template <int G>
+template <int G, class Run>
 __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, float& m_run, LdsK& L,
                                          Handoff& hb, uint32_t qw, int lane,
-                                         int64_t bh, int nxt, const TileRun& run) {
+                                         int64_t bh, int nxt, const Run& run) {
     constexpr int NBT = 64 / G;
     const int n = lane & 15, kg = lane >> 4;
 
@@ -165,13 +165,14 @@ struct VState {
 };
 
 // Value side of one tile, reading p and alpha from `hb`.
+template <int G, class Run>
 __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VState& st, LdsV& L,
                                            const Handoff& hb, int lane, int64_t bh,
-                                           int nxt, const TileRun& run) {
+                                           int nxt, const Run& run) {
     const int n = lane & 15, kg = lane >> 4;
     // ---- stage value codes and side values, then prefetch tile i + 2
     stage_values(cur, L.vl, L.vsl, lane);
-    load_vtile(p, run, bh, nxt, lane, cur);
+    load_vtile<G>(p, run, bh, nxt, lane, cur);
 
     // ---- rescale what was accumulated with the previous maximum
     const float alpha = hb.alpha;
@@ -233,7 +234,7 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
     }
 }
 
-template <int G>
+template <int G, bool PAGED>
 __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
     __shared__ Lds L;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -243,12 +244,34 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
     const int s = slot_of_block(p, tail);
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int64_t slot = (int64_t(b) * p.Hq + kvh) * p.S + s;
-    if (tail) {
-        tail_split<1>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
-        return;
+    // paged: the sequence's own length, fixed-size splits (as in the GQA kernel)
+    int t_lo, t_hi;
+    [[maybe_unused]] PagedRun prun;
+    if constexpr (PAGED) {
+        if (tail) {
+            const int len = seq_len(p, b);
+            const int64_t nblk = len / G;
+            tail_split<1>(p, PagedBlocks{}, b, kvh, s, reinterpret_cast<float*>(L.k.qa),
+                          reinterpret_cast<float*>(L.v.pa), len, nblk, int(nblk * G / 64));
+            return;
+        }
+        t_lo = s * p.chunk;
+        prun = paged_run<G>(p, b, kvh, t_lo, lane);
+        const int ntiles = seq_len(p, b) / G * G / 64;
+        t_hi = t_lo + p.chunk < ntiles ? t_lo + p.chunk : ntiles;
+        if (t_lo >= t_hi) {
+            empty_partial<1>(p, b, kvh, s);
+            return;
+        }
+        prun.t_last = t_hi - 1;
+    } else {
+        if (tail) {
+            tail_split<1>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
+            return;
+        }
+        t_lo = int(int64_t(s) * p.ntiles / p.S_main);
+        t_hi = int(int64_t(s + 1) * p.ntiles / p.S_main);
     }
-    const int t_lo = int(int64_t(s) * p.ntiles / p.S_main);
-    const int t_hi = int(int64_t(s + 1) * p.ntiles / p.S_main);
     const int ntl = t_hi - t_lo;
 
     if (wave == 0) {
@@ -257,7 +280,7 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
         const uint32_t qw = (lane & 1) ? pair_hi(qq.x, qq.y) : pair_lo(qq.x, qq.y);
         float m_run = -INFINITY;
         KTile ta, tb;
-        const TileRun run = tile_run<G>(p, bh, t_lo, t_hi);
+        const auto run = pick_run<G, PAGED>(p, prun, bh, t_lo, t_hi);
         load_ktile<G>(p, run, bh, t_lo, lane, ta);
         load_ktile<G>(p, run, bh, t_lo + 1, lane, tb);
         // keep these loads ahead of (not interleaved with) the prefetch of tile 2
@@ -293,22 +316,22 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
             for (int u = 0; u < 4; ++u) st.O[P][u] = f32x4{0.f, 0.f, 0.f, 0.f};
         // value work trails the key work by one tile: tile j after barrier j
         VTile ta, tb;
-        const TileRun run = tile_run<G>(p, bh, t_lo, t_hi);
-        load_vtile(p, run, bh, t_lo, lane, ta);
-        load_vtile(p, run, bh, t_lo + 1, lane, tb);
+        const auto run = pick_run<G, PAGED>(p, prun, bh, t_lo, t_hi);
+        load_vtile<G>(p, run, bh, t_lo, lane, ta);
+        load_vtile<G>(p, run, bh, t_lo + 1, lane, tb);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        value_tile(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + 2, run);
+        value_tile<G>(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + 2, run);
         __syncthreads();
         int j = 1;
         for (; j + 1 < ntl; j += 2) {
-            value_tile(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
+            value_tile<G>(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
             __syncthreads();
-            value_tile(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + j + 3, run);
+            value_tile<G>(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + j + 3, run);
             __syncthreads();
         }
         if (j < ntl) {
-            value_tile(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
+            value_tile<G>(p, tb, st, L.v, L.hb[1], lane, bh, t_lo + j + 2, run);
             __syncthreads();
         }
         // ---- epilogue: l and the value-zero sums (hi + lo rows; lanes 0..3
@@ -602,9 +625,21 @@ hipError_t launch_decode_mha(const DecodeArgs& a, hipStream_t st) {
         return hipGetLastError();
     }
     if (a.g.kG == 64)
-        hipExtLaunchKernelGGL(k_decode_mha<64>, grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+        hipExtLaunchKernelGGL((k_decode_mha<64, false>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
     else
-        hipExtLaunchKernelGGL(k_decode_mha<32>, grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+        hipExtLaunchKernelGGL((k_decode_mha<32, false>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+    return hipGetLastError();
+}
+
+bool mha_cfg_supported(const kvq_cache_cfg& c, int Hq) { return mfma_cfg_ok(c) && Hq == c.n_kv_heads; }
+
+hipError_t launch_decode_mha_paged(const DecodeArgs& a, hipStream_t st) {
+    const MfmaParams p = mfma_params(a);
+    const dim3 grid(a.S, a.g.Hkv, a.g.B);
+    if (a.g.kG == 64)
+        hipExtLaunchKernelGGL((k_decode_mha<64, true>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+    else
+        hipExtLaunchKernelGGL((k_decode_mha<32, true>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
     return hipGetLastError();
 }
 

@@ -141,6 +141,8 @@ struct PagedPlan {
 };
 PagedPlan plan_paged(const kvq_paged& c, int Hq, int n_splits, int max_len, Variant v);
 hipError_t launch_decode_gqa_paged(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_mha_paged(const DecodeArgs& a, hipStream_t st);
+bool mha_cfg_supported(const kvq_cache_cfg& c, int Hq);
 hipError_t launch_decode_generic_paged(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace kvq

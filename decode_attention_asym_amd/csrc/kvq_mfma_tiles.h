@@ -547,6 +547,17 @@ __device__ __forceinline__ void load_vtile(const MfmaParams& p, const PagedRun& 
     r.vs = make_uint4(a.x, a.y, b.x, b.y);
 }
 
+// the code-tile run of a main split: contiguous (one buffer resource per
+// run) or paged (per-tile resources over the pages of the block table,
+// loaded at the kernel's start)
+template <int G, bool PAGED>
+__device__ __forceinline__ auto pick_run(const MfmaParams& p, const PagedRun& prun, int64_t bh, int t_lo, int t_hi) {
+    if constexpr (PAGED)
+        return prun;
+    else
+        return tile_run<G>(p, bh, t_lo, t_hi);
+}
+
 // contiguous runs, same call shape as the paged overload
 template <int G>
 __device__ __forceinline__ void load_vtile(const MfmaParams& p, const TileRun& run, int64_t bh, int tt, int lane,

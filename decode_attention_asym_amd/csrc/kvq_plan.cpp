@@ -85,11 +85,13 @@ SplitPlan plan_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64
 PagedPlan plan_paged(const kvq_paged& c, int Hq, int n_splits, int max_len, Variant v) {
     const int64_t G = c.cfg.key.group;
     PagedPlan pp;
-    if (v == V_GQA) {
+    if (v == V_GQA || v == V_MHA) {
         const int64_t ntiles = int64_t(max_len) / G * G / 64;
         const int64_t units = int64_t(c.cfg.batch) * c.cfg.n_kv_heads;
-        // as for a contiguous cache: fill the GPU, runs of at least 16 tiles
-        const int64_t fill = (3072 + units - 1) / units, runs = (ntiles + 15) / 16;
+        // as for a contiguous cache: fill the GPU, runs of at least 16 (GQA)
+        // / 8 (MHA) tiles
+        const int64_t target = v == V_MHA ? 1536 : 3072, min_run = v == V_MHA ? 8 : 16;
+        const int64_t fill = (target + units - 1) / units, runs = (ntiles + min_run - 1) / min_run;
         const int64_t want = n_splits > 0 ? n_splits : clamp64(fill < runs ? fill : runs, 1, KVQ_MAX_SPLITS - 1);
         int64_t chunk = ntiles > 0 ? (ntiles + want - 1) / want : 1;
         // the page numbers of a run sit one per lane: at most 64 key blocks
@@ -111,13 +113,17 @@ PagedPlan plan_paged(const kvq_paged& c, int Hq, int n_splits, int max_len, Vari
 }
 
 Variant pick_paged_variant(const kvq_paged& c, int Hq, int n_splits, int max_len) {
-    // the MFMA kernel while its main splits fit the merge's slot limit
+    // the MFMA kernels while their main splits fit the merge's slot limit
     if (gqa_cfg_supported(c.cfg, Hq) && plan_paged(c, Hq, n_splits, max_len, V_GQA).S <= KVQ_MAX_SPLITS)
         return V_GQA;
+    if (mha_cfg_supported(c.cfg, Hq) && plan_paged(c, Hq, n_splits, max_len, V_MHA).S <= KVQ_MAX_SPLITS)
+        return V_MHA;
     return V_GENERIC;
 }
 
-const char* paged_variant_name(Variant v) { return v == V_GQA ? "gqa_mfma_paged" : "generic_paged"; }
+const char* paged_variant_name(Variant v) {
+    return v == V_GQA ? "gqa_mfma_paged" : v == V_MHA ? "mha_mfma_paged" : "generic_paged";
+}
 
 int max_slots(const kvq_cache& c, int Hq, int n_splits, Variant v) {
     const int64_t want = n_splits > 0 ? n_splits : auto_main(c, Hq, v, c.cfg.max_tokens / 64);

@@ -284,6 +284,7 @@ def test_paged_variant_choice():
         assert kvq.kv_paged_variant(gqa, 8, 1 << 20) == "generic_paged"
         assert kvq.kv_paged_variant(gqa, 16, 4096) == "generic_paged"   # 8 q heads per KV head
         assert kvq.kv_paged_variant(d64, 8, 256) == "generic_paged"
+        assert kvq.kv_paged_variant(gqa, 2, 4096) == "mha_mfma_paged"    # one query head per KV head
         assert kvq.kv_paged_variant(mla, 16, 1024) == "generic_paged"
         assert kvq.kv_paged_variant(gqa, 8, -1) == "invalid"
     finally:
