@@ -383,9 +383,9 @@ struct Lds4 {
     float misc[4];
 };
 
-template <int G>
+template <int G, class Run>
 __device__ __forceinline__ void key_tile4(const MfmaParams& p, KTile4& cur, float& m_run, LdsK4& L, Handoff& hb,
-                                          uint32_t qw, int lane, int64_t bh, int nxt, const TileRun& run) {
+                                          uint32_t qw, int lane, int64_t bh, int nxt, const Run& run) {
     constexpr int NBT = 64 / G;
     const int n = lane & 15, kg = lane >> 4;
     stage_keys4<G>(cur, L.kl, L.ksl, lane);
@@ -460,12 +460,12 @@ struct VState4 {
     f32x4 Z;
 };
 
-template <int G>
+template <int G, class Run>
 __device__ __forceinline__ void value_tile4(const MfmaParams& p, VTile4& cur, VState4& st, LdsV4& L, const Handoff& hb,
-                                            int lane, int64_t bh, int nxt, const TileRun& run) {
+                                            int lane, int64_t bh, int nxt, const Run& run) {
     const int n = lane & 15, kg = lane >> 4;
     stage_values4(cur, L.vl, L.vsl, lane);
-    load_vtile4(p, run, bh, nxt, lane, cur);
+    load_vtile4<G>(p, run, bh, nxt, lane, cur);
     const float alpha = hb.alpha;
     if (alpha < 1.0f) {
 #pragma unroll
@@ -517,7 +517,7 @@ __device__ __forceinline__ void value_tile4(const MfmaParams& p, VTile4& cur, VS
     }
 }
 
-template <int G>
+template <int G, bool PAGED>
 __global__ __launch_bounds__(128) void k_decode_mha4(MfmaParams p) {
     __shared__ Lds4 L;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -527,12 +527,33 @@ __global__ __launch_bounds__(128) void k_decode_mha4(MfmaParams p) {
     const int s = slot_of_block(p, tail);
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int64_t slot = (int64_t(b) * p.Hq + kvh) * p.S + s;
-    if (tail) {
-        tail_split<1, 4>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
-        return;
+    int t_lo, t_hi;
+    [[maybe_unused]] PagedRun prun;
+    if constexpr (PAGED) {
+        if (tail) {
+            const int len = seq_len(p, b);
+            const int64_t nblk = len / G;
+            tail_split<1, PagedBlocks, 4>(p, PagedBlocks{}, b, kvh, s, reinterpret_cast<float*>(L.k.qa),
+                                         reinterpret_cast<float*>(L.v.pa), len, nblk, int(nblk * G / 64));
+            return;
+        }
+        t_lo = s * p.chunk;
+        prun = paged_run<G>(p, b, kvh, t_lo, lane);
+        const int ntiles = seq_len(p, b) / G * G / 64;
+        t_hi = t_lo + p.chunk < ntiles ? t_lo + p.chunk : ntiles;
+        if (t_lo >= t_hi) {
+            empty_partial<1>(p, b, kvh, s);
+            return;
+        }
+        prun.t_last = t_hi - 1;
+    } else {
+        if (tail) {
+            tail_split<1, 4>(p, b, kvh, s, reinterpret_cast<float*>(L.k.qa), reinterpret_cast<float*>(L.v.pa));
+            return;
+        }
+        t_lo = int(int64_t(s) * p.ntiles / p.S_main);
+        t_hi = int(int64_t(s + 1) * p.ntiles / p.S_main);
     }
-    const int t_lo = int(int64_t(s) * p.ntiles / p.S_main);
-    const int t_hi = int(int64_t(s + 1) * p.ntiles / p.S_main);
     const int ntl = t_hi - t_lo;
 
     if (wave == 0) {
@@ -540,7 +561,7 @@ __global__ __launch_bounds__(128) void k_decode_mha4(MfmaParams p) {
         const uint32_t qw = (lane & 1) ? pair_hi(qq.x, qq.y) : pair_lo(qq.x, qq.y);
         float m_run = -INFINITY;
         KTile4 ta, tb;
-        const TileRun run = tile_run4<G>(p, bh, t_lo, t_hi);
+        const auto run = pick_run4<G, PAGED>(p, prun, bh, t_lo, t_hi);
         load_ktile4<G>(p, run, bh, t_lo, lane, ta);
         load_ktile4<G>(p, run, bh, t_lo + 1, lane, tb);
         __builtin_amdgcn_sched_barrier(0);
@@ -568,9 +589,9 @@ __global__ __launch_bounds__(128) void k_decode_mha4(MfmaParams p) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) st.O[P][u] = f32x4{0.f, 0.f, 0.f, 0.f};
         VTile4 ta, tb;
-        const TileRun run = tile_run4<G>(p, bh, t_lo, t_hi);
-        load_vtile4(p, run, bh, t_lo, lane, ta);
-        load_vtile4(p, run, bh, t_lo + 1, lane, tb);
+        const auto run = pick_run4<G, PAGED>(p, prun, bh, t_lo, t_hi);
+        load_vtile4<G>(p, run, bh, t_lo, lane, ta);
+        load_vtile4<G>(p, run, bh, t_lo + 1, lane, tb);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         value_tile4<G>(p, ta, st, L.v, L.hb[0], lane, bh, t_lo + 2, run);
@@ -619,9 +640,9 @@ hipError_t launch_decode_mha(const DecodeArgs& a, hipStream_t st) {
     const dim3 grid(a.S, a.g.Hkv, a.g.B);
     if (a.g.kbits == 4) {
         if (a.g.kG == 64)
-            hipExtLaunchKernelGGL(k_decode_mha4<64>, grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+            hipExtLaunchKernelGGL((k_decode_mha4<64, false>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
         else
-            hipExtLaunchKernelGGL(k_decode_mha4<32>, grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+            hipExtLaunchKernelGGL((k_decode_mha4<32, false>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
         return hipGetLastError();
     }
     if (a.g.kG == 64)
@@ -631,11 +652,18 @@ hipError_t launch_decode_mha(const DecodeArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-bool mha_cfg_supported(const kvq_cache_cfg& c, int Hq) { return mfma_cfg_ok(c) && Hq == c.n_kv_heads; }
+bool mha_cfg_supported(const kvq_cache_cfg& c, int Hq) { return (mfma_cfg_ok(c) || mfma_cfg_ok4(c)) && Hq == c.n_kv_heads; }
 
 hipError_t launch_decode_mha_paged(const DecodeArgs& a, hipStream_t st) {
     const MfmaParams p = mfma_params(a);
     const dim3 grid(a.S, a.g.Hkv, a.g.B);
+    if (a.g.kbits == 4) {
+        if (a.g.kG == 64)
+            hipExtLaunchKernelGGL((k_decode_mha4<64, true>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+        else
+            hipExtLaunchKernelGGL((k_decode_mha4<32, true>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
+        return hipGetLastError();
+    }
     if (a.g.kG == 64)
         hipExtLaunchKernelGGL((k_decode_mha<64, true>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
     else

@@ -558,6 +558,76 @@ __device__ __forceinline__ auto pick_run(const MfmaParams& p, const PagedRun& pr
         return tile_run<G>(p, bh, t_lo, t_hi);
 }
 
+// 4-bit tiles over pages: G = 64, one 4 KB page block per tile; G = 32, two
+// 2 KB blocks (tokens 0..31, 32..63), as the contiguous layout splits them
+template <int G>
+__device__ __forceinline__ void load_ktile4(const MfmaParams& p, const PagedRun& run, int64_t, int tt, int lane,
+                                            KTile4& r) {
+    constexpr int W = G / 8;
+    const bool in = tt <= run.t_last;
+    const int64_t ra = paged_row<G>(p, run, tt, 0);
+    const uint16_t* side = lane < 32 ? p.ks : p.kz;
+    if (G == 64) {
+        const __amdgpu_buffer_rsrc_t rs = page_rsrc(p.kc + ra * D * W, in ? 4096 : 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r.k[q] = ld_run(rs, 16 * lane + 1024 * q);
+        const uint2 v = ld_stream(reinterpret_cast<const uint2*>(side + ra * D) + (lane & 31));
+        r.ks = make_uint4(v.x, v.y, 0u, 0u);
+    } else {
+        const int64_t rb = paged_row<G>(p, run, tt, 1);
+        const __amdgpu_buffer_rsrc_t rsa = page_rsrc(p.kc + ra * D * W, in ? 2048 : 0);
+        const __amdgpu_buffer_rsrc_t rsb = page_rsrc(p.kc + rb * D * W, in ? 2048 : 0);
+        r.k[0] = ld_run(rsa, 16 * lane);
+        r.k[1] = ld_run(rsa, 16 * lane + 1024);
+        r.k[2] = ld_run(rsb, 16 * lane);
+        r.k[3] = ld_run(rsb, 16 * lane + 1024);
+        r.ks = ld_stream(reinterpret_cast<const uint4*>(side + ((lane & 16) ? rb : ra) * D) + (lane & 15));
+    }
+}
+
+template <int G>
+__device__ __forceinline__ void load_vtile4(const MfmaParams& p, const PagedRun& run, int64_t, int tt, int lane,
+                                            VTile4& r) {
+    const bool in = tt <= run.t_last;
+    const int64_t ra = paged_row<G>(p, run, tt, 0);
+    const int t = 4 * ((lane & 31) >> 1) + (lane & 1);
+    int64_t vrow;
+    if (G == 64) {
+        const __amdgpu_buffer_rsrc_t rs = page_rsrc(p.vc + ra * 64 * 16, in ? 4096 : 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r.v[q] = ld_run(rs, 16 * lane + 1024 * q);
+        vrow = ra * 64 + t;
+    } else {
+        const int64_t rb = paged_row<G>(p, run, tt, 1);
+        const __amdgpu_buffer_rsrc_t rsa = page_rsrc(p.vc + ra * 32 * 16, in ? 2048 : 0);
+        const __amdgpu_buffer_rsrc_t rsb = page_rsrc(p.vc + rb * 32 * 16, in ? 2048 : 0);
+        r.v[0] = ld_run(rsa, 16 * lane);
+        r.v[1] = ld_run(rsa, 16 * lane + 1024);
+        r.v[2] = ld_run(rsb, 16 * lane);
+        r.v[3] = ld_run(rsb, 16 * lane + 1024);
+        vrow = t < 32 ? ra * 32 + t : rb * 32 + (t - 32);
+    }
+    const uint16_t* vside = (lane < 32 ? p.vs : p.vz) + vrow * 4;
+    const uint2 a = ld_stream(reinterpret_cast<const uint2*>(vside));
+    const uint2 b = ld_stream(reinterpret_cast<const uint2*>(vside + 8));
+    r.vs = make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// 4-bit runs: contiguous or paged
+template <int G, bool PAGED>
+__device__ __forceinline__ auto pick_run4(const MfmaParams& p, const PagedRun& prun, int64_t bh, int t_lo, int t_hi) {
+    if constexpr (PAGED)
+        return prun;
+    else
+        return tile_run4<G>(p, bh, t_lo, t_hi);
+}
+// the contiguous value loader with the paged overload's call shape
+template <int G>
+__device__ __forceinline__ void load_vtile4(const MfmaParams& p, const TileRun& run, int64_t bh, int tt, int lane,
+                                            VTile4& r) {
+    load_vtile4(p, run, bh, tt, lane, r);
+}
+
 // contiguous runs, same call shape as the paged overload
 template <int G>
 __device__ __forceinline__ void load_vtile(const MfmaParams& p, const TileRun& run, int64_t bh, int tt, int lane,

@@ -285,6 +285,12 @@ def test_paged_variant_choice():
         assert kvq.kv_paged_variant(gqa, 16, 4096) == "generic_paged"   # 8 q heads per KV head
         assert kvq.kv_paged_variant(d64, 8, 256) == "generic_paged"
         assert kvq.kv_paged_variant(gqa, 2, 4096) == "mha_mfma_paged"    # one query head per KV head
+        g4 = _paged(kivi_cfg(batch=4, n_kv_heads=2, max_tokens=8192, kG=64, kbits=4, vbits=4), 64)
+        try:
+            assert kvq.kv_paged_variant(g4, 8, 4096) == "gqa_mfma_paged"
+            assert kvq.kv_paged_variant(g4, 2, 4096) == "mha_mfma_paged"
+        finally:
+            kvq.kv_paged_destroy(g4)
         assert kvq.kv_paged_variant(mla, 16, 1024) == "generic_paged"
         assert kvq.kv_paged_variant(gqa, 8, -1) == "invalid"
     finally:

@@ -28,6 +28,9 @@ def _workload(shape, T):
         "mha_d64": (5, 2, 2, 64, 32, 2, 2),
         "mha_d128": (4, 2, 2, 128, 64, 2, 2),
         "mha_d128_g32": (4, 2, 2, 128, 32, 2, 2),
+        "gqa4_4bit_g64": (6, 8, 2, 128, 64, 4, 4),
+        "gqa4_4bit_g32": (6, 8, 2, 128, 32, 4, 4),
+        "mha_d128_4bit": (4, 2, 2, 128, 64, 4, 4),
         "kv4bit": (4, 4, 2, 64, 32, 4, 4),
         "d32_g64": (3, 2, 2, 32, 64, 2, 2),
     }[shape]
@@ -153,7 +156,7 @@ def _check_decode(orc, pg, k_full, v_full, q, got, seqs=None):
 
 
 @pytest.mark.parametrize("shape", ["gqa4_g64", "gqa4_g32", "mha_d64", "mha_d128", "mha_d128_g32", "kv4bit", "mla",
-                                   "d32_g64"])
+                                   "d32_g64", "gqa4_4bit_g64", "gqa4_4bit_g32", "mha_d128_4bit"])
 def test_paged_ragged_append_and_decode(orc, shape):
     w = _workload(shape, 700)
     final = _final_lengths(w)
