@@ -364,6 +364,48 @@ kvq_status kv_paged_decode(const kvq_paged* c, const void* q, int32_t Hq, float 
     return hip_status(launch_merge(a, st));
 }
 
+kvq_status kv_paged_decode_step(kvq_paged* c, const void* k, const void* v, const void* q, int32_t Hq, float sigma,
+                                const int32_t* n_new, int32_t* seq_lens, const int32_t* block_table, int32_t max_len,
+                                int32_t n_splits, uint32_t flags, void* out, void* ws, uint64_t ws_bytes,
+                                void* stream) {
+    if (!c || !k || !v || !q || !out || !ws || !seq_lens || !block_table) return KVQ_E_NULL;
+    if (flags & ~KVQ_STEP_ADVANCE_LENGTHS) return KVQ_E_SHAPE;
+    if (Hq < 1 || Hq % c->cfg.n_kv_heads != 0) return KVQ_E_SHAPE;
+    if (n_splits < 0 || n_splits > KVQ_MAX_SPLITS) return KVQ_E_SHAPE;
+    if (max_len < 1 || max_len > c->cfg.max_tokens) return KVQ_E_SHAPE;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(out) || !aligned16(ws)) return KVQ_E_ALIGN;
+    if (!aligned4(seq_lens) || !aligned4(block_table) || !aligned4(n_new)) return KVQ_E_ALIGN;
+    const Variant v_ = pick_paged_variant(*c, Hq, n_splits, max_len);
+    if (v_ != V_GQA && v_ != V_MHA) return KVQ_E_UNSUPPORTED;
+    const PagedPlan pp = plan_paged(*c, Hq, n_splits, max_len, v_);
+    DecodeArgs a{};
+    a.pc = c;
+    a.g = geom_of(c->cfg);
+    a.q = q;
+    a.Hq = Hq;
+    a.sigma = sigma;
+    a.out = out;
+    a.S = pp.S;
+    a.S_main = pp.S_main;
+    a.chunk = pp.chunk;
+    a.max_len = max_len;
+    a.ps = paged_seq(*c, block_table, seq_lens, n_new);
+    const uint64_t need = uint64_t(a.g.B) * Hq * a.S * (a.g.vd + 2) * 4;
+    if (ws_bytes < need) return KVQ_E_WORKSPACE;
+    a.ws_acc = static_cast<float*>(ws);
+    a.ws_ml = a.ws_acc + uint64_t(a.g.B) * Hq * a.S * a.g.vd;
+    a.ev_start = g_ev_before;
+    a.ev_stop = g_ev_after;
+    a.k_new = k;
+    a.v_new = v;
+    a.fuse = 1;
+    a.lens_adv = (flags & KVQ_STEP_ADVANCE_LENGTHS) ? seq_lens : nullptr;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e = v_ == V_GQA ? launch_decode_gqa_paged(a, st) : launch_decode_mha_paged(a, st);
+    if (e != hipSuccess) return KVQ_E_HIP;
+    return hip_status(launch_merge(a, st));
+}
+
 const char* kv_paged_variant(const kvq_paged* c, int32_t Hq, int32_t max_len) {
     if (!c || Hq < 1 || Hq % c->cfg.n_kv_heads != 0 || max_len < 0 || max_len > c->cfg.max_tokens)
         return "invalid";

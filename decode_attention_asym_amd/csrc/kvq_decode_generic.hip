@@ -161,14 +161,30 @@ __global__ __launch_bounds__(256) void k_decode_generic(GenParams p) {
 // o = sum_s acc_s 2^{m_s - m} / L.  Empty slots (m_s = -inf, l_s = 0, from
 // splits past a short paged sequence) weigh 0; a sequence with no tokens
 // gets o = 0.
+// The paged decode step's length advance, after every pass-1 workgroup has
+// read the lengths: sequence b gains the row the step appended to it (the
+// validity rule of the kernels' paged_step_len).
+struct MergeAdvance {
+    int32_t* lens;             // null: nothing to advance
+    const int32_t* n_new;      // rows per sequence (0 or 1), null = 1
+    int Hq;
+    int64_t lim;               // min(capacity, max_len)
+};
+
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ ws_acc,
                                                const float* __restrict__ ws_ml, int S, int vd,
-                                               uint16_t* __restrict__ out) {
+                                               uint16_t* __restrict__ out, MergeAdvance adv) {
     __shared__ float wsh[KVQ_MAX_SPLITS];
     __shared__ float red[4];
     __shared__ float tot[2];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t pair = blockIdx.x;
+    if (adv.lens && tid == 0 && pair % adv.Hq == 0) {
+        const int64_t b = pair / adv.Hq;
+        const int raw = adv.lens[b];
+        const int nn = adv.n_new ? adv.n_new[b] : 1;
+        if (raw >= 0 && (nn == 0 || nn == 1) && int64_t(raw) + nn <= adv.lim) adv.lens[b] = raw + nn;
+    }
     const float* ml = ws_ml + pair * S * 2;
     const float mi = tid < S ? ml[tid * 2] : -INFINITY;
     const float wm = wave_max(mi);
@@ -287,8 +303,14 @@ hipError_t launch_decode_generic_paged(const DecodeArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t st) {
+    MergeAdvance adv;
+    adv.lens = a.lens_adv;
+    adv.n_new = a.ps.n_new;
+    adv.Hq = a.Hq;
+    const int64_t cap = int64_t(a.ps.maxb) * a.g.kG;
+    adv.lim = cap < a.max_len ? cap : a.max_len;
     hipLaunchKernelGGL(k_merge, dim3(a.g.B * a.Hq), dim3(256), 0, st, a.ws_acc, a.ws_ml, a.S,
-                       a.g.vd, static_cast<uint16_t*>(a.out));
+                       a.g.vd, static_cast<uint16_t*>(a.out), adv);
     return hipGetLastError();
 }
 

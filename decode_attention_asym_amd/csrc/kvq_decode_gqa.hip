@@ -330,16 +330,20 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
     int t_lo, t_hi;
     [[maybe_unused]] PagedRun prun;
     if constexpr (PAGED) {
+        // the step's fused append (if any) adds token len0; main splits cover the
+        // tiles complete before it, the tail everything after them
+        int len0, n_app;
+        paged_step_len(p, b, G, len0, n_app);
+        const int ntiles = len0 / G * G / 64;
         if (tail) {
-            const int len = seq_len(p, b);
-            const int64_t nblk = len / G;
+            if (n_app) fused_append_paged<G, 2>(p, b, kvh, len0);
+            const int T1 = len0 + n_app;
             tail_split<HG>(p, PagedBlocks{}, b, kvh, s, reinterpret_cast<float*>(L.k.qa),
-                           reinterpret_cast<float*>(L.v.pa), len, nblk, int(nblk * G / 64));
+                               reinterpret_cast<float*>(L.v.pa), T1, T1 / G, ntiles);
             return;
         }
         t_lo = s * p.chunk;
         prun = paged_run<G>(p, b, kvh, t_lo, lane);
-        const int ntiles = seq_len(p, b) / G * G / 64;
         t_hi = t_lo + p.chunk < ntiles ? t_lo + p.chunk : ntiles;
         if (t_lo >= t_hi) {
             empty_partial<HG>(p, b, kvh, s);
@@ -686,16 +690,20 @@ __global__ __launch_bounds__(128) void k_decode_gqa4(MfmaParams p) {
     int t_lo, t_hi;
     [[maybe_unused]] PagedRun prun;
     if constexpr (PAGED) {
+        // the step's fused append (if any) adds token len0; main splits cover the
+        // tiles complete before it, the tail everything after them
+        int len0, n_app;
+        paged_step_len(p, b, G, len0, n_app);
+        const int ntiles = len0 / G * G / 64;
         if (tail) {
-            const int len = seq_len(p, b);
-            const int64_t nblk = len / G;
+            if (n_app) fused_append_paged<G, 4>(p, b, kvh, len0);
+            const int T1 = len0 + n_app;
             tail_split<HG, PagedBlocks, 4>(p, PagedBlocks{}, b, kvh, s, reinterpret_cast<float*>(L.k.qa),
-                                         reinterpret_cast<float*>(L.v.pa), len, nblk, int(nblk * G / 64));
+                               reinterpret_cast<float*>(L.v.pa), T1, T1 / G, ntiles);
             return;
         }
         t_lo = s * p.chunk;
         prun = paged_run<G>(p, b, kvh, t_lo, lane);
-        const int ntiles = seq_len(p, b) / G * G / 64;
         t_hi = t_lo + p.chunk < ntiles ? t_lo + p.chunk : ntiles;
         if (t_lo >= t_hi) {
             empty_partial<HG>(p, b, kvh, s);

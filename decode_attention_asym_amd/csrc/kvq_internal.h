@@ -109,6 +109,8 @@ struct DecodeArgs {
     // workgroup stores before attending
     const void *k_new, *v_new;
     int fuse;
+    // paged decode step: lengths to advance in the merge launch (null = no)
+    int32_t* lens_adv;
 };
 
 Variant pick_variant(const kvq_cache& c, int Hq);

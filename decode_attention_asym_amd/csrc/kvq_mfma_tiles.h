@@ -61,10 +61,13 @@ struct MfmaParams {
     // [0, max_len]), pool size, tiles per main split
     const int32_t *table, *lens;
     int maxb, npages, chunk, max_len;
-    // fused append of token T - 1 (see fused_append)
+    // fused append of token T - 1 (see fused_append), or for a paged cache
+    // of token lens[b] of each sequence (fused_append_paged; n_new: rows per
+    // sequence, 0 or 1, null = 1)
     const uint16_t *k_new, *v_new;
-    uint32_t* vc_w;
-    uint16_t *vs_w, *vz_w, *kr_w;
+    uint32_t *vc_w, *kc_w;
+    uint16_t *vs_w, *vz_w, *kr_w, *ks_w, *kz_w;
+    const int32_t* n_new;
     int fuse;
 };
 
@@ -105,6 +108,10 @@ inline MfmaParams mfma_params(const DecodeArgs& a) {
     p.vs_w = static_cast<uint16_t*>(buf.v_scale);
     p.vz_w = static_cast<uint16_t*>(buf.v_zero);
     p.kr_w = static_cast<uint16_t*>(buf.k_resid);
+    p.kc_w = static_cast<uint32_t*>(buf.k_codes);
+    p.ks_w = static_cast<uint16_t*>(buf.k_scale);
+    p.kz_w = static_cast<uint16_t*>(buf.k_zero);
+    p.n_new = a.ps.n_new;
     p.fuse = a.fuse;
     return p;
 }
@@ -788,10 +795,13 @@ __device__ void tail_split(const MfmaParams& p, const Blocks& blocks, int b, int
         }
         // (a separate pass, so that the residual row's registers are free)
         if (valid && !resid) {
-            // token i of quantized block jb
-            const int i = int(t - jb * p.G);
+            // token i of quantized block jb or jb + 1 (the tail starts at
+            // block jb's first token)
+            const int jt = int(t - t0);
+            const int64_t rowq = jt < p.G ? row0 : row1;
+            const int i = jt < p.G ? jt : jt - p.G;
             for (int c0 = 0; c0 < D; c0 += 16) {
-                const int64_t side = row0 * D + c0;
+                const int64_t side = rowq * D + c0;
                 uint32_t wd[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) wd[e] = p.kc[(side + e) * (p.G / PER) + i / PER];
@@ -905,6 +915,77 @@ __device__ void fused_append(const MfmaParams& p, int b, int kvh, int lane) {
     // the stores complete before either wave reads these rows back
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     __syncthreads();
+}
+
+// The paged decode step's append of token L of sequence b, done by the tail
+// workgroup (both waves) before it attends: the value row is quantized into
+// its page; the key goes into residual row L mod G, or, when it is the
+// block's last, the block (G - 1 residual rows and the new key) is
+// quantized per channel into its page.  The same device code as the append
+// kernels (bit-identical).  Main splits read only tiles complete before the
+// step, so no other workgroup reads these rows.
+template <int G, int BITS>
+__device__ void fused_append_paged(const MfmaParams& p, int b, int kvh, int64_t L) {
+    const int tid = threadIdx.x;
+    const int64_t bh = int64_t(b) * p.Hkv + kvh;
+    constexpr int TPR = D / 8;
+    const PagedSeq ps{p.table, p.lens, p.n_new, p.maxb, p.npages};
+    if (tid < TPR) {
+        qdev::ValueArgs va;
+        va.vin = p.v_new;
+        va.n_in = 1;
+        va.row0 = 0;
+        va.n_tok = 1;
+        va.vd = D;
+        va.BH = 0;
+        va.codes = p.vc_w;
+        va.scale = p.vs_w;
+        va.zero = p.vz_w;
+        const qdev::PagedRows rows{ps, p.Hkv, G, 1};
+        qdev::quant_values_thread<BITS>(va, rows, bh * TPR + tid);
+    }
+    if (L % G == G - 1) {
+        const int64_t fb = L / G;
+        const int64_t dst = qdev::paged_block_row(ps, b, kvh, p.Hkv, fb);
+        if (dst >= 0) {
+            const qdev::KeyJob j{p.k_new + bh * D, p.kr + bh * G * D, fb * G, L, fb * G, dst};
+            // a multiple of 64 when a channel pair spans several waves' lanes
+            const int64_t nk = qdev::key_threads_per_block<G, BITS>(D);
+            for (int64_t base = 0; base < nk; base += blockDim.x) {
+                const int64_t idx = base + tid;
+                if (idx < nk) {
+                    int64_t unit;
+                    int cp, sp;
+                    qdev::key_thread_coords<G, BITS>(idx, D, unit, cp, sp);
+                    qdev::quant_key_pair<G, BITS>(j, D, cp, sp, p.kc_w, p.ks_w, p.kz_w);
+                }
+            }
+        }
+    } else if (tid >= 64 && tid < 64 + TPR) {
+        const int v = tid - 64;
+        *reinterpret_cast<uint4*>(p.kr_w + (bh * G + L % G) * D + v * 8) =
+            *reinterpret_cast<const uint4*>(p.k_new + bh * D + v * 8);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __syncthreads();
+}
+
+// Tokens and appended rows of sequence b in a paged call.  Without the fused
+// append: the clamped length, none appended.  With it: the length before the
+// step and 1 when the step appends to b (lens[b] >= 0, n_new[b] in {0, 1},
+// within capacity and max_len), else the clamped length and 0.
+__device__ __forceinline__ void paged_step_len(const MfmaParams& p, int b, int G, int& L, int& n_app) {
+    L = seq_len(p, b);
+    n_app = 0;
+    if (p.fuse) {
+        const int raw = p.lens[b];
+        const int nn = p.n_new ? p.n_new[b] : 1;
+        const int64_t lim = int64_t(p.maxb) * G < p.max_len ? int64_t(p.maxb) * G : p.max_len;
+        if (raw >= 0 && (nn == 0 || nn == 1) && int64_t(raw) + nn <= lim) {
+            L = raw;
+            n_app = nn;
+        }
+    }
 }
 
 // the contiguous cache's tail: its counters are in the parameters

@@ -29,131 +29,7 @@ __global__ __launch_bounds__(256) void k_quant_values(ValueArgs a, ContigRows ro
     quant_values_thread<BITS>(a, rows, idx);
 }
 
-// -------------------------------------------------------------------- keys
-// One thread = 2 adjacent channels over up to 32 rows of one G-token block
-// (4-byte loads; lanes side by side read contiguous bytes of a row); for
-// G > 32 the SPL = G/32 threads of a channel pair sit in one wave and merge
-// their min/max by shuffles.  Each thread writes its rows' codes as
-// consecutive words of the channel's G*BITS/32.
-template <int W>
-struct WordVec;
-template <> struct WordVec<1> { static __device__ void st(uint32_t* p, const uint32_t* w) { p[0] = w[0]; } };
-template <> struct WordVec<2> {
-    static __device__ void st(uint32_t* p, const uint32_t* w) { *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]); }
-};
-template <> struct WordVec<4> {
-    static __device__ void st(uint32_t* p, const uint32_t* w) {
-        *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-};
-template <> struct WordVec<8> {
-    static __device__ void st(uint32_t* p, const uint32_t* w) {
-        reinterpret_cast<uint4*>(p)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        reinterpret_cast<uint4*>(p)[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    }
-};
-
-template <int G, int BITS>
-struct KeyShape {
-    static constexpr int PER = 32 / BITS;
-    static constexpr int W = G / PER;            // words per (block, channel)
-    static constexpr int TG = G < 32 ? G : 32;   // rows per thread
-    static constexpr int SPL = G / TG;           // threads per channel pair
-    static constexpr int CPW = 64 / SPL;         // channel pairs per wave (SPL > 1)
-    static constexpr int WT = TG / PER;          // words per thread and channel
-};
-
-// Threads per (sequence, KV head, block).  With SPL > 1 a wave holds the SPL
-// row ranges of CPW channel pairs, so the count is rounded up to whole waves;
-// lanes past the last pair (kd / 2 < CPW) take part in the shuffles only.
-template <int G, int BITS>
-__host__ __device__ inline int64_t key_threads_per_block(int kd) {
-    using S = KeyShape<G, BITS>;
-    const int tpb = kd / 2;
-    return S::SPL == 1 ? tpb : int64_t((tpb + S::CPW - 1) / S::CPW) * 64;
-}
-
-// thread idx -> (block unit, channel pair, row range)
-template <int G, int BITS>
-__device__ __forceinline__ void key_thread_coords(int64_t idx, int kd, int64_t& unit, int& cp, int& sp) {
-    using S = KeyShape<G, BITS>;
-    const int tpb = kd / 2;
-    if (S::SPL == 1) {
-        sp = 0;
-        cp = int(idx % tpb);
-        unit = idx / tpb;
-    } else {
-        const int lane = int(idx & 63);
-        const int64_t wv = idx >> 6;
-        const int chunks = (tpb + S::CPW - 1) / S::CPW;
-        sp = lane / S::CPW;
-        cp = int(wv % chunks) * S::CPW + lane % S::CPW;
-        unit = wv / chunks;
-    }
-}
-
-// One key block as a thread sees it: token tok < in_tok0 is residual row
-// tok - res_tok0, later ones input row tok - in_tok0; codes go to block row
-// dst (codes at dst * kd * W, side values at dst * kd).
-struct KeyJob {
-    const uint16_t* kin;     // input rows of this (sequence, KV head)
-    const uint16_t* resid;   // residual rows of this (sequence, KV head)
-    int64_t blk_tok0, in_tok0, res_tok0;
-    int64_t dst;
-};
-
-template <int G, int BITS>
-__device__ __forceinline__ void quant_key_pair(const KeyJob& j, int kd, int cp, int sp,
-                                               uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
-                                               uint16_t* __restrict__ zero) {
-    using S = KeyShape<G, BITS>;
-    constexpr float L = float((1 << BITS) - 1);
-    const bool active = cp < kd / 2;
-    uint32_t raw[S::TG];
-#pragma unroll
-    for (int i = 0; i < S::TG; ++i) {
-        const int64_t tok = j.blk_tok0 + sp * S::TG + i;
-        const uint16_t* row = tok < j.in_tok0 ? j.resid + (tok - j.res_tok0) * kd : j.kin + (tok - j.in_tok0) * kd;
-        raw[i] = active ? ld_once1(row + 2 * cp) : 0u;
-    }
-    // per-channel min / max over the rows, both channels at once (packed
-    // fp16, exact; -0 is canonicalised after), then across the row ranges
-    f16x2 mn2 = as_h2(raw[0]), mx2 = mn2;
-#pragma unroll
-    for (int i = 1; i < S::TG; ++i) {
-        mn2 = __builtin_elementwise_min(mn2, as_h2(raw[i]));
-        mx2 = __builtin_elementwise_max(mx2, as_h2(raw[i]));
-    }
-#pragma unroll
-    for (int o = S::CPW; o < 64 && S::SPL > 1; o <<= 1) {
-        mn2 = __builtin_elementwise_min(mn2, as_h2(__shfl_xor(__builtin_bit_cast(uint32_t, mn2), o)));
-        mx2 = __builtin_elementwise_max(mx2, as_h2(__shfl_xor(__builtin_bit_cast(uint32_t, mx2), o)));
-    }
-    if (!active) return;
-    GroupQ q[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) q[e] = make_group(float(mn2[e]) + 0.0f, float(mx2[e]) + 0.0f, L);
-    const int64_t side = j.dst * kd + 2 * cp;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        uint32_t words[S::WT];
-#pragma unroll
-        for (int w = 0; w < S::WT; ++w) words[w] = 0;
-        const float nmn = -q[e].mn;
-#pragma unroll
-        for (int i = 0; i < S::TG; ++i) {
-            const float d = e == 0 ? sub_half<0>(raw[i], nmn) : sub_half<1>(raw[i], nmn);
-            words[i / S::PER] |= code_of(d, q[e]) << (BITS * (i % S::PER));
-        }
-        WordVec<S::WT>::st(codes + (side + e) * S::W + sp * S::WT, words);
-    }
-    if (sp == 0) {
-        *reinterpret_cast<uint32_t*>(scale + side) =
-            uint32_t(float_to_half_bits(q[0].scale)) | (uint32_t(float_to_half_bits(q[1].scale)) << 16);
-        *reinterpret_cast<uint32_t*>(zero + side) =
-            uint32_t(float_to_half_bits(q[0].mn)) | (uint32_t(float_to_half_bits(q[1].mn)) << 16);
-    }
-}
+// The key quantizer (KeyShape, KeyJob, quant_key_pair) lives in kvq_quant_dev.h.
 
 // Contiguous cache: blocks blk0 .. blk0 + nb - 1 of every (sequence, KV head)
 struct KeyArgs {

@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(HERE, "libkvq.so")
 KVQ_KIND_KIVI, KVQ_KIND_MLA = 0, 1
 KVQ_AXIS_PER_CHANNEL, KVQ_AXIS_PER_TOKEN = 0, 1
 KVQ_APPEND_NO_AUTOFLUSH = 1
+KVQ_STEP_ADVANCE_LENGTHS = 1
 KVQ_MAX_SPLITS = 256
 STATUS = {0: "KVQ_OK", -1: "KVQ_E_NULL", -2: "KVQ_E_SHAPE", -3: "KVQ_E_ALIGN",
           -4: "KVQ_E_CAPACITY", -5: "KVQ_E_UNSUPPORTED", -6: "KVQ_E_WORKSPACE",
@@ -27,7 +28,8 @@ EXPORTS = ["kv_cache_buffer_bytes", "kv_cache_init", "kv_cache_destroy", "kv_cac
            "kv_decode_workspace_bytes", "kv_decode_attention", "kv_set_timing_events",
            "kv_decode_variant", "kvq_status_str",
            "kv_paged_buffer_bytes", "kv_paged_init", "kv_paged_destroy", "kv_paged_append",
-           "kv_paged_workspace_bytes", "kv_paged_decode", "kv_paged_variant", "kv_decode_step"]
+           "kv_paged_workspace_bytes", "kv_paged_decode", "kv_paged_variant", "kv_decode_step",
+           "kv_paged_decode_step"]
 
 
 class KvqError(RuntimeError):
@@ -89,6 +91,7 @@ def lib():
             "kv_paged_decode": (C.c_int, [p, p, i32, C.c_float, p, p, i32, i32, p, p, u64, p]),
             "kv_paged_variant": (C.c_char_p, [p, i32, i32]),
             "kv_decode_step": (C.c_int, [p, p, p, p, i32, C.c_float, i32, p, p, u64, p]),
+            "kv_paged_decode_step": (C.c_int, [p, p, p, p, i32, C.c_float, p, p, p, i32, i32, u32, p, p, u64, p]),
         }
         for name, (res, args) in sig.items():
             try:
@@ -211,6 +214,14 @@ def kv_paged_decode(handle, q_ptr, n_q_heads: int, softmax_scale: float, seq_len
                     max_len: int, n_splits: int, out_ptr, ws_ptr, ws_bytes: int, stream=None) -> None:
     _check(lib().kv_paged_decode(handle, q_ptr, n_q_heads, C.c_float(softmax_scale), seq_lens_ptr, table_ptr,
                                  max_len, n_splits, out_ptr, ws_ptr, ws_bytes, stream), "kv_paged_decode")
+
+
+def kv_paged_decode_step(handle, k_ptr, v_ptr, q_ptr, n_q_heads: int, softmax_scale: float, n_new_ptr,
+                         seq_lens_ptr, table_ptr, max_len: int, n_splits: int, flags: int, out_ptr, ws_ptr,
+                         ws_bytes: int, stream=None) -> None:
+    _check(lib().kv_paged_decode_step(handle, k_ptr, v_ptr, q_ptr, n_q_heads, C.c_float(softmax_scale), n_new_ptr,
+                                      seq_lens_ptr, table_ptr, max_len, n_splits, flags, out_ptr, ws_ptr, ws_bytes,
+                                      stream), "kv_paged_decode_step")
 
 
 def kv_paged_variant(handle, n_q_heads: int, max_len: int) -> str:
@@ -391,6 +402,22 @@ class PagedCache:
 
     def variant(self, n_q_heads: int, max_len: int) -> str:
         return kv_paged_variant(self.handle, n_q_heads, max_len)
+
+    def step(self, k, v, q, softmax_scale: float, seq_lens, block_table, max_len: int, n_new=None,
+             advance: bool = True, n_splits: int = 0, out=None, ws=None):
+        """One paged decode step (kv_paged_decode_step): k, v [B][Hkv][1][d]."""
+        torch = self.torch
+        B, Hq = q.shape[0], q.shape[1]
+        if out is None:
+            out = torch.empty((B, Hq, self.cfg.value.dim), dtype=torch.float16, device=self.device)
+        if ws is None:
+            ws = self.workspace(Hq, max_len, n_splits)
+        kv_paged_decode_step(self.handle, k.data_ptr(), v.data_ptr(), q.data_ptr(), Hq, softmax_scale,
+                             None if n_new is None else n_new.data_ptr(), seq_lens.data_ptr(),
+                             block_table.data_ptr(), max_len, n_splits,
+                             KVQ_STEP_ADVANCE_LENGTHS if advance else 0, out.data_ptr(), ws.data_ptr(),
+                             ws.numel(), self.stream())
+        return out
 
     def views(self):
         """Typed views of the page pools and the residual in the documented layouts."""

@@ -252,6 +252,35 @@ kvq_status kv_paged_decode(const kvq_paged* cache, const void* q_fp16, int32_t n
                            int32_t n_splits, void* out_fp16, void* workspace, uint64_t workspace_bytes,
                            void* hip_stream);
 
+/* kv_paged_decode_step flag: advance seq_lens[b] by the row appended to
+ * sequence b, on the device, after the step's reads of it (in the step's
+ * last launch).  With it the step's arguments need not change from one step
+ * to the next, so a caller can capture the step in a HIP graph and replay it
+ * (no memset nodes, no host reads). */
+#define KVQ_STEP_ADVANCE_LENGTHS 1u
+
+/* One paged decode step ("Kod ve Entegrasyon Haritası": paged 2-bit
+ * kernels for serving; "İddia ve Gerçeklik: KIVI": append and in-loop
+ * dequantized attention on the decode path): sequence b with n_new[b] = 1
+ * (or n_new NULL) appends one token (k_fp16 / v_fp16 [B][Hkv][1][d]) at
+ * token seq_lens[b], then every sequence attends over its tokens, the new
+ * one included.  Two launches: the attention kernel's tail workgroup stores
+ * the value row and either the residual key or, when the key completes its
+ * block, the block quantized per channel (the append kernels' own code), and
+ * then attends; the merge follows.  Caches are bit-identical to
+ * kv_paged_append + kv_paged_decode over the grown lengths; outputs too,
+ * except for a sequence whose block completes in this step (its new block is
+ * read on the tail path instead of a matrix-core tile; same tolerance).
+ * max_len bounds every length after the step.  Only the shapes with a
+ * matrix-core paged kernel (kv_paged_variant "gqa_mfma_paged" or
+ * "mha_mfma_paged"); others return KVQ_E_UNSUPPORTED.
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE (n_q_heads, n_splits, max_len, flags),
+ * KVQ_E_ALIGN, KVQ_E_WORKSPACE, KVQ_E_UNSUPPORTED, KVQ_E_HIP. */
+kvq_status kv_paged_decode_step(kvq_paged* cache, const void* k_fp16, const void* v_fp16, const void* q_fp16,
+                                int32_t n_q_heads, float softmax_scale, const int32_t* n_new, int32_t* seq_lens,
+                                const int32_t* block_table, int32_t max_len, int32_t n_splits, uint32_t flags,
+                                void* out_fp16, void* workspace, uint64_t workspace_bytes, void* hip_stream);
+
 /* Name of the kernel kv_paged_decode would launch (automatic splits). */
 const char* kv_paged_variant(const kvq_paged* cache, int32_t n_q_heads, int32_t max_len);
 

@@ -322,3 +322,40 @@ def test_decode_step_validation_before_hip():
         assert kvq.kv_cache_state(h) == (0, 0)   # nothing happened
     finally:
         kvq.kv_cache_destroy(h)
+
+
+def test_paged_decode_step_validation_before_hip():
+    L = kvq.lib()
+    h = _paged(kivi_cfg(batch=2, n_kv_heads=2, max_tokens=256, kG=64), 16)
+    d64 = _paged(kivi_cfg(kd=64, vd=64), 8)
+    k, v, q, nn, lens, table, out, ws = (0x100000 * (i + 1) for i in range(8))
+    try:
+        need = kvq.kv_paged_workspace_bytes(h, 8, 256)
+        ok = [h, k, v, q, 8, C.c_float(0.1), nn, lens, table, 256, 0, 1, out, ws, need, None]
+
+        def call(i, val):
+            a = list(ok)
+            a[i] = val
+            return L.kv_paged_decode_step(*a)
+
+        for i in (0, 1, 2, 3, 7, 8, 12, 13):
+            assert call(i, None) == -1, i
+        assert call(11, 2) == -2        # unknown flag
+        assert call(4, 7) == -2         # not a multiple of Hkv
+        assert call(9, 0) == -2         # max_len
+        assert call(9, 257) == -2
+        assert call(10, 300) == -2      # n_splits
+        for i in (1, 2, 3, 12, 13):
+            assert call(i, ok[i] + 8) == -3, i
+        for i in (6, 7, 8):
+            assert call(i, ok[i] + 2) == -3, i
+        assert call(14, 16) == -6       # workspace
+        a = list(ok)
+        a[6], a[14] = None, 16          # n_new optional: reaches the workspace check
+        assert L.kv_paged_decode_step(*a) == -6
+        a = list(ok)
+        a[0], a[4] = d64, 8
+        assert L.kv_paged_decode_step(*a) == -5   # no matrix-core paged kernel for D = 64
+    finally:
+        kvq.kv_paged_destroy(h)
+        kvq.kv_paged_destroy(d64)

@@ -265,3 +265,107 @@ def test_paged_gqa_ragged_4k(orc, T, G):
             ref = oracle_slice(orc, w, k_full[b, h, :F], v_full[b, h, :F], pg.cap // w.kG, pg.cap)
             assert_slices_equal(pg.gather(b, h), ref, f"b{b} h{h}")
     log(f"[paged gqa 4k G{G}] max|err| {worst:.3e} mean excess {excess:.2e}")
+
+
+def _rows_at(w, k_full, v_full, lens, n_new):
+    """[B][Hkv][1][d] inputs: row lens[b] of each sequence that appends."""
+    k = np.zeros((w.batch, w.n_kv_heads, 1, w.kd), np.uint16)
+    v = np.zeros((w.batch, w.n_kv_heads, 1, w.vd), np.uint16)
+    for b in range(w.batch):
+        if n_new[b]:
+            k[b, :, 0] = k_full[b, :, lens[b]]
+            v[b, :, 0] = v_full[b, :, lens[b]]
+    return k, v
+
+
+@pytest.mark.parametrize("shape", ["gqa4_g64", "gqa4_g32", "mha_d128", "gqa4_4bit_g64"])
+def test_paged_decode_step(orc, shape):
+    """kv_paged_decode_step (append fused into the attention launch, lengths
+    advanced on the device) against kv_paged_append + kv_paged_decode over
+    G + 2 steps in which some sequences sit out: caches bit-identical after
+    every step, outputs bit-identical for every sequence whose block did not
+    complete in the step, all within 2e-3 of the oracle."""
+    t = torch()
+    G = 32 if shape == "gqa4_g32" else 64
+    w = _workload(shape, 5 * G)
+    lens0 = np.array([G - 1, G - 2, 0, 5, 2 * G - 1, 3 * G - 3][:w.batch], np.int32)
+    steps = G + 2
+    nn_all = np.array([[0 if (j + b) % 5 == 0 else 1 for b in range(w.batch)] for j in range(steps)], np.int32)
+    final = lens0 + nn_all.sum(0).astype(np.int32)
+    assert final.max() <= w.T
+    k_full, v_full, q = synth.keys(w), synth.values(w), synth.query(w)
+    a, ref = Paged(w, final), Paged(w, final)
+    for pg in (a, ref):
+        pg.append(k_full, v_full, lens0)
+    assert a.pc.variant(w.n_q_heads, a.cap) in ("gqa_mfma_paged", "mha_mfma_paged")
+    lens_dev = t.from_numpy(lens0.copy()).cuda()
+    qd = dev_f16(q)
+    ws = a.pc.workspace(w.n_q_heads, a.cap)
+    for j in range(steps):
+        nn = nn_all[j]
+        kn, vn = _rows_at(w, k_full, v_full, ref.lens, nn)
+        completes = (ref.lens % G == G - 1) & (nn == 1)
+        out = a.pc.step(dev_f16(kn), dev_f16(vn), qd, w.sigma, lens_dev, a.table_dev, a.cap,
+                        n_new=t.from_numpy(nn.copy()).cuda(), ws=ws)
+        t.cuda.synchronize()
+        got = host_u16(out).view(np.float16).astype(np.float64)
+        ref.append(k_full, v_full, nn)
+        want = ref.decode(q, a.cap)
+        assert np.array_equal(lens_dev.cpu().numpy(), ref.lens), j
+        same = ~completes
+        assert np.array_equal(got[same], want[same]), (shape, j)
+        a.lens = ref.lens.copy()
+        if j % 7 == 0 or completes.any():
+            _check_decode(orc, a, k_full, v_full, q, got)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            assert_slices_equal(a.gather(b, h), ref.gather(b, h), f"{shape} b{b} h{h}")
+    _check_cache(orc, a, k_full, v_full)
+
+
+def test_paged_decode_step_graph(orc):
+    """The paged decode step with its device-side length advance, captured
+    once in a HIP graph and replayed: after every replay (with eager input
+    updates and synchronisation in between) the output and the lengths equal
+    an eager step on a twin cache, and the cache matches the oracle."""
+    t = torch()
+    w = _workload("gqa4_g64", 2 * 64 + 20)
+    lens0 = np.array([60, 62, 1, 64, 100, 127], np.int32)
+    R = 6
+    final = lens0 + R
+    k_full, v_full, q = synth.keys(w), synth.values(w), synth.query(w)
+    g_pg, e_pg = Paged(w, final), Paged(w, final)
+    for pg in (g_pg, e_pg):
+        pg.append(k_full, v_full, lens0)
+    qd = dev_f16(q)
+    kn_s = t.zeros((w.batch, w.n_kv_heads, 1, w.kd), dtype=t.float16, device="cuda")
+    vn_s = t.zeros((w.batch, w.n_kv_heads, 1, w.vd), dtype=t.float16, device="cuda")
+    out_s = t.empty((w.batch, w.n_q_heads, w.vd), dtype=t.float16, device="cuda")
+    ws_s = g_pg.pc.workspace(w.n_q_heads, g_pg.cap)
+    lens_g = t.from_numpy(lens0.copy()).cuda()
+    lens_e = t.from_numpy(lens0.copy()).cuda()
+    t.cuda.synchronize()
+    graph = t.cuda.CUDAGraph()
+    with t.cuda.graph(graph):
+        g_pg.pc.step(kn_s, vn_s, qd, w.sigma, lens_g, g_pg.table_dev, g_pg.cap, out=out_s, ws=ws_s)
+    t.cuda.synchronize()
+    assert np.array_equal(lens_g.cpu().numpy(), lens0)   # capture runs nothing
+    host = lens0.copy()
+    for r in range(R):
+        kn, vn = _rows_at(w, k_full, v_full, host, np.ones(w.batch, np.int32))
+        kn_s.copy_(dev_f16(kn))
+        vn_s.copy_(dev_f16(vn))
+        t.cuda.synchronize()
+        graph.replay()
+        t.cuda.synchronize()
+        got = host_u16(out_s).view(np.float16)
+        want = host_u16(e_pg.pc.step(dev_f16(kn), dev_f16(vn), qd, w.sigma, lens_e, e_pg.table_dev, e_pg.cap))
+        t.cuda.synchronize()
+        host = host + 1
+        assert np.array_equal(lens_g.cpu().numpy(), host), r
+        assert np.array_equal(lens_e.cpu().numpy(), host), r
+        assert np.array_equal(got.view(np.uint16), want), r
+        log(f"[graph] replay {r}: output and lengths equal the eager step")
+    g_pg.lens = host.copy()
+    _check_cache(orc, g_pg, k_full, v_full)
+    _check_decode(orc, g_pg, k_full, v_full, q, host_u16(out_s).view(np.float16).astype(np.float64))
