@@ -358,9 +358,10 @@ def main():
 def main_paged(args, w, dev):
     """The same step on a paged cache: sequence b holds lens[b] tokens
     (uniform in [T/2, T], the longest exactly T), its key blocks in pages of
-    a shuffled pool; each step appends one token to every sequence
-    (kv_paged_append) and attends over each sequence's own length
-    (kv_paged_decode)."""
+    a shuffled pool; each step appends one token to every sequence and
+    attends over each sequence's own length: kv_paged_decode_step (the
+    append inside the attention launch), or with --separate-calls
+    kv_paged_append then kv_paged_decode."""
     import torch
 
     from decode_attention_asym_amd import kvq, synth
@@ -422,6 +423,8 @@ def main_paged(args, w, dev):
 
     lib = kvq.lib()
     c_append, c_decode, c_timing = lib.kv_paged_append, lib.kv_paged_decode, lib.kv_set_timing_events
+    fused = not args.separate_calls and caches[0].variant(w.n_q_heads, max_len).endswith("mfma_paged")
+    c_step = lib.kv_paged_decode_step if fused else None
     handles = [c.handle for c in caches]
     tptr = [t.data_ptr() for t in tables]
     lptr = [t.data_ptr() for t in lens_dev]
@@ -434,6 +437,12 @@ def main_paged(args, w, dev):
         if timed:
             st = c_timing(*evs[i - args.warmup])
             assert st == 0, st
+        if c_step is not None:
+            # lengths before the step, not advanced: step j of every layer reads lens0 + j
+            st = c_step(handles[layer], kptr[j], vptr[j], qptr, w.n_q_heads, w.sigma, None, lptr[j], tptr[layer],
+                        max_len, args.splits, 0, optr, wptr, wbytes, sptr)
+            assert st == 0, kvq.kvq_status_str(st)
+            return
         st = c_append(handles[layer], kptr[j], vptr[j], 1, None, lptr[j], tptr[layer], sptr)
         assert st == 0, kvq.kvq_status_str(st)
         st = c_decode(handles[layer], qptr, w.n_q_heads, w.sigma, lptr[j + 1], tptr[layer], max_len, args.splits,
@@ -485,7 +494,8 @@ def main_paged(args, w, dev):
         "config": {"workload": w.name + "_paged_ragged", "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.kd, "context": f"{int(lens0.min())}..{w.T}",
                    "mean_context": round(float(lens0.mean()), 1), "G": w.kG, "bits": w.kbits,
-                   "value_group": w.vG, "layers": L, "page_tokens": w.kG, "parallelism": "none (1 GPU)"},
+                   "value_group": w.vG, "layers": L, "page_tokens": w.kG, "parallelism": "none (1 GPU)",
+                   "step": "fused decode step" if fused else "append + decode"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": profiled_traffic(variant, w.name + "_paged_ragged"),
