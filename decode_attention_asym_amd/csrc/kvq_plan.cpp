@@ -30,14 +30,25 @@ int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > h
 // and in the merge than they gain (measured on MI355X, 32K-token GQA at one
 // sequence: 255 splits 36 us per step, 32 splits 27 us).  Non-decreasing in
 // ntiles, so the slot bound at full capacity covers every length.
+//
+// Workgroup targets (measured on MI355X, four interleaved runs per point):
+// the 2-bit GQA kernel holds 8 workgroups per CU (2048 on the GPU); 6144 of
+// them (three full rounds) beat 3072 (one and a half) by ~3% on the 32K
+// batch-32 workload (150 vs 155 us) and on the 128K batch-4 one.  The 4-bit
+// GQA kernel (6 per CU) was flat between 3072 and 8192.
+int64_t wg_target(const kvq_cache_cfg& cfg, Variant v) {
+    if (v == V_MHA) return 1536;
+    if (v == V_GQA) return cfg.key.bits == 2 ? 6144 : 3072;
+    return 2048;
+}
 int64_t auto_main(const kvq_cache& c, int Hq, Variant v, int64_t ntiles) {
     // MLA: one four-wave workgroup per CU, Hq / 64 of them per sequence and split
     if (v == V_MLA) return clamp64((256 * 64 / Hq + c.cfg.batch - 1) / c.cfg.batch, 1, KVQ_MAX_SPLITS);
     const bool tiled = v == V_GQA || v == V_MHA;
     const int64_t units = tiled ? int64_t(c.cfg.batch) * c.cfg.n_kv_heads : int64_t(c.cfg.batch) * Hq;
     // measured on MI355X: about 12 tiles per two-wave workgroup suit the MHA
-    // kernel (64 tiles per sequence at 4K tokens), 6 waves per SIMD the GQA one
-    const int64_t target = v == V_MHA ? 1536 : tiled ? 3072 : 2048;
+    // kernel (64 tiles per sequence at 4K tokens)
+    const int64_t target = wg_target(c.cfg, v);
     int64_t want = (target + units - 1) / units;
     if (tiled) {
         const int64_t min_run = v == V_MHA ? 8 : 16;
@@ -90,7 +101,7 @@ PagedPlan plan_paged(const kvq_paged& c, int Hq, int n_splits, int max_len, Vari
         const int64_t units = int64_t(c.cfg.batch) * c.cfg.n_kv_heads;
         // as for a contiguous cache: fill the GPU, runs of at least 16 (GQA)
         // / 8 (MHA) tiles
-        const int64_t target = v == V_MHA ? 1536 : 3072, min_run = v == V_MHA ? 8 : 16;
+        const int64_t target = wg_target(c.cfg, v), min_run = v == V_MHA ? 8 : 16;
         const int64_t fill = (target + units - 1) / units, runs = (ntiles + min_run - 1) / min_run;
         const int64_t want = n_splits > 0 ? n_splits : clamp64(fill < runs ? fill : runs, 1, KVQ_MAX_SPLITS - 1);
         int64_t chunk = ntiles > 0 ? (ntiles + want - 1) / want : 1;
