@@ -177,8 +177,8 @@ def cpu_baseline(w, k, v, q, cap, n_pairs, lens=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
+              "sharding the decode step across GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
     import torch
 

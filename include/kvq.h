@@ -74,7 +74,7 @@ typedef enum kvq_status {
     KVQ_E_SHAPE = -2,       /* inconsistent or unsupported dimensions        */
     KVQ_E_ALIGN = -3,       /* a device pointer is not 16-byte aligned       */
     KVQ_E_CAPACITY = -4,    /* tokens would exceed max_tokens / the residual */
-    KVQ_E_UNSUPPORTED = -5, /* valid request this build does not implement   */
+    KVQ_E_UNSUPPORTED = -5, /* valid request the library does not implement  */
     KVQ_E_WORKSPACE = -6,   /* workspace smaller than required               */
     KVQ_E_HIP = -7,         /* a HIP launch failed                           */
     KVQ_E_STATE = -8        /* the cache holds no tokens to attend over      */
