@@ -74,6 +74,8 @@ def lib():
         for f in (L.orc_attention_kivi, L.orc_attention_mla):
             f.restype = C.c_int
             f.argtypes = [C.POINTER(OrcCache), p, i32, C.c_float, p, i64, p, C.c_int]
+        L.orc_prefill_attention.restype = C.c_int
+        L.orc_prefill_attention.argtypes = [p, p, p, i64, i64, i64, i64, i32, i32, C.c_double, p, i64, p, C.c_int]
         _lib = L
     return _lib
 
@@ -246,3 +248,29 @@ def attention_kivi(cache: Cache, q_bits, sigma: float, pairs=None, nthreads=None
 def attention_mla(cache: Cache, q_bits, sigma: float, pairs=None, nthreads=None):
     """q_bits: uint16 [B][Hq][vd + kd] -> fp64 [B][Hq][vd] (or [npairs][vd])."""
     return _attention(lib().orc_attention_mla, cache, q_bits, sigma, pairs, nthreads)
+
+
+def prefill_attention(q_bits, k_bits, v_bits, sigma: float, rows=None, nthreads=None):
+    """Causal prefill attention (fp64): q uint16 [B][Hq][T][d], k / v uint16
+    [B][Hkv][T][d|dv]; rows: (b, h, i) triples, default every row.  Returns
+    fp64 [nrows][dv] (or [B][Hq][T][dv] when rows is None)."""
+    q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    k = np.ascontiguousarray(k_bits, dtype=np.uint16)
+    v = np.ascontiguousarray(v_bits, dtype=np.uint16)
+    B, Hq, T, d = q.shape
+    Hkv, dv = k.shape[1], v.shape[3]
+    full = rows is None
+    if full:
+        bb, hh, ii = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(T), indexing="ij")
+        rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
+    rr = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    out = np.empty((rr.shape[0], dv), np.float64)
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    L = lib()
+    rc = L.orc_prefill_attention(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, T, d, dv, C.c_double(sigma), _ptr(rr),
+                                 rr.shape[0], _ptr(out), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle prefill attention rejected its input")
+    return out.reshape(B, Hq, T, dv) if full else out
+

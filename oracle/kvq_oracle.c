@@ -339,3 +339,74 @@ int orc_attention_mla(const orc_cache* c, const uint16_t* q, int32_t Hq, float s
                       const int32_t* pairs, int64_t npairs, double* out, int nthreads) {
     return run_attention(c, q, Hq, sigma, pairs, npairs, out, nthreads, 1);
 }
+
+/* ---------------------------------------------------------- prefill attention
+ * "Makale Bülteni -- KIVI", section "Kod ve Entegrasyon Haritası": in the
+ * prefill phase KIVI runs ordinary attention over the prompt's full-precision
+ * keys and values (a FlashAttention kernel there); the cache is quantized from
+ * those same fp16 tensors.  This is that attention written out: causal, every
+ * query position i of a prompt attends to positions 0..i, query head h to KV
+ * head h / (Hq / Hkv), in binary64 over the fp16 inputs. */
+
+typedef struct {
+    const uint16_t *q, *k, *v; int64_t Hq, Hkv, T; int32_t d, dv; double sigma;
+    const int64_t* rows; int64_t lo, hi; double* out; int err;
+} pf_job;
+
+static void* pf_worker(void* arg) {
+    pf_job* J = (pf_job*)arg;
+    double* s = (double*)malloc(sizeof(double) * (size_t)J->T);
+    if (!s) { J->err = -1; return NULL; }
+    const int64_t group = J->Hq / J->Hkv;
+    for (int64_t r = J->lo; r < J->hi; ++r) {
+        const int64_t b = J->rows[3 * r], h = J->rows[3 * r + 1], i = J->rows[3 * r + 2];
+        if (b < 0 || h < 0 || h >= J->Hq || i < 0 || i >= J->T) { J->err = -1; break; }
+        const int64_t kvh = h / group;
+        const uint16_t* qi = J->q + ((b * J->Hq + h) * J->T + i) * J->d;
+        const uint16_t* kb = J->k + (b * J->Hkv + kvh) * J->T * J->d;
+        const uint16_t* vb = J->v + (b * J->Hkv + kvh) * J->T * J->dv;
+        double mx = -INFINITY;
+        for (int64_t j = 0; j <= i; ++j) {
+            double dot = 0.0;
+            for (int32_t c = 0; c < J->d; ++c)
+                dot += (double)orc_half_to_float(qi[c]) * (double)orc_half_to_float(kb[j * J->d + c]);
+            s[j] = J->sigma * dot;
+            if (s[j] > mx) mx = s[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j <= i; ++j) { s[j] = exp(s[j] - mx); l += s[j]; }
+        double* o = J->out + r * J->dv;
+        for (int32_t c = 0; c < J->dv; ++c) o[c] = 0.0;
+        for (int64_t j = 0; j <= i; ++j)
+            for (int32_t c = 0; c < J->dv; ++c) o[c] += s[j] * (double)orc_half_to_float(vb[j * J->dv + c]);
+        for (int32_t c = 0; c < J->dv; ++c) o[c] /= l;
+    }
+    free(s);
+    return NULL;
+}
+
+int orc_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B, int64_t Hq,
+                          int64_t Hkv, int64_t T, int32_t d, int32_t dv, double sigma, const int64_t* rows,
+                          int64_t nrows, double* out, int nthreads) {
+    if (!q || !k || !v || !rows || !out || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || T <= 0 ||
+        d <= 0 || dv <= 0 || nrows <= 0)
+        return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[3 * r] >= B) return -1;
+    if (nthreads <= 0) nthreads = 1;
+    if (nthreads > nrows) nthreads = (int)nrows;
+    pf_job* jobs = (pf_job*)calloc((size_t)nthreads, sizeof(pf_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); return -1; }
+    for (int t = 0; t < nthreads; ++t) {
+        pf_job j = {q, k, v, Hq, Hkv, T, d, dv, sigma, rows, nrows * t / nthreads, nrows * (t + 1) / nthreads, out, 0};
+        jobs[t] = j;
+    }
+    for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, pf_worker, &jobs[t]);
+    pf_worker(&jobs[0]);
+    int err = jobs[0].err;
+    for (int t = 1; t < nthreads; ++t) { pthread_join(th[t], NULL); err |= jobs[t].err; }
+    free(jobs);
+    free(th);
+    return err ? -1 : 0;
+}

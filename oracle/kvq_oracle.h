@@ -111,6 +111,18 @@ int orc_attention_mla(const orc_cache* c, const uint16_t* q, int32_t Hq,
                       float sigma, const int32_t* pairs, int64_t npairs,
                       double* out, int nthreads);
 
+/* Causal prefill attention in fp64 over fp16 prompt tensors ("Makale Bülteni
+ * -- KIVI", section "Kod ve Entegrasyon Haritası": ordinary attention over the
+ * full-precision prompt in the prefill phase).
+ *   q : fp16 [B][Hq][T][d], k : fp16 [B][Hkv][T][d], v : fp16 [B][Hkv][T][dv]
+ *   rows : nrows triples (b, h, i); out : fp64 [nrows][dv]
+ * out = sum_{j <= i} exp(s_j - max) v_j / sum_{j <= i} exp(s_j - max) with
+ * s_j = sigma * q_i . k_j, KV head h / (Hq / Hkv).  Returns 0, or -1 on a bad
+ * argument or row. */
+int orc_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B, int64_t Hq,
+                          int64_t Hkv, int64_t T, int32_t d, int32_t dv, double sigma, const int64_t* rows,
+                          int64_t nrows, double* out, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
