@@ -32,6 +32,7 @@ SOURCES = {
     "kvq_decode_gqa.hip": VGPR_FORM,
     "kvq_decode_mha.hip": VGPR_FORM,
     "kvq_decode_mla.hip": VGPR_FORM,
+    "kvq_prefill.hip": VGPR_FORM,
 }
 FLAGS = COMMON + VGPR_FORM   # kept for tools that print the main flag set
 

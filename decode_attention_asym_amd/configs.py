@@ -98,4 +98,11 @@ WORKLOADS = [
              64, 64, 4, 512, 32, 2, 20.0),
 ]
 
-BY_NAME = {w.name: w for w in WORKLOADS}
+# Prompt (prefill) workloads: causal attention over the prompt's fp16 K / V
+# with the bulk quantize fused in.  Mistral-7B-shaped GQA layer, a 4096-token
+# prompt per sequence.
+PREFILL_WORKLOADS = [
+    _kivi("mistral_7b_gqa_prefill_b4_t4096", 5, 4, 32, 8, 128, 4096, 64),
+]
+
+BY_NAME = {w.name: w for w in WORKLOADS + PREFILL_WORKLOADS}

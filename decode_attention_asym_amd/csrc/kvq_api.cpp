@@ -464,6 +464,49 @@ kvq_status kv_decode_step(kvq_cache* c, const void* k, const void* v, const void
     return kv_decode_attention(c, q, Hq, sigma, n_splits, out, ws, ws_bytes, stream);
 }
 
+kvq_status kv_prefill_attention(kvq_cache* c, const void* q, const void* k, const void* v, int64_t n, int32_t Hq,
+                                float sigma, uint32_t flags, void* out, void* stream) {
+    if (!c || !q || !k || !v || !out) return KVQ_E_NULL;
+    if (flags & ~KVQ_PREFILL_ATTENTION_ONLY) return KVQ_E_SHAPE;
+    if (n < 1 || n > INT32_MAX - 63) return KVQ_E_SHAPE;
+    if (Hq < 1 || Hq % c->cfg.n_kv_heads != 0) return KVQ_E_SHAPE;
+    // grid: (query blocks, query heads, sequences)
+    if (Hq > 65535 || c->cfg.batch > 65535) return KVQ_E_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return KVQ_E_ALIGN;
+    if (!prefill_supported(c->cfg)) return KVQ_E_UNSUPPORTED;
+    const bool quant = (flags & KVQ_PREFILL_ATTENTION_ONLY) == 0;
+    const Geom g = geom_of(c->cfg);
+    if (quant && c->T != 0) return KVQ_E_STATE;
+    if (quant && n > g.cap) return KVQ_E_CAPACITY;
+    PrefillArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.out = static_cast<uint16_t*>(out);
+    a.B = g.B;
+    a.Hq = Hq;
+    a.Hkv = g.Hkv;
+    a.T = int(n);
+    a.sigma2 = sigma * 1.4426950408889634f;
+    a.quant = quant ? 1 : 0;
+    a.kc = static_cast<uint32_t*>(c->buf.k_codes);
+    a.vc = static_cast<uint32_t*>(c->buf.v_codes);
+    a.ks = static_cast<uint16_t*>(c->buf.k_scale);
+    a.kz = static_cast<uint16_t*>(c->buf.k_zero);
+    a.vs = static_cast<uint16_t*>(c->buf.v_scale);
+    a.vz = static_cast<uint16_t*>(c->buf.v_zero);
+    a.kr = static_cast<uint16_t*>(c->buf.k_resid);
+    a.cap = g.cap;
+    a.nblk_cap = g.nblk_cap;
+    if (launch_prefill(a, c->cfg, static_cast<hipStream_t>(stream)) != hipSuccess) return KVQ_E_HIP;
+    if (quant) {
+        // what kv_quantize_append(c, k, v, n, 0) leaves on an empty cache
+        c->nblk = n / g.kG;
+        c->T = n;
+    }
+    return KVQ_OK;
+}
+
 kvq_status kv_set_timing_events(void* before, void* after) {
     if ((before == nullptr) != (after == nullptr)) return KVQ_E_NULL;
     g_ev_before = static_cast<hipEvent_t>(before);

@@ -147,4 +147,18 @@ hipError_t launch_decode_mha_paged(const DecodeArgs& a, hipStream_t st);
 bool mha_cfg_supported(const kvq_cache_cfg& c, int Hq);
 hipError_t launch_decode_generic_paged(const DecodeArgs& a, hipStream_t st);
 
+// ---- prefill attention fused with the bulk quantize (kvq_prefill.hip) ----
+struct PrefillArgs {
+    const uint16_t *q, *k, *v;   // q [B][Hq][T][128], k / v [B][Hkv][T][128] (fp16)
+    uint16_t* out;               // [B][Hq][T][128] (fp16)
+    int B, Hq, Hkv, T;
+    float sigma2;                // softmax scale * log2(e)
+    int quant;                   // also quantize the prompt into the cache
+    uint32_t *kc, *vc;           // cache arrays (contiguous layout)
+    uint16_t *ks, *kz, *vs, *vz, *kr;
+    int64_t cap, nblk_cap;
+};
+bool prefill_supported(const kvq_cache_cfg& c);
+hipError_t launch_prefill(const PrefillArgs& a, const kvq_cache_cfg& c, hipStream_t st);
+
 }  // namespace kvq

@@ -19,6 +19,7 @@ KVQ_KIND_KIVI, KVQ_KIND_MLA = 0, 1
 KVQ_AXIS_PER_CHANNEL, KVQ_AXIS_PER_TOKEN = 0, 1
 KVQ_APPEND_NO_AUTOFLUSH = 1
 KVQ_STEP_ADVANCE_LENGTHS = 1
+KVQ_PREFILL_ATTENTION_ONLY = 1
 KVQ_MAX_SPLITS = 256
 STATUS = {0: "KVQ_OK", -1: "KVQ_E_NULL", -2: "KVQ_E_SHAPE", -3: "KVQ_E_ALIGN",
           -4: "KVQ_E_CAPACITY", -5: "KVQ_E_UNSUPPORTED", -6: "KVQ_E_WORKSPACE",
@@ -29,7 +30,7 @@ EXPORTS = ["kv_cache_buffer_bytes", "kv_cache_init", "kv_cache_destroy", "kv_cac
            "kv_decode_variant", "kvq_status_str",
            "kv_paged_buffer_bytes", "kv_paged_init", "kv_paged_destroy", "kv_paged_append",
            "kv_paged_workspace_bytes", "kv_paged_decode", "kv_paged_variant", "kv_decode_step",
-           "kv_paged_decode_step"]
+           "kv_paged_decode_step", "kv_prefill_attention"]
 
 
 class KvqError(RuntimeError):
@@ -92,6 +93,7 @@ def lib():
             "kv_paged_variant": (C.c_char_p, [p, i32, i32]),
             "kv_decode_step": (C.c_int, [p, p, p, p, i32, C.c_float, i32, p, p, u64, p]),
             "kv_paged_decode_step": (C.c_int, [p, p, p, p, i32, C.c_float, p, p, p, i32, i32, u32, p, p, u64, p]),
+            "kv_prefill_attention": (C.c_int, [p, p, p, p, i64, i32, C.c_float, u32, p, p]),
         }
         for name, (res, args) in sig.items():
             try:
@@ -172,6 +174,12 @@ def kv_decode_step(handle, k_ptr, v_ptr, q_ptr, n_q_heads: int, softmax_scale: f
                    out_ptr, ws_ptr, ws_bytes: int, stream=None) -> None:
     _check(lib().kv_decode_step(handle, k_ptr, v_ptr, q_ptr, n_q_heads, C.c_float(softmax_scale), n_splits,
                                 out_ptr, ws_ptr, ws_bytes, stream), "kv_decode_step")
+
+
+def kv_prefill_attention(handle, q_ptr, k_ptr, v_ptr, n: int, n_q_heads: int, softmax_scale: float, flags: int,
+                         out_ptr, stream=None) -> None:
+    _check(lib().kv_prefill_attention(handle, q_ptr, k_ptr, v_ptr, n, n_q_heads, C.c_float(softmax_scale), flags,
+                                      out_ptr, stream), "kv_prefill_attention")
 
 
 def kv_set_timing_events(ev_before, ev_after) -> None:
@@ -302,6 +310,16 @@ class DeviceCache:
 
     def variant(self, n_q_heads: int) -> str:
         return kv_decode_variant(self.handle, n_q_heads)
+
+    def prefill(self, q, k, v, softmax_scale: float, flags: int = 0, out=None):
+        """Causal attention of the prompt (q [B][Hq][n][d], k / v [B][Hkv][n][d]) and,
+        unless KVQ_PREFILL_ATTENTION_ONLY, its append to this empty cache
+        (kv_prefill_attention).  Returns out [B][Hq][n][d]."""
+        if out is None:
+            out = self.torch.empty(q.shape, dtype=self.torch.float16, device=self.device)
+        kv_prefill_attention(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), q.shape[2], q.shape[1],
+                             softmax_scale, flags, out.data_ptr(), self.stream())
+        return out
 
     def step(self, k, v, q, softmax_scale: float, n_splits: int = 0, out=None, ws=None):
         """Append one token per sequence (k, v: [B][Hkv][1][d]) and attend (kv_decode_step)."""

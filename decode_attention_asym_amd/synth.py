@@ -28,7 +28,7 @@ import numpy as np
 from .configs import Workload
 
 SEED_BASE = 0x4B495649
-T_KEY, T_VALUE, T_QUERY, T_OUTLIER, T_LENS, T_PAGES = 0, 1, 2, 3, 4, 5
+T_KEY, T_VALUE, T_QUERY, T_OUTLIER, T_LENS, T_PAGES, T_PROMPT_Q = 0, 1, 2, 3, 4, 5, 6
 
 
 def _rng(w: Workload, *words: int) -> np.random.Generator:
@@ -65,6 +65,22 @@ def query(w: Workload) -> np.ndarray:
     """uint16 [B][Hq][qd]."""
     x = _normal(_rng(w, T_QUERY), (w.batch, w.n_q_heads, w.qd))
     return x.astype(np.float16).view(np.uint16)
+
+
+def prompt_queries(w: Workload, T: int | None = None, threads=None) -> np.ndarray:
+    """uint16 [B][Hq][T][qd]: the query rows of a prompt (prefill), N(0, 1),
+    one stream per (sequence, query head)."""
+    T = w.T if T is None else T
+    out = np.empty((w.batch, w.n_q_heads, T, w.qd), np.uint16)
+
+    def job(bh):
+        b, h = divmod(bh, w.n_q_heads)
+        out[b, h] = _normal(_rng(w, T_PROMPT_Q, b, h), (T, w.qd)).astype(np.float16).view(np.uint16)
+
+    n = threads or min(16, os.cpu_count() or 1)
+    with cf.ThreadPoolExecutor(max_workers=n) as ex:
+        list(ex.map(job, range(w.batch * w.n_q_heads)))
+    return out
 
 
 def _fill(fn, w: Workload, T: int, dim: int, out: np.ndarray | None, threads: int | None):

@@ -77,7 +77,7 @@ typedef enum kvq_status {
     KVQ_E_UNSUPPORTED = -5, /* valid request the library does not implement  */
     KVQ_E_WORKSPACE = -6,   /* workspace smaller than required               */
     KVQ_E_HIP = -7,         /* a HIP launch failed                           */
-    KVQ_E_STATE = -8        /* the cache holds no tokens to attend over      */
+    KVQ_E_STATE = -8        /* no tokens to attend over; prefill: not empty  */
 } kvq_status;
 
 enum { KVQ_KIND_KIVI = 0, KVQ_KIND_MLA = 1 };
@@ -301,6 +301,33 @@ const char* kv_paged_variant(const kvq_paged* cache, int32_t n_q_heads, int32_t 
 kvq_status kv_decode_step(kvq_cache* cache, const void* k_fp16, const void* v_fp16, const void* q_fp16,
                           int32_t n_q_heads, float softmax_scale, int32_t n_splits, void* out_fp16,
                           void* workspace, uint64_t workspace_bytes, void* hip_stream);
+
+/* kv_prefill_attention flag: attention only; the cache is neither read nor
+ * written (any length), e.g. to time the attention without the quantize. */
+#define KVQ_PREFILL_ATTENTION_ONLY 1u
+
+/* Prefill of an empty cache ("Makale Bülteni -- KIVI", section "Kod ve
+ * Entegrasyon Haritası": the prefill phase runs ordinary attention over the
+ * full-precision prompt; the cache is quantized from the same tensors).  One
+ * kernel launch computes the causal attention of the n-token prompt,
+ *   out[b][h][i] = sum_{j <= i} softmax_j(softmax_scale * q_i . k_j) v_j,
+ * query head h reading KV head h / (n_q_heads / n_kv_heads), and appends the
+ * prompt's keys and values to the cache exactly as kv_quantize_append(cache,
+ * k, v, n, 0) would (every full key block quantized, the rest in the
+ * residual; same bits), leaving T = n.
+ *   q_fp16   [B][n_q_heads][n][128] (fp16, device, 16-B aligned)
+ *   k_fp16, v_fp16 [B][n_kv_heads][n][128] (the kv_quantize_append layout)
+ *   out_fp16 [B][n_q_heads][n][128]
+ * Weights enter the PV product as fp16 (as FlashAttention does); sums in
+ * fp32.  Needs key and value dim 128, key groups of 32 or 64 tokens, 2- or
+ * 4-bit codes, 32-channel value groups (else KVQ_E_UNSUPPORTED) and, unless
+ * KVQ_PREFILL_ATTENTION_ONLY, an empty cache (else KVQ_E_STATE).
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE (n < 1, n_q_heads, flags, grid limits),
+ * KVQ_E_CAPACITY (n > max_tokens), KVQ_E_ALIGN, KVQ_E_STATE,
+ * KVQ_E_UNSUPPORTED, KVQ_E_HIP. */
+kvq_status kv_prefill_attention(kvq_cache* cache, const void* q_fp16, const void* k_fp16, const void* v_fp16,
+                                int64_t n, int32_t n_q_heads, float softmax_scale, uint32_t flags, void* out_fp16,
+                                void* hip_stream);
 
 /* Profiling hook: when both are non-NULL (hipEvent_t, created by the caller),
  * later kv_decode_attention / kv_decode_step / kv_paged_decode calls launch their split-K pass-1 kernel with

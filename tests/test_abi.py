@@ -359,3 +359,33 @@ def test_paged_decode_step_validation_before_hip():
     finally:
         kvq.kv_paged_destroy(h)
         kvq.kv_paged_destroy(d64)
+
+
+def test_prefill_validation_before_hip():
+    L = kvq.lib()
+    h = kvq.kv_cache_init(kivi_cfg(batch=2, n_kv_heads=2, max_tokens=256, kG=64), kvq.CacheBuffers(*FAKE))
+    d64 = kvq.kv_cache_init(kivi_cfg(kd=64, vd=64), kvq.CacheBuffers(*FAKE))
+    q, k, v, out = (0x100000 * (i + 1) for i in range(4))
+    try:
+        ok = [h, q, k, v, 100, 8, C.c_float(0.1), 0, out, None]
+
+        def call(i, val):
+            a = list(ok)
+            a[i] = val
+            return L.kv_prefill_attention(*a)
+
+        for i in (0, 1, 2, 3, 8):
+            assert call(i, None) == -1, i
+        assert call(7, 2) == -2          # unknown flag
+        assert call(4, 0) == -2          # n
+        assert call(5, 7) == -2          # not a multiple of Hkv
+        assert call(5, 70000) == -2      # grid limit
+        for i in (1, 2, 3, 8):
+            assert call(i, ok[i] + 8) == -3, i
+        assert call(4, 257) == -4        # beyond capacity
+        a = list(ok)
+        a[0] = d64
+        assert L.kv_prefill_attention(*a) == -5   # head dim 64: no prefill kernel
+    finally:
+        kvq.kv_cache_destroy(h)
+        kvq.kv_cache_destroy(d64)
