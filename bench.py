@@ -11,7 +11,11 @@ are seeded synthetic fp16 tensors already resident in HBM.  Prints ONE JSON
 line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers L]
-                  [--no-cpu-baseline] [--paged] [--separate-calls]
+                  [--no-cpu-baseline] [--paged] [--separate-calls] [--prefill]
+
+--prefill times the prompt instead: one step = kv_prefill_attention of the
+whole prompt (causal attention on the matrix cores with the bulk quantize of
+its keys and values fused in) into an empty cache.
 """
 from __future__ import annotations
 
@@ -30,6 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
 DEFAULT_WORKLOAD = "mistral_7b_gqa_t32805"
+PREFILL_WORKLOAD = "mistral_7b_gqa_prefill_b4_t4096"
 
 
 class HipEvents:
@@ -64,6 +69,7 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=100000, help="prefill: oracle rows timed for the CPU baseline")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--layers", type=int, default=0,
                     help="caches to rotate over (default: enough for 1 GB, at most 32)")
@@ -75,6 +81,9 @@ def parse():
                     help="sequences per step (default: the workload's); names the workload ..._b<N>")
     ap.add_argument("--bits", type=int, default=0, choices=[0, 2, 4],
                     help="key and value code width (default: the workload's); names the workload ..._<N>bit")
+    ap.add_argument("--prefill", action="store_true",
+                    help="prefill: causal prompt attention fused with the bulk quantize (kv_prefill_attention) "
+                         "on the prefill workload")
     ap.add_argument("--separate-calls", action="store_true",
                     help="step as kv_quantize_append + kv_decode_attention instead of kv_decode_step")
     return ap.parse_args()
@@ -187,6 +196,8 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
+    if args.prefill and args.workload == DEFAULT_WORKLOAD:
+        args.workload = PREFILL_WORKLOAD
     w = configs.BY_NAME[args.workload]
     if args.batch:
         import dataclasses
@@ -196,6 +207,9 @@ def main():
         w = dataclasses.replace(w, kbits=args.bits, vbits=args.bits, name=f"{w.name}_{args.bits}bit")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.prefill:
+        main_prefill(args, w, dev)
+        return
     if args.paged:
         main_paged(args, w, dev)
         return
@@ -515,6 +529,115 @@ def main_paged(args, w, dev):
     print(json.dumps(res), flush=True)
     for c in caches:
         c.close()
+
+
+def prefill_flops(w) -> int:
+    """Algorithmic flops of causal attention over a T-token prompt: row i
+    attends to i + 1 keys, 2 * d flops per key for q . k and 2 * d for p v,
+    so sum_i (i + 1) * 2 (d_qk + d_v) = (d_qk + d_v) T (T + 1) per head."""
+    return w.batch * w.n_q_heads * (w.qd + w.vd) * w.T * (w.T + 1)
+
+
+def cpu_baseline_prefill(w, q, k, v, n_rows):
+    """The oracle's prefill attention, as it stands, on n_rows rows spread
+    over the prompt (every host core), scaled to flops/s by each row's own
+    causal window."""
+    import oracle
+
+    rng = np.random.default_rng(0)
+    rows = np.stack([rng.integers(0, w.batch, n_rows), rng.integers(0, w.n_q_heads, n_rows),
+                     rng.integers(0, w.T, n_rows)], axis=1).astype(np.int64)
+    cores = min(16, os.cpu_count() or 1)
+    t0 = time.perf_counter()
+    oracle.prefill_attention(q, k, v, w.sigma, rows=rows, nthreads=cores)
+    dt = time.perf_counter() - t0
+    flops = float(np.sum(2 * (w.qd + w.vd) * (rows[:, 2] + 1)))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(cores, n_rows), "kind": "oracle",
+            "sample": f"{n_rows} random (sequence, head, row) outputs of the prompt, fp64; {dt:.2f} s wall"}
+
+
+def main_prefill(args, w, dev):
+    """One step = kv_prefill_attention of the whole prompt into an empty
+    cache (the reset between steps is host-side only)."""
+    import torch
+
+    from decode_attention_asym_amd import kvq, synth
+
+    t0 = time.time()
+    q, k, v = synth.prompt_queries(w), synth.keys(w), synth.values(w)
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def dev16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.float16).to(dev)
+
+    qd, kd, vd = dev16(q), dev16(k), dev16(v)
+    cache = kvq.DeviceCache(kvq.cfg_for(w, -(-w.T // w.kG) * w.kG), device=dev)
+    out = torch.empty((w.batch, w.n_q_heads, w.T, w.vd), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+    lib = kvq.lib()
+    sptr = stream.cuda_stream
+
+    def run(flags, n, append_first=False):
+        for _ in range(n):
+            lib.kv_cache_reset(cache.handle)
+            if append_first:
+                st = lib.kv_quantize_append(cache.handle, kd.data_ptr(), vd.data_ptr(), w.T, 0, sptr)
+                assert st == 0, kvq.kvq_status_str(st)
+            st = lib.kv_prefill_attention(cache.handle, qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), w.T,
+                                          w.n_q_heads, C.c_float(w.sigma), flags, out.data_ptr(), sptr)
+            assert st == 0, kvq.kvq_status_str(st)
+
+    def timed(flags, n, append_first=False):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run(flags, n, append_first)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    # the fused step (the reported figure) over all K steps; then, for
+    # context, attention alone and append + attention alone, interleaved with
+    # the fused step in three rounds so that clock drift shows in all three
+    only = kvq.KVQ_PREFILL_ATTENTION_ONLY
+    run(0, max(1, args.warmup))
+    run(only, max(1, args.warmup))
+    ms = timed(0, args.steps)
+    n_ctx = max(1, args.steps // 3)
+    rounds = [(timed(0, n_ctx), timed(only, n_ctx), timed(only, n_ctx, append_first=True)) for _ in range(3)]
+    ms_fused_ctx, ms_attn, ms_sep = (float(np.mean([r[i] for r in rounds])) for i in range(3))
+    flops = prefill_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "prefill attention TFLOP/s (causal, bulk quantize fused), prompt tokens/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.kd, "prompt_tokens": w.T, "G": w.kG, "bits": w.kbits, "value_group": w.vG,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_prefill (one launch per step)", "avg_us": round(ms * 1e3, 2),
+                     "alg_flops_per_launch": int(flops)},
+        "extra": {
+            "prompt_tokens_per_s": round(w.batch * w.T / (ms * 1e-3), 1),
+            "interleaved_rounds_ms": {"fused": round(ms_fused_ctx, 4), "attention_only": round(ms_attn, 4),
+                                      "append_then_attention_only": round(ms_sep, 4)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(w, q, k, v, args.cpu_rows)
+    print(json.dumps(res), flush=True)
+    cache.close()
 
 
 if __name__ == "__main__":

@@ -468,7 +468,8 @@ kvq_status kv_prefill_attention(kvq_cache* c, const void* q, const void* k, cons
                                 float sigma, uint32_t flags, void* out, void* stream) {
     if (!c || !q || !k || !v || !out) return KVQ_E_NULL;
     if (flags & ~KVQ_PREFILL_ATTENTION_ONLY) return KVQ_E_SHAPE;
-    if (n < 1 || n > INT32_MAX - 63) return KVQ_E_SHAPE;
+    // a (sequence, head) slice of the prompt is addressed with 32-bit byte offsets
+    if (n < 1 || n > (int64_t(1) << 23)) return KVQ_E_SHAPE;
     if (Hq < 1 || Hq % c->cfg.n_kv_heads != 0) return KVQ_E_SHAPE;
     // grid: (query blocks, query heads, sequences)
     if (Hq > 65535 || c->cfg.batch > 65535) return KVQ_E_SHAPE;

@@ -12,10 +12,10 @@
 // Work split: one four-wave workgroup per (64 query rows, query head,
 // sequence); wave w owns rows 16w .. 16w + 15.  It walks the 64-token key /
 // value tiles 0 .. i of its causal window (the diagonal tile last, with the
-// mask), staging each tile in LDS: keys row-major, values transposed
-// (channel-major), so that both products read 16-byte or 8-byte rows.
+// mask), staging each tile in LDS row-major (keys and values alike).
 //   S^T = K Q^T  (A = key rows from LDS, B = the query rows, in registers)
-//   O^T = V^T P^T (A = value columns from LDS, B = the weights, in registers)
+//   O^T = V^T P^T (A = value columns, read from the value rows with the
+//                 transposing ds_read_b64_tr_b16; B = the weights, in registers)
 // With these orientations each lane holds one query row in both results: the
 // weights of S^T's accumulator feed O^T's B operand without leaving the lane,
 // and the softmax rescale and the final 1/l stay lane-local.  Softmax in
@@ -23,10 +23,12 @@
 // more than 2^8 (weights stay <= 256 in fp16); weights are rounded to fp16
 // for the second product, l sums them in fp32.
 //
-// Fused quantize: the workgroup of the first query head of each KV head and
-// query block i also quantizes tile i (values of its rows, the key blocks it
-// completes, the unfilled block's rows into the residual) with the append
-// kernels' device code, so the cache equals kv_quantize_append's bit for bit.
+// Fused quantize: the workgroups of query block i quantize tile i (values of
+// its rows, the key blocks it completes, the unfilled block's rows into the
+// residual) from the copy they staged in LDS for their last (diagonal) step,
+// split over the KV head's query heads, with the append kernels' device code:
+// the cache equals kv_quantize_append's bit for bit and the prompt is read
+// from HBM once.
 #include "kvq_quant_dev.h"
 
 namespace kvq {
@@ -34,7 +36,9 @@ namespace {
 
 constexpr int PD = 128;     // head dim of q, k and v
 constexpr int PKS = 68;     // dwords per staged key row (128 fp16 + 8 pad)
-constexpr int PVS = 36;     // dwords per staged value column (64 fp16 + 8 pad)
+// dwords per staged value row (128 fp16 + 16 pad): the 16 lanes of a
+// transposed read name 4 rows x 4 channel quads, at banks 8e + 2q (mod 64)
+constexpr int PVR = 72;
 constexpr float PTAU = 8.0f;
 
 typedef _Float16 pf16x8 __attribute__((ext_vector_type(8)));
@@ -44,102 +48,127 @@ __device__ __forceinline__ pf16x8 as_pf16x8(uint32_t a, uint32_t b, uint32_t c, 
     typedef uint32_t u4v __attribute__((ext_vector_type(4)));
     return __builtin_bit_cast(pf16x8, u4v{a, b, c, d});
 }
-__device__ __forceinline__ uint32_t plo(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
-__device__ __forceinline__ uint32_t phi(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, h2{_Float16(a), _Float16(b)});
 }
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 struct PrefillLds {
     __attribute__((aligned(16))) uint32_t kl[64 * PKS];    // key rows of the tile
-    __attribute__((aligned(16))) uint32_t vt[PD * PVS];    // value columns of the tile
+    __attribute__((aligned(16))) uint32_t vl[64 * PVR];    // value rows of the tile
 };
 
-// One 64-token tile in registers: thread t holds key row t >> 2, channels
-// 32 (t & 3) .. + 31, and value rows 2 (t & 31), + 1, channels 16 (t >> 5) .. + 15
+// One 64-token tile in registers: thread t holds key and value row t >> 2,
+// channels 32 (t & 3) .. + 31
 struct PTile {
-    uint4 k[4];
-    uint4 va[2], vb[2];
+    uint4 k[4], v[4];
 };
 
-__device__ __forceinline__ void load_ptile(const PrefillArgs& a, const uint16_t* kbase, const uint16_t* vbase,
-                                           int t0, int tid, PTile& r) {
-    const int kr = t0 + (tid >> 2), kq = tid & 3;
-    const bool kin = kr < a.T;
-    const uint16_t* kp = kbase + int64_t(kin ? kr : 0) * PD + 32 * kq;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r.k[e] = kin ? ld16(kp + 8 * e) : make_uint4(0u, 0u, 0u, 0u);
-    const int vr = t0 + 2 * (tid & 31), vc = 16 * (tid >> 5);
-    const bool va = vr < a.T, vb = vr + 1 < a.T;
-    const uint16_t* vp = vbase + int64_t(va ? vr : 0) * PD + vc;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        r.va[e] = va ? ld16(vp + 8 * e) : make_uint4(0u, 0u, 0u, 0u);
-        r.vb[e] = vb ? ld16(vp + PD + 8 * e) : make_uint4(0u, 0u, 0u, 0u);
+typedef short ps4 __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j receives 16-bit
+// element j & 3 of the 8-byte rows named by lanes (j >> 2) + 4e, e = 0..3
+// (read off an in-bounds probe on gfx950)
+__device__ __forceinline__ uint2 ld_tr16(const uint32_t* p) {
+    const ps4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) ps4*)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+
+// staged tiles as the quantizers' inputs: tile row tok - t0
+struct LdsValueSrc {
+    const uint32_t* vl;
+    __device__ uint4 row8(int64_t, int64_t tok, int sub) const {
+        return *reinterpret_cast<const uint4*>(vl + tok * PVR + 4 * sub);
     }
+};
+struct LdsKeySrc {
+    const uint32_t* kl;
+    int64_t t0;
+    __device__ uint32_t pair(int64_t tok, int cp) const { return kl[(tok - t0) * PKS + cp]; }
+};
+
+// buffer resource over the n_rows rows of one (sequence, head) slice: rows
+// past the prompt read as zeros (the range check), without a branch
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const uint16_t* base, int n_rows) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, n_rows * PD * 2, 0x00020000);
+}
+__device__ __forceinline__ uint4 ldr(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+    const u4v v = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void load_rows(__amdgpu_buffer_rsrc_t rs, int t0, int tid, uint4* r) {
+    const int off = (t0 + (tid >> 2)) * (PD * 2) + 64 * (tid & 3);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = ldr(rs, off + 16 * e);
 }
 
 __device__ __forceinline__ void stage_ptile(const PTile& r, PrefillLds& L, int tid) {
     uint32_t* kd = L.kl + (tid >> 2) * PKS + 16 * (tid & 3);
+    uint32_t* vd = L.vl + (tid >> 2) * PVR + 16 * (tid & 3);
 #pragma unroll
     for (int e = 0; e < 4; ++e) *reinterpret_cast<uint4*>(kd + 4 * e) = r.k[e];
-    // value column c, dword tp: tokens 2tp, 2tp + 1
-    const int tp = tid & 31, c0 = 16 * (tid >> 5);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const uint32_t a[4] = {r.va[e].x, r.va[e].y, r.va[e].z, r.va[e].w};
-        const uint32_t b[4] = {r.vb[e].x, r.vb[e].y, r.vb[e].z, r.vb[e].w};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int c = c0 + 8 * e + 2 * w;
-            L.vt[c * PVS + tp] = plo(a[w], b[w]);
-            L.vt[(c + 1) * PVS + tp] = phi(a[w], b[w]);
-        }
-    }
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<uint4*>(vd + 4 * e) = r.v[e];
 }
 
 // The tile's share of the cache: values of rows t0 .. t0 + n - 1, the key
 // blocks inside them that the prompt fills, and the residual rows of the
-// unfilled block (the same device functions as the append kernels).
+// unfilled block, read from the staged tile (the append kernels' device
+// functions, so the same bits).  The work is six one-wave units, spread over
+// the grp workgroups of the KV head's query heads (workgroup r takes units
+// r, r + grp, ..., its k-th unit on wave k):
+//   units 0, 1: key channel pairs 32u .. 32u + 31 of the 64-token block
+//               (G = 64) or key block u (G = 32), then (unit 0) the residual;
+//   units 2..5: value rows 16 (u - 2) .. + 15.
 template <int G, int KB, int VB>
-__device__ void quantize_tile(const PrefillArgs& a, int64_t bh, int t0, int tid) {
+__device__ void quantize_tile(const PrefillArgs& a, const PrefillLds& L, int64_t bh, int t0, int r, int grp,
+                              int wave, int lane) {
     const int n = a.T - t0 < 64 ? a.T - t0 : 64;
-    {
+    const int nfull = a.T / G;   // key blocks the prompt fills
+    for (int u = r + grp * wave; u < 6; u += 4 * grp) {
+        if (u < 2) {
+            // one wave of the key threads of the tile's block(s): 64 per
+            // block for G = 32; for G = 64 a block takes two waves (row
+            // halves 32 lanes apart)
+            int64_t unit;
+            int cp, sp;
+            qdev::key_thread_coords<G, KB>(64 * u + lane, PD, unit, cp, sp);
+            const int64_t blk = t0 / G + unit;
+            if (blk < nfull) {
+                const qdev::KeyJob j{a.k + bh * int64_t(a.T) * PD, a.kr + bh * G * PD, blk * G, 0, 0,
+                                     bh * a.nblk_cap + blk};
+                qdev::quant_key_pair<G, KB>(j, PD, cp, sp, a.kc, a.ks, a.kz, LdsKeySrc{L.kl, t0});
+            }
+            if (u == 0) {
+                // residual: rows nfull * G .. T - 1 that lie in this tile
+                const int r0 = nfull * G > t0 ? nfull * G : t0;
+                for (int i = lane; i < (t0 + n - r0) * (PD / 8); i += 64) {
+                    const int t = r0 + i / (PD / 8), c = 8 * (i % (PD / 8));
+                    *reinterpret_cast<uint4*>(a.kr + (bh * G + (t - nfull * G)) * PD + c) =
+                        *reinterpret_cast<const uint4*>(L.kl + (t - t0) * PKS + c / 2);
+                }
+            }
+            continue;
+        }
+        const int v0 = 16 * (u - 2);
+        const int nv = n - v0 < 16 ? n - v0 : 16;
+        if (nv <= 0) continue;
         qdev::ValueArgs va;
-        va.vin = a.v + bh * int64_t(a.T) * PD;
+        va.vin = nullptr;   // rows come from the staged tile
         va.n_in = a.T;
-        va.row0 = t0;
-        va.n_tok = n;
+        va.row0 = t0 + v0;
+        va.n_tok = nv;
         va.vd = PD;
         va.BH = 1;
         va.codes = a.vc;
         va.scale = a.vs;
         va.zero = a.vz;
-        const qdev::ContigRows rows{a.cap, bh * a.cap + t0, n};
-        if (tid < qdev::value_threads(1, n, PD)) qdev::quant_values_thread<VB>(va, rows, tid);
-    }
-    constexpr int NB = 64 / G;
-    const int64_t per = qdev::key_threads_per_block<G, KB>(PD);   // whole waves when a pair spans lanes
-    const int nfull = a.T / G;                                    // blocks the prompt fills
-    if (tid < NB * per) {
-        int64_t unit;
-        int cp, sp;
-        qdev::key_thread_coords<G, KB>(tid, PD, unit, cp, sp);
-        const int64_t blk = t0 / G + unit;
-        if (blk < nfull) {
-            const qdev::KeyJob j{a.k + bh * int64_t(a.T) * PD, a.kr + bh * G * PD, blk * G, 0, 0,
-                                 bh * a.nblk_cap + blk};
-            qdev::quant_key_pair<G, KB>(j, PD, cp, sp, a.kc, a.ks, a.kz);
-        }
-    }
-    // residual: rows nfull * G .. T - 1 that lie in this tile
-    const int r0 = nfull * G > t0 ? nfull * G : t0;
-    for (int i = tid; i < (t0 + n - r0) * (PD / 8); i += 256) {
-        const int t = r0 + i / (PD / 8), c = 8 * (i % (PD / 8));
-        *reinterpret_cast<uint4*>(a.kr + (bh * G + (t - nfull * G)) * PD + c) =
-            ld16(a.k + (bh * int64_t(a.T) + t) * PD + c);
+        const qdev::ContigRows rows{a.cap, bh * a.cap + t0 + v0, nv};
+        // 4 rows x 8 channels per thread, whole 4-lane groups: lanes past
+        // the count would index the next (sequence, head)
+        if (lane < qdev::value_threads(1, nv, PD))
+            qdev::quant_values_thread<VB>(va, rows, lane, LdsValueSrc{L.vl + v0 * PVR});
     }
 }
 
@@ -153,18 +182,17 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
     const int hq = blockIdx.y, b = blockIdx.z;
     const int grp = a.Hq / a.Hkv, kvh = hq / grp;
     const int64_t bh = int64_t(b) * a.Hkv + kvh;
-    const uint16_t* kbase = a.k + bh * int64_t(a.T) * PD;
-    const uint16_t* vbase = a.v + bh * int64_t(a.T) * PD;
+    const __amdgpu_buffer_rsrc_t krs = slice_rsrc(a.k + bh * int64_t(a.T) * PD, a.T);
+    const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(a.v + bh * int64_t(a.T) * PD, a.T);
 
     // query row of this lane (the B operand of S^T): channels 32ks + 8kg .. + 7
     const int qrow = 64 * qb + 16 * wave + n;
     pf16x8 qb8[4];
     {
-        const bool in = qrow < a.T;
-        const uint16_t* qp = a.q + ((int64_t(b) * a.Hq + hq) * a.T + (in ? qrow : 0)) * PD + 8 * kg;
+        const __amdgpu_buffer_rsrc_t qrs = slice_rsrc(a.q + (int64_t(b) * a.Hq + hq) * int64_t(a.T) * PD, a.T);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const uint4 w = in ? ld16(qp + 32 * ks) : make_uint4(0u, 0u, 0u, 0u);
+            const uint4 w = ldr(qrs, qrow * (PD * 2) + 64 * ks + 16 * kg);
             qb8[ks] = as_pf16x8(w.x, w.y, w.z, w.w);
         }
     }
@@ -173,13 +201,16 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
     for (int c = 0; c < 8; ++c) O[c] = pf32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.0f;
 
+    // the next tile's rows: keys issued right after staging, values after
+    // the softmax (not live across the first product)
     PTile cur;
-    load_ptile(a, kbase, vbase, 0, tid, cur);
+    load_rows(krs, 0, tid, cur.k);
+    load_rows(vrs, 0, tid, cur.v);
     for (int j = 0; j <= qb; ++j) {
         __syncthreads();   // every wave is done with tile j - 1
         stage_ptile(cur, L, tid);
         __syncthreads();
-        if (j < qb) load_ptile(a, kbase, vbase, 64 * (j + 1), tid, cur);
+        if (j < qb) load_rows(krs, 64 * (j + 1), tid, cur.k);
 
         // ---- S^T = K Q^T: lane (n, kg) gets tokens 16cb + 4kg + i of row n
         pf32x4 S[4];
@@ -191,6 +222,7 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
                 const uint4 kw = *reinterpret_cast<const uint4*>(L.kl + (16 * cb + n) * PKS + 16 * ks + 4 * kg);
                 S[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_pf16x8(kw.x, kw.y, kw.z, kw.w), qb8[ks], S[cb], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // ---- online softmax (log2 units), the diagonal tile masked
         float s[16];
@@ -228,17 +260,22 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
             l += p0 + p1;
             pw[e / 2] = pack_h2(p0, p1);
         }
+        if (j < qb) load_rows(vrs, 64 * (j + 1), tid, cur.v);
         // ---- O^T += V^T P^T over 2 K-steps of 32 tokens: K order of lane
         // group kg = tokens 32ks + 4kg + 0..3, then 32ks + 16 + 4kg + 0..3
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const pf16x8 P = as_pf16x8(pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]);
+            // lane n names value row 32ks + 4kg + (n >> 2) (and + 16), channels
+            // 16c + 4 (n & 3) .. + 3; it receives channel 16c + n of the four
+            // rows 32ks + 4kg + e (then + 16), e = 0..3
+            const uint32_t* vr = L.vl + (32 * ks + 4 * kg + (n >> 2)) * PVR + 2 * (n & 3);
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const uint32_t* vr = L.vt + (16 * c + n) * PVS + 16 * ks + 2 * kg;
-                const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-                const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+                const uint2 lo = ld_tr16(vr + 8 * c);
+                const uint2 hi = ld_tr16(vr + 16 * PVR + 8 * c);
                 O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_pf16x8(lo.x, lo.y, hi.x, hi.y), P, O[c], 0, 0, 0);
+                if (c & 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -253,7 +290,9 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
             *reinterpret_cast<uint2*>(op + 16 * c) = make_uint2(pack_h2(O[c][0] * inv, O[c][1] * inv),
                                                                 pack_h2(O[c][2] * inv, O[c][3] * inv));
     }
-    if (a.quant && hq % grp == 0) quantize_tile<G, KB, VB>(a, bh, 64 * qb, tid);
+    // ---- the diagonal tile, still staged, into the cache (after the output,
+    // when the accumulators are dead)
+    if (a.quant) quantize_tile<G, KB, VB>(a, L, bh, 64 * qb, hq % grp, grp, wave, lane);
 }
 
 }  // namespace

@@ -143,16 +143,26 @@ struct PagedRows {
 // a multiple of 4 (vd / 8 is)
 __host__ __device__ inline int64_t value_threads(int BH, int64_t n_tok, int vd) { return int64_t(BH) * ((n_tok + VT - 1) / VT) * (vd / 8); }
 
+// Where a value row comes from: input row row0 + tok of (b, kvh) in global
+// memory (read once), or a tile staged in LDS.
+struct GlobalValueSrc {
+    const uint16_t* vin;
+    int64_t n_in, row0;
+    int vd;
+    __device__ uint4 row8(int64_t bh, int64_t tok, int sub) const {
+        return ld_once4(vin + ((bh * n_in) + row0 + tok) * vd + sub * 8);
+    }
+};
+
 // Thread idx < value_threads(...) quantizes 8 channels of up to VT rows;
 // the 4 threads of a 32-channel group are adjacent lanes and exchange their
 // min / max by shuffles, so callers keep whole 4-lane groups together.
 // Rows tok < rows.count(bh) are quantized into rows.row(bh, tok) (skipped
-// when that is negative).
-template <int BITS, class Rows>
-__device__ __forceinline__ void quant_values_thread(const ValueArgs& a, const Rows& rows, int64_t idx) {
+// when that is negative); src.row8(bh, tok, sub) supplies channels
+// 8 sub .. 8 sub + 7 of row tok.
+template <int BITS, class Rows, class Src>
+__device__ __forceinline__ void quant_values_thread(const ValueArgs& a, const Rows& rows, int64_t idx, const Src& src) {
 #pragma clang fp contract(off)
-    const uint16_t* __restrict__ vin = a.vin;
-    const int64_t n_in = a.n_in, row0 = a.row0;
     const int vd = a.vd;
     uint32_t* __restrict__ codes = a.codes;
     uint16_t* __restrict__ scale = a.scale;
@@ -169,8 +179,7 @@ __device__ __forceinline__ void quant_values_thread(const ValueArgs& a, const Ro
 #pragma unroll
     for (int j = 0; j < VT; ++j) {
         const int64_t tok = tq * VT + j;
-        raw[j] = tok < cnt ? ld_once4(vin + ((bh * n_in) + row0 + tok) * vd + sub * 8)
-                           : make_uint4(0u, 0u, 0u, 0u);
+        raw[j] = tok < cnt ? src.row8(bh, tok, sub) : make_uint4(0u, 0u, 0u, 0u);
     }
     const int vWT = vd * BITS / 32;
 #pragma unroll
@@ -212,6 +221,11 @@ __device__ __forceinline__ void quant_values_thread(const ValueArgs& a, const Ro
             zero[side] = float_to_half_bits(q.mn);
         }
     }
+}
+
+template <int BITS, class Rows>
+__device__ __forceinline__ void quant_values_thread(const ValueArgs& a, const Rows& rows, int64_t idx) {
+    quant_values_thread<BITS>(a, rows, idx, GlobalValueSrc{a.vin, a.n_in, a.row0, a.vd});
 }
 
 // -------------------------------------------------------------------- keys
@@ -287,10 +301,22 @@ struct KeyJob {
     int64_t dst;
 };
 
-template <int G, int BITS>
+// Where a key row comes from: the job's residual / input rows in global
+// memory (read once), or a tile staged in LDS.  pair(tok, cp) = channels
+// 2 cp, 2 cp + 1 of token tok.
+struct GlobalKeySrc {
+    const KeyJob& j;
+    int kd;
+    __device__ uint32_t pair(int64_t tok, int cp) const {
+        const uint16_t* row = tok < j.in_tok0 ? j.resid + (tok - j.res_tok0) * kd : j.kin + (tok - j.in_tok0) * kd;
+        return ld_once1(row + 2 * cp);
+    }
+};
+
+template <int G, int BITS, class Src>
 __device__ __forceinline__ void quant_key_pair(const KeyJob& j, int kd, int cp, int sp,
                                                uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
-                                               uint16_t* __restrict__ zero) {
+                                               uint16_t* __restrict__ zero, const Src& src) {
 #pragma clang fp contract(off)
     using S = KeyShape<G, BITS>;
     constexpr float L = float((1 << BITS) - 1);
@@ -299,8 +325,7 @@ __device__ __forceinline__ void quant_key_pair(const KeyJob& j, int kd, int cp, 
 #pragma unroll
     for (int i = 0; i < S::TG; ++i) {
         const int64_t tok = j.blk_tok0 + sp * S::TG + i;
-        const uint16_t* row = tok < j.in_tok0 ? j.resid + (tok - j.res_tok0) * kd : j.kin + (tok - j.in_tok0) * kd;
-        raw[i] = active ? ld_once1(row + 2 * cp) : 0u;
+        raw[i] = active ? src.pair(tok, cp) : 0u;
     }
     // per-channel min / max over the rows, both channels at once (packed
     // fp16, exact; -0 is canonicalised after), then across the row ranges
@@ -339,6 +364,13 @@ __device__ __forceinline__ void quant_key_pair(const KeyJob& j, int kd, int cp, 
         *reinterpret_cast<uint32_t*>(zero + side) =
             uint32_t(float_to_half_bits(q[0].mn)) | (uint32_t(float_to_half_bits(q[1].mn)) << 16);
     }
+}
+
+template <int G, int BITS>
+__device__ __forceinline__ void quant_key_pair(const KeyJob& j, int kd, int cp, int sp,
+                                               uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
+                                               uint16_t* __restrict__ zero) {
+    quant_key_pair<G, BITS>(j, kd, cp, sp, codes, scale, zero, GlobalKeySrc{j, kd});
 }
 
 }  // namespace qdev

@@ -322,7 +322,8 @@ kvq_status kv_decode_step(kvq_cache* cache, const void* k_fp16, const void* v_fp
  * fp32.  Needs key and value dim 128, key groups of 32 or 64 tokens, 2- or
  * 4-bit codes, 32-channel value groups (else KVQ_E_UNSUPPORTED) and, unless
  * KVQ_PREFILL_ATTENTION_ONLY, an empty cache (else KVQ_E_STATE).
- * Errors: KVQ_E_NULL, KVQ_E_SHAPE (n < 1, n_q_heads, flags, grid limits),
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE (n outside [1, 2^23], n_q_heads, flags,
+ * grid limits),
  * KVQ_E_CAPACITY (n > max_tokens), KVQ_E_ALIGN, KVQ_E_STATE,
  * KVQ_E_UNSUPPORTED, KVQ_E_HIP. */
 kvq_status kv_prefill_attention(kvq_cache* cache, const void* q_fp16, const void* k_fp16, const void* v_fp16,
