@@ -132,16 +132,25 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState
     for (int ksx = 0; ksx < 4; ++ksx) {
 #pragma unroll
         for (int be = 0; be < NBT; ++be) {
-            const uint4 a = *reinterpret_cast<const uint4*>(L.qa + (be * 8 + (n & 7)) * QSTR + 16 * ksx + 4 * kg);
-            const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
             // byte n & 3 of word row n >> 2 (G = 64; (n >> 2) & 1 of block be
             // for G = 32) of channels 32ksx + 8kg + 0..7
             const CodeRegs c = code_operands(ld_tr8(L.kl + key_row_dw<G>(ksx, be, kg, n)));
             if (G == 64) {
+                // A rows 0..7 = q' with rows 8..15 zero (token positions 0, 2)
+                // and the reverse (1, 3), from q' rows n and n ^ 8 (rows 8..15
+                // of the buffer are zero for G = 64): tokens 4n + 2v land in
+                // rows 0..7 and 4n + 2v + 1 in rows 8..15 of accumulator v
+                const uint4 ae = *reinterpret_cast<const uint4*>(L.qa + n * QSTR + 16 * ksx + 4 * kg);
+                const uint4 ao = *reinterpret_cast<const uint4*>(L.qa + (n ^ 8) * QSTR + 16 * ksx + 4 * kg);
+                const f16x8 Ae = as_f16x8(ae.x, ae.y, ae.z, ae.w), Ao = as_f16x8(ao.x, ao.y, ao.z, ao.w);
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x00030003u << (2 * u)), S[u], 0, 0, 0);
+                for (int v = 0; v < 2; ++v) {
+                    S[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, code_slice(c, 0x00030003u << (4 * v)), S[v], 0, 0, 0);
+                    S[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, code_slice(c, 0x00030003u << (4 * v + 2)), S[v], 0, 0, 0);
+                }
             } else {
+                const uint4 a = *reinterpret_cast<const uint4*>(L.qa + (be * 8 + (n & 7)) * QSTR + 16 * ksx + 4 * kg);
+                const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
 #pragma unroll
                 for (int v = 0; v < 2; ++v) {
                     const uint32_t mk = 0x00030003u << (2 * (2 * v + (n >> 3)));
@@ -151,17 +160,17 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState
         }
     }
 
-    // ---- softmax.  Lane (n, kg) holds rows 4kg..4kg+3; rows 8..15 repeat
-    // rows 0..7, so lanes kg and kg+2 see heads 2(kg&1), 2(kg&1)+1 (hi/lo row
-    // pairs) and split the columns' tokens so that each lane ends up with a
-    // token pair 4k + j, 4k + j + 2:
-    //   G = 64: tile u, column n is token 4n + u; lanes kg < 2 take tiles 0, 2
-    //           and kg >= 2 tiles 1, 3 (k = n, j = kg >> 1);
-    //   G = 32: tile 2be + v, column n is token
-    //           32be + 16((n & 7) >> 2) + 4(n & 3) + 2v + (n >> 3); lanes
-    //           kg < 2 take block 0 and kg >= 2 block 1 (j = n >> 3).
+    // ---- softmax.  Lane (n, kg) holds rows 4kg..4kg+3; lanes kg and kg+2
+    // see heads 2(kg&1), 2(kg&1)+1 (hi/lo row pairs) and split the columns'
+    // tokens so that each lane ends up with a token pair 4k + j, 4k + j + 2:
+    //   G = 64: accumulator v, column n holds token 4n + 2v in rows 0..7
+    //           (lanes kg < 2) and 4n + 2v + 1 in rows 8..15 (k = n,
+    //           j = kg >> 1);
+    //   G = 32: A rows 8..15 repeat rows 0..7; tile 2be + v, column n is
+    //           token 32be + 16((n & 7) >> 2) + 4(n & 3) + 2v + (n >> 3);
+    //           lanes kg < 2 take block 0 and kg >= 2 block 1 (j = n >> 3).
     const bool odd = (kg & 1) != 0;
-    const bool up2 = (kg >> 1) != 0;
+    [[maybe_unused]] const bool up2 = (kg >> 1) != 0;
     float sA[2], sB[2];
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
@@ -169,7 +178,7 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState
         float Sv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            Sv[e] = G == 64 ? (up2 ? S[2 * v + 1][e] : S[2 * v][e]) : (up2 ? S[2 + v][e] : S[v][e]);
+            Sv[e] = G == 64 ? S[v][e] : (up2 ? S[2 + v][e] : S[v][e]);
         const int up = G == 64 ? 2 * v + (kg >> 1) : 2 * v + (n >> 3);
         const int be = G == 64 ? 0 : (kg >> 1);
         const float f = p.sigma2 * __builtin_ldexpf(1.0f, 24 - 2 * up);
@@ -361,6 +370,10 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
     const int ntl = t_hi - t_lo;
 
     if (wave == 0) {
+        // G = 64 uses q' rows 0..7; rows 8..15 are the zero rows of the
+        // split A operands
+        if (G == 64)
+            for (int i = lane; i < 8 * QSTR; i += 64) L.k.qa[8 * QSTR + i] = 0u;
         // query channels 8 chunk .. 8 chunk + 7 of head hh, in quad order
         const uint4 raw = *reinterpret_cast<const uint4*>(p.q + ((int64_t(b) * p.Hq + hq0 + hh) * D + 8 * chunk));
         const uint32_t qv[4] = {pair_lo(raw.x, raw.y), pair_hi(raw.x, raw.y), pair_lo(raw.z, raw.w),
