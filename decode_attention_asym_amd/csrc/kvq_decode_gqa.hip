@@ -476,6 +476,7 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
 
 struct LdsK4 {
     __attribute__((aligned(16))) uint32_t kl[KTILE4_DW];
+    __attribute__((aligned(16))) uint32_t qz[QSTR];   // a zero row (the idle half of split A operands)
     __attribute__((aligned(16))) uint32_t qa[2 * 8 * QSTR];
     __attribute__((aligned(16))) uint32_t ksl[2 * 2 * 64];
     float bias[8];
@@ -528,36 +529,38 @@ __device__ __forceinline__ void key_tile4(const MfmaParams& p, KTile4& cur, KSta
     // ---- S = q' . codes: per K-step of 32 channels, two transposed reads
     // (tile tokens 0..31 and 32..63; for G = 32 the two blocks) of two
     // nibbles each.  S[2r + nib], column n = token 32r + 2n + nib.
-    f32x4 S[4];
+    f32x4 S[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) S[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 2; ++u) S[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ksx = 0; ksx < 4; ++ksx) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int be = G == 64 ? 0 : r;
-            const uint4 a = *reinterpret_cast<const uint4*>(L.qa + (be * 8 + (n & 7)) * QSTR + 16 * ksx + 4 * kg);
+            // q' in A rows 8r .. 8r + 7, the other half zero: half r of the
+            // tile lands in rows 8r .. 8r + 7 of the accumulators
+            const uint32_t* arow = (n >> 3) == r ? L.qa + (be * 8 + (n & 7)) * QSTR : L.qz;
+            const uint4 a = *reinterpret_cast<const uint4*>(arow + 16 * ksx + 4 * kg);
             const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
             const CodeRegs c = code_operands(ld_tr8(L.kl + key_row_dw4<G>(ksx, r, kg, n)));
 #pragma unroll
             for (int nib = 0; nib < 2; ++nib)
-                S[2 * r + nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x000F000Fu << (4 * nib)),
-                                                                       S[2 * r + nib], 0, 0, 0);
+                S[nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x000F000Fu << (4 * nib)), S[nib],
+                                                               0, 0, 0);
         }
     }
 
-    // ---- softmax: lanes kg and kg + 2 see heads 2(kg&1), 2(kg&1)+1 (rows 8..15
-    // repeat rows 0..7); lanes kg < 2 take the first half of the tile
-    // (r = 0), kg >= 2 the second, so a lane holds tokens 32r + 2n, + 1
+    // ---- softmax: lanes kg and kg + 2 see heads 2(kg&1), 2(kg&1)+1; lanes
+    // kg < 2 hold the first half of the tile (r = 0, rows 0..7), kg >= 2 the
+    // second (rows 8..15), so a lane holds tokens 32r + 2n, + 1
     const bool odd = (kg & 1) != 0;
-    const bool up2 = (kg >> 1) != 0;
     const int beh = G == 64 ? 0 : (kg >> 1);
     float sA[2], sB[2];
 #pragma unroll
     for (int nib = 0; nib < 2; ++nib) {
         float Sv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Sv[e] = up2 ? S[2 + nib][e] : S[nib][e];
+        for (int e = 0; e < 4; ++e) Sv[e] = S[nib][e];
         const float f = p.sigma2 * __builtin_ldexpf(1.0f, 24 - 4 * nib);
         sA[nib] = fmaf(Sv[0] + Sv[1], f, L.bias[beh * 4 + 2 * (kg & 1)]);
         sB[nib] = fmaf(Sv[2] + Sv[3], f, L.bias[beh * 4 + 2 * (kg & 1) + 1]);
@@ -734,6 +737,7 @@ __global__ __launch_bounds__(128) void k_decode_gqa4(MfmaParams p) {
     const int ntl = t_hi - t_lo;
 
     if (wave == 0) {
+        for (int i = lane; i < QSTR; i += 64) L.k.qz[i] = 0u;   // the zero row of the split A operands
         const uint4 raw = *reinterpret_cast<const uint4*>(p.q + ((int64_t(b) * p.Hq + hq0 + hh) * D + 8 * chunk));
         const uint32_t qv[4] = {pair_lo(raw.x, raw.y), pair_hi(raw.x, raw.y), pair_lo(raw.z, raw.w),
                                 pair_hi(raw.z, raw.w)};
