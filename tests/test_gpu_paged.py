@@ -278,7 +278,8 @@ def _rows_at(w, k_full, v_full, lens, n_new):
     return k, v
 
 
-@pytest.mark.parametrize("shape", ["gqa4_g64", "gqa4_g32", "mha_d128", "gqa4_4bit_g64"])
+@pytest.mark.parametrize("shape", ["gqa4_g64", "gqa4_g32", "mha_d128", "gqa4_4bit_g64", "gqa4_4bit_g32",
+                                   "mha_d128_4bit", "mha_d128_g32"])
 def test_paged_decode_step(orc, shape):
     """kv_paged_decode_step (append fused into the attention launch, lengths
     advanced on the device) against kv_paged_append + kv_paged_decode over
@@ -286,7 +287,7 @@ def test_paged_decode_step(orc, shape):
     every step, outputs bit-identical for every sequence whose block did not
     complete in the step, all within 2e-3 of the oracle."""
     t = torch()
-    G = 32 if shape == "gqa4_g32" else 64
+    G = 32 if shape in ("gqa4_g32", "gqa4_4bit_g32", "mha_d128_g32") else 64
     w = _workload(shape, 5 * G)
     lens0 = np.array([G - 1, G - 2, 0, 5, 2 * G - 1, 3 * G - 3][:w.batch], np.int32)
     steps = G + 2
