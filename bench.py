@@ -109,6 +109,21 @@ def profiled_traffic(variant: str, workload: str):
     return int(rec["traffic_bytes"])
 
 
+def gpu_clock_state():
+    """Current shader / memory clock and power of GPU 0 as rocm-smi prints
+    them (a child process reading the driver's counters; None when the tool
+    is missing or says nothing)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "-d", "0", "--showclocks", "--showpower"], capture_output=True, text=True,
+                           timeout=20)
+    except Exception:
+        return None
+    keep = [" ".join(ln.split()) for ln in r.stdout.splitlines()
+            if any(t in ln for t in ("sclk", "mclk", "Power (W)", "Socket Graphics Package Power", "fclk"))]
+    return keep or None
+
+
 def copy_probe():
     """A plain device-to-device copy of known size, for scaling the HBM byte
     counters (FETCH_SIZE / WRITE_SIZE) of the decode kernel."""
@@ -354,6 +369,7 @@ def main():
             "hbm_frac_whole_step": round(value / HBM_PEAK_GBPS, 4),
             "pass1_us_p10_p50_p90": [round(float(np.percentile(p1_sorted, x)) * 1e3, 2) for x in (10, 50, 90)],
             "copy_ceiling_GBps": round(copy_gbps, 1),
+            "gpu_clock_after_timed_steps": gpu_clock_state(),
             "pass1_frac_of_copy_ceiling": round(achieved / copy_gbps, 4),
             "quantize_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 2),
             "quantize_ms": round(q_ms, 4),
