@@ -68,7 +68,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-pairs", type=int, default=256)
+    ap.add_argument("--cpu-pairs", type=int, default=1024)
     ap.add_argument("--cpu-rows", type=int, default=100000, help="prefill: oracle rows timed for the CPU baseline")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--layers", type=int, default=0,
