@@ -471,8 +471,8 @@ kvq_status kv_prefill_attention(kvq_cache* c, const void* q, const void* k, cons
     // a (sequence, head) slice of the prompt is addressed with 32-bit byte offsets
     if (n < 1 || n > (int64_t(1) << 23)) return KVQ_E_SHAPE;
     if (Hq < 1 || Hq % c->cfg.n_kv_heads != 0) return KVQ_E_SHAPE;
-    // grid: (query blocks, query heads, sequences)
-    if (Hq > 65535 || c->cfg.batch > 65535) return KVQ_E_SHAPE;
+    // one grid dimension of (query blocks) x (query heads) x (sequences) workgroups
+    if (((n + 63) / 64) * int64_t(Hq) * c->cfg.batch > INT32_MAX) return KVQ_E_SHAPE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return KVQ_E_ALIGN;
     if (!prefill_supported(c->cfg)) return KVQ_E_UNSUPPORTED;
     const bool quant = (flags & KVQ_PREFILL_ATTENTION_ONLY) == 0;

@@ -177,9 +177,11 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
     __shared__ PrefillLds L;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, kg = lane >> 4;
-    // the longest causal windows start first
-    const int qb = int(gridDim.x) - 1 - int(blockIdx.x);
-    const int hq = blockIdx.y, b = blockIdx.z;
+    // one grid dimension, query block slowest: the longest causal windows of
+    // every (head, sequence) start first, the shortest fill the end
+    const int nqb = (a.T + 63) / 64, units = a.Hq * a.B;
+    const int qb = nqb - 1 - int(blockIdx.x) / units;
+    const int hq = int(blockIdx.x) % units % a.Hq, b = int(blockIdx.x) % units / a.Hq;
     const int grp = a.Hq / a.Hkv, kvh = hq / grp;
     const int64_t bh = int64_t(b) * a.Hkv + kvh;
     const __amdgpu_buffer_rsrc_t krs = slice_rsrc(a.k + bh * int64_t(a.T) * PD, a.T);
@@ -303,7 +305,7 @@ bool prefill_supported(const kvq_cache_cfg& c) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, const kvq_cache_cfg& c, hipStream_t st) {
-    const dim3 grid((a.T + 63) / 64, a.Hq, a.B);
+    const dim3 grid(unsigned((a.T + 63) / 64) * unsigned(a.Hq * a.B));
 #define KVQ_PF(GG, KK, VV)                                                                  \
     if (c.key.group == GG && c.key.bits == KK && c.value.bits == VV) {                      \
         hipLaunchKernelGGL((k_prefill<GG, KK, VV>), grid, dim3(256), 0, st, a);             \

@@ -379,7 +379,9 @@ def test_prefill_validation_before_hip():
         assert call(7, 2) == -2          # unknown flag
         assert call(4, 0) == -2          # n
         assert call(5, 7) == -2          # not a multiple of Hkv
-        assert call(5, 70000) == -2      # grid limit
+        a = list(ok)
+        a[4], a[5] = 1 << 23, 70000      # (query blocks) x heads x sequences above 2^31 - 1
+        assert L.kv_prefill_attention(*a) == -2
         for i in (1, 2, 3, 8):
             assert call(i, ok[i] + 8) == -3, i
         assert call(4, 257) == -4        # beyond capacity
