@@ -9,10 +9,14 @@
 // G-token blocks with the unfilled block kept in fp16, values per token).
 // This kernel does both in one pass over the prompt in HBM.
 //
-// Work split: one four-wave workgroup per (64 query rows, query head,
-// sequence); wave w owns rows 16w .. 16w + 15.  It walks the 64-token key /
-// value tiles 0 .. i of its causal window (the diagonal tile last, with the
-// mask), staging each tile in LDS row-major (keys and values alike).
+// Work split: one eight-wave workgroup per (128 query rows, query head,
+// sequence); wave w owns rows 16w .. 16w + 15.  The grid is one dimension
+// with the query block slowest, so the longest causal windows of every head
+// start first and the shortest fill the end.  A workgroup walks the 64-token
+// key / value tiles of its causal window, staging each tile in LDS row-major
+// (keys and values alike) for all eight waves, in two buffers so that one
+// barrier per tile suffices; on the two diagonal tiles a wave masks the tile
+// that crosses its rows and skips one that lies wholly after them.
 //   S^T = K Q^T  (A = key rows from LDS, B = the query rows, in registers)
 //   O^T = V^T P^T (A = value columns, read from the value rows with the
 //                 transposing ds_read_b64_tr_b16; B = the weights, in registers)
@@ -23,18 +27,20 @@
 // more than 2^8 (weights stay <= 256 in fp16); weights are rounded to fp16
 // for the second product, l sums them in fp32.
 //
-// Fused quantize: the workgroups of query block i quantize tile i (values of
-// its rows, the key blocks it completes, the unfilled block's rows into the
-// residual) from the copy they staged in LDS for their last (diagonal) step,
-// split over the KV head's query heads, with the append kernels' device code:
-// the cache equals kv_quantize_append's bit for bit and the prompt is read
-// from HBM once.
+// Fused quantize: the workgroups of query block i quantize its tiles 2i and
+// 2i + 1 (values of their rows, the key blocks they complete, the unfilled
+// block's rows into the residual) from the copies still staged in the two LDS
+// buffers after the loop, split over the KV head's query heads, with the
+// append kernels' device code: the cache equals kv_quantize_append's bit for
+// bit and the prompt is read from HBM once.
 #include "kvq_quant_dev.h"
 
 namespace kvq {
 namespace {
 
 constexpr int PD = 128;     // head dim of q, k and v
+constexpr int PNW = 8;      // waves per workgroup, 16 query rows each
+constexpr int PBM = 16 * PNW;
 constexpr int PKS = 68;     // dwords per staged key row (128 fp16 + 8 pad)
 // dwords per staged value row (128 fp16 + 16 pad): the 16 lanes of a
 // transposed read name 4 rows x 4 channel quads, at banks 8e + 2q (mod 64)
@@ -53,15 +59,20 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h2{_Float16(a), _Float16(b)});
 }
 
-struct PrefillLds {
+struct PrefillBuf {
     __attribute__((aligned(16))) uint32_t kl[64 * PKS];    // key rows of the tile
     __attribute__((aligned(16))) uint32_t vl[64 * PVR];    // value rows of the tile
 };
+// tile j is staged in buffer j & 1, so the block's two diagonal tiles are both
+// still staged after the loop (70 KB: two eight-wave workgroups per CU)
+struct PrefillLds {
+    PrefillBuf buf[2];
+};
 
-// One 64-token tile in registers: thread t holds key and value row t >> 2,
-// channels 32 (t & 3) .. + 31
+// One 64-token tile in registers: thread t holds key and value row t >> 3,
+// channels 16 (t & 7) .. + 15
 struct PTile {
-    uint4 k[4], v[4];
+    uint4 k[2], v[2];
 };
 
 typedef short ps4 __attribute__((ext_vector_type(4)));
@@ -98,88 +109,94 @@ __device__ __forceinline__ uint4 ldr(__amdgpu_buffer_rsrc_t r, int byte_off) {
 }
 
 __device__ __forceinline__ void load_rows(__amdgpu_buffer_rsrc_t rs, int t0, int tid, uint4* r) {
-    const int off = (t0 + (tid >> 2)) * (PD * 2) + 64 * (tid & 3);
+    const int off = (t0 + (tid >> 3)) * (PD * 2) + 32 * (tid & 7);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = ldr(rs, off + 16 * e);
+    for (int e = 0; e < 2; ++e) r[e] = ldr(rs, off + 16 * e);
 }
 
-__device__ __forceinline__ void stage_ptile(const PTile& r, PrefillLds& L, int tid) {
-    uint32_t* kd = L.kl + (tid >> 2) * PKS + 16 * (tid & 3);
-    uint32_t* vd = L.vl + (tid >> 2) * PVR + 16 * (tid & 3);
+__device__ __forceinline__ void stage_ptile(const PTile& r, PrefillBuf& L, int tid) {
+    uint32_t* kd = L.kl + (tid >> 3) * PKS + 8 * (tid & 7);
+    uint32_t* vd = L.vl + (tid >> 3) * PVR + 8 * (tid & 7);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) *reinterpret_cast<uint4*>(kd + 4 * e) = r.k[e];
+    for (int e = 0; e < 2; ++e) *reinterpret_cast<uint4*>(kd + 4 * e) = r.k[e];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) *reinterpret_cast<uint4*>(vd + 4 * e) = r.v[e];
+    for (int e = 0; e < 2; ++e) *reinterpret_cast<uint4*>(vd + 4 * e) = r.v[e];
 }
 
-// The tile's share of the cache: values of rows t0 .. t0 + n - 1, the key
-// blocks inside them that the prompt fills, and the residual rows of the
-// unfilled block, read from the staged tile (the append kernels' device
-// functions, so the same bits).  The work is six one-wave units, spread over
-// the grp workgroups of the KV head's query heads (workgroup r takes units
-// r, r + grp, ..., its k-th unit on wave k):
+// The block's share of the cache: for each of its tiles (2qb and, inside
+// the prompt, 2qb + 1), the values of its rows, the key blocks inside it that
+// the prompt fills, and the residual rows of the unfilled block, read from
+// the staged tile (the append kernels' device functions, so the same bits).
+// Per tile the work is six one-wave units, spread over the grp workgroups of
+// the KV head's query heads (workgroup r takes units r, r + grp, ..., the
+// k-th of them on wave k mod 8):
 //   units 0, 1: key channel pairs 32u .. 32u + 31 of the 64-token block
 //               (G = 64) or key block u (G = 32), then (unit 0) the residual;
 //   units 2..5: value rows 16 (u - 2) .. + 15.
 template <int G, int KB, int VB>
-__device__ void quantize_tile(const PrefillArgs& a, const PrefillLds& L, int64_t bh, int t0, int r, int grp,
-                              int wave, int lane) {
+__device__ void quantize_unit(const PrefillArgs& a, const PrefillBuf& L, int64_t bh, int t0, int u, int lane) {
     const int n = a.T - t0 < 64 ? a.T - t0 : 64;
     const int nfull = a.T / G;   // key blocks the prompt fills
-    for (int u = r + grp * wave; u < 6; u += 4 * grp) {
-        if (u < 2) {
-            // one wave of the key threads of the tile's block(s): 64 per
-            // block for G = 32; for G = 64 a block takes two waves (row
-            // halves 32 lanes apart)
-            int64_t unit;
-            int cp, sp;
-            qdev::key_thread_coords<G, KB>(64 * u + lane, PD, unit, cp, sp);
-            const int64_t blk = t0 / G + unit;
-            if (blk < nfull) {
-                const qdev::KeyJob j{a.k + bh * int64_t(a.T) * PD, a.kr + bh * G * PD, blk * G, 0, 0,
-                                     bh * a.nblk_cap + blk};
-                qdev::quant_key_pair<G, KB>(j, PD, cp, sp, a.kc, a.ks, a.kz, LdsKeySrc{L.kl, t0});
-            }
-            if (u == 0) {
-                // residual: rows nfull * G .. T - 1 that lie in this tile
-                const int r0 = nfull * G > t0 ? nfull * G : t0;
-                for (int i = lane; i < (t0 + n - r0) * (PD / 8); i += 64) {
-                    const int t = r0 + i / (PD / 8), c = 8 * (i % (PD / 8));
-                    *reinterpret_cast<uint4*>(a.kr + (bh * G + (t - nfull * G)) * PD + c) =
-                        *reinterpret_cast<const uint4*>(L.kl + (t - t0) * PKS + c / 2);
-                }
-            }
-            continue;
+    if (u < 2) {
+        // one wave of the key threads of the tile's block(s): 64 per block for
+        // G = 32; for G = 64 a block takes two waves (row halves 32 lanes apart)
+        int64_t unit;
+        int cp, sp;
+        qdev::key_thread_coords<G, KB>(64 * u + lane, PD, unit, cp, sp);
+        const int64_t blk = t0 / G + unit;
+        if (blk < nfull) {
+            const qdev::KeyJob j{a.k + bh * int64_t(a.T) * PD, a.kr + bh * G * PD, blk * G, 0, 0,
+                                 bh * a.nblk_cap + blk};
+            qdev::quant_key_pair<G, KB>(j, PD, cp, sp, a.kc, a.ks, a.kz, LdsKeySrc{L.kl, t0});
         }
-        const int v0 = 16 * (u - 2);
-        const int nv = n - v0 < 16 ? n - v0 : 16;
-        if (nv <= 0) continue;
-        qdev::ValueArgs va;
-        va.vin = nullptr;   // rows come from the staged tile
-        va.n_in = a.T;
-        va.row0 = t0 + v0;
-        va.n_tok = nv;
-        va.vd = PD;
-        va.BH = 1;
-        va.codes = a.vc;
-        va.scale = a.vs;
-        va.zero = a.vz;
-        const qdev::ContigRows rows{a.cap, bh * a.cap + t0 + v0, nv};
-        // 4 rows x 8 channels per thread, whole 4-lane groups: lanes past
-        // the count would index the next (sequence, head)
-        if (lane < qdev::value_threads(1, nv, PD))
-            qdev::quant_values_thread<VB>(va, rows, lane, LdsValueSrc{L.vl + v0 * PVR});
+        if (u == 0) {
+            // residual: rows nfull * G .. T - 1 that lie in this tile
+            const int r0 = nfull * G > t0 ? nfull * G : t0;
+            for (int i = lane; i < (t0 + n - r0) * (PD / 8); i += 64) {
+                const int t = r0 + i / (PD / 8), c = 8 * (i % (PD / 8));
+                *reinterpret_cast<uint4*>(a.kr + (bh * G + (t - nfull * G)) * PD + c) =
+                    *reinterpret_cast<const uint4*>(L.kl + (t - t0) * PKS + c / 2);
+            }
+        }
+        return;
+    }
+    const int v0 = 16 * (u - 2);
+    const int nv = n - v0 < 16 ? n - v0 : 16;
+    if (nv <= 0) return;
+    qdev::ValueArgs va;
+    va.vin = nullptr;   // rows come from the staged tile
+    va.n_in = a.T;
+    va.row0 = t0 + v0;
+    va.n_tok = nv;
+    va.vd = PD;
+    va.BH = 1;
+    va.codes = a.vc;
+    va.scale = a.vs;
+    va.zero = a.vz;
+    const qdev::ContigRows rows{a.cap, bh * a.cap + t0 + v0, nv};
+    // 4 rows x 8 channels per thread, whole 4-lane groups: lanes past the
+    // count would index the next (sequence, head)
+    if (lane < qdev::value_threads(1, nv, PD))
+        qdev::quant_values_thread<VB>(va, rows, lane, LdsValueSrc{L.vl + v0 * PVR});
+}
+
+template <int G, int KB, int VB>
+__device__ void quantize_block(const PrefillArgs& a, const PrefillLds& L, int64_t bh, int qb, int ntile, int r,
+                               int grp, int wave, int lane) {
+    for (int u = r + grp * wave; u < 12; u += PNW * grp) {
+        const int tile = 2 * qb + u / 6;
+        if (tile < ntile) quantize_unit<G, KB, VB>(a, L.buf[tile & 1], bh, 64 * tile, u % 6, lane);
     }
 }
 
 template <int G, int KB, int VB>
-__global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
+__global__ __launch_bounds__(64 * PNW) void k_prefill(PrefillArgs a) {
     __shared__ PrefillLds L;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, kg = lane >> 4;
     // one grid dimension, query block slowest: the longest causal windows of
     // every (head, sequence) start first, the shortest fill the end
-    const int nqb = (a.T + 63) / 64, units = a.Hq * a.B;
+    const int nqb = (a.T + PBM - 1) / PBM, units = a.Hq * a.B;
     const int qb = nqb - 1 - int(blockIdx.x) / units;
     const int hq = int(blockIdx.x) % units % a.Hq, b = int(blockIdx.x) % units / a.Hq;
     const int grp = a.Hq / a.Hkv, kvh = hq / grp;
@@ -188,7 +205,8 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
     const __amdgpu_buffer_rsrc_t vrs = slice_rsrc(a.v + bh * int64_t(a.T) * PD, a.T);
 
     // query row of this lane (the B operand of S^T): channels 32ks + 8kg .. + 7
-    const int qrow = 64 * qb + 16 * wave + n;
+    const int row0 = PBM * qb + 16 * wave;   // the wave's first row
+    const int qrow = row0 + n;
     pf16x8 qb8[4];
     {
         const __amdgpu_buffer_rsrc_t qrs = slice_rsrc(a.q + (int64_t(b) * a.Hq + hq) * int64_t(a.T) * PD, a.T);
@@ -203,81 +221,94 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
     for (int c = 0; c < 8; ++c) O[c] = pf32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.0f;
 
+    // tiles 0 .. ntile - 1: the causal window of the block's last row, within
+    // the prompt; tiles 2qb and 2qb + 1 are the block's own (quantized here)
+    const int last_tile = (a.T - 1) / 64;
+    const int ntile = (2 * qb + 1 < last_tile ? 2 * qb + 1 : last_tile) + 1;
     // the next tile's rows: keys issued right after staging, values after
     // the softmax (not live across the first product)
     PTile cur;
     load_rows(krs, 0, tid, cur.k);
     load_rows(vrs, 0, tid, cur.v);
-    for (int j = 0; j <= qb; ++j) {
-        __syncthreads();   // every wave is done with tile j - 1
-        stage_ptile(cur, L, tid);
+    for (int j = 0; j < ntile; ++j) {
+        // buffer j & 1 held tile j - 2: every wave finished that tile before
+        // the barrier after staging tile j - 1, so one barrier per tile
+        PrefillBuf& B = L.buf[j & 1];
+        stage_ptile(cur, B, tid);
         __syncthreads();
-        if (j < qb) load_rows(krs, 64 * (j + 1), tid, cur.k);
-
-        // ---- S^T = K Q^T: lane (n, kg) gets tokens 16cb + 4kg + i of row n
-        pf32x4 S[4];
+        if (j + 1 < ntile) load_rows(krs, 64 * (j + 1), tid, cur.k);
+        // this wave's rows see none of the tile (skip), part of it (mask), or all
+        const bool none = 64 * j > row0 + 15;
+        const bool part = 64 * j + 63 > row0;
+        uint32_t pw[8];
+        if (!none) {
+            // ---- S^T = K Q^T: lane (n, kg) gets tokens 16cb + 4kg + i of row n
+            pf32x4 S[4];
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            S[cb] = pf32x4{0.f, 0.f, 0.f, 0.f};
+            for (int cb = 0; cb < 4; ++cb) {
+                S[cb] = pf32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const uint4 kw = *reinterpret_cast<const uint4*>(L.kl + (16 * cb + n) * PKS + 16 * ks + 4 * kg);
-                S[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_pf16x8(kw.x, kw.y, kw.z, kw.w), qb8[ks], S[cb], 0, 0, 0);
+                for (int ks = 0; ks < 4; ++ks) {
+                    const uint4 kw = *reinterpret_cast<const uint4*>(B.kl + (16 * cb + n) * PKS + 16 * ks + 4 * kg);
+                    S[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_pf16x8(kw.x, kw.y, kw.z, kw.w), qb8[ks], S[cb],
+                                                                   0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // ---- online softmax (log2 units), the diagonal tile masked
-        float s[16];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s[4 * cb + i] = S[cb][i] * a.sigma2;
-        if (j == qb) {
+            // ---- online softmax (log2 units), tokens after the row masked
+            float s[16];
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (16 * cb + 4 * kg + i > 16 * wave + n) s[4 * cb + i] = -INFINITY;
+                for (int i = 0; i < 4; ++i) s[4 * cb + i] = S[cb][i] * a.sigma2;
+            if (part) {
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (64 * j + 16 * cb + 4 * kg + i > qrow) s[4 * cb + i] = -INFINITY;
+            }
+            float mx = s[0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+            if (__builtin_amdgcn_ballot_w64(mx > m + PTAU) != 0) {
+                // exact row maximum over the four lanes of the row (kg = 0..3)
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float mn = fmaxf(m, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m - mn);
+                m = mn;
+                l *= alpha;
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) O[c][i] *= alpha;
+            }
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(s[e] - m), p1 = __builtin_amdgcn_exp2f(s[e + 1] - m);
+                l += p0 + p1;
+                pw[e / 2] = pack_h2(p0, p1);
+            }
         }
-        float mx = s[0];
+        if (j + 1 < ntile) load_rows(vrs, 64 * (j + 1), tid, cur.v);
+        if (!none) {
+            // ---- O^T += V^T P^T over 2 K-steps of 32 tokens: K order of lane
+            // group kg = tokens 32ks + 4kg + 0..3, then 32ks + 16 + 4kg + 0..3
 #pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-        if (__builtin_amdgcn_ballot_w64(mx > m + PTAU) != 0) {
-            // exact row maximum over the four lanes of the row (kg = 0..3)
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mn = fmaxf(m, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m - mn);
-            m = mn;
-            l *= alpha;
+            for (int ks = 0; ks < 2; ++ks) {
+                const pf16x8 P = as_pf16x8(pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]);
+                // lane n names value row 32ks + 4kg + (n >> 2) (and + 16), channels
+                // 16c + 4 (n & 3) .. + 3; it receives channel 16c + n of the four
+                // rows 32ks + 4kg + e (then + 16), e = 0..3
+                const uint32_t* vr = B.vl + (32 * ks + 4 * kg + (n >> 2)) * PVR + 2 * (n & 3);
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) O[c][i] *= alpha;
-        }
-        uint32_t pw[8];
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(s[e] - m), p1 = __builtin_amdgcn_exp2f(s[e + 1] - m);
-            l += p0 + p1;
-            pw[e / 2] = pack_h2(p0, p1);
-        }
-        if (j < qb) load_rows(vrs, 64 * (j + 1), tid, cur.v);
-        // ---- O^T += V^T P^T over 2 K-steps of 32 tokens: K order of lane
-        // group kg = tokens 32ks + 4kg + 0..3, then 32ks + 16 + 4kg + 0..3
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const pf16x8 P = as_pf16x8(pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]);
-            // lane n names value row 32ks + 4kg + (n >> 2) (and + 16), channels
-            // 16c + 4 (n & 3) .. + 3; it receives channel 16c + n of the four
-            // rows 32ks + 4kg + e (then + 16), e = 0..3
-            const uint32_t* vr = L.vl + (32 * ks + 4 * kg + (n >> 2)) * PVR + 2 * (n & 3);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const uint2 lo = ld_tr16(vr + 8 * c);
-                const uint2 hi = ld_tr16(vr + 16 * PVR + 8 * c);
-                O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_pf16x8(lo.x, lo.y, hi.x, hi.y), P, O[c], 0, 0, 0);
-                if (c & 1) __builtin_amdgcn_sched_barrier(0);
+                for (int c = 0; c < 8; ++c) {
+                    const uint2 lo = ld_tr16(vr + 8 * c);
+                    const uint2 hi = ld_tr16(vr + 16 * PVR + 8 * c);
+                    O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_pf16x8(lo.x, lo.y, hi.x, hi.y), P, O[c], 0, 0, 0);
+                    if (c & 1) __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     }
@@ -292,9 +323,9 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a) {
             *reinterpret_cast<uint2*>(op + 16 * c) = make_uint2(pack_h2(O[c][0] * inv, O[c][1] * inv),
                                                                 pack_h2(O[c][2] * inv, O[c][3] * inv));
     }
-    // ---- the diagonal tile, still staged, into the cache (after the output,
-    // when the accumulators are dead)
-    if (a.quant) quantize_tile<G, KB, VB>(a, L, bh, 64 * qb, hq % grp, grp, wave, lane);
+    // ---- the block's tiles, both still staged, into the cache (after the
+    // output, when the accumulators are dead)
+    if (a.quant) quantize_block<G, KB, VB>(a, L, bh, qb, ntile, hq % grp, grp, wave, lane);
 }
 
 }  // namespace
@@ -305,10 +336,10 @@ bool prefill_supported(const kvq_cache_cfg& c) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, const kvq_cache_cfg& c, hipStream_t st) {
-    const dim3 grid(unsigned((a.T + 63) / 64) * unsigned(a.Hq * a.B));
+    const dim3 grid(unsigned((a.T + PBM - 1) / PBM) * unsigned(a.Hq * a.B));
 #define KVQ_PF(GG, KK, VV)                                                                  \
     if (c.key.group == GG && c.key.bits == KK && c.value.bits == VV) {                      \
-        hipLaunchKernelGGL((k_prefill<GG, KK, VV>), grid, dim3(256), 0, st, a);             \
+        hipLaunchKernelGGL((k_prefill<GG, KK, VV>), grid, dim3(64 * PNW), 0, st, a);         \
         return hipGetLastError();                                                           \
     }
     KVQ_PF(64, 2, 2)
