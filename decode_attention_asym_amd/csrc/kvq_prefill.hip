@@ -47,6 +47,11 @@ constexpr int PKS = 68;     // dwords per staged key row (128 fp16 + 8 pad)
 constexpr int PVR = 72;
 constexpr float PTAU = 8.0f;
 
+template <bool B>
+struct Diag {
+    static constexpr bool value = B;
+};
+
 typedef _Float16 pf16x8 __attribute__((ext_vector_type(8)));
 typedef float pf32x4 __attribute__((ext_vector_type(4)));
 
@@ -230,16 +235,18 @@ __global__ __launch_bounds__(64 * PNW) void k_prefill(PrefillArgs a) {
     PTile cur;
     load_rows(krs, 0, tid, cur.k);
     load_rows(vrs, 0, tid, cur.v);
-    for (int j = 0; j < ntile; ++j) {
+    auto step = [&](int j, auto diag) {
+        constexpr bool DIAG = decltype(diag)::value;
         // buffer j & 1 held tile j - 2: every wave finished that tile before
         // the barrier after staging tile j - 1, so one barrier per tile
         PrefillBuf& B = L.buf[j & 1];
         stage_ptile(cur, B, tid);
         __syncthreads();
         if (j + 1 < ntile) load_rows(krs, 64 * (j + 1), tid, cur.k);
-        // this wave's rows see none of the tile (skip), part of it (mask), or all
-        const bool none = 64 * j > row0 + 15;
-        const bool part = 64 * j + 63 > row0;
+        // every row sees all of a tile before the block's own two; on those two
+        // a wave's rows see none of the tile (skip), part of it (mask), or all
+        const bool none = DIAG && 64 * j > row0 + 15;
+        const bool part = DIAG && 64 * j + 63 > row0;
         uint32_t pw[8];
         if (!none) {
             // ---- S^T = K Q^T: lane (n, kg) gets tokens 16cb + 4kg + i of row n
@@ -255,12 +262,13 @@ __global__ __launch_bounds__(64 * PNW) void k_prefill(PrefillArgs a) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // ---- online softmax (log2 units), tokens after the row masked
+            // ---- online softmax (log2 units), tokens after the row masked; the
+            // logits stay unscaled, sigma2 enters the maximum and the exponent's FMA
             float s[16];
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s[4 * cb + i] = S[cb][i] * a.sigma2;
+                for (int i = 0; i < 4; ++i) s[4 * cb + i] = S[cb][i];
             if (part) {
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb)
@@ -271,6 +279,7 @@ __global__ __launch_bounds__(64 * PNW) void k_prefill(PrefillArgs a) {
             float mx = s[0];
 #pragma unroll
             for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+            mx *= a.sigma2;
             if (__builtin_amdgcn_ballot_w64(mx > m + PTAU) != 0) {
                 // exact row maximum over the four lanes of the row (kg = 0..3)
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -286,7 +295,8 @@ __global__ __launch_bounds__(64 * PNW) void k_prefill(PrefillArgs a) {
             }
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(s[e] - m), p1 = __builtin_amdgcn_exp2f(s[e + 1] - m);
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[e], a.sigma2, -m));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[e + 1], a.sigma2, -m));
                 l += p0 + p1;
                 pw[e / 2] = pack_h2(p0, p1);
             }
@@ -311,7 +321,12 @@ __global__ __launch_bounds__(64 * PNW) void k_prefill(PrefillArgs a) {
                 }
             }
         }
-    }
+    };
+    // tiles before the block's own two need no causal mask
+    const int nfull = 2 * qb < ntile ? 2 * qb : ntile;
+    int j = 0;
+    for (; j < nfull; ++j) step(j, Diag<false>{});
+    for (; j < ntile; ++j) step(j, Diag<true>{});
     // ---- l over the row's four lanes, O / l, fp16 rows to out
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
