@@ -41,9 +41,11 @@ namespace {
 constexpr int PD = 128;     // head dim of q, k and v
 constexpr int PNW = 8;      // waves per workgroup, 16 query rows each
 constexpr int PBM = 16 * PNW;
-constexpr int PKS = 68;     // dwords per staged key row (128 fp16 + 8 pad)
-// dwords per staged value row (128 fp16 + 16 pad): the 16 lanes of a
-// transposed read name 4 rows x 4 channel quads, at banks 8e + 2q (mod 64)
+// dwords per staged key and value row (128 fp16 + 16 pad).  A row stride of
+// 8 banks (mod 64) suits both the 16-byte key reads and the transposed value
+// reads: the LDS bank-conflict counter reads a third of what a 4-bank stride
+// gives for either array (measured over whole launches)
+constexpr int PKS = 72;
 constexpr int PVR = 72;
 constexpr float PTAU = 8.0f;
 
