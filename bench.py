@@ -110,18 +110,21 @@ def profiled_traffic(variant: str, workload: str):
 
 
 def gpu_clock_state():
-    """Current shader / memory clock and power of GPU 0 as rocm-smi prints
-    them (a child process reading the driver's counters; None when the tool
-    is missing or says nothing)."""
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "-d", "0", "--showclocks", "--showpower"], capture_output=True, text=True,
-                           timeout=20)
-    except Exception:
-        return None
-    keep = [" ".join(ln.split()) for ln in r.stdout.splitlines()
-            if any(t in ln for t in ("sclk", "mclk", "Power (W)", "Socket Graphics Package Power", "fclk"))]
-    return keep or None
+    """Current shader / memory / fabric clock levels of the first AMD GPU, as
+    the driver's sysfs files mark them ('*'); plain file reads, so no child
+    process starts from this GPU process.  None when the files are missing."""
+    import glob
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        keep = []
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    keep += [f"{name[7:]} {ln.strip()}" for ln in f if ln.rstrip().endswith("*")]
+            except OSError:
+                continue
+        if keep:
+            return keep
+    return None
 
 
 def copy_probe():

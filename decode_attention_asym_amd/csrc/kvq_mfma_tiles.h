@@ -41,10 +41,10 @@ __device__ __forceinline__ uint2 ld_stream(const uint2* p) {
 constexpr int D = 128;      // head dim
 constexpr int KTILE_DW = 512;   // key-code tile in LDS (dwords): the cache layout, copied
 constexpr int VTILE_DW = 528;   // value-code tile in LDS (dwords): the cache layout + pad
-// q' and p' rows are read as 16-byte A operands, lane n taking row n; the
-// row strides sit 8 banks apart (mod 64) for rows 0..7, which the LDS
-// bank-conflict counter showed to serve such reads with the fewest conflicts
-// (4 banks apart, as with 68 and 36 dwords, measured 2.5x the conflict cycles)
+// q' and p' rows are read as 16-byte A operands, lane n taking row n: with
+// these strides rows 0..7 start on eight distinct multiples of 8 banks
+// (mod 64), which the LDS bank-conflict counter showed to serve such reads
+// with the fewest conflicts (68- and 36-dword rows measured 2.5x the cycles)
 constexpr int QSTR = 72;    // dwords per q' row (128 fp16 + pad)
 constexpr int ASTR = 40;    // dwords per p' row (64 fp16 + pad)
 constexpr int PSTR = 68;    // floats per row of the weight tile in LDS
