@@ -71,6 +71,17 @@ void sizes_of(const kvq_cache_cfg& c, kvq_buffer_sizes* s) {
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E_HIP; }
 
+// An explicit split count must keep every run of the matrix-core kernels
+// within what their 32-bit buffer offsets address (nblk quantized blocks);
+// the automatic plan always does.
+bool splits_fit(const kvq_cache& c, Variant v, int n_splits, int64_t nblk) {
+    if (n_splits == 0 || (v != V_GQA && v != V_MHA)) return true;
+    const int64_t ntiles = nblk * c.cfg.key.group / 64;
+    int64_t s = n_splits < KVQ_MAX_SPLITS - 1 ? n_splits : KVQ_MAX_SPLITS - 1;
+    s = s < ntiles ? s : ntiles;
+    return runs_fit(c.cfg, ntiles, s);
+}
+
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 void paged_sizes_of(const kvq_cache_cfg& c, int32_t n_pages, kvq_buffer_sizes* s) {
@@ -218,6 +229,7 @@ kvq_status kv_decode_workspace_bytes(const kvq_cache* c, int32_t Hq, int32_t n_s
     if (n_splits < 0 || n_splits > KVQ_MAX_SPLITS) return KVQ_E_SHAPE;
     const Geom g = geom_of(c->cfg);
     const Variant v = pick_variant(*c, Hq);
+    if (!splits_fit(*c, v, n_splits, g.nblk_cap)) return KVQ_E_SHAPE;
     const int S = max_slots(*c, Hq, n_splits, v);   // covers every length up to capacity
     *bytes = uint64_t(g.B) * Hq * S * (g.vd + 2) * 4;
     return KVQ_OK;
@@ -235,6 +247,7 @@ kvq_status kv_decode_attention(const kvq_cache* c, const void* q, int32_t Hq, fl
     a.c = c;
     a.g = geom_of(c->cfg);
     const Variant v = pick_variant(*c, Hq);
+    if (!splits_fit(*c, v, n_splits, c->nblk)) return KVQ_E_SHAPE;
     a.q = q;
     a.Hq = Hq;
     a.sigma = sigma;
@@ -426,6 +439,7 @@ kvq_status kv_decode_step(kvq_cache* c, const void* k, const void* v, const void
     const int64_t T1 = c->T + 1;
     // the block count after the append (auto-flush when the key fills it)
     const int64_t nblk1 = c->nblk + (R + 1 >= g.kG ? 1 : 0);
+    if (!splits_fit(*c, v_, n_splits, nblk1)) return KVQ_E_SHAPE;
     const SplitPlan sp = plan_splits(*c, Hq, n_splits, T1, nblk1, v_);
     const uint64_t need = uint64_t(g.B) * Hq * sp.S * (g.vd + 2) * 4;
     if (ws_bytes < need) return KVQ_E_WORKSPACE;

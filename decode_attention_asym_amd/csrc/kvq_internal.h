@@ -124,6 +124,12 @@ struct SplitPlan {
 SplitPlan plan_splits(const kvq_cache& c, int Hq, int n_splits, int64_t T, int64_t nblk, Variant v);
 // Upper bound of SplitPlan::S over every T <= capacity.
 int max_slots(const kvq_cache& c, int Hq, int n_splits, Variant v);
+// Longest run of 64-token tiles one split of a matrix-core kernel may take
+// (its code bytes stay below 2^30), and whether S_main splits of ntiles
+// tiles respect it.  The automatic plans always do; an explicit split count
+// that does not is rejected.
+int64_t max_run_tiles(const kvq_cache_cfg& cfg);
+bool runs_fit(const kvq_cache_cfg& cfg, int64_t ntiles, int64_t S_main);
 
 bool gqa_supported(const kvq_cache& c, int Hq);
 bool gqa_cfg_supported(const kvq_cache_cfg& c, int Hq);

@@ -41,6 +41,23 @@ int64_t wg_target(const kvq_cache_cfg& cfg, Variant v) {
     if (v == V_GQA) return cfg.key.bits == 2 ? 6144 : 3072;
     return 2048;
 }
+}  // namespace
+
+// The matrix-core kernels address a split's code run through a buffer
+// resource with 32-bit byte offsets: a run holds at most 2^30 bytes of key
+// or value codes (2^19 tiles of 64 tokens at 2 bits, 2^18 at 4 bits).
+int64_t max_run_tiles(const kvq_cache_cfg& cfg) {
+    const int64_t bits = cfg.key.bits > cfg.value.bits ? cfg.key.bits : cfg.value.bits;
+    const int64_t dim = cfg.key.dim > cfg.value.dim ? cfg.key.dim : cfg.value.dim;
+    return (int64_t(1) << 30) / (64 * dim * bits / 8);
+}
+
+bool runs_fit(const kvq_cache_cfg& cfg, int64_t ntiles, int64_t S_main) {
+    return S_main < 1 || (ntiles + S_main - 1) / S_main <= max_run_tiles(cfg);
+}
+
+namespace {
+
 int64_t auto_main(const kvq_cache& c, int Hq, Variant v, int64_t ntiles) {
     // MLA: one four-wave workgroup per CU, Hq / 64 of them per sequence and split
     if (v == V_MLA) return clamp64((256 * 64 / Hq + c.cfg.batch - 1) / c.cfg.batch, 1, KVQ_MAX_SPLITS);
@@ -53,6 +70,11 @@ int64_t auto_main(const kvq_cache& c, int Hq, Variant v, int64_t ntiles) {
     if (tiled) {
         const int64_t min_run = v == V_MHA ? 8 : 16;
         want = want < (ntiles + min_run - 1) / min_run ? want : (ntiles + min_run - 1) / min_run;
+        // and no run longer than a buffer resource addresses (at most 128
+        // splits for the 2^31-token capacity limit)
+        const int64_t max_run = max_run_tiles(c.cfg);
+        const int64_t need = (ntiles + max_run - 1) / max_run;
+        want = want > need ? want : need;
     }
     return clamp64(want, 1, KVQ_MAX_SPLITS);
 }

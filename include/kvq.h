@@ -152,7 +152,11 @@ kvq_status kv_quantize_append(kvq_cache* cache, const void* k_fp16, const void* 
 
 /* Quantize the residual as the next key block if it holds exactly G keys;
  * otherwise do nothing (a partial block is never quantized, which is why the
- * residual exists).  *n_blocks_flushed (may be NULL) receives 1 or 0. */
+ * residual exists: "İddia ve Gerçeklik: KIVI" keeps the keys of the group
+ * that is not full yet in full precision, since per-channel statistics need
+ * all G of its tokens).  It serves appends made with KVQ_APPEND_NO_AUTOFLUSH;
+ * the default append flushes by itself.  *n_blocks_flushed (may be NULL)
+ * receives 1 or 0.  Errors: KVQ_E_NULL, KVQ_E_HIP. */
 kvq_status kv_flush_residual(kvq_cache* cache, void* hip_stream, int32_t* n_blocks_flushed);
 
 /* Split-K: the context is cut into n_splits contiguous token ranges handled
@@ -160,8 +164,12 @@ kvq_status kv_flush_residual(kvq_cache* cache, void* hip_stream, int32_t* n_bloc
 #define KVQ_MAX_SPLITS 256
 
 /* Workspace bytes kv_decode_attention needs for n_q_heads and n_splits
- * (0 = automatic; the automatic figure covers every cache length up to
- * max_tokens).  Errors: KVQ_E_NULL, KVQ_E_SHAPE. */
+ * (0 = automatic; the figure covers every cache length up to max_tokens).
+ * The matrix-core kernels address one split's codes with 32-bit offsets: an
+ * explicit n_splits that would give a split more than 2^30 bytes of key or
+ * value codes at full capacity (2^25 tokens at 2 bits, 2^24 at 4 bits, for
+ * dim 128) is rejected with KVQ_E_SHAPE; the automatic plan never does.
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE. */
 kvq_status kv_decode_workspace_bytes(const kvq_cache* cache, int32_t n_q_heads,
                                      int32_t n_splits, uint64_t* bytes);
 
@@ -174,8 +182,10 @@ kvq_status kv_decode_workspace_bytes(const kvq_cache* cache, int32_t n_q_heads,
  * KIVI"; "QuantMLA Mimarisi ve Temel Bileşenleri").  q_fp16, out_fp16 and
  * workspace are caller-owned device arrays, 16-byte aligned.
  * Errors: KVQ_E_NULL, KVQ_E_SHAPE (n_q_heads not a positive multiple of
- * Hkv, n_splits outside [0, KVQ_MAX_SPLITS]), KVQ_E_ALIGN, KVQ_E_STATE (no
- * tokens), KVQ_E_WORKSPACE, KVQ_E_HIP. */
+ * Hkv, n_splits outside [0, KVQ_MAX_SPLITS], or an explicit n_splits whose
+ * splits would exceed 2^30 bytes of codes each at the current length, as
+ * for kv_decode_workspace_bytes), KVQ_E_ALIGN, KVQ_E_STATE (no tokens),
+ * KVQ_E_WORKSPACE, KVQ_E_HIP. */
 kvq_status kv_decode_attention(const kvq_cache* cache, const void* q_fp16, int32_t n_q_heads,
                                float softmax_scale, int32_t n_splits, void* out_fp16,
                                void* workspace, uint64_t workspace_bytes, void* hip_stream);

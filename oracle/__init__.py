@@ -46,12 +46,23 @@ class OrcCache(C.Structure):
                 ("v_zero", C.c_void_p)]
 
 
+def default_threads() -> int:
+    """Worker threads for the oracle: the CPUs this process may run on, at
+    most 16 (a GPU host's share per GPU, whatever the machine's count)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def lib():
-    """Load the oracle library, building it first only if it is missing."""
+    """Load the oracle library.  It is compiled by build() only (never here:
+    a process that has initialised a GPU must not start a compiler)."""
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
-            build()
+            raise RuntimeError(f"{_LIB} is not built; run __graft_entry__.build() or oracle.build()")
         L = C.CDLL(_LIB)
         p, i64, i32 = C.c_void_p, C.c_int64, C.c_int32
         L.orc_half_to_float.restype = C.c_float
@@ -133,8 +144,23 @@ def unpack(words, n: int, bits: int) -> np.ndarray:
     return codes
 
 
-def quantize_keys(k_bits, G: int, bits: int, nblk_cap: int | None = None):
-    """k_bits: uint16 [B][H][T][D] -> dict(k_codes, k_scale, k_zero, k_resid, R)."""
+def _per_sequence(fn, B: int, threads: int | None) -> None:
+    """Run fn(b) for every sequence b, on up to `threads` threads (the C
+    calls release the GIL; each writes a disjoint slice)."""
+    threads = default_threads() if threads is None else max(1, threads)
+    if threads == 1 or B == 1:
+        for b in range(B):
+            fn(b)
+        return
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(max_workers=min(threads, B)) as ex:
+        list(ex.map(fn, range(B)))
+
+
+def quantize_keys(k_bits, G: int, bits: int, nblk_cap: int | None = None, threads: int | None = 1):
+    """k_bits: uint16 [B][H][T][D] -> dict(k_codes, k_scale, k_zero, k_resid, R).
+    threads > 1 (None = default_threads()) quantizes the sequences in
+    parallel, one oracle call each; the result is the same."""
     k = np.ascontiguousarray(k_bits, dtype=np.uint16)
     B, H, T, D = k.shape
     if nblk_cap is None:
@@ -144,15 +170,21 @@ def quantize_keys(k_bits, G: int, bits: int, nblk_cap: int | None = None):
     scale = np.zeros((B, H, nblk_cap, D), np.uint16)
     zero = np.zeros((B, H, nblk_cap, D), np.uint16)
     resid = np.zeros((B, H, G, D), np.uint16)
-    R = lib().orc_quantize_keys(_ptr(k), B, H, T, D, G, bits, nblk_cap,
-                                _ptr(codes), _ptr(scale), _ptr(zero), _ptr(resid))
-    if R < 0:
+    rs = [0] * B
+
+    def one(b):
+        rs[b] = lib().orc_quantize_keys(_ptr(k[b]), 1, H, T, D, G, bits, nblk_cap, _ptr(codes[b]), _ptr(scale[b]),
+                                        _ptr(zero[b]), _ptr(resid[b]))
+
+    _per_sequence(one, B, threads)
+    if min(rs) < 0:
         raise ValueError("oracle quantize_keys rejected its input")
-    return dict(k_codes=codes, k_scale=scale, k_zero=zero, k_resid=resid, R=int(R))
+    return dict(k_codes=codes, k_scale=scale, k_zero=zero, k_resid=resid, R=int(rs[0]))
 
 
-def quantize_values(v_bits, Gv: int, bits: int, tok_cap: int | None = None):
-    """v_bits: uint16 [B][H][T][D] -> dict(v_codes, v_scale, v_zero)."""
+def quantize_values(v_bits, Gv: int, bits: int, tok_cap: int | None = None, threads: int | None = 1):
+    """v_bits: uint16 [B][H][T][D] -> dict(v_codes, v_scale, v_zero); threads
+    as for quantize_keys."""
     v = np.ascontiguousarray(v_bits, dtype=np.uint16)
     B, H, T, D = v.shape
     if tok_cap is None:
@@ -160,9 +192,14 @@ def quantize_values(v_bits, Gv: int, bits: int, tok_cap: int | None = None):
     codes = np.zeros((B, H, tok_cap, D * bits // 32), np.uint32)
     scale = np.zeros((B, H, tok_cap, D // Gv), np.uint16)
     zero = np.zeros((B, H, tok_cap, D // Gv), np.uint16)
-    rc = lib().orc_quantize_values(_ptr(v), B, H, T, D, Gv, bits, tok_cap,
-                                   _ptr(codes), _ptr(scale), _ptr(zero))
-    if rc != 0:
+    rcs = [0] * B
+
+    def one(b):
+        rcs[b] = lib().orc_quantize_values(_ptr(v[b]), 1, H, T, D, Gv, bits, tok_cap, _ptr(codes[b]), _ptr(scale[b]),
+                                           _ptr(zero[b]))
+
+    _per_sequence(one, B, threads)
+    if min(rcs) != 0:
         raise ValueError("oracle quantize_values rejected its input")
     return dict(v_codes=codes, v_scale=scale, v_zero=zero)
 
@@ -188,23 +225,24 @@ class Cache:
 
 
 def build_cache(k_bits, v_bits, kG, kbits, vG, vbits, nblk_cap=None, tok_cap=None,
-                kq_blocks: int | None = None) -> Cache:
+                kq_blocks: int | None = None, threads: int | None = 1) -> Cache:
     """Oracle cache of T tokens.  kq_blocks (default floor(T/kG)) quantized
-    key blocks; the remaining T - kq_blocks*kG (<= kG) keys stay fp16."""
+    key blocks; the remaining T - kq_blocks*kG (<= kG) keys stay fp16.
+    threads: as for quantize_keys."""
     T = k_bits.shape[2]
     assert v_bits.shape[2] == T
     if kq_blocks is None:
-        keys = quantize_keys(k_bits, kG, kbits, nblk_cap)
+        keys = quantize_keys(k_bits, kG, kbits, nblk_cap, threads=threads)
         kq = -1
     else:
         Tq = kq_blocks * kG
         assert 0 <= T - Tq <= kG
         keys = quantize_keys(np.ascontiguousarray(k_bits[:, :, :Tq]), kG, kbits,
-                             nblk_cap if nblk_cap is not None else max(1, kq_blocks))
+                             nblk_cap if nblk_cap is not None else max(1, kq_blocks), threads=threads)
         keys["k_resid"][:, :, :T - Tq] = k_bits[:, :, Tq:]
         keys["R"] = T - Tq
         kq = kq_blocks
-    values = quantize_values(v_bits, vG, vbits, tok_cap)
+    values = quantize_values(v_bits, vG, vbits, tok_cap, threads=threads)
     return Cache(T, kG, kbits, vG, vbits, keys, values, kq)
 
 
@@ -233,7 +271,7 @@ def _attention(fn, cache: Cache, q_bits, sigma, pairs, nthreads):
         out = np.empty((pa.shape[0], cache.s.vd), np.float64)
         pp, n = _ptr(pa), pa.shape[0]
     if nthreads is None:
-        nthreads = os.cpu_count() or 1
+        nthreads = default_threads()
     rc = fn(C.byref(cache.s), _ptr(q), Hq, C.c_float(sigma), pp, n, _ptr(out), int(nthreads))
     if rc != 0:
         raise ValueError("oracle attention rejected its input")
@@ -266,7 +304,7 @@ def prefill_attention(q_bits, k_bits, v_bits, sigma: float, rows=None, nthreads=
     rr = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
     out = np.empty((rr.shape[0], dv), np.float64)
     if nthreads is None:
-        nthreads = os.cpu_count() or 1
+        nthreads = default_threads()
     L = lib()
     rc = L.orc_prefill_attention(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, T, d, dv, C.c_double(sigma), _ptr(rr),
                                  rr.shape[0], _ptr(out), int(nthreads))

@@ -10,6 +10,12 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    # The oracle library is compiled only by its build(); a fresh checkout
+    # gets it here, before any test has touched a GPU (a process that has
+    # initialised one must not start a compiler).
+    import oracle
+    if not os.path.exists(oracle._LIB):
+        oracle.build()
 
 
 @pytest.fixture(scope="session")

@@ -147,6 +147,28 @@ def test_decode_validation_before_hip():
         kvq.kv_cache_destroy(h)
 
 
+@pytest.mark.parametrize("kbits,limit_tokens", [(2, 1 << 25), (4, 1 << 24)])
+def test_split_runs_stay_within_32_bit_offsets(kbits, limit_tokens):
+    """A matrix-core split addresses its codes with 32-bit byte offsets: an
+    explicit split count that would give one split more than 2^30 bytes of
+    codes (2^19 tiles at 2 bits, 2^18 at 4) is refused before any HIP call;
+    the automatic plan splits such caches further by itself."""
+    cap = 1 << 27
+    cfg = kivi_cfg(batch=1, n_kv_heads=1, max_tokens=cap, kG=64, kbits=kbits, vbits=kbits)
+    h = kvq.kv_cache_init(cfg, kvq.CacheBuffers(*FAKE))
+    try:
+        assert kvq.kv_decode_variant(h, 4) == "gqa_mfma"
+        need = cap // limit_tokens                       # splits of at most limit_tokens each
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kv_decode_workspace_bytes(h, 4, need - 1)
+        assert e.value.status == -2
+        assert kvq.kv_decode_workspace_bytes(h, 4, need) == 4 * (need + 1) * (128 + 2) * 4
+        auto = kvq.kv_decode_workspace_bytes(h, 4, 0) // (4 * (128 + 2) * 4) - 1
+        assert need <= auto <= kvq.KVQ_MAX_SPLITS - 1
+    finally:
+        kvq.kv_cache_destroy(h)
+
+
 def test_status_strings():
     for s in kvq.STATUS:
         assert kvq.kvq_status_str(s) not in ("", "unknown status")
