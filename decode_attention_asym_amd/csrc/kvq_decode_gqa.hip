@@ -11,11 +11,13 @@
 // Haritası"), which makes QK^T and PV dense enough for the matrix cores.
 //
 // How the contractions reach v_mfma_f32_16x16x32_f16 exactly:
-//  * a 2-bit code c placed in bits [2u, 2u+1] of an fp16 lane (all other bits
-//    zero) is the subnormal c * 4^u * 2^-24: exact, and gfx950 MFMA consumes
-//    fp16 subnormals exactly.  One v_perm_b32 gathers one code byte from
-//    each of two words into the two fp16 halves of a register; one AND per
-//    code position then yields an operand register.  The power-of-two
+//  * a 2-bit code c alone in bits [f, f+1] of an fp16 lane (all other bits
+//    zero) is the exact subnormal c * 2^(f - 24).  The transposed LDS read
+//    hands each lane the code bytes of its MFMA column; one shift per
+//    register of two bytes puts them at bit 6 or bit 2 of the fp16 halves,
+//    and one AND per code position then leaves one code in bits 6..7 or
+//    8..9 of each half (fields high in the mantissa keep the matrix cores'
+//    sums accurate; kvq_mfma_tiles.h, code_operands).  The power-of-two
 //    factors are undone on the fp32 results.
 //  * keys: khat = code * s + z with s, z per (block, channel).  The scale is
 //    folded into the query (q' = q * s, exact in fp32) which is fed as two
@@ -148,16 +150,16 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState
                 const f16x8 Ae = as_f16x8(ae.x, ae.y, ae.z, ae.w), Ao = as_f16x8(ao.x, ao.y, ao.z, ao.w);
 #pragma unroll
                 for (int v = 0; v < 2; ++v) {
-                    S[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, code_slice(c, 0x00030003u << (4 * v)), S[v], 0, 0, 0);
-                    S[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, code_slice(c, 0x00030003u << (4 * v + 2)), S[v], 0, 0, 0);
+                    S[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ae, code_slice2(c, 2 * v), S[v], 0, 0, 0);
+                    S[v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ao, code_slice2(c, 2 * v + 1), S[v], 0, 0, 0);
                 }
             } else {
                 const uint4 a = *reinterpret_cast<const uint4*>(L.qa + (be * 8 + (n & 7)) * QSTR + 16 * ksx + 4 * kg);
                 const f16x8 A = as_f16x8(a.x, a.y, a.z, a.w);
 #pragma unroll
                 for (int v = 0; v < 2; ++v) {
-                    const uint32_t mk = 0x00030003u << (2 * (2 * v + (n >> 3)));
-                    S[2 * be + v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, mk), S[2 * be + v], 0, 0, 0);
+                    const uint32_t mk = code_mask2(n >> 3);   // position 2v + (n >> 3)
+                    S[2 * be + v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice_set(c, v != 0, mk), S[2 * be + v], 0, 0, 0);
                 }
             }
         }
@@ -184,7 +186,7 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, KState
             Sv[e] = G == 64 ? S[v][e] : (up2 ? S[2 + v][e] : S[v][e]);
         const int up = G == 64 ? 2 * v + (kg >> 1) : 2 * v + (n >> 3);
         const int be = G == 64 ? 0 : (kg >> 1);
-        const float f = p.sigma2 * __builtin_ldexpf(1.0f, 24 - 2 * up);
+        const float f = p.sigma2 * code_unscale2(up);
         sA[v] = fmaf(Sv[0] + Sv[1], f, L.bias[be * 4 + 2 * (kg & 1)]);
         sB[v] = fmaf(Sv[2] + Sv[3], f, L.bias[be * 4 + 2 * (kg & 1) + 1]);
     }
@@ -317,7 +319,7 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
             const CodeRegs c = code_operands(ld_tr8(L.vl + value_row_dw(ksx, P, kg, n)));
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                st.O[P][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x00030003u << (2 * u)),
+                st.O[P][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice2(c, u),
                                                                     st.O[P][u], 0, 0, 0);
         }
     }
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
                 for (int u = 0; u < 4; ++u) {
                     const int c = 64 * P + 32 * (n >> 3) + 4 * (n & 7) + u;
                     const int g = 2 * P + (n >> 3);
-                    const float f = __builtin_ldexpf(1.0f, 24 - 2 * u);
+                    const float f = code_unscale2(u);
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
                         const int h = 2 * (kg & 1) + j;
@@ -475,7 +477,8 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
 // ---------------------------------------------------------------------------
 // 4-bit keys and values: the same two-wave pipeline over the 4 KB tiles of
 // kvq_mfma_tiles.h.  A code byte holds two tokens (keys) or two channels
-// (values), taken by the masks 0x000F000F << 4 nib.
+// (values), taken by one mask each from the copies of the bytes shifted to
+// put the low or the high nibble at bits 6..9 of the fp16 halves.
 
 struct LdsK4 {
     __attribute__((aligned(16))) uint32_t kl[KTILE4_DW];
@@ -548,7 +551,7 @@ __device__ __forceinline__ void key_tile4(const MfmaParams& p, KTile4& cur, KSta
             const CodeRegs c = code_operands(ld_tr8(L.kl + key_row_dw4<G>(ksx, r, kg, n)));
 #pragma unroll
             for (int nib = 0; nib < 2; ++nib)
-                S[nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x000F000Fu << (4 * nib)), S[nib],
+                S[nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice4(c, nib), S[nib],
                                                                0, 0, 0);
         }
     }
@@ -564,7 +567,7 @@ __device__ __forceinline__ void key_tile4(const MfmaParams& p, KTile4& cur, KSta
         float Sv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) Sv[e] = S[nib][e];
-        const float f = p.sigma2 * __builtin_ldexpf(1.0f, 24 - 4 * nib);
+        const float f = p.sigma2 * code_unscale4();
         sA[nib] = fmaf(Sv[0] + Sv[1], f, L.bias[beh * 4 + 2 * (kg & 1)]);
         sB[nib] = fmaf(Sv[2] + Sv[3], f, L.bias[beh * 4 + 2 * (kg & 1) + 1]);
     }
@@ -689,7 +692,7 @@ __device__ __forceinline__ void value_tile4(const MfmaParams& p, VTile4& cur, VS
             const CodeRegs c = code_operands(ld_tr8(L.vl + value_row_dw4(ksx, P, kg, n)));
 #pragma unroll
             for (int nib = 0; nib < 2; ++nib)
-                st.O[P][nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x000F000Fu << (4 * nib)),
+                st.O[P][nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice4(c, nib),
                                                                       st.O[P][nib], 0, 0, 0);
         }
     }
@@ -810,7 +813,7 @@ __global__ __launch_bounds__(128) void k_decode_gqa4(MfmaParams p) {
 #pragma unroll
                 for (int nib = 0; nib < 2; ++nib) {
                     const int c = 32 * P + 8 * (n >> 2) + 2 * (n & 3) + nib;
-                    const float f = __builtin_ldexpf(1.0f, 24 - 4 * nib);
+                    const float f = code_unscale4();
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
                         const int h = 2 * kg + j;

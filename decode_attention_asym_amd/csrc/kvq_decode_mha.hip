@@ -9,8 +9,9 @@
 //
 // With a single query head both contractions are matrix-vector products, yet
 // the matrix cores still take them more cheaply than the VALU: the 2-bit
-// codes enter v_mfma_f32_16x16x32_f16 exactly as fp16 subnormals (one
-// v_perm_b32 plus one AND per register of two codes, as in the GQA kernel),
+// codes enter v_mfma_f32_16x16x32_f16 exactly as fp16 subnormals (a shift
+// per register of two code bytes and one AND per register of two codes, as
+// in the GQA kernel),
 // and the hi/lo halves of the folded scales ride along as extra rows of the
 // A operand at no cost.  The VALU is left with the unpacking, the online
 // softmax and the scale folding.
@@ -101,12 +102,12 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, float&
             if (G == 64) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x00030003u << (2 * u)), S[u], 0, 0, 0);
+                    S[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice2(c, u), S[u], 0, 0, 0);
             } else {
 #pragma unroll
                 for (int v = 0; v < 2; ++v) {
-                    const uint32_t mk = 0x00030003u << (2 * (2 * v + (n >> 3)));
-                    S[2 * be + v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, mk), S[2 * be + v], 0, 0, 0);
+                    const uint32_t mk = code_mask2(n >> 3);   // position 2v + (n >> 3)
+                    S[2 * be + v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice_set(c, v != 0, mk), S[2 * be + v], 0, 0, 0);
                 }
             }
         }
@@ -121,7 +122,7 @@ __device__ __forceinline__ void key_tile(const MfmaParams& p, KTile& cur, float&
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int up = G == 64 ? i : 2 * (i & 1) + (n >> 3);   // code position in the byte
-        const float f = p.sigma2 * __builtin_ldexpf(1.0f, 24 - 2 * up);
+        const float f = p.sigma2 * code_unscale2(up);
         x[i] = fmaf(S[i][0] + S[i][1], f, bias[G == 64 ? 0 : (i >> 1)]);
     }
     const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -228,7 +229,7 @@ __device__ __forceinline__ void value_tile(const MfmaParams& p, VTile& cur, VSta
             const CodeRegs c = code_operands(ld_tr8(L.vl + value_row_dw(ksx, P, kg, n)));
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                st.O[P][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x00030003u << (2 * u)),
+                st.O[P][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice2(c, u),
                                                                     st.O[P][u], 0, 0, 0);
         }
     }
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
                     const int c = 64 * P + 32 * (n >> 3) + 4 * (n & 7) + u;
                     const float hi = up ? st.O[P][u][2] : st.O[P][u][0];
                     const float lo = up ? st.O[P][u][3] : st.O[P][u][1];
-                    p.ws_acc[slot * D + c] = fmaf(hi + lo, __builtin_ldexpf(1.0f, 24 - 2 * u), P ? zb1 : zb0);
+                    p.ws_acc[slot * D + c] = fmaf(hi + lo, code_unscale2(u), P ? zb1 : zb0);
                 }
         }
         if (lane == 0) {
@@ -422,14 +423,14 @@ __device__ __forceinline__ void key_tile4(const MfmaParams& p, KTile4& cur, floa
             const CodeRegs c = code_operands(ld_tr8(L.kl + key_row_dw4<G>(ksx, r, kg, n)));
 #pragma unroll
             for (int nib = 0; nib < 2; ++nib)
-                S[2 * r + nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x000F000Fu << (4 * nib)),
+                S[2 * r + nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice4(c, nib),
                                                                        S[2 * r + nib], 0, 0, 0);
         }
     }
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float f = p.sigma2 * __builtin_ldexpf(1.0f, 24 - 4 * (i & 1));
+        const float f = p.sigma2 * code_unscale4();
         x[i] = fmaf(S[i][0] + S[i][1], f, bias[G == 64 ? 0 : (i >> 1)]);
     }
     const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -515,7 +516,7 @@ __device__ __forceinline__ void value_tile4(const MfmaParams& p, VTile4& cur, VS
             const CodeRegs c = code_operands(ld_tr8(L.vl + value_row_dw4(ksx, P, kg, n)));
 #pragma unroll
             for (int nib = 0; nib < 2; ++nib)
-                st.O[P][nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice(c, 0x000F000Fu << (4 * nib)),
+                st.O[P][nib] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, code_slice4(c, nib),
                                                                       st.O[P][nib], 0, 0, 0);
         }
     }
@@ -627,7 +628,7 @@ __global__ __launch_bounds__(128) void k_decode_mha4(MfmaParams p) {
                     const int c = 32 * P + 8 * (n >> 2) + 2 * (n & 3) + nib;
                     const float zb = sel4(P, vz0, vz1, vz2, vz3);
                     p.ws_acc[slot * D + c] = fmaf(st.O[P][nib][0] + st.O[P][nib][1],
-                                                  __builtin_ldexpf(1.0f, 24 - 4 * nib), zb);
+                                                  code_unscale4(), zb);
                 }
         }
         if (lane == 0) {

@@ -25,7 +25,7 @@
 //    (v_mfma_f32_16x16x32_f16, Q in registers, the hi tile transposed to
 //    token-major through a wave-private LDS block); the RoPE term of one
 //    (16-head, 32-channel) block per wave uses exact 4-bit code operands
-//    (fp16 subnormals) against q' = q_r * s_k in hi/lo rows plus the bias
+//    (the codes as fp16 integers) against q' = q_r * s_k in hi/lo rows plus the bias
 //    sum_c q_r z_k, or the fp16 residual keys;
 //  * softmax: wave w sums the 8 partials of heads [8w, 8w + 8), runs the
 //    online softmax in log2 units (lazily moved maxima) and writes fp16

@@ -352,8 +352,8 @@ __device__ __forceinline__ void load_vtile(const MfmaParams& p, const TileRun& r
 
 // ---- 4-bit tiles: 4 KB of key codes and 4 KB of value codes per 64-token
 // tile (16 words per token, G/8 words per key block and channel); side
-// values as for 2 bits.  A code nibble ANDed into an fp16 lane at bits
-// [4 nib, 4 nib + 3] is the exact subnormal code * 16^nib * 2^-24, so each
+// values as for 2 bits.  A code nibble alone in bits 6..9 of an fp16 lane
+// is the exact subnormal code * 2^-18 (code_operands, code_slice4), so each
 // code byte feeds two MFMAs instead of four: twice the bytes and transposed
 // reads per tile, the same MFMA and AND counts.
 struct KTile4 {
@@ -715,20 +715,47 @@ __device__ __forceinline__ int value_row_dw(int ksx, int P, int kg, int n) {
     return vtile_dw(32 * ksx + 8 * kg + (n >> 1), 4 * P + 2 * (n & 1));
 }
 
-// The 8 code bytes e = 0..7 of a transposed read as MFMA operand registers
-// r.x, r.x >> 8, r.y, r.y >> 8: ANDed with a mask that keeps one 2-bit code
-// position in bytes 0 and 2, their fp16 halves hold bytes (0, 2), (1, 3),
-// (4, 6), (5, 7), i.e. the K index runs over e in the quad order 0, 2, 1, 3.
-// The A operands (q', p') are laid out in the same order.
+// The 8 code bytes e = 0..7 of a transposed read as MFMA operand registers.
+// An fp16 lane whose only set bits are one code field is the subnormal
+// code * 2^(f - 24), f the field's lowest bit: an exact operand.  But the
+// matrix cores align the 32 products of a dot product to the largest
+// product's nominal exponent, and a subnormal operand counts with the
+// exponent of 2^-14 whatever its leading zeros: a field low in the mantissa
+// loses that many bits of the sum's precision (measured on gfx950
+// v_mfma_f32_16x16x32_f16: codes at bits 0..1 gave sums off by ~2^12 ulps
+// of the largest product; single products are exact).  So each code is read
+// from a copy of the bytes shifted to put its field at bits 6..9 of its fp16
+// half (at most 2 leading zeros below the top mantissa bit):
+//   a: bytes at bit 6 of each half -- 2-bit positions u = 0, 1 (fields 6..7,
+//      8..9) and the low 4-bit nibble (field 6..9);
+//   b: bytes at bit 2 -- 2-bit positions u = 2, 3 and the high nibble.
+// Register j of a set holds bytes (0, 2), (1, 3), (4, 6), (5, 7) in its two
+// halves (a shift spills neighbouring bytes only outside the fields), so
+// the K index runs over e in the quad order 0, 2, 1, 3; the A operands (q',
+// p') are laid out in the same order.  Results carry a factor
+// 2^-(24 - f): code_unscale2 / code_unscale4 undo it.
 struct CodeRegs {
-    uint32_t x0, x1, x2, x3;
+    uint32_t a[4], b[4];
 };
 __device__ __forceinline__ CodeRegs code_operands(uint2 r) {
-    return CodeRegs{r.x, r.x >> 8, r.y, r.y >> 8};
+    return CodeRegs{{r.x << 6, r.x >> 2, r.y << 6, r.y >> 2}, {r.x << 2, r.x >> 6, r.y << 2, r.y >> 6}};
 }
-__device__ __forceinline__ f16x8 code_slice(const CodeRegs& c, uint32_t mk) {
-    return as_f16x8(c.x0 & mk, c.x1 & mk, c.x2 & mk, c.x3 & mk);
+// 2-bit code position u (0..3) of every byte; `lanes_mk` variant: the set
+// (u >> 1) is uniform and the field (u & 1) may differ per lane
+__device__ __forceinline__ uint32_t code_mask2(int u) { return 0x00030003u << (6 + 2 * (u & 1)); }
+__device__ __forceinline__ f16x8 code_slice_set(const CodeRegs& c, bool hi_set, uint32_t mk) {
+    const uint32_t* x = hi_set ? c.b : c.a;
+    return as_f16x8(x[0] & mk, x[1] & mk, x[2] & mk, x[3] & mk);
 }
+__device__ __forceinline__ f16x8 code_slice2(const CodeRegs& c, int u) {
+    return code_slice_set(c, u >= 2, code_mask2(u));
+}
+// 4-bit nibble nib (0: low, 1: high) of every byte, field 6..9
+__device__ __forceinline__ f16x8 code_slice4(const CodeRegs& c, int nib) {
+    return code_slice_set(c, nib != 0, 0x03C003C0u);
+}
+__device__ __forceinline__ float code_unscale2(int u) { return __builtin_ldexpf(1.0f, 18 - 2 * (u & 1)); }
+__device__ __forceinline__ float code_unscale4() { return __builtin_ldexpf(1.0f, 18); }
 
 // ---- trailing tokens [ntiles*64, T) on the VALU: partial key block and the
 // fp16 residual keys, one token per lane for the logits, two channels per

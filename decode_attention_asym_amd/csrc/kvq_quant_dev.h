@@ -10,12 +10,17 @@
 //
 // Exactness: codes must equal round_half_even(fl32(fl32(x - mn) / scale))
 // with an IEEE binary32 division.  A correctly rounded division costs ~10
-// VALU instructions, so each code is first taken from q = fl32(x - mn) *
-// rcp(scale) (v_rcp_f32, <= 1 ulp).  |q - fl32(true quotient)| <= 6.6e-7 for
-// quotients <= 2^bits - 1, so whenever q lies more than 2^-19 from a
-// half-integer both round to the same integer; a code closer than that to a
-// tie takes the IEEE division (a branch per code: on fp16 data about 1 code
-// in 10^4 does, so a wave almost never executes the division).
+// VALU instructions, so each code is first taken from q = fl32(d * r) with
+// d = fl32(x - mn) and r = rcp(scale) (v_rcp_f32: within 1 ulp of 1/scale).
+// With Q = d / scale <= L = 2^bits - 1, r = (1 + e1) / scale, |e1| <= 2^-23,
+// q = d r (1 + e2) and fl32(Q) = Q (1 + e3), |e2|, |e3| <= 2^-24, so
+// |q - fl32(Q)| <= Q (2^-23 + 2^-24 + 2^-24) (1 + 2^-22) ~ L * 2^-22:
+// 7.2e-7 at 2 bits, 3.6e-6 at 4 bits.  Whenever q lies farther than a band
+// above that bound from a half-integer -- 2^-19 (1.9e-6) at 2 bits, 2^-17
+// (7.6e-6) at 4 bits -- both round to the same integer; a code within its
+// band of a tie takes the IEEE division (a branch per code: on N(0, 1) fp16
+// groups of 32, 1.4e-4 (2 bits) / 2.5e-4 (4 bits) of the codes do, so a
+// wave rarely executes the division).
 // No clamp is needed: 0 <= fl32(x - mn) <= fl32(max - mn), so both quotients
 // round into [0, 2^bits - 1].  Floating-point contraction is off in every
 // function here (the including file's setting does not matter).
@@ -29,7 +34,11 @@ namespace kvq {
 namespace {
 namespace qdev {
 
-constexpr float kTieBand = 0.5f - 0x1p-19f;
+// |q - k| above this sends a code to the IEEE division (see above)
+template <int BITS>
+constexpr float tie_band() { return BITS == 2 ? 0.5f - 0x1p-19f : 0.5f - 0x1p-17f; }
+static_assert(3.0 * 0x1p-22 * (1 + 0x1p-20) < 0x1p-19 && 15.0 * 0x1p-22 * (1 + 0x1p-20) < 0x1p-17,
+              "tie bands must exceed the reciprocal path's error bound L * 2^-22");
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f16x2 as_h2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
@@ -73,12 +82,14 @@ __device__ __forceinline__ GroupQ make_group(float mn, float mx, float L) {
 
 // code of d = fl32(x - mn): round-half-even of d * rcp, or of the IEEE
 // quotient d / scale when the product lies within the tie band (scale == 0
-// gives rcp == 0, product 0, never in the band)
+// gives rcp == 0, product 0, never in the band).  qa - k is exact (both lie
+// in one binade's grid, |qa - k| <= 1/2).
+template <int BITS>
 __device__ __forceinline__ uint32_t code_of(float d, const GroupQ& q) {
 #pragma clang fp contract(off)
     const float qa = d * q.rcp;
     float k = __builtin_rintf(qa);
-    if (__builtin_fabsf(qa - k) > kTieBand) k = __builtin_rintf(d / q.scale);
+    if (__builtin_fabsf(qa - k) > tie_band<BITS>()) k = __builtin_rintf(d / q.scale);
     return static_cast<uint32_t>(k);
 }
 
@@ -203,8 +214,8 @@ __device__ __forceinline__ void quant_values_thread(const ValueArgs& a, const Ro
         const float nmn = -q.mn;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            packed |= code_of(sub_half<0>(w[i], nmn), q) << (BITS * (2 * i));
-            packed |= code_of(sub_half<1>(w[i], nmn), q) << (BITS * (2 * i + 1));
+            packed |= code_of<BITS>(sub_half<0>(w[i], nmn), q) << (BITS * (2 * i));
+            packed |= code_of<BITS>(sub_half<1>(w[i], nmn), q) << (BITS * (2 * i + 1));
         }
         // the same for the 4 lanes of a group (same bh, same token)
         const int64_t row = tok < cnt ? rows.row(bh, tok) : -1;
@@ -354,7 +365,7 @@ __device__ __forceinline__ void quant_key_pair(const KeyJob& j, int kd, int cp, 
 #pragma unroll
         for (int i = 0; i < S::TG; ++i) {
             const float d = e == 0 ? sub_half<0>(raw[i], nmn) : sub_half<1>(raw[i], nmn);
-            words[i / S::PER] |= code_of(d, q[e]) << (BITS * (i % S::PER));
+            words[i / S::PER] |= code_of<BITS>(d, q[e]) << (BITS * (i % S::PER));
         }
         WordVec<S::WT>::st(codes + (side + e) * S::W + sp * S::WT, words);
     }

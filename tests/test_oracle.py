@@ -199,10 +199,16 @@ def test_pack_roundtrip(orc, bits):
     assert (orc.unpack(words, codes.size, bits) == codes).all()
 
 
-def test_layout_dequant_tracks_input(orc):
+@pytest.mark.parametrize("G,kbits,vbits", [(32, 2, 2), (64, 2, 2), (64, 4, 4), (32, 4, 4), (64, 4, 2), (16, 2, 4)])
+def test_layout_dequant_tracks_input(orc, G, kbits, vbits):
     """Dequantized keys/values, read through the documented layout by numpy,
-    sit within the I2 bound of the input at the same (token, channel)."""
-    w = configs.WORKLOADS[0]
+    sit within the I2 bound of the input at the same (token, channel), for
+    both key groups of the workloads (32, 64) and both code widths (the MLA
+    RoPE key is a 4-bit, G = 64 key stream).  A transposed, mis-indexed or
+    mis-packed store fails this at any of these settings."""
+    import dataclasses
+    w = dataclasses.replace(configs.WORKLOADS[0], kG=G, kbits=kbits, vbits=vbits)
+    Lk, Lv = (1 << kbits) - 1, (1 << vbits) - 1
     for b, hh in [(0, 0), (0, 1)]:
         k = synth.key_slice(w, b, hh)[None, None]
         v = synth.value_slice(w, b, hh)[None, None]
@@ -212,15 +218,20 @@ def test_layout_dequant_tracks_input(orc):
         assert np.array_equal(vh, orc.dequant_values(cache, 0, 0))
         kx, vx = f16(k[0, 0]), f16(v[0, 0])
         nb = w.T // w.kG
+        assert nb >= 3
         for blk in range(nb):
             sl = slice(blk * w.kG, (blk + 1) * w.kG)
             rngk = kx[sl].max(0) - kx[sl].min(0)
-            assert (np.abs(kh[sl] - kx[sl]) <= rngk / 3 * (0.5 + 3 * 2.0 ** -11) * (1 + 1e-6) + 1e-9).all()
+            bound = rngk / Lk * (0.5 + Lk * 2.0 ** -11) * (1 + 1e-6) + 1e-9
+            assert (np.abs(kh[sl] - kx[sl]) <= bound).all()
+            # a tighter bound than a neighbouring token's value would meet
+            assert np.abs(kh[sl] - kx[sl]).max() < np.abs(np.diff(kx[sl], axis=0)).max()
         assert np.array_equal(kh[nb * w.kG:], kx[nb * w.kG:])  # residual kept exactly
         for g in range(w.vd // w.vG):
             sl = slice(g * w.vG, (g + 1) * w.vG)
             rngv = vx[:, sl].max(1, keepdims=True) - vx[:, sl].min(1, keepdims=True)
-            assert (np.abs(vh[:, sl] - vx[:, sl]) <= rngv / 3 * (0.5 + 3 * 2.0 ** -11) * (1 + 1e-6) + 1e-9).all()
+            bound = rngv / Lv * (0.5 + Lv * 2.0 ** -11) * (1 + 1e-6) + 1e-9
+            assert (np.abs(vh[:, sl] - vx[:, sl]) <= bound).all()
 
 
 def test_outlier_confinement(orc):
