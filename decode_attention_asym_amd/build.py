@@ -33,6 +33,7 @@ SOURCES = {
     "kvq_decode_mha.hip": VGPR_FORM,
     "kvq_decode_mla.hip": VGPR_FORM,
     "kvq_prefill.hip": VGPR_FORM,
+    "kvq_noalloc.hip": [],
 }
 FLAGS = COMMON + VGPR_FORM   # kept for tools that print the main flag set
 

@@ -108,6 +108,20 @@ PagedSeq paged_seq(const kvq_paged& c, const int32_t* table, const int32_t* lens
 
 }  // namespace
 
+namespace kvq {
+
+kvq_status decode_workspace_now(const kvq_cache& c, int Hq, int n_splits, uint64_t* bytes) {
+    if (Hq < 1 || Hq % c.cfg.n_kv_heads != 0) return KVQ_E_SHAPE;
+    if (n_splits < 0 || n_splits > KVQ_MAX_SPLITS) return KVQ_E_SHAPE;
+    const Variant v = pick_variant(c, Hq);
+    if (!splits_fit(c, v, n_splits, c.nblk)) return KVQ_E_SHAPE;
+    const SplitPlan sp = plan_splits(c, Hq, n_splits, c.T, c.nblk, v);
+    *bytes = uint64_t(c.cfg.batch) * Hq * sp.S * (c.cfg.value.dim + 2) * 4;
+    return KVQ_OK;
+}
+
+}  // namespace kvq
+
 extern "C" {
 
 const char* kvq_status_str(kvq_status s) {
@@ -121,6 +135,7 @@ const char* kvq_status_str(kvq_status s) {
         case KVQ_E_WORKSPACE: return "workspace too small";
         case KVQ_E_HIP: return "HIP launch failed";
         case KVQ_E_STATE: return "cache holds no tokens";
+        case KVQ_E_SCRATCH: return "partials exceed the static scratch array";
     }
     return "unknown status";
 }

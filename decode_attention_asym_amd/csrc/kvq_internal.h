@@ -131,6 +131,10 @@ int max_slots(const kvq_cache& c, int Hq, int n_splits, Variant v);
 int64_t max_run_tiles(const kvq_cache_cfg& cfg);
 bool runs_fit(const kvq_cache_cfg& cfg, int64_t ntiles, int64_t S_main);
 
+// Partial-slot bytes kv_decode_attention needs at the cache's current
+// length (checks n_q_heads and n_splits as it does).
+kvq_status decode_workspace_now(const kvq_cache& c, int Hq, int n_splits, uint64_t* bytes);
+
 bool gqa_supported(const kvq_cache& c, int Hq);
 bool gqa_cfg_supported(const kvq_cache_cfg& c, int Hq);
 bool mha_supported(const kvq_cache& c, int Hq);

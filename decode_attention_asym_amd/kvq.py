@@ -21,16 +21,17 @@ KVQ_APPEND_NO_AUTOFLUSH = 1
 KVQ_STEP_ADVANCE_LENGTHS = 1
 KVQ_PREFILL_ATTENTION_ONLY = 1
 KVQ_MAX_SPLITS = 256
+KVQ_SCRATCH_BYTES = 32 << 20
 STATUS = {0: "KVQ_OK", -1: "KVQ_E_NULL", -2: "KVQ_E_SHAPE", -3: "KVQ_E_ALIGN",
           -4: "KVQ_E_CAPACITY", -5: "KVQ_E_UNSUPPORTED", -6: "KVQ_E_WORKSPACE",
-          -7: "KVQ_E_HIP", -8: "KVQ_E_STATE"}
+          -7: "KVQ_E_HIP", -8: "KVQ_E_STATE", -9: "KVQ_E_SCRATCH"}
 EXPORTS = ["kv_cache_buffer_bytes", "kv_cache_init", "kv_cache_destroy", "kv_cache_reset",
            "kv_cache_state", "kv_quantize_append", "kv_flush_residual",
            "kv_decode_workspace_bytes", "kv_decode_attention", "kv_set_timing_events",
            "kv_decode_variant", "kvq_status_str",
            "kv_paged_buffer_bytes", "kv_paged_init", "kv_paged_destroy", "kv_paged_append",
            "kv_paged_workspace_bytes", "kv_paged_decode", "kv_paged_variant", "kv_decode_step",
-           "kv_paged_decode_step", "kv_prefill_attention"]
+           "kv_paged_decode_step", "kv_prefill_attention", "kv_decode_attention_noalloc"]
 
 
 class KvqError(RuntimeError):
@@ -92,6 +93,7 @@ def lib():
             "kv_paged_decode": (C.c_int, [p, p, i32, C.c_float, p, p, i32, i32, p, p, u64, p]),
             "kv_paged_variant": (C.c_char_p, [p, i32, i32]),
             "kv_decode_step": (C.c_int, [p, p, p, p, i32, C.c_float, i32, p, p, u64, p]),
+            "kv_decode_attention_noalloc": (C.c_int, [p, p, i32, C.c_float, i32, p, p]),
             "kv_paged_decode_step": (C.c_int, [p, p, p, p, i32, C.c_float, p, p, p, i32, i32, u32, p, p, u64, p]),
             "kv_prefill_attention": (C.c_int, [p, p, p, p, i64, i32, C.c_float, u32, p, p]),
         }
@@ -168,6 +170,12 @@ def kv_decode_attention(handle, q_ptr, n_q_heads: int, softmax_scale: float, n_s
                         out_ptr, ws_ptr, ws_bytes: int, stream=None) -> None:
     _check(lib().kv_decode_attention(handle, q_ptr, n_q_heads, C.c_float(softmax_scale), n_splits,
                                      out_ptr, ws_ptr, ws_bytes, stream), "kv_decode_attention")
+
+
+def kv_decode_attention_noalloc(handle, q_ptr, n_q_heads: int, softmax_scale: float, n_splits: int, out_ptr,
+                                stream=None) -> None:
+    _check(lib().kv_decode_attention_noalloc(handle, q_ptr, n_q_heads, C.c_float(softmax_scale), n_splits, out_ptr,
+                                             stream), "kv_decode_attention_noalloc")
 
 
 def kv_decode_step(handle, k_ptr, v_ptr, q_ptr, n_q_heads: int, softmax_scale: float, n_splits: int,
@@ -306,6 +314,16 @@ class DeviceCache:
             ws = self.workspace(Hq, n_splits)
         kv_decode_attention(self.handle, q.data_ptr(), Hq, softmax_scale, n_splits,
                             out.data_ptr(), ws.data_ptr(), ws.numel(), self.stream())
+        return out
+
+    def decode_noalloc(self, q, softmax_scale: float, n_splits: int = 0, out=None):
+        """kv_decode_attention_noalloc: partials in the library's static scratch."""
+        torch = self.torch
+        B, Hq = q.shape[0], q.shape[1]
+        if out is None:
+            out = torch.empty((B, Hq, self.cfg.value.dim), dtype=torch.float16, device=self.device)
+        kv_decode_attention_noalloc(self.handle, q.data_ptr(), Hq, softmax_scale, n_splits, out.data_ptr(),
+                                    self.stream())
         return out
 
     def variant(self, n_q_heads: int) -> str:

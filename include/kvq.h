@@ -77,7 +77,8 @@ typedef enum kvq_status {
     KVQ_E_UNSUPPORTED = -5, /* valid request the library does not implement  */
     KVQ_E_WORKSPACE = -6,   /* workspace smaller than required               */
     KVQ_E_HIP = -7,         /* a HIP launch failed                           */
-    KVQ_E_STATE = -8        /* no tokens to attend over; prefill: not empty  */
+    KVQ_E_STATE = -8,       /* no tokens to attend over; prefill: not empty  */
+    KVQ_E_SCRATCH = -9      /* the partials exceed the static scratch array  */
 } kvq_status;
 
 enum { KVQ_KIND_KIVI = 0, KVQ_KIND_MLA = 1 };
@@ -339,6 +340,27 @@ kvq_status kv_decode_step(kvq_cache* cache, const void* k_fp16, const void* v_fp
 kvq_status kv_prefill_attention(kvq_cache* cache, const void* q_fp16, const void* k_fp16, const void* v_fp16,
                                 int64_t n, int32_t n_q_heads, float softmax_scale, uint32_t flags, void* out_fp16,
                                 void* hip_stream);
+
+/* Bytes of the static device array (one per GPU, held until the process
+ * ends) in which kv_decode_attention_noalloc keeps its split partials. */
+#define KVQ_SCRATCH_BYTES (32u << 20)
+
+/* kv_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels, split plan and results bit for bit, with
+ * the split partials in the library's static array of KVQ_SCRATCH_BYTES on
+ * the current device instead of a caller workspace.  No device memory is
+ * allocated or freed.  The array's address is looked up once per device, on
+ * the first call made with that device current.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (two streams, two
+ * threads) race and must be ordered by the caller.  Nothing needs clearing
+ * between calls (each call writes every partial its merge reads).
+ * Arguments as kv_decode_attention.  Errors: those of kv_decode_attention
+ * except KVQ_E_WORKSPACE, and KVQ_E_SCRATCH when the partials,
+ * B * n_q_heads * slots * (vd + 2) * 4 bytes, exceed KVQ_SCRATCH_BYTES
+ * (fewer splits, a smaller batch or the workspace entry point then serve). */
+kvq_status kv_decode_attention_noalloc(const kvq_cache* cache, const void* q_fp16, int32_t n_q_heads,
+                                       float softmax_scale, int32_t n_splits, void* out_fp16, void* hip_stream);
 
 /* Profiling hook: when both are non-NULL (hipEvent_t, created by the caller),
  * later kv_decode_attention / kv_decode_step / kv_paged_decode calls launch their split-K pass-1 kernel with

@@ -169,6 +169,30 @@ def test_split_runs_stay_within_32_bit_offsets(kbits, limit_tokens):
         kvq.kv_cache_destroy(h)
 
 
+def test_noalloc_validation_before_hip():
+    """kv_decode_attention_noalloc checks its arguments on the host, as
+    kv_decode_attention does, before it looks up its scratch array."""
+    h = make_handle()
+    try:
+        for args, st in [((0, 8), -1), ((0x1000, 6), -2), ((0x1000, 0), -2)]:
+            with pytest.raises(kvq.KvqError) as e:
+                kvq.kv_decode_attention_noalloc(h, args[0], args[1], 1.0, 0, 0x2000)
+            assert e.value.status == st
+        for s_, st in [(-1, -2), (257, -2)]:
+            with pytest.raises(kvq.KvqError) as e:
+                kvq.kv_decode_attention_noalloc(h, 0x1000, 8, 1.0, s_, 0x2000)
+            assert e.value.status == st
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kv_decode_attention_noalloc(h, 0x1008, 8, 1.0, 0, 0x2000)
+        assert e.value.status == -3
+        with pytest.raises(kvq.KvqError) as e:                # empty cache
+            kvq.kv_decode_attention_noalloc(h, 0x1000, 8, 1.0, 0, 0x2000)
+        assert e.value.status == -8
+        assert kvq.kvq_status_str(-9) == "partials exceed the static scratch array"
+    finally:
+        kvq.kv_cache_destroy(h)
+
+
 def test_status_strings():
     for s in kvq.STATUS:
         assert kvq.kvq_status_str(s) not in ("", "unknown status")
