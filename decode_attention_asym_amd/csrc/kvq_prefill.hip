@@ -24,8 +24,11 @@
 // weights of S^T's accumulator feed O^T's B operand without leaving the lane,
 // and the softmax rescale and the final 1/l stay lane-local.  Softmax in
 // log2 units with the running maximum moved only when a logit exceeds it by
-// more than 2^8 (weights stay <= 256 in fp16); weights are rounded to fp16
-// for the second product, l sums them in fp32.
+// more than 2^8 (weights stay <= 256 in fp16).  The weights enter the second
+// product as fp16 pairs hi = fp16(p), lo = fp16(p - hi) (two products into
+// one accumulator), so they keep ~22 bits where FlashAttention's single fp16
+// weight keeps 11: with unrounded sums l the output is then within the fp16
+// rounding of the result, not within 2^-11 max|v| of it.
 //
 // Fused quantize: the workgroups of query block i quantize its tiles 2i and
 // 2i + 1 (values of their rows, the key blocks they complete, the unfilled
@@ -61,6 +64,7 @@ __device__ __forceinline__ pf16x8 as_pf16x8(uint32_t a, uint32_t b, uint32_t c, 
     typedef uint32_t u4v __attribute__((ext_vector_type(4)));
     return __builtin_bit_cast(pf16x8, u4v{a, b, c, d});
 }
+typedef _Float16 f16x2p __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, h2{_Float16(a), _Float16(b)});
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(64 * PNW) void k_prefill(PrefillArgs a) {
         // a wave's rows see none of the tile (skip), part of it (mask), or all
         const bool none = DIAG && 64 * j > row0 + 15;
         const bool part = DIAG && 64 * j + 63 > row0;
-        uint32_t pw[8];
+        uint32_t pw[8], pl[8];
         if (!none) {
             // ---- S^T = K Q^T: lane (n, kg) gets tokens 16cb + 4kg + i of row n
             pf32x4 S[4];
@@ -301,6 +305,9 @@ __global__ __launch_bounds__(64 * PNW) void k_prefill(PrefillArgs a) {
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(s[e + 1], a.sigma2, -m));
                 l += p0 + p1;
                 pw[e / 2] = pack_h2(p0, p1);
+                // p - hi is exact in fp32 (hi is p rounded to 11 bits)
+                const f16x2p h = __builtin_bit_cast(f16x2p, pw[e / 2]);
+                pl[e / 2] = pack_h2(p0 - float(h[0]), p1 - float(h[1]));
             }
         }
         if (j + 1 < ntile) load_rows(vrs, 64 * (j + 1), tid, cur.v);
@@ -310,6 +317,7 @@ __global__ __launch_bounds__(64 * PNW) void k_prefill(PrefillArgs a) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const pf16x8 P = as_pf16x8(pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]);
+                const pf16x8 Pl = as_pf16x8(pl[4 * ks], pl[4 * ks + 1], pl[4 * ks + 2], pl[4 * ks + 3]);
                 // lane n names value row 32ks + 4kg + (n >> 2) (and + 16), channels
                 // 16c + 4 (n & 3) .. + 3; it receives channel 16c + n of the four
                 // rows 32ks + 4kg + e (then + 16), e = 0..3
@@ -318,7 +326,9 @@ __global__ __launch_bounds__(64 * PNW) void k_prefill(PrefillArgs a) {
                 for (int c = 0; c < 8; ++c) {
                     const uint2 lo = ld_tr16(vr + 8 * c);
                     const uint2 hi = ld_tr16(vr + 16 * PVR + 8 * c);
-                    O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_pf16x8(lo.x, lo.y, hi.x, hi.y), P, O[c], 0, 0, 0);
+                    const pf16x8 Vt = as_pf16x8(lo.x, lo.y, hi.x, hi.y);
+                    O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vt, P, O[c], 0, 0, 0);
+                    O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Vt, Pl, O[c], 0, 0, 0);
                     if (c & 1) __builtin_amdgcn_sched_barrier(0);
                 }
             }

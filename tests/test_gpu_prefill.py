@@ -2,22 +2,22 @@
 cores, fused with the bulk quantize of the prompt) through the C ABI.
 
 Outputs are compared with the oracle's fp64 causal attention over the same
-fp16 bits.  Tolerance, from the arithmetic: the weights enter the PV product
-rounded to fp16 (relative error <= 2^-11 each) while l sums them unrounded,
-so |o - o_exact| <= 2^-11 sum_j p_j |v_j| / l <= 2^-11 max |v|; the fp16
-output adds half an ulp, <= 2^-11 |o| <= 2^-11 max |v|.  Hence max-abs
-<= 2^-10 max |v| (logits are fp32 sums of exact fp16 products, their error
-is orders below).  The cache must equal, bit for bit, both a twin cache
-filled by kv_quantize_append from the same tensors and the oracle's
-quantizer.
+fp16 bits, at the decode path's bar: max-abs 2e-3 (fp16 output against the
+unrounded fp64 result) plus the mean-excess bound.  From the arithmetic: the
+weights enter the PV product as fp16 hi + lo pairs (relative error ~2^-22)
+against an unrounded l, the logits are fp32 sums of exact fp16 products, and
+the fp16 output adds at most half an ulp (9.8e-4 for |o| < 4, 1.95e-3 below
+8), so the kernel's own error is orders below the bar.  The cache must
+equal, bit for bit, both a twin cache filled by kv_quantize_append from the
+same tensors and the oracle's quantizer.
 """
 import dataclasses
 
 import numpy as np
 import pytest
 
-from gpu_util import (assert_slices_equal, configs, dev_f16, host_u16, kvq, log, mean_excess, new_cache,
-                      oracle_slice, slice_of, synth, torch)
+from gpu_util import (MEAN_EXCESS_TOL, TOL, assert_slices_equal, configs, dev_f16, host_u16, kvq, log, mean_excess,
+                      new_cache, oracle_slice, slice_of, synth, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,9 +29,7 @@ SHAPES = {  # B, Hq, Hkv, G, key bits, value bits
     "gqa4_4bit": (2, 8, 2, 64, 4, 4),
     "gqa4_k2v4_g32": (1, 4, 1, 32, 2, 4),
 }
-# mean error beyond the fp16 rounding of the exact result: the fp16 weights
-# are unbiased, so over many outputs it stays far below the max-abs bound
-MEAN_TOL = 1e-4
+MEAN_TOL = MEAN_EXCESS_TOL
 
 
 def _workload(shape, T):
@@ -45,7 +43,7 @@ def _inputs(w):
 
 
 def _tol(v):
-    return 2.0 ** -10 * float(np.abs(v.view(np.float16).astype(np.float64)).max())
+    return TOL
 
 
 def _cap(w):
@@ -152,10 +150,10 @@ def test_decode_after_prefill_equals_decode_after_append(orc):
     twin.close()
 
 
-def test_prefill_full_size_sampled_rows(orc):
+def test_prefill_full_size_every_row(orc):
     """The Mistral-7B-shaped prompt (32 query / 8 KV heads, D 128, G 64) at
-    4096 tokens, one sequence: sampled rows (tile edges, first and last rows
-    of every head, random ones) against the oracle, the whole cache against
+    4096 tokens, one sequence: every output row against the oracle (about
+    137 GFLOP of fp64 work, ~10 s on 16 host cores), the whole cache against
     kv_quantize_append."""
     t = torch()
     w = dataclasses.replace(configs.BY_NAME["mistral_7b_gqa_prefill_b4_t4096"], batch=1)
@@ -165,11 +163,8 @@ def test_prefill_full_size_sampled_rows(orc):
     twin.append(dev_f16(k), dev_f16(v))
     t.cuda.synchronize()
     got = host_u16(out).view(np.float16).astype(np.float64)
-    rng = np.random.default_rng(11)
-    rows = [(0, h, i) for h in (0, 3, 4, 31) for i in (0, 1, 63, 64, 65, 2047, 4032, 4095)]
-    rows += [(0, int(h), int(i)) for h, i in zip(rng.integers(0, 32, 40), rng.integers(0, 4096, 40))]
-    worst, excess = _check_out(orc, w, q, k, v, got, rows=np.array(rows))
-    log(f"[prefill full] {len(rows)} rows: max|err| {worst:.3e} mean excess {excess:.2e}")
+    worst, excess = _check_out(orc, w, q, k, v, got)
+    log(f"[prefill full] {w.n_q_heads * w.T} rows: max|err| {worst:.3e} mean excess {excess:.2e}")
     for name, a in dc.arrays.items():
         assert t.equal(a, twin.arrays[name]) or name == "k_resid", name
     assert dc.state() == twin.state()
