@@ -80,7 +80,7 @@ def parse():
     ap.add_argument("--batch", type=int, default=0,
                     help="sequences per step (default: the workload's); names the workload ..._b<N>")
     ap.add_argument("--bits", type=int, default=0, choices=[0, 2, 4],
-                    help="key and value code width (default: the workload's); names the workload ..._<N>bit")
+                    help="key and value code width (default: the workload's; MLA: the content latent's, the RoPE key stays 4-bit)")
     ap.add_argument("--prefill", action="store_true",
                     help="prefill: causal prompt attention fused with the bulk quantize (kv_prefill_attention) "
                          "on the prefill workload")
@@ -223,6 +223,10 @@ def main():
     if args.bits and w.kind == "kivi" and args.bits != w.kbits:
         import dataclasses
         w = dataclasses.replace(w, kbits=args.bits, vbits=args.bits, name=f"{w.name}_{args.bits}bit")
+    if args.bits and w.kind == "mla" and args.bits != w.vbits:
+        # the content latent's width (the RoPE key is 4-bit either way)
+        import dataclasses
+        w = dataclasses.replace(w, vbits=args.bits, name=f"{w.name}_content{args.bits}bit")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.prefill:
@@ -364,7 +368,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.kd, "context": w.T, "G": w.kG,
-                   "bits": w.kbits, "value_group": w.vG, "layers": L, "parallelism": "none (1 GPU)"},
+                   "bits": w.kbits if w.kind == "kivi" else w.vbits, "value_group": w.vG, "layers": L,
+                   "parallelism": "none (1 GPU)", **({"rope_bits": w.kbits} if w.kind == "mla" else {})},
         "roofline": roofline,
         "extra": {
             "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),

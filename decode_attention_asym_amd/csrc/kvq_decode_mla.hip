@@ -1,8 +1,9 @@
 // kvq_decode_mla.hip -- split-K decode attention on MFMA for absorbed MLA
 // caches: one latent KV head shared by 64 or 128 query heads; a 512-dim
-// content latent in 2-bit per-token codes (32-channel groups) that serves as
-// both key and value, and a 64-dim decoupled RoPE key in 4-bit per-channel
-// codes over 64-token blocks (fp16 for the block that is not yet full).
+// content latent in 2- or 4-bit per-token codes (32-channel groups) that
+// serves as both key and value, and a 64-dim decoupled RoPE key in 4-bit
+// per-channel codes over 64-token blocks (fp16 for the block that is not yet
+// full).  QuantMLA's INT2 and INT4 content paths are both served.
 //
 // Method ("QuantMLA: Düşük Bitli MLA KV Önbellekleme için Fonksiyon Uyumlu
 // Çift Yollu Kuantizasyon", sections "Giriş ve Problem Analizi" and "QuantMLA
@@ -18,7 +19,8 @@
 // Wave w owns latent channels [64w, 64w + 64) and does all the work on
 // them, so every content element is dequantized once per workgroup:
 //  * dequant: codes become exact fp16 integers by an exponent trick
-//    ((bits & mask) | exponent of 2^(10-2u) is 2^(10-2u) + code);
+//    ((bits & mask) | exponent of 2^(10-b u) is 2^(10-b u) + code for the
+//    b-bit code at position u of its byte);
 //    c_hat = code * s + z is one fused fp16 FMA (the correctly rounded hi)
 //    plus the fp32 remainder c_hat - hi (lo);
 //  * QK^T: partial logits of all 64 heads over the wave's own channels
@@ -67,7 +69,7 @@ constexpr float TAU = 8.0f;  // lazy-rescale threshold (log2 units)
 struct MlaParams {
     const uint32_t* kc;          // RoPE codes [B][nblk_cap][64][8]
     const uint16_t *ks, *kz, *kr;
-    const uint32_t* vc;          // content codes [B][cap][32]
+    const uint32_t* vc;          // content codes [B][cap][16 * bits]
     const uint16_t *vs, *vz;     // content side [B][cap][16]
     const uint16_t* q;           // [B][Hq][576]
     float *ws_acc, *ws_ml;
@@ -81,7 +83,7 @@ struct Lds {
     __attribute__((aligned(16))) float sx[2][NW][16 * SXS];  // partial logits [buf][wave][token][head]
     __attribute__((aligned(16))) float srx[2][NW][16 * 20];  // RoPE partials [buf][wave][token][16 heads]
     __attribute__((aligned(16))) uint32_t chw[NW][16 * CWS]; // per wave: hi, token-major [token][64 fp16]
-    __attribute__((aligned(16))) uint32_t cst[NW][4 * 16];   // per wave: content codes [word][token]
+    __attribute__((aligned(16))) uint32_t cst[NW][8 * 16];   // per wave: content codes [word][token] (4 or 8 words)
     __attribute__((aligned(16))) uint32_t sst[NW][2 * 2 * 8];  // per wave: [scale|zero][group][16 fp16]
     __attribute__((aligned(16))) uint32_t pm[2][HQ * PS];    // weights fp16 [buf][head][16 tokens]
     __attribute__((aligned(16))) uint32_t rc[8 * RCS];       // RoPE codes of the block [word][channel]
@@ -155,7 +157,11 @@ struct Frags {
     uint32_t h[2][4], l[2][4];   // [channel 2*c32 + v][token pair]
 };
 
+// Content code width VB (2 or 4): a wave's 64 channels are CW words per token.
+template <int VB>
 __global__ __launch_bounds__(512) void k_decode_mla(MlaParams p) {
+    constexpr int CW = 64 * VB / 32;    // own code words per token
+    constexpr int VWT = VD * VB / 32;   // code words per token
     __shared__ Lds L;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, kg = lane >> 4;        // 16x16x32 operand layout
@@ -190,28 +196,32 @@ __global__ __launch_bounds__(512) void k_decode_mla(MlaParams p) {
 
     // per-lane dequant constants: channels ch0 + 2*c32 + v sit at code
     // position u = 2(c32 & 1) + v of byte (c32 & 7) >> 1 of word c32 >> 3
+    // (2 bits), or in nibble v of byte c32 & 3 of word c32 >> 2 (4 bits)
     uint32_t dmk[2], de2[2], dnb[2];
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
-        const int u = 2 * (c32 & 1) + v;
-        const uint32_t ex = uint32_t(25 - 2 * u) << 10;   // exponent field of 2^(10-2u)
-        dmk[v] = 0x00030003u << (2 * u);
+        const int u = VB == 2 ? 2 * (c32 & 1) + v : v;
+        const uint32_t ex = uint32_t(25 - VB * u) << 10;   // exponent field of 2^(10-VB*u)
+        dmk[v] = (VB == 2 ? 0x00030003u : 0x000F000Fu) << (VB * u);
         de2[v] = ex | (ex << 16);
         dnb[v] = de2[v] | 0x80008000u;
     }
-    const uint32_t csel = byte_pair_sel((c32 & 7) >> 1);
+    const uint32_t csel = byte_pair_sel(VB == 2 ? (c32 & 7) >> 1 : c32 & 3);
+    const int cword = VB == 2 ? c32 >> 3 : c32 >> 2;      // own word of the lane's channels
     const uint32_t rsel = byte_pair_sel((n & 7) >> 1);    // RoPE: byte of the lane's token
     // (its code is the low nibble for even n, the high one for odd n)
     const int mr = wave >> 1, kr = wave & 1;              // this wave's RoPE block
 
-    // content loads (two tiles ahead): code word (lane & 3) of the own 4 words
-    // of token t0 + (lane >> 2); side (lanes < 32): scale (lanes < 16) / zero
-    // pair of the own 2 groups of token t0 + (lane & 15)
-    const uint32_t* vcb = p.vc + int64_t(b) * p.cap * 32 + 4 * wave + (lane & 3);
+    // content loads (two tiles ahead): code words CW/4 * (lane & 3) .. of the
+    // own CW words of token t0 + (lane >> 2) (one word at 2 bits, two at 4);
+    // side (lanes < 32): scale (lanes < 16) / zero pair of the own 2 groups of
+    // token t0 + (lane & 15)
+    const uint32_t* vcb = p.vc + int64_t(b) * p.cap * VWT + CW * wave + (CW / 4) * (lane & 3);
     const uint16_t* vsb = ((lane & 16) ? p.vz : p.vs) + int64_t(b) * p.cap * 16 + 2 * wave;
-    auto load_content = [&](int tile, uint32_t& cw, uint32_t& sw) {
+    auto load_content = [&](int tile, uint2& cw, uint32_t& sw) {
         const int64_t t0 = int64_t(tile) * 16;
-        cw = vcb[(t0 + (lane >> 2)) * 32];
+        const uint32_t* src = vcb + (t0 + (lane >> 2)) * VWT;
+        cw = VB == 2 ? make_uint2(src[0], 0u) : *reinterpret_cast<const uint2*>(src);
         sw = lane < 32 ? *reinterpret_cast<const uint32_t*>(vsb + (t0 + (lane & 15)) * 16) : 0u;
     };
     // RoPE block loads: code word tid of the block; side (tid < 64)
@@ -222,7 +232,8 @@ __global__ __launch_bounds__(512) void k_decode_mla(MlaParams p) {
                        : 0u;
     };
     // tile i's content words in slot (i - t_lo) & 1
-    uint32_t cwq[2] = {0u, 0u}, swq[2] = {0u, 0u}, rw_n = 0u, rsw_n = 0u;
+    uint2 cwq[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
+    uint32_t swq[2] = {0u, 0u}, rw_n = 0u, rsw_n = 0u;
     load_content(t_lo, cwq[0], swq[0]);
     if (t_lo + 1 < t_hi) load_content(t_lo + 1, cwq[1], swq[1]);
     if (int64_t(t_lo) * 16 / GR < p.nblk) load_rope(int64_t(t_lo) * 16 / GR, rw_n, rsw_n);
@@ -232,7 +243,7 @@ __global__ __launch_bounds__(512) void k_decode_mla(MlaParams p) {
     int64_t cur_blk = -1;
 
     // ---- stage 1 of tile i: dequant, QK^T partials -> sx[i & 1]
-    auto front = [&](int i, Frags& fr, uint32_t& cwr, uint32_t& swr) {
+    auto front = [&](int i, Frags& fr, uint2& cwr, uint32_t& swr) {
         const int64_t t0 = int64_t(i) * 16;
         const int64_t blk = t0 / GR;
         const bool qrope = blk < p.nblk;
@@ -263,9 +274,11 @@ __global__ __launch_bounds__(512) void k_decode_mla(MlaParams p) {
         }
         // stage the own codes and side values, prefetch tile i + 2
         {
-            const uint32_t cw = cwr, sw = swr;
+            const uint2 cw = cwr;
+            const uint32_t sw = swr;
             if (i + 2 < t_hi) load_content(i + 2, cwr, swr);
-            L.cst[wave][(lane & 3) * 16 + (lane >> 2)] = cw;
+            L.cst[wave][(CW / 4) * (lane & 3) * 16 + (lane >> 2)] = cw.x;
+            if (VB == 4) L.cst[wave][(2 * (lane & 3) + 1) * 16 + (lane >> 2)] = cw.y;
             // lane (sz, tl) holds groups (0, 1) of token tl; even tl writes
             // group 0 of tokens (tl, tl + 1), odd tl group 1
             const uint32_t other = uint32_t(__builtin_amdgcn_update_dpp(0, int(sw), 0xb1, 0xf, 0xf, false));
@@ -278,7 +291,7 @@ __global__ __launch_bounds__(512) void k_decode_mla(MlaParams p) {
         wave_sync();
         // dequant channels ch0 + 2*c32 + v of tokens 8*h32 .. 8*h32 + 7
         {
-            const uint32_t* cs = L.cst[wave] + (c32 >> 3) * 16 + 8 * h32;
+            const uint32_t* cs = L.cst[wave] + cword * 16 + 8 * h32;
             const uint4 wa = *reinterpret_cast<const uint4*>(cs);
             const uint4 wb = *reinterpret_cast<const uint4*>(cs + 4);
             const uint32_t x[4] = {__builtin_amdgcn_perm(wa.y, wa.x, csel), __builtin_amdgcn_perm(wa.w, wa.z, csel),
@@ -498,8 +511,8 @@ __global__ __launch_bounds__(512) void k_decode_mla(MlaParams p) {
 bool mla_supported(const kvq_cache& c, int Hq) {
     const kvq_cache_cfg& g = c.cfg;
     return g.kind == KVQ_KIND_MLA && g.n_kv_heads == 1 && g.key.bits == 4 && g.key.dim == KD &&
-           g.key.group == GR && g.value.bits == 2 && g.value.dim == VD && g.value.group == 32 &&
-           (Hq == 64 || Hq == 128);
+           g.key.group == GR && (g.value.bits == 2 || g.value.bits == 4) && g.value.dim == VD &&
+           g.value.group == 32 && (Hq == 64 || Hq == 128);
 }
 
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st) {
@@ -525,7 +538,10 @@ hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st) {
     p.sigma2 = a.sigma * 1.4426950408889634f;
     p.neg1 = -1.0f;
     const dim3 grid(a.S, a.g.B, a.Hq / HQ);
-    hipExtLaunchKernelGGL(k_decode_mla, grid, dim3(64 * NW), 0, st, a.ev_start, a.ev_stop, 0, p);
+    if (c.cfg.value.bits == 4)
+        hipExtLaunchKernelGGL(k_decode_mla<4>, grid, dim3(64 * NW), 0, st, a.ev_start, a.ev_stop, 0, p);
+    else
+        hipExtLaunchKernelGGL(k_decode_mla<2>, grid, dim3(64 * NW), 0, st, a.ev_start, a.ev_stop, 0, p);
     return hipGetLastError();
 }
 

@@ -22,6 +22,8 @@ pytestmark = pytest.mark.gpu
 def _workload(shape, T):
     if shape == "mla":
         return configs.Workload("paged_mla", 520, "mla", 3, 16, 1, T, 64, 64, 4, 512, 32, 2, 20.0)
+    if shape == "mla_int4":   # INT4 content latent and INT4 RoPE key
+        return configs.Workload("paged_mla4", 521, "mla", 3, 16, 1, T, 64, 64, 4, 512, 32, 4, 20.0)
     d = {
         "gqa4_g64": (6, 8, 2, 128, 64, 2, 2),
         "gqa4_g32": (6, 8, 2, 128, 32, 2, 2),
@@ -155,7 +157,7 @@ def _check_decode(orc, pg, k_full, v_full, q, got, seqs=None):
     return worst, excess
 
 
-@pytest.mark.parametrize("shape", ["gqa4_g64", "gqa4_g32", "mha_d64", "mha_d128", "mha_d128_g32", "kv4bit", "mla",
+@pytest.mark.parametrize("shape", ["gqa4_g64", "gqa4_g32", "mha_d64", "mha_d128", "mha_d128_g32", "kv4bit", "mla", "mla_int4",
                                    "d32_g64", "gqa4_4bit_g64", "gqa4_4bit_g32", "mha_d128_4bit"])
 def test_paged_ragged_append_and_decode(orc, shape):
     w = _workload(shape, 700)

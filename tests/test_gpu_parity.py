@@ -103,8 +103,8 @@ def _tiny(T, Hq=4, Hkv=2, D=64, G=32, kbits=2, vbits=2, B=2, idx=200):
     return configs.Workload("tiny", idx, "kivi", B, Hq, Hkv, T, D, G, kbits, D, 32, vbits, 50.0)
 
 
-def _mla_tiny(T, Hq=16, B=2, idx=300):
-    return configs.Workload("mla_tiny", idx, "mla", B, Hq, 1, T, 64, 64, 4, 512, 32, 2, 20.0)
+def _mla_tiny(T, Hq=16, B=2, idx=300, vbits=2):
+    return configs.Workload("mla_tiny", idx, "mla", B, Hq, 1, T, 64, 64, 4, 512, 32, vbits, 20.0)
 
 
 def _check_decode(orc, w, dc, k, v, n_splits=0, kq_blocks=None):
@@ -146,16 +146,23 @@ def _shape(shape, T):
         return _mla_tiny(T, Hq=64)
     if shape == "mla128":
         return _mla_tiny(T, Hq=128, B=1)
+    # QuantMLA's INT4 content latent (RoPE key INT4 as always)
+    if shape == "mla4":
+        return _mla_tiny(T, vbits=4, idx=310)
+    if shape == "mla4_64":
+        return _mla_tiny(T, Hq=64, vbits=4, idx=311)
+    if shape == "mla4_128":
+        return _mla_tiny(T, Hq=128, B=1, vbits=4, idx=312)
     raise KeyError(shape)
 
 
 @pytest.mark.parametrize("T", [1, 15, 31, 32, 33, 101, 3 * 64 + 5, 700])
 @pytest.mark.parametrize("shape", ["mha", "mha128_g32", "mha128_g64", "gqa4", "gqa8_g64", "mla", "mla64",
                                    "mla128", "gqa4_4bit_g64", "gqa4_4bit_g32", "mha128_4bit_g64",
-                                   "mha128_4bit_g32"])
+                                   "mha128_4bit_g32", "mla4", "mla4_64", "mla4_128"])
 def test_edge_lengths(orc, T, shape):
     if shape in ("mha", "mha128_g32", "mha128_g64", "mla64", "mla128", "gqa4_4bit_g64", "gqa4_4bit_g32",
-                 "mha128_4bit_g64", "mha128_4bit_g32"):
+                 "mha128_4bit_g64", "mha128_4bit_g32", "mla4", "mla4_64", "mla4_128"):
         w = _shape(shape, T)
     elif shape == "gqa4":
         w = _tiny(T, Hq=8, Hkv=2, D=128)
@@ -175,7 +182,8 @@ def test_edge_lengths(orc, T, shape):
 
 
 @pytest.mark.parametrize("n_splits", [1, 2, 3, 7, 64, 256])
-@pytest.mark.parametrize("shape", ["gqa4", "mha128_g32", "mla64", "gqa4_4bit_g64", "gqa4_4bit_g32", "mha128_4bit_g32"])
+@pytest.mark.parametrize("shape", ["gqa4", "mha128_g32", "mla64", "gqa4_4bit_g64", "gqa4_4bit_g32", "mha128_4bit_g32",
+                                   "mla4_64", "mla4"])
 def test_split_counts(orc, n_splits, shape):
     w = _tiny(1000, Hq=8, Hkv=2, D=128, G=32) if shape == "gqa4" else _shape(shape, 1000)
     cap = w.capacity()
@@ -242,7 +250,7 @@ def test_unflushed_full_residual(orc):
     _check_decode(orc, w, dc, k, v)
 
 
-@pytest.mark.parametrize("shape", ["gqa4_g32", "mha128_g32", "gqa4_g64", "mha128_g64", "mla64"])
+@pytest.mark.parametrize("shape", ["gqa4_g32", "mha128_g32", "gqa4_g64", "mha128_g64", "mla64", "mla4_64"])
 def test_unflushed_full_residual_mfma(orc, shape):
     """MFMA kernels: the KIVI tail then holds the longest it can, a whole
     quantized block plus a full residual (G = 32), or a full residual of 64
@@ -391,14 +399,15 @@ def test_random_bit_pattern_fuzz(orc, G, bits):
                             oracle_slice(orc, w, k[0, h], v[0, h], cap // G, cap), f"fuzz G{G} b{bits} h{h}")
 
 
-@pytest.mark.parametrize("shape", ["gqa4_g64", "gqa4", "mha128_g32", "mha128_g64", "mha", "mla64", "gqa4_4bit_g64",
+@pytest.mark.parametrize("shape", ["gqa4_g64", "gqa4", "mha128_g32", "mha128_g64", "mha", "mla64", "mla4_64",
+                                   "gqa4_4bit_g64",
                                    "gqa4_4bit_g32", "mha128_4bit_g64", "mha128_4bit_g32"])
 def test_decode_step_matches_separate_calls(orc, shape):
     """kv_decode_step (append fused into the attention launch for the GQA and
     MHA kernels while no block completes) against kv_quantize_append +
     kv_decode_attention: caches and outputs bit-identical over steps that
     cross key-block boundaries, starting from an empty cache."""
-    G = 64 if shape in ("gqa4_g64", "mha128_g64", "mla64", "gqa4_4bit_g64", "mha128_4bit_g64") else 32
+    G = 64 if shape in ("gqa4_g64", "mha128_g64", "mla64", "mla4_64", "gqa4_4bit_g64", "mha128_4bit_g64") else 32
     n0 = 2 * G - 3
     steps = G + 6
     w = _shape(shape, n0 + steps)
@@ -453,5 +462,30 @@ def test_gqa_4bit_full_size(orc, G):
     worst = float(np.abs(got - ref).max())
     excess = mean_excess(got.ravel(), ref.ravel())
     log(f"[4-bit G{G}] max|err| {worst:.3e} mean excess {excess:.2e}")
+    assert worst <= TOL
+    assert excess <= MEAN_EXCESS_TOL
+
+
+def test_mla_int4_full_size(orc):
+    """QuantMLA's INT4/INT4 cache (content latent and RoPE key both 4-bit) at
+    the MLA workload's shape, 8 sequences of 16384 tokens, 128 heads: the
+    whole cache bit-exact and every (sequence, head) within 2e-3."""
+    import dataclasses
+    base = configs.BY_NAME["mla_absorbed_b64_t16384"]
+    w = dataclasses.replace(base, name="mla_int4_b8", vbits=4, batch=8)
+    cap = w.capacity(64)
+    k, v, q = synth.keys(w), synth.values(w), synth.query(w)
+    dc = new_cache(w, cap)
+    dc.append(dev_f16(k), dev_f16(v))
+    assert dc.variant(w.n_q_heads) == "mla_mfma"
+    got = _decode(dc, w, q)
+    host = _host_arrays(dc)
+    dc.close()
+    cache = orc.build_cache(k, v, w.kG, w.kbits, w.vG, w.vbits, nblk_cap=cap // w.kG, tok_cap=cap, threads=None)
+    assert_cache_equal(host, cache, w.T, w.n_blocks, "mla int4")
+    ref = oracle_attention(orc, w, cache, q)
+    worst = float(np.abs(got - ref).max())
+    excess = mean_excess(got.ravel(), ref.ravel())
+    log(f"[mla int4] max|err| {worst:.3e} mean excess {excess:.2e} max|o| {np.abs(ref).max():.3f}")
     assert worst <= TOL
     assert excess <= MEAN_EXCESS_TOL

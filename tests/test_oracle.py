@@ -332,9 +332,13 @@ def test_attention_bruteforce_workload0(orc):
     assert np.abs(got - ref).max() <= 1e-12
 
 
+@pytest.mark.parametrize("vbits", [2, 4])
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
-def test_attention_bruteforce_mla(orc, T):
-    w = configs.Workload("m", 150, "mla", 2, 8, 1, T, 64, 64, 4, 128, 32, 2, 20.0)
+def test_attention_bruteforce_mla(orc, T, vbits):
+    """MLA with the content latent at INT2 or INT4 (QuantMLA's two content
+    widths) and the RoPE key at INT4, against numpy over the documented
+    layouts."""
+    w = configs.Workload("m", 150, "mla", 2, 8, 1, T, 64, 64, 4, 128, 32, vbits, 20.0)
     cache, _, _ = _cache_for(orc, w)
     q = synth.query(w)
     got = orc.attention_mla(cache, q, w.sigma, nthreads=2)
