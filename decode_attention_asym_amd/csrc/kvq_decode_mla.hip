@@ -14,33 +14,43 @@
 // content quantizer and per-channel key quantizer are KIVI's ("Makale
 // Bülteni -- KIVI", section "İddia ve Gerçeklik: KIVI").
 //
-// One workgroup of 8 waves (two per SIMD) takes 64 query heads of one
-// sequence over a run of 16-token tiles; 128 heads take two workgroups.
-// Wave w owns latent channels [64w, 64w + 64) and does all the work on
-// them, so every content element is dequantized once per workgroup:
+// Arithmetic:
 //  * dequant: codes become exact fp16 integers by an exponent trick
-//    ((bits & mask) | exponent of 2^(10-b u) is 2^(10-b u) + code for the
-//    b-bit code at position u of its byte);
-//    c_hat = code * s + z is one fused fp16 FMA (the correctly rounded hi)
-//    plus the fp32 remainder c_hat - hi (lo);
-//  * QK^T: partial logits of all 64 heads over the wave's own channels
-//    (v_mfma_f32_16x16x32_f16, Q in registers, the hi tile transposed to
-//    token-major through a wave-private LDS block); the RoPE term of one
-//    (16-head, 32-channel) block per wave uses exact 4-bit code operands
-//    (the codes as fp16 integers) against q' = q_r * s_k in hi/lo rows plus the bias
-//    sum_c q_r z_k, or the fp16 residual keys;
-//  * softmax: wave w sums the 8 partials of heads [8w, 8w + 8), runs the
-//    online softmax in log2 units (lazily moved maxima) and writes fp16
-//    weights; the row sums add up the same fp16 values;
-//  * PV: O[64 heads][own channels] += P . (hi + lo) on
-//    v_mfma_f32_32x32x16_f16.
-// Three tiles are in flight: a step does PV of tile i-2, the softmax of tile
-// i-1 and dequant + QK^T of tile i, with one workgroup barrier, so the matrix
-// work of one wave overlaps the vector work of the other.
-// Tokens at or past T in the last tile get zero weight; their codes are read
-// (they lie inside the caller's capacity) but never contribute.
+//    ((bits & mask) | exponent of 2^(10-f) is 2^(10-f) + code for the code
+//    in bit field f of its byte); c_hat = code * s + z is one fused fp16 FMA
+//    (the correctly rounded hi) plus the fp32 remainder c_hat - hi (lo);
+//  * QK^T with the hi latent (v_mfma_f32_16x16x32_f16); the RoPE term uses
+//    exact 4-bit code operands (the codes as fp16 integers) against
+//    q' = q_r * s_k in hi/lo rows plus the bias sum_c q_r z_k, or the fp16
+//    residual keys;
+//  * online softmax in log2 units (maxima moved lazily, by more than TAU),
+//    fp16 weights whose row sums add up the same fp16 values;
+//  * PV: O += P . (hi + lo) on v_mfma_f32_32x32x16_f16.
+//
+// Work split.  One workgroup of four waves, one per SIMD, takes 64 query
+// heads of one sequence over a run of 16-token tiles (128 heads take two
+// workgroups).  One wave per SIMD gets 512 registers: the 64 x 128 PV
+// accumulators of a wave and its 16 heads' content query rows (the QK^T A
+// operands, which the matrix instructions read there directly) sit in its
+// accumulation registers, the dequantized latent of two tiles in its vector
+// registers.
+//  * QK^T and the softmax by heads: wave w owns heads [16w, 16w + 16) of the
+//    workgroup over the whole 576-wide contraction; the tile's hi latent is
+//    read token-major from LDS as the B operand.  A logit needs no sum
+//    across waves.
+//  * PV by latent channels: wave w owns channels [128w, 128w + 128), which it
+//    dequantized itself, for the workgroup's 64 heads (the weights read from
+//    LDS as A operands).  Column j of channel block u is channel
+//    128w + 4j + u: a lane's four channels are the four codes of one 2-bit
+//    code byte.
+// Software pipeline, one workgroup barrier per tile: step k runs PV of tile
+// k - 1, QK^T of tile k and the dequant of tile k + 1, then the softmax of
+// tile k, the RoPE operands of tile k + 1's block, the staging of tile k + 2
+// into LDS and the global loads of tile k + 4.
 #include <hip/hip_fp16.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "kvq_internal.h"
 
@@ -57,13 +67,7 @@ constexpr int VD = 512;      // content latent dim
 constexpr int KD = 64;       // RoPE dim
 constexpr int QD = VD + KD;  // query row
 constexpr int GR = 64;       // RoPE key block (tokens)
-constexpr int HQ = 64;       // query heads per workgroup
-constexpr int NW = 8;        // waves per workgroup
-constexpr int CWS = 36;      // dwords per token row of a wave's hi block (64 fp16 + pad)
-constexpr int SXS = 68;      // floats per token row of a partial-logit block (64 heads + pad)
-constexpr int RCS = 68;      // dwords per word row of the RoPE code block (64 + pad)
 constexpr int QRS = 36;      // dwords per head row of q' (64 fp16 + pad)
-constexpr int PS = 12;       // dwords per head row of P (16 fp16 + pad)
 constexpr float TAU = 8.0f;  // lazy-rescale threshold (log2 units)
 
 struct MlaParams {
@@ -77,23 +81,6 @@ struct MlaParams {
     int64_t T, nblk, cap, nblk_cap;
     float sigma2;                // softmax scale * log2(e)
     float neg1;                  // -1, kept opaque so c*s + z - hi stays one mixed FMA
-};
-
-struct Lds {
-    __attribute__((aligned(16))) float sx[2][NW][16 * SXS];  // partial logits [buf][wave][token][head]
-    __attribute__((aligned(16))) float srx[2][NW][16 * 20];  // RoPE partials [buf][wave][token][16 heads]
-    __attribute__((aligned(16))) uint32_t chw[NW][16 * CWS]; // per wave: hi, token-major [token][64 fp16]
-    __attribute__((aligned(16))) uint32_t cst[NW][8 * 16];   // per wave: content codes [word][token] (4 or 8 words)
-    __attribute__((aligned(16))) uint32_t sst[NW][2 * 2 * 8];  // per wave: [scale|zero][group][16 fp16]
-    __attribute__((aligned(16))) uint32_t pm[2][HQ * PS];    // weights fp16 [buf][head][16 tokens]
-    __attribute__((aligned(16))) uint32_t rc[8 * RCS];       // RoPE codes of the block [word][channel]
-    uint32_t rs[2 * 32];                                     // RoPE [scale|zero][64 fp16]
-    __attribute__((aligned(16))) uint32_t qr[HQ * 32];       // q_r fp16 [head][64]
-    __attribute__((aligned(16))) uint32_t qrh[HQ * QRS];     // q' = q_r * s_k, hi [head][64 fp16]
-    __attribute__((aligned(16))) uint32_t qrl[HQ * QRS];     // lo
-    float rbias[HQ];                                         // RoPE zero bias of the block per head
-    float alpha[2][HQ];                                      // rescale factors [buf][head]
-    __attribute__((aligned(16))) int wflag[2][NW];           // softmax wave w moved some maxima
 };
 
 __device__ __forceinline__ float lo_h(uint32_t w) { return float(__builtin_bit_cast(f16x2, w)[0]); }
@@ -153,346 +140,403 @@ __device__ __forceinline__ void dequant_pair(uint32_t h, uint32_t bias2, uint32_
     lo = __builtin_bit_cast(uint32_t, lv);
 }
 
-struct Frags {
-    uint32_t h[2][4], l[2][4];   // [channel 2*c32 + v][token pair]
+constexpr int HW = 64;      // query heads per workgroup
+constexpr int NW4 = 4;      // waves per workgroup
+constexpr int CHS = 260;    // dwords per token row of a hi tile (512 fp16 + pad)
+constexpr int PS2 = 12;     // dwords per head row of P (16 fp16 + pad)
+constexpr int RRS = 512;    // dwords per staged RoPE record
+
+struct Lds4w {
+    __attribute__((aligned(16))) uint32_t ch[2][16 * CHS];       // hi latent [tile parity][token][512 fp16]
+    __attribute__((aligned(16))) uint32_t pm[2][HW * PS2];       // weights fp16 [tile parity][head][16 tokens]
+    __attribute__((aligned(16))) uint32_t cst[2][NW4][16 * 16];  // per wave: content codes [parity][word][token]
+    __attribute__((aligned(16))) uint32_t sst[2][NW4][64];       // per wave: [parity][scale|zero][group][token pair]
+    // RoPE record of a tile [tile mod 4]: quantized block: codes [word][64
+    // channels] (dwords 0..127), the block's scales and zeros (128..191);
+    // residual block: the tile's 16 fp16 key rows (dwords 0..511)
+    __attribute__((aligned(16))) uint32_t rr[4][RRS];
+    __attribute__((aligned(16))) uint32_t qr[HW * QRS];          // q_r fp16 [head][64 + pad]
+    __attribute__((aligned(16))) uint4 qa[NW4][4][64];           // per lane: q' hi/lo A operands [kr][hl]
+    __attribute__((aligned(16))) float alpha[2][HW];             // rescale factors [tile parity][head]
+    __attribute__((aligned(16))) int wflag[2][NW4];              // wave w moved some of its maxima
 };
 
-// Content code width VB (2 or 4): a wave's 64 channels are CW words per token.
+struct Frags {
+    uint32_t h[4][4], l[4][4];   // [channel block u][token pair]
+};
+
+// One tile's global loads, two steps ahead of their staging into LDS.
+struct Pre {
+    uint4 cw;       // own content code words of token t0 + (lane >> 2)
+    uint32_t sw;    // content scale or zero pair of token t0 + (lane & 15)
+    uint2 rw;       // RoPE record dwords tid, tid + 256
+};
+
 template <int VB>
-__global__ __launch_bounds__(512) void k_decode_mla(MlaParams p) {
-    constexpr int CW = 64 * VB / 32;    // own code words per token
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_decode_mla(MlaParams p) {
+    constexpr int CW = 128 * VB / 32;   // own code words per token (8 or 16)
     constexpr int VWT = VD * VB / 32;   // code words per token
-    __shared__ Lds L;
+    __shared__ Lds4w L;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, kg = lane >> 4;        // 16x16x32 operand layout
     const int c32 = lane & 31, h32 = lane >> 5;     // 32x32x16 operand layout
-    const int tq = lane & 15, hp = lane >> 4;       // softmax: token, head pair
-    const int s = blockIdx.x, b = blockIdx.y;       // blockIdx.z: group of 64 query heads
+    const int s = blockIdx.x, b = blockIdx.y;
     const int t_lo = int(int64_t(s) * p.ntiles / p.S);
     const int t_hi = int(int64_t(s + 1) * p.ntiles / p.S);
-    const int64_t qrow0 = int64_t(b) * p.Hq + int64_t(blockIdx.z) * HQ;
-    const int ch0 = 64 * wave;                      // first own latent channel
+    const int64_t qrow0 = int64_t(b) * p.Hq + HW * blockIdx.z;   // first query row of the workgroup
+    const int hw0 = 16 * wave;    // first own head (QK^T, softmax)
+    const int ch0 = 128 * wave;   // first own latent channel (PV)
+    if (t_lo >= t_hi) {
+        // an empty run (the split plans make none): an empty partial
+        for (int i = tid; i < HW * VD; i += 256) p.ws_acc[((qrow0 + i / VD) * p.S + s) * VD + i % VD] = 0.0f;
+        if (tid < HW) {
+            p.ws_ml[((qrow0 + tid) * p.S + s) * 2] = -INFINITY;
+            p.ws_ml[((qrow0 + tid) * p.S + s) * 2 + 1] = 0.0f;
+        }
+        return;
+    }
 
-    // ---- q_r to LDS; content query rows of the own channels as A operands
-    for (int i = tid; i < HQ * 32; i += 512)
-        L.qr[i] = reinterpret_cast<const uint32_t*>(p.q + (qrow0 + i / 32) * QD + VD)[i % 32];
-    f16x8 QA[4][2];
+    // ---- q_r of the 64 heads to LDS; the own heads' content rows as A
+    // operands: QA[ks] = channels 32ks + 8kg .. + 7 of head hw0 + n
+    for (int i = tid; i < HW * 32; i += 256)
+        L.qr[(i >> 5) * QRS + (i & 31)] = reinterpret_cast<const uint32_t*>(p.q + (qrow0 + (i >> 5)) * QD + VD)[i & 31];
+    // (kept in accumulation registers, which the matrix instructions read
+    // directly: the vector registers hold the dequantized latent)
+    f16x8 QA[16];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            QA[m][ks] = as_f16x8(*reinterpret_cast<const uint4*>(
-                p.q + (qrow0 + 16 * m + n) * QD + ch0 + 32 * ks + 8 * kg));
+    for (int ks = 0; ks < 16; ++ks) {
+        QA[ks] = as_f16x8(*reinterpret_cast<const uint4*>(p.q + (qrow0 + hw0 + n) * QD + 32 * ks + 8 * kg));
+        asm volatile("" : "+a"(QA[ks]));
+    }
 
-    f32x16 O[2][2];   // [32-head row block][channel 2*c32 + v]
+    f32x16 O[2][4];   // [32-head row block m][channel block u]
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int v = 0; v < 2; ++v)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) O[m][v][e] = 0.0f;
-    // softmax state of heads 8w + 2hp + e, this lane's token share
-    float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.0f, 0.0f};
+            for (int e = 0; e < 16; ++e) O[m][u][e] = 0.0f;
+    // softmax state of heads hw0 + 4kg + j, and this lane's token share of
+    // their row sums
+    float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, lrun[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 rb = f32x4{0.f, 0.f, 0.f, 0.f};   // RoPE bias of the block, rows 4kg + j
 
-    // per-lane dequant constants: channels ch0 + 2*c32 + v sit at code
-    // position u = 2(c32 & 1) + v of byte (c32 & 7) >> 1 of word c32 >> 3
-    // (2 bits), or in nibble v of byte c32 & 3 of word c32 >> 2 (4 bits)
-    uint32_t dmk[2], de2[2], dnb[2];
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-        const int u = VB == 2 ? 2 * (c32 & 1) + v : v;
-        const uint32_t ex = uint32_t(25 - VB * u) << 10;   // exponent field of 2^(10-VB*u)
-        dmk[v] = (VB == 2 ? 0x00030003u : 0x000F000Fu) << (VB * u);
-        de2[v] = ex | (ex << 16);
-        dnb[v] = de2[v] | 0x80008000u;
-    }
-    const uint32_t csel = byte_pair_sel(VB == 2 ? (c32 & 7) >> 1 : c32 & 3);
-    const int cword = VB == 2 ? c32 >> 3 : c32 >> 2;      // own word of the lane's channels
-    const uint32_t rsel = byte_pair_sel((n & 7) >> 1);    // RoPE: byte of the lane's token
-    // (its code is the low nibble for even n, the high one for odd n)
-    const int mr = wave >> 1, kr = wave & 1;              // this wave's RoPE block
+    // Dequant layout: lane (c32, h32) takes channels ch0 + 4c32 + u of tokens
+    // 8h32 .. 8h32 + 7.  2 bits: code u of byte c32 & 3 of own word c32 >> 2;
+    // 4 bits: nibble u & 1 of byte 2(c32 & 1) + (u >> 1) of own word c32 >> 1
+    const int cword = VB == 2 ? c32 >> 2 : c32 >> 1;
+    const uint32_t csel0 = byte_pair_sel(VB == 2 ? c32 & 3 : 2 * (c32 & 1));
+    const uint32_t csel1 = byte_pair_sel(VB == 2 ? c32 & 3 : 2 * (c32 & 1) + 1);
+    const uint32_t rsel = byte_pair_sel((n & 7) >> 1);   // RoPE: byte of the lane's token
 
-    // content loads (two tiles ahead): code words CW/4 * (lane & 3) .. of the
-    // own CW words of token t0 + (lane >> 2) (one word at 2 bits, two at 4);
-    // side (lanes < 32): scale (lanes < 16) / zero pair of the own 2 groups of
-    // token t0 + (lane & 15)
+    // ---- global loads of tile t (clamped to the last tile: a load past the
+    // run reads valid memory and is never used).  Content: own words
+    // (CW / 4)(lane & 3) .. of token t0 + (lane >> 2); lane (sz, gp, tl)
+    // takes the scale (sz = 0) or zero pair of own groups 2gp, 2gp + 1 of
+    // token t0 + tl.  RoPE record dwords tid and tid + 256.
     const uint32_t* vcb = p.vc + int64_t(b) * p.cap * VWT + CW * wave + (CW / 4) * (lane & 3);
-    const uint16_t* vsb = ((lane & 16) ? p.vz : p.vs) + int64_t(b) * p.cap * 16 + 2 * wave;
-    auto load_content = [&](int tile, uint2& cw, uint32_t& sw) {
-        const int64_t t0 = int64_t(tile) * 16;
+    const uint16_t* vsb = ((lane & 32) ? p.vz : p.vs) + int64_t(b) * p.cap * 16 + 4 * wave + 2 * ((lane >> 4) & 1);
+    auto load = [&](int t, Pre& P) __attribute__((always_inline)) {
+        t = t < p.ntiles ? t : p.ntiles - 1;
+        const int64_t t0 = int64_t(t) * 16;
         const uint32_t* src = vcb + (t0 + (lane >> 2)) * VWT;
-        cw = VB == 2 ? make_uint2(src[0], 0u) : *reinterpret_cast<const uint2*>(src);
-        sw = lane < 32 ? *reinterpret_cast<const uint32_t*>(vsb + (t0 + (lane & 15)) * 16) : 0u;
-    };
-    // RoPE block loads: code word tid of the block; side (tid < 64)
-    auto load_rope = [&](int64_t blk, uint32_t& rw, uint32_t& rsw) {
-        rw = p.kc[(int64_t(b) * p.nblk_cap + blk) * GR * 8 + tid];
-        rsw = tid < 64 ? reinterpret_cast<const uint32_t*>((tid < 32 ? p.ks : p.kz) +
-                                                           (int64_t(b) * p.nblk_cap + blk) * KD)[tid & 31]
-                       : 0u;
-    };
-    // tile i's content words in slot (i - t_lo) & 1
-    uint2 cwq[2] = {make_uint2(0u, 0u), make_uint2(0u, 0u)};
-    uint32_t swq[2] = {0u, 0u}, rw_n = 0u, rsw_n = 0u;
-    load_content(t_lo, cwq[0], swq[0]);
-    if (t_lo + 1 < t_hi) load_content(t_lo + 1, cwq[1], swq[1]);
-    if (int64_t(t_lo) * 16 / GR < p.nblk) load_rope(int64_t(t_lo) * 16 / GR, rw_n, rsw_n);
-    __syncthreads();
-
-    Frags F[2];        // tile i's operands in F[(i - t_lo) & 1]
-    int64_t cur_blk = -1;
-
-    // ---- stage 1 of tile i: dequant, QK^T partials -> sx[i & 1]
-    auto front = [&](int i, Frags& fr, uint2& cwr, uint32_t& swr) {
-        const int64_t t0 = int64_t(i) * 16;
+        if (VB == 2) {
+            const uint2 w = *reinterpret_cast<const uint2*>(src);
+            P.cw = make_uint4(w.x, w.y, 0u, 0u);
+        } else {
+            P.cw = *reinterpret_cast<const uint4*>(src);
+        }
+        P.sw = *reinterpret_cast<const uint32_t*>(vsb + (t0 + (lane & 15)) * 16);
         const int64_t blk = t0 / GR;
-        const bool qrope = blk < p.nblk;
-        if (qrope && blk != cur_blk) {
-            // entering a quantized RoPE block: codes, side, q' = q_r * s_k, bias
-            L.rc[(tid & 7) * RCS + (tid >> 3)] = rw_n;
-            if (tid < 64) L.rs[tid] = rsw_n;
-            cur_blk = blk;
-            if (blk + 1 < p.nblk && (blk + 1) * GR < int64_t(t_hi) * 16) load_rope(blk + 1, rw_n, rsw_n);
-            __syncthreads();
-            // lane (cp = lane & 31) takes channel pair cp of heads 2*(tid >> 6)
-            // + (lane >> 5) + 16k; the bias sum runs over the 32 lanes of a head
-            const int cp = lane & 31;
-            const uint32_t sv = L.rs[cp], zv = L.rs[32 + cp];
+        const uint32_t *ax, *ay;
+        if (blk < p.nblk) {
+            // codes: dword tid < 128 is word 2(t mod 4) + (tid >> 6) of
+            // channel tid & 63; dwords 128..191 the scales, then the zeros
+            const int64_t row = int64_t(b) * p.nblk_cap + blk;
+            const uint32_t* kc = p.kc + row * GR * 8;
+            ax = tid < 128 ? kc + (tid & 63) * 8 + 2 * (t & 3) + (tid >> 6)
+                 : tid < 192 ? reinterpret_cast<const uint32_t*>(((tid & 32) ? p.kz : p.ks) + row * KD) + (tid & 31)
+                             : kc;
+            ay = kc;
+        } else {
+            // the residual key rows t0 - 64 nblk .. + 15 (inside its 64 rows)
+            const uint32_t* kr = reinterpret_cast<const uint32_t*>(p.kr + (int64_t(b) * GR + (t0 - p.nblk * GR)) * KD);
+            ax = kr + tid;
+            ay = kr + tid + 256;
+        }
+        P.rw = make_uint2(*ax, *ay);
+    };
+    // ---- staging of tile t into LDS (content: wave-private; RoPE record:
+    // shared).  Tokens at or past T get scale and zero 0, so they dequantize
+    // to exact zeros.
+    auto stage = [&](int t, const Pre& P) __attribute__((always_inline)) {
+        uint32_t* cst = L.cst[t & 1][wave];
+        const int tk = lane >> 2, w0 = (CW / 4) * (lane & 3);
+        cst[w0 * 16 + tk] = P.cw.x;
+        cst[(w0 + 1) * 16 + tk] = P.cw.y;
+        if (VB == 4) {
+            cst[(w0 + 2) * 16 + tk] = P.cw.z;
+            cst[(w0 + 3) * 16 + tk] = P.cw.w;
+        }
+        const int sz = lane >> 5, gp = (lane >> 4) & 1, tl = lane & 15;
+        const uint32_t sw = int64_t(t) * 16 + tl < p.T ? P.sw : 0u;
+        // lane (sz, gp, tl) holds groups (2gp, 2gp + 1) of token tl; even tl
+        // writes group 2gp of tokens (tl, tl + 1), odd tl group 2gp + 1
+        const uint32_t other = uint32_t(__builtin_amdgcn_update_dpp(0, int(sw), 0xb1, 0xf, 0xf, false));
+        const bool odd = (tl & 1) != 0;
+        const uint32_t wv = odd ? __builtin_amdgcn_perm(sw, other, 0x07060302u)
+                                : __builtin_amdgcn_perm(other, sw, 0x05040100u);
+        L.sst[t & 1][wave][(sz * 4 + 2 * gp + (odd ? 1 : 0)) * 8 + (tl >> 1)] = wv;
+        L.rr[t & 3][tid] = P.rw.x;
+        L.rr[t & 3][tid + 256] = P.rw.y;
+    };
+
+    // ---- q' = q_r * s_k (hi/lo A operands, lane-private) and the bias of
+    // the own heads for the quantized block of tile t (record staged)
+    auto fold = [&](int t) __attribute__((always_inline)) {
+        const uint32_t* rec = L.rr[t & 3];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int h = 2 * wave + (lane >> 5) + 16 * k;
-                const uint32_t qv = L.qr[h * 32 + cp];
-                uint32_t hi, lo;
-                split_prod2(lo_h(qv), lo_h(sv), hi_h(qv), hi_h(sv), hi, lo);
-                L.qrh[h * QRS + cp] = hi;
-                L.qrl[h * QRS + cp] = lo;
-                float bp = fmaf(hi_h(qv), hi_h(zv), lo_h(qv) * lo_h(zv));
-                bp = row_sum16(bp);
-                bp += __shfl_xor(bp, 16);
-                if (cp == 0) L.rbias[h] = bp;
+        for (int kr = 0; kr < 2; ++kr) {
+            const uint4 sv = *reinterpret_cast<const uint4*>(rec + 128 + 16 * kr + 4 * kg);
+            const uint4 zv = *reinterpret_cast<const uint4*>(rec + 160 + 16 * kr + 4 * kg);
+            const uint4 qv = *reinterpret_cast<const uint4*>(L.qr + (hw0 + n) * QRS + 16 * kr + 4 * kg);
+            const uint32_t sa[4] = {sv.x, sv.y, sv.z, sv.w};
+            const uint32_t qa[4] = {qv.x, qv.y, qv.z, qv.w};
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) split_prod2(lo_h(qa[e]), lo_h(sa[e]), hi_h(qa[e]), hi_h(sa[e]), hi[e], lo[e]);
+            L.qa[wave][kr * 2][lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            L.qa[wave][kr * 2 + 1][lane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            // bias sum_c q_r z_k: every column of B holds the zeros
+            rb = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(qv), as_f16x8(zv), kr ? rb : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        }
+    };
+
+    // ---- dequant of tile t (codes staged): hi token-major into its LDS tile
+    // for QK^T, hi and lo of the own channels into F for PV
+    auto dequant = [&](int t, Frags& F) __attribute__((always_inline)) {
+        const uint32_t* cs = L.cst[t & 1][wave] + cword * 16 + 8 * h32;
+        const uint4 wa = *reinterpret_cast<const uint4*>(cs);
+        const uint4 wb = *reinterpret_cast<const uint4*>(cs + 4);
+        const uint32_t wt[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+        const uint32_t* sp = L.sst[t & 1][wave] + (c32 >> 3) * 8 + 4 * h32;
+        const uint4 sv = *reinterpret_cast<const uint4*>(sp);
+        const uint4 zv = *reinterpret_cast<const uint4*>(sp + 32);
+        const uint32_t sa[4] = {sv.x, sv.y, sv.z, sv.w}, za[4] = {zv.x, zv.y, zv.z, zv.w};
+        uint32_t* chb = L.ch[t & 1];
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+            // code bytes of tokens 8h32 + 2q2 (low half) and + 1 (high half)
+            const uint32_t x0 = __builtin_amdgcn_perm(wt[2 * q2 + 1], wt[2 * q2], csel0);
+            const uint32_t x1 = VB == 2 ? x0 : __builtin_amdgcn_perm(wt[2 * q2 + 1], wt[2 * q2], csel1);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                // field f of the code in its byte; (bits & mask) | exponent of
+                // 2^(10 - f) is the fp16 2^(10 - f) + code
+                const int f = VB == 2 ? 2 * u : 4 * (u & 1);
+                const uint32_t mk = (VB == 2 ? 0x00030003u : 0x000F000Fu) << f;
+                const uint32_t ex = uint32_t(25 - f) << 10;
+                const uint32_t x = (VB == 2 || u < 2) ? x0 : x1;
+                dequant_pair((x & mk) | ex | (ex << 16), ex | (ex << 16) | 0x80008000u, sa[q2], za[q2], p.neg1,
+                             F.h[u][q2], F.l[u][q2]);
             }
+            // hi, token-major: channels ch0 + 4c32 .. + 3 of the two tokens
+            uint32_t* row = chb + (8 * h32 + 2 * q2) * CHS + 64 * wave + 2 * c32;
+            *reinterpret_cast<uint2*>(row) = make_uint2(__builtin_amdgcn_perm(F.h[1][q2], F.h[0][q2], 0x05040100u),
+                                                        __builtin_amdgcn_perm(F.h[3][q2], F.h[2][q2], 0x05040100u));
+            *reinterpret_cast<uint2*>(row + CHS) =
+                make_uint2(__builtin_amdgcn_perm(F.h[1][q2], F.h[0][q2], 0x07060302u),
+                           __builtin_amdgcn_perm(F.h[3][q2], F.h[2][q2], 0x07060302u));
         }
-        // stage the own codes and side values, prefetch tile i + 2
-        {
-            const uint2 cw = cwr;
-            const uint32_t sw = swr;
-            if (i + 2 < t_hi) load_content(i + 2, cwr, swr);
-            L.cst[wave][(CW / 4) * (lane & 3) * 16 + (lane >> 2)] = cw.x;
-            if (VB == 4) L.cst[wave][(2 * (lane & 3) + 1) * 16 + (lane >> 2)] = cw.y;
-            // lane (sz, tl) holds groups (0, 1) of token tl; even tl writes
-            // group 0 of tokens (tl, tl + 1), odd tl group 1
-            const uint32_t other = uint32_t(__builtin_amdgcn_update_dpp(0, int(sw), 0xb1, 0xf, 0xf, false));
-            const int sz = (lane >> 4) & 1, tl = lane & 15;
-            const bool odd = (tl & 1) != 0;
-            const uint32_t wv = odd ? __builtin_amdgcn_perm(sw, other, 0x07060302u)
-                                    : __builtin_amdgcn_perm(other, sw, 0x05040100u);
-            if (lane < 32) L.sst[wave][(sz * 2 + (odd ? 1 : 0)) * 8 + (tl >> 1)] = wv;
+    };
+
+    // ---- content part of the logits of the own 16 heads over tile t
+    auto qk_content = [&](int t) __attribute__((always_inline)) {
+        f32x4 S = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t* chr = L.ch[t & 1] + n * CHS + 4 * kg;
+        // B operands requested in batches ahead of their products
+        constexpr int NB = 4;
+#pragma unroll
+        for (int kb = 0; kb < 16; kb += NB) {
+            uint4 Bk[NB];
+#pragma unroll
+            for (int j = 0; j < NB; ++j) Bk[j] = *reinterpret_cast<const uint4*>(chr + 16 * (kb + j));
+#pragma unroll
+            for (int j = 0; j < NB; ++j) S = __builtin_amdgcn_mfma_f32_16x16x32_f16(QA[kb + j], as_f16x8(Bk[j]), S, 0, 0, 0);
         }
-        wave_sync();
-        // dequant channels ch0 + 2*c32 + v of tokens 8*h32 .. 8*h32 + 7
-        {
-            const uint32_t* cs = L.cst[wave] + cword * 16 + 8 * h32;
-            const uint4 wa = *reinterpret_cast<const uint4*>(cs);
-            const uint4 wb = *reinterpret_cast<const uint4*>(cs + 4);
-            const uint32_t x[4] = {__builtin_amdgcn_perm(wa.y, wa.x, csel), __builtin_amdgcn_perm(wa.w, wa.z, csel),
-                                   __builtin_amdgcn_perm(wb.y, wb.x, csel), __builtin_amdgcn_perm(wb.w, wb.z, csel)};
-            const uint32_t* sp = L.sst[wave] + (c32 >> 4) * 8 + 4 * h32;
-            const uint4 sv = *reinterpret_cast<const uint4*>(sp);
-            const uint4 zv = *reinterpret_cast<const uint4*>(sp + 16);
-            uint32_t sa[4] = {sv.x, sv.y, sv.z, sv.w}, za[4] = {zv.x, zv.y, zv.z, zv.w};
-            if (t0 + 16 > p.T) {
-                // tokens at or past T: scale and zero 0, so every value is 0
-#pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2) {
-                    const int64_t ta = t0 + 8 * h32 + 2 * q2;
-                    const uint32_t keep = (ta < p.T ? 0x0000ffffu : 0u) | (ta + 1 < p.T ? 0xffff0000u : 0u);
-                    sa[q2] &= keep;
-                    za[q2] &= keep;
-                }
-            }
-#pragma unroll
-            for (int v = 0; v < 2; ++v)
-#pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2)
-                    dequant_pair((x[q2] & dmk[v]) | de2[v], dnb[v], sa[q2], za[q2], p.neg1, fr.h[v][q2],
-                                 fr.l[v][q2]);
-            // token-major hi: token 8*h32 + 2*q2 (+1), channels 2*c32, 2*c32 + 1
-            uint32_t* cw = L.chw[wave];
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2) {
-                cw[(8 * h32 + 2 * q2) * CWS + c32] = __builtin_amdgcn_perm(fr.h[1][q2], fr.h[0][q2], 0x05040100u);
-                cw[(8 * h32 + 2 * q2 + 1) * CWS + c32] = __builtin_amdgcn_perm(fr.h[1][q2], fr.h[0][q2], 0x07060302u);
-            }
-        }
-        wave_sync();
-        // partial logits of all 64 heads over the own channels
-        f32x4 Sc[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) Sc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const f16x8 Bv = as_f16x8(*reinterpret_cast<const uint4*>(L.chw[wave] + n * CWS + 16 * ks + 4 * kg));
-#pragma unroll
-            for (int m = 0; m < 4; ++m) Sc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(QA[m][ks], Bv, Sc[m], 0, 0, 0);
-        }
-        // RoPE partial of heads 16mr .. 16mr + 15 over channels 32kr .. 32kr + 31
-        // to srx: A = q' hi, lo against the codes as exact fp16 integers (low
-        // nibble: (bits | exponent of 2^10) is 2^10 + code, high nibble: 2^6 +
-        // code), or q_r against the fp16 residual keys
-        const int hr = 16 * mr + n;
-        f32x4 Sr = f32x4{0.f, 0.f, 0.f, 0.f};
+        return S;
+    };
+
+    // ---- RoPE part of the logits over tile t, softmax, weights to LDS
+    auto qk_rope_softmax = [&](int t, f32x4 S) __attribute__((always_inline)) {
+        const int64_t t0 = int64_t(t) * 16;
+        const bool qrope = t0 / GR < p.nblk;
+        const uint32_t* rec = L.rr[t & 3];
         if (qrope) {
-            const int wr = 2 * int((t0 % GR) / 16) + (n >> 3);   // code word of token n
+            // q' hi, lo against the codes as exact fp16 integers: channel c
+            // of token n is nibble n & 1 of byte (n & 7) >> 1 of word
+            // (n >> 3) of the tile's two
             const bool hin = (n & 1) != 0;
             const uint32_t nm = hin ? 0x00f000f0u : 0x000f000fu;
             const uint32_t ne = hin ? 0x54005400u : 0x64006400u;   // 2^6 | 2^10 exponent pairs
-            const f16x2 nb = __builtin_bit_cast(f16x2, hin ? 0xd400d400u : 0xe400e400u);
-            const uint32_t* src = L.rc + wr * RCS + 32 * kr + 8 * kg;
-            const uint4 w0 = *reinterpret_cast<const uint4*>(src);
-            const uint4 w1 = *reinterpret_cast<const uint4*>(src + 4);
-            auto code2 = [&](uint32_t hw, uint32_t lw) {
-                const uint32_t x = (__builtin_amdgcn_perm(hw, lw, rsel) & nm) | ne;
-                return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, x) + nb);
+            const f16x2 nbias = __builtin_bit_cast(f16x2, hin ? 0xd400d400u : 0xe400e400u);
+            auto code2 = [&](uint32_t hw, uint32_t lw) __attribute__((always_inline)) {
+                const uint32_t xx = (__builtin_amdgcn_perm(hw, lw, rsel) & nm) | ne;
+                return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, xx) + nbias);
             };
-            const f16x8 Bv = as_f16x8(code2(w0.y, w0.x), code2(w0.w, w0.z), code2(w1.y, w1.x), code2(w1.w, w1.z));
-            const f16x8 Ah = as_f16x8(*reinterpret_cast<const uint4*>(L.qrh + hr * QRS + 16 * kr + 4 * kg));
-            const f16x8 Al = as_f16x8(*reinterpret_cast<const uint4*>(L.qrl + hr * QRS + 16 * kr + 4 * kg));
-            Sr = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bv, Sr, 0, 0, 0);
-            Sr = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bv, Sr, 0, 0, 0);
+#pragma unroll
+            for (int kr = 0; kr < 2; ++kr) {
+                const uint32_t* src = rec + (n >> 3) * 64 + 32 * kr + 8 * kg;
+                const uint4 w0 = *reinterpret_cast<const uint4*>(src);
+                const uint4 w1 = *reinterpret_cast<const uint4*>(src + 4);
+                const f16x8 Bv = as_f16x8(code2(w0.y, w0.x), code2(w0.w, w0.z), code2(w1.y, w1.x), code2(w1.w, w1.z));
+                S = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(L.qa[wave][kr * 2][lane]), Bv, S, 0, 0, 0);
+                S = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(L.qa[wave][kr * 2 + 1][lane]), Bv, S, 0, 0, 0);
+            }
         } else {
-            // residual keys, fp16: row t0 + n - nblk*64 of the residual
-            const int64_t r = t0 + n - p.nblk * GR;
-            uint4 kv = make_uint4(0u, 0u, 0u, 0u);
-            if (r < GR && t0 + n < p.T)
-                kv = *reinterpret_cast<const uint4*>(p.kr + (int64_t(b) * GR + r) * KD + 32 * kr + 8 * kg);
-            const f16x8 Aq = as_f16x8(*reinterpret_cast<const uint4*>(L.qr + hr * 32 + 16 * kr + 4 * kg));
-            Sr = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aq, as_f16x8(kv), Sr, 0, 0, 0);
-        }
-        *reinterpret_cast<f32x4*>(L.srx[i & 1][wave] + n * 20 + 4 * kg) = Sr;
-        // partial logits to sx[i & 1][wave][token n][heads 16m + 4kg .. +3]
-        float* dst = L.sx[i & 1][wave] + n * SXS + 4 * kg;
+            // q_r against the fp16 residual key rows of the record
 #pragma unroll
-        for (int m = 0; m < 4; ++m) *reinterpret_cast<f32x4*>(dst + 16 * m) = Sc[m];
-    };
-
-    // ---- stage 2 of tile i: sum the partials of heads 8w + 2hp + e, softmax,
-    // weights -> pm[i & 1], rescale factors -> alpha[i & 1], wflag[i & 1]
-    auto softmax = [&](int i) {
-        const int64_t t0 = int64_t(i) * 16;
-        const bool qrope = t0 / GR < p.nblk;
-        const int bf = i & 1;
-        const int h0 = 8 * wave + 2 * hp;
-        float x[2] = {0.0f, 0.0f};
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float2 v = *reinterpret_cast<const float2*>(L.sx[bf][w] + tq * SXS + h0);
-            x[0] += v.x;
-            x[1] += v.y;
-        }
-        // RoPE partials of heads h0, h0 + 1: waves 2(h0 >> 4) and 2(h0 >> 4) + 1
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const float2 v = *reinterpret_cast<const float2*>(L.srx[bf][2 * (h0 >> 4) + r] + tq * 20 + (h0 & 15));
-            x[0] += v.x;
-            x[1] += v.y;
-        }
-        const bool valid = t0 + tq < p.T;
-        bool over = false;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const float bias = qrope ? L.rbias[h0 + e] : 0.0f;
-            x[e] = valid ? (x[e] + bias) * p.sigma2 : -INFINITY;
-            over = over || x[e] > mrun[e] + TAU;
-        }
-        const bool moved = __builtin_amdgcn_ballot_w64(over) != 0;
-        if (moved) {
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const float mn = fmaxf(mrun[e], row_max16(x[e]));
-                const float a = __builtin_amdgcn_exp2f(mrun[e] - mn);
-                mrun[e] = mn;
-                lrun[e] *= a;
-                if (tq == 0) L.alpha[bf][h0 + e] = a;
+            for (int kr = 0; kr < 2; ++kr) {
+                const f16x8 Bv = as_f16x8(*reinterpret_cast<const uint4*>(rec + n * 32 + 16 * kr + 4 * kg));
+                const f16x8 Aq = as_f16x8(*reinterpret_cast<const uint4*>(L.qr + (hw0 + n) * QRS + 16 * kr + 4 * kg));
+                S = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aq, Bv, S, 0, 0, 0);
             }
         }
-        if (lane == 0) L.wflag[bf][wave] = moved ? 1 : 0;
-        _Float16 ph[2];
+        // ---- softmax of rows 4kg + j (head hw0 + 4kg + j), column n (token t0 + n)
+        const bool valid = t0 + n < p.T;
+        float x[4];
+        bool over = false;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const float pv = valid ? __builtin_amdgcn_exp2f(x[e] - mrun[e]) : 0.0f;
-            ph[e] = _Float16(pv);
-            lrun[e] += float(ph[e]);
+        for (int j = 0; j < 4; ++j) {
+            x[j] = valid ? (S[j] + (qrope ? rb[j] : 0.0f)) * p.sigma2 : -INFINITY;
+            over = over || x[j] > mrun[j] + TAU;
         }
-        // even tq writes tokens (tq, tq + 1) of head h0, odd tq those of h0 + 1
-        const uint32_t mine = __builtin_bit_cast(uint32_t, f16x2{ph[0], ph[1]});
-        const uint32_t other = uint32_t(__builtin_amdgcn_update_dpp(0, int(mine), 0xb1, 0xf, 0xf, false));
-        const bool odd = (tq & 1) != 0;
-        const uint32_t wv = odd ? __builtin_amdgcn_perm(mine, other, 0x07060302u)
-                                : __builtin_amdgcn_perm(other, mine, 0x05040100u);
-        L.pm[bf][(h0 + (odd ? 1 : 0)) * PS + (tq >> 1)] = wv;
+        const bool moved = __builtin_amdgcn_ballot_w64(over) != 0;
+        float a[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if (moved) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float mn = fmaxf(mrun[j], row_max16(x[j]));
+                a[j] = __builtin_amdgcn_exp2f(mrun[j] - mn);
+                mrun[j] = mn;
+                lrun[j] *= a[j];
+            }
+        }
+        if (n == 0) *reinterpret_cast<float4*>(L.alpha[t & 1] + hw0 + 4 * kg) = make_float4(a[0], a[1], a[2], a[3]);
+        if (lane == 0) L.wflag[t & 1][wave] = moved ? 1 : 0;
+        _Float16* pmh = reinterpret_cast<_Float16*>(L.pm[t & 1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const _Float16 ph = _Float16(valid ? __builtin_amdgcn_exp2f(x[j] - mrun[j]) : 0.0f);
+            lrun[j] += float(ph);
+            pmh[(hw0 + 4 * kg + j) * (2 * PS2) + n] = ph;
+        }
     };
 
-    // ---- stage 3 of tile i: rescale, O += P . (hi + lo)
-    auto pv_stage = [&](int i, const Frags& fr) {
-        const int bf = i & 1;
-        const int4 fa = *reinterpret_cast<const int4*>(L.wflag[bf]);
-        const int4 fb = *reinterpret_cast<const int4*>(L.wflag[bf] + 4);
-        if ((fa.x | fa.y | fa.z | fa.w | fb.x | fb.y | fb.z | fb.w) != 0) {
+    // ---- O *= alpha per head when some maximum moved at tile t (not on the
+    // run's first tile, where O is still zero).  Row e of block m is head
+    // 32m + 8(e >> 2) + 4h32 + (e & 3).  Each accumulator is scaled where it
+    // lives, in its accumulation register (read, multiply, write back), so
+    // that they stay there for the whole loop; the matrix instructions that
+    // last wrote them finished a barrier ago.
+    auto rescale = [&](int t) __attribute__((always_inline)) {
+        const int4 fl = *reinterpret_cast<const int4*>(L.wflag[t & 1]);
+        if (t > t_lo && (fl.x | fl.y | fl.z | fl.w) != 0) {
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    // row e of block m is head 32m + 8(e >> 2) + 4h32 + (e & 3),
-                    // whose softmax ran on wave 4m + (e >> 2)
-                    const int h = 32 * m + 8 * (e >> 2) + 4 * h32 + (e & 3);
-                    const int hw = 4 * m + (e >> 2);
-                    const int fl = hw == 0 ? fa.x : hw == 1 ? fa.y : hw == 2 ? fa.z : hw == 3 ? fa.w
-                                 : hw == 4 ? fb.x : hw == 5 ? fb.y : hw == 6 ? fb.z : fb.w;
-                    const float a = fl ? L.alpha[bf][h] : 1.0f;
-                    O[m][0][e] *= a;
-                    O[m][1][e] *= a;
+                    const float f = L.alpha[t & 1][32 * m + 8 * (e >> 2) + 4 * h32 + (e & 3)];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        float tmp;
+                        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                                     : "+a"(O[m][u][e]), "=&v"(tmp)
+                                     : "v"(f));
+                    }
                 }
+            // wait states between these writes and the matrix instructions
+            // that read the same registers next
+            asm volatile("s_nop 7");
         }
+    };
+
+    // ---- O += P . (hi + lo) for the 64 heads over the own channels, tile t
+    auto pv_mfma = [&](int t, const Frags& F) __attribute__((always_inline)) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const f16x8 A = as_f16x8(*reinterpret_cast<const uint4*>(L.pm[bf] + (32 * m + c32) * PS + 4 * h32));
+            const f16x8 A = as_f16x8(*reinterpret_cast<const uint4*>(L.pm[t & 1] + (32 * m + c32) * PS2 + 4 * h32));
 #pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                O[m][v] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    A, as_f16x8(fr.h[v][0], fr.h[v][1], fr.h[v][2], fr.h[v][3]), O[m][v], 0, 0, 0);
-                O[m][v] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    A, as_f16x8(fr.l[v][0], fr.l[v][1], fr.l[v][2], fr.l[v][3]), O[m][v], 0, 0, 0);
+            for (int u = 0; u < 4; ++u) {
+                O[m][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    A, as_f16x8(F.h[u][0], F.h[u][1], F.h[u][2], F.h[u][3]), O[m][u], 0, 0, 0);
+                O[m][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    A, as_f16x8(F.l[u][0], F.l[u][1], F.l[u][2], F.l[u][3]), O[m][u], 0, 0, 0);
             }
         }
     };
 
-    // step k: PV of tile t_lo + k - 2, softmax of t_lo + k - 1, front of
-    // t_lo + k; the operands of tile i live in F[(i - t_lo) & 1]
-    const int nt = t_hi - t_lo;
-    // Waves w and w + 4 share a SIMD; the second one runs its softmax before
-    // its PV so that the two overlap matrix and vector work.
-    const bool sm_first = wave >= 4;
-    for (int k = 0; k < nt + 2; k += 2) {
-        if (sm_first && k >= 1 && k - 1 < nt) softmax(t_lo + k - 1);
-        if (k >= 2) pv_stage(t_lo + k - 2, F[0]);
-        if (!sm_first && k >= 1 && k - 1 < nt) softmax(t_lo + k - 1);
-        if (k < nt) front(t_lo + k, F[0], cwq[0], swq[0]);
+    // ---- step k: PV of tile k - 1 (fragments Fc), QK^T of tile k and the
+    // dequant of tile k + 1 (into Fc: tiles k - 1 and k + 1 share a slot),
+    // then the softmax of tile k, the RoPE operands of tile k + 1, the staging
+    // of tile k + 2 (from Ps) and the loads of tile k + 4 (into Ps).  Past
+    // the run's last tile the dequant, staging and loads work on clamped
+    // (valid, unused) data, so every step has the same shape.
+    auto step = [&](int k, auto pv_on, Frags& Fc, Pre& Ps) __attribute__((always_inline)) {
+        if constexpr (decltype(pv_on)::value) {
+            rescale(k - 1);
+            pv_mfma(k - 1, Fc);
+        }
+        const f32x4 S = qk_content(k);
+        dequant(k + 1, Fc);
+        qk_rope_softmax(k, S);
+        const int64_t t1 = int64_t(k + 1) * 16;
+        if (k + 1 < t_hi && t1 / GR < p.nblk && t1 % GR == 0) fold(k + 1);
+        stage(k + 2, Ps);
+        load(k + 4, Ps);
         __syncthreads();
-        if (k + 1 >= nt + 2) break;
-        if (sm_first && k < nt) softmax(t_lo + k);
-        if (k >= 1) pv_stage(t_lo + k - 1, F[1]);
-        if (!sm_first && k < nt) softmax(t_lo + k);
-        if (k + 1 < nt) front(t_lo + k + 1, F[1], cwq[1], swq[1]);
-        __syncthreads();
+    };
+
+    // ---- prologue: tiles t_lo, t_lo + 1 staged, t_lo's RoPE operands and
+    // dequant; tiles t_lo + 2, + 3 in flight
+    Frags F0, F1;
+    Pre P0, P1;
+    load(t_lo, P0);
+    load(t_lo + 1, P1);
+    __syncthreads();   // L.qr
+    stage(t_lo, P0);
+    stage(t_lo + 1, P1);
+    load(t_lo + 2, P0);
+    load(t_lo + 3, P1);
+    __syncthreads();
+    if (int64_t(t_lo) * 16 / GR < p.nblk) fold(t_lo);
+    dequant(t_lo, F0);
+    __syncthreads();
+
+    // tile t's fragments sit in F0 when t - t_lo is even, else in F1
+    step(t_lo, std::false_type{}, F1, P0);
+    int k = t_lo + 1;
+    for (; k + 1 < t_hi; k += 2) {
+        step(k, std::true_type{}, F0, P1);
+        step(k + 1, std::true_type{}, F1, P0);
+    }
+    if (k < t_hi) {
+        step(k, std::true_type{}, F0, P1);
+        rescale(k);
+        pv_mfma(k, F1);
+    } else {
+        rescale(k - 1);
+        pv_mfma(k - 1, F0);
     }
 
     // ---- epilogue: running maxima and row sums, partial outputs
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const float l = row_sum16(lrun[e]);
-        if (tq == 0) {
-            const int64_t slot = (qrow0 + 8 * wave + 2 * hp + e) * p.S + s;
-            p.ws_ml[slot * 2] = mrun[e];
+    for (int j = 0; j < 4; ++j) {
+        const float l = row_sum16(lrun[j]);
+        if (n == 0) {
+            const int64_t slot = (qrow0 + hw0 + 4 * kg + j) * p.S + s;
+            p.ws_ml[slot * 2] = mrun[j];
             p.ws_ml[slot * 2 + 1] = l;
         }
     }
@@ -501,8 +545,8 @@ __global__ __launch_bounds__(512) void k_decode_mla(MlaParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int h = 32 * m + 8 * (e >> 2) + 4 * h32 + (e & 3);
-            *reinterpret_cast<float2*>(p.ws_acc + ((qrow0 + h) * p.S + s) * VD + ch0 + 2 * c32) =
-                make_float2(O[m][0][e], O[m][1][e]);
+            *reinterpret_cast<float4*>(p.ws_acc + ((qrow0 + h) * p.S + s) * VD + ch0 + 4 * c32) =
+                make_float4(O[m][0][e], O[m][1][e], O[m][2][e], O[m][3][e]);
         }
 }
 
@@ -537,11 +581,11 @@ hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st) {
     p.nblk_cap = a.g.nblk_cap;
     p.sigma2 = a.sigma * 1.4426950408889634f;
     p.neg1 = -1.0f;
-    const dim3 grid(a.S, a.g.B, a.Hq / HQ);
+    const dim3 grid(a.S, a.g.B, a.Hq / HW);
     if (c.cfg.value.bits == 4)
-        hipExtLaunchKernelGGL(k_decode_mla<4>, grid, dim3(64 * NW), 0, st, a.ev_start, a.ev_stop, 0, p);
+        hipExtLaunchKernelGGL(k_decode_mla<4>, grid, dim3(64 * NW4), 0, st, a.ev_start, a.ev_stop, 0, p);
     else
-        hipExtLaunchKernelGGL(k_decode_mla<2>, grid, dim3(64 * NW), 0, st, a.ev_start, a.ev_stop, 0, p);
+        hipExtLaunchKernelGGL(k_decode_mla<2>, grid, dim3(64 * NW4), 0, st, a.ev_start, a.ev_stop, 0, p);
     return hipGetLastError();
 }
 

@@ -489,3 +489,39 @@ def test_mla_int4_full_size(orc):
     log(f"[mla int4] max|err| {worst:.3e} mean excess {excess:.2e} max|o| {np.abs(ref).max():.3f}")
     assert worst <= TOL
     assert excess <= MEAN_EXCESS_TOL
+
+
+def _rising_keys(w, k_u16, q_u16, rate):
+    """Keys whose logits climb by about `rate` (natural units) per token for
+    the mean query of each KV head's group, so that the kernels' running
+    maxima move over and over after the first tile (and the accumulators get
+    rescaled mid-run); the values are untouched."""
+    k = k_u16.view(np.float16).astype(np.float64)
+    q = q_u16.view(np.float16).astype(np.float64)
+    g = w.n_q_heads // w.n_kv_heads
+    qk = q[..., -w.kd:]   # the part of q that meets the keys: all of it (KIVI), q_r (MLA)
+    ramp = np.arange(k.shape[2], dtype=np.float64)[:, None]
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            rows = qk[b, h * g:(h + 1) * g]
+            d = rows.mean(axis=0)
+            d /= np.linalg.norm(d)
+            a = rate / (w.sigma * np.abs(rows @ d).mean())
+            k[b, h] += a * ramp * d[None, :]
+    return k.astype(np.float16).view(np.uint16)
+
+
+@pytest.mark.parametrize("n_splits", [0, 1])
+@pytest.mark.parametrize("shape", ["mha128_g32", "mha128_g64", "gqa4_g64", "gqa4", "gqa4_4bit_g64", "mla64",
+                                   "mla128", "mla4_128"])
+def test_rising_logits(orc, shape, n_splits):
+    """Maxima that keep moving: every lazy rescale path against the oracle."""
+    T = 700
+    w = _tiny(T, Hq=8, Hkv=2, D=128) if shape == "gqa4" else _shape(shape, T)
+    cap = w.capacity(16)
+    k = _rising_keys(w, synth.keys(w), synth.query(w), 0.5)
+    v = synth.values(w)
+    dc = new_cache(w, cap)
+    dc.append(dev_f16(k), dev_f16(v))
+    log(f"[rising {shape}] variant {dc.variant(w.n_q_heads)}, splits {n_splits}")
+    _check_decode(orc, w, dc, k, v, n_splits=n_splits)
