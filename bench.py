@@ -109,6 +109,25 @@ def profiled_traffic(variant: str, workload: str):
     return int(rec["traffic_bytes"])
 
 
+def profiled_counters(variant: str, workload: str):
+    """The dominant kernel's rocprofv3 counters (MfmaUtil, VALUBusy, SALUBusy,
+    LDSBankConflict in percent, profiles/counters.json), or None when no
+    measurement exists or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{variant}/{workload}")
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in rec["source"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest()[:16] != rec["sha256_16"]:
+        return None
+    return {k: rec[k] for k in ("MfmaUtil", "VALUBusy", "SALUBusy", "LDSBankConflict", "profile")}
+
+
 def gpu_clock_state():
     """Current shader / memory / fabric clock levels of the first AMD GPU, as
     the driver's sysfs files mark them ('*'); plain file reads, so no child
@@ -344,6 +363,7 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
                     "traffic": profiled_traffic(variant, w.name),
+                    "counters": profiled_counters(variant, w.name),
                     "kernel": "decode pass-1 (" + variant + ")", "avg_us": round(p1_avg * 1e3, 2),
                     "alg_flops_per_launch": int(p1_flops), "alg_bytes_per_launch": int(p1_bytes),
                     "hbm_GBps": round(achieved, 2)}
@@ -351,6 +371,7 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": profiled_traffic(variant, w.name),
+                    "counters": profiled_counters(variant, w.name),
                     "kernel": "decode pass-1 (" + variant + ")", "avg_us": round(p1_avg * 1e3, 2),
                     "alg_bytes_per_launch": int(p1_bytes)}
     res = {
@@ -537,6 +558,7 @@ def main_paged(args, w, dev):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": profiled_traffic(variant, w.name + "_paged_ragged"),
+                     "counters": profiled_counters(variant, w.name + "_paged_ragged"),
                      "kernel": "decode pass-1 (" + variant + ")", "avg_us": round(p1_avg * 1e3, 2),
                      "alg_bytes_per_launch": int(p1_bytes)},
         "extra": {
@@ -649,7 +671,8 @@ def main_prefill(args, w, dev):
                    "head_dim": w.kd, "prompt_tokens": w.T, "G": w.kG, "bits": w.kbits, "value_group": w.vG,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": profiled_traffic("prefill", w.name), "counters": profiled_counters("prefill", w.name),
                      "kernel": "k_prefill (one launch per step)", "avg_us": round(ms * 1e3, 2),
                      "alg_flops_per_launch": int(flops)},
         "extra": {
