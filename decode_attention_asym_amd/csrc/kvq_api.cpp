@@ -124,8 +124,9 @@ kvq_status decode_workspace_now(const kvq_cache& c, int Hq, int n_splits, uint64
 
 extern "C" {
 
-const char* kvq_status_str(kvq_status s) {
-    switch (s) {
+const char* kvq_status_str(int32_t status) {
+    // an int, not the enum: any value a caller passes is defined behaviour
+    switch (status) {
         case KVQ_OK: return "ok";
         case KVQ_E_NULL: return "null pointer";
         case KVQ_E_SHAPE: return "bad shape";

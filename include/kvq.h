@@ -372,8 +372,9 @@ kvq_status kv_set_timing_events(void* ev_before, void* ev_after);
 /* Name of the decode kernel variant kv_decode_attention would launch. */
 const char* kv_decode_variant(const kvq_cache* cache, int32_t n_q_heads);
 
-/* Static description of a status code. */
-const char* kvq_status_str(kvq_status status);
+/* Static description of a status code (any int: values that are no
+ * kvq_status give "unknown status"). */
+const char* kvq_status_str(int32_t status);
 
 #ifdef __cplusplus
 }

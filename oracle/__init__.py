@@ -18,18 +18,32 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
-_LIB = os.path.join(_HERE, "libkvq_oracle.so")
+# KVQ_ORACLE_LIB selects another build (the sanitizer build below)
+_LIB = os.environ.get("KVQ_ORACLE_LIB") or os.path.join(_HERE, "libkvq_oracle.so")
 _CFLAGS = ["-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared",
            "-ffp-contract=off", "-fno-fast-math", "-pthread"]
+SAN_LIB = os.path.join(_HERE, "libkvq_oracle_san.so")
 
 
 def build() -> str:
     """Compile the oracle with gcc (always recompiles)."""
-    tmp = _LIB + ".tmp"
+    lib_path = os.path.join(_HERE, "libkvq_oracle.so")
+    tmp = lib_path + ".tmp"
     cmd = ["gcc", *_CFLAGS, _SRC, "-lm", "-o", tmp]
     subprocess.run(cmd, check=True, cwd=_HERE)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+def build_sanitized(clang: str) -> str:
+    """The oracle under AddressSanitizer and UndefinedBehaviorSanitizer, built
+    with `clang` (the one whose ASan runtime gets preloaded)."""
+    tmp = SAN_LIB + ".tmp"
+    cmd = [clang, *[f for f in _CFLAGS if f != "-O2"], "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-shared-libsan", _SRC, "-lm", "-o", tmp]
+    subprocess.run(cmd, check=True, cwd=_HERE)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
 
 
 _lib = None
