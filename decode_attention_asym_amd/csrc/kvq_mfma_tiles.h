@@ -734,11 +734,24 @@ __device__ __forceinline__ int value_row_dw(int ksx, int P, int kg, int n) {
 // the K index runs over e in the quad order 0, 2, 1, 3; the A operands (q',
 // p') are laid out in the same order.  Results carry a factor
 // 2^-(24 - f): code_unscale2 / code_unscale4 undo it.
+// The shifts run on the 8 bytes as one 64-bit word: v_lshlrev_b64 /
+// v_lshrrev_b64 issue at the rate of 32-bit shifts on gfx950 (an in-bounds
+// probe timed 8 of each per loop at the same 1.27 ms), so four of them
+// replace eight.  The bits that cross between the two words land at bits
+// 0..5 or 10..15 of a half, outside every field.  The shift counts come from
+// opaque scalar registers: with constant counts the compiler splits each
+// 64-bit shift into two 32-bit ones.
 struct CodeRegs {
     uint32_t a[4], b[4];
 };
 __device__ __forceinline__ CodeRegs code_operands(uint2 r) {
-    return CodeRegs{{r.x << 6, r.x >> 2, r.y << 6, r.y >> 2}, {r.x << 2, r.x >> 6, r.y << 2, r.y >> 6}};
+    const uint64_t w = (uint64_t(r.y) << 32) | r.x;
+    uint32_t s2, s6;
+    asm("s_mov_b32 %0, 2" : "=s"(s2));
+    asm("s_mov_b32 %0, 6" : "=s"(s6));
+    const uint64_t l6 = w << s6, r2 = w >> s2, l2 = w << s2, r6 = w >> s6;
+    return CodeRegs{{uint32_t(l6), uint32_t(r2), uint32_t(l6 >> 32), uint32_t(r2 >> 32)},
+                    {uint32_t(l2), uint32_t(r6), uint32_t(l2 >> 32), uint32_t(r6 >> 32)}};
 }
 // 2-bit code position u (0..3) of every byte; `lanes_mk` variant: the set
 // (u >> 1) is uniform and the field (u & 1) may differ per lane
