@@ -332,9 +332,9 @@ __global__ __launch_bounds__(128) void k_decode_gqa(MfmaParams p) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 15, kg = lane >> 4;
     const int hh = lane >> 4, chunk = lane & 15;
-    const int kvh = blockIdx.y, b = blockIdx.z;
+    int b, kvh;
     bool tail;
-    const int s = slot_of_block(p, tail);
+    const int s = block_coords<!PAGED>(p, b, kvh, tail);
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int hq0 = kvh * HG;
     // a paged sequence has its own length; main split s takes tiles
@@ -704,9 +704,9 @@ __global__ __launch_bounds__(128) void k_decode_gqa4(MfmaParams p) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 15, kg = lane >> 4;
     const int hh = lane >> 4, chunk = lane & 15;
-    const int kvh = blockIdx.y, b = blockIdx.z;
+    int b, kvh;
     bool tail;
-    const int s = slot_of_block(p, tail);
+    const int s = block_coords<!PAGED>(p, b, kvh, tail);
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int hq0 = kvh * HG;
     int t_lo, t_hi;
@@ -842,7 +842,7 @@ bool gqa_cfg_supported(const kvq_cache_cfg& c, int Hq) {
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
     const MfmaParams p = mfma_params(a);
-    const dim3 grid(a.S, a.g.Hkv, a.g.B);
+    const dim3 grid = decode_grid<true>(a.S, a.g.Hkv, a.g.B);
     if (a.g.kbits == 4) {
         if (a.g.kG == 64)
             hipExtLaunchKernelGGL((k_decode_gqa4<64, false>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
@@ -859,7 +859,7 @@ hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
 
 hipError_t launch_decode_gqa_paged(const DecodeArgs& a, hipStream_t st) {
     const MfmaParams p = mfma_params(a);
-    const dim3 grid(a.S, a.g.Hkv, a.g.B);
+    const dim3 grid = decode_grid<false>(a.S, a.g.Hkv, a.g.B);
     if (a.g.kbits == 4) {
         if (a.g.kG == 64)
             hipExtLaunchKernelGGL((k_decode_gqa4<64, true>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);

@@ -240,9 +240,9 @@ __global__ __launch_bounds__(128) void k_decode_mha(MfmaParams p) {
     __shared__ Lds L;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 15, kg = lane >> 4;
-    const int kvh = blockIdx.y, b = blockIdx.z;
+    int b, kvh;
     bool tail;
-    const int s = slot_of_block(p, tail);
+    const int s = block_coords<false>(p, b, kvh, tail);
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int64_t slot = (int64_t(b) * p.Hq + kvh) * p.S + s;
     // paged: the sequence's own length, fixed-size splits (as in the GQA kernel)
@@ -527,9 +527,9 @@ __global__ __launch_bounds__(128) void k_decode_mha4(MfmaParams p) {
     __shared__ Lds4 L;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n = lane & 15, kg = lane >> 4;
-    const int kvh = blockIdx.y, b = blockIdx.z;
+    int b, kvh;
     bool tail;
-    const int s = slot_of_block(p, tail);
+    const int s = block_coords<false>(p, b, kvh, tail);
     const int64_t bh = int64_t(b) * p.Hkv + kvh;
     const int64_t slot = (int64_t(b) * p.Hq + kvh) * p.S + s;
     int t_lo, t_hi;
@@ -646,7 +646,7 @@ bool mha_supported(const kvq_cache& c, int Hq) {
 
 hipError_t launch_decode_mha(const DecodeArgs& a, hipStream_t st) {
     const MfmaParams p = mfma_params(a);
-    const dim3 grid(a.S, a.g.Hkv, a.g.B);
+    const dim3 grid = decode_grid<false>(a.S, a.g.Hkv, a.g.B);
     if (a.g.kbits == 4) {
         if (a.g.kG == 64)
             hipExtLaunchKernelGGL((k_decode_mha4<64, false>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
@@ -665,7 +665,7 @@ bool mha_cfg_supported(const kvq_cache_cfg& c, int Hq) { return (mfma_cfg_ok(c) 
 
 hipError_t launch_decode_mha_paged(const DecodeArgs& a, hipStream_t st) {
     const MfmaParams p = mfma_params(a);
-    const dim3 grid(a.S, a.g.Hkv, a.g.B);
+    const dim3 grid = decode_grid<false>(a.S, a.g.Hkv, a.g.B);
     if (a.g.kbits == 4) {
         if (a.g.kG == 64)
             hipExtLaunchKernelGGL((k_decode_mha4<64, true>), grid, dim3(128), 0, st, a.ev_start, a.ev_stop, 0, p);
