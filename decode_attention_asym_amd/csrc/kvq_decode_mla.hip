@@ -199,16 +199,30 @@ void k_decode_mla(MlaParams p) {
 
     // ---- q_r of the 64 heads to LDS; the own heads' content rows as A
     // operands: QA[ks] = channels 32ks + 8kg .. + 7 of head hw0 + n
-    for (int i = tid; i < HW * 32; i += 256)
-        L.qr[(i >> 5) * QRS + (i & 31)] = reinterpret_cast<const uint32_t*>(p.q + (qrow0 + (i >> 5)) * QD + VD)[i & 31];
+    // (8 dwords per thread, all loads issued before the first store)
+    static_assert(HW * 32 % 256 == 0, "q_r dwords per thread");
+    uint32_t qrv[HW * 32 / 256];
+#pragma unroll
+    for (int j = 0; j < HW * 32 / 256; ++j) {
+        const int i = tid + 256 * j;
+        qrv[j] = reinterpret_cast<const uint32_t*>(p.q + (qrow0 + (i >> 5)) * QD + VD)[i & 31];
+    }
+#pragma unroll
+    for (int j = 0; j < HW * 32 / 256; ++j) {
+        const int i = tid + 256 * j;
+        L.qr[(i >> 5) * QRS + (i & 31)] = qrv[j];
+    }
     // (kept in accumulation registers, which the matrix instructions read
     // directly: the vector registers hold the dequantized latent)
+    // All 16 loads are issued before the first register constraint: with
+    // the constraint next to each load, every load waited for the previous
+    // one (16 memory latencies in a row at the start of each workgroup).
     f16x8 QA[16];
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
+    for (int ks = 0; ks < 16; ++ks)
         QA[ks] = as_f16x8(*reinterpret_cast<const uint4*>(p.q + (qrow0 + hw0 + n) * QD + 32 * ks + 8 * kg));
-        asm volatile("" : "+a"(QA[ks]));
-    }
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+a"(QA[ks]));
 
     f32x16 O[2][4];   // [32-head row block m][channel block u]
 #pragma unroll
