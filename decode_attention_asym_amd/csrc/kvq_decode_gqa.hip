@@ -25,13 +25,16 @@
 //    sum_c q_c z_c is a per-(head, block) bias computed on the VALU.
 //  * values: vhat = code * s + z with s, z per (token, 32-channel group).
 //    The scale is folded into the softmax weights (p' = p * s) as hi/lo
-//    rows; sum_t p_t z_t per (head, group) is accumulated on the VALU.
+//    rows; sum_t p_t z_t per (head, group) and sum_t p_t come from two more
+//    MFMAs per tile over the weights' hi/lo rows.
 //  * online softmax in log2 units; the running maximum only moves when a
 //    tile exceeds it by more than 2^8 (weights stay <= 256, fp16-safe).
 // One two-wave workgroup handles one contiguous run of 64-token tiles of one
 // (sequence, KV head); the global loads of later tiles overlap the current
 // tile.  The keys of a trailing partial tile and the residual are
-// handled by one extra workgroup per (sequence, KV head) on the VALU.
+// handled by one extra workgroup per (sequence, KV head) on the VALU.  Over a
+// contiguous cache the grid is split-major (block_coords in
+// kvq_mfma_tiles.h).
 #include "kvq_mfma_tiles.h"
 
 namespace kvq {
