@@ -31,8 +31,7 @@ SOURCES = {
     "kvq_decode_generic.hip": VGPR_FORM,
     "kvq_decode_gqa.hip": VGPR_FORM,
     "kvq_decode_mha.hip": VGPR_FORM,
-    # MLA: its accumulators live in the accumulation registers
-    "kvq_decode_mla.hip": [],
+    "kvq_decode_mla.hip": VGPR_FORM,
     "kvq_prefill.hip": VGPR_FORM,
     "kvq_noalloc.hip": [],
 }

@@ -27,26 +27,31 @@
 //    fp16 weights whose row sums add up the same fp16 values;
 //  * PV: O += P . (hi + lo) on v_mfma_f32_32x32x16_f16.
 //
-// Work split.  One workgroup of four waves, one per SIMD, takes 64 query
-// heads of one sequence over a run of 16-token tiles (128 heads take two
-// workgroups).  One wave per SIMD gets 512 registers: the 64 x 128 PV
-// accumulators of a wave and its 16 heads' content query rows (the QK^T A
-// operands, which the matrix instructions read there directly) sit in its
-// accumulation registers, the dequantized latent of two tiles in its vector
-// registers.
-//  * QK^T and the softmax by heads: wave w owns heads [16w, 16w + 16) of the
-//    workgroup over the whole 576-wide contraction; the tile's hi latent is
-//    read token-major from LDS as the B operand.  A logit needs no sum
-//    across waves.
-//  * PV by latent channels: wave w owns channels [128w, 128w + 128), which it
-//    dequantized itself, for the workgroup's 64 heads (the weights read from
-//    LDS as A operands).  Column j of channel block u is channel
-//    128w + 4j + u: a lane's four channels are the four codes of one 2-bit
-//    code byte.
-// Software pipeline, one workgroup barrier per tile: step k runs PV of tile
-// k - 1, QK^T of tile k and the dequant of tile k + 1, then the softmax of
-// tile k, the RoPE operands of tile k + 1's block, the staging of tile k + 2
-// into LDS and the global loads of tile k + 4.
+// Work split.  One workgroup of twelve waves (three per SIMD, 168 vector
+// registers each) takes 64 query heads of one sequence over a run of 16-token
+// tiles (128 heads take two workgroups).  The waves have two roles:
+//  * waves 0..7 dequantize and run PV by latent channels: wave v owns
+//    channels [64v, 64v + 64) for the workgroup's 64 heads.  Its lanes
+//    dequantize those channels of the tile (hi and lo stay in its registers
+//    as the PV B operands, hi is also written token-major to LDS) and read
+//    the weights from LDS as A operands.  Column j of channel block u is
+//    channel 64v + 2j + u, so a lane's two channels share one code byte;
+//  * waves 8..11 run QK^T and the softmax by heads: wave w owns heads
+//    [16w, 16w + 16) over the whole 576-wide contraction, its content query
+//    rows in registers as A operands, the tile's hi latent read from LDS as
+//    the B operand.  A logit needs no sum across waves.  They issue at a
+//    raised priority: their chain (LDS reads, QK^T, softmax, weights to LDS)
+//    sets the pace of a step, and the dequant and PV waves fill the gaps.
+//    Measured on MI355X, B64 x 128 heads x 16K tokens: 612-618 us per launch
+//    against 849-855 us for a four-wave kernel in which every wave did both
+//    roles (one wave per SIMD, no other wave to hide its latencies), and
+//    630-650 us without the raised priority.
+// Software pipeline, one workgroup barrier per tile: in step k the dequant
+// waves run PV of tile k - 1 (weights written in step k - 1), the dequant of
+// tile k + 1, the staging of their codes of tile k + 2 and the loads of tile
+// k + 4; the softmax waves run QK^T and the softmax of tile k (hi written in
+// step k - 1), the RoPE operands of tile k + 1's block, the staging of tile
+// k + 2's RoPE record and its loads of tile k + 4.
 #include <hip/hip_fp16.h>
 #include <math.h>
 
@@ -116,10 +121,6 @@ __device__ __forceinline__ float row_sum16(float x) {
     x += dpp<0x141>(x);
     return x + dpp<0x140>(x);
 }
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
 // byte k of `lo_word` -> byte 0, of `hi_word` -> byte 2, bytes 1 and 3 zero
 __device__ __forceinline__ uint32_t byte_pair_sel(int k) {
     return uint32_t(k) | (0x0cu << 8) | ((4u + uint32_t(k)) << 16) | (0x0cu << 24);
@@ -141,55 +142,51 @@ __device__ __forceinline__ void dequant_pair(uint32_t h, uint32_t bias2, uint32_
 }
 
 constexpr int HW = 64;      // query heads per workgroup
-constexpr int NW4 = 4;      // waves per workgroup
-constexpr int CHS = 260;    // dwords per token row of a hi tile (512 fp16 + pad)
+constexpr int CHS = 264;    // dwords per token row of a hi tile (512 fp16 + pad)
 constexpr int PS2 = 12;     // dwords per head row of P (16 fp16 + pad)
 constexpr int RRS = 512;    // dwords per staged RoPE record
 
-struct Lds4w {
+constexpr int NVW = 8;      // dequant + PV waves (64 latent channels each)
+constexpr int NQW = 4;      // QK^T + softmax waves (16 heads each)
+
+// What the PV waves touch comes first, within 64 KB of the start (the reach
+// of an LDS instruction's immediate offset from one base register).
+struct LdsMla {
     __attribute__((aligned(16))) uint32_t ch[2][16 * CHS];       // hi latent [tile parity][token][512 fp16]
     __attribute__((aligned(16))) uint32_t pm[2][HW * PS2];       // weights fp16 [tile parity][head][16 tokens]
-    __attribute__((aligned(16))) uint32_t cst[2][NW4][16 * 16];  // per wave: content codes [parity][word][token]
-    __attribute__((aligned(16))) uint32_t sst[2][NW4][64];       // per wave: [parity][scale|zero][group][token pair]
+    __attribute__((aligned(16))) uint32_t cst[2][NVW][8 * 16];   // per PV wave: content codes [parity][word][token]
+    __attribute__((aligned(16))) uint32_t sst[2][NVW][32];       // per PV wave: [parity][scale|zero][group][token pair]
+    __attribute__((aligned(16))) float alpha[2][HW];             // rescale factors [tile parity][head]
+    __attribute__((aligned(16))) int wflag[2][NQW];              // softmax wave w moved some of its maxima
     // RoPE record of a tile [tile mod 4]: quantized block: codes [word][64
     // channels] (dwords 0..127), the block's scales and zeros (128..191);
     // residual block: the tile's 16 fp16 key rows (dwords 0..511)
     __attribute__((aligned(16))) uint32_t rr[4][RRS];
     __attribute__((aligned(16))) uint32_t qr[HW * QRS];          // q_r fp16 [head][64 + pad]
-    __attribute__((aligned(16))) uint4 qa[NW4][4][64];           // per lane: q' hi/lo A operands [kr][hl]
-    __attribute__((aligned(16))) float alpha[2][HW];             // rescale factors [tile parity][head]
-    __attribute__((aligned(16))) int wflag[2][NW4];              // wave w moved some of its maxima
+    __attribute__((aligned(16))) uint4 qa[NQW][4][64];           // per softmax-wave lane: q' hi/lo A operands [kr][hl]
 };
 
 struct Frags {
-    uint32_t h[4][4], l[4][4];   // [channel block u][token pair]
-};
-
-// One tile's global loads, two steps ahead of their staging into LDS.
-struct Pre {
-    uint4 cw;       // own content code words of token t0 + (lane >> 2)
-    uint32_t sw;    // content scale or zero pair of token t0 + (lane & 15)
-    uint2 rw;       // RoPE record dwords tid, tid + 256
+    uint32_t h[2][4], l[2][4];   // [channel block u][token pair]
 };
 
 template <int VB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * (NVW + NQW)) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void k_decode_mla(MlaParams p) {
-    constexpr int CW = 128 * VB / 32;   // own code words per token (8 or 16)
+    constexpr int CWv = 64 * VB / 32;   // own code words per token (4 or 8)
     constexpr int VWT = VD * VB / 32;   // code words per token
-    __shared__ Lds4w L;
+    __shared__ LdsMla L;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const bool vrole = wave < NVW;
     const int n = lane & 15, kg = lane >> 4;        // 16x16x32 operand layout
     const int c32 = lane & 31, h32 = lane >> 5;     // 32x32x16 operand layout
     const int s = blockIdx.x, b = blockIdx.y;
     const int t_lo = int(int64_t(s) * p.ntiles / p.S);
     const int t_hi = int(int64_t(s + 1) * p.ntiles / p.S);
     const int64_t qrow0 = int64_t(b) * p.Hq + HW * blockIdx.z;   // first query row of the workgroup
-    const int hw0 = 16 * wave;    // first own head (QK^T, softmax)
-    const int ch0 = 128 * wave;   // first own latent channel (PV)
     if (t_lo >= t_hi) {
-        // an empty run (the split plans make none): an empty partial
-        for (int i = tid; i < HW * VD; i += 256) p.ws_acc[((qrow0 + i / VD) * p.S + s) * VD + i % VD] = 0.0f;
+        for (int i = tid; i < HW * VD; i += 64 * (NVW + NQW))
+            p.ws_acc[((qrow0 + i / VD) * p.S + s) * VD + i % VD] = 0.0f;
         if (tid < HW) {
             p.ws_ml[((qrow0 + tid) * p.S + s) * 2] = -INFINITY;
             p.ws_ml[((qrow0 + tid) * p.S + s) * 2 + 1] = 0.0f;
@@ -197,371 +194,381 @@ void k_decode_mla(MlaParams p) {
         return;
     }
 
-    // ---- q_r of the 64 heads to LDS; the own heads' content rows as A
-    // operands: QA[ks] = channels 32ks + 8kg .. + 7 of head hw0 + n
-    // (8 dwords per thread, all loads issued before the first store)
-    static_assert(HW * 32 % 256 == 0, "q_r dwords per thread");
-    uint32_t qrv[HW * 32 / 256];
+    if (vrole) {
+        // ================= dequant + PV: latent channels [ch0, ch0 + 64)
+        const int vw = wave, ch0 = 64 * vw;
+        f32x16 O[2][2];   // [32-head row block m][channel block u]: column j is channel ch0 + 2j + u
 #pragma unroll
-    for (int j = 0; j < HW * 32 / 256; ++j) {
-        const int i = tid + 256 * j;
-        qrv[j] = reinterpret_cast<const uint32_t*>(p.q + (qrow0 + (i >> 5)) * QD + VD)[i & 31];
-    }
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int j = 0; j < HW * 32 / 256; ++j) {
-        const int i = tid + 256 * j;
-        L.qr[(i >> 5) * QRS + (i & 31)] = qrv[j];
-    }
-    // (kept in accumulation registers, which the matrix instructions read
-    // directly: the vector registers hold the dequantized latent)
-    // All 16 loads are issued before the first register constraint: with
-    // the constraint next to each load, every load waited for the previous
-    // one (16 memory latencies in a row at the start of each workgroup).
-    f16x8 QA[16];
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks)
-        QA[ks] = as_f16x8(*reinterpret_cast<const uint4*>(p.q + (qrow0 + hw0 + n) * QD + 32 * ks + 8 * kg));
+                for (int e = 0; e < 16; ++e) O[m][u][e] = 0.0f;
+        // lane (c32, h32) dequantizes channels ch0 + 2c32 + u of tokens
+        // 8h32 .. 8h32 + 7.  2 bits: own word c32 >> 3, byte (c32 & 7) >> 1,
+        // field 4(c32 & 1) + 2u; 4 bits: own word c32 >> 2, byte c32 & 3,
+        // field 4u
+        const int cword = VB == 2 ? c32 >> 3 : c32 >> 2;
+        const uint32_t csel = byte_pair_sel(VB == 2 ? (c32 & 7) >> 1 : c32 & 3);
+        const int f0 = VB == 2 ? 4 * (c32 & 1) : 0;
+        uint32_t mk[2], exx[2], bias2[2];
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+a"(QA[ks]));
-
-    f32x16 O[2][4];   // [32-head row block m][channel block u]
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) O[m][u][e] = 0.0f;
-    // softmax state of heads hw0 + 4kg + j, and this lane's token share of
-    // their row sums
-    float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, lrun[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4 rb = f32x4{0.f, 0.f, 0.f, 0.f};   // RoPE bias of the block, rows 4kg + j
-
-    // Dequant layout: lane (c32, h32) takes channels ch0 + 4c32 + u of tokens
-    // 8h32 .. 8h32 + 7.  2 bits: code u of byte c32 & 3 of own word c32 >> 2;
-    // 4 bits: nibble u & 1 of byte 2(c32 & 1) + (u >> 1) of own word c32 >> 1
-    const int cword = VB == 2 ? c32 >> 2 : c32 >> 1;
-    const uint32_t csel0 = byte_pair_sel(VB == 2 ? c32 & 3 : 2 * (c32 & 1));
-    const uint32_t csel1 = byte_pair_sel(VB == 2 ? c32 & 3 : 2 * (c32 & 1) + 1);
-    const uint32_t rsel = byte_pair_sel((n & 7) >> 1);   // RoPE: byte of the lane's token
-
-    // ---- global loads of tile t (clamped to the last tile: a load past the
-    // run reads valid memory and is never used).  Content: own words
-    // (CW / 4)(lane & 3) .. of token t0 + (lane >> 2); lane (sz, gp, tl)
-    // takes the scale (sz = 0) or zero pair of own groups 2gp, 2gp + 1 of
-    // token t0 + tl.  RoPE record dwords tid and tid + 256.
-    const uint32_t* vcb = p.vc + int64_t(b) * p.cap * VWT + CW * wave + (CW / 4) * (lane & 3);
-    const uint16_t* vsb = ((lane & 32) ? p.vz : p.vs) + int64_t(b) * p.cap * 16 + 4 * wave + 2 * ((lane >> 4) & 1);
-    auto load = [&](int t, Pre& P) __attribute__((always_inline)) {
-        t = t < p.ntiles ? t : p.ntiles - 1;
-        const int64_t t0 = int64_t(t) * 16;
-        const uint32_t* src = vcb + (t0 + (lane >> 2)) * VWT;
-        if (VB == 2) {
-            const uint2 w = *reinterpret_cast<const uint2*>(src);
-            P.cw = make_uint4(w.x, w.y, 0u, 0u);
-        } else {
-            P.cw = *reinterpret_cast<const uint4*>(src);
+        for (int u = 0; u < 2; ++u) {
+            const int f = f0 + (VB == 2 ? 2 : 4) * u;
+            const uint32_t m1 = (VB == 2 ? 3u : 15u) << f;
+            const uint32_t ex = uint32_t(25 - f) << 10;
+            mk[u] = m1 | (m1 << 16);
+            exx[u] = ex | (ex << 16);
+            bias2[u] = exx[u] | 0x80008000u;
         }
-        P.sw = *reinterpret_cast<const uint32_t*>(vsb + (t0 + (lane & 15)) * 16);
-        const int64_t blk = t0 / GR;
-        const uint32_t *ax, *ay;
-        if (blk < p.nblk) {
-            // codes: dword tid < 128 is word 2(t mod 4) + (tid >> 6) of
-            // channel tid & 63; dwords 128..191 the scales, then the zeros
-            const int64_t row = int64_t(b) * p.nblk_cap + blk;
-            const uint32_t* kc = p.kc + row * GR * 8;
-            ax = tid < 128 ? kc + (tid & 63) * 8 + 2 * (t & 3) + (tid >> 6)
-                 : tid < 192 ? reinterpret_cast<const uint32_t*>(((tid & 32) ? p.kz : p.ks) + row * KD) + (tid & 31)
-                             : kc;
-            ay = kc;
-        } else {
-            // the residual key rows t0 - 64 nblk .. + 15 (inside its 64 rows)
-            const uint32_t* kr = reinterpret_cast<const uint32_t*>(p.kr + (int64_t(b) * GR + (t0 - p.nblk * GR)) * KD);
-            ax = kr + tid;
-            ay = kr + tid + 256;
-        }
-        P.rw = make_uint2(*ax, *ay);
-    };
-    // ---- staging of tile t into LDS (content: wave-private; RoPE record:
-    // shared).  Tokens at or past T get scale and zero 0, so they dequantize
-    // to exact zeros.
-    auto stage = [&](int t, const Pre& P) __attribute__((always_inline)) {
-        uint32_t* cst = L.cst[t & 1][wave];
-        const int tk = lane >> 2, w0 = (CW / 4) * (lane & 3);
-        cst[w0 * 16 + tk] = P.cw.x;
-        cst[(w0 + 1) * 16 + tk] = P.cw.y;
-        if (VB == 4) {
-            cst[(w0 + 2) * 16 + tk] = P.cw.z;
-            cst[(w0 + 3) * 16 + tk] = P.cw.w;
-        }
-        const int sz = lane >> 5, gp = (lane >> 4) & 1, tl = lane & 15;
-        const uint32_t sw = int64_t(t) * 16 + tl < p.T ? P.sw : 0u;
-        // lane (sz, gp, tl) holds groups (2gp, 2gp + 1) of token tl; even tl
-        // writes group 2gp of tokens (tl, tl + 1), odd tl group 2gp + 1
-        const uint32_t other = uint32_t(__builtin_amdgcn_update_dpp(0, int(sw), 0xb1, 0xf, 0xf, false));
-        const bool odd = (tl & 1) != 0;
-        const uint32_t wv = odd ? __builtin_amdgcn_perm(sw, other, 0x07060302u)
-                                : __builtin_amdgcn_perm(other, sw, 0x05040100u);
-        L.sst[t & 1][wave][(sz * 4 + 2 * gp + (odd ? 1 : 0)) * 8 + (tl >> 1)] = wv;
-        L.rr[t & 3][tid] = P.rw.x;
-        L.rr[t & 3][tid + 256] = P.rw.y;
-    };
-
-    // ---- q' = q_r * s_k (hi/lo A operands, lane-private) and the bias of
-    // the own heads for the quantized block of tile t (record staged)
-    auto fold = [&](int t) __attribute__((always_inline)) {
-        const uint32_t* rec = L.rr[t & 3];
+        // loads: lane (token lane >> 2, words (CWv / 4)(lane & 3) ..) of the
+        // own code words; lane (sz = lane >> 5, tl = lane & 15) the scale
+        // (sz = 0) or zero pair of the own groups of token tl
+        const uint32_t* vcb = p.vc + int64_t(b) * p.cap * VWT + CWv * vw + (CWv / 4) * (lane & 3);
+        const uint16_t* vsb = ((lane & 32) ? p.vz : p.vs) + int64_t(b) * p.cap * 16 + 2 * vw;
+        struct PreV {
+            uint2 cw;
+            uint32_t sw;
+        };
+        // (a load past the run is clamped to the last tile: it reads valid
+        // memory and is never used)
+        auto load = [&](int t, PreV& P) __attribute__((always_inline)) {
+            t = t < p.ntiles ? t : p.ntiles - 1;
+            const int64_t t0 = int64_t(t) * 16;
+            const uint32_t* src = vcb + (t0 + (lane >> 2)) * VWT;
+            if (VB == 2) P.cw = make_uint2(*src, 0u);
+            else P.cw = *reinterpret_cast<const uint2*>(src);
+            P.sw = *reinterpret_cast<const uint32_t*>(vsb + (t0 + (lane & 15)) * 16);
+        };
+        // staging into the wave's own LDS slots; tokens at or past T get scale
+        // and zero 0, so they dequantize to exact zeros.  Lane (sz, tl) with
+        // even tl writes the first own group of tokens (tl, tl + 1), odd tl
+        // the second group of tokens (tl - 1, tl)
+        auto stage = [&](int t, const PreV& P) __attribute__((always_inline)) {
+            uint32_t* cst = L.cst[t & 1][vw];
+            const int tk = lane >> 2, wd = (CWv / 4) * (lane & 3);
+            cst[wd * 16 + tk] = P.cw.x;
+            if (VB == 4) cst[(wd + 1) * 16 + tk] = P.cw.y;
+            const int sz = lane >> 5, tl = lane & 15;
+            const uint32_t sw = int64_t(t) * 16 + tl < p.T ? P.sw : 0u;
+            const uint32_t other = uint32_t(__builtin_amdgcn_update_dpp(0, int(sw), 0xb1, 0xf, 0xf, false));
+            const bool odd = (tl & 1) != 0;
+            const uint32_t wv = odd ? __builtin_amdgcn_perm(sw, other, 0x07060302u)
+                                    : __builtin_amdgcn_perm(other, sw, 0x05040100u);
+            if ((lane & 16) == 0) L.sst[t & 1][vw][(sz * 2 + (odd ? 1 : 0)) * 8 + (tl >> 1)] = wv;
+        };
+        // dequant of tile t (codes staged): hi and lo of the own channels into
+        // F, hi token-major into the LDS tile that the softmax waves read
+        auto dequant = [&](int t, Frags& F) __attribute__((always_inline)) {
+            const uint32_t* cs = L.cst[t & 1][vw] + cword * 16 + 8 * h32;
+            const uint4 wa = *reinterpret_cast<const uint4*>(cs);
+            const uint4 wb = *reinterpret_cast<const uint4*>(cs + 4);
+            const uint32_t wt[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+            const uint32_t* sp = L.sst[t & 1][vw] + (c32 >> 4) * 8 + 4 * h32;
+            const uint4 sv = *reinterpret_cast<const uint4*>(sp);
+            const uint4 zv = *reinterpret_cast<const uint4*>(sp + 16);
+            const uint32_t sa[4] = {sv.x, sv.y, sv.z, sv.w}, za[4] = {zv.x, zv.y, zv.z, zv.w};
+            uint32_t* chb = L.ch[t & 1];
 #pragma unroll
-        for (int kr = 0; kr < 2; ++kr) {
-            const uint4 sv = *reinterpret_cast<const uint4*>(rec + 128 + 16 * kr + 4 * kg);
-            const uint4 zv = *reinterpret_cast<const uint4*>(rec + 160 + 16 * kr + 4 * kg);
-            const uint4 qv = *reinterpret_cast<const uint4*>(L.qr + (hw0 + n) * QRS + 16 * kr + 4 * kg);
-            const uint32_t sa[4] = {sv.x, sv.y, sv.z, sv.w};
-            const uint32_t qa[4] = {qv.x, qv.y, qv.z, qv.w};
-            uint32_t hi[4], lo[4];
+            for (int q2 = 0; q2 < 4; ++q2) {
+                // code bytes of tokens 8h32 + 2q2 (low half) and + 1 (high half)
+                const uint32_t x = __builtin_amdgcn_perm(wt[2 * q2 + 1], wt[2 * q2], csel);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) split_prod2(lo_h(qa[e]), lo_h(sa[e]), hi_h(qa[e]), hi_h(sa[e]), hi[e], lo[e]);
-            L.qa[wave][kr * 2][lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            L.qa[wave][kr * 2 + 1][lane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-            // bias sum_c q_r z_k: every column of B holds the zeros
-            rb = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(qv), as_f16x8(zv), kr ? rb : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        }
-    };
-
-    // ---- dequant of tile t (codes staged): hi token-major into its LDS tile
-    // for QK^T, hi and lo of the own channels into F for PV
-    auto dequant = [&](int t, Frags& F) __attribute__((always_inline)) {
-        const uint32_t* cs = L.cst[t & 1][wave] + cword * 16 + 8 * h32;
-        const uint4 wa = *reinterpret_cast<const uint4*>(cs);
-        const uint4 wb = *reinterpret_cast<const uint4*>(cs + 4);
-        const uint32_t wt[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-        const uint32_t* sp = L.sst[t & 1][wave] + (c32 >> 3) * 8 + 4 * h32;
-        const uint4 sv = *reinterpret_cast<const uint4*>(sp);
-        const uint4 zv = *reinterpret_cast<const uint4*>(sp + 32);
-        const uint32_t sa[4] = {sv.x, sv.y, sv.z, sv.w}, za[4] = {zv.x, zv.y, zv.z, zv.w};
-        uint32_t* chb = L.ch[t & 1];
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-            // code bytes of tokens 8h32 + 2q2 (low half) and + 1 (high half)
-            const uint32_t x0 = __builtin_amdgcn_perm(wt[2 * q2 + 1], wt[2 * q2], csel0);
-            const uint32_t x1 = VB == 2 ? x0 : __builtin_amdgcn_perm(wt[2 * q2 + 1], wt[2 * q2], csel1);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                // field f of the code in its byte; (bits & mask) | exponent of
-                // 2^(10 - f) is the fp16 2^(10 - f) + code
-                const int f = VB == 2 ? 2 * u : 4 * (u & 1);
-                const uint32_t mk = (VB == 2 ? 0x00030003u : 0x000F000Fu) << f;
-                const uint32_t ex = uint32_t(25 - f) << 10;
-                const uint32_t x = (VB == 2 || u < 2) ? x0 : x1;
-                dequant_pair((x & mk) | ex | (ex << 16), ex | (ex << 16) | 0x80008000u, sa[q2], za[q2], p.neg1,
-                             F.h[u][q2], F.l[u][q2]);
+                for (int u = 0; u < 2; ++u)
+                    dequant_pair((x & mk[u]) | exx[u], bias2[u], sa[q2], za[q2], p.neg1, F.h[u][q2], F.l[u][q2]);
+                // hi, token-major: channels ch0 + 2c32, + 1 of the two tokens
+                uint32_t* row = chb + (8 * h32 + 2 * q2) * CHS + 32 * vw + c32;
+                row[0] = __builtin_amdgcn_perm(F.h[1][q2], F.h[0][q2], 0x05040100u);
+                row[CHS] = __builtin_amdgcn_perm(F.h[1][q2], F.h[0][q2], 0x07060302u);
             }
-            // hi, token-major: channels ch0 + 4c32 .. + 3 of the two tokens
-            uint32_t* row = chb + (8 * h32 + 2 * q2) * CHS + 64 * wave + 2 * c32;
-            *reinterpret_cast<uint2*>(row) = make_uint2(__builtin_amdgcn_perm(F.h[1][q2], F.h[0][q2], 0x05040100u),
-                                                        __builtin_amdgcn_perm(F.h[3][q2], F.h[2][q2], 0x05040100u));
-            *reinterpret_cast<uint2*>(row + CHS) =
-                make_uint2(__builtin_amdgcn_perm(F.h[1][q2], F.h[0][q2], 0x07060302u),
-                           __builtin_amdgcn_perm(F.h[3][q2], F.h[2][q2], 0x07060302u));
-        }
-    };
-
-    // ---- content part of the logits of the own 16 heads over tile t
-    auto qk_content = [&](int t) __attribute__((always_inline)) {
-        f32x4 S = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint32_t* chr = L.ch[t & 1] + n * CHS + 4 * kg;
-        // B operands requested in batches ahead of their products
-        constexpr int NB = 4;
+        };
+        // O *= alpha per head when some maximum moved at tile t (not on the
+        // run's first tile, where O is still zero).  Row e of block m is head
+        // 32m + 8(e >> 2) + 4h32 + (e & 3): four factors per LDS read, one
+        // group of rows at a time (the factors of all rows at once would not
+        // fit the register budget)
+        auto rescale = [&](int t) __attribute__((always_inline)) {
+            const int4 fl = *reinterpret_cast<const int4*>(L.wflag[t & 1]);
+            if (t > t_lo && (fl.x | fl.y | fl.z | fl.w) != 0) {
 #pragma unroll
-        for (int kb = 0; kb < 16; kb += NB) {
-            uint4 Bk[NB];
+                for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int j = 0; j < NB; ++j) Bk[j] = *reinterpret_cast<const uint4*>(chr + 16 * (kb + j));
+                    for (int g = 0; g < 4; ++g) {
+                        const float4 f = *reinterpret_cast<const float4*>(L.alpha[t & 1] + 32 * m + 8 * g + 4 * h32);
+                        const float fa[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
-            for (int j = 0; j < NB; ++j) S = __builtin_amdgcn_mfma_f32_16x16x32_f16(QA[kb + j], as_f16x8(Bk[j]), S, 0, 0, 0);
-        }
-        return S;
-    };
-
-    // ---- RoPE part of the logits over tile t, softmax, weights to LDS
-    auto qk_rope_softmax = [&](int t, f32x4 S) __attribute__((always_inline)) {
-        const int64_t t0 = int64_t(t) * 16;
-        const bool qrope = t0 / GR < p.nblk;
-        const uint32_t* rec = L.rr[t & 3];
-        if (qrope) {
-            // q' hi, lo against the codes as exact fp16 integers: channel c
-            // of token n is nibble n & 1 of byte (n & 7) >> 1 of word
-            // (n >> 3) of the tile's two
-            const bool hin = (n & 1) != 0;
-            const uint32_t nm = hin ? 0x00f000f0u : 0x000f000fu;
-            const uint32_t ne = hin ? 0x54005400u : 0x64006400u;   // 2^6 | 2^10 exponent pairs
-            const f16x2 nbias = __builtin_bit_cast(f16x2, hin ? 0xd400d400u : 0xe400e400u);
-            auto code2 = [&](uint32_t hw, uint32_t lw) __attribute__((always_inline)) {
-                const uint32_t xx = (__builtin_amdgcn_perm(hw, lw, rsel) & nm) | ne;
-                return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, xx) + nbias);
-            };
+                        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int kr = 0; kr < 2; ++kr) {
-                const uint32_t* src = rec + (n >> 3) * 64 + 32 * kr + 8 * kg;
-                const uint4 w0 = *reinterpret_cast<const uint4*>(src);
-                const uint4 w1 = *reinterpret_cast<const uint4*>(src + 4);
-                const f16x8 Bv = as_f16x8(code2(w0.y, w0.x), code2(w0.w, w0.z), code2(w1.y, w1.x), code2(w1.w, w1.z));
-                S = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(L.qa[wave][kr * 2][lane]), Bv, S, 0, 0, 0);
-                S = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(L.qa[wave][kr * 2 + 1][lane]), Bv, S, 0, 0, 0);
-            }
-        } else {
-            // q_r against the fp16 residual key rows of the record
-#pragma unroll
-            for (int kr = 0; kr < 2; ++kr) {
-                const f16x8 Bv = as_f16x8(*reinterpret_cast<const uint4*>(rec + n * 32 + 16 * kr + 4 * kg));
-                const f16x8 Aq = as_f16x8(*reinterpret_cast<const uint4*>(L.qr + (hw0 + n) * QRS + 16 * kr + 4 * kg));
-                S = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aq, Bv, S, 0, 0, 0);
-            }
-        }
-        // ---- softmax of rows 4kg + j (head hw0 + 4kg + j), column n (token t0 + n)
-        const bool valid = t0 + n < p.T;
-        float x[4];
-        bool over = false;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x[j] = valid ? (S[j] + (qrope ? rb[j] : 0.0f)) * p.sigma2 : -INFINITY;
-            over = over || x[j] > mrun[j] + TAU;
-        }
-        const bool moved = __builtin_amdgcn_ballot_w64(over) != 0;
-        float a[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-        if (moved) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float mn = fmaxf(mrun[j], row_max16(x[j]));
-                a[j] = __builtin_amdgcn_exp2f(mrun[j] - mn);
-                mrun[j] = mn;
-                lrun[j] *= a[j];
-            }
-        }
-        if (n == 0) *reinterpret_cast<float4*>(L.alpha[t & 1] + hw0 + 4 * kg) = make_float4(a[0], a[1], a[2], a[3]);
-        if (lane == 0) L.wflag[t & 1][wave] = moved ? 1 : 0;
-        _Float16* pmh = reinterpret_cast<_Float16*>(L.pm[t & 1]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const _Float16 ph = _Float16(valid ? __builtin_amdgcn_exp2f(x[j] - mrun[j]) : 0.0f);
-            lrun[j] += float(ph);
-            pmh[(hw0 + 4 * kg + j) * (2 * PS2) + n] = ph;
-        }
-    };
-
-    // ---- O *= alpha per head when some maximum moved at tile t (not on the
-    // run's first tile, where O is still zero).  Row e of block m is head
-    // 32m + 8(e >> 2) + 4h32 + (e & 3).  Each accumulator is scaled where it
-    // lives, in its accumulation register (read, multiply, write back), so
-    // that they stay there for the whole loop; the matrix instructions that
-    // last wrote them finished a barrier ago.
-    auto rescale = [&](int t) __attribute__((always_inline)) {
-        const int4 fl = *reinterpret_cast<const int4*>(L.wflag[t & 1]);
-        if (t > t_lo && (fl.x | fl.y | fl.z | fl.w) != 0) {
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float f = L.alpha[t & 1][32 * m + 8 * (e >> 2) + 4 * h32 + (e & 3)];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        float tmp;
-                        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                                     : "+a"(O[m][u][e]), "=&v"(tmp)
-                                     : "v"(f));
+                            for (int u = 0; u < 2; ++u) O[m][u][4 * g + i] *= fa[i];
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                }
-            // wait states between these writes and the matrix instructions
-            // that read the same registers next
-            asm volatile("s_nop 7");
-        }
-    };
-
-    // ---- O += P . (hi + lo) for the 64 heads over the own channels, tile t
-    auto pv_mfma = [&](int t, const Frags& F) __attribute__((always_inline)) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const f16x8 A = as_f16x8(*reinterpret_cast<const uint4*>(L.pm[t & 1] + (32 * m + c32) * PS2 + 4 * h32));
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                O[m][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    A, as_f16x8(F.h[u][0], F.h[u][1], F.h[u][2], F.h[u][3]), O[m][u], 0, 0, 0);
-                O[m][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    A, as_f16x8(F.l[u][0], F.l[u][1], F.l[u][2], F.l[u][3]), O[m][u], 0, 0, 0);
             }
+        };
+        // O += P . (hi + lo) for the 64 heads over the own channels, tile t
+        auto pv_mfma = [&](int t, const Frags& F) __attribute__((always_inline)) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const f16x8 A = as_f16x8(*reinterpret_cast<const uint4*>(L.pm[t & 1] + (32 * m + c32) * PS2 + 4 * h32));
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    O[m][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        A, as_f16x8(F.h[u][0], F.h[u][1], F.h[u][2], F.h[u][3]), O[m][u], 0, 0, 0);
+                    O[m][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        A, as_f16x8(F.l[u][0], F.l[u][1], F.l[u][2], F.l[u][3]), O[m][u], 0, 0, 0);
+                }
+            }
+        };
+        // step k: PV of tile k - 1 (weights written by the softmax waves in
+        // step k - 1), the dequant of tile k + 1 into the same slot, the
+        // staging of tile k + 2 and the loads of tile k + 4
+        auto step = [&](int k, auto pv_on, Frags& Fc, PreV& Ps) __attribute__((always_inline)) {
+            if constexpr (decltype(pv_on)::value) {
+                rescale(k - 1);
+                pv_mfma(k - 1, Fc);
+                // the slot's old fragments are dead once the products are issued
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            dequant(k + 1, Fc);
+            stage(k + 2, Ps);
+            load(k + 4, Ps);
+            __syncthreads();
+        };
+        // prologue: tiles t_lo, t_lo + 1 staged and t_lo dequantized; tiles
+        // t_lo + 2, + 3 in flight.  Tile t's fragments sit in F0 when t - t_lo
+        // is even, else in F1 (tiles k - 1 and k + 1 share a slot)
+        Frags F0, F1;
+        PreV P0, P1;
+        load(t_lo, P0);
+        load(t_lo + 1, P1);
+        __syncthreads();   // (1) L.qr
+        stage(t_lo, P0);
+        stage(t_lo + 1, P1);
+        load(t_lo + 2, P0);
+        load(t_lo + 3, P1);
+        __syncthreads();   // (2) staged
+        dequant(t_lo, F0);
+        __syncthreads();   // (3) hi of tile t_lo, q' of its block
+        step(t_lo, std::false_type{}, F1, P0);
+        int k = t_lo + 1;
+        for (; k + 1 < t_hi; k += 2) {
+            step(k, std::true_type{}, F0, P1);
+            step(k + 1, std::true_type{}, F1, P0);
         }
-    };
-
-    // ---- step k: PV of tile k - 1 (fragments Fc), QK^T of tile k and the
-    // dequant of tile k + 1 (into Fc: tiles k - 1 and k + 1 share a slot),
-    // then the softmax of tile k, the RoPE operands of tile k + 1, the staging
-    // of tile k + 2 (from Ps) and the loads of tile k + 4 (into Ps).  Past
-    // the run's last tile the dequant, staging and loads work on clamped
-    // (valid, unused) data, so every step has the same shape.
-    auto step = [&](int k, auto pv_on, Frags& Fc, Pre& Ps) __attribute__((always_inline)) {
-        if constexpr (decltype(pv_on)::value) {
-            rescale(k - 1);
-            pv_mfma(k - 1, Fc);
-        }
-        const f32x4 S = qk_content(k);
-        dequant(k + 1, Fc);
-        qk_rope_softmax(k, S);
-        const int64_t t1 = int64_t(k + 1) * 16;
-        if (k + 1 < t_hi && t1 / GR < p.nblk && t1 % GR == 0) fold(k + 1);
-        stage(k + 2, Ps);
-        load(k + 4, Ps);
-        __syncthreads();
-    };
-
-    // ---- prologue: tiles t_lo, t_lo + 1 staged, t_lo's RoPE operands and
-    // dequant; tiles t_lo + 2, + 3 in flight
-    Frags F0, F1;
-    Pre P0, P1;
-    load(t_lo, P0);
-    load(t_lo + 1, P1);
-    __syncthreads();   // L.qr
-    stage(t_lo, P0);
-    stage(t_lo + 1, P1);
-    load(t_lo + 2, P0);
-    load(t_lo + 3, P1);
-    __syncthreads();
-    if (int64_t(t_lo) * 16 / GR < p.nblk) fold(t_lo);
-    dequant(t_lo, F0);
-    __syncthreads();
-
-    // tile t's fragments sit in F0 when t - t_lo is even, else in F1
-    step(t_lo, std::false_type{}, F1, P0);
-    int k = t_lo + 1;
-    for (; k + 1 < t_hi; k += 2) {
-        step(k, std::true_type{}, F0, P1);
-        step(k + 1, std::true_type{}, F1, P0);
-    }
-    if (k < t_hi) {
-        step(k, std::true_type{}, F0, P1);
-        rescale(k);
-        pv_mfma(k, F1);
-    } else {
+        // PV of tile k - 1, and when tile k is the run's last, the last step:
+        // nothing past the run is dequantized, staged or loaded
         rescale(k - 1);
         pv_mfma(k - 1, F0);
-    }
-
-    // ---- epilogue: running maxima and row sums, partial outputs
+        if (k < t_hi) {
+            __syncthreads();
+            rescale(k);
+            pv_mfma(k, F1);
+        }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float l = row_sum16(lrun[j]);
-        if (n == 0) {
-            const int64_t slot = (qrow0 + hw0 + 4 * kg + j) * p.S + s;
-            p.ws_ml[slot * 2] = mrun[j];
-            p.ws_ml[slot * 2 + 1] = l;
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int h = 32 * m + 8 * (e >> 2) + 4 * h32 + (e & 3);
+                *reinterpret_cast<float2*>(p.ws_acc + ((qrow0 + h) * p.S + s) * VD + ch0 + 2 * c32) =
+                    make_float2(O[m][0][e], O[m][1][e]);
+            }
+    } else {
+        // ================= QK^T + softmax: heads [hw0, hw0 + 16)
+        const int qw = wave - NVW, rtid = tid - 64 * NVW;
+        // these waves set the pace of a step: they issue first
+        __builtin_amdgcn_s_setprio(2);
+        const int hw0 = 16 * qw;
+        const uint32_t rsel = byte_pair_sel((n & 7) >> 1);   // RoPE: byte of the lane's token
+        static_assert(HW * 32 % 256 == 0, "q_r dwords per thread");
+        uint32_t qrv[HW * 32 / 256];
+#pragma unroll
+        for (int j = 0; j < HW * 32 / 256; ++j) {
+            const int i = rtid + 256 * j;
+            qrv[j] = reinterpret_cast<const uint32_t*>(p.q + (qrow0 + (i >> 5)) * QD + VD)[i & 31];
+        }
+#pragma unroll
+        for (int j = 0; j < HW * 32 / 256; ++j) {
+            const int i = rtid + 256 * j;
+            L.qr[(i >> 5) * QRS + (i & 31)] = qrv[j];
+        }
+        // the own heads' content rows as A operands: QA[ks] = channels
+        // 32ks + 8kg .. + 7 of head hw0 + n
+        f16x8 QA[16];
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks)
+            QA[ks] = as_f16x8(*reinterpret_cast<const uint4*>(p.q + (qrow0 + hw0 + n) * QD + 32 * ks + 8 * kg));
+        float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, lrun[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 rb = f32x4{0.f, 0.f, 0.f, 0.f};   // RoPE bias of the block, rows 4kg + j
+        // loads of tile t's RoPE record, dwords rtid and rtid + 256 (clamped
+        // to the last tile like the content loads).  Quantized block: dword
+        // rtid < 128 is word 2(t mod 4) + (rtid >> 6) of channel rtid & 63,
+        // dwords 128..191 the scales, then the zeros; residual block: the
+        // key rows t0 - 64 nblk .. + 15
+        auto load = [&](int t, uint2& rw) __attribute__((always_inline)) {
+            t = t < p.ntiles ? t : p.ntiles - 1;
+            const int64_t t0 = int64_t(t) * 16;
+            const int64_t blk = t0 / GR;
+            const uint32_t *ax, *ay;
+            if (blk < p.nblk) {
+                const int64_t row = int64_t(b) * p.nblk_cap + blk;
+                const uint32_t* kc = p.kc + row * GR * 8;
+                ax = rtid < 128 ? kc + (rtid & 63) * 8 + 2 * (t & 3) + (rtid >> 6)
+                     : rtid < 192 ? reinterpret_cast<const uint32_t*>(((rtid & 32) ? p.kz : p.ks) + row * KD) + (rtid & 31)
+                                  : kc;
+                ay = kc;
+            } else {
+                const uint32_t* kr = reinterpret_cast<const uint32_t*>(p.kr + (int64_t(b) * GR + (t0 - p.nblk * GR)) * KD);
+                ax = kr + rtid;
+                ay = kr + rtid + 256;
+            }
+            rw = make_uint2(*ax, *ay);
+        };
+        auto stage = [&](int t, const uint2& rw) __attribute__((always_inline)) {
+            L.rr[t & 3][rtid] = rw.x;
+            L.rr[t & 3][rtid + 256] = rw.y;
+        };
+        // q' = q_r * s_k (hi/lo A operands, lane-private) and the bias of the
+        // own heads for the quantized block of tile t (record staged)
+        auto fold = [&](int t) __attribute__((always_inline)) {
+            const uint32_t* rec = L.rr[t & 3];
+#pragma unroll
+            for (int kr = 0; kr < 2; ++kr) {
+                const uint4 sv = *reinterpret_cast<const uint4*>(rec + 128 + 16 * kr + 4 * kg);
+                const uint4 zv = *reinterpret_cast<const uint4*>(rec + 160 + 16 * kr + 4 * kg);
+                const uint4 qv = *reinterpret_cast<const uint4*>(L.qr + (hw0 + n) * QRS + 16 * kr + 4 * kg);
+                const uint32_t sa[4] = {sv.x, sv.y, sv.z, sv.w};
+                const uint32_t qa[4] = {qv.x, qv.y, qv.z, qv.w};
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) split_prod2(lo_h(qa[e]), lo_h(sa[e]), hi_h(qa[e]), hi_h(sa[e]), hi[e], lo[e]);
+                L.qa[qw][kr * 2][lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                L.qa[qw][kr * 2 + 1][lane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                // bias sum_c q_r z_k: every column of B holds the zeros
+                rb = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(qv), as_f16x8(zv), kr ? rb : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            }
+        };
+        // content part of the logits of the own 16 heads over tile t, the B
+        // operands requested in batches ahead of their products
+        auto qk_content = [&](int t) __attribute__((always_inline)) {
+            f32x4 S = f32x4{0.f, 0.f, 0.f, 0.f};
+            const uint32_t* chr = L.ch[t & 1] + n * CHS + 4 * kg;
+            constexpr int NB = 4;
+#pragma unroll
+            for (int kb = 0; kb < 16; kb += NB) {
+                uint4 Bk[NB];
+#pragma unroll
+                for (int j = 0; j < NB; ++j) Bk[j] = *reinterpret_cast<const uint4*>(chr + 16 * (kb + j));
+#pragma unroll
+                for (int j = 0; j < NB; ++j) S = __builtin_amdgcn_mfma_f32_16x16x32_f16(QA[kb + j], as_f16x8(Bk[j]), S, 0, 0, 0);
+            }
+            return S;
+        };
+        // RoPE part of the logits over tile t, softmax, weights to LDS
+        auto qk_rope_softmax = [&](int t, f32x4 S) __attribute__((always_inline)) {
+            const int64_t t0 = int64_t(t) * 16;
+            const bool qrope = t0 / GR < p.nblk;
+            const uint32_t* rec = L.rr[t & 3];
+            if (qrope) {
+                // q' hi, lo against the codes as exact fp16 integers: channel c
+                // of token n is nibble n & 1 of byte (n & 7) >> 1 of word
+                // (n >> 3) of the tile's two
+                const bool hin = (n & 1) != 0;
+                const uint32_t nm = hin ? 0x00f000f0u : 0x000f000fu;
+                const uint32_t ne = hin ? 0x54005400u : 0x64006400u;
+                const f16x2 nbias = __builtin_bit_cast(f16x2, hin ? 0xd400d400u : 0xe400e400u);
+                auto code2 = [&](uint32_t hw, uint32_t lw) __attribute__((always_inline)) {
+                    const uint32_t xx = (__builtin_amdgcn_perm(hw, lw, rsel) & nm) | ne;
+                    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, xx) + nbias);
+                };
+#pragma unroll
+                for (int kr = 0; kr < 2; ++kr) {
+                    const uint32_t* src = rec + (n >> 3) * 64 + 32 * kr + 8 * kg;
+                    const uint4 w0 = *reinterpret_cast<const uint4*>(src);
+                    const uint4 w1 = *reinterpret_cast<const uint4*>(src + 4);
+                    const f16x8 Bv = as_f16x8(code2(w0.y, w0.x), code2(w0.w, w0.z), code2(w1.y, w1.x), code2(w1.w, w1.z));
+                    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(L.qa[qw][kr * 2][lane]), Bv, S, 0, 0, 0);
+                    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(L.qa[qw][kr * 2 + 1][lane]), Bv, S, 0, 0, 0);
+                }
+            } else {
+                // q_r against the fp16 residual key rows of the record
+#pragma unroll
+                for (int kr = 0; kr < 2; ++kr) {
+                    const f16x8 Bv = as_f16x8(*reinterpret_cast<const uint4*>(rec + n * 32 + 16 * kr + 4 * kg));
+                    const f16x8 Aq = as_f16x8(*reinterpret_cast<const uint4*>(L.qr + (hw0 + n) * QRS + 16 * kr + 4 * kg));
+                    S = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aq, Bv, S, 0, 0, 0);
+                }
+            }
+            // softmax of rows 4kg + j (head hw0 + 4kg + j), column n (token t0 + n)
+            const bool valid = t0 + n < p.T;
+            float x[4];
+            bool over = false;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[j] = valid ? (S[j] + (qrope ? rb[j] : 0.0f)) * p.sigma2 : -INFINITY;
+                over = over || x[j] > mrun[j] + TAU;
+            }
+            const bool moved = __builtin_amdgcn_ballot_w64(over) != 0;
+            float a[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+            if (moved) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float mn = fmaxf(mrun[j], row_max16(x[j]));
+                    a[j] = __builtin_amdgcn_exp2f(mrun[j] - mn);
+                    mrun[j] = mn;
+                    lrun[j] *= a[j];
+                }
+            }
+            if (n == 0) *reinterpret_cast<float4*>(L.alpha[t & 1] + hw0 + 4 * kg) = make_float4(a[0], a[1], a[2], a[3]);
+            if (lane == 0) L.wflag[t & 1][qw] = moved ? 1 : 0;
+            _Float16* pmh = reinterpret_cast<_Float16*>(L.pm[t & 1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const _Float16 ph = _Float16(valid ? __builtin_amdgcn_exp2f(x[j] - mrun[j]) : 0.0f);
+                lrun[j] += float(ph);
+                pmh[(hw0 + 4 * kg + j) * (2 * PS2) + n] = ph;
+            }
+        };
+        // step k: QK^T and softmax of tile k (its hi latent dequantized in
+        // step k - 1), the RoPE operands of tile k + 1's block, the staging
+        // of tile k + 2's RoPE record and the loads of tile k + 4's
+        auto step = [&](int k, uint2& Rs) __attribute__((always_inline)) {
+            const f32x4 S = qk_content(k);
+            qk_rope_softmax(k, S);
+            const int64_t t1 = int64_t(k + 1) * 16;
+            if (k + 1 < t_hi && t1 / GR < p.nblk && t1 % GR == 0) fold(k + 1);
+            stage(k + 2, Rs);
+            load(k + 4, Rs);
+            __syncthreads();
+        };
+        // prologue: records of tiles t_lo, t_lo + 1 staged, the RoPE operands
+        // of t_lo's block; tiles t_lo + 2, + 3 in flight
+        uint2 R0, R1;
+        load(t_lo, R0);
+        load(t_lo + 1, R1);
+        __syncthreads();   // (1) L.qr
+        stage(t_lo, R0);
+        stage(t_lo + 1, R1);
+        load(t_lo + 2, R0);
+        load(t_lo + 3, R1);
+        __syncthreads();   // (2) staged
+        if (int64_t(t_lo) * 16 / GR < p.nblk) fold(t_lo);
+        __syncthreads();   // (3)
+        step(t_lo, R0);
+        int k = t_lo + 1;
+        for (; k + 1 < t_hi; k += 2) {
+            step(k, R1);
+            step(k + 1, R0);
+        }
+        if (k < t_hi) step(k, R1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float l = row_sum16(lrun[j]);
+            if (n == 0) {
+                const int64_t slot = (qrow0 + hw0 + 4 * kg + j) * p.S + s;
+                p.ws_ml[slot * 2] = mrun[j];
+                p.ws_ml[slot * 2 + 1] = l;
+            }
         }
     }
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int h = 32 * m + 8 * (e >> 2) + 4 * h32 + (e & 3);
-            *reinterpret_cast<float4*>(p.ws_acc + ((qrow0 + h) * p.S + s) * VD + ch0 + 4 * c32) =
-                make_float4(O[m][0][e], O[m][1][e], O[m][2][e], O[m][3][e]);
-        }
 }
 
 }  // namespace
@@ -597,9 +604,9 @@ hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st) {
     p.neg1 = -1.0f;
     const dim3 grid(a.S, a.g.B, a.Hq / HW);
     if (c.cfg.value.bits == 4)
-        hipExtLaunchKernelGGL(k_decode_mla<4>, grid, dim3(64 * NW4), 0, st, a.ev_start, a.ev_stop, 0, p);
+        hipExtLaunchKernelGGL(k_decode_mla<4>, grid, dim3(64 * (NVW + NQW)), 0, st, a.ev_start, a.ev_stop, 0, p);
     else
-        hipExtLaunchKernelGGL(k_decode_mla<2>, grid, dim3(64 * NW4), 0, st, a.ev_start, a.ev_stop, 0, p);
+        hipExtLaunchKernelGGL(k_decode_mla<2>, grid, dim3(64 * (NVW + NQW)), 0, st, a.ev_start, a.ev_stop, 0, p);
     return hipGetLastError();
 }
 

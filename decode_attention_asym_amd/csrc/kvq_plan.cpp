@@ -59,7 +59,7 @@ bool runs_fit(const kvq_cache_cfg& cfg, int64_t ntiles, int64_t S_main) {
 namespace {
 
 int64_t auto_main(const kvq_cache& c, int Hq, Variant v, int64_t ntiles) {
-    // MLA: one four-wave workgroup per CU, Hq / 64 of them per sequence and split
+    // MLA: one twelve-wave workgroup per CU, Hq / 64 of them per sequence and split
     if (v == V_MLA) return clamp64((256 * 64 / Hq + c.cfg.batch - 1) / c.cfg.batch, 1, KVQ_MAX_SPLITS);
     const bool tiled = v == V_GQA || v == V_MHA;
     const int64_t units = tiled ? int64_t(c.cfg.batch) * c.cfg.n_kv_heads : int64_t(c.cfg.batch) * Hq;
