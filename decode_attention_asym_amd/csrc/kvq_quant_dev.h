@@ -54,6 +54,11 @@ __device__ __forceinline__ uint4 ld_once4(const uint16_t* p) {
 __device__ __forceinline__ uint32_t ld_once1(const uint16_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
 }
+typedef unsigned int qu2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ld_once2(const uint16_t* p) {
+    const qu2 v = __builtin_nontemporal_load(reinterpret_cast<const qu2*>(p));
+    return make_uint2(v.x, v.y);
+}
 
 // fl32(x - mn) for the fp16 half HALF of w, in one instruction: v_fma_mix
 // converts the fp16 operand exactly and rounds x * 1 + (-mn) once
@@ -263,31 +268,33 @@ template <> struct WordVec<8> {
     }
 };
 
+// A thread takes CPT = 2 or 4 adjacent channels (one 4- or 8-byte load per
+// row) of up to 32 rows of a block.
 template <int G, int BITS>
 struct KeyShape {
     static constexpr int PER = 32 / BITS;
     static constexpr int W = G / PER;            // words per (block, channel)
     static constexpr int TG = G < 32 ? G : 32;   // rows per thread
-    static constexpr int SPL = G / TG;           // threads per channel pair
-    static constexpr int CPW = 64 / SPL;         // channel pairs per wave (SPL > 1)
+    static constexpr int SPL = G / TG;           // threads per channel unit
+    static constexpr int CPW = 64 / SPL;         // channel units per wave (SPL > 1)
     static constexpr int WT = TG / PER;          // words per thread and channel
 };
 
 // Threads per (sequence, KV head, block).  With SPL > 1 a wave holds the SPL
 // row ranges of CPW channel pairs, so the count is rounded up to whole waves;
 // lanes past the last pair (kd / 2 < CPW) take part in the shuffles only.
-template <int G, int BITS>
+template <int G, int BITS, int CPT = 2>
 __host__ __device__ inline int64_t key_threads_per_block(int kd) {
     using S = KeyShape<G, BITS>;
-    const int tpb = kd / 2;
+    const int tpb = kd / CPT;
     return S::SPL == 1 ? tpb : int64_t((tpb + S::CPW - 1) / S::CPW) * 64;
 }
 
-// thread idx -> (block unit, channel pair, row range)
-template <int G, int BITS>
+// thread idx -> (block unit, channel unit, row range)
+template <int G, int BITS, int CPT = 2>
 __device__ __forceinline__ void key_thread_coords(int64_t idx, int kd, int64_t& unit, int& cp, int& sp) {
     using S = KeyShape<G, BITS>;
-    const int tpb = kd / 2;
+    const int tpb = kd / CPT;
     if (S::SPL == 1) {
         sp = 0;
         cp = int(idx % tpb);
@@ -314,74 +321,92 @@ struct KeyJob {
 
 // Where a key row comes from: the job's residual / input rows in global
 // memory (read once), or a tile staged in LDS.  pair(tok, cp) = channels
-// 2 cp, 2 cp + 1 of token tok.
+// 2 cp, 2 cp + 1 of token tok; quad(tok, cq) = channels 4 cq .. 4 cq + 3.
 struct GlobalKeySrc {
     const KeyJob& j;
     int kd;
-    __device__ uint32_t pair(int64_t tok, int cp) const {
-        const uint16_t* row = tok < j.in_tok0 ? j.resid + (tok - j.res_tok0) * kd : j.kin + (tok - j.in_tok0) * kd;
-        return ld_once1(row + 2 * cp);
+    __device__ const uint16_t* row(int64_t tok) const {
+        return tok < j.in_tok0 ? j.resid + (tok - j.res_tok0) * kd : j.kin + (tok - j.in_tok0) * kd;
     }
+    __device__ uint32_t pair(int64_t tok, int cp) const { return ld_once1(row(tok) + 2 * cp); }
+    __device__ uint2 quad(int64_t tok, int cq) const { return ld_once2(row(tok) + 4 * cq); }
 };
 
-template <int G, int BITS, class Src>
+template <int G, int BITS, int CPT = 2, class Src>
 __device__ __forceinline__ void quant_key_pair(const KeyJob& j, int kd, int cp, int sp,
                                                uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
                                                uint16_t* __restrict__ zero, const Src& src) {
 #pragma clang fp contract(off)
+    static_assert(CPT == 2 || CPT == 4, "two or four channels per thread");
     using S = KeyShape<G, BITS>;
+    constexpr int NP = CPT / 2;   // channel pairs per thread
     constexpr float L = float((1 << BITS) - 1);
-    const bool active = cp < kd / 2;
-    uint32_t raw[S::TG];
+    const bool active = cp < kd / CPT;
+    uint32_t raw[S::TG][NP];
 #pragma unroll
     for (int i = 0; i < S::TG; ++i) {
         const int64_t tok = j.blk_tok0 + sp * S::TG + i;
-        raw[i] = active ? src.pair(tok, cp) : 0u;
+        if constexpr (CPT == 2) {
+            raw[i][0] = active ? src.pair(tok, cp) : 0u;
+        } else {
+            const uint2 w = active ? src.quad(tok, cp) : make_uint2(0u, 0u);
+            raw[i][0] = w.x;
+            raw[i][1] = w.y;
+        }
     }
-    // per-channel min / max over the rows, both channels at once (packed
+    // per-channel min / max over the rows, a channel pair at once (packed
     // fp16, exact; -0 is canonicalised after), then across the row ranges
-    f16x2 mn2 = as_h2(raw[0]), mx2 = mn2;
+    f16x2 mn2[NP], mx2[NP];
 #pragma unroll
-    for (int i = 1; i < S::TG; ++i) {
-        mn2 = __builtin_elementwise_min(mn2, as_h2(raw[i]));
-        mx2 = __builtin_elementwise_max(mx2, as_h2(raw[i]));
-    }
+    for (int c = 0; c < NP; ++c) {
+        mn2[c] = as_h2(raw[0][c]);
+        mx2[c] = mn2[c];
 #pragma unroll
-    for (int o = S::CPW; o < 64 && S::SPL > 1; o <<= 1) {
-        mn2 = __builtin_elementwise_min(mn2, as_h2(__shfl_xor(__builtin_bit_cast(uint32_t, mn2), o)));
-        mx2 = __builtin_elementwise_max(mx2, as_h2(__shfl_xor(__builtin_bit_cast(uint32_t, mx2), o)));
+        for (int i = 1; i < S::TG; ++i) {
+            mn2[c] = __builtin_elementwise_min(mn2[c], as_h2(raw[i][c]));
+            mx2[c] = __builtin_elementwise_max(mx2[c], as_h2(raw[i][c]));
+        }
+#pragma unroll
+        for (int o = S::CPW; o < 64 && S::SPL > 1; o <<= 1) {
+            mn2[c] = __builtin_elementwise_min(mn2[c], as_h2(__shfl_xor(__builtin_bit_cast(uint32_t, mn2[c]), o)));
+            mx2[c] = __builtin_elementwise_max(mx2[c], as_h2(__shfl_xor(__builtin_bit_cast(uint32_t, mx2[c]), o)));
+        }
     }
     if (!active) return;
-    GroupQ q[2];
+    GroupQ q[CPT];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) q[e] = make_group(float(mn2[e]) + 0.0f, float(mx2[e]) + 0.0f, L);
-    const int64_t side = j.dst * kd + 2 * cp;
+    for (int e = 0; e < CPT; ++e) q[e] = make_group(float(mn2[e >> 1][e & 1]) + 0.0f, float(mx2[e >> 1][e & 1]) + 0.0f, L);
+    const int64_t side = j.dst * kd + CPT * cp;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < CPT; ++e) {
         uint32_t words[S::WT];
 #pragma unroll
         for (int w = 0; w < S::WT; ++w) words[w] = 0;
         const float nmn = -q[e].mn;
 #pragma unroll
         for (int i = 0; i < S::TG; ++i) {
-            const float d = e == 0 ? sub_half<0>(raw[i], nmn) : sub_half<1>(raw[i], nmn);
+            const float d = (e & 1) == 0 ? sub_half<0>(raw[i][e >> 1], nmn) : sub_half<1>(raw[i][e >> 1], nmn);
             words[i / S::PER] |= code_of<BITS>(d, q[e]) << (BITS * (i % S::PER));
         }
         WordVec<S::WT>::st(codes + (side + e) * S::W + sp * S::WT, words);
     }
     if (sp == 0) {
-        *reinterpret_cast<uint32_t*>(scale + side) =
-            uint32_t(float_to_half_bits(q[0].scale)) | (uint32_t(float_to_half_bits(q[1].scale)) << 16);
-        *reinterpret_cast<uint32_t*>(zero + side) =
-            uint32_t(float_to_half_bits(q[0].mn)) | (uint32_t(float_to_half_bits(q[1].mn)) << 16);
+        uint32_t sv[NP], zv[NP];
+#pragma unroll
+        for (int c = 0; c < NP; ++c) {
+            sv[c] = uint32_t(float_to_half_bits(q[2 * c].scale)) | (uint32_t(float_to_half_bits(q[2 * c + 1].scale)) << 16);
+            zv[c] = uint32_t(float_to_half_bits(q[2 * c].mn)) | (uint32_t(float_to_half_bits(q[2 * c + 1].mn)) << 16);
+        }
+        WordVec<NP>::st(reinterpret_cast<uint32_t*>(scale + side), sv);
+        WordVec<NP>::st(reinterpret_cast<uint32_t*>(zero + side), zv);
     }
 }
 
-template <int G, int BITS>
+template <int G, int BITS, int CPT = 2>
 __device__ __forceinline__ void quant_key_pair(const KeyJob& j, int kd, int cp, int sp,
                                                uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
                                                uint16_t* __restrict__ zero) {
-    quant_key_pair<G, BITS>(j, kd, cp, sp, codes, scale, zero, GlobalKeySrc{j, kd});
+    quant_key_pair<G, BITS, CPT>(j, kd, cp, sp, codes, scale, zero, GlobalKeySrc{j, kd});
 }
 
 }  // namespace qdev
