@@ -193,6 +193,26 @@ def test_split_counts(orc, n_splits, shape):
     _check_decode(orc, w, dc, k, v, n_splits=n_splits)
 
 
+@pytest.mark.parametrize("D,G,kbits", [(96, 64, 2), (160, 64, 2), (256, 64, 2), (256, 32, 4), (96, 32, 2),
+                                        (96, 128, 2), (192, 128, 2), (64, 16, 4)])
+def test_key_widths(orc, D, G, kbits):
+    """Key dimensions whose channel quads fill whole waves (256 at G = 64,
+    192 at G = 128, any at G <= 32) take the four-channel key quantizer
+    threads, the others (96 and 160 at G = 64, 96 at G = 128) the
+    two-channel ones: every cache slice matches the oracle bit for bit and
+    the attention stays within the bar."""
+    w = _tiny(3 * G + 11, Hq=4, Hkv=2, D=D, G=G, kbits=kbits)
+    cap = w.capacity(16)
+    k, v = synth.keys(w), synth.values(w)
+    dc = new_cache(w, cap)
+    dc.append(dev_f16(k), dev_f16(v))
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            assert_slices_equal(slice_of(dc, b, h, w.T, w.T // w.kG),
+                                oracle_slice(orc, w, k[b, h], v[b, h], cap // w.kG, cap), f"D{D} G{G}")
+    _check_decode(orc, w, dc, k, v)
+
+
 def _cache_arrays(dc, T, nblk):
     B, H = dc.cfg.batch, dc.cfg.n_kv_heads
     return [slice_of(dc, b, h, T, nblk) for b in range(B) for h in range(H)]
